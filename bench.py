@@ -1,0 +1,304 @@
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+A step is one verify round over one batch of synthetic inputs: for the chain
+workload (default, B=256 sequences, N=7 drafts, V=128256, bf16 logits, T=1)
+spec_verify_chain plus kv_compact_indices.  Inputs are resident in HBM before
+the timed region; the step cycles through a pool of distinct logit sets
+(8 x 0.99 GB for the chain workload, far beyond the 256 MB Infinity Cache)
+and uses a fresh Philox round per step.
+
+Timing: W untimed warm-up steps, then K steps bracketed by a device
+synchronize and HIP events on the stream the library launches on.  The
+dominant kernel (row statistics) is timed by events the library records
+around it in every timed step.
+
+Output: one JSON line (see the keys below); also the oracle timed on this
+host's cores on a bounded sample (cpu_baseline).
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+  python bench.py --copy-calibration     # plain copy of known size, for PMC scaling
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_stats_chain_c3_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
+                  for f in ("specverify.hip", "sv_device.h")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(stats_launch_bytes: int):
+    """HBM bytes per launch of the row-statistics kernel from the committed
+    rocprofv3 PMC summary, if it was taken on the current kernel source."""
+    try:
+        with open(PROFILE_PMC) as f:
+            p = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    if p.get("kernel_hash") != kernel_hash():
+        return None, "stale"
+    return int(p["hbm_bytes_per_launch"]), p
+
+
+def build_pool(w, pool: int, device: str):
+    import synth
+    sets = []
+    for i in range(pool):
+        log(f"[bench] generating logit set {i + 1}/{pool} ({w.name})")
+        if w.kind == "chain":
+            sets.append(synth.chain_inputs(w, seed=9000 + i, device=device))
+        elif w.kind == "tree_static":
+            sets.append(synth.static_tree_inputs(w, seed=9000 + i, device=device))
+        else:
+            sets.append(synth.dynamic_tree_inputs(w, seed=9000 + i, device=device))
+    return sets
+
+
+def algorithmic_bytes(w, s) -> tuple:
+    """(bytes of every logit row the step can need, bytes the row-statistics
+    kernel reads) for one step on logit set s."""
+    import synth
+    if w.kind == "chain":
+        full = synth.algorithmic_bytes_chain(w.B, w.N, w.V, w.elem_bytes)
+        stats = w.B * 2 * w.N * w.V * w.elem_bytes
+        return full, stats
+    par = s["parents"].cpu().numpy()
+    full = synth.algorithmic_bytes_tree(par if par.ndim == 2 else par[None].repeat(w.B, 0), w.V, w.elem_bytes)
+    import numpy as np
+    p2 = par if par.ndim == 2 else np.repeat(par[None], w.B, 0)
+    internal = sum(len(set(int(x) for x in row[1:])) for row in p2)
+    stats = 2 * internal * w.V * w.elem_bytes
+    return full, stats
+
+
+def cpu_baseline(w, sets, budget_s: float):
+    """The oracle, as it stands, on this host's cores over a bounded sample of
+    the same workload; rounds/s scaled from sequences/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = min(os.cpu_count() or 1, 16)
+    s = sets[0]
+    zq, zp = synth.to_oracle(s["zq"]), synth.to_oracle(s["zp"])
+    done_seq, t_total, reps = 0, 0.0, 0
+    B = w.B
+    chunk = min(B, max(threads, 8))
+    while t_total < budget_s and reps < 64:
+        lo = (reps * chunk) % B
+        hi = min(B, lo + chunk)
+        t0 = time.perf_counter()
+        if w.kind == "chain":
+            oracle.verify_chain(zq, zp, s["d"].cpu().numpy(), 1, reps, w.T, b_range=(lo, hi), nthreads=threads)
+        else:
+            oracle.verify_tree(zq, zp, s["tokens"].cpu().numpy(), s["parents"].cpu().numpy(), 1, reps, w.T,
+                               max_depth=w.depth, b_range=(lo, hi), nthreads=threads)
+        t_total += time.perf_counter() - t0
+        done_seq += hi - lo
+        reps += 1
+    rounds_per_s = (done_seq / B) / t_total
+    return {"value": rounds_per_s, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done_seq} sequences ({done_seq / B:.3g} rounds of B={B}) of logit set 0, "
+                      f"{t_total:.1f} s, {threads} OpenMP threads; rounds/s = sequences/s / B"}
+
+
+def copy_calibration():
+    """A plain device copy of known size (for scaling PMC byte counters)."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--pool", type=int, default=None)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are independent; "
+              "see DESIGN.md for how the step shards). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import rejection_sampling_verify_14_amd as sv
+    import synth
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w = synth.WORKLOADS[args.workload]
+    pool = args.pool or w.pool
+    sets = build_pool(w, pool, "cuda")
+    hip = Hip()
+    dev = "cuda"
+    B = w.B
+    if w.kind == "chain":
+        outs = sv.alloc_chain_outputs(B, w.N, dev)
+        ws = torch.empty(sv.chain_workspace_bytes(B, w.N, w.V), dtype=torch.uint8, device=dev)
+        width = w.N + 1
+    else:
+        T = sets[0]["zq"].shape[1] - 1
+        outs = sv.alloc_tree_outputs(B, T, w.depth, dev)
+        ws = torch.empty(sv.tree_workspace_bytes(B, T, w.V), dtype=torch.uint8, device=dev)
+        width = w.depth + 1
+    kv_out = {"src_rows": torch.empty((B, width), dtype=torch.int32, device=dev),
+              "kv_len": torch.empty(B, dtype=torch.int32, device=dev)}
+    kv_len_in = torch.full((B,), max(w.L0, 0), dtype=torch.int32, device=dev)
+    kv = None
+    if w.kind == "tree_dynamic":
+        kv = synth.kv_buffer(B, 4096 + w.budget, w.kv_heads, w.kv_dim, seed=5, device=dev)
+
+    def step(i, timing=None):
+        s = sets[i % pool]
+        if w.kind == "chain":
+            sv.spec_verify_chain(s["zq"], s["zp"], s["d"], seed=2026, round=i, temperature=w.T, out=outs,
+                                 workspace=ws, timing=timing)
+            sv.kv_compact_indices(None, outs["num_accepted"], kv_len_in, w.N, out=kv_out)
+        else:
+            sv.spec_verify_tree(s["zq"], s["zp"], s["tokens"], s["parents"], seed=2026, round=i, temperature=w.T,
+                                max_depth=w.depth, out=outs, workspace=ws, timing=timing)
+            sv.kv_compact_indices(outs["path_nodes"], outs["num_accepted"], kv_len_in, w.depth, kv=kv, out=kv_out)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(hip.event(), hip.event()) for _ in range(K)]
+    t_begin, t_end = hip.event(), hip.event()
+    stream = torch.cuda.current_stream()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    log(f"[bench] timing {K} steps")
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(t_begin), ctypes.c_void_p(stream.cuda_stream))
+    wall0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, timing=ev[i])
+    hip.lib.hipEventRecord(ctypes.c_void_p(t_end), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hip.elapsed_ms(t_begin, t_end)
+    stats_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    ms_step = total_ms / K
+    k_mean = sum(stats_ms) / K
+    full_bytes, stats_bytes = algorithmic_bytes(w, sets[0])
+    if w.kind != "chain":
+        per = [algorithmic_bytes(w, s) for s in sets]
+        full_bytes = sum(p[0] for p in per) / len(per)
+        stats_bytes = sum(p[1] for p in per) / len(per)
+    rounds_per_s = 1000.0 / ms_step
+    eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
+    k_gbps = stats_bytes / (k_mean * 1e-3) / 1e9
+    acc = outs["num_accepted"].float()
+    traffic, pmc = load_traffic(int(stats_bytes)) if w.name == "c3" else (None, None)
+    result = {
+        "metric": "verified rounds/s + achieved HBM GB/s (% peak), B=256 N=7 V=128256",
+        "value": round(rounds_per_s, 2),
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {"c3": "chain verify B=256 N=7 V=128256 bf16 logits T=1.0",
+                         "c2": "chain verify B=64 N=5 V=32000 fp32 logits T=1.0",
+                         "c4": "static 26-node tree verify B=32 V=128256 bf16 logits T=1.0",
+                         "c5": "dynamic 61-node tree verify B=128 V=152064 bf16 T=0.7 + KV gather"}[w.name],
+            "logits": w.dtype, "B": B, "V": w.V, "pool_sets": pool,
+            "arithmetic": "row statistics f32 (f64 accumulation), accept ratio and sampled rows f64",
+        },
+        "effective_GBps": round(eff_gbps, 1),
+        "effective_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(full_bytes),
+        "mean_accepted": round(float(acc[acc >= 0].mean()), 4),
+        "roofline": {
+            "kernel": "k_stats_chain (row statistics)" if w.kind == "chain" else "k_stats_tree (row statistics)",
+            "bound": "hbm",
+            "achieved": round(k_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(k_mean, 5),
+            "algorithmic_bytes_per_launch": int(stats_bytes),
+        },
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")
+        result["cpu_baseline"] = cpu_baseline(w, sets, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) speculative-decoding
+ * verify-and-accept library, libspecverify.so.
+ *
+ * Pages the operations follow (cited by title and section):
+ *   [PT] "Decodificacao Especulativa e EAGLE-3", ai-engineering.academy,
+ *        Fase 10 - Licao 15 (the same lesson exists in Persian on
+ *        nextadmin.net).
+ *   [ZH] "投机解码与 EAGLE：步骤、发展历史与三代差异", caijizhuo.github.io.
+ * Notation: q = verifier (target) distribution, p = draft distribution.
+ *
+ * Conventions shared by every entry point
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates, frees or synchronises.  All work is enqueued
+ *     on `stream` (a hipStream_t; 0 = the null stream) in order, so outputs
+ *     are ready when that stream reaches the point after the call.
+ *   - Host-checkable argument errors return a status before anything is
+ *     launched (SV_EINVAL, SV_EDTYPE, SV_ESHAPE, SV_EALIGN, SV_EWORKSPACE);
+ *     SV_EHIP reports a failed launch.  Outputs are then unspecified.
+ *   - Data errors found on the device are reported per sequence, never by
+ *     status: out_num_accepted[b] = -1 and out_tokens row b all -1.  They are
+ *     NaN or +inf in a logit row the outcome reads, a row that is all -inf, a
+ *     token outside [0, V), a parent outside [0, n), or a walk longer than
+ *     max_depth.
+ *   - Logit rows: element (b, r, t) of a logits array lives at
+ *     base + (b*seq_stride + r*row_stride + t) elements.  Row starts must be
+ *     16-byte aligned (base and both strides times the element size
+ *     multiples of 16); V is arbitrary.
+ *   - Temperature T > 0 divides both q- and p-logits before the softmax.
+ *   - Uniforms: Philox4x32-10 (Salmon et al., SC'11), key = seed, counter =
+ *     (position, sequence, round low 32 bits, (round bits 32..59) << 4).  The
+ *     accept uniform of position/node n is the 53-bit double of words 0,1 of
+ *     the block at position n; the sampling uniform of slot s is the one of
+ *     words 2,3 of the block at position s.  A call is a pure function of its
+ *     inputs and (seed, round).
+ *   - Reentrant; no global mutable state; calls on different streams may
+ *     overlap as long as they use different workspaces and outputs.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum sv_status {
+    SV_OK = 0,
+    SV_EINVAL = 1,      /* NULL required pointer, bad count, T <= 0, ... */
+    SV_EDTYPE = 2,      /* dtype not SV_F32 / SV_BF16 */
+    SV_ESHAPE = 3,      /* N > 64, T+1 > 1024, max_depth < 0, ... */
+    SV_EALIGN = 4,      /* logit rows / KV rows not 16-byte aligned */
+    SV_EWORKSPACE = 5,  /* workspace NULL or smaller than required */
+    SV_EHIP = 6         /* a HIP launch failed */
+};
+
+enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
+
+/* Optional timing hook: when non-NULL, `stats_begin` and `stats_end` are
+ * recorded on `stream` right before and right after the row-statistics
+ * kernel (the pass that streams the logit rows), so a caller can time it. */
+typedef struct sv_timing {
+    hipEvent_t stats_begin;
+    hipEvent_t stats_end;
+} sv_timing;
+
+/* ABI version (incremented on any signature change). */
+int sv_abi_version(void);
+
+/* Static text for a status code. */
+const char* sv_status_string(int status);
+
+/* Workspace bytes spec_verify_chain needs for (B, N, V); 0 on bad sizes. */
+size_t sv_chain_workspace_bytes(int B, int N, int V);
+
+/* Workspace bytes spec_verify_tree needs for (B, T, V); 0 on bad sizes. */
+size_t sv_tree_workspace_bytes(int B, int T, int V);
+
+/*
+ * spec_verify_chain -- one verify round of B independent chains of N draft
+ * tokens ([PT] "O Conceito": N stacked accept calls over one verifier pass
+ * that returns q_1..q_{N+1}; walk left to right; at the first rejection j
+ * sample residual(q_j, p_j) and stop; if all are accepted sample a bonus
+ * token from q_{N+1}.  [PT] Implementando, Passo 1 (accept iff
+ * u < min(1, q(d)/p(d)), zero draft probability accepts) and Passo 2 (the
+ * residual (q-p)_+ normalised, q itself when it sums to zero).  [ZH]
+ * section 2 states the same three steps.)
+ *
+ *   target_logits  [B, N+1, V]  q-logits; row i tests draft d_{i+1}, row N is
+ *                               the bonus distribution (read only when all N
+ *                               drafts are accepted).
+ *   draft_logits   [B, N, V]    p-logits (may be NULL when N == 0).
+ *   dtype          SV_F32 or SV_BF16 (both logit arrays).
+ *   draft_tokens   [B, N] int32 d_1..d_N.
+ *   B >= 0, 0 <= N <= 64, V >= 1, T > 0.
+ * Outputs (out_tokens and out_num_accepted required, the rest optional):
+ *   out_tokens        [B, N+1] int32: d_1..d_k, the correction or bonus
+ *                     token, then -1.
+ *   out_num_accepted  [B] int32: k in [0, N], or -1 on a data error.
+ *   out_accept        [B, N] int8: the accept decision of every position
+ *                     (positions after the first rejection are decided too).
+ *   out_probs         [B, N, 2] float: (q_i(d_i), p_i(d_i)).
+ *   out_residual_mass [B] double: sum_t (q_{k+1}(t) - p_{k+1}(t))_+ after a
+ *                     rejection, 0 after the bonus.
+ * Sampling is an inverse CDF in token-id order: the first token whose
+ * running weight exceeds u*W, W the total weight, accumulated in double.
+ * workspace: device memory of at least sv_chain_workspace_bytes(B, N, V)
+ * bytes (no alignment beyond 256 bytes needed; contents need not be
+ * initialised).
+ */
+int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                      const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
+                      const int32_t* draft_tokens, int B, int N, int V, uint64_t seed, uint64_t round,
+                      float temperature, int32_t* out_tokens, int32_t* out_num_accepted, int8_t* out_accept,
+                      float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
+                      const sv_timing* timing, hipStream_t stream);
+
+/*
+ * spec_verify_tree -- one verify round over B flattened draft trees ([ZH]
+ * section 3: the tree is flattened into a sequence with numbered nodes and
+ * verified by one pass in which a node sees only itself and its ancestors;
+ * section 4, "eagle_round" step 4: walk from the root accepting children;
+ * [PT] O Conceito, EAGLE-2: the verifier scores every candidate in one pass
+ * and the most probable accepted path is kept).
+ *
+ * Reading of the walk: node n >= 1 is tested with q and p at parent(n) and
+ * its accept uniform; from the root, the walk descends into the
+ * lowest-index accepted child (siblings are expected in descending draft
+ * probability, so this is the most probable accepted path); it stops at a
+ * leaf (bonus sampled from that leaf's q) or at a node none of whose
+ * children is accepted (residual of that node's q and p).  The sampling
+ * uniform is that of slot depth(stop) + 1, so a path-shaped tree reproduces
+ * spec_verify_chain bit for bit.
+ *
+ *   target_logits  [B, T+1, V]  q-logits per node (node 0 = root).
+ *   draft_logits   [B, T+1, V]  p-logits per node (rows of leaves unread).
+ *   node_tokens    [B, T+1] int32 (entry 0 unread).
+ *   parents        [T+1] int32 when parents_shared != 0, else [B, T+1];
+ *                  parents[n] in [0, n) for n >= 1 (entry 0 unread).
+ *   0 <= T <= 1023, 0 <= max_depth <= T... (max_depth >= tree depth).
+ * Outputs (tokens, path_nodes, num_accepted required):
+ *   out_tokens        [B, max_depth+1] int32: tokens of the accepted path,
+ *                     then the correction/bonus token, then -1.
+ *   out_path_nodes    [B, max_depth+1] int32: 0, the accepted nodes, -1.
+ *   out_num_accepted  [B] int32: accepted depth k, or -1.
+ *   out_accept        [B, T+1] int8: the decision of every node (node 0: 1).
+ *   out_probs         [B, T+1, 2] float: (q_par(tok_n), p_par(tok_n)), node 0
+ *                     (0, 0).
+ *   out_residual_mass [B] double, as for chains.
+ */
+int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                     const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
+                     const int32_t* node_tokens, const int32_t* parents, int parents_shared, int B, int T, int V,
+                     int max_depth, uint64_t seed, uint64_t round, float temperature, int32_t* out_tokens,
+                     int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept, float* out_probs,
+                     double* out_residual_mass, void* workspace, size_t workspace_bytes, const sv_timing* timing,
+                     hipStream_t stream);
+
+/*
+ * kv_compact_indices -- KV rollback and compaction after a verify round
+ * ([PT] Implementando, Passo 4 and "Reversao de KV cache": a logical KV
+ * length truncated at the rejection; [ZH] section 3: after acceptance the
+ * KV rows of the accepted path are copied together and the other branches
+ * dropped).
+ *
+ * kv_len_in[b] = L0 is the KV row of node 0 (the pending token); the verify
+ * pass wrote node n (chain position n) at row L0 + n.  Accepting k drafts
+ * keeps k + 1 rows: out_src_rows[b, i] = L0 + path[i] for i <= k (path =
+ * identity for chains, path_nodes == NULL), -1 after; out_kv_len[b] =
+ * L0 + k + 1.  A sequence with num_accepted < 0 keeps out_kv_len = L0 and
+ * gets -1 rows.  A path that is not strictly increasing from node 0, or rows
+ * outside [0, kv_rows), mark the sequence with out_kv_len = -1 and leave its
+ * KV untouched.
+ *
+ * When kv != NULL the gather is done in place: for every plane (K and V of
+ * every layer, plane_stride bytes apart), row L0 + path[i] of sequence b
+ * (seq_stride bytes per sequence, row_stride bytes per row, row_bytes bytes
+ * copied) moves to row L0 + i.  Every source row is read before it can be
+ * overwritten.  kv, the strides and row_bytes must be multiples of 16.
+ */
+int kv_compact_indices(const int32_t* path_nodes, const int32_t* num_accepted, const int32_t* kv_len_in, int B,
+                       int max_depth, int32_t* out_src_rows, int32_t* out_kv_len, void* kv, int kv_rows,
+                       int64_t seq_stride, int64_t row_stride, int row_bytes, int n_planes, int64_t plane_stride,
+                       hipStream_t stream);
+
+/*
+ * sv_philox_uniforms -- the uniforms the verify step draws, for tests of
+ * the device generator: for sequences [0, nseq) and positions 1..npos,
+ * out_acc[s*npos + p-1] and out_samp[s*npos + p-1] (device double arrays,
+ * either may be NULL).
+ */
+int sv_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc, double* out_samp,
+                       hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,262 @@
+"""MI355X (gfx950) speculative-decoding verify-and-accept step.
+
+Thin Python binding of ``libspecverify.so`` (C ABI declared in
+``include/specverify.h``).  This module only marshals arguments: it checks
+tensor shapes, allocates outputs and the workspace with torch on the logits'
+device, and passes raw device pointers plus torch's current HIP stream.  All
+of the step runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback, and importing this module raises if the library is not built.
+
+Functions (same names as the C ABI):
+  spec_verify_chain  -- chain verify ([PT] "Decodificacao Especulativa e
+                        EAGLE-3", O Conceito and Implementando, Passo 1-3)
+  spec_verify_tree   -- flattened-tree verify ([ZH] "投机解码与 EAGLE",
+                        sections 3 and 4)
+  kv_compact_indices -- KV rollback / compaction ([PT] Passo 4; [ZH]
+                        section 3)
+  sv_philox_uniforms -- the step's uniforms (for tests)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SV_F32, SV_BF16 = 0, 1
+STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EDTYPE", 3: "SV_ESHAPE", 4: "SV_EALIGN", 5: "SV_EWORKSPACE",
+          6: "SV_EHIP"}
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({_lib().sv_status_string(code).decode()})")
+
+
+class SvTiming(ctypes.Structure):
+    _fields_ = [("stats_begin", ctypes.c_void_p), ("stats_end", ctypes.c_void_p)]
+
+
+_L = None
+
+
+def _lib():
+    global _L
+    if _L is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, u64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64, ctypes.c_size_t
+        L.sv_abi_version.restype = i32
+        L.sv_abi_version.argtypes = []
+        L.sv_status_string.restype = ctypes.c_char_p
+        L.sv_status_string.argtypes = [i32]
+        L.sv_chain_workspace_bytes.restype = sz
+        L.sv_chain_workspace_bytes.argtypes = [i32, i32, i32]
+        L.sv_tree_workspace_bytes.restype = sz
+        L.sv_tree_workspace_bytes.argtypes = [i32, i32, i32]
+        L.spec_verify_chain.restype = i32
+        L.spec_verify_chain.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, u64, u64,
+                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
+        L.spec_verify_tree.restype = i32
+        L.spec_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, u64, u64,
+                                       ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
+        L.kv_compact_indices.restype = i32
+        L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
+        L.sv_philox_uniforms.restype = i32
+        L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
+        if L.sv_abi_version() != 1:
+            raise ImportError("libspecverify.so ABI version mismatch")
+        _L = L
+    return _L
+
+
+def library():
+    """The loaded ctypes library (raises ImportError if it is not built)."""
+    return _lib()
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SV_F32
+    if t.dtype == torch.bfloat16:
+        return SV_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _check_logits(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be [B, rows, V] with a unit stride on V")
+
+
+def _timing(timing):
+    if timing is None:
+        return None
+    t = SvTiming(timing[0], timing[1])
+    return ctypes.byref(t)
+
+
+def chain_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(_lib().sv_chain_workspace_bytes(B, N, V))
+
+
+def tree_workspace_bytes(B: int, T: int, V: int) -> int:
+    return int(_lib().sv_tree_workspace_bytes(B, T, V))
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def alloc_chain_outputs(B: int, N: int, device):
+    return {
+        "tokens": torch.empty((B, N + 1), dtype=torch.int32, device=device),
+        "num_accepted": torch.empty(B, dtype=torch.int32, device=device),
+        "accept": torch.empty((B, N), dtype=torch.int8, device=device),
+        "probs": torch.empty((B, N, 2), dtype=torch.float32, device=device),
+        "residual_mass": torch.empty(B, dtype=torch.float64, device=device),
+    }
+
+
+def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor], draft_tokens: torch.Tensor,
+                      seed: int, round: int, temperature: float = 1.0, *, out: Optional[dict] = None,
+                      workspace: Optional[torch.Tensor] = None, timing=None, stream=None) -> dict:
+    """Verify B chains: target_logits [B, N+1, V], draft_logits [B, N, V]
+    (float32 or bfloat16), draft_tokens [B, N] int32.  Returns (or fills)
+    a dict with tokens [B, N+1], num_accepted [B], accept [B, N] (int8),
+    probs [B, N, 2] (q(d), p(d)) and residual_mass [B]."""
+    _check_logits(target_logits, "target_logits")
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    if N > 0:
+        _check_logits(draft_logits, "draft_logits")
+        if draft_logits.shape != (B, N, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B, N, V] with the dtype of target_logits")
+        if draft_tokens.shape != (B, N) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+            raise ValueError("draft_tokens must be a contiguous int32 [B, N] tensor")
+    dev = target_logits.device
+    o = out if out is not None else alloc_chain_outputs(B, N, dev)
+    nbytes = chain_workspace_bytes(B, N, V)
+    ws = _workspace(nbytes, dev, workspace)
+    dl = draft_logits if N > 0 else None
+    rc = _lib().spec_verify_chain(
+        _p(target_logits), target_logits.stride(0), target_logits.stride(1),
+        _p(dl), dl.stride(0) if dl is not None else 0, dl.stride(1) if dl is not None else 0,
+        _dtype_code(target_logits), _p(draft_tokens) if N > 0 else None, B, N, V, seed & (2 ** 64 - 1),
+        round & (2 ** 64 - 1), float(temperature), _p(o["tokens"]), _p(o["num_accepted"]), _p(o.get("accept")),
+        _p(o.get("probs")), _p(o.get("residual_mass")), _p(ws), ws.numel() * ws.element_size(), _timing(timing),
+        _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_chain")
+    return o
+
+
+def alloc_tree_outputs(B: int, T: int, max_depth: int, device):
+    return {
+        "tokens": torch.empty((B, max_depth + 1), dtype=torch.int32, device=device),
+        "path_nodes": torch.empty((B, max_depth + 1), dtype=torch.int32, device=device),
+        "num_accepted": torch.empty(B, dtype=torch.int32, device=device),
+        "accept": torch.empty((B, T + 1), dtype=torch.int8, device=device),
+        "probs": torch.empty((B, T + 1, 2), dtype=torch.float32, device=device),
+        "residual_mass": torch.empty(B, dtype=torch.float64, device=device),
+    }
+
+
+def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, node_tokens: torch.Tensor,
+                     parents: torch.Tensor, seed: int, round: int, temperature: float = 1.0, *, max_depth: int,
+                     out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, timing=None,
+                     stream=None) -> dict:
+    """Verify B flattened trees: logits [B, T+1, V] per node, node_tokens
+    [B, T+1] int32, parents [T+1] (shared) or [B, T+1] int32."""
+    _check_logits(target_logits, "target_logits")
+    _check_logits(draft_logits, "draft_logits")
+    B, nn, V = target_logits.shape
+    T = nn - 1
+    if draft_logits.shape != (B, nn, V) or draft_logits.dtype != target_logits.dtype:
+        raise ValueError("draft_logits must be [B, T+1, V] with the dtype of target_logits")
+    if node_tokens.shape != (B, nn) or node_tokens.dtype != torch.int32 or not node_tokens.is_contiguous():
+        raise ValueError("node_tokens must be a contiguous int32 [B, T+1] tensor")
+    if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.shape not in ((nn,), (B, nn)):
+        raise ValueError("parents must be a contiguous int32 [T+1] or [B, T+1] tensor")
+    dev = target_logits.device
+    o = out if out is not None else alloc_tree_outputs(B, T, max_depth, dev)
+    nbytes = tree_workspace_bytes(B, T, V)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = _lib().spec_verify_tree(
+        _p(target_logits), target_logits.stride(0), target_logits.stride(1), _p(draft_logits),
+        draft_logits.stride(0), draft_logits.stride(1), _dtype_code(target_logits), _p(node_tokens), _p(parents),
+        1 if parents.dim() == 1 else 0, B, T, V, max_depth, seed & (2 ** 64 - 1), round & (2 ** 64 - 1),
+        float(temperature), _p(o["tokens"]), _p(o["path_nodes"]), _p(o["num_accepted"]), _p(o.get("accept")),
+        _p(o.get("probs")), _p(o.get("residual_mass")), _p(ws), ws.numel() * ws.element_size(), _timing(timing),
+        _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_tree")
+    return o
+
+
+def kv_compact_indices(path_nodes: Optional[torch.Tensor], num_accepted: torch.Tensor, kv_len_in: torch.Tensor,
+                       max_depth: int, kv: Optional[torch.Tensor] = None, *, stacked_planes: bool = False,
+                       out: Optional[dict] = None, stream=None) -> dict:
+    """KV rollback/compaction.  path_nodes [B, max_depth+1] int32 (None for
+    a chain); kv (optional) is compacted in place: [B, L, ...] or, with
+    stacked_planes=True, [P, B, L, ...] (P planes, e.g. K and V of every
+    layer).  Returns src_rows [B, max_depth+1] and kv_len [B]."""
+    B = num_accepted.shape[0]
+    dev = num_accepted.device
+    o = out if out is not None else {
+        "src_rows": torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev),
+        "kv_len": torch.empty(B, dtype=torch.int32, device=dev),
+    }
+    kv_args = (None, 0, 0, 0, 0, 0, 0)
+    if kv is not None:
+        planes = kv if stacked_planes else kv.unsqueeze(0)
+        if planes.dim() < 3 or planes.shape[1] != B:
+            raise ValueError("kv must be [B, L, ...] (or [P, B, L, ...] with stacked_planes=True)")
+        es = planes.element_size()
+        row = planes[0, 0, 0]
+        if not row.is_contiguous():
+            raise ValueError("a KV row must be contiguous")
+        kv_args = (_p(planes), planes.shape[2], planes.stride(1) * es, planes.stride(2) * es, row.numel() * es,
+                   planes.shape[0], planes.stride(0) * es)
+    rc = _lib().kv_compact_indices(_p(path_nodes), _p(num_accepted), _p(kv_len_in), B, max_depth, _p(o["src_rows"]),
+                                   _p(o["kv_len"]), *kv_args, _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "kv_compact_indices")
+    return o
+
+
+def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda", stream=None):
+    """(u_acc, u_samp) [nseq, npos] float64 for positions 1..npos."""
+    a = torch.empty((nseq, npos), dtype=torch.float64, device=device)
+    s = torch.empty((nseq, npos), dtype=torch.float64, device=device)
+    rc = _lib().sv_philox_uniforms(seed & (2 ** 64 - 1), round & (2 ** 64 - 1), nseq, npos, _p(a), _p(s),
+                                   _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "sv_philox_uniforms")
+    return a, s
+
+
+__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "sv_philox_uniforms",
+           "chain_workspace_bytes", "tree_workspace_bytes", "alloc_chain_outputs", "alloc_tree_outputs",
+           "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16"]

@@ -1,0 +1,124 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, and rejects bad arguments with the documented status
+before launching anything.  Also: the product package never reaches the
+oracle and fails loudly when its library is missing."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+PKG = os.path.join(ROOT, "rejection_sampling_verify_14_amd")
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import rejection_sampling_verify_14_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from rejection_sampling_verify_14_amd.csrc.build import build
+        build()
+    m.library()
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\(", text, re.M)))
+
+
+def test_header_symbols_exported(sv):
+    names = _declared()
+    assert {"spec_verify_chain", "spec_verify_tree", "kv_compact_indices"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", sv.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = set(line.split()[-1] for line in out.stdout.splitlines() if line.strip())
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(sv.LIB_PATH)
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings_and_sizes(sv):
+    L = sv.library()
+    assert L.sv_abi_version() == 1
+    for code in range(7):
+        assert L.sv_status_string(code)
+    assert sv.chain_workspace_bytes(256, 7, 128256) > 0
+    assert sv.chain_workspace_bytes(1, 65, 10) == 0
+    assert sv.tree_workspace_bytes(1, 1024, 10) == 0
+    # workspace grows with every dimension
+    assert sv.chain_workspace_bytes(2, 7, 128256) > sv.chain_workspace_bytes(1, 7, 128256)
+    assert sv.chain_workspace_bytes(1, 7, 2 * 128256) > sv.chain_workspace_bytes(1, 7, 128256)
+
+
+FAKE = 0x10000  # 16-byte aligned host address never dereferenced: validation returns first
+
+
+def _chain(L, **kw):
+    a = dict(tq=FAKE, qs=8 * 32, qr=32, tp=FAKE, ps=8 * 32, pr=32, dt=0, d=FAKE, B=2, N=3, V=32, seed=0, rnd=0,
+             T=1.0, tok=FAKE, num=FAKE, acc=None, probs=None, mass=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return L.spec_verify_chain(a["tq"], a["qs"], a["qr"], a["tp"], a["ps"], a["pr"], a["dt"], a["d"], a["B"], a["N"],
+                               a["V"], a["seed"], a["rnd"], a["T"], a["tok"], a["num"], a["acc"], a["probs"],
+                               a["mass"], a["ws"], a["wsb"], None, None)
+
+
+def test_chain_argument_errors(sv):
+    L = sv.library()
+    assert _chain(L, dt=7) == 2                      # SV_EDTYPE
+    assert _chain(L, T=0.0) == 1 and _chain(L, T=-1.0) == 1 and _chain(L, T=float("nan")) == 1
+    assert _chain(L, N=65) == 3                      # SV_ESHAPE
+    assert _chain(L, V=0) == 1 and _chain(L, B=-1) == 1 and _chain(L, N=-1) == 1
+    assert _chain(L, tok=None) == 1 and _chain(L, num=None) == 1 and _chain(L, tq=None) == 1
+    assert _chain(L, tp=None) == 1 and _chain(L, d=None) == 1
+    assert _chain(L, tq=FAKE + 4) == 4               # SV_EALIGN
+    assert _chain(L, qr=33) == 4 and _chain(L, ps=8 * 32 + 2) == 4
+    assert _chain(L, dt=1, qr=4) == 4                # 4 bf16 = 8 bytes per row step
+    assert _chain(L, wsb=16) == 5 and _chain(L, ws=None) == 5   # SV_EWORKSPACE
+    assert _chain(L, B=0) == 0                       # empty batch: nothing to do
+
+
+def test_tree_and_kv_argument_errors(sv):
+    L = sv.library()
+
+    def tree(**kw):
+        a = dict(tq=FAKE, tp=FAKE, dt=0, tok=FAKE, par=FAKE, shared=1, B=2, T=5, V=32, md=3, T_=1.0, out=FAKE,
+                 path=FAKE, num=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return L.spec_verify_tree(a["tq"], 6 * 32, 32, a["tp"], 6 * 32, 32, a["dt"], a["tok"], a["par"], a["shared"],
+                                  a["B"], a["T"], a["V"], a["md"], 0, 0, a["T_"], a["out"], a["path"], a["num"],
+                                  None, None, None, a["ws"], a["wsb"], None, None)
+    assert tree(T=1024) == 3 and tree(md=6) == 3 and tree(md=-1) == 1
+    assert tree(par=None) == 1 and tree(path=None) == 1 and tree(T_=0.0) == 1 and tree(dt=9) == 2
+    assert tree(wsb=100) == 5 and tree(B=0) == 0
+    kv = L.kv_compact_indices
+    assert kv(None, FAKE, FAKE, 2, -1, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1
+    assert kv(None, None, FAKE, 2, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1
+    assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE + 8, 64, 4096, 64, 64, 1, 0, None) == 4
+    assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 72, 1, 0, None) == 4
+    assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 128, 1, 0, None) == 1  # row > stride
+    assert kv(None, FAKE, FAKE, 0, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 0
+    assert L.sv_philox_uniforms(0, 0, -1, 3, FAKE, None, None) == 1
+
+
+def test_product_never_reaches_the_oracle():
+    for dirpath, _, files in os.walk(PKG):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
+                assert "sv_oracle" not in text
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    code = ("import rejection_sampling_verify_14_amd as m, sys\n"
+            f"m.LIB_PATH = {str(tmp_path / 'nope.so')!r}\n"
+            "m._L = None\n"
+            "try:\n    m.library()\nexcept ImportError as e:\n    print('IMPORT-ERROR', e); sys.exit(0)\n"
+            "sys.exit(3)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
+    assert r.returncode == 0 and "IMPORT-ERROR" in r.stdout, r.stdout + r.stderr

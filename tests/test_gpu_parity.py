@@ -1,0 +1,336 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name before it runs.  Sizes: reduced cases span
+several 4096-element chunks and a ragged tail and run the oracle on every
+sequence; the full-size workloads (C1..C5) run the device path in the launch
+configuration the benchmark times and the oracle on a window of sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from _gpu import log, run_chain, run_tree
+from oracle import compare
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_14_amd as sv
+    sv.library()
+    oracle.lib()
+
+
+def _done(name, rep):
+    log(f"[parity] {name}: {rep.summary()}")
+    rep.check()
+
+
+# --------------------------------------------------------------------------- #
+# Philox
+# --------------------------------------------------------------------------- #
+def test_device_philox_matches_oracle():
+    """10^7 counters (10 seeds/rounds x 1000 sequences x 1000 positions):
+    the device uniforms equal the oracle's bit for bit."""
+    import rejection_sampling_verify_14_amd as sv
+    for i, (seed, rnd) in enumerate([(0, 0), (1, 7), (2 ** 40 + 3, 2 ** 33 + 9), (123456789, 499), (7, 2 ** 32),
+                                     (2 ** 64 - 1, 2 ** 60 - 1), (42, 1), (99, 12), (5, 6), (31337, 0)]):
+        log(f"[philox] seed={seed} round={rnd}")
+        a, s = sv.sv_philox_uniforms(seed, rnd, 1000, 1000)
+        ea, es = oracle.uniform_grid(seed, rnd, 1000, 1000)
+        assert np.array_equal(a.cpu().numpy(), ea)
+        assert np.array_equal(s.cpu().numpy(), es)
+
+
+# --------------------------------------------------------------------------- #
+# Chains, reduced sizes (oracle on every sequence)
+# --------------------------------------------------------------------------- #
+CHAIN_CASES = [
+    # name, workload, overrides (B, N, V, T, dtype)
+    ("c2_small_ragged", "c2", dict(B=16, N=5, V=9001)),
+    ("c3_small_bf16", "c3", dict(B=24, N=7, V=20011)),
+    ("c3_temp07", "c3", dict(B=16, N=4, V=12289, T=0.7)),
+    ("c3_n1", "c3", dict(B=40, N=1, V=5000)),
+    ("c3_n64", "c3", dict(B=4, N=64, V=3001)),
+    ("c1_tiny_v", "c1", dict(B=50, N=4, V=32)),
+    ("v_tail_only", "c2", dict(B=8, N=3, V=7)),
+    ("v_one_token", "c2", dict(B=4, N=2, V=1)),
+    ("f32_temp19", "c2", dict(B=12, N=6, V=4097, T=1.9)),
+]
+
+
+@pytest.mark.parametrize("name,wl,ov", CHAIN_CASES, ids=[c[0] for c in CHAIN_CASES])
+def test_chain_parity_reduced(name, wl, ov):
+    log(f"[case] {name}")
+    w = W[wl].with_sizes(**{k: v for k, v in ov.items() if k in ("V", "T")})
+    rep = compare.Report()
+    for rnd in range(3):
+        r, g, _ = run_chain(w, seed=1000 + rnd, rnd=rnd, B=ov.get("B"), N=ov.get("N"))
+        rep.merge(r)
+    _done(name, rep)
+
+
+def test_chain_n0_plain_sampling():
+    """N = 0: the step samples q_1 directly (no drafts)."""
+    log("[case] chain_n0")
+    w = W["c3"].with_sizes(V=30001)
+    rep, g, _ = run_chain(w, seed=3, rnd=3, B=32, N=0)
+    assert (g["num_accepted"] == 0).all()
+    _done("chain_n0", rep)
+
+
+def test_chain_edge_cases():
+    """NaN / +inf / all -inf rows, out-of-range tokens, -inf draft logit at d
+    (accepted), q(d) = -inf (rejected), p == q (all accepted), and masked
+    vocab entries, all in one batch."""
+    log("[case] chain_edges")
+    w = W["c2"].with_sizes(V=6007)
+    B, N = 12, 4
+
+    def plant(inp):
+        zq, zp, d = inp["zq"], inp["zp"], inp["d"]
+        zq[1, 2, 100] = float("nan")
+        zp[2, 0, 5] = float("inf")
+        zq[3, 1, :] = float("-inf")
+        d[4, 3] = w.V
+        d[5, 0] = -1
+        zp[6, 0, int(d[6, 0])] = float("-inf")
+        zq[7, 0, int(d[7, 0])] = float("-inf")
+        zp[8] = zq[8, :N]
+        zq[9, :, ::3] = float("-inf")
+        zp[9, :, ::3] = float("-inf")
+        d[9] = ((d[9] // 3) * 3 + 1).clamp(max=w.V - 2)  # unmasked ids (V - 2 = 2 mod 3)
+        zq[10, N, 7] = float("nan")   # bonus row: matters only if all are accepted
+        zp[10] = zq[10, :N]          # ... which they are
+    rep, g, _ = run_chain(w, seed=11, rnd=2, B=B, N=N, modify=plant)
+    k = g["num_accepted"]
+    assert k[1] == -1 and k[2] == -1 and k[3] == -1 and k[4] == -1 and k[5] == -1 and k[10] == -1
+    assert g["accept"][6, 0] == 1 and g["accept"][7, 0] == 0 and k[8] == N
+    _done("chain_edges", rep)
+
+
+def test_chain_strided_inputs():
+    """Sequence and row strides larger than the packed layout."""
+    log("[case] chain_strided")
+    w = W["c3"].with_sizes(V=8000)
+    B, N = 10, 3
+    inp = synth.chain_inputs(w, 5, "cuda", B=B, N=N)
+    bigq = torch.zeros((B, N + 3, w.V + 24), dtype=inp["zq"].dtype, device="cuda")
+    bigp = torch.zeros((B, N + 2, w.V + 40), dtype=inp["zp"].dtype, device="cuda")
+    bigq[:, :N + 1, :w.V] = inp["zq"]
+    bigp[:, :N, :w.V] = inp["zp"]
+    inp2 = {"zq": bigq[:, :N + 1, :w.V], "zp": bigp[:, :N, :w.V], "d": inp["d"]}
+    rep, g, _ = run_chain(w, seed=5, rnd=0, inputs=inp2)
+    _done("chain_strided", rep)
+
+
+# --------------------------------------------------------------------------- #
+# Chains, full sizes
+# --------------------------------------------------------------------------- #
+def test_c1_full_10000_rounds():
+    """C1 (B=1, N=4, V=32, fp32), 10,000 rounds with Philox keyed by
+    (seed, round, position); fixed logits, fresh d ~ p each round."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] c1_full")
+    w = W["c1"]
+    zq, zp = synth.chain_logits(w, 0, "cuda")
+    R = w.rounds
+    d_all = synth.chain_draft_tokens(w, zp.expand(R, -1, -1).contiguous(), seed=77)
+    outs = sv.alloc_chain_outputs(1, w.N, "cuda")
+    ws = torch.empty(sv.chain_workspace_bytes(1, w.N, w.V), dtype=torch.uint8, device="cuda")
+    toks, ks, accs, probs, mass = [], [], [], [], []
+    for r in range(R):
+        sv.spec_verify_chain(zq, zp, d_all[r:r + 1], seed=0, round=r, temperature=w.T, out=outs, workspace=ws)
+        toks.append(outs["tokens"].clone())
+        ks.append(outs["num_accepted"].clone())
+        accs.append(outs["accept"].clone())
+        probs.append(outs["probs"].clone())
+        mass.append(outs["residual_mass"].clone())
+    torch.cuda.synchronize()
+    g = {"tokens": torch.cat(toks).cpu().numpy(), "num_accepted": torch.cat(ks).cpu().numpy(),
+         "accept": torch.cat(accs).cpu().numpy(), "probs": torch.cat(probs).cpu().numpy(),
+         "residual_mass": torch.cat(mass).cpu().numpy()}
+    rep = compare.Report()
+    zqn, zpn, dn = synth.to_oracle(zq), synth.to_oracle(zp), d_all.cpu().numpy()
+    for r in range(R):
+        o = oracle.verify_chain(zqn, zpn, dn[r:r + 1], 0, r, w.T, nthreads=1,
+                                query=compare.sampled_tokens({k: v[r:r + 1] for k, v in g.items()}))
+        rep.merge(compare.compare_chain({k: v[r:r + 1] for k, v in g.items()}, o))
+    _done("c1_full", rep)
+
+
+@pytest.mark.parametrize("wl,rounds,window", [("c2", 3, 64), ("c3", 2, 24)])
+def test_chain_full_size(wl, rounds, window):
+    """C2 (all 64 sequences) and C3 (a window of sequences per round) at full
+    size, in the benchmark's launch configuration."""
+    w = W[wl]
+    rep = compare.Report()
+    for rnd in range(rounds):
+        lo = (rnd * 97) % (w.B - window + 1)
+        log(f"[case] {wl}_full round={rnd} window=({lo},{lo + window})")
+        r, g, _ = run_chain(w, seed=500 + rnd, rnd=rnd, b_range=(lo, lo + window))
+        log(f"   mean accepted {g['num_accepted'].mean():.3f} of {w.N}")
+        rep.merge(r)
+    _done(f"{wl}_full", rep)
+
+
+# --------------------------------------------------------------------------- #
+# Trees
+# --------------------------------------------------------------------------- #
+def test_path_tree_equals_chain_on_device():
+    """A path-shaped tree gives exactly the chain's outputs on the device."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] path_tree_eq_chain")
+    w = W["c3"].with_sizes(V=10007)
+    B, N = 20, 6
+    inp = synth.chain_inputs(w, 8, "cuda", B=B, N=N)
+    ch = sv.spec_verify_chain(inp["zq"], inp["zp"], inp["d"], seed=4, round=9, temperature=0.9)
+    zpt = torch.cat([inp["zp"], inp["zq"][:, N:N + 1]], dim=1).contiguous()
+    tok = torch.cat([torch.zeros((B, 1), dtype=torch.int32, device="cuda"), inp["d"]], dim=1).contiguous()
+    par = torch.arange(-1, N, dtype=torch.int32, device="cuda")
+    tr = sv.spec_verify_tree(inp["zq"], zpt, tok, par, seed=4, round=9, temperature=0.9, max_depth=N)
+    torch.cuda.synchronize()
+    assert torch.equal(ch["num_accepted"], tr["num_accepted"])
+    assert torch.equal(ch["tokens"], tr["tokens"])
+    assert torch.equal(ch["accept"], tr["accept"][:, 1:])
+    assert torch.equal(ch["probs"], tr["probs"][:, 1:])
+    assert torch.equal(ch["residual_mass"], tr["residual_mass"])
+
+
+def test_static_tree_reduced():
+    log("[case] static_tree_reduced")
+    w = W["c4"].with_sizes(V=9001)
+    rep = compare.Report()
+    for rnd in range(3):
+        inp = synth.static_tree_inputs(w, 40 + rnd, "cuda", B=12)
+        r, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 40 + rnd, rnd, w.T, w.depth)
+        rep.merge(r)
+    _done("static_tree_reduced", rep)
+
+
+def test_dynamic_tree_reduced():
+    log("[case] dynamic_tree_reduced")
+    w = W["c5"].with_sizes(V=7001)
+    rep = compare.Report()
+    for rnd in range(2):
+        inp = synth.dynamic_tree_inputs(w, 60 + rnd, "cuda", B=10)
+        r, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 60 + rnd, rnd, w.T, w.depth)
+        rep.merge(r)
+    _done("dynamic_tree_reduced", rep)
+
+
+def test_tree_edge_cases():
+    """Root-only tree (bonus from q_root), a bad parent, a walk deeper than
+    max_depth, NaN in an internal row -- per-sequence -1 flags."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] tree_edges")
+    w = W["c4"].with_sizes(V=3000)
+    inp = synth.static_tree_inputs(w, 3, "cuda", B=6)
+    zq, zp, tok = inp["zq"], inp["zp"], inp["tokens"]
+    par = inp["parents"].expand(6, -1).contiguous().clone()
+    par[1, 7] = 9           # parent not below the node
+    zq[2, 3, 11] = float("nan")
+    tok[3, 5] = w.V
+    rep, g = run_tree(zq, zp, tok, par, 3, 1, w.T, w.depth)
+    assert g["num_accepted"][1] == -1 and g["num_accepted"][2] == -1 and g["num_accepted"][3] == -1
+    _done("tree_edges", rep)
+    # a single-node tree: bonus straight from the root
+    one = sv.spec_verify_tree(zq[:, :1].contiguous(), zp[:, :1].contiguous(), tok[:, :1].contiguous(),
+                              torch.tensor([-1], dtype=torch.int32, device="cuda"), seed=1, round=1,
+                              temperature=1.0, max_depth=0)
+    torch.cuda.synchronize()
+    assert (one["num_accepted"] == 0).all()
+    o = oracle.verify_tree(synth.to_oracle(zq[:, :1].contiguous()), synth.to_oracle(zp[:, :1].contiguous()),
+                           tok[:, :1].cpu().numpy(), np.array([-1], np.int32), 1, 1, 1.0, max_depth=0)
+    assert np.array_equal(one["tokens"].cpu().numpy(), o["tokens"])
+    # walk deeper than max_depth on an all-accepting path tree
+    B, D = 3, 5
+    zq2 = zq[:B, :D + 1].contiguous()
+    zp2 = zq2.clone()
+    tok2 = torch.zeros((B, D + 1), dtype=torch.int32, device="cuda")
+    par2 = torch.arange(-1, D, dtype=torch.int32, device="cuda")
+    deep = sv.spec_verify_tree(zq2, zp2, tok2, par2, seed=0, round=0, temperature=1.0, max_depth=D - 1)
+    torch.cuda.synchronize()
+    assert (deep["num_accepted"] == -1).all()
+
+
+@pytest.mark.parametrize("wl", ["c4", "c5"])
+def test_tree_full_size(wl):
+    """C4 (static 26-node tree, B=32) and C5 (dynamic 61-node trees, B=128,
+    T=0.7) at full size; the oracle checks a window of sequences."""
+    w = W[wl]
+    log(f"[case] {wl}_full")
+    if wl == "c4":
+        inp = synth.static_tree_inputs(w, 900, "cuda")
+        rng = (0, w.B)
+    else:
+        inp = synth.dynamic_tree_inputs(w, 901, "cuda")
+        rng = (40, 56)
+    rep, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 900, 3, w.T, w.depth, b_range=rng)
+    log(f"   mean accepted depth {g['num_accepted'].mean():.3f}")
+    _done(f"{wl}_full", rep)
+
+
+# --------------------------------------------------------------------------- #
+# KV compaction
+# --------------------------------------------------------------------------- #
+def test_kv_compaction_full_c5():
+    """C5's KV buffer [B=128, 4096+60, 8, 128] bf16 (two planes): the
+    in-place gather equals torch.index_select on a copy, the indices and
+    lengths equal the oracle's, and rows outside the kept path are
+    untouched."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] kv_c5_full")
+    w = W["c5"]
+    B, L = w.B, 4096 + w.budget
+    rng = np.random.default_rng(0)
+    # a valid random path per sequence (strictly increasing from node 0)
+    k = rng.integers(0, w.depth + 1, size=B).astype(np.int32)
+    k[5] = -1
+    path = np.full((B, w.depth + 1), -1, np.int32)
+    for b in range(B):
+        if k[b] >= 0:
+            path[b, :k[b] + 1] = [0] + sorted(rng.choice(np.arange(1, w.budget + 1), size=k[b], replace=False))
+    L0 = np.full(B, w.L0, np.int32)
+    kv = torch.stack([synth.kv_buffer(B, L, w.kv_heads, w.kv_dim, seed=s, device="cuda") for s in (1, 2)])
+    orig = kv.clone()
+    out = sv.kv_compact_indices(torch.tensor(path, device="cuda"), torch.tensor(k, device="cuda"),
+                                torch.tensor(L0, device="cuda"), w.depth, kv=kv, stacked_planes=True)
+    torch.cuda.synchronize()
+    src_o, len_o = oracle.kv_compact(path, k, L0, w.depth)
+    assert np.array_equal(out["src_rows"].cpu().numpy(), src_o)
+    assert np.array_equal(out["kv_len"].cpu().numpy(), len_o)
+    expect = orig.clone()
+    for b in range(B):
+        if k[b] > 0:
+            rows = torch.tensor(src_o[b, :k[b] + 1], device="cuda", dtype=torch.long)
+            expect[:, b, w.L0:w.L0 + k[b] + 1] = torch.index_select(orig[:, b], 1, rows)
+    assert torch.equal(kv, expect)
+
+
+def test_kv_chain_indices_and_invalid_paths():
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] kv_chain_invalid")
+    k = torch.tensor([3, 0, -1, 2, 2], dtype=torch.int32, device="cuda")
+    L0 = torch.tensor([10, 20, 30, 40, 50], dtype=torch.int32, device="cuda")
+    out = sv.kv_compact_indices(None, k, L0, 4)
+    torch.cuda.synchronize()
+    src_o, len_o = oracle.kv_compact(None, k.cpu().numpy(), L0.cpu().numpy(), 4)
+    assert np.array_equal(out["src_rows"].cpu().numpy(), src_o)
+    assert np.array_equal(out["kv_len"].cpu().numpy(), len_o)
+    # a path that is not strictly increasing, and one past kv_rows
+    path = torch.tensor([[0, 2, 1, -1, -1], [0, 3, 60, -1, -1]], dtype=torch.int32, device="cuda")
+    kv = torch.zeros((2, 64, 16), dtype=torch.bfloat16, device="cuda")
+    before = kv.clone()
+    out = sv.kv_compact_indices(path, torch.tensor([2, 2], dtype=torch.int32, device="cuda"),
+                                torch.tensor([0, 10], dtype=torch.int32, device="cuda"), 4, kv=kv)
+    torch.cuda.synchronize()
+    assert out["kv_len"].tolist() == [-1, -1]
+    assert torch.equal(kv, before)
