@@ -23,9 +23,11 @@
  *     token outside [0, V), a parent outside [0, n), or a walk longer than
  *     max_depth.
  *   - Logit rows: element (b, r, t) of a logits array lives at
- *     base + (b*seq_stride + r*row_stride + t) elements.  Row starts must be
- *     16-byte aligned (base and both strides times the element size
- *     multiples of 16); V is arbitrary.
+ *     base + (b*seq_stride + r*row_stride + t) elements.  The base must be
+ *     aligned to the element size (SV_EALIGN otherwise); V and the strides
+ *     are arbitrary.  Rows whose start is 16-byte aligned (e.g. V a multiple
+ *     of 8 for bf16, of 4 for fp32) stream entirely as 16-byte vectors;
+ *     others take a short scalar head.
  *   - Temperature T > 0 divides both q- and p-logits before the softmax.
  *   - Uniforms: Philox4x32-10 (Salmon et al., SC'11), key = seed, counter =
  *     (position, sequence, round low 32 bits, (round bits 32..59) << 4).  The
@@ -53,7 +55,7 @@ enum sv_status {
     SV_EINVAL = 1,      /* NULL required pointer, bad count, T <= 0, ... */
     SV_EDTYPE = 2,      /* dtype not SV_F32 / SV_BF16 */
     SV_ESHAPE = 3,      /* N > 64, T+1 > 1024, max_depth < 0, ... */
-    SV_EALIGN = 4,      /* logit rows / KV rows not 16-byte aligned */
+    SV_EALIGN = 4,      /* logits not element-aligned / KV rows not 16-byte aligned */
     SV_EWORKSPACE = 5,  /* workspace NULL or smaller than required */
     SV_EHIP = 6         /* a HIP launch failed */
 };
@@ -141,7 +143,8 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  *   node_tokens    [B, T+1] int32 (entry 0 unread).
  *   parents        [T+1] int32 when parents_shared != 0, else [B, T+1];
  *                  parents[n] in [0, n) for n >= 1 (entry 0 unread).
- *   0 <= T <= 1023, 0 <= max_depth <= T... (max_depth >= tree depth).
+ *   0 <= T <= 1023, 0 <= max_depth <= T; a walk longer than max_depth is a
+ *   data error, so max_depth should be at least the tree's depth.
  * Outputs (tokens, path_nodes, num_accepted required):
  *   out_tokens        [B, max_depth+1] int32: tokens of the accepted path,
  *                     then the correction/bonus token, then -1.

@@ -107,6 +107,12 @@ def _swap_library(path):
     return prev
 
 
+def _temperature(T) -> float:
+    """The temperature as the device library receives it: a 32-bit float
+    (the C ABI's `float temperature`), widened exactly to double."""
+    return float(np.float32(T))
+
+
 def _dtype_code(a: np.ndarray) -> int:
     if a.dtype == np.float32:
         return F32
@@ -234,6 +240,7 @@ def _alloc_out(B: int, width: int, nslots: int, rows: int, tree: bool, query):
 def verify_chain(zq, zp, d, seed: int, rnd: int, T: float = 1.0, *, u=None, b_range=None, nthreads=None,
                  query=None):
     """Chain verify of B sequences.  zq [B, N+1, V], zp [B, N, V], d [B, N].
+    T is rounded to float32 first, as the device library receives it.
 
     u (optional) [B, 2N+1] overrides Philox: accept uniforms of positions
     1..N, then sampling uniforms of slots 1..N+1.  b_range = (lo, hi)
@@ -256,7 +263,7 @@ def verify_chain(zq, zp, d, seed: int, rnd: int, T: float = 1.0, *, u=None, b_ra
     lo, hi = b_range if b_range is not None else (0, B)
     o, s = _alloc_out(B, N + 1, max(N, 1), N + 1, False, query)
     rc = lib().orc_verify_chain(_ptr(zq), qs, qr, _ptr(zp), ps, pr, _dtype_code(zq), _ptr(d), B, N, V, seed, rnd,
-                                float(T), _ptr(u), lo, hi, nthreads or threads_available(), ctypes.byref(s))
+                                _temperature(T), _ptr(u), lo, hi, nthreads or threads_available(), ctypes.byref(s))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o
@@ -278,7 +285,7 @@ def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.
     lo, hi = b_range if b_range is not None else (0, B)
     o, s = _alloc_out(B, max_depth + 1, nn, nn, True, query)
     rc = lib().orc_verify_tree(_ptr(zq), qs, qr, _ptr(zp), ps, pr, _dtype_code(zq), _ptr(node_tokens), _ptr(parents),
-                               shared, B, Tn, V, max_depth, seed, rnd, float(T), _ptr(u), lo, hi,
+                               shared, B, Tn, V, max_depth, seed, rnd, _temperature(T), _ptr(u), lo, hi,
                                nthreads or threads_available(), ctypes.byref(s))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")

@@ -48,8 +48,10 @@ __device__ __forceinline__ void accumulate_values(const float* x, float c, doubl
 #pragma unroll
     for (int i = 1; i < K; ++i) lm = fmaxf(lm, x[i]);
     // move the reference when the first finite value arrives or the maximum
-    // jumps by more than 2^64 (keeps every fp32 term below 2^64)
-    if ((lm - ref) * c > 64.0f) {
+    // grows by more than one binary order of magnitude: the terms that
+    // dominate the sum then have exponent arguments in (-few, 1], where the
+    // fp32 rounding of (x - ref) * c is smallest
+    if ((lm - ref) * c > 1.0f) {
         acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
         ref = lm;
     }
@@ -78,11 +80,22 @@ __device__ __forceinline__ void combine_stat(float& m, double& s, float m2, doub
 template <int DT, int U>
 __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row, int V, float c, double cd)
 {
-    constexpr int EPV = 16 / elem_bytes<DT>();
-    const int nvec = V / EPV;
-    const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
+    constexpr int EB = elem_bytes<DT>();
+    constexpr int EPV = 16 / EB;
     float ref = -INFINITY;
     double acc = 0.0;
+    // elements before the first 16-byte boundary (rows need only be
+    // element-aligned); the rest of the row streams as 16-byte vectors
+    int head = (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
+    head = head < V ? head : V;
+    if ((int)threadIdx.x < head) {
+        float x[1] = {load_logit<DT>(row, threadIdx.x)};
+        accumulate_values<1>(x, c, cd, ref, acc);
+    }
+    row += head * EB;
+    V -= head;
+    const int nvec = V / EPV;
+    const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
     int v = threadIdx.x;
     for (; v + (U - 1) * kBlock < nvec; v += U * kBlock) {
         uint4 raw[U];
@@ -205,7 +218,12 @@ __device__ __forceinline__ void fill_residual_state(SeqState& s, const RowStat& 
     s.mp = rp.m;
     s.sq = rq.s;
     s.sp = rp.s;
-    s.theta = (float)(((double)rq.m - (double)rp.m) + (double)T * (log(rq.s) - log(rp.s)));
+    const double theta = ((double)rq.m - (double)rp.m) + (double)T * (log(rq.s) - log(rp.s));
+    // margin: pass-1 sums carry a relative error well below 1e-6 each; the
+    // margin covers ten times that plus the fp32 rounding of theta
+    const double margin = 4e-6 * (double)T + 2.5e-7 * fabs(theta) + 1e-30;
+    s.thr_lo = (float)(theta - margin);
+    s.thr_hi = (float)(theta + margin);
 }
 
 // One wave64 per chain; lane i handles position i+1.
@@ -433,7 +451,7 @@ template <int DT>
 __device__ __forceinline__ void load_chunk16(const char* __restrict__ row, int V, int c, int tid, float* x)
 {
     const int64_t e0 = (int64_t)c * kChunk + (int64_t)tid * kPerThread;
-    if (e0 + kPerThread <= V) {
+    if (e0 + kPerThread <= V && (((uintptr_t)(row + e0 * elem_bytes<DT>())) & 15u) == 0) {
         const uint4* p = reinterpret_cast<const uint4*>(row + e0 * elem_bytes<DT>());
         constexpr int NV = kPerThread * elem_bytes<DT>() / 16;
         uint4 raw[NV];
@@ -447,14 +465,12 @@ __device__ __forceinline__ void load_chunk16(const char* __restrict__ row, int V
     }
 }
 
-// Chunk sums.  Residual: {sum a, sum b, sum_{q>p} a, sum_{q>p} b} with
-// a = exp((zq - mq)/T), b = exp((zp - mp)/T).  Bonus: {m_c, sum exp((z -
-// m_c)/T), bad flag, 0} with m_c the chunk maximum.
+// Chunk sums of the row(s) a sequence samples from (see ChunkSums).
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_sample_partials(const char* __restrict__ zq, const char* __restrict__ zp,
                                                             int V, int nchunks, double invT,
                                                             const SeqState* __restrict__ st,
-                                                            double4* __restrict__ partials)
+                                                            ChunkSums* __restrict__ partials)
 {
     constexpr int EB = elem_bytes<DT>();
     const int c = blockIdx.x, b = blockIdx.y;
@@ -464,26 +480,38 @@ __global__ __launch_bounds__(kBlock) void k_sample_partials(const char* __restri
     __shared__ float redf[kWaves];
     float xq[kPerThread];
     load_chunk16<DT>(zq + s.q_off * EB, V, c, threadIdx.x, xq);
-    double4 out;
+    ChunkSums out;
+    out.pad = 0.0;
     if (s.mode == kModeResidual) {
         float xp[kPerThread];
         load_chunk16<DT>(zp + s.p_off * EB, V, c, threadIdx.x, xp);
-        double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0;
+        double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0, na = 0.0, nb = 0.0;
+        float dmin = INFINITY, dmax = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const double a = exp(((double)xq[j] - (double)s.mq) * invT);
             const double bb = exp(((double)xp[j] - (double)s.mp) * invT);
             sa += a;
             sb += bb;
-            if (xq[j] - xp[j] > s.theta) {
+            const float d = xq[j] - xp[j];
+            if (d > s.thr_hi) {
                 pa += a;
                 pb += bb;
+            } else if (d >= s.thr_lo) {
+                na += a;
+                nb += bb;
+                dmin = fminf(dmin, d);
+                dmax = fmaxf(dmax, d);
             }
         }
-        out.x = block_sum(sa, red);
-        out.y = block_sum(sb, red);
-        out.z = block_sum(pa, red);
-        out.w = block_sum(pb, red);
+        out.sa = block_sum(sa, red);
+        out.sb = block_sum(sb, red);
+        out.pa = block_sum(pa, red);
+        out.pb = block_sum(pb, red);
+        out.na = block_sum(na, red);
+        out.nb = block_sum(nb, red);
+        out.dmax = block_max(dmax, redf);
+        out.dmin = -block_max(-dmin, redf);
     } else {
         float lm = -INFINITY;
         int bad = 0;
@@ -498,28 +526,34 @@ __global__ __launch_bounds__(kBlock) void k_sample_partials(const char* __restri
 #pragma unroll
             for (int j = 0; j < kPerThread; ++j) sa += exp(((double)xq[j] - (double)mc) * invT);
         }
-        out.x = (double)mc;
-        out.y = block_sum(sa, red);
-        out.z = (double)__syncthreads_or(bad);
-        out.w = 0.0;
+        out.sa = (double)mc;
+        out.sb = block_sum(sa, red);
+        out.pa = (double)__syncthreads_or(bad);
+        out.pb = out.na = out.nb = 0.0;
+        out.dmin = out.dmax = 0.0f;
     }
     if (threadIdx.x == 0) partials[(int64_t)b * nchunks + c] = out;
 }
 
-// Weight of element j of the chunk for the final rescan (same formulas as the
-// partials): residual a - rho*b on {q > p}, q itself on fallback, bonus
-// exp((z - m_c)/T).
-struct SampleParams {
-    double rho;
-    double mc;
-    int mode;      // 0 residual, 1 bonus, 2 residual fell back to q
-};
+constexpr int kModeFallback = 2;  // residual of total zero: sample q itself
+
+// Exact weight of one element of the residual: a - rho*b where q > p for
+// certain, max(0, a - rho*b) in the near-threshold band, 0 below it.
+__device__ __forceinline__ double residual_weight(float xq, float xp, const SeqState& s, double invT, double rho)
+{
+    const float d = xq - xp;
+    if (!(d >= s.thr_lo)) return 0.0;
+    const double a = exp(((double)xq - (double)s.mq) * invT);
+    const double bb = exp(((double)xp - (double)s.mp) * invT);
+    const double w = a - rho * bb;
+    return (d > s.thr_hi) ? w : fmax(0.0, w);
+}
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict__ zq, const char* __restrict__ zp,
                                                          int V, int nchunks, double invT,
                                                          const SeqState* __restrict__ st,
-                                                         const double4* __restrict__ partials, int width,
+                                                         const ChunkSums* __restrict__ partials, int width,
                                                          int32_t* __restrict__ out_tokens,
                                                          int32_t* __restrict__ out_num,
                                                          int32_t* __restrict__ out_path,
@@ -532,33 +566,56 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
     if (s.status) return;
     __shared__ double red[kWaves];
     __shared__ float redf[kWaves];
+    __shared__ double s_near[kMaxChunks];
     __shared__ int s_chunk;
     __shared__ double s_base;
     __shared__ int s_owner;
-    const double4* P = partials + (int64_t)b * nchunks;
+    const ChunkSums* P = partials + (int64_t)b * nchunks;
     // chunks per thread (contiguous groups, token order)
     const int g = (nchunks + kBlock - 1) / kBlock;
     const int c0 = tid * g;
     const int c1 = min(nchunks, c0 + g);
+    const char* qrow = zq + s.q_off * EB;
+    const char* prow = zp + s.p_off * EB;
 
     // --- totals ---
-    double rho = 0.0, M = 0.0, Wtot = 0.0, resid_mass = 0.0;
+    double rho = 0.0, M = 0.0, resid_mass = 0.0;
     int mode = s.mode;
     if (mode == kModeResidual) {
         double sq = 0.0, sp = 0.0;
         for (int c = c0; c < c1; ++c) {
-            sq += P[c].x;
-            sp += P[c].y;
+            sq += P[c].sa;
+            sp += P[c].sb;
         }
         sq = block_sum(sq, red);
         sp = block_sum(sp, red);
         rho = sq / sp;
-        double w = 0.0;
-        for (int c = c0; c < c1; ++c) w += P[c].z - rho * P[c].w;
-        Wtot = block_sum(w, red);
+        // near-threshold tokens: exact when they share one zq - zp (one ratio
+        // q/p), else the chunk is rescanned below with the exact rho
+        for (int c = tid; c < nchunks; c += kBlock) {
+            const ChunkSums p = P[c];
+            s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
+            float xq[kPerThread], xp[kPerThread];
+            load_chunk16<DT>(qrow, V, c, tid, xq);
+            load_chunk16<DT>(prow, V, c, tid, xp);
+            double w = 0.0;
+            for (int j = 0; j < kPerThread; ++j) {
+                const float d = xq[j] - xp[j];
+                if (d >= s.thr_lo && !(d > s.thr_hi)) w += residual_weight(xq[j], xp[j], s, invT, rho);
+            }
+            w = block_sum(w, red);
+            if (tid == 0) s_near[c] = w;
+            __syncthreads();
+        }
+        double wsum = 0.0;
+        for (int c = c0; c < c1; ++c) wsum += (P[c].pa - rho * P[c].pb) + s_near[c];
+        const double Wtot = block_sum(wsum, red);
         if (!(Wtot > 0.0)) {
-            mode = 2;  // the residual is empty: sample from q itself
-            Wtot = sq;
+            mode = kModeFallback;
             resid_mass = 0.0;
         } else {
             resid_mass = Wtot / sq;
@@ -567,18 +624,12 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
         float lm = -INFINITY;
         int bad = 0;
         for (int c = c0; c < c1; ++c) {
-            lm = fmaxf(lm, (float)P[c].x);
-            bad |= P[c].z != 0.0;
+            lm = fmaxf(lm, (float)P[c].sa);
+            bad |= P[c].pa != 0.0;
         }
         M = (double)block_max(lm, redf);
         bad = __syncthreads_or(bad);
-        double w = 0.0;
-        if (M != -INFINITY) {
-            for (int c = c0; c < c1; ++c)
-                if (P[c].x != -INFINITY) w += P[c].y * exp((P[c].x - M) * invT);
-        }
-        Wtot = block_sum(w, red);
-        if (bad || !(Wtot > 0.0) || !(Wtot < INFINITY)) {
+        if (bad || M == -INFINITY) {
             for (int i = tid; i < width; i += kBlock) {
                 out_tokens[(int64_t)b * width + i] = -1;
                 if (out_path) out_path[(int64_t)b * width + i] = -1;
@@ -587,22 +638,22 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
             return;
         }
     }
-    const double target = s.u * Wtot;
+    auto chunk_weight = [&](int c) -> double {
+        const ChunkSums& p = P[c];
+        if (mode == kModeResidual) return (p.pa - rho * p.pb) + s_near[c];
+        if (mode == kModeFallback) return p.sa;
+        return (p.sa == -INFINITY) ? 0.0 : p.sb * exp((p.sa - M) * invT);
+    };
 
-    // --- locate the chunk: first chunk whose running weight exceeds target ---
+    // --- locate the chunk: first chunk whose running weight exceeds u*W ---
     // The owner is the last thread whose group starts at or below the
     // threshold; it scans its group and, if rounding leaves the threshold past
     // its end, takes its last chunk of positive weight.
-    auto chunk_weight = [&](int c) -> double {
-        const double4 p = P[c];
-        if (mode == kModeResidual) return p.z - rho * p.w;
-        if (mode == 2) return p.x;
-        return (p.x == -INFINITY) ? 0.0 : p.y * exp((p.x - M) * invT);
-    };
     double gsum = 0.0;
     for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
-    double gtotal;
-    const double gbase = block_exclusive_scan(gsum, red, &gtotal);
+    double Wtot;
+    const double gbase = block_exclusive_scan(gsum, red, &Wtot);
+    const double target = s.u * Wtot;
     if (tid == 0) {
         s_owner = -1;
         s_chunk = 0;  // never left unset, even if no thread could claim
@@ -640,11 +691,11 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
 
     // --- rescan the chunk ---
     float xq[kPerThread], xp[kPerThread];
-    load_chunk16<DT>(zq + s.q_off * EB, V, cs, tid, xq);
-    if (mode == kModeResidual) load_chunk16<DT>(zp + s.p_off * EB, V, cs, tid, xp);
+    load_chunk16<DT>(qrow, V, cs, tid, xq);
+    if (mode == kModeResidual) load_chunk16<DT>(prow, V, cs, tid, xp);
     double scale = 1.0, mc = 0.0;
     if (mode == kModeBonus) {
-        mc = P[cs].x;
+        mc = P[cs].sa;
         scale = exp((mc - M) * invT);
     }
     double w[kPerThread];
@@ -652,15 +703,9 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
         double v;
-        if (mode == kModeResidual) {
-            v = (xq[j] - xp[j] > s.theta)
-                    ? exp(((double)xq[j] - (double)s.mq) * invT) - rho * exp(((double)xp[j] - (double)s.mp) * invT)
-                    : 0.0;
-        } else if (mode == 2) {
-            v = exp(((double)xq[j] - (double)s.mq) * invT);
-        } else {
-            v = exp(((double)xq[j] - mc) * invT);
-        }
+        if (mode == kModeResidual) v = residual_weight(xq[j], xp[j], s, invT, rho);
+        else if (mode == kModeFallback) v = exp(((double)xq[j] - (double)s.mq) * invT);
+        else v = exp(((double)xq[j] - mc) * invT);
         w[j] = v;
         tsum += v;
     }
@@ -737,16 +782,17 @@ Layout make_layout(int B, int rows_per_seq, int V)
     L.stats = 0;
     L.seq = align_up((size_t)B * rows_per_seq * sizeof(sv::RowStat));
     L.part = L.seq + align_up((size_t)B * sizeof(sv::SeqState));
-    L.total = L.part + align_up((size_t)B * nchunks_of(V) * sizeof(double4));
+    L.total = L.part + align_up((size_t)B * nchunks_of(V) * sizeof(sv::ChunkSums));
     return L;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Rows need only be element-aligned (strides are in elements); 16-byte
+// aligned rows take the all-vector path.
 int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
 {
-    if (!aligned16(base)) return SV_EALIGN;
-    if ((seq_stride * es) % 16 != 0 || (row_stride * es) % 16 != 0) return SV_EALIGN;
+    if (((uintptr_t)base % (uintptr_t)es) != 0) return SV_EALIGN;
     if (seq_stride < 0 || row_stride < 0) return SV_EINVAL;
     return SV_OK;
 }
@@ -769,7 +815,7 @@ const char* sv_status_string(int status)
         case SV_EINVAL: return "invalid argument";
         case SV_EDTYPE: return "unsupported dtype";
         case SV_ESHAPE: return "unsupported shape";
-        case SV_EALIGN: return "logit or KV rows not 16-byte aligned";
+        case SV_EALIGN: return "logits not element-aligned or KV rows not 16-byte aligned";
         case SV_EWORKSPACE: return "workspace missing or too small";
         case SV_EHIP: return "HIP launch failed";
         default: return "unknown status";
@@ -778,13 +824,13 @@ const char* sv_status_string(int status)
 
 size_t sv_chain_workspace_bytes(int B, int N, int V)
 {
-    if (B < 0 || N < 0 || N > 64 || V < 1) return 0;
+    if (B < 0 || N < 0 || N > 64 || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
     return make_layout(B, 2 * N, V).total;
 }
 
 size_t sv_tree_workspace_bytes(int B, int T, int V)
 {
-    if (B < 0 || T < 0 || T + 1 > sv::kMaxNodes || V < 1) return 0;
+    if (B < 0 || T < 0 || T + 1 > sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
     return make_layout(B, 2 * (T + 1), V).total;
 }
 
@@ -797,7 +843,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
 {
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
     if (B < 0 || N < 0 || V < 1 || !(temperature > 0.0f) || !(temperature < INFINITY)) return SV_EINVAL;
-    if (N > 64) return SV_ESHAPE;
+    if (N > 64 || V > sv::kMaxChunks * sv::kChunk) return SV_ESHAPE;
     if (B == 0) return SV_OK;
     if (!target_logits || !out_tokens || !out_num_accepted) return SV_EINVAL;
     if (N > 0 && (!draft_logits || !draft_tokens)) return SV_EINVAL;
@@ -812,7 +858,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     char* ws = static_cast<char*>(workspace);
     sv::RowStat* stats = reinterpret_cast<sv::RowStat*>(ws + L.stats);
     sv::SeqState* seq = reinterpret_cast<sv::SeqState*>(ws + L.seq);
-    double4* part = reinterpret_cast<double4*>(ws + L.part);
+    sv::ChunkSums* part = reinterpret_cast<sv::ChunkSums*>(ws + L.part);
     const char* zq = static_cast<const char*>(target_logits);
     const char* zp = static_cast<const char*>(draft_logits ? draft_logits : target_logits);
     const double invT = 1.0 / (double)temperature;
@@ -867,7 +913,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
     if (B < 0 || T < 0 || V < 1 || max_depth < 0 || !(temperature > 0.0f) || !(temperature < INFINITY))
         return SV_EINVAL;
-    if (T + 1 > sv::kMaxNodes || max_depth > T) return SV_ESHAPE;
+    if (T + 1 > sv::kMaxNodes || max_depth > T || V > sv::kMaxChunks * sv::kChunk) return SV_ESHAPE;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_logits || !node_tokens || !parents || !out_tokens || !out_path_nodes ||
         !out_num_accepted)
@@ -884,7 +930,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     char* ws = static_cast<char*>(workspace);
     sv::RowStat* stats = reinterpret_cast<sv::RowStat*>(ws + L.stats);
     sv::SeqState* seq = reinterpret_cast<sv::SeqState*>(ws + L.seq);
-    double4* part = reinterpret_cast<double4*>(ws + L.part);
+    sv::ChunkSums* part = reinterpret_cast<sv::ChunkSums*>(ws + L.part);
     const char* zq = static_cast<const char*>(target_logits);
     const char* zp = static_cast<const char*>(draft_logits);
     const double invT = 1.0 / (double)temperature;

@@ -133,13 +133,31 @@ struct __align__(16) SeqState {
     double u;         // sampling uniform
     float mq;         // pass-1 references of the q / p rows (residual only)
     float mp;
-    float theta;      // q_t > p_t  <=>  zq_t - zp_t > theta (from pass-1 stats)
+    // q_t > p_t  <=>  zq_t - zp_t > theta, theta from the pass-1 statistics.
+    // Tokens with zq - zp above thr_hi certainly have q > p, below thr_lo
+    // certainly q < p; the band between is resolved exactly by the sampler.
+    float thr_lo;
+    float thr_hi;
     int k;            // accepted count (= slot of the sampled token)
     int status;       // 0 ok, 1 data error
     int mode;         // 0 residual, 1 bonus
-    int pad[4];
+    int pad[3];
 };
-static_assert(sizeof(SeqState) == 64 + 16, "SeqState layout");
+static_assert(sizeof(SeqState) == 80, "SeqState layout");
+
+// Per-chunk sums of the sampled row(s).  Residual: sa = sum a, sb = sum b
+// (a = exp((zq - mq)/T), b = exp((zp - mp)/T)); pa, pb = the same over the
+// tokens certainly in {q > p}; na, nb = over the near-threshold tokens, whose
+// smallest and largest zq - zp are dmin, dmax.  Bonus: sa = chunk maximum of
+// z, sb = sum exp((z - sa)/T), pa = 1 if the chunk holds NaN or +inf.
+struct __align__(16) ChunkSums {
+    double sa, sb, pa, pb, na, nb;
+    float dmin, dmax;
+    double pad;
+};
+static_assert(sizeof(ChunkSums) == 64, "ChunkSums layout");
+
+constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk
 
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;

@@ -112,7 +112,7 @@ def verifier_logits(w: Workload, rows: int, g: torch.Generator, device) -> torch
     z = torch.randn((rows, w.V), generator=g, device=device, dtype=torch.float32) * w.sigma_q
     if w.prior == "peaks":
         scores = torch.rand((rows, w.V), generator=g, device=device)
-        ids = torch.topk(scores, w.peaks, dim=1).indices  # distinct random ids per row
+        ids = torch.topk(scores, min(w.peaks, w.V), dim=1).indices  # distinct random ids per row
         z.scatter_add_(1, ids, torch.full(ids.shape, w.peak_boost, device=device))
     elif w.prior == "zipf":
         z += _zipf_prior(w, device)

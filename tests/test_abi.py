@@ -75,9 +75,9 @@ def test_chain_argument_errors(sv):
     assert _chain(L, V=0) == 1 and _chain(L, B=-1) == 1 and _chain(L, N=-1) == 1
     assert _chain(L, tok=None) == 1 and _chain(L, num=None) == 1 and _chain(L, tq=None) == 1
     assert _chain(L, tp=None) == 1 and _chain(L, d=None) == 1
-    assert _chain(L, tq=FAKE + 4) == 4               # SV_EALIGN
-    assert _chain(L, qr=33) == 4 and _chain(L, ps=8 * 32 + 2) == 4
-    assert _chain(L, dt=1, qr=4) == 4                # 4 bf16 = 8 bytes per row step
+    assert _chain(L, tq=FAKE + 2) == 4               # SV_EALIGN: fp32 logits at a 2-byte offset
+    assert _chain(L, dt=1, tp=FAKE + 1) == 4         # bf16 logits at an odd address
+    assert _chain(L, qr=-32) == 1                    # negative stride
     assert _chain(L, wsb=16) == 5 and _chain(L, ws=None) == 5   # SV_EWORKSPACE
     assert _chain(L, B=0) == 0                       # empty batch: nothing to do
 

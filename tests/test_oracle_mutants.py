@@ -54,7 +54,7 @@ def _battery():
     yield lambda: P.test_n0_is_plain_categorical_sampling(oracle)
     yield lambda: P.test_theorem_on_oracle_primitives(oracle, 5, 2)
     yield lambda: P.test_accept_rule_edges(oracle)
-    for V, N, T in [(5, 2, 1.0), (5, 2, 0.7)]:
+    for V, N, T in [(5, 2, 1.0), (5, 2, 0.75)]:
         yield lambda V=V, N=N, T=T: P.test_chain_structure_under_forced_uniforms(oracle, V, N, T)
     yield lambda: P.test_chain_uses_documented_uniforms(oracle)
     yield lambda: P.test_residual_of_equal_rows_falls_back_to_q(oracle)

@@ -115,7 +115,7 @@ def test_n0_is_plain_categorical_sampling(orc):
     """With no drafts the step samples q_1 by inverse CDF: identical to
     np.searchsorted(cumsum(q), u * sum(q), 'right') on the same uniform."""
     rng = np.random.default_rng(5)
-    B, V, T = 300, 1000, 0.8
+    B, V, T = 300, 1000, 0.8125  # exactly representable in fp32, as the ABI passes T
     zq = rng.normal(0, 3, size=(B, 1, V))
     zp = np.zeros((B, 0, V))
     out = orc.verify_chain(zq, zp, np.zeros((B, 0), np.int32), seed=9, rnd=4, T=T)
@@ -180,7 +180,7 @@ def test_accept_rule_edges(orc):
     assert np.isinf(out["ratio"][3, 0])  # p(d) = 0
 
 
-@pytest.mark.parametrize("V,N,T", [(4, 1, 1.0), (5, 2, 1.0), (8, 2, 1.0), (5, 2, 0.7), (6, 1, 1.6)])
+@pytest.mark.parametrize("V,N,T", [(4, 1, 1.0), (5, 2, 1.0), (8, 2, 1.0), (5, 2, 0.75), (6, 1, 1.625)])
 def test_chain_structure_under_forced_uniforms(orc, V, N, T):
     """For every draft vector and every forced accept/reject pattern, the
     chain keeps d_1..d_k up to the first rejection k+1, then emits one token
