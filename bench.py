@@ -9,8 +9,8 @@ and uses a fresh Philox round per step.
 
 Timing: W untimed warm-up steps, then K steps bracketed by a device
 synchronize and HIP events on the stream the library launches on.  The
-dominant kernel (row statistics) is timed by events the library records
-around it in every timed step.
+dominant kernel (the one verify launch: row statistics, accept, sampling) is
+timed by events the library records around it in every timed step.
 
 Output: one JSON line (see the keys below); also the oracle timed on this
 host's cores on a bounded sample (cpu_baseline).
@@ -32,7 +32,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k_stats_chain_c3_pmc.json")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_verify_chain_c3_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
                   for f in ("specverify.hip", "sv_device.h")]
 
@@ -76,9 +76,9 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(stats_launch_bytes: int):
-    """HBM bytes per launch of the row-statistics kernel from the committed
-    rocprofv3 PMC summary, if it was taken on the current kernel source."""
+def load_traffic():
+    """HBM bytes per launch of the verify kernel from the committed rocprofv3
+    PMC summary, if it was taken on the current kernel source."""
     try:
         with open(PROFILE_PMC) as f:
             p = json.load(f)
@@ -103,21 +103,17 @@ def build_pool(w, pool: int, device: str):
     return sets
 
 
-def algorithmic_bytes(w, s) -> tuple:
-    """(bytes of every logit row the step can need, bytes the row-statistics
-    kernel reads) for one step on logit set s."""
+def algorithmic_bytes(w, s) -> int:
+    """Bytes of every logit row one step can need, each read once (chain:
+    B*(2N+1)*V*s; tree: q at every node plus p at every internal node)."""
+    import numpy as np
+
     import synth
     if w.kind == "chain":
-        full = synth.algorithmic_bytes_chain(w.B, w.N, w.V, w.elem_bytes)
-        stats = w.B * 2 * w.N * w.V * w.elem_bytes
-        return full, stats
+        return synth.algorithmic_bytes_chain(w.B, w.N, w.V, w.elem_bytes)
     par = s["parents"].cpu().numpy()
-    full = synth.algorithmic_bytes_tree(par if par.ndim == 2 else par[None].repeat(w.B, 0), w.V, w.elem_bytes)
-    import numpy as np
     p2 = par if par.ndim == 2 else np.repeat(par[None], w.B, 0)
-    internal = sum(len(set(int(x) for x in row[1:])) for row in p2)
-    stats = 2 * internal * w.V * w.elem_bytes
-    return full, stats
+    return synth.algorithmic_bytes_tree(p2, w.V, w.elem_bytes)
 
 
 def cpu_baseline(w, sets, budget_s: float):
@@ -132,8 +128,8 @@ def cpu_baseline(w, sets, budget_s: float):
     zq, zp = synth.to_oracle(s["zq"]), synth.to_oracle(s["zp"])
     done_seq, t_total, reps = 0, 0.0, 0
     B = w.B
-    chunk = min(B, max(threads, 8))
-    while t_total < budget_s and reps < 64:
+    chunk = min(B, max(2 * threads, 8))
+    while t_total < budget_s:
         lo = (reps * chunk) % B
         hi = min(B, lo + chunk)
         t0 = time.perf_counter()
@@ -199,12 +195,12 @@ def main():
     B = w.B
     if w.kind == "chain":
         outs = sv.alloc_chain_outputs(B, w.N, dev)
-        ws = torch.empty(sv.chain_workspace_bytes(B, w.N, w.V), dtype=torch.uint8, device=dev)
+        ws = sv.alloc_workspace(sv.chain_workspace_bytes(B, w.N, w.V), dev)
         width = w.N + 1
     else:
         T = sets[0]["zq"].shape[1] - 1
         outs = sv.alloc_tree_outputs(B, T, w.depth, dev)
-        ws = torch.empty(sv.tree_workspace_bytes(B, T, w.V), dtype=torch.uint8, device=dev)
+        ws = sv.alloc_workspace(sv.tree_workspace_bytes(B, T, w.V), dev)
         width = w.depth + 1
     kv_out = {"src_rows": torch.empty((B, width), dtype=torch.int32, device=dev),
               "kv_len": torch.empty(B, dtype=torch.int32, device=dev)}
@@ -246,16 +242,13 @@ def main():
     stats_ms = [hip.elapsed_ms(a, b) for a, b in ev]
     ms_step = total_ms / K
     k_mean = sum(stats_ms) / K
-    full_bytes, stats_bytes = algorithmic_bytes(w, sets[0])
-    if w.kind != "chain":
-        per = [algorithmic_bytes(w, s) for s in sets]
-        full_bytes = sum(p[0] for p in per) / len(per)
-        stats_bytes = sum(p[1] for p in per) / len(per)
+    per_set = [algorithmic_bytes(w, s) for s in sets]
+    full_bytes = sum(per_set) / len(per_set)
     rounds_per_s = 1000.0 / ms_step
     eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
-    k_gbps = stats_bytes / (k_mean * 1e-3) / 1e9
+    k_gbps = full_bytes / (k_mean * 1e-3) / 1e9
     acc = outs["num_accepted"].float()
-    traffic, pmc = load_traffic(int(stats_bytes)) if w.name == "c3" else (None, None)
+    traffic, pmc = load_traffic() if w.name == "c3" else (None, None)
     result = {
         "metric": "verified rounds/s + achieved HBM GB/s (% peak), B=256 N=7 V=128256",
         "value": round(rounds_per_s, 2),
@@ -282,7 +275,7 @@ def main():
         "algorithmic_bytes_per_step": int(full_bytes),
         "mean_accepted": round(float(acc[acc >= 0].mean()), 4),
         "roofline": {
-            "kernel": "k_stats_chain (row statistics)" if w.kind == "chain" else "k_stats_tree (row statistics)",
+            "kernel": "k_verify (fused row statistics, accept, sampling)",
             "bound": "hbm",
             "achieved": round(k_gbps, 1),
             "peak": PEAK_HBM_GBPS,
@@ -290,7 +283,7 @@ def main():
             "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "kernel_ms": round(k_mean, 5),
-            "algorithmic_bytes_per_launch": int(stats_bytes),
+            "algorithmic_bytes_per_launch": int(full_bytes),
         },
         "wall_s_timed": round(wall, 3),
     }

@@ -35,8 +35,16 @@
  *     the block at position n; the sampling uniform of slot s is the one of
  *     words 2,3 of the block at position s.  A call is a pure function of its
  *     inputs and (seed, round).
- *   - Reentrant; no global mutable state; calls on different streams may
- *     overlap as long as they use different workspaces and outputs.
+ *   - Reentrant; calls on different streams may overlap as long as they use
+ *     different workspaces and outputs.  The only process-wide state is a
+ *     call counter (an atomic) that tags each call's results, and cached
+ *     occupancy figures.
+ *   - Each verify call is two kernel launches: row statistics, then accept
+ *     and sampling.  For chains the row-statistics work is split into equal
+ *     ranges, one per wave the device holds at once, so the summation order
+ *     of a row's statistics (and with it the last bits of q(d), p(d)) depends
+ *     on B, N, V and the device's compute-unit count; decisions and tokens
+ *     differ only where a uniform falls within rounding of a threshold.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -63,8 +71,9 @@ enum sv_status {
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
 /* Optional timing hook: when non-NULL, `stats_begin` and `stats_end` are
- * recorded on `stream` right before and right after the row-statistics
- * kernel (the pass that streams the logit rows), so a caller can time it. */
+ * recorded on `stream` right before and right after the verify kernel (the
+ * one launch that streams the logit rows and samples), so a caller can time
+ * it. */
 typedef struct sv_timing {
     hipEvent_t stats_begin;
     hipEvent_t stats_end;
@@ -111,8 +120,10 @@ size_t sv_tree_workspace_bytes(int B, int T, int V);
  * Sampling is an inverse CDF in token-id order: the first token whose
  * running weight exceeds u*W, W the total weight, accumulated in double.
  * workspace: device memory of at least sv_chain_workspace_bytes(B, N, V)
- * bytes (no alignment beyond 256 bytes needed; contents need not be
- * initialised).
+ * bytes, 16-byte aligned, ZERO-FILLED before its first use.  It holds
+ * per-call records and counters tagged with the call, so after that single
+ * zero fill it is reused as is (with any B, N, V that fit).  Calls that
+ * overlap in time must use different workspaces.
  */
 int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
                       const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
@@ -154,6 +165,8 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  *   out_probs         [B, T+1, 2] float: (q_par(tok_n), p_par(tok_n)), node 0
  *                     (0, 0).
  *   out_residual_mass [B] double, as for chains.
+ * workspace: at least sv_tree_workspace_bytes(B, T, V) bytes, zero-filled
+ * before first use, as for chains.
  */
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
                      const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,

@@ -121,12 +121,19 @@ def tree_workspace_bytes(B: int, T: int, V: int) -> int:
     return int(_lib().sv_tree_workspace_bytes(B, T, V))
 
 
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled workspace (the library's counters start at zero and
+    every call leaves them zero, so one workspace serves any number of
+    calls)."""
+    return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
 def _workspace(nbytes: int, device, workspace):
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError("workspace too small")
         return workspace
-    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    return alloc_workspace(nbytes, device)
 
 
 def alloc_chain_outputs(B: int, N: int, device):
@@ -258,5 +265,5 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
 
 
 __all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "sv_philox_uniforms",
-           "chain_workspace_bytes", "tree_workspace_bytes", "alloc_chain_outputs", "alloc_tree_outputs",
+           "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",
            "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16"]

@@ -1,4 +1,4 @@
-// specverify.hip -- gfx950 kernels and C ABI of the verify-and-accept step
+// specverify.hip -- gfx950 kernel and C ABI of the verify-and-accept step
 // (Leviathan rejection sampling over chains and flattened draft trees).
 //
 // Pages followed (title and section):
@@ -10,28 +10,43 @@
 //        section 3 (flattened tree, one verifier pass) and section 4
 //        ("eagle_round" step 4, the walk from the root).
 //
-// One call is four kernels on the caller's stream:
-//   1. row statistics: every q/p row the accept tests read is streamed once
-//      (16-byte loads, 4 in flight per thread); per row (m, s) with
-//      s = sum exp((z - m)/T) from the hardware exp2 in fp32, summed in
-//      pairs of 32 and accumulated in double.  This is the HBM-bound pass.
-//   2. accept: one wave64 per chain (lane i = position i+1; ballot + ffs
-//      finds the first rejection) or one block per tree (every node tested
-//      in parallel, then a wave walks the parent array with ballots).  The
-//      ratio q(d)/p(d) is formed in double from the row statistics.
-//   3. sampling partials: the one or two rows the sample needs are split in
-//      4096-element chunks; each block evaluates its chunk in double (exp of
-//      (z - m)/T per element) and writes chunk sums.
-//   4. sampling final: one block per sequence combines the chunk sums, finds
-//      the chunk holding u*W, rescans it with a block-wide prefix scan and
-//      writes the token (inverse CDF in token order).
-// The residual avoids a third sweep: with pass-1 statistics it decides which
-// tokens have q > p (a log-domain comparison), accumulates sum a_t, sum b_t
-// and the same two sums over that set in double, and forms
-// W = sum_{q>p} a_t - (Sq/Sp) sum_{q>p} b_t once the exact Sq, Sp are known.
+// One call is two kernel launches on the caller's stream.
+//   * Row kernel, one block per (sequence b, row, segment) of every q/p logit
+//     row that an accept test reads: it streams the segment (16-byte loads,
+//     eight per thread per batch, the next batch issued before the current
+//     one is used) and stores (m, s), s = sum exp((z - m)/T) from the
+//     hardware exp2 in fp32, summed in groups of 32 and accumulated in
+//     double.  This is the HBM-bound part.  The last of b's blocks to finish
+//     (an arrival counter per sequence) runs b's accept step: one wave64 for
+//     a chain (lane i = position i+1, ratio q(d)/p(d) in double, ballot + ffs
+//     for the first rejection) or the whole block for a tree (every node
+//     tested in parallel, then a wave walks the parent array with ballots).
+//     For bf16 logits a few extra blocks fill a table of exp(z/T) for every
+//     bf16 bit pattern.
+//   * Sample kernel, one block per (b, 4096-token chunk) of the row(s) b
+//     samples from: chunk sums in double (exp from the table, or a
+//     table-driven fp64 routine for fp32 logits).  The last of b's blocks to
+//     finish runs the final step: it combines the chunk sums, finds the chunk
+//     holding u*W, rescans it with a block-wide prefix scan and writes the
+//     token (inverse CDF in token order).
+// Blocks of one kernel exchange data through self-validating records
+// (sv_device.h): no cache-wide fences and no waits on blocks that have not
+// started; the row kernel's results reach the sample kernel across the
+// kernel boundary.
+//
+// The residual avoids an extra sweep: with pass-1 statistics it decides
+// which tokens certainly have q > p or q < p (a log-domain comparison with a
+// margin), accumulates sum a_t, sum b_t, the same two sums over the certain
+// q > p set and over the near-threshold band in double, and forms
+// W = sum_{q>p} (a_t - rho b_t) + band, rho = Sq/Sp, once the exact Sq, Sp
+// are known.  The band is exact: its tokens share one zq - zp (one ratio
+// q/p) or their chunk is rescanned with the exact rho.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
+
+#include <atomic>
 
 #include "sv_device.h"
 #include "specverify.h"
@@ -39,7 +54,7 @@
 namespace sv {
 
 // ===========================================================================
-// 1. Row statistics
+// Pass 1: row statistics
 // ===========================================================================
 template <int K>
 __device__ __forceinline__ void accumulate_values(const float* x, float c, double cd, float& ref, double& acc)
@@ -76,42 +91,99 @@ __device__ __forceinline__ void combine_stat(float& m, double& s, float m2, doub
     m = M;
 }
 
-// (m, s) of one row, valid in thread 0.
+// One batch of U 16-byte vectors per thread (vectors past the end carry
+// -inf): the reference moves first if the batch's maximum calls for it, then
+// the terms are summed in fp32 groups of (at most) 32 and added to the
+// double accumulator.
 template <int DT, int U>
-__device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row, int V, float c, double cd)
+__device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, double cd, float& ref, double& acc)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int GE = (U * EPV < 32) ? U * EPV : 32;  // elements per fp32 group
+    constexpr int G = GE / EPV;                          // vectors per group
+    static_assert(U % G == 0, "batch must hold whole groups");
+    float lm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float x[EPV];
+        decode16<DT>(raw[u], x);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
+    }
+    if ((lm - ref) * c > 1.0f) {
+        acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
+        ref = lm;
+    }
+    const float r = (ref == -INFINITY) ? 0.0f : ref;
+#pragma unroll
+    for (int g = 0; g < U / G; ++g) {
+        float e[GE];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            float x[EPV];
+            decode16<DT>(raw[g * G + u], x);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f((x[i] - r) * c);
+        }
+#pragma unroll
+        for (int w = 1; w < GE; w <<= 1) {
+#pragma unroll
+            for (int i = 0; i + w < GE; i += 2 * w) e[i] += e[i + w];
+        }
+        acc += (double)e[0];
+    }
+}
+
+// A 16-byte vector of -inf logits (pads the last batch of a row).
+template <int DT>
+__device__ __forceinline__ uint4 neg_inf16()
+{
+    const uint32_t w = (DT == DT_BF16) ? 0xff80ff80u : 0xff800000u;
+    return make_uint4(w, w, w, w);
+}
+
+// (m, s) of n consecutive elements starting at `row`, valid in thread 0.
+// Rows need only be element-aligned: the elements before the first 16-byte
+// boundary are read one by one, the rest as 16-byte vectors in batches of U
+// per thread, the next batch's loads issued before the current batch is used
+// (the last batch is padded with -inf, so every batch is a full set of
+// loads in flight).
+template <int DT, int U>
+__device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row, int n, float c, double cd)
 {
     constexpr int EB = elem_bytes<DT>();
     constexpr int EPV = 16 / EB;
     float ref = -INFINITY;
     double acc = 0.0;
-    // elements before the first 16-byte boundary (rows need only be
-    // element-aligned); the rest of the row streams as 16-byte vectors
     int head = (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
-    head = head < V ? head : V;
+    head = head < n ? head : n;
     if ((int)threadIdx.x < head) {
         float x[1] = {load_logit<DT>(row, threadIdx.x)};
         accumulate_values<1>(x, c, cd, ref, acc);
     }
     row += head * EB;
-    V -= head;
-    const int nvec = V / EPV;
+    n -= head;
+    const int nvec = n / EPV;
     const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
+    const int nbatch = (nvec + U * kBlock - 1) / (U * kBlock);
     int v = threadIdx.x;
-    for (; v + (U - 1) * kBlock < nvec; v += U * kBlock) {
-        uint4 raw[U];
+    uint4 cur[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = vrow[v + u * kBlock];
-        float x[U * EPV];
+    for (int u = 0; u < U; ++u) cur[u] = (v + u * kBlock < nvec) ? stream_load16(vrow + v + u * kBlock) : neg_inf16<DT>();
+    for (int bt = 0; bt < nbatch; ++bt) {
+        const int nv = v + U * kBlock;
+        uint4 nxt[U];
+        if (bt + 1 < nbatch) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) decode16<DT>(raw[u], x + u * EPV);
-        accumulate_values<U * EPV>(x, c, cd, ref, acc);
+            for (int u = 0; u < U; ++u)
+                nxt[u] = (nv + u * kBlock < nvec) ? stream_load16(vrow + nv + u * kBlock) : neg_inf16<DT>();
+        }
+        accumulate_batch<DT, U>(cur, c, cd, ref, acc);
+        v = nv;
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
-    for (; v < nvec; v += kBlock) {
-        float x[EPV];
-        decode16<DT>(vrow[v], x);
-        accumulate_values<EPV>(x, c, cd, ref, acc);
-    }
-    const int tail = V - nvec * EPV;
+    const int tail = n - nvec * EPV;
     if ((int)threadIdx.x < tail) {
         float x[1] = {load_logit<DT>(row, (int64_t)nvec * EPV + threadIdx.x)};
         accumulate_values<1>(x, c, cd, ref, acc);
@@ -125,6 +197,7 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     __shared__ float red_m[kWaves];
     __shared__ double red_s[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
     if (lane == 0) {
         red_m[wave] = ref;
         red_s[wave] = acc;
@@ -133,7 +206,6 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     RowStat st;
     st.m = red_m[0];
     st.s = red_s[0];
-    st.pad = 0;
     if (threadIdx.x == 0) {
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) combine_stat(st.m, st.s, red_m[w], red_s[w], cd);
@@ -141,52 +213,215 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     return st;
 }
 
-// Chain: block r covers row j = r % (2N) of sequence b = r / (2N): q row j
-// for j < N, else p row j - N.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_stats_chain(const char* __restrict__ zq, int64_t qs, int64_t qr,
-                                                        const char* __restrict__ zp, int64_t ps, int64_t pr, int N,
-                                                        int V, float c, double cd, RowStat* __restrict__ stats)
-{
-    constexpr int EB = elem_bytes<DT>();
-    const int row = blockIdx.x;
-    const int b = row / (2 * N);
-    const int j = row - b * 2 * N;
-    const char* base = (j < N) ? zq + ((int64_t)b * qs + (int64_t)j * qr) * EB
-                               : zp + ((int64_t)b * ps + (int64_t)(j - N) * pr) * EB;
-    const RowStat st = block_row_stats<DT, 4>(base, V, c, cd);
-    if (threadIdx.x == 0) stats[row] = st;
-}
-
-// Tree: block r covers node n of sequence b, q (which 0) or p (which 1);
-// nodes without children are skipped (their rows are never tested against).
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_stats_tree(const char* __restrict__ zq, int64_t qs, int64_t qr,
-                                                       const char* __restrict__ zp, int64_t ps, int64_t pr,
-                                                       const int32_t* __restrict__ parents, int parents_shared,
-                                                       int nn, int V, float c, double cd,
-                                                       RowStat* __restrict__ stats)
-{
-    constexpr int EB = elem_bytes<DT>();
-    const int row = blockIdx.x;  // (b * nn + n) * 2 + which
-    const int which = row & 1;
-    const int bn = row >> 1;
-    const int b = bn / nn;
-    const int n = bn - b * nn;
-    const int32_t* par = parents_shared ? parents : parents + (int64_t)b * nn;
-    int found = 0;
-    for (int m = n + 1 + (int)threadIdx.x; m < nn; m += kBlock) found |= (par[m] == n);
-    if (!__syncthreads_or(found)) return;
-    const char* base = which == 0 ? zq + ((int64_t)b * qs + (int64_t)n * qr) * EB
-                                  : zp + ((int64_t)b * ps + (int64_t)n * pr) * EB;
-    const RowStat st = block_row_stats<DT, 4>(base, V, c, cd);
-    if (threadIdx.x == 0) stats[row] = st;
-}
-
 __device__ __forceinline__ bool stat_bad(const RowStat& r) { return !(r.s > 0.0 && r.s < INFINITY); }
 
+
 // ===========================================================================
-// 2. Accept
+// Parameters of one call
+// ===========================================================================
+struct VerifyParams {
+    const char* zq;
+    const char* zp;
+    int64_t qs, qr, ps, pr;   // sequence / row strides (elements)
+    const int32_t* tokens;    // chain: draft tokens [B, N]; tree: node tokens [B, T+1]
+    const int32_t* parents;   // tree only
+    int parents_shared;
+    int B, V, N, nn;          // chain: N drafts, nn = N+1; tree: nn = T+1 nodes, N unused
+    int max_depth, width;     // output row width (chain N+1, tree max_depth+1)
+    int rows;                 // pass-1 rows per sequence (chain 2N, tree 2 nn)
+    int segs, seg_len;        // segments per row, elements per segment
+    int r_items, nch;         // row blocks per sequence (trees), sample chunks per sequence
+    int cpb, groups;          // sample chunks per block, sample blocks per sequence
+    // chains: pass-1 rows flattened (row-major, V elements each) and cut into
+    // W equal wave ranges at multiples of 64 elements
+    int64_t E, E64;           // elements, ceil(E / 64)
+    int W, MP;                // waves, record slots per row
+    uint64_t seed, round;
+    float T, c;               // temperature, log2(e)/T
+    double cd, invT;
+    uint32_t epoch;
+    // workspace
+    uint64_t* chunk_arrivals; // [B] epoch-tagged arrival counters of the sample blocks
+    char* stats;              // [B * rows][MP] RowStat records (row kernel -> sample kernel)
+    char* part;               // [B][nch] ChunkSums records
+    uint32_t stats_bytes, part_bytes;
+    double* table;            // [65536] exp(z/T) per bf16 bit pattern, or null
+    // outputs
+    int32_t* out_tokens;
+    int32_t* out_path;
+    int32_t* out_num;
+    int8_t* out_acc;
+    float* out_probs;
+    double* out_resid;
+};
+
+// ~0.5 s of polling; never reached (every record waited for is stored by a
+// block that has already finished its part)
+constexpr int kSpinLimit = 1 << 19;
+
+// Poll a record until it is this call's and whole; false on timeout.
+template <int K>
+__device__ __forceinline__ bool wait_record(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4* a, uint32_t epoch)
+{
+    int spins = 0;
+    while (!try_record<K>(r, off, a, epoch)) {
+        if (++spins > kSpinLimit) return false;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return true;
+}
+
+// Block-wide: wait for n consecutive K-atom records starting at byte `off`;
+// true if all arrived.
+template <int K>
+__device__ __forceinline__ bool wait_records(__amdgpu_buffer_rsrc_t r, uint32_t off, int n, uint32_t epoch)
+{
+    int ok = 1;
+    for (int i = threadIdx.x; i < n; i += kBlock) {
+        u32x4 a[K];
+        ok &= wait_record<K>(r, off + 16u * K * (uint32_t)i, a, epoch) ? 1 : 0;
+    }
+    return __syncthreads_and(ok) != 0;
+}
+
+// Arrival index of the caller among this call's arrivals at a counter (0 for
+// the first).  A counter still carrying an earlier call's epoch is claimed
+// with a compare-exchange that installs this call's epoch; after that the
+// low word counts.
+__device__ __forceinline__ uint32_t arrive(uint64_t* ctr, uint32_t epoch)
+{
+    uint64_t cur = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while ((uint32_t)(cur >> 32) != epoch) {
+        const uint64_t want = ((uint64_t)epoch << 32) | 1u;
+        if (__hip_atomic_compare_exchange_strong(ctr, &cur, want, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+            return 0u;
+    }
+    return (uint32_t)__hip_atomic_fetch_add(ctr, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stats_rsrc(const VerifyParams& P)
+{
+    return make_rsrc(P.stats, P.stats_bytes);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const VerifyParams& P)
+{
+    return make_rsrc(P.part, P.part_bytes);
+}
+
+__device__ __forceinline__ uint32_t stat_off(const VerifyParams& P, int64_t grow, int slot)
+{
+    return (uint32_t)((grow * P.MP + slot) * kRowStatBytes);
+}
+
+// First element of wave w's range of the flattened pass-1 rows (chains).
+__device__ __forceinline__ int64_t wave_begin(const VerifyParams& P, int w)
+{
+    if (w >= P.W) return P.E;
+    const int64_t e = 64 * ((int64_t)w * P.E64 / P.W);
+    return e < P.E ? e : P.E;
+}
+
+// The wave whose range holds element e (the last wave starting at or before
+// e: empty ranges in between are skipped).
+__device__ __forceinline__ int wave_of(const VerifyParams& P, int64_t e)
+{
+    const int64_t k = e / 64;
+    const int64_t w = ((k + 1) * P.W + P.E64 - 1) / P.E64 - 1;
+    return (int)(w < P.W - 1 ? w : P.W - 1);
+}
+
+__device__ __forceinline__ uint32_t chunk_off(const VerifyParams& P, int b, int c)
+{
+    return (uint32_t)(((int64_t)b * P.nch + c) * kChunkSumsBytes);
+}
+
+__device__ __forceinline__ void put_chunk(const VerifyParams& P, int b, int c, const ChunkSums& v)
+{
+    u32x4 a[4];
+    pack(v, a);
+    put_record<4>(part_rsrc(P), chunk_off(P, b, c), a, P.epoch);
+}
+
+// A chunk record already known to be this call's.
+__device__ __forceinline__ ChunkSums get_chunk(const VerifyParams& P, int b, int c)
+{
+    const __amdgpu_buffer_rsrc_t r = part_rsrc(P);
+    u32x4 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = get_atom(r, chunk_off(P, b, c) + 16u * i);
+    return unpack_chunk(a);
+}
+
+// Statistics of pass-1 row `row` of sequence b from its records: for chains
+// the pieces that wave ranges cut it into, for trees its segments.  A record
+// that is not this call's (never expected) poisons the result.
+__device__ __forceinline__ RowStat load_row_stat(const VerifyParams& P, int b, int row)
+{
+    const __amdgpu_buffer_rsrc_t r = stats_rsrc(P);
+    const int64_t grow = (int64_t)b * P.rows + row;
+    int n = P.segs, w0 = 0;
+    if (P.W > 0) {
+        const int64_t e0 = grow * P.V, e1 = e0 + P.V;
+        w0 = wave_of(P, e0);
+        n = wave_of(P, e1 - 1) - w0 + 1;
+    }
+    RowStat acc{0.0, -INFINITY};
+    bool ok = true;
+    for (int i = 0; i < n; ++i) {
+        if (P.W > 0) {
+            // skip waves whose (empty) range holds none of the row
+            const int64_t lo = wave_begin(P, w0 + i), hi = wave_begin(P, w0 + i + 1);
+            if (hi <= lo) continue;
+        }
+        u32x4 a[1];
+        ok &= try_record<1>(r, stat_off(P, grow, i), a, P.epoch);
+        const RowStat x = unpack_rowstat(a);
+        combine_stat(acc.m, acc.s, x.m, x.s, P.cd);
+    }
+    if (!ok) acc.s = NAN;
+    return acc;
+}
+
+template <int DT>
+__device__ __forceinline__ const char* qrow_ptr(const VerifyParams& P, int b, int r)
+{
+    return P.zq + ((int64_t)b * P.qs + (int64_t)r * P.qr) * elem_bytes<DT>();
+}
+
+template <int DT>
+__device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, int r)
+{
+    return P.zp + ((int64_t)b * P.ps + (int64_t)r * P.pr) * elem_bytes<DT>();
+}
+
+// exp((z - m)/T) over the logits of one row.  For bf16 logits it is the
+// table entry of z's bit pattern, exp(z/T), times exp(-m/T), when |m/T| is
+// small enough that neither factor leaves the double range for the logits of
+// the row (z <= m + T ln 2); otherwise, and for fp32 logits, it is computed.
+struct ExpRow {
+    const double* tab;
+    double m, scale, invT;
+    __device__ __forceinline__ double operator()(float z) const
+    {
+        if (tab) return tab[__float_as_uint(z) >> 16] * scale;
+        return exp64(((double)z - m) * invT);
+    }
+};
+
+__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m)
+{
+    ExpRow e;
+    e.m = m;
+    e.invT = P.invT;
+    const double t = m * P.invT;
+    e.tab = (P.table && fabs(t) <= 600.0) ? P.table : nullptr;
+    e.scale = e.tab ? exp(-t) : 1.0;
+    return e;
+}
+
+// ===========================================================================
+// Accept
 // ===========================================================================
 struct AcceptOut {
     double lq, lp;  // log q(d), log p(d)
@@ -226,99 +461,76 @@ __device__ __forceinline__ void fill_residual_state(SeqState& s, const RowStat& 
     s.thr_hi = (float)(theta + margin);
 }
 
-// One wave64 per chain; lane i handles position i+1.
+// Chain accept of sequence b, run by wave 0 (lane i = position i+1): b's
+// state into `out` (LDS); with `outputs`, also the accept flags and
+// probabilities.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_accept_chain(
-    const char* __restrict__ zq, int64_t qs, int64_t qr, const char* __restrict__ zp, int64_t ps, int64_t pr,
-    const int32_t* __restrict__ d, int B, int N, int V, uint64_t seed, uint64_t round, double invT, float T,
-    const RowStat* __restrict__ stats, SeqState* __restrict__ st, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_num, int8_t* __restrict__ out_acc, float* __restrict__ out_probs)
+__device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool outputs)
 {
-    constexpr int EB = elem_bytes<DT>();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int b = blockIdx.x * kWaves + wave;
-    if (b >= B) return;  // whole wave
-    const int width = N + 1;
+    const int lane = threadIdx.x;
+    const int N = P.N;
     const bool active = lane < N;
     int err = 0, acc = 1;
     RowStat rq{}, rp{};
     if (active) {
-        const int tok = d[(int64_t)b * N + lane];
-        rq = stats[(int64_t)b * 2 * N + lane];
-        rp = stats[(int64_t)b * 2 * N + N + lane];
-        if (tok < 0 || tok >= V || stat_bad(rq) || stat_bad(rp)) {
+        const int tok = P.tokens[(int64_t)b * N + lane];
+        rq = load_row_stat(P, b, lane);
+        rp = load_row_stat(P, b, N + lane);
+        if (tok < 0 || tok >= P.V || stat_bad(rq) || stat_bad(rp)) {
             err = 1;
         } else {
-            const double u = accept_uniform(seed, round, (uint32_t)b, (uint32_t)(lane + 1));
-            const AcceptOut o = accept_one<DT>(zq + ((int64_t)b * qs + (int64_t)lane * qr) * EB,
-                                               zp + ((int64_t)b * ps + (int64_t)lane * pr) * EB, tok, rq, rp,
-                                               invT, u);
+            const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(lane + 1));
+            const AcceptOut o = accept_one<DT>(qrow_ptr<DT>(P, b, lane), prow_ptr<DT>(P, b, lane), tok, rq, rp,
+                                               P.invT, u);
             acc = o.accepted;
-            if (out_probs) {
-                out_probs[((int64_t)b * N + lane) * 2 + 0] = (float)exp(o.lq);
-                out_probs[((int64_t)b * N + lane) * 2 + 1] = (float)exp(o.lp);
+            if (outputs && P.out_probs) {
+                P.out_probs[((int64_t)b * N + lane) * 2 + 0] = (float)exp(o.lq);
+                P.out_probs[((int64_t)b * N + lane) * 2 + 1] = (float)exp(o.lp);
             }
         }
     }
     const uint64_t errmask = __ballot(err);
     const uint64_t rejmask = __ballot(active && !acc);
+    SeqState s{};
     if (errmask) {
-        for (int i = lane; i < width; i += 64) out_tokens[(int64_t)b * width + i] = -1;
-        if (lane == 0) {
-            out_num[b] = -1;
-            st[b].status = 1;
-        }
+        s.status = 1;
+        if (lane == 0) out = s;
         return;
     }
     const int k = rejmask ? (__ffsll((unsigned long long)rejmask) - 1) : N;
-    if (active && out_acc) out_acc[(int64_t)b * N + lane] = (int8_t)acc;
-    for (int i = lane; i < width; i += 64) out_tokens[(int64_t)b * width + i] = (i < k) ? d[(int64_t)b * N + i] : -1;
+    if (outputs && active && P.out_acc) P.out_acc[(int64_t)b * N + lane] = (int8_t)acc;
     // statistics of row k (residual) travel from lane k
     RowStat kq, kp;
-    kq.m = __shfl(rq.m, k < N ? k : 0, 64);
-    kq.s = __shfl(rq.s, k < N ? k : 0, 64);
-    kp.m = __shfl(rp.m, k < N ? k : 0, 64);
-    kp.s = __shfl(rp.s, k < N ? k : 0, 64);
-    if (lane == 0) {
-        out_num[b] = k;
-        SeqState s{};
-        s.k = k;
-        s.status = 0;
-        s.u = sample_uniform(seed, round, (uint32_t)b, (uint32_t)(k + 1));
-        s.q_off = (int64_t)b * qs + (int64_t)k * qr;
-        if (k < N) {
-            s.p_off = (int64_t)b * ps + (int64_t)k * pr;
-            fill_residual_state(s, kq, kp, T);
-        } else {
-            s.p_off = 0;
-            s.mode = kModeBonus;
-        }
-        st[b] = s;
-    }
+    const int src = k < N ? k : 0;
+    kq.m = __shfl(rq.m, src, 64);
+    kq.s = __shfl(rq.s, src, 64);
+    kp.m = __shfl(rp.m, src, 64);
+    kp.s = __shfl(rp.s, src, 64);
+    s.k = k;
+    s.node = k;
+    s.status = 0;
+    s.u = sample_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(k + 1));
+    if (k < N) fill_residual_state(s, kq, kp, P.T);
+    else s.mode = kModeBonus;
+    if (lane == 0) out = s;
 }
 
-// One block per tree: every node n >= 1 is tested against its parent's q/p
-// rows, then wave 0 walks from the root into the lowest-index accepted child.
 constexpr int kMaxNodes = 1024;
 
+// Tree accept of sequence b, run by the whole block: every node n >= 1 is
+// tested against its parent's q/p rows, then wave 0 walks from the root into
+// the lowest-index accepted child.  The state goes to `out` and the path to
+// `path` (both LDS); with `outputs`, also the accept flags and probabilities.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_accept_tree(
-    const char* __restrict__ zq, int64_t qs, int64_t qr, const char* __restrict__ zp, int64_t ps, int64_t pr,
-    const int32_t* __restrict__ node_tokens, const int32_t* __restrict__ parents, int parents_shared, int B, int T,
-    int V, int max_depth, uint64_t seed, uint64_t round, double invT, float temp, const RowStat* __restrict__ stats,
-    SeqState* __restrict__ st, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_path,
-    int32_t* __restrict__ out_num, int8_t* __restrict__ out_acc, float* __restrict__ out_probs)
+__device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t* path, bool outputs)
 {
-    constexpr int EB = elem_bytes<DT>();
-    const int b = blockIdx.x;
-    const int nn = T + 1;
-    const int width = max_depth + 1;
+    const int nn = P.nn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     __shared__ int s_par[kMaxNodes];
     __shared__ unsigned char s_acc[kMaxNodes];
     __shared__ unsigned char s_kids[kMaxNodes];
-    const int32_t* par = parents_shared ? parents : parents + (int64_t)b * nn;
-    const int32_t* tok = node_tokens + (int64_t)b * nn;
+    const int32_t* par = P.parents_shared ? P.parents : P.parents + (int64_t)b * nn;
+    const int32_t* tok = P.tokens + (int64_t)b * nn;
     for (int n = tid; n < nn; n += kBlock) {
         s_kids[n] = 0;
         s_acc[n] = 0;
@@ -332,51 +544,46 @@ __global__ __launch_bounds__(kBlock) void k_accept_tree(
             if (p < 0 || p >= n) err = 1;
             else s_kids[p] = 1;
             const int t = tok[n];
-            if (t < 0 || t >= V) err = 1;
+            if (t < 0 || t >= P.V) err = 1;
         }
     }
     err = __syncthreads_or(err);
     if (!err) {
         for (int n = 1 + tid; n < nn; n += kBlock) {
             const int p = s_par[n];
-            const RowStat rq = stats[((int64_t)b * nn + p) * 2 + 0];
-            const RowStat rp = stats[((int64_t)b * nn + p) * 2 + 1];
+            const RowStat rq = load_row_stat(P, b, 2 * p + 0);
+            const RowStat rp = load_row_stat(P, b, 2 * p + 1);
             if (stat_bad(rq) || stat_bad(rp)) {
                 err = 1;
                 continue;
             }
-            const double u = accept_uniform(seed, round, (uint32_t)b, (uint32_t)n);
-            const AcceptOut o = accept_one<DT>(zq + ((int64_t)b * qs + (int64_t)p * qr) * EB,
-                                               zp + ((int64_t)b * ps + (int64_t)p * pr) * EB, tok[n], rq, rp, invT,
-                                               u);
+            const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)n);
+            const AcceptOut o =
+                accept_one<DT>(qrow_ptr<DT>(P, b, p), prow_ptr<DT>(P, b, p), tok[n], rq, rp, P.invT, u);
             s_acc[n] = (unsigned char)o.accepted;
-            if (out_acc) out_acc[(int64_t)b * nn + n] = (int8_t)o.accepted;
-            if (out_probs) {
-                out_probs[((int64_t)b * nn + n) * 2 + 0] = (float)exp(o.lq);
-                out_probs[((int64_t)b * nn + n) * 2 + 1] = (float)exp(o.lp);
+            if (outputs && P.out_acc) P.out_acc[(int64_t)b * nn + n] = (int8_t)o.accepted;
+            if (outputs && P.out_probs) {
+                P.out_probs[((int64_t)b * nn + n) * 2 + 0] = (float)exp(o.lq);
+                P.out_probs[((int64_t)b * nn + n) * 2 + 1] = (float)exp(o.lp);
             }
         }
     }
     err = __syncthreads_or(err);
+    SeqState s{};
     if (err) {
-        for (int i = tid; i < width; i += kBlock) {
-            out_tokens[(int64_t)b * width + i] = -1;
-            out_path[(int64_t)b * width + i] = -1;
-        }
-        if (tid == 0) {
-            out_num[b] = -1;
-            st[b].status = 1;
-        }
+        s.status = 1;
+        if (tid == 0) out = s;
         return;
     }
-    if (tid == 0) {
-        if (out_acc) out_acc[(int64_t)b * nn] = 1;
-        if (out_probs) {
-            out_probs[(int64_t)b * nn * 2 + 0] = 0.0f;
-            out_probs[(int64_t)b * nn * 2 + 1] = 0.0f;
+    if (tid == 0 && outputs) {
+        if (P.out_acc) P.out_acc[(int64_t)b * nn] = 1;
+        if (P.out_probs) {
+            P.out_probs[(int64_t)b * nn * 2 + 0] = 0.0f;
+            P.out_probs[(int64_t)b * nn * 2 + 1] = 0.0f;
         }
     }
     if (wave != 0) return;
+    if (lane == 0) path[0] = 0;
     int cur = 0, depth = 0, residual = 0, werr = 0;
     for (;;) {
         if (!s_kids[cur]) break;  // leaf: bonus from q at cur
@@ -394,56 +601,29 @@ __global__ __launch_bounds__(kBlock) void k_accept_tree(
             residual = 1;
             break;
         }
-        if (depth + 1 > max_depth) {
+        if (depth + 1 > P.max_depth) {
             werr = 1;
             break;
         }
         ++depth;
-        if (lane == 0) {
-            out_path[(int64_t)b * width + depth] = next;
-            out_tokens[(int64_t)b * width + depth - 1] = tok[next];
-        }
+        if (lane == 0) path[depth] = next;
         cur = next;
     }
     if (werr) {
-        for (int i = lane; i < width; i += 64) {
-            out_tokens[(int64_t)b * width + i] = -1;
-            out_path[(int64_t)b * width + i] = -1;
-        }
-        if (lane == 0) {
-            out_num[b] = -1;
-            st[b].status = 1;
-        }
-        return;
-    }
-    for (int i = lane; i < width; i += 64) {
-        if (i > depth) {
-            out_tokens[(int64_t)b * width + i] = -1;
-            out_path[(int64_t)b * width + i] = -1;
-        }
-    }
-    if (lane == 0) {
-        out_path[(int64_t)b * width] = 0;
-        out_num[b] = depth;
-        SeqState s{};
+        s.status = 1;
+    } else {
         s.k = depth;
+        s.node = cur;
         s.status = 0;
-        s.u = sample_uniform(seed, round, (uint32_t)b, (uint32_t)(depth + 1));
-        s.q_off = (int64_t)b * qs + (int64_t)cur * qr;
-        if (residual) {
-            s.p_off = (int64_t)b * ps + (int64_t)cur * pr;
-            fill_residual_state(s, stats[((int64_t)b * nn + cur) * 2 + 0], stats[((int64_t)b * nn + cur) * 2 + 1],
-                                temp);
-        } else {
-            s.p_off = 0;
-            s.mode = kModeBonus;
-        }
-        st[b] = s;
+        s.u = sample_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(depth + 1));
+        if (residual) fill_residual_state(s, load_row_stat(P, b, 2 * cur), load_row_stat(P, b, 2 * cur + 1), P.T);
+        else s.mode = kModeBonus;
     }
+    if (lane == 0) out = s;
 }
 
 // ===========================================================================
-// 3./4. Sampling
+// Sampling
 // ===========================================================================
 // The 16 elements of thread `tid` in chunk `c` (contiguous, token order);
 // entries past V read as -inf.
@@ -465,51 +645,64 @@ __device__ __forceinline__ void load_chunk16(const char* __restrict__ row, int V
     }
 }
 
+constexpr int kModeFallback = 2;  // residual of total zero: sample q itself
+
+// Rows a sequence samples from, with the row index clamped into range (the
+// clamp keeps any index in bounds whatever the state holds).
+template <int DT>
+__device__ __forceinline__ const char* sample_qrow(const VerifyParams& P, int b, const SeqState& s)
+{
+    const int node = min(max(s.node, 0), P.nn - 1);
+    return qrow_ptr<DT>(P, b, node);
+}
+
+template <int DT>
+__device__ __forceinline__ const char* sample_prow(const VerifyParams& P, int b, const SeqState& s)
+{
+    const int lim = (P.parents ? P.nn : P.N) - 1;
+    const int node = min(max(s.node, 0), max(lim, 0));
+    return prow_ptr<DT>(P, b, node);
+}
+
 // Chunk sums of the row(s) a sequence samples from (see ChunkSums).
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_sample_partials(const char* __restrict__ zq, const char* __restrict__ zp,
-                                                            int V, int nchunks, double invT,
-                                                            const SeqState* __restrict__ st,
-                                                            ChunkSums* __restrict__ partials)
+__device__ ChunkSums chunk_sums(const VerifyParams& P, int b, const SeqState& s, int c)
 {
-    constexpr int EB = elem_bytes<DT>();
-    const int c = blockIdx.x, b = blockIdx.y;
-    const SeqState s = st[b];
-    if (s.status) return;
-    __shared__ double red[kWaves];
     __shared__ float redf[kWaves];
     float xq[kPerThread];
-    load_chunk16<DT>(zq + s.q_off * EB, V, c, threadIdx.x, xq);
-    ChunkSums out;
-    out.pad = 0.0;
+    load_chunk16<DT>(sample_qrow<DT>(P, b, s), P.V, c, threadIdx.x, xq);
+    ChunkSums out{};
     if (s.mode == kModeResidual) {
         float xp[kPerThread];
-        load_chunk16<DT>(zp + s.p_off * EB, V, c, threadIdx.x, xp);
-        double sa = 0.0, sb = 0.0, pa = 0.0, pb = 0.0, na = 0.0, nb = 0.0;
+        load_chunk16<DT>(sample_prow<DT>(P, b, s), P.V, c, threadIdx.x, xp);
+        double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sa sb pa pb na nb
         float dmin = INFINITY, dmax = -INFINITY;
+        const ExpRow eq = exp_row(P, s.mq), ep = exp_row(P, s.mp);
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const double a = exp(((double)xq[j] - (double)s.mq) * invT);
-            const double bb = exp(((double)xp[j] - (double)s.mp) * invT);
-            sa += a;
-            sb += bb;
+            const double a = eq(xq[j]);
+            const double bb = ep(xp[j]);
+            acc[0] += a;
+            acc[1] += bb;
             const float d = xq[j] - xp[j];
             if (d > s.thr_hi) {
-                pa += a;
-                pb += bb;
+                acc[2] += a;
+                acc[3] += bb;
             } else if (d >= s.thr_lo) {
-                na += a;
-                nb += bb;
+                acc[4] += a;
+                acc[5] += bb;
                 dmin = fminf(dmin, d);
                 dmax = fmaxf(dmax, d);
             }
         }
-        out.sa = block_sum(sa, red);
-        out.sb = block_sum(sb, red);
-        out.pa = block_sum(pa, red);
-        out.pb = block_sum(pb, red);
-        out.na = block_sum(na, red);
-        out.nb = block_sum(nb, red);
+        __shared__ double red6[kWaves * 6];
+        block_sum_n<6>(acc, red6);
+        out.sa = acc[0];
+        out.sb = acc[1];
+        out.pa = acc[2];
+        out.pb = acc[3];
+        out.na = acc[4];
+        out.nb = acc[5];
         out.dmax = block_max(dmax, redf);
         out.dmin = -block_max(-dmin, redf);
     } else {
@@ -521,125 +714,186 @@ __global__ __launch_bounds__(kBlock) void k_sample_partials(const char* __restri
             bad |= (xq[j] != xq[j]) || (xq[j] == INFINITY);
         }
         const float mc = block_max(lm, redf);
-        double sa = 0.0;
+        double sa[1] = {0.0};
         if (mc != -INFINITY) {
+            const ExpRow ec = exp_row(P, mc);
 #pragma unroll
-            for (int j = 0; j < kPerThread; ++j) sa += exp(((double)xq[j] - (double)mc) * invT);
+            for (int j = 0; j < kPerThread; ++j) sa[0] += ec(xq[j]);
         }
+        __shared__ double red1[kWaves];
+        block_sum_n<1>(sa, red1);
         out.sa = (double)mc;
-        out.sb = block_sum(sa, red);
-        out.pa = (double)__syncthreads_or(bad);
-        out.pb = out.na = out.nb = 0.0;
-        out.dmin = out.dmax = 0.0f;
+        out.sb = sa[0];
+        out.flags = __syncthreads_or(bad) ? kFlagBad : 0u;
     }
-    if (threadIdx.x == 0) partials[(int64_t)b * nchunks + c] = out;
+    return out;
 }
-
-constexpr int kModeFallback = 2;  // residual of total zero: sample q itself
 
 // Exact weight of one element of the residual: a - rho*b where q > p for
 // certain, max(0, a - rho*b) in the near-threshold band, 0 below it.
-__device__ __forceinline__ double residual_weight(float xq, float xp, const SeqState& s, double invT, double rho)
+__device__ __forceinline__ double residual_weight(float xq, float xp, const SeqState& s, const ExpRow& eq,
+                                                  const ExpRow& ep, double rho)
 {
     const float d = xq - xp;
     if (!(d >= s.thr_lo)) return 0.0;
-    const double a = exp(((double)xq - (double)s.mq) * invT);
-    const double bb = exp(((double)xp - (double)s.mp) * invT);
+    const double a = eq(xq);
+    const double bb = ep(xp);
     const double w = a - rho * bb;
     return (d > s.thr_hi) ? w : fmax(0.0, w);
 }
 
+// One chunk of a logit row held in LDS in its storage format.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict__ zq, const char* __restrict__ zp,
-                                                         int V, int nchunks, double invT,
-                                                         const SeqState* __restrict__ st,
-                                                         const ChunkSums* __restrict__ partials, int width,
-                                                         int32_t* __restrict__ out_tokens,
-                                                         int32_t* __restrict__ out_num,
-                                                         int32_t* __restrict__ out_path,
-                                                         double* __restrict__ out_resid)
+struct Staged;
+template <>
+struct Staged<DT_BF16> {
+    uint16_t v[kChunk];
+    __device__ __forceinline__ float get(int i) const { return __uint_as_float((uint32_t)v[i] << 16); }
+    __device__ __forceinline__ void set(int i, float x) { v[i] = (uint16_t)(__float_as_uint(x) >> 16); }
+};
+template <>
+struct Staged<DT_F32> {
+    float v[kChunk];
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
+    __device__ __forceinline__ void set(int i, float x) { v[i] = x; }
+};
+
+// This thread's 16 tokens of chunk c into LDS (tokens past V as -inf).
+template <int DT>
+__device__ __forceinline__ void stage_chunk(const char* row, int V, int c, Staged<DT>& dst)
 {
-    constexpr int EB = elem_bytes<DT>();
-    const int b = blockIdx.x;
+    float x[kPerThread];
+    load_chunk16<DT>(row, V, c, threadIdx.x, x);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) dst.set(threadIdx.x * kPerThread + j, x[j]);
+}
+
+// Block-wide: the outputs of sequence b.  k < 0 or token < 0 marks the
+// sequence as failed (every slot -1).
+template <bool TREE>
+__device__ void emit(const VerifyParams& P, int b, int k, int token, double resid, const int32_t* path)
+{
+    const int width = P.width;
+    const bool ok = k >= 0 && token >= 0;
+    for (int i = threadIdx.x; i < width; i += kBlock) {
+        int32_t t = -1, pn = -1;
+        if (ok) {
+            if (TREE) {
+                if (i <= k) pn = path[i];
+                if (i < k) {
+                    const int node = path[i + 1];
+                    t = P.tokens[(int64_t)b * P.nn + min(max(node, 0), P.nn - 1)];
+                }
+            } else if (i < k) {
+                t = P.tokens[(int64_t)b * P.N + i];
+            }
+            if (i == k) t = token;
+        }
+        P.out_tokens[(int64_t)b * width + i] = t;
+        if (TREE) P.out_path[(int64_t)b * width + i] = pn;
+    }
+    if (threadIdx.x == 0) {
+        P.out_num[b] = ok ? k : -1;
+        if (P.out_resid) P.out_resid[b] = ok ? resid : 0.0;
+    }
+}
+
+// Final step of sequence b: wait for its chunks, totals, chunk location,
+// rescan, outputs.
+template <int DT, bool TREE>
+__device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path)
+{
     const int tid = threadIdx.x;
-    const SeqState s = st[b];
-    if (s.status) return;
+    const int nchunks = P.nch;
+    const double invT = P.invT;
     __shared__ double red[kWaves];
     __shared__ float redf[kWaves];
     __shared__ double s_near[kMaxChunks];
     __shared__ int s_chunk;
     __shared__ double s_base;
     __shared__ int s_owner;
-    const ChunkSums* P = partials + (int64_t)b * nchunks;
-    // chunks per thread (contiguous groups, token order)
+    __shared__ int s_token;
+    __shared__ Staged<DT> s_q, s_p;
+    const bool chunks_ok = wait_records<4>(part_rsrc(P), chunk_off(P, b, 0), nchunks, P.epoch);
+    int timed_out = 0;
+    for (int c = tid; c < nchunks; c += kBlock) timed_out |= (get_chunk(P, b, c).flags & kFlagTimeout) != 0;
+    timed_out = __syncthreads_or(timed_out);
+    if (!chunks_ok || timed_out || s.status) {
+        emit<TREE>(P, b, -1, -1, 0.0, path);
+        return;
+    }
     const int g = (nchunks + kBlock - 1) / kBlock;
     const int c0 = tid * g;
     const int c1 = min(nchunks, c0 + g);
-    const char* qrow = zq + s.q_off * EB;
-    const char* prow = zp + s.p_off * EB;
+    const char* qrow = sample_qrow<DT>(P, b, s);
+    const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
+    const ExpRow eq = exp_row(P, s.mq), ep = exp_row(P, s.mp);
 
     // --- totals ---
     double rho = 0.0, M = 0.0, resid_mass = 0.0;
     int mode = s.mode;
     if (mode == kModeResidual) {
-        double sq = 0.0, sp = 0.0;
+        double sqp[2] = {0.0, 0.0};
         for (int c = c0; c < c1; ++c) {
-            sq += P[c].sa;
-            sp += P[c].sb;
+            const ChunkSums p = get_chunk(P, b, c);
+            sqp[0] += p.sa;
+            sqp[1] += p.sb;
         }
-        sq = block_sum(sq, red);
-        sp = block_sum(sp, red);
-        rho = sq / sp;
+        __shared__ double red2[kWaves * 2];
+        block_sum_n<2>(sqp, red2);
+        const double sq = sqp[0];
+        rho = sqp[0] / sqp[1];
         // near-threshold tokens: exact when they share one zq - zp (one ratio
         // q/p), else the chunk is rescanned below with the exact rho
         for (int c = tid; c < nchunks; c += kBlock) {
-            const ChunkSums p = P[c];
+            const ChunkSums p = get_chunk(P, b, c);
             s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
         }
         __syncthreads();
         for (int c = 0; c < nchunks; ++c) {
             if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
-            float xq[kPerThread], xp[kPerThread];
-            load_chunk16<DT>(qrow, V, c, tid, xq);
-            load_chunk16<DT>(prow, V, c, tid, xp);
-            double w = 0.0;
+            stage_chunk<DT>(qrow, P.V, c, s_q);
+            stage_chunk<DT>(prow, P.V, c, s_p);
+            double w[1] = {0.0};
+#pragma unroll 4
             for (int j = 0; j < kPerThread; ++j) {
-                const float d = xq[j] - xp[j];
-                if (d >= s.thr_lo && !(d > s.thr_hi)) w += residual_weight(xq[j], xp[j], s, invT, rho);
+                const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
+                const float d = zq - zp;
+                if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(zq, zp, s, eq, ep, rho);
             }
-            w = block_sum(w, red);
-            if (tid == 0) s_near[c] = w;
+            block_sum_n<1>(w, red);
+            if (tid == 0) s_near[c] = w[0];
             __syncthreads();
         }
-        double wsum = 0.0;
-        for (int c = c0; c < c1; ++c) wsum += (P[c].pa - rho * P[c].pb) + s_near[c];
-        const double Wtot = block_sum(wsum, red);
-        if (!(Wtot > 0.0)) {
+        double wsum[1] = {0.0};
+        for (int c = c0; c < c1; ++c) {
+            const ChunkSums p = get_chunk(P, b, c);
+            wsum[0] += (p.pa - rho * p.pb) + s_near[c];
+        }
+        block_sum_n<1>(wsum, red);
+        if (!(wsum[0] > 0.0)) {
             mode = kModeFallback;
             resid_mass = 0.0;
         } else {
-            resid_mass = Wtot / sq;
+            resid_mass = wsum[0] / sq;
         }
     } else {
         float lm = -INFINITY;
         int bad = 0;
         for (int c = c0; c < c1; ++c) {
-            lm = fmaxf(lm, (float)P[c].sa);
-            bad |= P[c].pa != 0.0;
+            const ChunkSums p = get_chunk(P, b, c);
+            lm = fmaxf(lm, (float)p.sa);
+            bad |= (p.flags & kFlagBad) != 0;
         }
         M = (double)block_max(lm, redf);
         bad = __syncthreads_or(bad);
         if (bad || M == -INFINITY) {
-            for (int i = tid; i < width; i += kBlock) {
-                out_tokens[(int64_t)b * width + i] = -1;
-                if (out_path) out_path[(int64_t)b * width + i] = -1;
-            }
-            if (tid == 0) out_num[b] = -1;
+            emit<TREE>(P, b, -1, -1, 0.0, path);
             return;
         }
     }
     auto chunk_weight = [&](int c) -> double {
-        const ChunkSums& p = P[c];
+        const ChunkSums p = get_chunk(P, b, c);
         if (mode == kModeResidual) return (p.pa - rho * p.pb) + s_near[c];
         if (mode == kModeFallback) return p.sa;
         return (p.sa == -INFINITY) ? 0.0 : p.sb * exp((p.sa - M) * invT);
@@ -682,7 +936,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
             pick = last;
             pick_base = last_base;
         }
-        s_chunk = pick;
+        s_chunk = pick < 0 ? 0 : pick;
         s_base = pick_base;
     }
     __syncthreads();
@@ -690,29 +944,33 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
     const double cbase = s_base;
 
     // --- rescan the chunk ---
-    float xq[kPerThread], xp[kPerThread];
-    load_chunk16<DT>(qrow, V, cs, tid, xq);
-    if (mode == kModeResidual) load_chunk16<DT>(prow, V, cs, tid, xp);
+    // Each thread stages its 16 tokens in LDS and walks them one at a time
+    // (it reads back only what it wrote itself).
+    stage_chunk<DT>(qrow, P.V, cs, s_q);
+    if (mode == kModeResidual) stage_chunk<DT>(prow, P.V, cs, s_p);
     double scale = 1.0, mc = 0.0;
     if (mode == kModeBonus) {
-        mc = P[cs].sa;
+        mc = get_chunk(P, b, cs).sa;
         scale = exp((mc - M) * invT);
     }
-    double w[kPerThread];
+    const ExpRow ec = exp_row(P, mc);
+    auto weight = [&](int j) -> double {
+        const int i = tid * kPerThread + j;
+        const float a = s_q.get(i);
+        if (mode == kModeResidual) return residual_weight(a, s_p.get(i), s, eq, ep, rho);
+        if (mode == kModeFallback) return eq(a);
+        return ec(a);
+    };
     double tsum = 0.0;
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-        double v;
-        if (mode == kModeResidual) v = residual_weight(xq[j], xp[j], s, invT, rho);
-        else if (mode == kModeFallback) v = exp(((double)xq[j] - (double)s.mq) * invT);
-        else v = exp(((double)xq[j] - mc) * invT);
-        w[j] = v;
-        tsum += v;
-    }
+#pragma unroll 4
+    for (int j = 0; j < kPerThread; ++j) tsum += weight(j);
     double ctotal;
     const double tbase = block_exclusive_scan(tsum, red, &ctotal);
     const double local = (target - cbase) / scale;
-    if (tid == 0) s_owner = -1;
+    if (tid == 0) {
+        s_owner = -1;
+        s_token = -1;
+    }
     __syncthreads();
     if (tsum > 0.0 && tbase <= local) atomicMax(&s_owner, tid);
     __syncthreads();
@@ -720,34 +978,193 @@ __global__ __launch_bounds__(kBlock) void k_sample_final(const char* __restrict_
         // no positive weight at or below the threshold in this chunk (only
         // possible through rounding): take its last element of positive weight
         int last = -1;
+#pragma unroll 4
         for (int j = 0; j < kPerThread; ++j)
-            if (w[j] > 0.0) last = cs * kChunk + tid * kPerThread + j;
-        __shared__ int s_last;
-        if (tid == 0) s_last = -1;
-        __syncthreads();
-        atomicMax(&s_last, last);
-        __syncthreads();
-        if (tid == 0) {
-            out_tokens[(int64_t)b * width + s.k] = s_last;
-            if (s_last < 0) out_num[b] = -1;
-            if (out_resid) out_resid[b] = (s.mode == kModeResidual) ? resid_mass : 0.0;
-        }
-        return;
-    }
-    if (tid == s_owner) {
+            if (weight(j) > 0.0) last = cs * kChunk + tid * kPerThread + j;
+        atomicMax(&s_token, last);
+    } else if (tid == s_owner) {
         double cum = tbase;
         int pick = -1, last = -1;
+#pragma unroll 4
         for (int j = 0; j < kPerThread; ++j) {
-            if (w[j] > 0.0) {
+            const double wj = weight(j);
+            if (wj > 0.0) {
                 last = j;
-                if (pick < 0 && cum + w[j] > local) pick = j;
+                if (pick < 0 && cum + wj > local) pick = j;
             }
-            cum += w[j];
+            cum += wj;
         }
         if (pick < 0) pick = last;
-        out_tokens[(int64_t)b * width + s.k] = cs * kChunk + tid * kPerThread + pick;
-        if (out_resid) out_resid[b] = (s.mode == kModeResidual) ? resid_mass : 0.0;
+        s_token = pick < 0 ? -1 : cs * kChunk + tid * kPerThread + pick;
     }
+    __syncthreads();
+    emit<TREE>(P, b, s.k, s_token, (s.mode == kModeResidual) ? resid_mass : 0.0, path);
+}
+
+// ===========================================================================
+// Kernels
+// ===========================================================================
+// 16-byte loads per thread per batch of a row block
+#ifndef SV_ROW_BATCH
+#define SV_ROW_BATCH 8
+#endif
+constexpr int kRowBatch = SV_ROW_BATCH;
+// Exp table for bf16 logits in the sample kernel (0 computes every exp)
+#ifndef SV_EXP_TABLE
+#define SV_EXP_TABLE 1
+#endif
+constexpr int kTablePerBlock = 1024;  // exp-table entries per table block
+
+// Share of the exp table (exp(v/T) for every bf16 bit pattern v, used by
+// ExpRow) filled by this block of a grid of `nblocks`.
+__device__ __forceinline__ void fill_table_share(const VerifyParams& P, int blk, int nblocks)
+{
+    const int lo = (int)((int64_t)blk * 65536 / nblocks), hi = (int)((int64_t)(blk + 1) * 65536 / nblocks);
+    for (int i = lo + (int)threadIdx.x; i < hi; i += kBlock) {
+        const float v = __uint_as_float((uint32_t)i << 16);
+        P.table[i] = exp((double)v * P.invT);
+    }
+}
+
+// (m, s) of n consecutive elements starting at `row`, by one wave (valid in
+// every lane): scalar head up to the first 16-byte boundary, 16-byte vectors
+// in batches of U per lane with the next batch issued before the current one
+// is used (the last padded with -inf), scalar tail.
+template <int DT, int U>
+__device__ __forceinline__ RowStat wave_row_stats(const char* __restrict__ row, int64_t n, float c, double cd)
+{
+    constexpr int EB = elem_bytes<DT>();
+    constexpr int EPV = 16 / EB;
+    const int lane = threadIdx.x & 63;
+    float ref = -INFINITY;
+    double acc = 0.0;
+    int64_t head = (int64_t)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
+    head = head < n ? head : n;
+    if (lane < head) {
+        float x[1] = {load_logit<DT>(row, lane)};
+        accumulate_values<1>(x, c, cd, ref, acc);
+    }
+    row += head * EB;
+    n -= head;
+    const int64_t nvec = n / EPV;
+    const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
+    const int64_t nbatch = (nvec + U * 64 - 1) / (U * 64);
+    int64_t v = lane;
+    uint4 cur[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = (v + u * 64 < nvec) ? stream_load16(vrow + v + u * 64) : neg_inf16<DT>();
+    for (int64_t bt = 0; bt < nbatch; ++bt) {
+        const int64_t nv = v + U * 64;
+        uint4 nxt[U];
+        if (bt + 1 < nbatch) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                nxt[u] = (nv + u * 64 < nvec) ? stream_load16(vrow + nv + u * 64) : neg_inf16<DT>();
+        }
+        accumulate_batch<DT, U>(cur, c, cd, ref, acc);
+        v = nv;
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    }
+    const int64_t tail = n - nvec * EPV;
+    if (lane < tail) {
+        float x[1] = {load_logit<DT>(row, nvec * EPV + lane)};
+        accumulate_values<1>(x, c, cd, ref, acc);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const float m2 = __shfl_xor(ref, off, 64);
+        const double s2 = __shfl_xor(acc, off, 64);
+        combine_stat(ref, acc, m2, s2, cd);
+    }
+    return RowStat{acc, ref};
+}
+
+// Row kernel for chains: the pass-1 rows of all sequences, flattened, are cut
+// into one equal range per wave; a wave streams its range without barriers
+// and stores one record per row piece it covers.  Every block also fills its
+// share of the exp table.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_stream(const VerifyParams P)
+{
+    if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
+    const int w = (int)blockIdx.x * kWaves + ((int)threadIdx.x >> 6);
+    int64_t e = wave_begin(P, w);
+    const int64_t e_end = wave_begin(P, w + 1);
+    while (e < e_end) {
+        const int64_t grow = e / P.V;
+        const int64_t o = e - grow * P.V;
+        const int64_t left = (int64_t)P.V - o;
+        const int64_t take = (e_end - e) < left ? (e_end - e) : left;
+        const int b = (int)(grow / P.rows), r = (int)(grow - (int64_t)b * P.rows);
+        const char* base = r < P.N ? qrow_ptr<DT>(P, b, r) : prow_ptr<DT>(P, b, r - P.N);
+        const RowStat st = wave_row_stats<DT, kRowBatch>(base + o * elem_bytes<DT>(), take, P.c, P.cd);
+        if ((threadIdx.x & 63) == 0) {
+            u32x4 a[1];
+            pack(st, a);
+            put_record<1>(stats_rsrc(P), stat_off(P, grow, w - wave_of(P, grow * P.V)), a, P.epoch);
+        }
+        e += take;
+    }
+}
+
+// Row kernel for trees: block (b, row, segment) streams one segment of a q/p
+// row that an accept test reads (rows of leaves get a placeholder record).
+// Every block also fills its share of the exp table.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
+{
+    if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
+    const int b = (int)blockIdx.x / P.r_items;
+    const int idx = (int)blockIdx.x - b * P.r_items;
+    const int row = idx / P.segs, seg = idx - row * P.segs;
+    const int node = row >> 1;
+    const int32_t* par = P.parents_shared ? P.parents : P.parents + (int64_t)b * P.nn;
+    int found = 0;
+    for (int m = node + 1 + (int)threadIdx.x; m < P.nn; m += kBlock) found |= (par[m] == node);
+    const bool work = __syncthreads_or(found) != 0;
+    const char* base = (row & 1) ? prow_ptr<DT>(P, b, node) : qrow_ptr<DT>(P, b, node);
+    RowStat st{0.0, -INFINITY};
+    if (work) {
+        const int begin = seg * P.seg_len;
+        const int n = min(P.V - begin, P.seg_len);
+        st = block_row_stats<DT, kRowBatch>(base + (int64_t)begin * elem_bytes<DT>(), n, P.c, P.cd);
+    }
+    if (threadIdx.x == 0) {
+        u32x4 a[1];
+        pack(st, a);
+        put_record<1>(stats_rsrc(P), stat_off(P, (int64_t)b * P.rows + row, seg), a, P.epoch);
+    }
+}
+
+// Sample kernel: block (b, group) runs b's accept step itself (a few records
+// and logits; group 0 writes the accept outputs), forms the chunk sums of its
+// group of chunks of the row(s) b samples from, and the last of b's blocks to
+// finish (an arrival counter per sequence) runs b's final step.
+template <int DT, bool TREE>
+__global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
+{
+    const int b = (int)blockIdx.x / P.groups;
+    const int g = (int)blockIdx.x - b * P.groups;
+    __shared__ SeqState s_state;
+    __shared__ int32_t s_path[kMaxNodes];
+    if constexpr (TREE) {
+        tree_accept<DT>(P, b, s_state, s_path, g == 0);
+    } else {
+        if (threadIdx.x < 64) chain_accept<DT>(P, b, s_state, g == 0);
+    }
+    __syncthreads();
+    const SeqState s = s_state;
+    const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
+    for (int c = c0; c < c1; ++c) {
+        ChunkSums out{};
+        if (s.status == 0) out = chunk_sums<DT>(P, b, s, c);
+        if (threadIdx.x == 0) put_chunk(P, b, c, out);
+    }
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
+    __syncthreads();
+    if (s_last) sample_final<DT, TREE>(P, b, s, s_path);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -772,24 +1189,117 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int nchunks_of(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
 
-struct Layout {
-    size_t stats, seq, part, total;
+// Row segments of about 128K elements (a multiple of 64 elements, so every
+// segment keeps the row's 16-byte alignment).
+constexpr int kSegTarget = 131072;
+void segments_of(int V, int* segs, int* seg_len)
+{
+    int s = (V + kSegTarget - 1) / kSegTarget;
+    if (s < 1) s = 1;
+    int len = (V + s - 1) / s;
+    len = (len + 63) / 64 * 64;
+    *seg_len = len;
+    *segs = (V + len - 1) / len;
+}
+
+constexpr int kTableEntries = 65536;
+constexpr int64_t kWaveMinElems = 32768;  // smallest range worth a wave of the chain row kernel
+constexpr int kSampleBlocksTarget = 1024;   // sample blocks aimed at per call
+
+// Blocks of a kernel the device holds at once (compute units x occupancy).
+template <typename K>
+int resident_blocks(K kernel, std::atomic<int>& cache)
+{
+    int v = cache.load();
+    if (v) return v;
+    int dev = 0, cus = 0, occ = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel), sv::kBlock, 0) !=
+            hipSuccess ||
+        occ <= 0)
+        return 0;
+    v = cus * occ;
+    cache.store(v);
+    return v;
+}
+
+// Blocks of the chain row kernel: as many as the device holds at once (one
+// round, so the equal ranges also finish together), fewer for small inputs.
+// dtype < 0 gives an upper bound over both dtypes (workspace sizing; without
+// a device, 2048 blocks).
+int stream_blocks(int dtype, int64_t E)
+{
+    static std::atomic<int> c_bf16{0}, c_f32{0};
+    int resident;
+    if (dtype < 0) {
+        const int a = resident_blocks(&sv::k_stream<sv::DT_BF16>, c_bf16);
+        const int b = resident_blocks(&sv::k_stream<sv::DT_F32>, c_f32);
+        resident = a > b ? a : b;
+        if (resident < 2048) resident = 2048;
+    } else {
+        resident = dtype == SV_BF16 ? resident_blocks(&sv::k_stream<sv::DT_BF16>, c_bf16)
+                                    : resident_blocks(&sv::k_stream<sv::DT_F32>, c_f32);
+    }
+    if (resident <= 0) return 0;
+    const int64_t want = (E + sv::kWaves * kWaveMinElems - 1) / (sv::kWaves * kWaveMinElems);
+    return (int)(want < 1 ? 1 : (want < resident ? want : resident));
+}
+
+// Pass-1 work split.  Chains: W waves over the flattened rows and MP record
+// slots per row (a row of V elements meets at most ceil(V / L) + 1 wave
+// ranges, L the shortest non-empty range).  Trees: one slot per segment.
+struct Split {
+    int blocks, W, MP;
+    int64_t E, E64;
 };
 
-Layout make_layout(int B, int rows_per_seq, int V)
+Split split_for(bool tree, int dtype, int B, int rows, int V)
+{
+    Split s{};
+    s.E = (int64_t)B * rows * V;
+    s.E64 = (s.E + 63) / 64;
+    if (tree) {
+        int segs, seg_len;
+        segments_of(V, &segs, &seg_len);
+        s.blocks = 0;
+        s.W = 0;
+        s.MP = segs;
+        return s;
+    }
+    s.blocks = stream_blocks(dtype, s.E);
+    s.W = s.blocks * sv::kWaves;
+    if (s.W <= 0) return s;
+    // no more waves than 64-element units: every range is then non-empty
+    // (waves past W get none)
+    if (s.E64 > 0 && s.W > s.E64) s.W = (int)s.E64;
+    int64_t per = s.E64 / s.W;
+    const int64_t L = 64 * (per < 1 ? 1 : per);
+    s.MP = (int)((V + L - 1) / L + 1);
+    return s;
+}
+
+struct Layout {
+    size_t chunk_arr, stats, part, table, total;
+};
+
+Layout make_layout(int B, int rows, int V, int MP)
 {
     Layout L;
-    L.stats = 0;
-    L.seq = align_up((size_t)B * rows_per_seq * sizeof(sv::RowStat));
-    L.part = L.seq + align_up((size_t)B * sizeof(sv::SeqState));
-    L.total = L.part + align_up((size_t)B * nchunks_of(V) * sizeof(sv::ChunkSums));
+    L.chunk_arr = 0;
+    L.stats = align_up((size_t)B * sizeof(uint64_t));
+    L.part = L.stats + align_up((size_t)B * rows * MP * sv::kRowStatBytes);
+    L.table = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
+    L.total = L.table + (size_t)kTableEntries * sizeof(double);
     return L;
 }
 
-bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// The record regions are addressed with 32-bit buffer offsets.
+bool regions_fit(const Layout& L)
+{
+    return L.part - L.stats <= (size_t)INT32_MAX && L.table - L.part <= (size_t)INT32_MAX;
+}
 
-// Rows need only be element-aligned (strides are in elements); 16-byte
-// aligned rows take the all-vector path.
 int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
 {
     if (((uintptr_t)base % (uintptr_t)es) != 0) return SV_EALIGN;
@@ -797,9 +1307,80 @@ int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
     return SV_OK;
 }
 
-int launch_status()
+std::atomic<uint32_t> g_epoch{0};
+uint32_t next_epoch()
 {
-    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+    uint32_t e;
+    do {
+        e = g_epoch.fetch_add(1) + 1;
+    } while (e == 0);
+    return e;
+}
+
+template <int DT, bool TREE>
+int launch_kernels(const sv::VerifyParams& P, int stream_grid, const sv_timing* timing, hipStream_t stream)
+{
+    const int64_t row_grid = TREE ? (int64_t)P.B * P.r_items : stream_grid;
+    const int64_t sample_grid = (int64_t)P.B * P.groups;
+    if (timing && timing->stats_begin && hipEventRecord(timing->stats_begin, stream) != hipSuccess) return SV_EHIP;
+    if (row_grid > 0) {
+        if (TREE)
+            hipLaunchKernelGGL((sv::k_rows<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
+        else
+            hipLaunchKernelGGL((sv::k_stream<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
+    }
+    hipLaunchKernelGGL((sv::k_sample<DT, TREE>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (timing && timing->stats_end && hipEventRecord(timing->stats_end, stream) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+template <bool TREE>
+int launch_verify(sv::VerifyParams& P, int dtype, const Split& S, void* workspace, const Layout& L,
+                  const sv_timing* timing, hipStream_t stream)
+{
+    char* ws = static_cast<char*>(workspace);
+    P.chunk_arrivals = reinterpret_cast<uint64_t*>(ws + L.chunk_arr);
+    P.stats = ws + L.stats;
+    P.part = ws + L.part;
+    P.stats_bytes = (uint32_t)(L.part - L.stats);
+    P.part_bytes = (uint32_t)(L.table - L.part);
+    const bool table = SV_EXP_TABLE && dtype == SV_BF16;
+    P.table = table ? reinterpret_cast<double*>(ws + L.table) : nullptr;
+    P.E = S.E;
+    P.E64 = S.E64;
+    P.W = S.W;
+    P.MP = S.MP;
+    P.epoch = next_epoch();
+    return dtype == SV_BF16 ? launch_kernels<sv::DT_BF16, TREE>(P, S.blocks, timing, stream)
+                            : launch_kernels<sv::DT_F32, TREE>(P, S.blocks, timing, stream);
+}
+
+void fill_common(sv::VerifyParams& P, int B, int V, int rows, uint64_t seed, uint64_t round, float temperature)
+{
+    P.B = B;
+    P.V = V;
+    P.rows = rows;
+    segments_of(V, &P.segs, &P.seg_len);
+    P.r_items = rows * P.segs;
+    P.nch = nchunks_of(V);
+    int64_t cpb = ((int64_t)P.nch * B + kSampleBlocksTarget - 1) / kSampleBlocksTarget;
+    P.cpb = (int)(cpb < 1 ? 1 : (cpb > P.nch ? P.nch : cpb));
+    P.groups = (P.nch + P.cpb - 1) / P.cpb;
+    P.seed = seed;
+    P.round = round;
+    P.T = temperature;
+    P.invT = 1.0 / (double)temperature;
+    P.cd = 1.4426950408889634074 / (double)temperature;  // log2(e) / T
+    P.c = (float)P.cd;
+}
+
+// Grids must fit an unsigned launch dimension.
+bool item_count_ok(int B, int rows, int V)
+{
+    int segs, seg_len;
+    segments_of(V, &segs, &seg_len);
+    return (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * nchunks_of(V) < (int64_t)INT32_MAX;
 }
 
 }  // namespace
@@ -825,13 +1406,13 @@ const char* sv_status_string(int status)
 size_t sv_chain_workspace_bytes(int B, int N, int V)
 {
     if (B < 0 || N < 0 || N > 64 || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * N, V).total;
+    return make_layout(B, 2 * N, V, split_for(false, -1, B, 2 * N, V).MP).total;
 }
 
 size_t sv_tree_workspace_bytes(int B, int T, int V)
 {
     if (B < 0 || T < 0 || T + 1 > sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * (T + 1), V).total;
+    return make_layout(B, 2 * (T + 1), V, split_for(true, -1, B, 2 * (T + 1), V).MP).total;
 }
 
 int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
@@ -851,55 +1432,37 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
     if (rc) return rc;
     if (N > 0 && (rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
-    if ((int64_t)B * 2 * N > INT32_MAX || B > 65535) return SV_ESHAPE;
-    const Layout L = make_layout(B, 2 * N, V);
-    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    if (!item_count_ok(B, 2 * N, V)) return SV_ESHAPE;
+    // the workspace is sized for the largest split any device can choose
+    const Layout Lb = make_layout(B, 2 * N, V, split_for(false, -1, B, 2 * N, V).MP);
+    if (!regions_fit(Lb)) return SV_ESHAPE;
+    if (!workspace || workspace_bytes < Lb.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
+    const Split S = split_for(false, dtype, B, 2 * N, V);
+    if (S.W <= 0) return SV_EHIP;
+    const Layout L = make_layout(B, 2 * N, V, S.MP);
 
-    char* ws = static_cast<char*>(workspace);
-    sv::RowStat* stats = reinterpret_cast<sv::RowStat*>(ws + L.stats);
-    sv::SeqState* seq = reinterpret_cast<sv::SeqState*>(ws + L.seq);
-    sv::ChunkSums* part = reinterpret_cast<sv::ChunkSums*>(ws + L.part);
-    const char* zq = static_cast<const char*>(target_logits);
-    const char* zp = static_cast<const char*>(draft_logits ? draft_logits : target_logits);
-    const double invT = 1.0 / (double)temperature;
-    const double cd = 1.4426950408889634074 / (double)temperature;  // log2(e) / T
-    const float c = (float)cd;
-    const int nch = nchunks_of(V);
-    const dim3 blk(sv::kBlock);
-
-    if (timing && timing->stats_begin && hipEventRecord(timing->stats_begin, stream) != hipSuccess) return SV_EHIP;
-    if (N > 0) {
-        if (dtype == SV_BF16)
-            sv::k_stats_chain<sv::DT_BF16><<<dim3(B * 2 * N), blk, 0, stream>>>(
-                zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, N, V, c, cd, stats);
-        else
-            sv::k_stats_chain<sv::DT_F32><<<dim3(B * 2 * N), blk, 0, stream>>>(
-                zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, N, V, c, cd, stats);
-        if ((rc = launch_status())) return rc;
-    }
-    if (timing && timing->stats_end && hipEventRecord(timing->stats_end, stream) != hipSuccess) return SV_EHIP;
-    const dim3 grid_acc((B + sv::kWaves - 1) / sv::kWaves);
-    if (dtype == SV_BF16)
-        sv::k_accept_chain<sv::DT_BF16><<<grid_acc, blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, draft_tokens, B, N, V, seed,
-            round, invT, temperature, stats, seq, out_tokens, out_num_accepted, out_accept, out_probs);
-    else
-        sv::k_accept_chain<sv::DT_F32><<<grid_acc, blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, draft_tokens, B, N, V, seed,
-            round, invT, temperature, stats, seq, out_tokens, out_num_accepted, out_accept, out_probs);
-    if ((rc = launch_status())) return rc;
-    if (dtype == SV_BF16) {
-        sv::k_sample_partials<sv::DT_BF16><<<dim3(nch, B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part);
-        sv::k_sample_final<sv::DT_BF16><<<dim3(B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part, N + 1,
-                                                                     out_tokens, out_num_accepted, nullptr,
-                                                                     out_residual_mass);
-    } else {
-        sv::k_sample_partials<sv::DT_F32><<<dim3(nch, B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part);
-        sv::k_sample_final<sv::DT_F32><<<dim3(B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part, N + 1,
-                                                                    out_tokens, out_num_accepted, nullptr,
-                                                                    out_residual_mass);
-    }
-    return launch_status();
+    sv::VerifyParams P{};
+    P.zq = static_cast<const char*>(target_logits);
+    P.zp = static_cast<const char*>(draft_logits ? draft_logits : target_logits);
+    P.qs = tgt_seq_stride;
+    P.qr = tgt_row_stride;
+    P.ps = drf_seq_stride;
+    P.pr = drf_row_stride;
+    P.tokens = draft_tokens;
+    P.parents = nullptr;
+    P.parents_shared = 1;
+    P.N = N;
+    P.nn = N + 1;
+    P.max_depth = N;
+    P.width = N + 1;
+    fill_common(P, B, V, 2 * N, seed, round, temperature);
+    P.out_tokens = out_tokens;
+    P.out_path = nullptr;
+    P.out_num = out_num_accepted;
+    P.out_acc = out_accept;
+    P.out_probs = out_probs;
+    P.out_resid = out_residual_mass;
+    return launch_verify<false>(P, dtype, S, workspace, L, timing, stream);
 }
 
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
@@ -923,57 +1486,34 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if (rc) return rc;
     if ((rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
     const int nn = T + 1;
-    if ((int64_t)B * 2 * nn > INT32_MAX || B > 65535) return SV_ESHAPE;
-    const Layout L = make_layout(B, 2 * nn, V);
-    if (!workspace || workspace_bytes < L.total || !aligned16(workspace)) return SV_EWORKSPACE;
+    if (!item_count_ok(B, 2 * nn, V)) return SV_ESHAPE;
+    const Split S = split_for(true, dtype, B, 2 * nn, V);
+    const Layout L = make_layout(B, 2 * nn, V, S.MP);
+    if (!regions_fit(L)) return SV_ESHAPE;
+    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
 
-    char* ws = static_cast<char*>(workspace);
-    sv::RowStat* stats = reinterpret_cast<sv::RowStat*>(ws + L.stats);
-    sv::SeqState* seq = reinterpret_cast<sv::SeqState*>(ws + L.seq);
-    sv::ChunkSums* part = reinterpret_cast<sv::ChunkSums*>(ws + L.part);
-    const char* zq = static_cast<const char*>(target_logits);
-    const char* zp = static_cast<const char*>(draft_logits);
-    const double invT = 1.0 / (double)temperature;
-    const double cd = 1.4426950408889634074 / (double)temperature;
-    const float c = (float)cd;
-    const int nch = nchunks_of(V);
-    const dim3 blk(sv::kBlock);
-
-    if (timing && timing->stats_begin && hipEventRecord(timing->stats_begin, stream) != hipSuccess) return SV_EHIP;
-    if (dtype == SV_BF16)
-        sv::k_stats_tree<sv::DT_BF16><<<dim3(B * 2 * nn), blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, parents, parents_shared, nn, V,
-            c, cd, stats);
-    else
-        sv::k_stats_tree<sv::DT_F32><<<dim3(B * 2 * nn), blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, parents, parents_shared, nn, V,
-            c, cd, stats);
-    if ((rc = launch_status())) return rc;
-    if (timing && timing->stats_end && hipEventRecord(timing->stats_end, stream) != hipSuccess) return SV_EHIP;
-    if (dtype == SV_BF16)
-        sv::k_accept_tree<sv::DT_BF16><<<dim3(B), blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, node_tokens, parents,
-            parents_shared, B, T, V, max_depth, seed, round, invT, temperature, stats, seq, out_tokens,
-            out_path_nodes, out_num_accepted, out_accept, out_probs);
-    else
-        sv::k_accept_tree<sv::DT_F32><<<dim3(B), blk, 0, stream>>>(
-            zq, tgt_seq_stride, tgt_row_stride, zp, drf_seq_stride, drf_row_stride, node_tokens, parents,
-            parents_shared, B, T, V, max_depth, seed, round, invT, temperature, stats, seq, out_tokens,
-            out_path_nodes, out_num_accepted, out_accept, out_probs);
-    if ((rc = launch_status())) return rc;
-    const int width = max_depth + 1;
-    if (dtype == SV_BF16) {
-        sv::k_sample_partials<sv::DT_BF16><<<dim3(nch, B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part);
-        sv::k_sample_final<sv::DT_BF16><<<dim3(B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part, width,
-                                                                     out_tokens, out_num_accepted, out_path_nodes,
-                                                                     out_residual_mass);
-    } else {
-        sv::k_sample_partials<sv::DT_F32><<<dim3(nch, B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part);
-        sv::k_sample_final<sv::DT_F32><<<dim3(B), blk, 0, stream>>>(zq, zp, V, nch, invT, seq, part, width,
-                                                                    out_tokens, out_num_accepted, out_path_nodes,
-                                                                    out_residual_mass);
-    }
-    return launch_status();
+    sv::VerifyParams P{};
+    P.zq = static_cast<const char*>(target_logits);
+    P.zp = static_cast<const char*>(draft_logits);
+    P.qs = tgt_seq_stride;
+    P.qr = tgt_row_stride;
+    P.ps = drf_seq_stride;
+    P.pr = drf_row_stride;
+    P.tokens = node_tokens;
+    P.parents = parents;
+    P.parents_shared = parents_shared ? 1 : 0;
+    P.N = 0;
+    P.nn = nn;
+    P.max_depth = max_depth;
+    P.width = max_depth + 1;
+    fill_common(P, B, V, 2 * nn, seed, round, temperature);
+    P.out_tokens = out_tokens;
+    P.out_path = out_path_nodes;
+    P.out_num = out_num_accepted;
+    P.out_acc = out_accept;
+    P.out_probs = out_probs;
+    P.out_resid = out_residual_mass;
+    return launch_verify<true>(P, dtype, S, workspace, L, timing, stream);
 }
 
 int sv_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc, double* out_samp,
@@ -987,7 +1527,7 @@ int sv_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double
     if (blocks > INT32_MAX) return SV_ESHAPE;
     sv::k_philox_uniforms<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(seed, round, nseq, npos, out_acc,
                                                                            out_samp);
-    return launch_status();
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 }  // extern "C"

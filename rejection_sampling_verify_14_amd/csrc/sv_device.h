@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "sv_exp_table.h"
+
 namespace sv {
 
 constexpr int kBlock = 256;          // threads per block in every kernel
@@ -74,6 +76,31 @@ __device__ __forceinline__ double sample_uniform(uint64_t seed, uint64_t round, 
 }
 
 // ---------------------------------------------------------------------------
+// exp in double: Tang's table-driven method (P.T.P. Tang, "Table-driven
+// implementation of the exponential function in IEEE floating-point
+// arithmetic", ACM TOMS 15(2), 1989).  x = (32 m + j) ln2/32 + r with
+// |r| <= ln2/64; exp(x) = 2^m 2^(j/32) (1 + expm1(r)), expm1 by its Taylor
+// polynomial to r^6/720 (truncation below 4e-18).  About 1.5 ulp.  Arguments
+// below -746 (and -inf) give 0; NaN is not propagated (callers screen it).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double exp64(double x)
+{
+    x = fmax(x, -746.0);
+    const double n = rint(x * k32ByLn2);
+    const int ni = (int)n;
+    double r = fma(-n, kLn2By32Hi, x);
+    r = fma(-n, kLn2By32Lo, r);
+    double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
+    p = fma(r, p, 1.0 / 24.0);
+    p = fma(r, p, 1.0 / 6.0);
+    p = fma(r, p, 0.5);
+    p = fma(r, p, 1.0);
+    p *= r;
+    const double t = kExp2Table[ni & 31];
+    return ldexp(fma(t, p, t), ni >> 5);
+}
+
+// ---------------------------------------------------------------------------
 // Logits
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -88,6 +115,23 @@ __device__ __forceinline__ float load_logit(const char* row, int64_t t)
     } else {
         return ((const float*)row)[t];
     }
+}
+
+// 16-byte streaming load of pass-1 rows.  SV_STREAM_NT selects the
+// nontemporal hint (rows are read once by pass 1; the rows a sequence samples
+// from are re-read soon after, so the default keeps ordinary caching).
+#ifndef SV_STREAM_NT
+#define SV_STREAM_NT 0
+#endif
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 stream_load16(const uint4* p)
+{
+#if SV_STREAM_NT
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+#else
+    return *p;
+#endif
 }
 
 template <int DT>
@@ -112,55 +156,207 @@ __device__ __forceinline__ void decode16(const uint4 v, float* x)
 }
 
 // ---------------------------------------------------------------------------
-// Workspace records
+// Records passed between blocks of one launch
 // ---------------------------------------------------------------------------
-// Statistics of one logit row: s = sum_t exp((z_t - m) / T) (accumulated in
-// double) with m a reference logit no more than 64 binary orders of
-// magnitude below the row maximum (the maximum itself unless the row is
-// pathological).  lse = m / T + log(s).
-struct __align__(16) RowStat {
+// A record is a whole number of 16-byte atoms whose last word is a tag:
+// tag = epoch ^ hash(every other word), with epoch a per-call number that is
+// never 0.  Writers store the atoms with agent-coherent (sc1) 16-byte buffer
+// stores and never wait; readers load all atoms with coherent loads and take
+// the record once the tag matches what they loaded.  A record left by an
+// earlier call fails the check (its tag carries another epoch), and so does a
+// record read while its stores are still landing (the hash no longer matches
+// the mixture), so no ordering between the stores is needed.  Coherent
+// accesses go to the level shared by all XCDs: no cache-wide write-back or
+// invalidation is involved.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCpolSc1 = 16;                            // agent-coherent access
+constexpr int kCpolSc1Volatile = 16 | (int)(1u << 31);  // ... never merged or hoisted
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void put_atom(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCpolSc1);
+}
+
+__device__ __forceinline__ u32x4 get_atom(__amdgpu_buffer_rsrc_t r, uint32_t off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1Volatile);
+}
+
+// Word hash of the record tags (multiply-rotate rounds and a final avalanche).
+__device__ __forceinline__ uint32_t hash_step(uint32_t h, uint32_t w)
+{
+    h ^= w * 0x9e3779b1u;
+    h = (h << 13) | (h >> 19);
+    return h * 0x85ebca77u + 0x27d4eb2fu;
+}
+
+__device__ __forceinline__ uint32_t hash_final(uint32_t h)
+{
+    h ^= h >> 15;
+    h *= 0xc2b2ae3du;
+    h ^= h >> 13;
+    h *= 0x165667b1u;
+    return h ^ (h >> 16);
+}
+
+template <int K>
+__device__ __forceinline__ uint32_t record_tag(const u32x4* a, uint32_t epoch)
+{
+    uint32_t h = 0x6a09e667u;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        h = hash_step(h, a[i].x);
+        h = hash_step(h, a[i].y);
+        h = hash_step(h, a[i].z);
+        if (i + 1 < K) h = hash_step(h, a[i].w);
+    }
+    return epoch ^ hash_final(h);
+}
+
+template <int K>
+__device__ __forceinline__ void put_record(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4* a, uint32_t epoch)
+{
+    a[K - 1].w = record_tag<K>(a, epoch);
+#pragma unroll
+    for (int i = 0; i < K; ++i) put_atom(r, off + 16u * i, a[i]);
+}
+
+template <int K>
+__device__ __forceinline__ bool try_record(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4* a, uint32_t epoch)
+{
+#pragma unroll
+    for (int i = 0; i < K; ++i) a[i] = get_atom(r, off + 16u * i);
+    return a[K - 1].w == record_tag<K>(a, epoch);
+}
+
+__device__ __forceinline__ uint32_t lo32(double d) { return (uint32_t)__double_as_longlong(d); }
+__device__ __forceinline__ uint32_t hi32(double d) { return (uint32_t)((uint64_t)__double_as_longlong(d) >> 32); }
+__device__ __forceinline__ double d64(uint32_t lo, uint32_t hi)
+{
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Plain coherent accesses (tree paths, outputs read back by later items).
+template <typename T>
+__device__ __forceinline__ void cput(T* p, T v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename T>
+__device__ __forceinline__ T cget(const T* p)
+{
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// All of this thread's memory operations have completed.
+__device__ __forceinline__ void ops_complete() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Statistics of one segment of one logit row: s = sum_t exp((z_t - m) / T)
+// (accumulated in double) with m a reference logit at most one binary order
+// of magnitude (in units of the scaled logits) below the segment maximum.
+// One atom.
+struct RowStat {
     double s;
     float m;
-    int pad;
 };
 
-// What the sampling kernels need to know about one sequence.
-struct __align__(16) SeqState {
-    int64_t q_off;    // element offset of the q row to sample from
-    int64_t p_off;    // element offset of the p row (residual only)
-    double sq;        // pass-1 sums of the q / p rows (residual only)
-    double sp;
+// What the sampling work of one sequence needs from its accept step.  Four
+// atoms.
+struct SeqState {
+    double sq, sp;    // pass-1 sums of the q / p rows (residual only)
     double u;         // sampling uniform
-    float mq;         // pass-1 references of the q / p rows (residual only)
-    float mp;
+    float mq, mp;     // pass-1 references of the q / p rows (residual only)
     // q_t > p_t  <=>  zq_t - zp_t > theta, theta from the pass-1 statistics.
     // Tokens with zq - zp above thr_hi certainly have q > p, below thr_lo
     // certainly q < p; the band between is resolved exactly by the sampler.
-    float thr_lo;
-    float thr_hi;
+    float thr_lo, thr_hi;
     int k;            // accepted count (= slot of the sampled token)
+    int node;         // row sampled from: chain position k, tree stop node
     int status;       // 0 ok, 1 data error
     int mode;         // 0 residual, 1 bonus
-    int pad[3];
 };
-static_assert(sizeof(SeqState) == 80, "SeqState layout");
 
 // Per-chunk sums of the sampled row(s).  Residual: sa = sum a, sb = sum b
 // (a = exp((zq - mq)/T), b = exp((zp - mp)/T)); pa, pb = the same over the
 // tokens certainly in {q > p}; na, nb = over the near-threshold tokens, whose
 // smallest and largest zq - zp are dmin, dmax.  Bonus: sa = chunk maximum of
-// z, sb = sum exp((z - sa)/T), pa = 1 if the chunk holds NaN or +inf.
-struct __align__(16) ChunkSums {
+// z, sb = sum exp((z - sa)/T).  flags: bit 0 NaN/+inf in the chunk, bit 1
+// the sequence state never arrived.  Four atoms.
+struct ChunkSums {
     double sa, sb, pa, pb, na, nb;
     float dmin, dmax;
-    double pad;
+    uint32_t flags;
 };
-static_assert(sizeof(ChunkSums) == 64, "ChunkSums layout");
 
-constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk
+constexpr uint32_t kRowStatBytes = 16, kSeqStateBytes = 64, kChunkSumsBytes = 64;
 
+__device__ __forceinline__ void pack(const RowStat& v, u32x4* a)
+{
+    a[0] = u32x4{lo32(v.s), hi32(v.s), __float_as_uint(v.m), 0u};
+}
+__device__ __forceinline__ RowStat unpack_rowstat(const u32x4* a)
+{
+    return RowStat{d64(a[0].x, a[0].y), __uint_as_float(a[0].z)};
+}
+
+__device__ __forceinline__ void pack(const SeqState& v, u32x4* a)
+{
+    a[0] = u32x4{lo32(v.sq), hi32(v.sq), lo32(v.sp), hi32(v.sp)};
+    a[1] = u32x4{lo32(v.u), hi32(v.u), __float_as_uint(v.mq), __float_as_uint(v.mp)};
+    a[2] = u32x4{__float_as_uint(v.thr_lo), __float_as_uint(v.thr_hi), (uint32_t)v.k, (uint32_t)v.node};
+    a[3] = u32x4{(uint32_t)v.status, (uint32_t)v.mode, 0u, 0u};
+}
+__device__ __forceinline__ SeqState unpack_state(const u32x4* a)
+{
+    SeqState s;
+    s.sq = d64(a[0].x, a[0].y);
+    s.sp = d64(a[0].z, a[0].w);
+    s.u = d64(a[1].x, a[1].y);
+    s.mq = __uint_as_float(a[1].z);
+    s.mp = __uint_as_float(a[1].w);
+    s.thr_lo = __uint_as_float(a[2].x);
+    s.thr_hi = __uint_as_float(a[2].y);
+    s.k = (int)a[2].z;
+    s.node = (int)a[2].w;
+    s.status = (int)a[3].x;
+    s.mode = (int)a[3].y;
+    return s;
+}
+
+__device__ __forceinline__ void pack(const ChunkSums& v, u32x4* a)
+{
+    a[0] = u32x4{lo32(v.sa), hi32(v.sa), lo32(v.sb), hi32(v.sb)};
+    a[1] = u32x4{lo32(v.pa), hi32(v.pa), lo32(v.pb), hi32(v.pb)};
+    a[2] = u32x4{lo32(v.na), hi32(v.na), lo32(v.nb), hi32(v.nb)};
+    a[3] = u32x4{__float_as_uint(v.dmin), __float_as_uint(v.dmax), v.flags, 0u};
+}
+__device__ __forceinline__ ChunkSums unpack_chunk(const u32x4* a)
+{
+    ChunkSums c;
+    c.sa = d64(a[0].x, a[0].y);
+    c.sb = d64(a[0].z, a[0].w);
+    c.pa = d64(a[1].x, a[1].y);
+    c.pb = d64(a[1].z, a[1].w);
+    c.na = d64(a[2].x, a[2].y);
+    c.nb = d64(a[2].z, a[2].w);
+    c.dmin = __uint_as_float(a[3].x);
+    c.dmax = __uint_as_float(a[3].y);
+    c.flags = a[3].z;
+    return c;
+}
+
+constexpr uint32_t kFlagBad = 1u;
+constexpr uint32_t kFlagTimeout = 2u;
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
+constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk
 
 // ---------------------------------------------------------------------------
 // Reductions (wave64 via shuffles, block via LDS)
@@ -192,6 +388,29 @@ __device__ __forceinline__ double block_sum(double v, double* red)
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) t += red[w];
     return t;
+}
+
+// Sum of K doubles over the block in one LDS round trip; results valid in
+// every thread.  `red` holds kWaves * K doubles.
+template <int K>
+__device__ __forceinline__ void block_sum_n(double* v, double* red)
+{
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = wave_sum(v[i]);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) red[wave * K + i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        double t = 0.0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) t += red[w * K + i];
+        v[i] = t;
+    }
 }
 
 __device__ __forceinline__ float block_max(float v, float* red)
