@@ -401,17 +401,19 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
 // the row (z <= m + T ln 2); otherwise, and for fp32 logits, it is computed.
 struct ExpRow {
     const double* tab;
+    const double* t32;  // 2^(j/32) for the computed path
     double m, scale, invT;
     __device__ __forceinline__ double operator()(float z) const
     {
         if (tab) return tab[__float_as_uint(z) >> 16] * scale;
-        return exp64(((double)z - m) * invT);
+        return exp64(((double)z - m) * invT, t32);
     }
 };
 
-__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m)
+__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* t32)
 {
     ExpRow e;
+    e.t32 = t32;
     e.m = m;
     e.invT = P.invT;
     const double t = m * P.invT;
@@ -664,67 +666,268 @@ __device__ __forceinline__ const char* sample_prow(const VerifyParams& P, int b,
     return prow_ptr<DT>(P, b, node);
 }
 
-// Chunk sums of the row(s) a sequence samples from (see ChunkSums).
+// A wave's view of a chunk: lane `lane` owns the 16-byte vectors
+// lane + 64*k, k < kChunk / (64 * elements per vector), so each load
+// instruction of the wave reads 1 KB of consecutive bytes.  A chunk takes
+// the vector path when its row is 16-byte aligned and it ends at or before V
+// (every chunk but possibly the last); otherwise its tokens are read one by
+// one (-inf past V).
 template <int DT>
-__device__ ChunkSums chunk_sums(const VerifyParams& P, int b, const SeqState& s, int c)
+__device__ __forceinline__ bool chunk_vectors(const char* row, int V, int c)
 {
-    __shared__ float redf[kWaves];
-    float xq[kPerThread];
-    load_chunk16<DT>(sample_qrow<DT>(P, b, s), P.V, c, threadIdx.x, xq);
-    ChunkSums out{};
-    if (s.mode == kModeResidual) {
-        float xp[kPerThread];
-        load_chunk16<DT>(sample_prow<DT>(P, b, s), P.V, c, threadIdx.x, xp);
-        double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sa sb pa pb na nb
-        float dmin = INFINITY, dmax = -INFINITY;
-        const ExpRow eq = exp_row(P, s.mq), ep = exp_row(P, s.mp);
+    return (((uintptr_t)row) & 15u) == 0 && (int64_t)(c + 1) * kChunk <= V;
+}
+
+constexpr int kLaneBatch = 4;  // 16-byte vectors a lane loads at once
+
+// The lane's h-th batch of vectors of chunk c.
+template <int DT>
+__device__ __forceinline__ void load_chunk_half(const char* __restrict__ row, int c, int h, int lane, uint4* raw)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    const uint4* v = reinterpret_cast<const uint4*>(row + (int64_t)c * kChunk * elem_bytes<DT>());
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            const double a = eq(xq[j]);
-            const double bb = ep(xp[j]);
-            acc[0] += a;
-            acc[1] += bb;
-            const float d = xq[j] - xp[j];
-            if (d > s.thr_hi) {
-                acc[2] += a;
-                acc[3] += bb;
-            } else if (d >= s.thr_lo) {
-                acc[4] += a;
-                acc[5] += bb;
-                dmin = fminf(dmin, d);
-                dmax = fmaxf(dmax, d);
+    for (int j = 0; j < kLaneBatch; ++j) raw[j] = v[lane + 64 * (kLaneBatch * h + j)];
+    (void)EPV;
+}
+
+// Token t of the lane's share in the element-by-element path.
+template <int DT>
+__device__ __forceinline__ float chunk_token(const char* row, int V, int c, int lane, int k, int i)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    const int64_t e = (int64_t)c * kChunk + (int64_t)(lane + 64 * k) * EPV + i;
+    return e < V ? load_logit<DT>(row, e) : -INFINITY;
+}
+
+// exp((z - m)/T) of one row with the evaluation method fixed at compile time
+// (TAB: ExpRow's table, else the fp64 routine).
+template <bool TAB>
+__device__ __forceinline__ double exp_of(const ExpRow& e, float z)
+{
+    if constexpr (TAB) return e.tab[__float_as_uint(z) >> 16] * e.scale;
+    else return exp64(((double)z - e.m) * e.invT, e.t32);
+}
+
+template <bool TAB>
+__device__ __forceinline__ void residual_token(float zq, float zp, const SeqState& s, const ExpRow& eq,
+                                               const ExpRow& ep, double* acc, float& dmin, float& dmax)
+{
+    const double a = exp_of<TAB>(eq, zq);
+    const double bb = exp_of<TAB>(ep, zp);
+    acc[0] += a;
+    acc[1] += bb;
+    const float d = zq - zp;
+    const bool above = d > s.thr_hi;
+    const bool near = !above && d >= s.thr_lo;
+    acc[2] += above ? a : 0.0;
+    acc[3] += above ? bb : 0.0;
+    acc[4] += near ? a : 0.0;
+    acc[5] += near ? bb : 0.0;
+    dmin = near ? fminf(dmin, d) : dmin;
+    dmax = near ? fmaxf(dmax, d) : dmax;
+}
+
+template <int DT, bool TAB>
+__device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
+                                               const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
+                                               double* acc, float& dmin, float& dmax)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 8, fp32 16
+    const int lane = threadIdx.x & 63;
+    if (chunk_vectors<DT>(qrow, P.V, c) && chunk_vectors<DT>(prow, P.V, c)) {
+#pragma unroll 1
+        for (int h = 0; h < PER / kLaneBatch; ++h) {
+            uint4 rq[kLaneBatch], rp[kLaneBatch];
+            load_chunk_half<DT>(qrow, c, h, lane, rq);
+            load_chunk_half<DT>(prow, c, h, lane, rp);
+#pragma unroll
+            for (int j = 0; j < kLaneBatch; ++j) {
+                float xq[EPV], xp[EPV];
+                decode16<DT>(rq[j], xq);
+                decode16<DT>(rp[j], xp);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) residual_token<TAB>(xq[i], xp[i], s, eq, ep, acc, dmin, dmax);
+                __builtin_amdgcn_sched_barrier(0);  // one vector's exps at a time
             }
         }
-        __shared__ double red6[kWaves * 6];
-        block_sum_n<6>(acc, red6);
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < PER; ++k)
+#pragma unroll 1
+            for (int i = 0; i < EPV; ++i)
+                residual_token<TAB>(chunk_token<DT>(qrow, P.V, c, lane, k, i), chunk_token<DT>(prow, P.V, c, lane, k, i),
+                                    s, eq, ep, acc, dmin, dmax);
+    }
+}
+
+// Maximum and NaN/+inf flag of the lane's tokens of a chunk.
+template <int DT>
+__device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qrow, int c, float& lm, int& bad)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int PER = kChunk / EPV / 64;
+    const int lane = threadIdx.x & 63;
+    auto take = [&](float x) {
+        lm = fmaxf(lm, x);
+        bad |= (x != x) || (x == INFINITY);
+    };
+    if (chunk_vectors<DT>(qrow, P.V, c)) {
+#pragma unroll 1
+        for (int h = 0; h < PER / kLaneBatch; ++h) {
+            uint4 rq[kLaneBatch];
+            load_chunk_half<DT>(qrow, c, h, lane, rq);
+#pragma unroll
+            for (int j = 0; j < kLaneBatch; ++j) {
+                float x[EPV];
+                decode16<DT>(rq[j], x);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) take(x[i]);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < PER; ++k)
+#pragma unroll 1
+            for (int i = 0; i < EPV; ++i) take(chunk_token<DT>(qrow, P.V, c, lane, k, i));
+    }
+}
+
+template <int DT, bool TAB>
+__device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* qrow, int c, const ExpRow& ec)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int PER = kChunk / EPV / 64;
+    const int lane = threadIdx.x & 63;
+    double sa = 0.0;
+    if (chunk_vectors<DT>(qrow, P.V, c)) {
+#pragma unroll 1
+        for (int h = 0; h < PER / kLaneBatch; ++h) {
+            uint4 rq[kLaneBatch];
+            load_chunk_half<DT>(qrow, c, h, lane, rq);
+#pragma unroll
+            for (int j = 0; j < kLaneBatch; ++j) {
+                float x[EPV];
+                decode16<DT>(rq[j], x);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) sa += exp_of<TAB>(ec, x[i]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < PER; ++k)
+#pragma unroll 1
+            for (int i = 0; i < EPV; ++i) sa += exp_of<TAB>(ec, chunk_token<DT>(qrow, P.V, c, lane, k, i));
+    }
+    return sa;
+}
+
+// Residual chunk sums of the whole chunks [ca, cb) of 16-byte aligned rows,
+// by one wave, stored as records: the loads of the next batch are issued
+// before the current batch is used, across chunk boundaries.
+template <int DT, bool TAB>
+__device__ void residual_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+                               int ca, int cb, const ExpRow& eq, const ExpRow& ep)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int NB = kChunk / EPV / 64 / kLaneBatch;  // batches per chunk: bf16 1, fp32 2
+    const int lane = threadIdx.x & 63;
+    const uint4* vq = reinterpret_cast<const uint4*>(qrow);
+    const uint4* vp = reinterpret_cast<const uint4*>(prow);
+    auto vec = [&](int t, int j) -> int64_t {
+        return (int64_t)(t / NB) * (kChunk / EPV) + 64 * (kLaneBatch * (t % NB) + j) + lane;
+    };
+    const int tend = cb * NB;
+    int t = ca * NB;
+    if (t >= tend) return;
+    uint4 cq[kLaneBatch], cp[kLaneBatch];
+#pragma unroll
+    for (int j = 0; j < kLaneBatch; ++j) {
+        cq[j] = vq[vec(t, j)];
+        cp[j] = vp[vec(t, j)];
+    }
+    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    float dmin = INFINITY, dmax = -INFINITY;
+    for (; t < tend; ++t) {
+        uint4 nq[kLaneBatch], np[kLaneBatch];
+        if (t + 1 < tend) {
+#pragma unroll
+            for (int j = 0; j < kLaneBatch; ++j) {
+                nq[j] = vq[vec(t + 1, j)];
+                np[j] = vp[vec(t + 1, j)];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kLaneBatch; ++j) {
+            float xq[EPV], xp[EPV];
+            decode16<DT>(cq[j], xq);
+            decode16<DT>(cp[j], xp);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) residual_token<TAB>(xq[i], xp[i], s, eq, ep, acc, dmin, dmax);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if ((t + 1) % NB == 0) {
+            ChunkSums out{};
+            out.sa = wave_sum(acc[0]);
+            out.sb = wave_sum(acc[1]);
+            out.pa = wave_sum(acc[2]);
+            out.pb = wave_sum(acc[3]);
+            out.na = wave_sum(acc[4]);
+            out.nb = wave_sum(acc[5]);
+            out.dmax = wave_max(dmax);
+            out.dmin = -wave_max(-dmin);
+            if (lane == 0) put_chunk(P, b, t / NB, out);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) acc[i] = 0.0;
+            dmin = INFINITY;
+            dmax = -INFINITY;
+        }
+#pragma unroll
+        for (int j = 0; j < kLaneBatch; ++j) {
+            cq[j] = nq[j];
+            cp[j] = np[j];
+        }
+    }
+}
+
+// Chunk sums of the row(s) a sequence samples from (see ChunkSums), by one
+// wave; valid in every lane.
+template <int DT>
+__device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, const char* qrow, const char* prow,
+                                     int c, const ExpRow& eq, const ExpRow& ep, const double* t32)
+{
+    ChunkSums out{};
+    if (s.mode == kModeResidual) {
+        double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sa sb pa pb na nb
+        float dmin = INFINITY, dmax = -INFINITY;
+        if (eq.tab && ep.tab) residual_chunk<DT, true>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
+        else residual_chunk<DT, false>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) acc[i] = wave_sum(acc[i]);
         out.sa = acc[0];
         out.sb = acc[1];
         out.pa = acc[2];
         out.pb = acc[3];
         out.na = acc[4];
         out.nb = acc[5];
-        out.dmax = block_max(dmax, redf);
-        out.dmin = -block_max(-dmin, redf);
+        out.dmax = wave_max(dmax);
+        out.dmin = -wave_max(-dmin);
     } else {
+        // the chunk maximum first, then the sum relative to it
         float lm = -INFINITY;
         int bad = 0;
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            lm = fmaxf(lm, xq[j]);
-            bad |= (xq[j] != xq[j]) || (xq[j] == INFINITY);
-        }
-        const float mc = block_max(lm, redf);
-        double sa[1] = {0.0};
+        bonus_max<DT>(P, qrow, c, lm, bad);
+        const float mc = wave_max(lm);
+        double sa = 0.0;
         if (mc != -INFINITY) {
-            const ExpRow ec = exp_row(P, mc);
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) sa[0] += ec(xq[j]);
+            const ExpRow ec = exp_row(P, mc, t32);
+            sa = ec.tab ? bonus_sum<DT, true>(P, qrow, c, ec) : bonus_sum<DT, false>(P, qrow, c, ec);
         }
-        __shared__ double red1[kWaves];
-        block_sum_n<1>(sa, red1);
         out.sa = (double)mc;
-        out.sb = sa[0];
-        out.flags = __syncthreads_or(bad) ? kFlagBad : 0u;
+        out.sb = wave_sum(sa);
+        out.flags = __any(bad) ? kFlagBad : 0u;
     }
     return out;
 }
@@ -801,7 +1004,8 @@ __device__ void emit(const VerifyParams& P, int b, int k, int token, double resi
 // Final step of sequence b: wait for its chunks, totals, chunk location,
 // rescan, outputs.
 template <int DT, bool TREE>
-__device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path)
+__device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path,
+                             const double* t32)
 {
     const int tid = threadIdx.x;
     const int nchunks = P.nch;
@@ -827,7 +1031,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     const int c1 = min(nchunks, c0 + g);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq), ep = exp_row(P, s.mp);
+    const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
 
     // --- totals ---
     double rho = 0.0, M = 0.0, resid_mass = 0.0;
@@ -953,7 +1157,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         mc = get_chunk(P, b, cs).sa;
         scale = exp((mc - M) * invT);
     }
-    const ExpRow ec = exp_row(P, mc);
+    const ExpRow ec = exp_row(P, mc, t32);
     auto weight = [&](int j) -> double {
         const int i = tid * kPerThread + j;
         const float a = s_q.get(i);
@@ -1012,6 +1216,10 @@ constexpr int kRowBatch = SV_ROW_BATCH;
 // Exp table for bf16 logits in the sample kernel (0 computes every exp)
 #ifndef SV_EXP_TABLE
 #define SV_EXP_TABLE 1
+#endif
+// The 32-entry table of the computed exp read from LDS (1) or constant memory
+#ifndef SV_EXP_T32_LDS
+#define SV_EXP_T32_LDS 1
 #endif
 constexpr int kTablePerBlock = 1024;  // exp-table entries per table block
 
@@ -1148,6 +1356,13 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     const int g = (int)blockIdx.x - b * P.groups;
     __shared__ SeqState s_state;
     __shared__ int32_t s_path[kMaxNodes];
+    __shared__ double s_t32[32];
+    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
+#if SV_EXP_T32_LDS
+    const double* t32 = s_t32;
+#else
+    const double* t32 = kExp2Table;
+#endif
     if constexpr (TREE) {
         tree_accept<DT>(P, b, s_state, s_path, g == 0);
     } else {
@@ -1156,15 +1371,33 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     __syncthreads();
     const SeqState s = s_state;
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
-    for (int c = c0; c < c1; ++c) {
-        ChunkSums out{};
-        if (s.status == 0) out = chunk_sums<DT>(P, b, s, c);
-        if (threadIdx.x == 0) put_chunk(P, b, c, out);
+    const char* qrow = sample_qrow<DT>(P, b, s);
+    const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
+    const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
+    // each wave takes a contiguous share of the block's chunks; whole chunks
+    // of aligned rows stream with loads in flight across chunk boundaries
+    const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+    const int wave = (int)threadIdx.x >> 6;
+    const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+    int c = ca;
+    if (s.status == 0 && s.mode == kModeResidual && ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
+        const int whole = min(cb, P.V / kChunk);
+        if (whole > c) {
+            if (eq.tab && ep.tab) residual_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+            else residual_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            c = whole;
+        }
     }
+    for (; c < cb; ++c) {
+        ChunkSums out{};
+        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, t32);
+        if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
+    }
+    __syncthreads();
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
     __syncthreads();
-    if (s_last) sample_final<DT, TREE>(P, b, s, s_path);
+    if (s_last) sample_final<DT, TREE>(P, b, s, s_path, t32);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -1204,7 +1437,6 @@ void segments_of(int V, int* segs, int* seg_len)
 
 constexpr int kTableEntries = 65536;
 constexpr int64_t kWaveMinElems = 32768;  // smallest range worth a wave of the chain row kernel
-constexpr int kSampleBlocksTarget = 1024;   // sample blocks aimed at per call
 
 // Blocks of a kernel the device holds at once (compute units x occupancy).
 template <typename K>
@@ -1317,9 +1549,23 @@ uint32_t next_epoch()
     return e;
 }
 
+// Sample blocks per sequence: enough for one round of the blocks the device
+// holds at once (a block's four waves share its chunks).
 template <int DT, bool TREE>
-int launch_kernels(const sv::VerifyParams& P, int stream_grid, const sv_timing* timing, hipStream_t stream)
+void set_groups(sv::VerifyParams& P)
 {
+    static std::atomic<int> cache{0};
+    const int resident = resident_blocks(&sv::k_sample<DT, TREE>, cache);
+    int groups = resident > 0 ? resident / (P.B > 0 ? P.B : 1) : 1;
+    groups = groups < 1 ? 1 : (groups > P.nch ? P.nch : groups);
+    P.cpb = (P.nch + groups - 1) / groups;
+    P.groups = (P.nch + P.cpb - 1) / P.cpb;
+}
+
+template <int DT, bool TREE>
+int launch_kernels(sv::VerifyParams& P, int stream_grid, const sv_timing* timing, hipStream_t stream)
+{
+    set_groups<DT, TREE>(P);
     const int64_t row_grid = TREE ? (int64_t)P.B * P.r_items : stream_grid;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     if (timing && timing->stats_begin && hipEventRecord(timing->stats_begin, stream) != hipSuccess) return SV_EHIP;
@@ -1364,9 +1610,6 @@ void fill_common(sv::VerifyParams& P, int B, int V, int rows, uint64_t seed, uin
     segments_of(V, &P.segs, &P.seg_len);
     P.r_items = rows * P.segs;
     P.nch = nchunks_of(V);
-    int64_t cpb = ((int64_t)P.nch * B + kSampleBlocksTarget - 1) / kSampleBlocksTarget;
-    P.cpb = (int)(cpb < 1 ? 1 : (cpb > P.nch ? P.nch : cpb));
-    P.groups = (P.nch + P.cpb - 1) / P.cpb;
     P.seed = seed;
     P.round = round;
     P.T = temperature;

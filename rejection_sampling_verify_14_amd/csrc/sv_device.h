@@ -12,7 +12,7 @@ namespace sv {
 
 constexpr int kBlock = 256;          // threads per block in every kernel
 constexpr int kWaves = kBlock / 64;  // wave64
-constexpr int kChunk = 4096;         // elements per sampling chunk (16 per thread)
+constexpr int kChunk = 2048;         // elements per sampling chunk (8 per thread)
 constexpr int kPerThread = kChunk / kBlock;
 constexpr int DT_F32 = 0;
 constexpr int DT_BF16 = 1;
@@ -80,10 +80,11 @@ __device__ __forceinline__ double sample_uniform(uint64_t seed, uint64_t round, 
 // implementation of the exponential function in IEEE floating-point
 // arithmetic", ACM TOMS 15(2), 1989).  x = (32 m + j) ln2/32 + r with
 // |r| <= ln2/64; exp(x) = 2^m 2^(j/32) (1 + expm1(r)), expm1 by its Taylor
-// polynomial to r^6/720 (truncation below 4e-18).  About 1.5 ulp.  Arguments
+// polynomial to r^6/720 (truncation below 4e-18).  About 1.5 ulp.  `tab`
+// holds the 32 values 2^(j/32) (kExp2Table, or a copy in LDS).  Arguments
 // below -746 (and -inf) give 0; NaN is not propagated (callers screen it).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double exp64(double x)
+__device__ __forceinline__ double exp64(double x, const double* __restrict__ tab)
 {
     x = fmax(x, -746.0);
     const double n = rint(x * k32ByLn2);
@@ -96,9 +97,12 @@ __device__ __forceinline__ double exp64(double x)
     p = fma(r, p, 0.5);
     p = fma(r, p, 1.0);
     p *= r;
-    const double t = kExp2Table[ni & 31];
+    const double t = tab[ni & 31];
     return ldexp(fma(t, p, t), ni >> 5);
 }
+
+// exp64 with the 2^(j/32) table read from constant memory.
+__device__ __forceinline__ double exp64(double x) { return exp64(x, kExp2Table); }
 
 // ---------------------------------------------------------------------------
 // Logits
@@ -152,6 +156,19 @@ __device__ __forceinline__ void decode16(const uint4 v, float* x)
     } else {
         x[0] = __uint_as_float(v.x); x[1] = __uint_as_float(v.y);
         x[2] = __uint_as_float(v.z); x[3] = __uint_as_float(v.w);
+    }
+}
+
+// Inverse of decode16 for values that are exactly representable (bf16 values
+// decoded from bf16 storage, or -inf).
+template <int DT>
+__device__ __forceinline__ uint4 encode16(const float* x)
+{
+    if constexpr (DT == DT_BF16) {
+        auto w = [&](int k) { return (__float_as_uint(x[2 * k]) >> 16) | (__float_as_uint(x[2 * k + 1]) & 0xFFFF0000u); };
+        return make_uint4(w(0), w(1), w(2), w(3));
+    } else {
+        return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]), __float_as_uint(x[3]));
     }
 }
 
