@@ -70,13 +70,14 @@ enum sv_status {
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
-/* Optional timing hook: when non-NULL, `stats_begin` and `stats_end` are
- * recorded on `stream` right before and right after the verify kernel (the
- * one launch that streams the logit rows and samples), so a caller can time
- * it. */
+/* Optional timing hook: when non-NULL, each non-NULL event is recorded on
+ * `stream`: `begin` right before the row-statistics kernel, `rows_done`
+ * between it and the accept/sampling kernel, `end` right after the latter,
+ * so a caller can time each kernel. */
 typedef struct sv_timing {
-    hipEvent_t stats_begin;
-    hipEvent_t stats_end;
+    hipEvent_t begin;
+    hipEvent_t rows_done;
+    hipEvent_t end;
 } sv_timing;
 
 /* ABI version (incremented on any signature change). */

@@ -39,7 +39,7 @@ class SpecVerifyError(RuntimeError):
 
 
 class SvTiming(ctypes.Structure):
-    _fields_ = [("stats_begin", ctypes.c_void_p), ("stats_end", ctypes.c_void_p)]
+    _fields_ = [("begin", ctypes.c_void_p), ("rows_done", ctypes.c_void_p), ("end", ctypes.c_void_p)]
 
 
 _L = None
@@ -71,7 +71,7 @@ def _lib():
         L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
         L.sv_philox_uniforms.restype = i32
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
-        if L.sv_abi_version() != 1:
+        if L.sv_abi_version() != 2:
             raise ImportError("libspecverify.so ABI version mismatch")
         _L = L
     return _L
@@ -107,9 +107,13 @@ def _check_logits(t: torch.Tensor, name: str):
 
 
 def _timing(timing):
+    """(begin, end) or (begin, rows_done, end) hipEvent_t handles, or None."""
     if timing is None:
         return None
-    t = SvTiming(timing[0], timing[1])
+    if len(timing) == 2:
+        t = SvTiming(timing[0], None, timing[1])
+    else:
+        t = SvTiming(timing[0], timing[1], timing[2])
     return ctypes.byref(t)
 
 

@@ -1568,16 +1568,17 @@ int launch_kernels(sv::VerifyParams& P, int stream_grid, const sv_timing* timing
     set_groups<DT, TREE>(P);
     const int64_t row_grid = TREE ? (int64_t)P.B * P.r_items : stream_grid;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
-    if (timing && timing->stats_begin && hipEventRecord(timing->stats_begin, stream) != hipSuccess) return SV_EHIP;
+    if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
     if (row_grid > 0) {
         if (TREE)
             hipLaunchKernelGGL((sv::k_rows<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
         else
             hipLaunchKernelGGL((sv::k_stream<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
     }
+    if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL((sv::k_sample<DT, TREE>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (timing && timing->stats_end && hipEventRecord(timing->stats_end, stream) != hipSuccess) return SV_EHIP;
+    if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -1630,7 +1631,7 @@ bool item_count_ok(int B, int rows, int V)
 
 extern "C" {
 
-int sv_abi_version(void) { return 1; }
+int sv_abi_version(void) { return 2; }
 
 const char* sv_status_string(int status)
 {
