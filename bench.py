@@ -33,7 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k_stream_c3_pmc.json")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_rows_c3_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
                   for f in ("specverify.hip", "sv_device.h")]
 
@@ -293,7 +293,7 @@ def main():
         "algorithmic_bytes_per_step": int(full_bytes),
         "mean_accepted": round(float(acc[acc >= 0].mean()), 4),
         "roofline": {
-            "kernel": "k_stream (row statistics)" if w.kind == "chain" else "k_rows (row statistics)",
+            "kernel": "k_rows (row statistics)",
             "bound": "hbm",
             "achieved": round(k_gbps, 1),
             "peak": PEAK_HBM_GBPS,

@@ -91,10 +91,17 @@ __device__ __forceinline__ void combine_stat(float& m, double& s, float m2, doub
     m = M;
 }
 
-// One batch of U 16-byte vectors per thread (vectors past the end carry
-// -inf): the reference moves first if the batch's maximum calls for it, then
-// the terms are summed in fp32 groups of (at most) 32 and added to the
-// double accumulator.
+// One batch of U 16-byte vectors per lane (vectors past the end carry -inf),
+// in fp32 groups of (at most) 32 terms exp2((x - ref) * c) added to the double
+// accumulator.  The reference is the same in every lane of the wave.  When a
+// group sum of any lane exceeds kGroupLimit (so a term exceeds it: an element
+// more than three binary orders of magnitude, in units of the scaled logits,
+// above the reference), is not finite, or comes before any reference exists,
+// the reference moves to the wave's maximum of the group and the group is
+// summed again; so the dominant terms keep exponent arguments below 3, where
+// the fp32 rounding of (x - ref) * c stays small.
+constexpr float kGroupLimit = 8.0f;
+
 template <int DT, int U>
 __device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, double cd, float& ref, double& acc)
 {
@@ -102,35 +109,54 @@ __device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, doub
     constexpr int GE = (U * EPV < 32) ? U * EPV : 32;  // elements per fp32 group
     constexpr int G = GE / EPV;                          // vectors per group
     static_assert(U % G == 0, "batch must hold whole groups");
-    float lm = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float x[EPV];
-        decode16<DT>(raw[u], x);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
-    }
-    if ((lm - ref) * c > 1.0f) {
-        acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
-        ref = lm;
-    }
-    const float r = (ref == -INFINITY) ? 0.0f : ref;
 #pragma unroll
     for (int g = 0; g < U / G; ++g) {
-        float e[GE];
+        auto group_sum = [&](float r) {
+            float e[GE];
 #pragma unroll
-        for (int u = 0; u < G; ++u) {
-            float x[EPV];
-            decode16<DT>(raw[g * G + u], x);
+            for (int u = 0; u < G; ++u) {
+                float x[EPV];
+                decode16<DT>(raw[g * G + u], x);
 #pragma unroll
-            for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f((x[i] - r) * c);
+                for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f((x[i] - r) * c);
+            }
+#pragma unroll
+            for (int w = 1; w < GE; w <<= 1) {
+#pragma unroll
+                for (int i = 0; i + w < GE; i += 2 * w) e[i] += e[i + w];
+            }
+            return e[0];
+        };
+        if (ref == -INFINITY) {
+            // no reference yet (uniform across the wave): take the group maximum
+            float lm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                float x[EPV];
+                decode16<DT>(raw[g * G + u], x);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
+            }
+            ref = wave_max(lm);
         }
+        float s = (ref == -INFINITY) ? 0.0f : group_sum(ref);
+        if (__any(!(s <= kGroupLimit))) {
+            float lm = -INFINITY;
 #pragma unroll
-        for (int w = 1; w < GE; w <<= 1) {
+            for (int u = 0; u < G; ++u) {
+                float x[EPV];
+                decode16<DT>(raw[g * G + u], x);
 #pragma unroll
-            for (int i = 0; i + w < GE; i += 2 * w) e[i] += e[i + w];
+                for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
+            }
+            lm = wave_max(lm);
+            if (lm > ref) {
+                acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
+                ref = lm;
+            }
+            s = (ref == -INFINITY) ? 0.0f : group_sum(ref);
         }
-        acc += (double)e[0];
+        acc += (double)s;
     }
 }
 
@@ -157,9 +183,13 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     double acc = 0.0;
     int head = (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
     head = head < n ? head : n;
+    // head and tail elements go to a per-lane accumulator of their own (the
+    // batch reference is wave-uniform)
+    float ref1 = -INFINITY;
+    double acc1 = 0.0;
     if ((int)threadIdx.x < head) {
         float x[1] = {load_logit<DT>(row, threadIdx.x)};
-        accumulate_values<1>(x, c, cd, ref, acc);
+        accumulate_values<1>(x, c, cd, ref1, acc1);
     }
     row += head * EB;
     n -= head;
@@ -186,8 +216,9 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     const int tail = n - nvec * EPV;
     if ((int)threadIdx.x < tail) {
         float x[1] = {load_logit<DT>(row, (int64_t)nvec * EPV + threadIdx.x)};
-        accumulate_values<1>(x, c, cd, ref, acc);
+        accumulate_values<1>(x, c, cd, ref1, acc1);
     }
+    combine_stat(ref, acc, ref1, acc1, cd);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
         const float m2 = __shfl_xor(ref, off, 64);
@@ -230,19 +261,15 @@ struct VerifyParams {
     int max_depth, width;     // output row width (chain N+1, tree max_depth+1)
     int rows;                 // pass-1 rows per sequence (chain 2N, tree 2 nn)
     int segs, seg_len;        // segments per row, elements per segment
-    int r_items, nch;         // row blocks per sequence (trees), sample chunks per sequence
+    int r_items, nch;         // row blocks per sequence (rows x segs), sample chunks per sequence
     int cpb, groups;          // sample chunks per block, sample blocks per sequence
-    // chains: pass-1 rows flattened (row-major, V elements each) and cut into
-    // W equal wave ranges at multiples of 64 elements
-    int64_t E, E64;           // elements, ceil(E / 64)
-    int W, MP;                // waves, record slots per row
     uint64_t seed, round;
     float T, c;               // temperature, log2(e)/T
     double cd, invT;
     uint32_t epoch;
     // workspace
     uint64_t* chunk_arrivals; // [B] epoch-tagged arrival counters of the sample blocks
-    char* stats;              // [B * rows][MP] RowStat records (row kernel -> sample kernel)
+    char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
     uint32_t stats_bytes, part_bytes;
     double* table;            // [65536] exp(z/T) per bf16 bit pattern, or null
@@ -311,24 +338,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t part_rsrc(const VerifyParams& 
 
 __device__ __forceinline__ uint32_t stat_off(const VerifyParams& P, int64_t grow, int slot)
 {
-    return (uint32_t)((grow * P.MP + slot) * kRowStatBytes);
-}
-
-// First element of wave w's range of the flattened pass-1 rows (chains).
-__device__ __forceinline__ int64_t wave_begin(const VerifyParams& P, int w)
-{
-    if (w >= P.W) return P.E;
-    const int64_t e = 64 * ((int64_t)w * P.E64 / P.W);
-    return e < P.E ? e : P.E;
-}
-
-// The wave whose range holds element e (the last wave starting at or before
-// e: empty ranges in between are skipped).
-__device__ __forceinline__ int wave_of(const VerifyParams& P, int64_t e)
-{
-    const int64_t k = e / 64;
-    const int64_t w = ((k + 1) * P.W + P.E64 - 1) / P.E64 - 1;
-    return (int)(w < P.W - 1 ? w : P.W - 1);
+    return (uint32_t)((grow * P.segs + slot) * kRowStatBytes);
 }
 
 __device__ __forceinline__ uint32_t chunk_off(const VerifyParams& P, int b, int c)
@@ -353,27 +363,16 @@ __device__ __forceinline__ ChunkSums get_chunk(const VerifyParams& P, int b, int
     return unpack_chunk(a);
 }
 
-// Statistics of pass-1 row `row` of sequence b from its records: for chains
-// the pieces that wave ranges cut it into, for trees its segments.  A record
-// that is not this call's (never expected) poisons the result.
+// Statistics of pass-1 row `row` of sequence b from the records of its
+// segments.  A record that is not this call's (never expected) poisons the
+// result.
 __device__ __forceinline__ RowStat load_row_stat(const VerifyParams& P, int b, int row)
 {
     const __amdgpu_buffer_rsrc_t r = stats_rsrc(P);
     const int64_t grow = (int64_t)b * P.rows + row;
-    int n = P.segs, w0 = 0;
-    if (P.W > 0) {
-        const int64_t e0 = grow * P.V, e1 = e0 + P.V;
-        w0 = wave_of(P, e0);
-        n = wave_of(P, e1 - 1) - w0 + 1;
-    }
     RowStat acc{0.0, -INFINITY};
     bool ok = true;
-    for (int i = 0; i < n; ++i) {
-        if (P.W > 0) {
-            // skip waves whose (empty) range holds none of the row
-            const int64_t lo = wave_begin(P, w0 + i), hi = wave_begin(P, w0 + i + 1);
-            if (hi <= lo) continue;
-        }
+    for (int i = 0; i < P.segs; ++i) {
         u32x4 a[1];
         ok &= try_record<1>(r, stat_off(P, grow, i), a, P.epoch);
         const RowStat x = unpack_rowstat(a);
@@ -1210,7 +1209,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
 // ===========================================================================
 // 16-byte loads per thread per batch of a row block
 #ifndef SV_ROW_BATCH
-#define SV_ROW_BATCH 8
+#define SV_ROW_BATCH 4
 #endif
 constexpr int kRowBatch = SV_ROW_BATCH;
 // Exp table for bf16 logits in the sample kernel (0 computes every exp)
@@ -1221,7 +1220,6 @@ constexpr int kRowBatch = SV_ROW_BATCH;
 #ifndef SV_EXP_T32_LDS
 #define SV_EXP_T32_LDS 1
 #endif
-constexpr int kTablePerBlock = 1024;  // exp-table entries per table block
 
 // Share of the exp table (exp(v/T) for every bf16 bit pattern v, used by
 // ExpRow) filled by this block of a grid of `nblocks`.
@@ -1234,104 +1232,33 @@ __device__ __forceinline__ void fill_table_share(const VerifyParams& P, int blk,
     }
 }
 
-// (m, s) of n consecutive elements starting at `row`, by one wave (valid in
-// every lane): scalar head up to the first 16-byte boundary, 16-byte vectors
-// in batches of U per lane with the next batch issued before the current one
-// is used (the last padded with -inf), scalar tail.
-template <int DT, int U>
-__device__ __forceinline__ RowStat wave_row_stats(const char* __restrict__ row, int64_t n, float c, double cd)
-{
-    constexpr int EB = elem_bytes<DT>();
-    constexpr int EPV = 16 / EB;
-    const int lane = threadIdx.x & 63;
-    float ref = -INFINITY;
-    double acc = 0.0;
-    int64_t head = (int64_t)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
-    head = head < n ? head : n;
-    if (lane < head) {
-        float x[1] = {load_logit<DT>(row, lane)};
-        accumulate_values<1>(x, c, cd, ref, acc);
-    }
-    row += head * EB;
-    n -= head;
-    const int64_t nvec = n / EPV;
-    const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
-    const int64_t nbatch = (nvec + U * 64 - 1) / (U * 64);
-    int64_t v = lane;
-    uint4 cur[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = (v + u * 64 < nvec) ? stream_load16(vrow + v + u * 64) : neg_inf16<DT>();
-    for (int64_t bt = 0; bt < nbatch; ++bt) {
-        const int64_t nv = v + U * 64;
-        uint4 nxt[U];
-        if (bt + 1 < nbatch) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                nxt[u] = (nv + u * 64 < nvec) ? stream_load16(vrow + nv + u * 64) : neg_inf16<DT>();
-        }
-        accumulate_batch<DT, U>(cur, c, cd, ref, acc);
-        v = nv;
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    }
-    const int64_t tail = n - nvec * EPV;
-    if (lane < tail) {
-        float x[1] = {load_logit<DT>(row, nvec * EPV + lane)};
-        accumulate_values<1>(x, c, cd, ref, acc);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float m2 = __shfl_xor(ref, off, 64);
-        const double s2 = __shfl_xor(acc, off, 64);
-        combine_stat(ref, acc, m2, s2, cd);
-    }
-    return RowStat{acc, ref};
-}
-
-// Row kernel for chains: the pass-1 rows of all sequences, flattened, are cut
-// into one equal range per wave; a wave streams its range without barriers
-// and stores one record per row piece it covers.  Every block also fills its
-// share of the exp table.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_stream(const VerifyParams P)
-{
-    if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
-    const int w = (int)blockIdx.x * kWaves + ((int)threadIdx.x >> 6);
-    int64_t e = wave_begin(P, w);
-    const int64_t e_end = wave_begin(P, w + 1);
-    while (e < e_end) {
-        const int64_t grow = e / P.V;
-        const int64_t o = e - grow * P.V;
-        const int64_t left = (int64_t)P.V - o;
-        const int64_t take = (e_end - e) < left ? (e_end - e) : left;
-        const int b = (int)(grow / P.rows), r = (int)(grow - (int64_t)b * P.rows);
-        const char* base = r < P.N ? qrow_ptr<DT>(P, b, r) : prow_ptr<DT>(P, b, r - P.N);
-        const RowStat st = wave_row_stats<DT, kRowBatch>(base + o * elem_bytes<DT>(), take, P.c, P.cd);
-        if ((threadIdx.x & 63) == 0) {
-            u32x4 a[1];
-            pack(st, a);
-            put_record<1>(stats_rsrc(P), stat_off(P, grow, w - wave_of(P, grow * P.V)), a, P.epoch);
-        }
-        e += take;
-    }
-}
-
-// Row kernel for trees: block (b, row, segment) streams one segment of a q/p
-// row that an accept test reads (rows of leaves get a placeholder record).
-// Every block also fills its share of the exp table.
-template <int DT>
+// Row kernel: block (b, row, segment) streams one segment of a pass-1 row
+// and stores its (m, s) record.  Chains: rows 0..N-1 are q rows 0..N-1 and
+// rows N..2N-1 the p rows.  Trees: row 2n is node n's q row and 2n+1 its p
+// row, streamed only for nodes that have a child (an accept test reads them;
+// the others get a placeholder record).  Many small blocks, dispatched as
+// compute units free up, balance the stream better than a resident grid
+// with fixed shares.  Every block also fills its share of the exp table.
+template <int DT, bool TREE>
 __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
 {
     if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
+    if (P.r_items == 0) return;  // no pass-1 rows (N = 0): the launch only fills the table
     const int b = (int)blockIdx.x / P.r_items;
     const int idx = (int)blockIdx.x - b * P.r_items;
     const int row = idx / P.segs, seg = idx - row * P.segs;
-    const int node = row >> 1;
-    const int32_t* par = P.parents_shared ? P.parents : P.parents + (int64_t)b * P.nn;
-    int found = 0;
-    for (int m = node + 1 + (int)threadIdx.x; m < P.nn; m += kBlock) found |= (par[m] == node);
-    const bool work = __syncthreads_or(found) != 0;
-    const char* base = (row & 1) ? prow_ptr<DT>(P, b, node) : qrow_ptr<DT>(P, b, node);
+    const char* base;
+    bool work = true;
+    if constexpr (TREE) {
+        const int node = row >> 1;
+        const int32_t* par = P.parents_shared ? P.parents : P.parents + (int64_t)b * P.nn;
+        int found = 0;
+        for (int m = node + 1 + (int)threadIdx.x; m < P.nn; m += kBlock) found |= (par[m] == node);
+        work = __syncthreads_or(found) != 0;
+        base = (row & 1) ? prow_ptr<DT>(P, b, node) : qrow_ptr<DT>(P, b, node);
+    } else {
+        base = row < P.N ? qrow_ptr<DT>(P, b, row) : prow_ptr<DT>(P, b, row - P.N);
+    }
     RowStat st{0.0, -INFINITY};
     if (work) {
         const int begin = seg * P.seg_len;
@@ -1422,9 +1349,12 @@ constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int nchunks_of(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
 
-// Row segments of about 128K elements (a multiple of 64 elements, so every
-// segment keeps the row's 16-byte alignment).
-constexpr int kSegTarget = 131072;
+// Row segments of about SV_SEG_TARGET elements (a multiple of 64 elements,
+// so every segment keeps the row's 16-byte alignment): one row block each.
+#ifndef SV_SEG_TARGET
+#define SV_SEG_TARGET 32768
+#endif
+constexpr int kSegTarget = SV_SEG_TARGET;
 void segments_of(int V, int* segs, int* seg_len)
 {
     int s = (V + kSegTarget - 1) / kSegTarget;
@@ -1436,18 +1366,17 @@ void segments_of(int V, int* segs, int* seg_len)
 }
 
 constexpr int kTableEntries = 65536;
-constexpr int64_t kWaveMinElems = 32768;  // smallest range worth a wave of the chain row kernel
 
 // Blocks of a kernel the device holds at once (compute units x occupancy).
 template <typename K>
-int resident_blocks(K kernel, std::atomic<int>& cache)
+int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 {
     int v = cache.load();
     if (v) return v;
     int dev = 0, cus = 0, occ = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel), sv::kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(kernel), block, 0) !=
             hipSuccess ||
         occ <= 0)
         return 0;
@@ -1456,71 +1385,18 @@ int resident_blocks(K kernel, std::atomic<int>& cache)
     return v;
 }
 
-// Blocks of the chain row kernel: as many as the device holds at once (one
-// round, so the equal ranges also finish together), fewer for small inputs.
-// dtype < 0 gives an upper bound over both dtypes (workspace sizing; without
-// a device, 2048 blocks).
-int stream_blocks(int dtype, int64_t E)
-{
-    static std::atomic<int> c_bf16{0}, c_f32{0};
-    int resident;
-    if (dtype < 0) {
-        const int a = resident_blocks(&sv::k_stream<sv::DT_BF16>, c_bf16);
-        const int b = resident_blocks(&sv::k_stream<sv::DT_F32>, c_f32);
-        resident = a > b ? a : b;
-        if (resident < 2048) resident = 2048;
-    } else {
-        resident = dtype == SV_BF16 ? resident_blocks(&sv::k_stream<sv::DT_BF16>, c_bf16)
-                                    : resident_blocks(&sv::k_stream<sv::DT_F32>, c_f32);
-    }
-    if (resident <= 0) return 0;
-    const int64_t want = (E + sv::kWaves * kWaveMinElems - 1) / (sv::kWaves * kWaveMinElems);
-    return (int)(want < 1 ? 1 : (want < resident ? want : resident));
-}
-
-// Pass-1 work split.  Chains: W waves over the flattened rows and MP record
-// slots per row (a row of V elements meets at most ceil(V / L) + 1 wave
-// ranges, L the shortest non-empty range).  Trees: one slot per segment.
-struct Split {
-    int blocks, W, MP;
-    int64_t E, E64;
-};
-
-Split split_for(bool tree, int dtype, int B, int rows, int V)
-{
-    Split s{};
-    s.E = (int64_t)B * rows * V;
-    s.E64 = (s.E + 63) / 64;
-    if (tree) {
-        int segs, seg_len;
-        segments_of(V, &segs, &seg_len);
-        s.blocks = 0;
-        s.W = 0;
-        s.MP = segs;
-        return s;
-    }
-    s.blocks = stream_blocks(dtype, s.E);
-    s.W = s.blocks * sv::kWaves;
-    if (s.W <= 0) return s;
-    // no more waves than 64-element units: every range is then non-empty
-    // (waves past W get none)
-    if (s.E64 > 0 && s.W > s.E64) s.W = (int)s.E64;
-    int64_t per = s.E64 / s.W;
-    const int64_t L = 64 * (per < 1 ? 1 : per);
-    s.MP = (int)((V + L - 1) / L + 1);
-    return s;
-}
-
 struct Layout {
     size_t chunk_arr, stats, part, table, total;
 };
 
-Layout make_layout(int B, int rows, int V, int MP)
+Layout make_layout(int B, int rows, int V)
 {
+    int segs, seg_len;
+    segments_of(V, &segs, &seg_len);
     Layout L;
     L.chunk_arr = 0;
-    L.stats = align_up((size_t)B * sizeof(uint64_t));
-    L.part = L.stats + align_up((size_t)B * rows * MP * sv::kRowStatBytes);
+    L.stats = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
+    L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
     L.table = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
     L.total = L.table + (size_t)kTableEntries * sizeof(double);
     return L;
@@ -1563,18 +1439,15 @@ void set_groups(sv::VerifyParams& P)
 }
 
 template <int DT, bool TREE>
-int launch_kernels(sv::VerifyParams& P, int stream_grid, const sv_timing* timing, hipStream_t stream)
+int launch_kernels(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
     set_groups<DT, TREE>(P);
-    const int64_t row_grid = TREE ? (int64_t)P.B * P.r_items : stream_grid;
+    // at least one row block: the row kernel also fills the exp table
+    const int64_t row_grid = P.r_items > 0 ? (int64_t)P.B * P.r_items : (P.table ? 1 : 0);
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
-    if (row_grid > 0) {
-        if (TREE)
-            hipLaunchKernelGGL((sv::k_rows<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
-        else
-            hipLaunchKernelGGL((sv::k_stream<DT>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
-    }
+    if (row_grid > 0)
+        hipLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
     if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL((sv::k_sample<DT, TREE>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
@@ -1583,8 +1456,8 @@ int launch_kernels(sv::VerifyParams& P, int stream_grid, const sv_timing* timing
 }
 
 template <bool TREE>
-int launch_verify(sv::VerifyParams& P, int dtype, const Split& S, void* workspace, const Layout& L,
-                  const sv_timing* timing, hipStream_t stream)
+int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout& L, const sv_timing* timing,
+                  hipStream_t stream)
 {
     char* ws = static_cast<char*>(workspace);
     P.chunk_arrivals = reinterpret_cast<uint64_t*>(ws + L.chunk_arr);
@@ -1594,13 +1467,9 @@ int launch_verify(sv::VerifyParams& P, int dtype, const Split& S, void* workspac
     P.part_bytes = (uint32_t)(L.table - L.part);
     const bool table = SV_EXP_TABLE && dtype == SV_BF16;
     P.table = table ? reinterpret_cast<double*>(ws + L.table) : nullptr;
-    P.E = S.E;
-    P.E64 = S.E64;
-    P.W = S.W;
-    P.MP = S.MP;
     P.epoch = next_epoch();
-    return dtype == SV_BF16 ? launch_kernels<sv::DT_BF16, TREE>(P, S.blocks, timing, stream)
-                            : launch_kernels<sv::DT_F32, TREE>(P, S.blocks, timing, stream);
+    return dtype == SV_BF16 ? launch_kernels<sv::DT_BF16, TREE>(P, timing, stream)
+                            : launch_kernels<sv::DT_F32, TREE>(P, timing, stream);
 }
 
 void fill_common(sv::VerifyParams& P, int B, int V, int rows, uint64_t seed, uint64_t round, float temperature)
@@ -1650,13 +1519,13 @@ const char* sv_status_string(int status)
 size_t sv_chain_workspace_bytes(int B, int N, int V)
 {
     if (B < 0 || N < 0 || N > 64 || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * N, V, split_for(false, -1, B, 2 * N, V).MP).total;
+    return make_layout(B, 2 * N, V).total;
 }
 
 size_t sv_tree_workspace_bytes(int B, int T, int V)
 {
     if (B < 0 || T < 0 || T + 1 > sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * (T + 1), V, split_for(true, -1, B, 2 * (T + 1), V).MP).total;
+    return make_layout(B, 2 * (T + 1), V).total;
 }
 
 int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
@@ -1677,13 +1546,9 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     if (rc) return rc;
     if (N > 0 && (rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
     if (!item_count_ok(B, 2 * N, V)) return SV_ESHAPE;
-    // the workspace is sized for the largest split any device can choose
-    const Layout Lb = make_layout(B, 2 * N, V, split_for(false, -1, B, 2 * N, V).MP);
-    if (!regions_fit(Lb)) return SV_ESHAPE;
-    if (!workspace || workspace_bytes < Lb.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
-    const Split S = split_for(false, dtype, B, 2 * N, V);
-    if (S.W <= 0) return SV_EHIP;
-    const Layout L = make_layout(B, 2 * N, V, S.MP);
+    const Layout L = make_layout(B, 2 * N, V);
+    if (!regions_fit(L)) return SV_ESHAPE;
+    if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
 
     sv::VerifyParams P{};
     P.zq = static_cast<const char*>(target_logits);
@@ -1706,7 +1571,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     P.out_acc = out_accept;
     P.out_probs = out_probs;
     P.out_resid = out_residual_mass;
-    return launch_verify<false>(P, dtype, S, workspace, L, timing, stream);
+    return launch_verify<false>(P, dtype, workspace, L, timing, stream);
 }
 
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
@@ -1731,8 +1596,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if ((rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
     const int nn = T + 1;
     if (!item_count_ok(B, 2 * nn, V)) return SV_ESHAPE;
-    const Split S = split_for(true, dtype, B, 2 * nn, V);
-    const Layout L = make_layout(B, 2 * nn, V, S.MP);
+    const Layout L = make_layout(B, 2 * nn, V);
     if (!regions_fit(L)) return SV_ESHAPE;
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
 
@@ -1757,7 +1621,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     P.out_acc = out_accept;
     P.out_probs = out_probs;
     P.out_resid = out_residual_mass;
-    return launch_verify<true>(P, dtype, S, workspace, L, timing, stream);
+    return launch_verify<true>(P, dtype, workspace, L, timing, stream);
 }
 
 int sv_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc, double* out_samp,
