@@ -119,10 +119,11 @@ def algorithmic_bytes(w, s) -> int:
 
 def row_kernel_bytes(w, s) -> int:
     """Bytes the row-statistics kernel must read once: every q/p row an
-    accept test uses (chain: B*2N*V*s; tree: q and p of every internal node)."""
+    accept test or the bonus uses (chain: B*(2N+1)*V*s; tree: q and p of
+    every internal node)."""
     import numpy as np
     if w.kind == "chain":
-        return w.B * 2 * w.N * w.V * w.elem_bytes
+        return w.B * (2 * w.N + 1) * w.V * w.elem_bytes
     par = s["parents"].cpu().numpy()
     p2 = par if par.ndim == 2 else np.repeat(par[None], w.B, 0)
     internal = 0

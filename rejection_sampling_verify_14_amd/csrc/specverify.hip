@@ -259,7 +259,7 @@ struct VerifyParams {
     int parents_shared;
     int B, V, N, nn;          // chain: N drafts, nn = N+1; tree: nn = T+1 nodes, N unused
     int max_depth, width;     // output row width (chain N+1, tree max_depth+1)
-    int rows;                 // pass-1 rows per sequence (chain 2N, tree 2 nn)
+    int rows;                 // pass-1 rows per sequence (chain 2N+1, tree 2 nn)
     int segs, seg_len;        // segments per row, elements per segment
     int r_items, nch;         // row blocks per sequence (rows x segs), sample chunks per sequence
     int cpb, groups;          // sample chunks per block, sample blocks per sequence
@@ -398,13 +398,16 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
 // table entry of z's bit pattern, exp(z/T), times exp(-m/T), when |m/T| is
 // small enough that neither factor leaves the double range for the logits of
 // the row (z <= m + T ln 2); otherwise, and for fp32 logits, it is computed.
+// `unscaled` gives the table entry itself (sums over a chunk take the factor
+// exp(-m/T) once).
 struct ExpRow {
-    const double* tab;
+    const double* tab;  // exp(v/T) for every bf16 bit pattern v, or null: computed
     const double* t32;  // 2^(j/32) for the computed path
     double m, scale, invT;
+    __device__ __forceinline__ double unscaled(float z) const { return tab[__float_as_uint(z) >> 16]; }
     __device__ __forceinline__ double operator()(float z) const
     {
-        if (tab) return tab[__float_as_uint(z) >> 16] * scale;
+        if (tab) return unscaled(z) * scale;
         return exp64(((double)z - m) * invT, t32);
     }
 };
@@ -476,7 +479,7 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     if (active) {
         const int tok = P.tokens[(int64_t)b * N + lane];
         rq = load_row_stat(P, b, lane);
-        rp = load_row_stat(P, b, N + lane);
+        rp = load_row_stat(P, b, N + 1 + lane);
         if (tok < 0 || tok >= P.V || stat_bad(rq) || stat_bad(rp)) {
             err = 1;
         } else {
@@ -511,8 +514,18 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     s.node = k;
     s.status = 0;
     s.u = sample_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(k + 1));
-    if (k < N) fill_residual_state(s, kq, kp, P.T);
-    else s.mode = kModeBonus;
+    if (k < N) {
+        fill_residual_state(s, kq, kp, P.T);
+    } else {
+        s.mode = kModeBonus;
+        const RowStat qn = load_row_stat(P, b, N);
+        if (stat_bad(qn)) {
+            s.status = 1;  // NaN, +inf or no mass in the bonus row
+        } else {
+            s.mq = qn.m;
+            s.bonus_ref = 1;
+        }
+    }
     if (lane == 0) out = s;
 }
 
@@ -677,17 +690,14 @@ __device__ __forceinline__ bool chunk_vectors(const char* row, int V, int c)
     return (((uintptr_t)row) & 15u) == 0 && (int64_t)(c + 1) * kChunk <= V;
 }
 
-constexpr int kLaneBatch = 4;  // 16-byte vectors a lane loads at once
+constexpr int kLaneAhead = 4;  // 16-byte vectors per row a lane keeps in flight
 
-// The lane's h-th batch of vectors of chunk c.
+// The lane's k-th vector of chunk c.
 template <int DT>
-__device__ __forceinline__ void load_chunk_half(const char* __restrict__ row, int c, int h, int lane, uint4* raw)
+__device__ __forceinline__ uint4 chunk_vec(const char* __restrict__ row, int c, int k, int lane)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
-    const uint4* v = reinterpret_cast<const uint4*>(row + (int64_t)c * kChunk * elem_bytes<DT>());
-#pragma unroll
-    for (int j = 0; j < kLaneBatch; ++j) raw[j] = v[lane + 64 * (kLaneBatch * h + j)];
-    (void)EPV;
+    return reinterpret_cast<const uint4*>(row)[(int64_t)c * (kChunk / EPV) + 64 * k + lane];
 }
 
 // Token t of the lane's share in the element-by-element path.
@@ -699,32 +709,51 @@ __device__ __forceinline__ float chunk_token(const char* row, int V, int c, int 
     return e < V ? load_logit<DT>(row, e) : -INFINITY;
 }
 
-// exp((z - m)/T) of one row with the evaluation method fixed at compile time
-// (TAB: ExpRow's table, else the fp64 routine).
+// exp((z - m)/T) / e.scale of one row with the evaluation method fixed at
+// compile time (TAB: ExpRow's table, unscaled; else the fp64 routine, whose
+// scale is 1).
 template <bool TAB>
 __device__ __forceinline__ double exp_of(const ExpRow& e, float z)
 {
-    if constexpr (TAB) return e.tab[__float_as_uint(z) >> 16] * e.scale;
+    if constexpr (TAB) return e.unscaled(z);
     else return exp64(((double)z - e.m) * e.invT, e.t32);
 }
 
-template <bool TAB>
-__device__ __forceinline__ void residual_token(float zq, float zp, const SeqState& s, const ExpRow& eq,
-                                               const ExpRow& ep, double* acc, float& dmin, float& dmax)
+// exp_of of K logits.
+template <bool TAB, int K>
+__device__ __forceinline__ void exp_vec(const ExpRow& e, const float* x, double* out)
 {
-    const double a = exp_of<TAB>(eq, zq);
-    const double bb = exp_of<TAB>(ep, zp);
-    acc[0] += a;
-    acc[1] += bb;
-    const float d = zq - zp;
-    const bool above = d > s.thr_hi;
-    const bool near = !above && d >= s.thr_lo;
-    acc[2] += above ? a : 0.0;
-    acc[3] += above ? bb : 0.0;
-    acc[4] += near ? a : 0.0;
-    acc[5] += near ? bb : 0.0;
-    dmin = near ? fminf(dmin, d) : dmin;
-    dmax = near ? fmaxf(dmax, d) : dmax;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        if constexpr (TAB) out[i] = e.unscaled(x[i]);
+        else out[i] = exp64(((double)x[i] - e.m) * e.invT, e.t32);
+    }
+}
+
+// The residual's per-chunk sums (see ChunkSums) over K token pairs, with the
+// exps unscaled as exp_of gives them.
+template <bool TAB, int K>
+__device__ __forceinline__ void residual_vec(const float* zq, const float* zp, const SeqState& s,
+                                             const ExpRow& eq, const ExpRow& ep, double* acc, float& dmin,
+                                             float& dmax)
+{
+    double a[K], bb[K];
+    exp_vec<TAB, K>(eq, zq, a);
+    exp_vec<TAB, K>(ep, zp, bb);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        acc[0] += a[i];
+        acc[1] += bb[i];
+        const float d = zq[i] - zp[i];
+        const bool above = d > s.thr_hi;
+        const bool near = !above && d >= s.thr_lo;
+        acc[2] += above ? a[i] : 0.0;
+        acc[3] += above ? bb[i] : 0.0;
+        acc[4] += near ? a[i] : 0.0;
+        acc[5] += near ? bb[i] : 0.0;
+        dmin = near ? fminf(dmin, d) : dmin;
+        dmax = near ? fmaxf(dmax, d) : dmax;
+    }
 }
 
 template <int DT, bool TAB>
@@ -736,28 +765,31 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
     constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 8, fp32 16
     const int lane = threadIdx.x & 63;
     if (chunk_vectors<DT>(qrow, P.V, c) && chunk_vectors<DT>(prow, P.V, c)) {
+        // one vector at a time, the next one's loads in flight
+        uint4 cq = chunk_vec<DT>(qrow, c, 0, lane), cp = chunk_vec<DT>(prow, c, 0, lane);
 #pragma unroll 1
-        for (int h = 0; h < PER / kLaneBatch; ++h) {
-            uint4 rq[kLaneBatch], rp[kLaneBatch];
-            load_chunk_half<DT>(qrow, c, h, lane, rq);
-            load_chunk_half<DT>(prow, c, h, lane, rp);
-#pragma unroll
-            for (int j = 0; j < kLaneBatch; ++j) {
-                float xq[EPV], xp[EPV];
-                decode16<DT>(rq[j], xq);
-                decode16<DT>(rp[j], xp);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) residual_token<TAB>(xq[i], xp[i], s, eq, ep, acc, dmin, dmax);
-                __builtin_amdgcn_sched_barrier(0);  // one vector's exps at a time
+        for (int k = 0; k < PER; ++k) {
+            uint4 nq = cq, np = cp;
+            if (k + 1 < PER) {
+                nq = chunk_vec<DT>(qrow, c, k + 1, lane);
+                np = chunk_vec<DT>(prow, c, k + 1, lane);
             }
+            float xq[EPV], xp[EPV];
+            decode16<DT>(cq, xq);
+            decode16<DT>(cp, xp);
+            residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+            cq = nq;
+            cp = np;
         }
     } else {
 #pragma unroll 1
         for (int k = 0; k < PER; ++k)
 #pragma unroll 1
-            for (int i = 0; i < EPV; ++i)
-                residual_token<TAB>(chunk_token<DT>(qrow, P.V, c, lane, k, i), chunk_token<DT>(prow, P.V, c, lane, k, i),
-                                    s, eq, ep, acc, dmin, dmax);
+            for (int i = 0; i < EPV; ++i) {
+                const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
+                const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
+                residual_vec<TAB, 1>(&zq, &zp, s, eq, ep, acc, dmin, dmax);
+            }
     }
 }
 
@@ -773,17 +805,15 @@ __device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qro
         bad |= (x != x) || (x == INFINITY);
     };
     if (chunk_vectors<DT>(qrow, P.V, c)) {
+        uint4 cur = chunk_vec<DT>(qrow, c, 0, lane);
 #pragma unroll 1
-        for (int h = 0; h < PER / kLaneBatch; ++h) {
-            uint4 rq[kLaneBatch];
-            load_chunk_half<DT>(qrow, c, h, lane, rq);
+        for (int k = 0; k < PER; ++k) {
+            const uint4 nxt = (k + 1 < PER) ? chunk_vec<DT>(qrow, c, k + 1, lane) : cur;
+            float x[EPV];
+            decode16<DT>(cur, x);
 #pragma unroll
-            for (int j = 0; j < kLaneBatch; ++j) {
-                float x[EPV];
-                decode16<DT>(rq[j], x);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) take(x[i]);
-            }
+            for (int i = 0; i < EPV; ++i) take(x[i]);
+            cur = nxt;
         }
     } else {
 #pragma unroll 1
@@ -801,92 +831,106 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
     const int lane = threadIdx.x & 63;
     double sa = 0.0;
     if (chunk_vectors<DT>(qrow, P.V, c)) {
+        uint4 cur = chunk_vec<DT>(qrow, c, 0, lane);
 #pragma unroll 1
-        for (int h = 0; h < PER / kLaneBatch; ++h) {
-            uint4 rq[kLaneBatch];
-            load_chunk_half<DT>(qrow, c, h, lane, rq);
+        for (int k = 0; k < PER; ++k) {
+            const uint4 nxt = (k + 1 < PER) ? chunk_vec<DT>(qrow, c, k + 1, lane) : cur;
+            float x[EPV];
+            decode16<DT>(cur, x);
+            double a[EPV];
+            exp_vec<TAB, EPV>(ec, x, a);
 #pragma unroll
-            for (int j = 0; j < kLaneBatch; ++j) {
-                float x[EPV];
-                decode16<DT>(rq[j], x);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) sa += exp_of<TAB>(ec, x[i]);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            for (int i = 0; i < EPV; ++i) sa += a[i];
+            cur = nxt;
         }
     } else {
 #pragma unroll 1
         for (int k = 0; k < PER; ++k)
 #pragma unroll 1
-            for (int i = 0; i < EPV; ++i) sa += exp_of<TAB>(ec, chunk_token<DT>(qrow, P.V, c, lane, k, i));
+            for (int i = 0; i < EPV; ++i) {
+                const float z = chunk_token<DT>(qrow, P.V, c, lane, k, i);
+                double a;
+                exp_vec<TAB, 1>(ec, &z, &a);
+                sa += a;
+            }
     }
     return sa;
 }
 
-// Residual chunk sums of the whole chunks [ca, cb) of 16-byte aligned rows,
-// by one wave, stored as records: the loads of the next batch are issued
-// before the current batch is used, across chunk boundaries.
-template <int DT, bool TAB>
-__device__ void residual_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
-                               int ca, int cb, const ExpRow& eq, const ExpRow& ep)
+// Chunk sums of the whole chunks [ca, cb) of 16-byte aligned rows, by one
+// wave, stored as records: the loads of the next batch are issued before the
+// current batch is used, across chunk boundaries.  BONUS: the q row alone,
+// summed against its pass-1 reference s.mq; otherwise the residual's sums
+// over the q and p rows.
+template <int DT, bool TAB, bool BONUS>
+__device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+                            int ca, int cb, const ExpRow& eq, const ExpRow& ep)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
-    constexpr int NB = kChunk / EPV / 64 / kLaneBatch;  // batches per chunk: bf16 1, fp32 2
+    constexpr int PER = kChunk / EPV / 64;  // vectors per lane per chunk: bf16 4, fp32 8
+    constexpr int D = kLaneAhead;
     const int lane = threadIdx.x & 63;
-    const uint4* vq = reinterpret_cast<const uint4*>(qrow);
-    const uint4* vp = reinterpret_cast<const uint4*>(prow);
-    auto vec = [&](int t, int j) -> int64_t {
-        return (int64_t)(t / NB) * (kChunk / EPV) + 64 * (kLaneBatch * (t % NB) + j) + lane;
-    };
-    const int tend = cb * NB;
-    int t = ca * NB;
-    if (t >= tend) return;
-    uint4 cq[kLaneBatch], cp[kLaneBatch];
+    // the lane's t-th vector of the range: vector k = t % PER of chunk ca + t / PER
+    auto vec_q = [&](int t) { return chunk_vec<DT>(qrow, ca + t / PER, t % PER, lane); };
+    auto vec_p = [&](int t) { return chunk_vec<DT>(prow, ca + t / PER, t % PER, lane); };
+    const int tend = (cb - ca) * PER;
+    if (tend <= 0) return;
+    // ring of the next D vectors per row; one vector is used per step (a
+    // rolled loop keeps one vector's lookups live at a time)
+    uint4 rq[D], rp[D];
 #pragma unroll
-    for (int j = 0; j < kLaneBatch; ++j) {
-        cq[j] = vq[vec(t, j)];
-        cp[j] = vp[vec(t, j)];
+    for (int j = 0; j < D; ++j) {
+        rq[j] = j < tend ? vec_q(j) : rq[0];
+        if constexpr (!BONUS) rp[j] = j < tend ? vec_p(j) : rp[0];
     }
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     float dmin = INFINITY, dmax = -INFINITY;
-    for (; t < tend; ++t) {
-        uint4 nq[kLaneBatch], np[kLaneBatch];
-        if (t + 1 < tend) {
+#pragma unroll 1
+    for (int t = 0; t < tend; ++t) {
+        const uint4 vq = rq[0];
+        uint4 vp;
+        if constexpr (!BONUS) vp = rp[0];
 #pragma unroll
-            for (int j = 0; j < kLaneBatch; ++j) {
-                nq[j] = vq[vec(t + 1, j)];
-                np[j] = vp[vec(t + 1, j)];
-            }
+        for (int j = 0; j + 1 < D; ++j) {
+            rq[j] = rq[j + 1];
+            if constexpr (!BONUS) rp[j] = rp[j + 1];
         }
-#pragma unroll
-        for (int j = 0; j < kLaneBatch; ++j) {
-            float xq[EPV], xp[EPV];
-            decode16<DT>(cq[j], xq);
-            decode16<DT>(cp[j], xp);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) residual_token<TAB>(xq[i], xp[i], s, eq, ep, acc, dmin, dmax);
-            __builtin_amdgcn_sched_barrier(0);
+        if (t + D < tend) {
+            rq[D - 1] = vec_q(t + D);
+            if constexpr (!BONUS) rp[D - 1] = vec_p(t + D);
         }
-        if ((t + 1) % NB == 0) {
+        float xq[EPV];
+        decode16<DT>(vq, xq);
+        if constexpr (BONUS) {
+            double a[EPV];
+            exp_vec<TAB, EPV>(eq, xq, a);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) acc[0] += a[i];
+        } else {
+            float xp[EPV];
+            decode16<DT>(vp, xp);
+            residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+        }
+        if ((t + 1) % PER == 0) {
             ChunkSums out{};
-            out.sa = wave_sum(acc[0]);
-            out.sb = wave_sum(acc[1]);
-            out.pa = wave_sum(acc[2]);
-            out.pb = wave_sum(acc[3]);
-            out.na = wave_sum(acc[4]);
-            out.nb = wave_sum(acc[5]);
-            out.dmax = wave_max(dmax);
-            out.dmin = -wave_max(-dmin);
-            if (lane == 0) put_chunk(P, b, t / NB, out);
+            if constexpr (BONUS) {
+                out.sa = (double)s.mq;
+                out.sb = wave_sum(acc[0]) * eq.scale;
+            } else {
+                out.sa = wave_sum(acc[0]) * eq.scale;
+                out.sb = wave_sum(acc[1]) * ep.scale;
+                out.pa = wave_sum(acc[2]) * eq.scale;
+                out.pb = wave_sum(acc[3]) * ep.scale;
+                out.na = wave_sum(acc[4]) * eq.scale;
+                out.nb = wave_sum(acc[5]) * ep.scale;
+                out.dmax = wave_max(dmax);
+                out.dmin = -wave_max(-dmin);
+            }
+            if (lane == 0) put_chunk(P, b, ca + t / PER, out);
 #pragma unroll
             for (int i = 0; i < 6; ++i) acc[i] = 0.0;
             dmin = INFINITY;
             dmax = -INFINITY;
-        }
-#pragma unroll
-        for (int j = 0; j < kLaneBatch; ++j) {
-            cq[j] = nq[j];
-            cp[j] = np[j];
         }
     }
 }
@@ -905,14 +949,20 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         else residual_chunk<DT, false>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
 #pragma unroll
         for (int i = 0; i < 6; ++i) acc[i] = wave_sum(acc[i]);
-        out.sa = acc[0];
-        out.sb = acc[1];
-        out.pa = acc[2];
-        out.pb = acc[3];
-        out.na = acc[4];
-        out.nb = acc[5];
+        out.sa = acc[0] * eq.scale;
+        out.sb = acc[1] * ep.scale;
+        out.pa = acc[2] * eq.scale;
+        out.pb = acc[3] * ep.scale;
+        out.na = acc[4] * eq.scale;
+        out.nb = acc[5] * ep.scale;
         out.dmax = wave_max(dmax);
         out.dmin = -wave_max(-dmin);
+    } else if (s.bonus_ref) {
+        // against the row's pass-1 reference (its NaN/+inf check is the
+        // pass-1 statistics')
+        const double sa = eq.tab ? bonus_sum<DT, true>(P, qrow, c, eq) : bonus_sum<DT, false>(P, qrow, c, eq);
+        out.sa = (double)s.mq;
+        out.sb = wave_sum(sa) * eq.scale;
     } else {
         // the chunk maximum first, then the sum relative to it
         float lm = -INFINITY;
@@ -920,12 +970,14 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         bonus_max<DT>(P, qrow, c, lm, bad);
         const float mc = wave_max(lm);
         double sa = 0.0;
+        double scale = 1.0;
         if (mc != -INFINITY) {
             const ExpRow ec = exp_row(P, mc, t32);
             sa = ec.tab ? bonus_sum<DT, true>(P, qrow, c, ec) : bonus_sum<DT, false>(P, qrow, c, ec);
+            scale = ec.scale;
         }
         out.sa = (double)mc;
-        out.sb = wave_sum(sa);
+        out.sb = wave_sum(sa) * scale;
         out.flags = __any(bad) ? kFlagBad : 0u;
     }
     return out;
@@ -1058,7 +1110,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
             stage_chunk<DT>(qrow, P.V, c, s_q);
             stage_chunk<DT>(prow, P.V, c, s_p);
             double w[1] = {0.0};
-#pragma unroll 4
+#pragma unroll 1
             for (int j = 0; j < kPerThread; ++j) {
                 const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
                 const float d = zq - zp;
@@ -1165,7 +1217,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         return ec(a);
     };
     double tsum = 0.0;
-#pragma unroll 4
+#pragma unroll 1
     for (int j = 0; j < kPerThread; ++j) tsum += weight(j);
     double ctotal;
     const double tbase = block_exclusive_scan(tsum, red, &ctotal);
@@ -1181,14 +1233,14 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         // no positive weight at or below the threshold in this chunk (only
         // possible through rounding): take its last element of positive weight
         int last = -1;
-#pragma unroll 4
+#pragma unroll 1
         for (int j = 0; j < kPerThread; ++j)
             if (weight(j) > 0.0) last = cs * kChunk + tid * kPerThread + j;
         atomicMax(&s_token, last);
     } else if (tid == s_owner) {
         double cum = tbase;
         int pick = -1, last = -1;
-#pragma unroll 4
+#pragma unroll 1
         for (int j = 0; j < kPerThread; ++j) {
             const double wj = weight(j);
             if (wj > 0.0) {
@@ -1233,8 +1285,8 @@ __device__ __forceinline__ void fill_table_share(const VerifyParams& P, int blk,
 }
 
 // Row kernel: block (b, row, segment) streams one segment of a pass-1 row
-// and stores its (m, s) record.  Chains: rows 0..N-1 are q rows 0..N-1 and
-// rows N..2N-1 the p rows.  Trees: row 2n is node n's q row and 2n+1 its p
+// and stores its (m, s) record.  Chains: rows 0..N are q rows 0..N (row N
+// the bonus row) and rows N+1..2N the p rows 0..N-1.  Trees: row 2n is node n's q row and 2n+1 its p
 // row, streamed only for nodes that have a child (an accept test reads them;
 // the others get a placeholder record).  Many small blocks, dispatched as
 // compute units free up, balance the stream better than a resident grid
@@ -1243,7 +1295,7 @@ template <int DT, bool TREE>
 __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
 {
     if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
-    if (P.r_items == 0) return;  // no pass-1 rows (N = 0): the launch only fills the table
+    if (P.r_items == 0) return;  // no pass-1 rows: the launch only fills the table
     const int b = (int)blockIdx.x / P.r_items;
     const int idx = (int)blockIdx.x - b * P.r_items;
     const int row = idx / P.segs, seg = idx - row * P.segs;
@@ -1257,7 +1309,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
         work = __syncthreads_or(found) != 0;
         base = (row & 1) ? prow_ptr<DT>(P, b, node) : qrow_ptr<DT>(P, b, node);
     } else {
-        base = row < P.N ? qrow_ptr<DT>(P, b, row) : prow_ptr<DT>(P, b, row - P.N);
+        base = row <= P.N ? qrow_ptr<DT>(P, b, row) : prow_ptr<DT>(P, b, row - P.N - 1);
     }
     RowStat st{0.0, -INFINITY};
     if (work) {
@@ -1307,11 +1359,17 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     const int wave = (int)threadIdx.x >> 6;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
     int c = ca;
-    if (s.status == 0 && s.mode == kModeResidual && ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
+    if (s.status == 0 && (s.mode == kModeResidual || s.bonus_ref) &&
+        ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
         const int whole = min(cb, P.V / kChunk);
         if (whole > c) {
-            if (eq.tab && ep.tab) residual_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-            else residual_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            if (s.mode == kModeResidual) {
+                if (eq.tab && ep.tab) chunk_range<DT, true, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+                else chunk_range<DT, false, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            } else {
+                if (eq.tab) chunk_range<DT, true, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+                else chunk_range<DT, false, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+            }
             c = whole;
         }
     }
@@ -1519,7 +1577,7 @@ const char* sv_status_string(int status)
 size_t sv_chain_workspace_bytes(int B, int N, int V)
 {
     if (B < 0 || N < 0 || N > 64 || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * N, V).total;
+    return make_layout(B, 2 * N + 1, V).total;
 }
 
 size_t sv_tree_workspace_bytes(int B, int T, int V)
@@ -1545,8 +1603,8 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
     if (rc) return rc;
     if (N > 0 && (rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
-    if (!item_count_ok(B, 2 * N, V)) return SV_ESHAPE;
-    const Layout L = make_layout(B, 2 * N, V);
+    if (!item_count_ok(B, 2 * N + 1, V)) return SV_ESHAPE;
+    const Layout L = make_layout(B, 2 * N + 1, V);
     if (!regions_fit(L)) return SV_ESHAPE;
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
 
@@ -1564,7 +1622,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     P.nn = N + 1;
     P.max_depth = N;
     P.width = N + 1;
-    fill_common(P, B, V, 2 * N, seed, round, temperature);
+    fill_common(P, B, V, 2 * N + 1, seed, round, temperature);
     P.out_tokens = out_tokens;
     P.out_path = nullptr;
     P.out_num = out_num_accepted;

@@ -298,13 +298,15 @@ struct SeqState {
     int node;         // row sampled from: chain position k, tree stop node
     int status;       // 0 ok, 1 data error
     int mode;         // 0 residual, 1 bonus
+    int bonus_ref;    // bonus: mq is the pass-1 reference of the bonus row
 };
 
 // Per-chunk sums of the sampled row(s).  Residual: sa = sum a, sb = sum b
 // (a = exp((zq - mq)/T), b = exp((zp - mp)/T)); pa, pb = the same over the
 // tokens certainly in {q > p}; na, nb = over the near-threshold tokens, whose
-// smallest and largest zq - zp are dmin, dmax.  Bonus: sa = chunk maximum of
-// z, sb = sum exp((z - sa)/T).  flags: bit 0 NaN/+inf in the chunk, bit 1
+// smallest and largest zq - zp are dmin, dmax.  Bonus: sa = the reference the
+// chunk is summed against (the chunk maximum of z, or the row's pass-1
+// reference when known), sb = sum exp((z - sa)/T).  flags: bit 0 NaN/+inf in the chunk, bit 1
 // the sequence state never arrived.  Four atoms.
 struct ChunkSums {
     double sa, sb, pa, pb, na, nb;
@@ -312,7 +314,7 @@ struct ChunkSums {
     uint32_t flags;
 };
 
-constexpr uint32_t kRowStatBytes = 16, kSeqStateBytes = 64, kChunkSumsBytes = 64;
+constexpr uint32_t kRowStatBytes = 16, kChunkSumsBytes = 64;
 
 __device__ __forceinline__ void pack(const RowStat& v, u32x4* a)
 {
@@ -321,30 +323,6 @@ __device__ __forceinline__ void pack(const RowStat& v, u32x4* a)
 __device__ __forceinline__ RowStat unpack_rowstat(const u32x4* a)
 {
     return RowStat{d64(a[0].x, a[0].y), __uint_as_float(a[0].z)};
-}
-
-__device__ __forceinline__ void pack(const SeqState& v, u32x4* a)
-{
-    a[0] = u32x4{lo32(v.sq), hi32(v.sq), lo32(v.sp), hi32(v.sp)};
-    a[1] = u32x4{lo32(v.u), hi32(v.u), __float_as_uint(v.mq), __float_as_uint(v.mp)};
-    a[2] = u32x4{__float_as_uint(v.thr_lo), __float_as_uint(v.thr_hi), (uint32_t)v.k, (uint32_t)v.node};
-    a[3] = u32x4{(uint32_t)v.status, (uint32_t)v.mode, 0u, 0u};
-}
-__device__ __forceinline__ SeqState unpack_state(const u32x4* a)
-{
-    SeqState s;
-    s.sq = d64(a[0].x, a[0].y);
-    s.sp = d64(a[0].z, a[0].w);
-    s.u = d64(a[1].x, a[1].y);
-    s.mq = __uint_as_float(a[1].z);
-    s.mp = __uint_as_float(a[1].w);
-    s.thr_lo = __uint_as_float(a[2].x);
-    s.thr_hi = __uint_as_float(a[2].y);
-    s.k = (int)a[2].z;
-    s.node = (int)a[2].w;
-    s.status = (int)a[3].x;
-    s.mode = (int)a[3].y;
-    return s;
 }
 
 __device__ __forceinline__ void pack(const ChunkSums& v, u32x4* a)
