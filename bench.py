@@ -241,23 +241,31 @@ def main():
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    ev = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
     t_begin, t_end = hip.event(), hip.event()
     stream = torch.cuda.current_stream()
     hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    # the timed steps carry no per-step events (their records would sit
+    # between the kernels); the kernel split is timed in a second pass
     log(f"[bench] timing {K} steps")
     torch.cuda.synchronize()
     hip.lib.hipEventRecord(ctypes.c_void_p(t_begin), ctypes.c_void_p(stream.cuda_stream))
     wall0 = time.perf_counter()
     for i in range(K):
-        step(args.warmup + i, timing=ev[i])
+        step(args.warmup + i)
     hip.lib.hipEventRecord(ctypes.c_void_p(t_end), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = hip.elapsed_ms(t_begin, t_end)
+    ms_step = total_ms / K
+    log(f"[bench] timing the kernels of {K} more steps")
+    ev = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
+    for i in range(K):
+        step(args.warmup + K + i, timing=ev[i])
+    torch.cuda.synchronize()
     rows_ms = [hip.elapsed_ms(a, b) for a, b, _ in ev]
     samp_ms = [hip.elapsed_ms(b, c) for _, b, c in ev]
-    ms_step = total_ms / K
+    # [begin, rows_done): the row-statistics kernel; [rows_done, end): the
+    # sample step (chains: accept, chunk sums, final; trees: one kernel)
     k_mean = sum(rows_ms) / K
     s_mean = sum(samp_ms) / K
     per_set = [algorithmic_bytes(w, s) for s in sets]
@@ -304,7 +312,7 @@ def main():
             "kernel_ms": round(k_mean, 5),
             "algorithmic_bytes_per_launch": int(row_bytes),
         },
-        "sample_kernel_ms": round(s_mean, 5),
+        "sample_step_ms": round(s_mean, 5),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

@@ -262,13 +262,14 @@ struct VerifyParams {
     int rows;                 // pass-1 rows per sequence (chain 2N+1, tree 2 nn)
     int segs, seg_len;        // segments per row, elements per segment
     int r_items, nch;         // row blocks per sequence (rows x segs), sample chunks per sequence
-    int cpb, groups;          // sample chunks per block, sample blocks per sequence
+    int cpb, groups;          // sample chunks per block, sample blocks (pieces) per sequence
     uint64_t seed, round;
     float T, c;               // temperature, log2(e)/T
     double cd, invT;
     uint32_t epoch;
     // workspace
     uint64_t* chunk_arrivals; // [B] epoch-tagged arrival counters of the sample blocks
+    SeqState* seqs;           // [B] chains: accept state of each sequence (accept kernel -> sample kernels)
     char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
     uint32_t stats_bytes, part_bytes;
@@ -476,6 +477,8 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     const bool active = lane < N;
     int err = 0, acc = 1;
     RowStat rq{}, rp{};
+    // the bonus row's statistics, loaded with the others (used if all accept)
+    const RowStat qn = load_row_stat(P, b, N);
     if (active) {
         const int tok = P.tokens[(int64_t)b * N + lane];
         rq = load_row_stat(P, b, lane);
@@ -518,7 +521,6 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
         fill_residual_state(s, kq, kp, P.T);
     } else {
         s.mode = kModeBonus;
-        const RowStat qn = load_row_stat(P, b, N);
         if (stat_bad(qn)) {
             s.status = 1;  // NaN, +inf or no mass in the bonus row
         } else {
@@ -745,14 +747,16 @@ __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, c
         acc[0] += a[i];
         acc[1] += bb[i];
         const float d = zq[i] - zp[i];
+        // 0/1 factors: fma with 1 adds exactly, with 0 leaves the sum
         const bool above = d > s.thr_hi;
         const bool near = !above && d >= s.thr_lo;
-        acc[2] += above ? a[i] : 0.0;
-        acc[3] += above ? bb[i] : 0.0;
-        acc[4] += near ? a[i] : 0.0;
-        acc[5] += near ? bb[i] : 0.0;
-        dmin = near ? fminf(dmin, d) : dmin;
-        dmax = near ? fmaxf(dmax, d) : dmax;
+        const double fa = above ? 1.0 : 0.0, fn = near ? 1.0 : 0.0;
+        acc[2] = fma(fa, a[i], acc[2]);
+        acc[3] = fma(fa, bb[i], acc[3]);
+        acc[4] = fma(fn, a[i], acc[4]);
+        acc[5] = fma(fn, bb[i], acc[5]);
+        dmin = (near && d < dmin) ? d : dmin;
+        dmax = (near && d > dmax) ? d : dmax;
     }
 }
 
@@ -765,21 +769,20 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
     constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 8, fp32 16
     const int lane = threadIdx.x & 63;
     if (chunk_vectors<DT>(qrow, P.V, c) && chunk_vectors<DT>(prow, P.V, c)) {
-        // one vector at a time, the next one's loads in flight
-        uint4 cq = chunk_vec<DT>(qrow, c, 0, lane), cp = chunk_vec<DT>(prow, c, 0, lane);
-#pragma unroll 1
+        // every load of the chunk issued first, then one vector at a time
+        uint4 vq[PER], vp[PER];
+#pragma unroll
         for (int k = 0; k < PER; ++k) {
-            uint4 nq = cq, np = cp;
-            if (k + 1 < PER) {
-                nq = chunk_vec<DT>(qrow, c, k + 1, lane);
-                np = chunk_vec<DT>(prow, c, k + 1, lane);
-            }
+            vq[k] = chunk_vec<DT>(qrow, c, k, lane);
+            vp[k] = chunk_vec<DT>(prow, c, k, lane);
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
             float xq[EPV], xp[EPV];
-            decode16<DT>(cq, xq);
-            decode16<DT>(cp, xp);
+            decode16<DT>(vq[k], xq);
+            decode16<DT>(vp[k], xp);
             residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
-            cq = nq;
-            cp = np;
+            __builtin_amdgcn_sched_barrier(0);
         }
     } else {
 #pragma unroll 1
@@ -805,15 +808,15 @@ __device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qro
         bad |= (x != x) || (x == INFINITY);
     };
     if (chunk_vectors<DT>(qrow, P.V, c)) {
-        uint4 cur = chunk_vec<DT>(qrow, c, 0, lane);
-#pragma unroll 1
+        uint4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[k] = chunk_vec<DT>(qrow, c, k, lane);
+#pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const uint4 nxt = (k + 1 < PER) ? chunk_vec<DT>(qrow, c, k + 1, lane) : cur;
             float x[EPV];
-            decode16<DT>(cur, x);
+            decode16<DT>(v[k], x);
 #pragma unroll
             for (int i = 0; i < EPV; ++i) take(x[i]);
-            cur = nxt;
         }
     } else {
 #pragma unroll 1
@@ -831,17 +834,18 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
     const int lane = threadIdx.x & 63;
     double sa = 0.0;
     if (chunk_vectors<DT>(qrow, P.V, c)) {
-        uint4 cur = chunk_vec<DT>(qrow, c, 0, lane);
-#pragma unroll 1
+        uint4 v[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) v[k] = chunk_vec<DT>(qrow, c, k, lane);
+#pragma unroll
         for (int k = 0; k < PER; ++k) {
-            const uint4 nxt = (k + 1 < PER) ? chunk_vec<DT>(qrow, c, k + 1, lane) : cur;
             float x[EPV];
-            decode16<DT>(cur, x);
+            decode16<DT>(v[k], x);
             double a[EPV];
             exp_vec<TAB, EPV>(ec, x, a);
 #pragma unroll
             for (int i = 0; i < EPV; ++i) sa += a[i];
-            cur = nxt;
+            __builtin_amdgcn_sched_barrier(0);
         }
     } else {
 #pragma unroll 1
@@ -875,8 +879,10 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
     auto vec_p = [&](int t) { return chunk_vec<DT>(prow, ca + t / PER, t % PER, lane); };
     const int tend = (cb - ca) * PER;
     if (tend <= 0) return;
-    // ring of the next D vectors per row; one vector is used per step (a
-    // rolled loop keeps one vector's lookups live at a time)
+    // D slots per row hold the next D vectors; step t uses slot t % D and
+    // refills it with vector t + D.  The loop is unrolled by D so the slots
+    // rotate without register moves (moving a register a load is still
+    // writing would wait for that load).
     uint4 rq[D], rp[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
@@ -886,51 +892,48 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
     double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
     float dmin = INFINITY, dmax = -INFINITY;
 #pragma unroll 1
-    for (int t = 0; t < tend; ++t) {
-        const uint4 vq = rq[0];
-        uint4 vp;
-        if constexpr (!BONUS) vp = rp[0];
+    for (int t0 = 0; t0 < tend; t0 += D) {
 #pragma unroll
-        for (int j = 0; j + 1 < D; ++j) {
-            rq[j] = rq[j + 1];
-            if constexpr (!BONUS) rp[j] = rp[j + 1];
-        }
-        if (t + D < tend) {
-            rq[D - 1] = vec_q(t + D);
-            if constexpr (!BONUS) rp[D - 1] = vec_p(t + D);
-        }
-        float xq[EPV];
-        decode16<DT>(vq, xq);
-        if constexpr (BONUS) {
-            double a[EPV];
-            exp_vec<TAB, EPV>(eq, xq, a);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) acc[0] += a[i];
-        } else {
-            float xp[EPV];
-            decode16<DT>(vp, xp);
-            residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
-        }
-        if ((t + 1) % PER == 0) {
-            ChunkSums out{};
-            if constexpr (BONUS) {
-                out.sa = (double)s.mq;
-                out.sb = wave_sum(acc[0]) * eq.scale;
-            } else {
-                out.sa = wave_sum(acc[0]) * eq.scale;
-                out.sb = wave_sum(acc[1]) * ep.scale;
-                out.pa = wave_sum(acc[2]) * eq.scale;
-                out.pb = wave_sum(acc[3]) * ep.scale;
-                out.na = wave_sum(acc[4]) * eq.scale;
-                out.nb = wave_sum(acc[5]) * ep.scale;
-                out.dmax = wave_max(dmax);
-                out.dmin = -wave_max(-dmin);
+        for (int j = 0; j < D; ++j) {
+            const int t = t0 + j;
+            if (t >= tend) break;
+            float xq[EPV], xp[EPV];
+            decode16<DT>(rq[j], xq);
+            if constexpr (!BONUS) decode16<DT>(rp[j], xp);
+            if (t + D < tend) {
+                rq[j] = vec_q(t + D);
+                if constexpr (!BONUS) rp[j] = vec_p(t + D);
             }
-            if (lane == 0) put_chunk(P, b, ca + t / PER, out);
+            if constexpr (BONUS) {
+                double a[EPV];
+                exp_vec<TAB, EPV>(eq, xq, a);
 #pragma unroll
-            for (int i = 0; i < 6; ++i) acc[i] = 0.0;
-            dmin = INFINITY;
-            dmax = -INFINITY;
+                for (int i = 0; i < EPV; ++i) acc[0] += a[i];
+            } else {
+                residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+            }
+            if ((t + 1) % PER == 0) {
+                ChunkSums out{};
+                if constexpr (BONUS) {
+                    out.sa = (double)s.mq;
+                    out.sb = wave_sum(acc[0]) * eq.scale;
+                } else {
+                    out.sa = wave_sum(acc[0]) * eq.scale;
+                    out.sb = wave_sum(acc[1]) * ep.scale;
+                    out.pa = wave_sum(acc[2]) * eq.scale;
+                    out.pb = wave_sum(acc[3]) * ep.scale;
+                    out.na = wave_sum(acc[4]) * eq.scale;
+                    out.nb = wave_sum(acc[5]) * ep.scale;
+                    out.dmax = wave_max(dmax);
+                    out.dmin = -wave_max(-dmin);
+                }
+                if (lane == 0) put_chunk(P, b, ca + t / PER, out);
+#pragma unroll
+                for (int i = 0; i < 6; ++i) acc[i] = 0.0;
+                dmin = INFINITY;
+                dmax = -INFINITY;
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one vector's work at a time
         }
     }
 }
@@ -1052,6 +1055,9 @@ __device__ void emit(const VerifyParams& P, int b, int k, int token, double resi
     }
 }
 
+// Chunk records the final step keeps in LDS.
+constexpr int kFinalCache = 256;
+
 // Final step of sequence b: wait for its chunks, totals, chunk location,
 // rescan, outputs.
 template <int DT, bool TREE>
@@ -1069,10 +1075,23 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     __shared__ int s_owner;
     __shared__ int s_token;
     __shared__ Staged<DT> s_q, s_p;
-    const bool chunks_ok = wait_records<4>(part_rsrc(P), chunk_off(P, b, 0), nchunks, P.epoch);
-    int timed_out = 0;
-    for (int c = tid; c < nchunks; c += kBlock) timed_out |= (get_chunk(P, b, c).flags & kFlagTimeout) != 0;
+    // the chunk records, waited for once and kept in LDS (the first
+    // kFinalCache of them; later ones are read again when needed)
+    __shared__ ChunkSums s_cs[kFinalCache];
+    int chunks_ok = 1, timed_out = 0;
+    for (int c = tid; c < nchunks; c += kBlock) {
+        u32x4 a[4];
+        if (wait_record<4>(part_rsrc(P), chunk_off(P, b, c), a, P.epoch)) {
+            const ChunkSums v = unpack_chunk(a);
+            timed_out |= (v.flags & kFlagTimeout) != 0;
+            if (c < kFinalCache) s_cs[c] = v;
+        } else {
+            chunks_ok = 0;
+        }
+    }
+    chunks_ok = __syncthreads_and(chunks_ok);
     timed_out = __syncthreads_or(timed_out);
+    auto chunk_at = [&](int c) -> ChunkSums { return c < kFinalCache ? s_cs[c] : get_chunk(P, b, c); };
     if (!chunks_ok || timed_out || s.status) {
         emit<TREE>(P, b, -1, -1, 0.0, path);
         return;
@@ -1090,7 +1109,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     if (mode == kModeResidual) {
         double sqp[2] = {0.0, 0.0};
         for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = get_chunk(P, b, c);
+            const ChunkSums p = chunk_at(c);
             sqp[0] += p.sa;
             sqp[1] += p.sb;
         }
@@ -1101,7 +1120,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         // near-threshold tokens: exact when they share one zq - zp (one ratio
         // q/p), else the chunk is rescanned below with the exact rho
         for (int c = tid; c < nchunks; c += kBlock) {
-            const ChunkSums p = get_chunk(P, b, c);
+            const ChunkSums p = chunk_at(c);
             s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
         }
         __syncthreads();
@@ -1110,7 +1129,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
             stage_chunk<DT>(qrow, P.V, c, s_q);
             stage_chunk<DT>(prow, P.V, c, s_p);
             double w[1] = {0.0};
-#pragma unroll 1
+#pragma unroll
             for (int j = 0; j < kPerThread; ++j) {
                 const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
                 const float d = zq - zp;
@@ -1122,7 +1141,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         }
         double wsum[1] = {0.0};
         for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = get_chunk(P, b, c);
+            const ChunkSums p = chunk_at(c);
             wsum[0] += (p.pa - rho * p.pb) + s_near[c];
         }
         block_sum_n<1>(wsum, red);
@@ -1136,7 +1155,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         float lm = -INFINITY;
         int bad = 0;
         for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = get_chunk(P, b, c);
+            const ChunkSums p = chunk_at(c);
             lm = fmaxf(lm, (float)p.sa);
             bad |= (p.flags & kFlagBad) != 0;
         }
@@ -1148,7 +1167,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         }
     }
     auto chunk_weight = [&](int c) -> double {
-        const ChunkSums p = get_chunk(P, b, c);
+        const ChunkSums p = chunk_at(c);
         if (mode == kModeResidual) return (p.pa - rho * p.pb) + s_near[c];
         if (mode == kModeFallback) return p.sa;
         return (p.sa == -INFINITY) ? 0.0 : p.sb * exp((p.sa - M) * invT);
@@ -1205,7 +1224,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     if (mode == kModeResidual) stage_chunk<DT>(prow, P.V, cs, s_p);
     double scale = 1.0, mc = 0.0;
     if (mode == kModeBonus) {
-        mc = get_chunk(P, b, cs).sa;
+        mc = chunk_at(cs).sa;
         scale = exp((mc - M) * invT);
     }
     const ExpRow ec = exp_row(P, mc, t32);
@@ -1216,9 +1235,14 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         if (mode == kModeFallback) return eq(a);
         return ec(a);
     };
+    // the thread's weights, their lookups issued together, kept for the
+    // sum, the fallback and the walk
+    double wv[kPerThread];
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) wv[j] = weight(j);
     double tsum = 0.0;
-#pragma unroll 1
-    for (int j = 0; j < kPerThread; ++j) tsum += weight(j);
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j) tsum += wv[j];
     double ctotal;
     const double tbase = block_exclusive_scan(tsum, red, &ctotal);
     const double local = (target - cbase) / scale;
@@ -1233,16 +1257,16 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         // no positive weight at or below the threshold in this chunk (only
         // possible through rounding): take its last element of positive weight
         int last = -1;
-#pragma unroll 1
+#pragma unroll
         for (int j = 0; j < kPerThread; ++j)
-            if (weight(j) > 0.0) last = cs * kChunk + tid * kPerThread + j;
+            if (wv[j] > 0.0) last = cs * kChunk + tid * kPerThread + j;
         atomicMax(&s_token, last);
     } else if (tid == s_owner) {
         double cum = tbase;
         int pick = -1, last = -1;
-#pragma unroll 1
+#pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
-            const double wj = weight(j);
+            const double wj = wv[j];
             if (wj > 0.0) {
                 last = j;
                 if (pick < 0 && cum + wj > local) pick = j;
@@ -1286,9 +1310,9 @@ __device__ __forceinline__ void fill_table_share(const VerifyParams& P, int blk,
 
 // Row kernel: block (b, row, segment) streams one segment of a pass-1 row
 // and stores its (m, s) record.  Chains: rows 0..N are q rows 0..N (row N
-// the bonus row) and rows N+1..2N the p rows 0..N-1.  Trees: row 2n is node n's q row and 2n+1 its p
-// row, streamed only for nodes that have a child (an accept test reads them;
-// the others get a placeholder record).  Many small blocks, dispatched as
+// the bonus row) and rows N+1..2N the p rows 0..N-1.  Trees: row 2n is node
+// n's q row and 2n+1 its p row, streamed only for nodes that have a child
+// (an accept test reads them; the others get a placeholder record).  Many small blocks, dispatched as
 // compute units free up, balance the stream better than a resident grid
 // with fixed shares.  Every block also fills its share of the exp table.
 template <int DT, bool TREE>
@@ -1328,7 +1352,7 @@ __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
 // and logits; group 0 writes the accept outputs), forms the chunk sums of its
 // group of chunks of the row(s) b samples from, and the last of b's blocks to
 // finish (an arrival counter per sequence) runs b's final step.
-template <int DT, bool TREE>
+template <int DT>
 __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
 {
     const int b = (int)blockIdx.x / P.groups;
@@ -1342,11 +1366,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
 #else
     const double* t32 = kExp2Table;
 #endif
-    if constexpr (TREE) {
-        tree_accept<DT>(P, b, s_state, s_path, g == 0);
-    } else {
-        if (threadIdx.x < 64) chain_accept<DT>(P, b, s_state, g == 0);
-    }
+    tree_accept<DT>(P, b, s_state, s_path, g == 0);
     __syncthreads();
     const SeqState s = s_state;
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
@@ -1382,7 +1402,72 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
     __syncthreads();
-    if (s_last) sample_final<DT, TREE>(P, b, s, s_path, t32);
+    if (s_last) sample_final<DT, true>(P, b, s, s_path, t32);
+}
+
+// ---------------------------------------------------------------------------
+// Chain sample step in three launches
+// ---------------------------------------------------------------------------
+// Each latency-bound step runs once per sequence, in its own launch: the
+// accept test (one wave per sequence), the chunk sums (many blocks per
+// sequence, where the arithmetic is), the final step (one block per
+// sequence).  Launch boundaries order them; nothing waits on another block.
+
+// Accept test of sequence blockIdx.x into P.seqs (and the accept outputs).
+template <int DT>
+__global__ __launch_bounds__(64) void k_accept(const VerifyParams P)
+{
+    chain_accept<DT>(P, (int)blockIdx.x, P.seqs[blockIdx.x], true);
+}
+
+// Block (b, g): chunk sums of group g of sequence b's chunks, one contiguous
+// share per wave, stored as records.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_chunks(const VerifyParams P)
+{
+    const int b = (int)blockIdx.x / P.groups;
+    const int g = (int)blockIdx.x - b * P.groups;
+    __shared__ double s_t32[32];
+    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
+    __syncthreads();
+    const SeqState s = P.seqs[b];
+    const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
+    const char* qrow = sample_qrow<DT>(P, b, s);
+    const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
+    const ExpRow eq = exp_row(P, s.mq, s_t32), ep = exp_row(P, s.mp, s_t32);
+    const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+    const int wave = (int)threadIdx.x >> 6;
+    const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+    int c = ca;
+    if (s.status == 0 && ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
+        const int whole = min(cb, P.V / kChunk);
+        if (whole > c) {
+            if (s.mode == kModeResidual) {
+                if (eq.tab && ep.tab) chunk_range<DT, true, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+                else chunk_range<DT, false, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            } else {
+                if (eq.tab) chunk_range<DT, true, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+                else chunk_range<DT, false, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+            }
+            c = whole;
+        }
+    }
+    for (; c < cb; ++c) {
+        ChunkSums out{};
+        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_t32);
+        if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
+    }
+}
+
+// Final step of sequence blockIdx.x.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_final(const VerifyParams P)
+{
+    __shared__ double s_t32[32];
+    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
+    __syncthreads();
+    const SeqState s = P.seqs[blockIdx.x];
+    sample_final<DT, false>(P, (int)blockIdx.x, s, nullptr, s_t32);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -1444,7 +1529,7 @@ int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 }
 
 struct Layout {
-    size_t chunk_arr, stats, part, table, total;
+    size_t chunk_arr, seqs, stats, part, table, total;
 };
 
 Layout make_layout(int B, int rows, int V)
@@ -1453,7 +1538,8 @@ Layout make_layout(int B, int rows, int V)
     segments_of(V, &segs, &seg_len);
     Layout L;
     L.chunk_arr = 0;
-    L.stats = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
+    L.seqs = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
+    L.stats = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
     L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
     L.table = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
     L.total = L.table + (size_t)kTableEntries * sizeof(double);
@@ -1485,29 +1571,54 @@ uint32_t next_epoch()
 
 // Sample blocks per sequence: enough for one round of the blocks the device
 // holds at once (a block's four waves share its chunks).
-template <int DT, bool TREE>
+template <int DT>
 void set_groups(sv::VerifyParams& P)
 {
     static std::atomic<int> cache{0};
-    const int resident = resident_blocks(&sv::k_sample<DT, TREE>, cache);
+    const int resident = resident_blocks(&sv::k_sample<DT>, cache);
     int groups = resident > 0 ? resident / (P.B > 0 ? P.B : 1) : 1;
     groups = groups < 1 ? 1 : (groups > P.nch ? P.nch : groups);
     P.cpb = (P.nch + groups - 1) / groups;
     P.groups = (P.nch + P.cpb - 1) / P.cpb;
 }
 
-template <int DT, bool TREE>
-int launch_kernels(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
+// Chunk-sum blocks per sequence (chains): about SV_CHUNKS_PER_BLOCK chunks
+// each.
+#ifndef SV_CHUNKS_PER_BLOCK
+#define SV_CHUNKS_PER_BLOCK 8
+#endif
+template <int DT>
+int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
-    set_groups<DT, TREE>(P);
+    int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
+    groups = groups < 1 ? 1 : groups;
+    P.cpb = (P.nch + groups - 1) / groups;
+    P.groups = (P.nch + P.cpb - 1) / P.cpb;
+    if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((sv::k_rows<DT, false>), dim3((unsigned)((int64_t)P.B * P.r_items)), dim3(sv::kBlock), 0,
+                       stream, P);
+    if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
+    hipLaunchKernelGGL((sv::k_accept<DT>), dim3((unsigned)P.B), dim3(64), 0, stream, P);
+    hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * P.groups)), dim3(sv::kBlock), 0, stream, P);
+    hipLaunchKernelGGL((sv::k_final<DT>), dim3((unsigned)P.B), dim3(sv::kBlock), 0, stream, P);
+    if (hipGetLastError() != hipSuccess) return SV_EHIP;
+    if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
+    return SV_OK;
+}
+
+// Trees: the row kernel, then the sample kernel.
+template <int DT>
+int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
+{
+    set_groups<DT>(P);
     // at least one row block: the row kernel also fills the exp table
     const int64_t row_grid = P.r_items > 0 ? (int64_t)P.B * P.r_items : (P.table ? 1 : 0);
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
     if (row_grid > 0)
-        hipLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
+        hipLaunchKernelGGL((sv::k_rows<DT, true>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
     if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((sv::k_sample<DT, TREE>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
+    hipLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
@@ -1519,6 +1630,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
 {
     char* ws = static_cast<char*>(workspace);
     P.chunk_arrivals = reinterpret_cast<uint64_t*>(ws + L.chunk_arr);
+    P.seqs = reinterpret_cast<sv::SeqState*>(ws + L.seqs);
     P.stats = ws + L.stats;
     P.part = ws + L.part;
     P.stats_bytes = (uint32_t)(L.part - L.stats);
@@ -1526,8 +1638,12 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     const bool table = SV_EXP_TABLE && dtype == SV_BF16;
     P.table = table ? reinterpret_cast<double*>(ws + L.table) : nullptr;
     P.epoch = next_epoch();
-    return dtype == SV_BF16 ? launch_kernels<sv::DT_BF16, TREE>(P, timing, stream)
-                            : launch_kernels<sv::DT_F32, TREE>(P, timing, stream);
+    if constexpr (!TREE)
+        return dtype == SV_BF16 ? launch_chain<sv::DT_BF16>(P, timing, stream)
+                                : launch_chain<sv::DT_F32>(P, timing, stream);
+    else
+        return dtype == SV_BF16 ? launch_tree<sv::DT_BF16>(P, timing, stream)
+                                : launch_tree<sv::DT_F32>(P, timing, stream);
 }
 
 void fill_common(sv::VerifyParams& P, int B, int V, int rows, uint64_t seed, uint64_t round, float temperature)
@@ -1551,7 +1667,7 @@ bool item_count_ok(int B, int rows, int V)
 {
     int segs, seg_len;
     segments_of(V, &segs, &seg_len);
-    return (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * nchunks_of(V) < (int64_t)INT32_MAX;
+    return 2 * (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * nchunks_of(V) < (int64_t)INT32_MAX;
 }
 
 }  // namespace
