@@ -273,7 +273,6 @@ struct VerifyParams {
     char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
     uint32_t stats_bytes, part_bytes;
-    double* table;            // [65536] exp(z/T) per bf16 bit pattern, or null
     // outputs
     int32_t* out_tokens;
     int32_t* out_path;
@@ -395,34 +394,23 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
     return P.zp + ((int64_t)b * P.ps + (int64_t)r * P.pr) * elem_bytes<DT>();
 }
 
-// exp((z - m)/T) over the logits of one row.  For bf16 logits it is the
-// table entry of z's bit pattern, exp(z/T), times exp(-m/T), when |m/T| is
-// small enough that neither factor leaves the double range for the logits of
-// the row (z <= m + T ln 2); otherwise, and for fp32 logits, it is computed.
-// `unscaled` gives the table entry itself (sums over a chunk take the factor
-// exp(-m/T) once).
+// exp((z - m)/T) over the logits of one row, m the row's reference (see
+// exp_rel).
 struct ExpRow {
-    const double* tab;  // exp(v/T) for every bf16 bit pattern v, or null: computed
-    const double* t32;  // 2^(j/32) for the computed path
-    double m, scale, invT;
-    __device__ __forceinline__ double unscaled(float z) const { return tab[__float_as_uint(z) >> 16]; }
-    __device__ __forceinline__ double operator()(float z) const
-    {
-        if (tab) return unscaled(z) * scale;
-        return exp64(((double)z - m) * invT, t32);
-    }
+    double m, invT;
+    lds_dptr t32;  // the block's copy of kExp2Table (see exp_rel)
+    __device__ __forceinline__ double operator()(float z) const { return exp_rel(((double)z - m) * invT, t32); }
 };
 
 __device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* t32)
 {
-    ExpRow e;
-    e.t32 = t32;
-    e.m = m;
-    e.invT = P.invT;
-    const double t = m * P.invT;
-    e.tab = (P.table && fabs(t) <= 600.0) ? P.table : nullptr;
-    e.scale = e.tab ? exp(-t) : 1.0;
-    return e;
+    return ExpRow{m, P.invT, (lds_dptr)t32};
+}
+
+// The block's copy of kExp2Table (call before a barrier).
+__device__ __forceinline__ void fill_t32(double* t32)
+{
+    if (threadIdx.x < 32) t32[threadIdx.x] = kExp2Table[threadIdx.x];
 }
 
 // ===========================================================================
@@ -692,7 +680,16 @@ __device__ __forceinline__ bool chunk_vectors(const char* row, int V, int c)
     return (((uintptr_t)row) & 15u) == 0 && (int64_t)(c + 1) * kChunk <= V;
 }
 
-constexpr int kLaneAhead = 4;  // 16-byte vectors per row a lane keeps in flight
+#ifndef SV_LANE_AHEAD
+#define SV_LANE_AHEAD 2
+#endif
+constexpr int kLaneAhead = SV_LANE_AHEAD;  // 16-byte vectors per row a lane keeps in flight
+#ifndef SV_STEP_BARRIER
+#define SV_STEP_BARRIER 1
+#endif
+#ifndef SV_CHUNK_WAVES
+#define SV_CHUNK_WAVES 0
+#endif
 
 // The lane's k-th vector of chunk c.
 template <int DT>
@@ -711,37 +708,23 @@ __device__ __forceinline__ float chunk_token(const char* row, int V, int c, int 
     return e < V ? load_logit<DT>(row, e) : -INFINITY;
 }
 
-// exp((z - m)/T) / e.scale of one row with the evaluation method fixed at
-// compile time (TAB: ExpRow's table, unscaled; else the fp64 routine, whose
-// scale is 1).
-template <bool TAB>
-__device__ __forceinline__ double exp_of(const ExpRow& e, float z)
-{
-    if constexpr (TAB) return e.unscaled(z);
-    else return exp64(((double)z - e.m) * e.invT, e.t32);
-}
-
-// exp_of of K logits.
-template <bool TAB, int K>
+// ExpRow of K logits.
+template <int K>
 __device__ __forceinline__ void exp_vec(const ExpRow& e, const float* x, double* out)
 {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        if constexpr (TAB) out[i] = e.unscaled(x[i]);
-        else out[i] = exp64(((double)x[i] - e.m) * e.invT, e.t32);
-    }
+    for (int i = 0; i < K; ++i) out[i] = e(x[i]);
 }
 
-// The residual's per-chunk sums (see ChunkSums) over K token pairs, with the
-// exps unscaled as exp_of gives them.
-template <bool TAB, int K>
+// The residual's per-chunk sums (see ChunkSums) over K token pairs.
+template <int K>
 __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, const SeqState& s,
                                              const ExpRow& eq, const ExpRow& ep, double* acc, float& dmin,
                                              float& dmax)
 {
     double a[K], bb[K];
-    exp_vec<TAB, K>(eq, zq, a);
-    exp_vec<TAB, K>(ep, zp, bb);
+    exp_vec<K>(eq, zq, a);
+    exp_vec<K>(ep, zp, bb);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         acc[0] += a[i];
@@ -760,7 +743,7 @@ __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, c
     }
 }
 
-template <int DT, bool TAB>
+template <int DT>
 __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
                                                const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
                                                double* acc, float& dmin, float& dmax)
@@ -781,7 +764,7 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
             float xq[EPV], xp[EPV];
             decode16<DT>(vq[k], xq);
             decode16<DT>(vp[k], xp);
-            residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+            residual_vec<EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -791,7 +774,7 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
             for (int i = 0; i < EPV; ++i) {
                 const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
                 const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
-                residual_vec<TAB, 1>(&zq, &zp, s, eq, ep, acc, dmin, dmax);
+                residual_vec<1>(&zq, &zp, s, eq, ep, acc, dmin, dmax);
             }
     }
 }
@@ -826,7 +809,7 @@ __device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qro
     }
 }
 
-template <int DT, bool TAB>
+template <int DT>
 __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* qrow, int c, const ExpRow& ec)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
@@ -842,7 +825,7 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
             float x[EPV];
             decode16<DT>(v[k], x);
             double a[EPV];
-            exp_vec<TAB, EPV>(ec, x, a);
+            exp_vec<EPV>(ec, x, a);
 #pragma unroll
             for (int i = 0; i < EPV; ++i) sa += a[i];
             __builtin_amdgcn_sched_barrier(0);
@@ -854,7 +837,7 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
             for (int i = 0; i < EPV; ++i) {
                 const float z = chunk_token<DT>(qrow, P.V, c, lane, k, i);
                 double a;
-                exp_vec<TAB, 1>(ec, &z, &a);
+                exp_vec<1>(ec, &z, &a);
                 sa += a;
             }
     }
@@ -866,7 +849,7 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
 // current batch is used, across chunk boundaries.  BONUS: the q row alone,
 // summed against its pass-1 reference s.mq; otherwise the residual's sums
 // over the q and p rows.
-template <int DT, bool TAB, bool BONUS>
+template <int DT, bool BONUS>
 __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
                             int ca, int cb, const ExpRow& eq, const ExpRow& ep)
 {
@@ -906,24 +889,24 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
             }
             if constexpr (BONUS) {
                 double a[EPV];
-                exp_vec<TAB, EPV>(eq, xq, a);
+                exp_vec<EPV>(eq, xq, a);
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) acc[0] += a[i];
             } else {
-                residual_vec<TAB, EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+                residual_vec<EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
             }
             if ((t + 1) % PER == 0) {
                 ChunkSums out{};
                 if constexpr (BONUS) {
                     out.sa = (double)s.mq;
-                    out.sb = wave_sum(acc[0]) * eq.scale;
+                    out.sb = wave_sum(acc[0]);
                 } else {
-                    out.sa = wave_sum(acc[0]) * eq.scale;
-                    out.sb = wave_sum(acc[1]) * ep.scale;
-                    out.pa = wave_sum(acc[2]) * eq.scale;
-                    out.pb = wave_sum(acc[3]) * ep.scale;
-                    out.na = wave_sum(acc[4]) * eq.scale;
-                    out.nb = wave_sum(acc[5]) * ep.scale;
+                    out.sa = wave_sum(acc[0]);
+                    out.sb = wave_sum(acc[1]);
+                    out.pa = wave_sum(acc[2]);
+                    out.pb = wave_sum(acc[3]);
+                    out.na = wave_sum(acc[4]);
+                    out.nb = wave_sum(acc[5]);
                     out.dmax = wave_max(dmax);
                     out.dmin = -wave_max(-dmin);
                 }
@@ -933,7 +916,9 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
                 dmin = INFINITY;
                 dmax = -INFINITY;
             }
+#if SV_STEP_BARRIER
             __builtin_amdgcn_sched_barrier(0);  // one vector's work at a time
+#endif
         }
     }
 }
@@ -948,24 +933,23 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
     if (s.mode == kModeResidual) {
         double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sa sb pa pb na nb
         float dmin = INFINITY, dmax = -INFINITY;
-        if (eq.tab && ep.tab) residual_chunk<DT, true>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
-        else residual_chunk<DT, false>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
+        residual_chunk<DT>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
 #pragma unroll
         for (int i = 0; i < 6; ++i) acc[i] = wave_sum(acc[i]);
-        out.sa = acc[0] * eq.scale;
-        out.sb = acc[1] * ep.scale;
-        out.pa = acc[2] * eq.scale;
-        out.pb = acc[3] * ep.scale;
-        out.na = acc[4] * eq.scale;
-        out.nb = acc[5] * ep.scale;
+        out.sa = acc[0];
+        out.sb = acc[1];
+        out.pa = acc[2];
+        out.pb = acc[3];
+        out.na = acc[4];
+        out.nb = acc[5];
         out.dmax = wave_max(dmax);
         out.dmin = -wave_max(-dmin);
     } else if (s.bonus_ref) {
         // against the row's pass-1 reference (its NaN/+inf check is the
         // pass-1 statistics')
-        const double sa = eq.tab ? bonus_sum<DT, true>(P, qrow, c, eq) : bonus_sum<DT, false>(P, qrow, c, eq);
+        const double sa = bonus_sum<DT>(P, qrow, c, eq);
         out.sa = (double)s.mq;
-        out.sb = wave_sum(sa) * eq.scale;
+        out.sb = wave_sum(sa);
     } else {
         // the chunk maximum first, then the sum relative to it
         float lm = -INFINITY;
@@ -973,14 +957,9 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         bonus_max<DT>(P, qrow, c, lm, bad);
         const float mc = wave_max(lm);
         double sa = 0.0;
-        double scale = 1.0;
-        if (mc != -INFINITY) {
-            const ExpRow ec = exp_row(P, mc, t32);
-            sa = ec.tab ? bonus_sum<DT, true>(P, qrow, c, ec) : bonus_sum<DT, false>(P, qrow, c, ec);
-            scale = ec.scale;
-        }
+        if (mc != -INFINITY) sa = bonus_sum<DT>(P, qrow, c, exp_row(P, mc, t32));
         out.sa = (double)mc;
-        out.sb = wave_sum(sa) * scale;
+        out.sb = wave_sum(sa);
         out.flags = __any(bad) ? kFlagBad : 0u;
     }
     return out;
@@ -1288,38 +1267,16 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
 #define SV_ROW_BATCH 4
 #endif
 constexpr int kRowBatch = SV_ROW_BATCH;
-// Exp table for bf16 logits in the sample kernel (0 computes every exp)
-#ifndef SV_EXP_TABLE
-#define SV_EXP_TABLE 1
-#endif
-// The 32-entry table of the computed exp read from LDS (1) or constant memory
-#ifndef SV_EXP_T32_LDS
-#define SV_EXP_T32_LDS 1
-#endif
-
-// Share of the exp table (exp(v/T) for every bf16 bit pattern v, used by
-// ExpRow) filled by this block of a grid of `nblocks`.
-__device__ __forceinline__ void fill_table_share(const VerifyParams& P, int blk, int nblocks)
-{
-    const int lo = (int)((int64_t)blk * 65536 / nblocks), hi = (int)((int64_t)(blk + 1) * 65536 / nblocks);
-    for (int i = lo + (int)threadIdx.x; i < hi; i += kBlock) {
-        const float v = __uint_as_float((uint32_t)i << 16);
-        P.table[i] = exp((double)v * P.invT);
-    }
-}
-
 // Row kernel: block (b, row, segment) streams one segment of a pass-1 row
 // and stores its (m, s) record.  Chains: rows 0..N are q rows 0..N (row N
 // the bonus row) and rows N+1..2N the p rows 0..N-1.  Trees: row 2n is node
 // n's q row and 2n+1 its p row, streamed only for nodes that have a child
 // (an accept test reads them; the others get a placeholder record).  Many small blocks, dispatched as
 // compute units free up, balance the stream better than a resident grid
-// with fixed shares.  Every block also fills its share of the exp table.
+// with fixed shares.
 template <int DT, bool TREE>
 __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
 {
-    if (P.table) fill_table_share(P, (int)blockIdx.x, (int)gridDim.x);
-    if (P.r_items == 0) return;  // no pass-1 rows: the launch only fills the table
     const int b = (int)blockIdx.x / P.r_items;
     const int idx = (int)blockIdx.x - b * P.r_items;
     const int row = idx / P.segs, seg = idx - row * P.segs;
@@ -1360,19 +1317,14 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     __shared__ SeqState s_state;
     __shared__ int32_t s_path[kMaxNodes];
     __shared__ double s_t32[32];
-    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
-#if SV_EXP_T32_LDS
-    const double* t32 = s_t32;
-#else
-    const double* t32 = kExp2Table;
-#endif
+    fill_t32(s_t32);
     tree_accept<DT>(P, b, s_state, s_path, g == 0);
     __syncthreads();
     const SeqState s = s_state;
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
+    const ExpRow eq = exp_row(P, s.mq, s_t32), ep = exp_row(P, s.mp, s_t32);
     // each wave takes a contiguous share of the block's chunks; whole chunks
     // of aligned rows stream with loads in flight across chunk boundaries
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
@@ -1383,26 +1335,21 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
         ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
         const int whole = min(cb, P.V / kChunk);
         if (whole > c) {
-            if (s.mode == kModeResidual) {
-                if (eq.tab && ep.tab) chunk_range<DT, true, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-                else chunk_range<DT, false, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-            } else {
-                if (eq.tab) chunk_range<DT, true, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-                else chunk_range<DT, false, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-            }
+            if (s.mode == kModeResidual) chunk_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            else chunk_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
             c = whole;
         }
     }
     for (; c < cb; ++c) {
         ChunkSums out{};
-        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, t32);
+        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_t32);
         if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
     }
     __syncthreads();
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
     __syncthreads();
-    if (s_last) sample_final<DT, true>(P, b, s, s_path, t32);
+    if (s_last) sample_final<DT, true>(P, b, s, s_path, s_t32);
 }
 
 // ---------------------------------------------------------------------------
@@ -1423,12 +1370,16 @@ __global__ __launch_bounds__(64) void k_accept(const VerifyParams P)
 // Block (b, g): chunk sums of group g of sequence b's chunks, one contiguous
 // share per wave, stored as records.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void k_chunks(const VerifyParams P)
+__global__ __launch_bounds__(kBlock) void
+#if SV_CHUNK_WAVES
+__attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES, SV_CHUNK_WAVES)))
+#endif
+k_chunks(const VerifyParams P)
 {
     const int b = (int)blockIdx.x / P.groups;
     const int g = (int)blockIdx.x - b * P.groups;
     __shared__ double s_t32[32];
-    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
+    fill_t32(s_t32);
     __syncthreads();
     const SeqState s = P.seqs[b];
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
@@ -1442,13 +1393,8 @@ __global__ __launch_bounds__(kBlock) void k_chunks(const VerifyParams P)
     if (s.status == 0 && ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
         const int whole = min(cb, P.V / kChunk);
         if (whole > c) {
-            if (s.mode == kModeResidual) {
-                if (eq.tab && ep.tab) chunk_range<DT, true, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-                else chunk_range<DT, false, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-            } else {
-                if (eq.tab) chunk_range<DT, true, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-                else chunk_range<DT, false, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-            }
+            if (s.mode == kModeResidual) chunk_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            else chunk_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
             c = whole;
         }
     }
@@ -1464,7 +1410,7 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void k_final(const VerifyParams P)
 {
     __shared__ double s_t32[32];
-    if (threadIdx.x < 32) s_t32[threadIdx.x] = kExp2Table[threadIdx.x];
+    fill_t32(s_t32);
     __syncthreads();
     const SeqState s = P.seqs[blockIdx.x];
     sample_final<DT, false>(P, (int)blockIdx.x, s, nullptr, s_t32);
@@ -1508,7 +1454,6 @@ void segments_of(int V, int* segs, int* seg_len)
     *segs = (V + len - 1) / len;
 }
 
-constexpr int kTableEntries = 65536;
 
 // Blocks of a kernel the device holds at once (compute units x occupancy).
 template <typename K>
@@ -1529,7 +1474,7 @@ int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 }
 
 struct Layout {
-    size_t chunk_arr, seqs, stats, part, table, total;
+    size_t chunk_arr, seqs, stats, part, total;
 };
 
 Layout make_layout(int B, int rows, int V)
@@ -1541,15 +1486,14 @@ Layout make_layout(int B, int rows, int V)
     L.seqs = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
     L.stats = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
     L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
-    L.table = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
-    L.total = L.table + (size_t)kTableEntries * sizeof(double);
+    L.total = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
     return L;
 }
 
 // The record regions are addressed with 32-bit buffer offsets.
 bool regions_fit(const Layout& L)
 {
-    return L.part - L.stats <= (size_t)INT32_MAX && L.table - L.part <= (size_t)INT32_MAX;
+    return L.part - L.stats <= (size_t)INT32_MAX && L.total - L.part <= (size_t)INT32_MAX;
 }
 
 int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
@@ -1587,6 +1531,7 @@ void set_groups(sv::VerifyParams& P)
 #ifndef SV_CHUNKS_PER_BLOCK
 #define SV_CHUNKS_PER_BLOCK 8
 #endif
+// Chains: the row kernel, then the sample step (accept, chunk sums, final).
 template <int DT>
 int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
@@ -1594,13 +1539,14 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
     groups = groups < 1 ? 1 : groups;
     P.cpb = (P.nch + groups - 1) / groups;
     P.groups = (P.nch + P.cpb - 1) / P.cpb;
+    const unsigned B = (unsigned)P.B;
     if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL((sv::k_rows<DT, false>), dim3((unsigned)((int64_t)P.B * P.r_items)), dim3(sv::kBlock), 0,
                        stream, P);
     if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((sv::k_accept<DT>), dim3((unsigned)P.B), dim3(64), 0, stream, P);
+    hipLaunchKernelGGL((sv::k_accept<DT>), dim3(B), dim3(64), 0, stream, P);
     hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * P.groups)), dim3(sv::kBlock), 0, stream, P);
-    hipLaunchKernelGGL((sv::k_final<DT>), dim3((unsigned)P.B), dim3(sv::kBlock), 0, stream, P);
+    hipLaunchKernelGGL((sv::k_final<DT>), dim3(B), dim3(sv::kBlock), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
@@ -1612,7 +1558,7 @@ int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream
 {
     set_groups<DT>(P);
     // at least one row block: the row kernel also fills the exp table
-    const int64_t row_grid = P.r_items > 0 ? (int64_t)P.B * P.r_items : (P.table ? 1 : 0);
+    const int64_t row_grid = (int64_t)P.B * P.r_items;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
     if (row_grid > 0)
@@ -1634,9 +1580,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     P.stats = ws + L.stats;
     P.part = ws + L.part;
     P.stats_bytes = (uint32_t)(L.part - L.stats);
-    P.part_bytes = (uint32_t)(L.table - L.part);
-    const bool table = SV_EXP_TABLE && dtype == SV_BF16;
-    P.table = table ? reinterpret_cast<double*>(ws + L.table) : nullptr;
+    P.part_bytes = (uint32_t)(L.total - L.part);
     P.epoch = next_epoch();
     if constexpr (!TREE)
         return dtype == SV_BF16 ? launch_chain<sv::DT_BF16>(P, timing, stream)

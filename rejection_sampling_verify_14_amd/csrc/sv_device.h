@@ -76,33 +76,62 @@ __device__ __forceinline__ double sample_uniform(uint64_t seed, uint64_t round, 
 }
 
 // ---------------------------------------------------------------------------
-// exp in double: Tang's table-driven method (P.T.P. Tang, "Table-driven
-// implementation of the exponential function in IEEE floating-point
-// arithmetic", ACM TOMS 15(2), 1989).  x = (32 m + j) ln2/32 + r with
-// |r| <= ln2/64; exp(x) = 2^m 2^(j/32) (1 + expm1(r)), expm1 by its Taylor
-// polynomial to r^6/720 (truncation below 4e-18).  About 1.5 ulp.  `tab`
-// holds the 32 values 2^(j/32) (kExp2Table, or a copy in LDS).  Arguments
-// below -746 (and -inf) give 0; NaN is not propagated (callers screen it).
+// exp of a logit relative to its row's reference, in double (Tang's
+// table-driven method, P.T.P. Tang, ACM TOMS 15(2), 1989).  x = (32 m + j)
+// ln2/32 + r with |r| <= ln2/64; exp(x) = 2^m 2^(j/32) (1 + r + r^2/2 + r^3/6
+// + r^4/24), whose truncation is below 1.3e-12 relative.  2^(j/32) comes from
+// the block's LDS copy of kExp2Table: its 32 doubles sit in distinct banks,
+// so a wave's lookups never conflict.  Every step is a full-rate operation:
+// the rounding of 32x/ln2 adds 1.5 * 2^52 (the low word then holds it) and
+// 2^m is added to the exponent field.  x below -40 gives 0: such a term is
+// below 5e-18 of the reference term exp(0) that every row holds, and 2^21 of
+// them stay below 1e-11 of the row's sum.  x must not exceed 700 (callers'
+// references are within 6T of their row's maximum).  NaN is not propagated
+// (callers screen it).
+//
+// SV_EXP_TANG 0 selects the form that reads exp(j/32), j = -1280..256, from
+// kExpTable in global memory instead (|r| <= 1/64, truncation below 8e-12;
+// x clamped to [-41, 8]): fewer operations, but a table read through the
+// memory pipeline per exp.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ double exp64(double x, const double* __restrict__ tab)
+#ifndef SV_EXP_TANG
+#define SV_EXP_TANG 1
+#endif
+typedef const double __attribute__((address_space(3)))* lds_dptr;  // LDS-typed: ds_read, 32-bit address
+
+__device__ __forceinline__ double exp_rel(double x, lds_dptr t32)
 {
-    x = fmax(x, -746.0);
-    const double n = rint(x * k32ByLn2);
-    const int ni = (int)n;
-    double r = fma(-n, kLn2By32Hi, x);
-    r = fma(-n, kLn2By32Lo, r);
-    double p = fma(r, 1.0 / 720.0, 1.0 / 120.0);
-    p = fma(r, p, 1.0 / 24.0);
-    p = fma(r, p, 1.0 / 6.0);
+    constexpr double kRound = 0x1.8p52;
+#if SV_EXP_TANG
+    const bool zero = x < -40.0;
+    x = fmax(x, -41.0);
+    const double kd = fma(x, k32ByLn2, kRound);
+    const int n = (int)(uint32_t)__double_as_longlong(kd);
+    const double nd = kd - kRound;
+    double r = fma(-nd, kLn2By32Hi, x);
+    r = fma(-nd, kLn2By32Lo, r);
+    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
     p = fma(r, p, 0.5);
     p = fma(r, p, 1.0);
     p *= r;
-    const double t = tab[ni & 31];
-    return ldexp(fma(t, p, t), ni >> 5);
+    const double t = t32[n & 31];
+    const double v = fma(t, p, t);
+    const double sc = __longlong_as_double(__double_as_longlong(v) + ((long long)(n >> 5) << 52));
+    return zero ? 0.0 : sc;
+#else
+    (void)t32;
+    x = fmin(fmax(x, -41.0), 8.0);
+    const double kd = fma(x, 32.0, kRound);
+    const int j = (int)(uint32_t)__double_as_longlong(kd);
+    const double r = fma(kd - kRound, -1.0 / 32.0, x);  // exact
+    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+    p = fma(r, p, 0.5);
+    p = fma(r, p, 1.0);
+    p *= r;
+    const double t = kExpTable[max(j, kExpTabLo - 1) - (kExpTabLo - 1)];
+    return fma(t, p, t);
+#endif
 }
-
-// exp64 with the 2^(j/32) table read from constant memory.
-__device__ __forceinline__ double exp64(double x) { return exp64(x, kExp2Table); }
 
 // ---------------------------------------------------------------------------
 // Logits
