@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 PROFILE_PMC = os.path.join(ROOT, "profiles", "k_rows_c3_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
-                  for f in ("specverify.hip", "sv_device.h")]
+                  for f in ("specverify.hip", "sv_device.h", "sv_exp_table.h")]
 
 
 def log(msg):

@@ -39,12 +39,11 @@
  *     different workspaces and outputs.  The only process-wide state is a
  *     call counter (an atomic) that tags each call's results, and cached
  *     occupancy figures.
- *   - Each verify call is two kernel launches: row statistics, then accept
- *     and sampling.  For chains the row-statistics work is split into equal
- *     ranges, one per wave the device holds at once, so the summation order
- *     of a row's statistics (and with it the last bits of q(d), p(d)) depends
- *     on B, N, V and the device's compute-unit count; decisions and tokens
- *     differ only where a uniform falls within rounding of a threshold.
+ *   - A chain verify call is four kernel launches (row statistics, accept,
+ *     chunk sums, final step); a tree verify call is two (row statistics,
+ *     accept and sampling).  Row statistics are summed per fixed segment of
+ *     about 32K tokens and combined in segment order, so results do not
+ *     depend on the device's compute-unit count.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -72,8 +71,9 @@ enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
 /* Optional timing hook: when non-NULL, each non-NULL event is recorded on
  * `stream`: `begin` right before the row-statistics kernel, `rows_done`
- * between it and the accept/sampling kernel, `end` right after the latter,
- * so a caller can time each kernel. */
+ * between it and the kernels of the sample step, `end` right after them, so
+ * a caller can time the row kernel and the sample step.  The records sit
+ * between kernels on the stream; timing costs a few microseconds a call. */
 typedef struct sv_timing {
     hipEvent_t begin;
     hipEvent_t rows_done;
