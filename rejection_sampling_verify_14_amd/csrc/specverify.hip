@@ -395,16 +395,16 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
 }
 
 // exp((z - m)/T) over the logits of one row, m the row's reference (see
-// exp_rel).
+// exp_rel); the argument is one fma, z/T - m/T.
 struct ExpRow {
-    double m, invT;
-    lds_dptr t32;  // the block's copy of kExp2Table (see exp_rel)
-    __device__ __forceinline__ double operator()(float z) const { return exp_rel(((double)z - m) * invT, t32); }
+    double invT, mb;  // 1/T and -m/T
+    lds_dptr t32;     // the block's copy of kExp2Table (see exp_rel)
+    __device__ __forceinline__ double operator()(float z) const { return exp_rel(fma((double)z, invT, mb), t32); }
 };
 
 __device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* t32)
 {
-    return ExpRow{m, P.invT, (lds_dptr)t32};
+    return ExpRow{P.invT, -m * P.invT, (lds_dptr)t32};
 }
 
 // The block's copy of kExp2Table (call before a barrier).
@@ -688,7 +688,7 @@ constexpr int kLaneAhead = SV_LANE_AHEAD;  // 16-byte vectors per row a lane kee
 #define SV_STEP_BARRIER 1
 #endif
 #ifndef SV_CHUNK_WAVES
-#define SV_CHUNK_WAVES 0
+#define SV_CHUNK_WAVES 4
 #endif
 
 // The lane's k-th vector of chunk c.
@@ -716,11 +716,28 @@ __device__ __forceinline__ void exp_vec(const ExpRow& e, const float* x, double*
     for (int i = 0; i < K; ++i) out[i] = e(x[i]);
 }
 
-// The residual's per-chunk sums (see ChunkSums) over K token pairs.
+// Centre and widened half-width of the near-threshold band [thr_lo, thr_hi]
+// as a test |d - mid| <= hw that every d in the band passes despite the
+// rounding of d - mid; tokens it admits beyond the band only trigger
+// near_chunk, whose own test is the exact one.
+struct NearBand {
+    float mid, hw;
+};
+
+__device__ __forceinline__ NearBand near_band(const SeqState& s)
+{
+    const float mid = 0.5f * s.thr_lo + 0.5f * s.thr_hi;
+    const float hw = (0.5f * s.thr_hi - 0.5f * s.thr_lo) * 1.001f + fabsf(mid) * 0x1.0p-20f + 0x1.0p-100f;
+    return {mid, hw};
+}
+
+// The residual's all-token and certain-region sums (sa sb pa pb of
+// ChunkSums) over K token pairs; nd tracks the smallest |d - mid| (see
+// NearBand), so a lane saw a near-threshold token iff nd <= hw.
 template <int K>
 __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, const SeqState& s,
-                                             const ExpRow& eq, const ExpRow& ep, double* acc, float& dmin,
-                                             float& dmax)
+                                             const NearBand& nb, const ExpRow& eq, const ExpRow& ep,
+                                             double* acc, float& nd)
 {
     double a[K], bb[K];
     exp_vec<K>(eq, zq, a);
@@ -730,27 +747,58 @@ __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, c
         acc[0] += a[i];
         acc[1] += bb[i];
         const float d = zq[i] - zp[i];
-        // 0/1 factors: fma with 1 adds exactly, with 0 leaves the sum
-        const bool above = d > s.thr_hi;
-        const bool near = !above && d >= s.thr_lo;
-        const double fa = above ? 1.0 : 0.0, fn = near ? 1.0 : 0.0;
+        // a 0/1 factor: fma with 1 adds exactly, with 0 leaves the sum
+        const double fa = d > s.thr_hi ? 1.0 : 0.0;
         acc[2] = fma(fa, a[i], acc[2]);
         acc[3] = fma(fa, bb[i], acc[3]);
-        acc[4] = fma(fn, a[i], acc[4]);
-        acc[5] = fma(fn, bb[i], acc[5]);
-        dmin = (near && d < dmin) ? d : dmin;
-        dmax = (near && d > dmax) ? d : dmax;
+        nd = fminf(nd, fabsf(d - nb.mid));  // NaN d leaves nd
     }
 }
 
+// Near-threshold band of chunk c (na nb dmin dmax of ChunkSums), element by
+// element in the lane order of the vector loops, so each lane's sums equal
+// those the fused loop would form.  Taken only when a wave saw a near token
+// in the chunk (none in most chunks).
 template <int DT>
-__device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
+__device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
+                                           const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
+                                           ChunkSums& out)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    constexpr int PER = kChunk / EPV / 64;
+    const int lane = threadIdx.x & 63;
+    double na = 0.0, nb = 0.0;
+    float dmin = INFINITY, dmax = -INFINITY;
+#pragma unroll 1
+    for (int k = 0; k < PER; ++k)
+#pragma unroll 1
+        for (int i = 0; i < EPV; ++i) {
+            const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
+            const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
+            const float d = zq - zp;
+            if (d >= s.thr_lo && !(d > s.thr_hi)) {
+                na += eq(zq);
+                nb += ep(zp);
+                dmin = fminf(dmin, d);
+                dmax = fmaxf(dmax, d);
+            }
+        }
+    out.na = wave_sum(na);
+    out.nb = wave_sum(nb);
+    out.dmax = wave_max(dmax);
+    out.dmin = -wave_max(-dmin);
+}
+
+template <int DT>
+__device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
                                                const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
-                                               double* acc, float& dmin, float& dmax)
+                                               double* acc)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 8, fp32 16
     const int lane = threadIdx.x & 63;
+    const NearBand nb = near_band(s);
+    float nd = INFINITY;
     if (chunk_vectors<DT>(qrow, P.V, c) && chunk_vectors<DT>(prow, P.V, c)) {
         // every load of the chunk issued first, then one vector at a time
         uint4 vq[PER], vp[PER];
@@ -764,7 +812,7 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
             float xq[EPV], xp[EPV];
             decode16<DT>(vq[k], xq);
             decode16<DT>(vp[k], xp);
-            residual_vec<EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+            residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -774,9 +822,10 @@ __device__ __forceinline__ void residual_chunk(const VerifyParams& P, const SeqS
             for (int i = 0; i < EPV; ++i) {
                 const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
                 const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
-                residual_vec<1>(&zq, &zp, s, eq, ep, acc, dmin, dmax);
+                residual_vec<1>(&zq, &zp, s, nb, eq, ep, acc, nd);
             }
     }
+    return nd <= nb.hw;
 }
 
 // Maximum and NaN/+inf flag of the lane's tokens of a chunk.
@@ -872,8 +921,9 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
         rq[j] = j < tend ? vec_q(j) : rq[0];
         if constexpr (!BONUS) rp[j] = j < tend ? vec_p(j) : rp[0];
     }
-    double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    float dmin = INFINITY, dmax = -INFINITY;
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    const NearBand nb = near_band(s);
+    float nd = INFINITY;
 #pragma unroll 1
     for (int t0 = 0; t0 < tend; t0 += D) {
 #pragma unroll
@@ -893,9 +943,10 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) acc[0] += a[i];
             } else {
-                residual_vec<EPV>(xq, xp, s, eq, ep, acc, dmin, dmax);
+                residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
             }
             if ((t + 1) % PER == 0) {
+                const int c = ca + t / PER;
                 ChunkSums out{};
                 if constexpr (BONUS) {
                     out.sa = (double)s.mq;
@@ -905,16 +956,14 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
                     out.sb = wave_sum(acc[1]);
                     out.pa = wave_sum(acc[2]);
                     out.pb = wave_sum(acc[3]);
-                    out.na = wave_sum(acc[4]);
-                    out.nb = wave_sum(acc[5]);
-                    out.dmax = wave_max(dmax);
-                    out.dmin = -wave_max(-dmin);
+                    out.dmin = INFINITY;
+                    out.dmax = -INFINITY;
+                    if (__ballot(nd <= nb.hw)) near_chunk<DT>(P, s, qrow, prow, c, eq, ep, out);
+                    nd = INFINITY;
                 }
-                if (lane == 0) put_chunk(P, b, ca + t / PER, out);
+                if (lane == 0) put_chunk(P, b, c, out);
 #pragma unroll
-                for (int i = 0; i < 6; ++i) acc[i] = 0.0;
-                dmin = INFINITY;
-                dmax = -INFINITY;
+                for (int i = 0; i < 4; ++i) acc[i] = 0.0;
             }
 #if SV_STEP_BARRIER
             __builtin_amdgcn_sched_barrier(0);  // one vector's work at a time
@@ -931,19 +980,17 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
 {
     ChunkSums out{};
     if (s.mode == kModeResidual) {
-        double acc[6] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // sa sb pa pb na nb
-        float dmin = INFINITY, dmax = -INFINITY;
-        residual_chunk<DT>(P, s, qrow, prow, c, eq, ep, acc, dmin, dmax);
+        double acc[4] = {0.0, 0.0, 0.0, 0.0};  // sa sb pa pb
+        const bool near = residual_chunk<DT>(P, s, qrow, prow, c, eq, ep, acc);
 #pragma unroll
-        for (int i = 0; i < 6; ++i) acc[i] = wave_sum(acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = wave_sum(acc[i]);
         out.sa = acc[0];
         out.sb = acc[1];
         out.pa = acc[2];
         out.pb = acc[3];
-        out.na = acc[4];
-        out.nb = acc[5];
-        out.dmax = wave_max(dmax);
-        out.dmin = -wave_max(-dmin);
+        out.dmin = INFINITY;
+        out.dmax = -INFINITY;
+        if (__ballot(near)) near_chunk<DT>(P, s, qrow, prow, c, eq, ep, out);
     } else if (s.bonus_ref) {
         // against the row's pass-1 reference (its NaN/+inf check is the
         // pass-1 statistics')
@@ -1372,7 +1419,7 @@ __global__ __launch_bounds__(64) void k_accept(const VerifyParams P)
 template <int DT>
 __global__ __launch_bounds__(kBlock) void
 #if SV_CHUNK_WAVES
-__attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES, SV_CHUNK_WAVES)))
+__attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
 #endif
 k_chunks(const VerifyParams P)
 {

@@ -76,61 +76,38 @@ __device__ __forceinline__ double sample_uniform(uint64_t seed, uint64_t round, 
 }
 
 // ---------------------------------------------------------------------------
-// exp of a logit relative to its row's reference, in double (Tang's
-// table-driven method, P.T.P. Tang, ACM TOMS 15(2), 1989).  x = (32 m + j)
-// ln2/32 + r with |r| <= ln2/64; exp(x) = 2^m 2^(j/32) (1 + r + r^2/2 + r^3/6
-// + r^4/24), whose truncation is below 1.3e-12 relative.  2^(j/32) comes from
-// the block's LDS copy of kExp2Table: its 32 doubles sit in distinct banks,
-// so a wave's lookups never conflict.  Every step is a full-rate operation:
-// the rounding of 32x/ln2 adds 1.5 * 2^52 (the low word then holds it) and
-// 2^m is added to the exponent field.  x below -40 gives 0: such a term is
-// below 5e-18 of the reference term exp(0) that every row holds, and 2^21 of
-// them stay below 1e-11 of the row's sum.  x must not exceed 700 (callers'
-// references are within 6T of their row's maximum).  NaN is not propagated
-// (callers screen it).
+// exp(x) in double by Tang's table-driven method (P.T.P. Tang, ACM TOMS
+// 15(2), 1989): n = round(32x/ln2), r = x - n ln2/32, so |r| <= ln2/64 up to
+// rounding, and exp(x) = 2^(n>>5) 2^((n&31)/32) exp(r) with exp(r) - 1 from
+// its Taylor polynomial of degree 4 (truncation below 1.3e-12 relative).
+// 2^((n&31)/32) comes from the block's LDS copy of kExp2Table: its 32
+// doubles sit in distinct banks, so a wave's lookups never conflict.
 //
-// SV_EXP_TANG 0 selects the form that reads exp(j/32), j = -1280..256, from
-// kExpTable in global memory instead (|r| <= 1/64, truncation below 8e-12;
-// x clamped to [-41, 8]): fewer operations, but a table read through the
-// memory pipeline per exp.
+// r is formed by one fma against ln2/32 rounded to a double: the product is
+// exact inside the fma, and the rounding of the constant shifts r by at most
+// |n| * 2.4e-18, below 1e-14 relative for |x| <= 40 and below 8e-14 over the
+// whole clamped range.  n is the low word of 32x/ln2 + 1.5 * 2^52.  x is
+// clamped below at -1000, where 2^(n>>5) underflows ldexp to exactly 0, so a
+// masked logit (-inf) contributes nothing; terms between exp(-745) and
+// exp(-708) come out as denormals.  x must not exceed 700 (callers' x are
+// relative to their row's reference, so at most 6T or so).  NaN is not
+// propagated (callers screen it).  About 15 full-rate operations.
 // ---------------------------------------------------------------------------
-#ifndef SV_EXP_TANG
-#define SV_EXP_TANG 1
-#endif
 typedef const double __attribute__((address_space(3)))* lds_dptr;  // LDS-typed: ds_read, 32-bit address
 
 __device__ __forceinline__ double exp_rel(double x, lds_dptr t32)
 {
     constexpr double kRound = 0x1.8p52;
-#if SV_EXP_TANG
-    const bool zero = x < -40.0;
-    x = fmax(x, -41.0);
+    x = fmax(x, -1000.0);
     const double kd = fma(x, k32ByLn2, kRound);
     const int n = (int)(uint32_t)__double_as_longlong(kd);
-    const double nd = kd - kRound;
-    double r = fma(-nd, kLn2By32Hi, x);
-    r = fma(-nd, kLn2By32Lo, r);
+    const double r = fma(kd - kRound, -kLn2By32, x);
     double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
     p = fma(r, p, 0.5);
     p = fma(r, p, 1.0);
     p *= r;
     const double t = t32[n & 31];
-    const double v = fma(t, p, t);
-    const double sc = __longlong_as_double(__double_as_longlong(v) + ((long long)(n >> 5) << 52));
-    return zero ? 0.0 : sc;
-#else
-    (void)t32;
-    x = fmin(fmax(x, -41.0), 8.0);
-    const double kd = fma(x, 32.0, kRound);
-    const int j = (int)(uint32_t)__double_as_longlong(kd);
-    const double r = fma(kd - kRound, -1.0 / 32.0, x);  // exact
-    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-    p = fma(r, p, 0.5);
-    p = fma(r, p, 1.0);
-    p *= r;
-    const double t = kExpTable[max(j, kExpTabLo - 1) - (kExpTabLo - 1)];
-    return fma(t, p, t);
-#endif
+    return ldexp(fma(t, p, t), n >> 5);
 }
 
 // ---------------------------------------------------------------------------
