@@ -670,20 +670,32 @@ __device__ __forceinline__ const char* sample_prow(const VerifyParams& P, int b,
 
 // A wave's view of a chunk: lane `lane` owns the 16-byte vectors
 // lane + 64*k, k < kChunk / (64 * elements per vector), so each load
-// instruction of the wave reads 1 KB of consecutive bytes.  A chunk takes
-// the vector path when its row is 16-byte aligned and it ends at or before V
-// (every chunk but possibly the last); otherwise its tokens are read one by
-// one (-inf past V).
+// instruction of the wave reads 1 KB of consecutive bytes.  Rows that are
+// 16-byte aligned with V a whole number of vectors are read as vectors, each
+// wholly inside the row or wholly past V (then -inf, chunk_vec_tail); other
+// rows token by token.
 template <int DT>
-__device__ __forceinline__ bool chunk_vectors(const char* row, int V, int c)
+__device__ __forceinline__ bool row_vectors(const char* row, int V)
 {
-    return (((uintptr_t)row) & 15u) == 0 && (int64_t)(c + 1) * kChunk <= V;
+    return (((uintptr_t)row) & 15u) == 0 && V % (16 / elem_bytes<DT>()) == 0;
+}
+
+// Whether chunk c ends at or before V (every chunk but possibly the last).
+__device__ __forceinline__ bool chunk_whole(int V, int c)
+{
+    return (int64_t)(c + 1) * kChunk <= V;
 }
 
 #ifndef SV_LANE_AHEAD
 #define SV_LANE_AHEAD 2
 #endif
-constexpr int kLaneAhead = SV_LANE_AHEAD;  // 16-byte vectors per row a lane keeps in flight
+#ifndef SV_BONUS_AHEAD
+#define SV_BONUS_AHEAD 4
+#endif
+// 16-byte vectors per row a lane keeps in flight: two rows of residual
+// steps, or one row of the shorter bonus steps
+constexpr int kLaneAhead = SV_LANE_AHEAD;
+constexpr int kBonusAhead = SV_BONUS_AHEAD;
 #ifndef SV_STEP_BARRIER
 #define SV_STEP_BARRIER 1
 #endif
@@ -706,6 +718,32 @@ __device__ __forceinline__ float chunk_token(const char* row, int V, int c, int 
     constexpr int EPV = 16 / elem_bytes<DT>();
     const int64_t e = (int64_t)c * kChunk + (int64_t)(lane + 64 * k) * EPV + i;
     return e < V ? load_logit<DT>(row, e) : -INFINITY;
+}
+
+// The lane's k-th vector of chunk c of a row that row_vectors admits, -inf
+// past V.
+template <int DT>
+__device__ __forceinline__ uint4 chunk_vec_tail(const char* __restrict__ row, int V, int c, int k, int lane)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    const int64_t e0 = (int64_t)c * kChunk + (int64_t)(64 * k + lane) * EPV;
+    if (e0 < V) return chunk_vec<DT>(row, c, k, lane);
+    const uint32_t ninf = DT == DT_BF16 ? 0xFF80FF80u : 0xFF800000u;
+    return make_uint4(ninf, ninf, ninf, ninf);
+}
+
+// The lane's k-th vector of chunk c, decoded, for any row (vec: the row
+// passes row_vectors).
+template <int DT>
+__device__ __forceinline__ void chunk_elems(const char* row, bool vec, int V, int c, int k, int lane, float* x)
+{
+    constexpr int EPV = 16 / elem_bytes<DT>();
+    if (vec) {
+        decode16<DT>(chunk_vec_tail<DT>(row, V, c, k, lane), x);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) x[i] = chunk_token<DT>(row, V, c, lane, k, i);
+    }
 }
 
 // ExpRow of K logits.
@@ -767,45 +805,50 @@ __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;
     const int lane = threadIdx.x & 63;
+    const bool vec = row_vectors<DT>(qrow, P.V) && row_vectors<DT>(prow, P.V);
     double na = 0.0, nb = 0.0;
     float dmin = INFINITY, dmax = -INFINITY;
 #pragma unroll 1
-    for (int k = 0; k < PER; ++k)
-#pragma unroll 1
+    for (int k = 0; k < PER; ++k) {
+        float xq[EPV], xp[EPV];
+        chunk_elems<DT>(qrow, vec, P.V, c, k, lane, xq);
+        chunk_elems<DT>(prow, vec, P.V, c, k, lane, xp);
+#pragma unroll
         for (int i = 0; i < EPV; ++i) {
-            const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
-            const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
-            const float d = zq - zp;
+            const float d = xq[i] - xp[i];
             if (d >= s.thr_lo && !(d > s.thr_hi)) {
-                na += eq(zq);
-                nb += ep(zp);
+                na += eq(xq[i]);
+                nb += ep(xp[i]);
                 dmin = fminf(dmin, d);
                 dmax = fmaxf(dmax, d);
             }
         }
+    }
     out.na = wave_sum(na);
     out.nb = wave_sum(nb);
     out.dmax = wave_max(dmax);
     out.dmin = -wave_max(-dmin);
 }
 
+// The residual's sums over chunk c by one wave (see residual_vec); returns
+// whether the wave saw a near-threshold token.  Vector rows: every load of
+// the chunk issued first, then one vector at a time.
 template <int DT>
 __device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
                                                const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
                                                double* acc)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
-    constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 8, fp32 16
+    constexpr int PER = kChunk / EPV / 64;  // vectors per lane: bf16 4, fp32 8
     const int lane = threadIdx.x & 63;
     const NearBand nb = near_band(s);
     float nd = INFINITY;
-    if (chunk_vectors<DT>(qrow, P.V, c) && chunk_vectors<DT>(prow, P.V, c)) {
-        // every load of the chunk issued first, then one vector at a time
+    if (row_vectors<DT>(qrow, P.V) && row_vectors<DT>(prow, P.V)) {
         uint4 vq[PER], vp[PER];
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
-            vq[k] = chunk_vec<DT>(qrow, c, k, lane);
-            vp[k] = chunk_vec<DT>(prow, c, k, lane);
+            vq[k] = chunk_vec_tail<DT>(qrow, P.V, c, k, lane);
+            vp[k] = chunk_vec_tail<DT>(prow, P.V, c, k, lane);
         }
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
@@ -817,13 +860,12 @@ __device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqS
         }
     } else {
 #pragma unroll 1
-        for (int k = 0; k < PER; ++k)
-#pragma unroll 1
-            for (int i = 0; i < EPV; ++i) {
-                const float zq = chunk_token<DT>(qrow, P.V, c, lane, k, i);
-                const float zp = chunk_token<DT>(prow, P.V, c, lane, k, i);
-                residual_vec<1>(&zq, &zp, s, nb, eq, ep, acc, nd);
-            }
+        for (int k = 0; k < PER; ++k) {
+            float xq[EPV], xp[EPV];
+            chunk_elems<DT>(qrow, false, P.V, c, k, lane, xq);
+            chunk_elems<DT>(prow, false, P.V, c, k, lane, xp);
+            residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
+        }
     }
     return nd <= nb.hw;
 }
@@ -835,26 +877,30 @@ __device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qro
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;
     const int lane = threadIdx.x & 63;
-    auto take = [&](float x) {
-        lm = fmaxf(lm, x);
-        bad |= (x != x) || (x == INFINITY);
+    auto take = [&](const float* x) {
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            lm = fmaxf(lm, x[i]);
+            bad |= (x[i] != x[i]) || (x[i] == INFINITY);
+        }
     };
-    if (chunk_vectors<DT>(qrow, P.V, c)) {
+    if (row_vectors<DT>(qrow, P.V)) {
         uint4 v[PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) v[k] = chunk_vec<DT>(qrow, c, k, lane);
+        for (int k = 0; k < PER; ++k) v[k] = chunk_vec_tail<DT>(qrow, P.V, c, k, lane);
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             float x[EPV];
             decode16<DT>(v[k], x);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) take(x[i]);
+            take(x);
         }
     } else {
 #pragma unroll 1
-        for (int k = 0; k < PER; ++k)
-#pragma unroll 1
-            for (int i = 0; i < EPV; ++i) take(chunk_token<DT>(qrow, P.V, c, lane, k, i));
+        for (int k = 0; k < PER; ++k) {
+            float x[EPV];
+            chunk_elems<DT>(qrow, false, P.V, c, k, lane, x);
+            take(x);
+        }
     }
 }
 
@@ -865,30 +911,30 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
     constexpr int PER = kChunk / EPV / 64;
     const int lane = threadIdx.x & 63;
     double sa = 0.0;
-    if (chunk_vectors<DT>(qrow, P.V, c)) {
+    auto add = [&](const float* x) {
+        double a[EPV];
+        exp_vec<EPV>(ec, x, a);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) sa += a[i];
+    };
+    if (row_vectors<DT>(qrow, P.V)) {
         uint4 v[PER];
 #pragma unroll
-        for (int k = 0; k < PER; ++k) v[k] = chunk_vec<DT>(qrow, c, k, lane);
+        for (int k = 0; k < PER; ++k) v[k] = chunk_vec_tail<DT>(qrow, P.V, c, k, lane);
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             float x[EPV];
             decode16<DT>(v[k], x);
-            double a[EPV];
-            exp_vec<EPV>(ec, x, a);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) sa += a[i];
+            add(x);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
 #pragma unroll 1
-        for (int k = 0; k < PER; ++k)
-#pragma unroll 1
-            for (int i = 0; i < EPV; ++i) {
-                const float z = chunk_token<DT>(qrow, P.V, c, lane, k, i);
-                double a;
-                exp_vec<1>(ec, &z, &a);
-                sa += a;
-            }
+        for (int k = 0; k < PER; ++k) {
+            float x[EPV];
+            chunk_elems<DT>(qrow, false, P.V, c, k, lane, x);
+            add(x);
+        }
     }
     return sa;
 }
@@ -904,7 +950,7 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;  // vectors per lane per chunk: bf16 4, fp32 8
-    constexpr int D = kLaneAhead;
+    constexpr int D = BONUS ? kBonusAhead : kLaneAhead;
     const int lane = threadIdx.x & 63;
     // the lane's t-th vector of the range: vector k = t % PER of chunk ca + t / PER
     auto vec_q = [&](int t) { return chunk_vec<DT>(qrow, ca + t / PER, t % PER, lane); };
@@ -1426,9 +1472,9 @@ k_chunks(const VerifyParams P)
     const int b = (int)blockIdx.x / P.groups;
     const int g = (int)blockIdx.x - b * P.groups;
     __shared__ double s_t32[32];
+    const SeqState s = P.seqs[b];  // in flight with the table fill
     fill_t32(s_t32);
     __syncthreads();
-    const SeqState s = P.seqs[b];
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
@@ -1457,9 +1503,9 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void k_final(const VerifyParams P)
 {
     __shared__ double s_t32[32];
+    const SeqState s = P.seqs[blockIdx.x];  // in flight with the table fill
     fill_t32(s_t32);
     __syncthreads();
-    const SeqState s = P.seqs[blockIdx.x];
     sample_final<DT, false>(P, (int)blockIdx.x, s, nullptr, s_t32);
 }
 
@@ -1576,7 +1622,7 @@ void set_groups(sv::VerifyParams& P)
 // Chunk-sum blocks per sequence (chains): about SV_CHUNKS_PER_BLOCK chunks
 // each.
 #ifndef SV_CHUNKS_PER_BLOCK
-#define SV_CHUNKS_PER_BLOCK 8
+#define SV_CHUNKS_PER_BLOCK 4
 #endif
 // Chains: the row kernel, then the sample step (accept, chunk sums, final).
 template <int DT>
