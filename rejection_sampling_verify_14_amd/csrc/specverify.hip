@@ -363,23 +363,55 @@ __device__ __forceinline__ ChunkSums get_chunk(const VerifyParams& P, int b, int
     return unpack_chunk(a);
 }
 
-// Statistics of pass-1 row `row` of sequence b from the records of its
-// segments.  A record that is not this call's (never expected) poisons the
-// result.
-__device__ __forceinline__ RowStat load_row_stat(const VerifyParams& P, int b, int row)
+// Statistics of pass-1 rows from the records of their segments, kStatBatch
+// segments per batch: every record of a batch is requested before any is
+// used, so a batch costs one memory round trip.  A record that is not this
+// call's (never expected) poisons the row's result (NaN sum).
+constexpr int kStatBatch = 8;
+
+// Requests the records of segments [i0, i0 + kStatBatch) of row `row` of b.
+__device__ __forceinline__ void issue_row_stat(const VerifyParams& P, int b, int row, int i0, u32x4* a)
 {
     const __amdgpu_buffer_rsrc_t r = stats_rsrc(P);
     const int64_t grow = (int64_t)b * P.rows + row;
-    RowStat acc{0.0, -INFINITY};
-    bool ok = true;
-    for (int i = 0; i < P.segs; ++i) {
-        u32x4 a[1];
-        ok &= try_record<1>(r, stat_off(P, grow, i), a, P.epoch);
-        const RowStat x = unpack_rowstat(a);
-        combine_stat(acc.m, acc.s, x.m, x.s, P.cd);
+#pragma unroll
+    for (int j = 0; j < kStatBatch; ++j)
+        if (i0 + j < P.segs) a[j] = get_atom(r, stat_off(P, grow, i0 + j));
+}
+
+// Folds the records requested by issue_row_stat into acc, in segment order.
+__device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int i0, const u32x4* a, RowStat& acc, bool& ok)
+{
+#pragma unroll
+    for (int j = 0; j < kStatBatch; ++j)
+        if (i0 + j < P.segs) {
+            ok &= a[j].w == record_tag<1>(&a[j], P.epoch);
+            const RowStat x = unpack_rowstat(&a[j]);
+            combine_stat(acc.m, acc.s, x.m, x.s, P.cd);
+        }
+}
+
+// Statistics of R rows of sequence b, every record of a batch of each row
+// requested before any is used.
+template <int R>
+__device__ __forceinline__ void load_row_stats(const VerifyParams& P, int b, const int* rows, RowStat* out)
+{
+    bool ok[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+        out[q] = RowStat{0.0, -INFINITY};
+        ok[q] = true;
     }
-    if (!ok) acc.s = NAN;
-    return acc;
+    for (int i0 = 0; i0 < P.segs; i0 += kStatBatch) {
+        u32x4 a[R][kStatBatch];
+#pragma unroll
+        for (int q = 0; q < R; ++q) issue_row_stat(P, b, rows[q], i0, a[q]);
+#pragma unroll
+        for (int q = 0; q < R; ++q) fold_row_stat(P, i0, a[q], out[q], ok[q]);
+    }
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+        if (!ok[q]) out[q].s = NAN;
 }
 
 template <int DT>
@@ -421,12 +453,11 @@ struct AcceptOut {
     int accepted;
 };
 
-template <int DT>
-__device__ __forceinline__ AcceptOut accept_one(const char* qrow, const char* prow, int tok, const RowStat& rq,
-                                                const RowStat& rp, double invT, double u)
+// Accept test of one draft token from its logits zqd (verifier) and zpd
+// (draft) and the two rows' statistics.
+__device__ __forceinline__ AcceptOut accept_logits(float zqd, float zpd, const RowStat& rq, const RowStat& rp,
+                                                   double invT, double u)
 {
-    const float zqd = load_logit<DT>(qrow, tok);
-    const float zpd = load_logit<DT>(prow, tok);
     AcceptOut o;
     o.lq = ((double)zqd - (double)rq.m) * invT - log(rq.s);
     o.lp = ((double)zpd - (double)rp.m) * invT - log(rp.s);
@@ -464,19 +495,26 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     const int N = P.N;
     const bool active = lane < N;
     int err = 0, acc = 1;
-    RowStat rq{}, rp{};
-    // the bonus row's statistics, loaded with the others (used if all accept)
-    const RowStat qn = load_row_stat(P, b, N);
+    // every independent load first: the token, then (with the token's
+    // logits in flight) the records of rows q_i, p_i and of the bonus row
+    // (used if all accept; inactive lanes read it three times)
+    const int tok = active ? P.tokens[(int64_t)b * N + lane] : 0;
+    const int rows[3] = {active ? lane : N, active ? N + 1 + lane : N, N};
+    const bool tok_ok = tok >= 0 && tok < P.V;
+    float zqd = 0.0f, zpd = 0.0f;
+    if (active && tok_ok) {
+        zqd = load_logit<DT>(qrow_ptr<DT>(P, b, lane), tok);
+        zpd = load_logit<DT>(prow_ptr<DT>(P, b, lane), tok);
+    }
+    RowStat st[3];
+    load_row_stats<3>(P, b, rows, st);
+    const RowStat rq = st[0], rp = st[1], qn = st[2];
     if (active) {
-        const int tok = P.tokens[(int64_t)b * N + lane];
-        rq = load_row_stat(P, b, lane);
-        rp = load_row_stat(P, b, N + 1 + lane);
-        if (tok < 0 || tok >= P.V || stat_bad(rq) || stat_bad(rp)) {
+        if (!tok_ok || stat_bad(rq) || stat_bad(rp)) {
             err = 1;
         } else {
             const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(lane + 1));
-            const AcceptOut o = accept_one<DT>(qrow_ptr<DT>(P, b, lane), prow_ptr<DT>(P, b, lane), tok, rq, rp,
-                                               P.invT, u);
+            const AcceptOut o = accept_logits(zqd, zpd, rq, rp, P.invT, u);
             acc = o.accepted;
             if (outputs && P.out_probs) {
                 P.out_probs[((int64_t)b * N + lane) * 2 + 0] = (float)exp(o.lq);
@@ -555,15 +593,19 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
     if (!err) {
         for (int n = 1 + tid; n < nn; n += kBlock) {
             const int p = s_par[n];
-            const RowStat rq = load_row_stat(P, b, 2 * p + 0);
-            const RowStat rp = load_row_stat(P, b, 2 * p + 1);
+            const int t = tok[n];
+            const float zqd = load_logit<DT>(qrow_ptr<DT>(P, b, p), t);
+            const float zpd = load_logit<DT>(prow_ptr<DT>(P, b, p), t);
+            const int rows[2] = {2 * p, 2 * p + 1};
+            RowStat st[2];
+            load_row_stats<2>(P, b, rows, st);
+            const RowStat rq = st[0], rp = st[1];
             if (stat_bad(rq) || stat_bad(rp)) {
                 err = 1;
                 continue;
             }
             const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)n);
-            const AcceptOut o =
-                accept_one<DT>(qrow_ptr<DT>(P, b, p), prow_ptr<DT>(P, b, p), tok[n], rq, rp, P.invT, u);
+            const AcceptOut o = accept_logits(zqd, zpd, rq, rp, P.invT, u);
             s_acc[n] = (unsigned char)o.accepted;
             if (outputs && P.out_acc) P.out_acc[(int64_t)b * nn + n] = (int8_t)o.accepted;
             if (outputs && P.out_probs) {
@@ -620,8 +662,14 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
         s.node = cur;
         s.status = 0;
         s.u = sample_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(depth + 1));
-        if (residual) fill_residual_state(s, load_row_stat(P, b, 2 * cur), load_row_stat(P, b, 2 * cur + 1), P.T);
-        else s.mode = kModeBonus;
+        if (residual) {
+            const int rows[2] = {2 * cur, 2 * cur + 1};
+            RowStat st[2];
+            load_row_stats<2>(P, b, rows, st);
+            fill_residual_state(s, st[0], st[1], P.T);
+        } else {
+            s.mode = kModeBonus;
+        }
     }
     if (lane == 0) out = s;
 }
@@ -1176,52 +1224,47 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
 
     // --- totals ---
-    double rho = 0.0, M = 0.0, resid_mass = 0.0;
+    double rho = 0.0, M = 0.0, sq = 0.0, resid_mass = 0.0;
     int mode = s.mode;
+    bool near_any = false;
     if (mode == kModeResidual) {
-        double sqp[2] = {0.0, 0.0};
+        // sums of a and b over the row, and how many chunks hold
+        // near-threshold tokens, in one reduction
+        double sqp[3] = {0.0, 0.0, 0.0};
         for (int c = c0; c < c1; ++c) {
             const ChunkSums p = chunk_at(c);
             sqp[0] += p.sa;
             sqp[1] += p.sb;
+            sqp[2] += (p.na != 0.0 || p.nb != 0.0 || p.dmin <= p.dmax) ? 1.0 : 0.0;
         }
-        __shared__ double red2[kWaves * 2];
-        block_sum_n<2>(sqp, red2);
-        const double sq = sqp[0];
+        __shared__ double red3[kWaves * 3];
+        block_sum_n<3>(sqp, red3);
+        sq = sqp[0];
         rho = sqp[0] / sqp[1];
-        // near-threshold tokens: exact when they share one zq - zp (one ratio
-        // q/p), else the chunk is rescanned below with the exact rho
-        for (int c = tid; c < nchunks; c += kBlock) {
-            const ChunkSums p = chunk_at(c);
-            s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
-        }
-        __syncthreads();
-        for (int c = 0; c < nchunks; ++c) {
-            if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
-            stage_chunk<DT>(qrow, P.V, c, s_q);
-            stage_chunk<DT>(prow, P.V, c, s_p);
-            double w[1] = {0.0};
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) {
-                const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
-                const float d = zq - zp;
-                if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(zq, zp, s, eq, ep, rho);
+        near_any = sqp[2] > 0.0;  // uniform across the block
+        if (near_any) {
+            // near-threshold tokens: exact when they share one zq - zp (one
+            // ratio q/p), else the chunk is rescanned with the exact rho
+            for (int c = tid; c < nchunks; c += kBlock) {
+                const ChunkSums p = chunk_at(c);
+                s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
             }
-            block_sum_n<1>(w, red);
-            if (tid == 0) s_near[c] = w[0];
             __syncthreads();
-        }
-        double wsum[1] = {0.0};
-        for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = chunk_at(c);
-            wsum[0] += (p.pa - rho * p.pb) + s_near[c];
-        }
-        block_sum_n<1>(wsum, red);
-        if (!(wsum[0] > 0.0)) {
-            mode = kModeFallback;
-            resid_mass = 0.0;
-        } else {
-            resid_mass = wsum[0] / sq;
+            for (int c = 0; c < nchunks; ++c) {
+                if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
+                stage_chunk<DT>(qrow, P.V, c, s_q);
+                stage_chunk<DT>(prow, P.V, c, s_p);
+                double w[1] = {0.0};
+#pragma unroll
+                for (int j = 0; j < kPerThread; ++j) {
+                    const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
+                    const float d = zq - zp;
+                    if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(zq, zp, s, eq, ep, rho);
+                }
+                block_sum_n<1>(w, red);
+                if (tid == 0) s_near[c] = w[0];
+                __syncthreads();
+            }
         }
     } else {
         float lm = -INFINITY;
@@ -1240,7 +1283,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     }
     auto chunk_weight = [&](int c) -> double {
         const ChunkSums p = chunk_at(c);
-        if (mode == kModeResidual) return (p.pa - rho * p.pb) + s_near[c];
+        if (mode == kModeResidual) return (p.pa - rho * p.pb) + (near_any ? s_near[c] : 0.0);
         if (mode == kModeFallback) return p.sa;
         return (p.sa == -INFINITY) ? 0.0 : p.sb * exp((p.sa - M) * invT);
     };
@@ -1252,7 +1295,18 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     double gsum = 0.0;
     for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
     double Wtot;
-    const double gbase = block_exclusive_scan(gsum, red, &Wtot);
+    double gbase = block_exclusive_scan(gsum, red, &Wtot);
+    if (mode == kModeResidual) {
+        // the residual's mass; none (q <= p everywhere) falls back to q
+        if (Wtot > 0.0) {
+            resid_mass = Wtot / sq;
+        } else {
+            mode = kModeFallback;
+            gsum = 0.0;
+            for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
+            gbase = block_exclusive_scan(gsum, red, &Wtot);
+        }
+    }
     const double target = s.u * Wtot;
     if (tid == 0) {
         s_owner = -1;
@@ -1503,9 +1557,10 @@ template <int DT>
 __global__ __launch_bounds__(kBlock) void k_final(const VerifyParams P)
 {
     __shared__ double s_t32[32];
-    const SeqState s = P.seqs[blockIdx.x];  // in flight with the table fill
+    const SeqState s = P.seqs[blockIdx.x];
+    // the table is first read after sample_final's first barrier, so its
+    // fill needs none of its own and the record loads overlap the state's
     fill_t32(s_t32);
-    __syncthreads();
     sample_final<DT, false>(P, (int)blockIdx.x, s, nullptr, s_t32);
 }
 
