@@ -677,8 +677,8 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
 // ===========================================================================
 // Sampling
 // ===========================================================================
-// The 16 elements of thread `tid` in chunk `c` (contiguous, token order);
-// entries past V read as -inf.
+// The kPerThread elements of thread `tid` in chunk `c` (contiguous, token
+// order); entries past V read as -inf.
 template <int DT>
 __device__ __forceinline__ void load_chunk16(const char* __restrict__ row, int V, int c, int tid, float* x)
 {
@@ -1119,30 +1119,28 @@ __device__ __forceinline__ double residual_weight(float xq, float xp, const SeqS
     return (d > s.thr_hi) ? w : fmax(0.0, w);
 }
 
-// One chunk of a logit row held in LDS in its storage format.
-template <int DT>
-struct Staged;
-template <>
-struct Staged<DT_BF16> {
-    uint16_t v[kChunk];
-    __device__ __forceinline__ float get(int i) const { return __uint_as_float((uint32_t)v[i] << 16); }
-    __device__ __forceinline__ void set(int i, float x) { v[i] = (uint16_t)(__float_as_uint(x) >> 16); }
-};
-template <>
-struct Staged<DT_F32> {
-    float v[kChunk];
-    __device__ __forceinline__ float get(int i) const { return v[i]; }
-    __device__ __forceinline__ void set(int i, float x) { v[i] = x; }
-};
-
-// This thread's 16 tokens of chunk c into LDS (tokens past V as -inf).
-template <int DT>
-__device__ __forceinline__ void stage_chunk(const char* row, int V, int c, Staged<DT>& dst)
+// Block-wide: every output slot of sequence b that does not depend on the
+// sampled token: slots i < k hold the accepted tokens, slots past k -1, and
+// (trees) the path up to depth k.  emit_sample then writes slot k, the count
+// and the residual mass; a failure rewrites everything through emit.
+template <bool TREE>
+__device__ void emit_accepted(const VerifyParams& P, int b, int k, const int32_t* path)
 {
-    float x[kPerThread];
-    load_chunk16<DT>(row, V, c, threadIdx.x, x);
-#pragma unroll
-    for (int j = 0; j < kPerThread; ++j) dst.set(threadIdx.x * kPerThread + j, x[j]);
+    const int width = P.width;
+    for (int i = threadIdx.x; i < width; i += kBlock) {
+        int32_t t = -1, pn = -1;
+        if (TREE) {
+            if (i <= k) pn = path[i];
+            if (i < k) {
+                const int node = path[i + 1];
+                t = P.tokens[(int64_t)b * P.nn + min(max(node, 0), P.nn - 1)];
+            }
+        } else if (i < k) {
+            t = P.tokens[(int64_t)b * P.N + i];
+        }
+        if (i != k) P.out_tokens[(int64_t)b * width + i] = t;
+        if (TREE) P.out_path[(int64_t)b * width + i] = pn;
+    }
 }
 
 // Block-wide: the outputs of sequence b.  k < 0 or token < 0 marks the
@@ -1175,235 +1173,286 @@ __device__ void emit(const VerifyParams& P, int b, int k, int token, double resi
     }
 }
 
+// One thread: the sampled slot of a sequence whose other slots emit_accepted
+// wrote.
+__device__ __forceinline__ void emit_sample(const VerifyParams& P, int b, int k, int token, double resid)
+{
+    P.out_tokens[(int64_t)b * P.width + k] = token;
+    P.out_num[b] = k;
+    if (P.out_resid) P.out_resid[b] = resid;
+}
+
 // Chunk records the final step keeps in LDS.
 constexpr int kFinalCache = 256;
+// Chunk records per lane of wave 0 whose loads are issued together.
+constexpr int kFinalLaneBatch = 4;
 
-// Final step of sequence b: wait for its chunks, totals, chunk location,
-// rescan, outputs.
+// What wave 0 of the final step hands the block.
+struct FinalPlan {
+    double rho, M, sq, cbase, target, resid;
+    int mode, cs, near_any, fail;
+};
+
+// Final step of sequence b: its chunk records, totals, chunk location,
+// rescan of that chunk, outputs.  Wave 0 alone reads the records (lane L
+// owns chunks [L*g, L*g + g), g = ceil(nch / 64)), forms the totals and
+// locates the chunk with wave scans and ballots, and hands the block a plan
+// through one barrier; the block then rescans the chunk.
 template <int DT, bool TREE>
 __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path,
                              const double* t32)
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nchunks = P.nch;
     const double invT = P.invT;
     __shared__ double red[kWaves];
-    __shared__ float redf[kWaves];
     __shared__ double s_near[kMaxChunks];
-    __shared__ int s_chunk;
-    __shared__ double s_base;
-    __shared__ int s_owner;
+    __shared__ FinalPlan s_plan;
+    __shared__ int s_cand[kWaves];
     __shared__ int s_token;
-    __shared__ Staged<DT> s_q, s_p;
-    // the chunk records, waited for once and kept in LDS (the first
-    // kFinalCache of them; later ones are read again when needed)
+    // the chunk records, kept in LDS (the first kFinalCache of them; later
+    // ones are read again when needed)
     __shared__ ChunkSums s_cs[kFinalCache];
-    int chunks_ok = 1, timed_out = 0;
-    for (int c = tid; c < nchunks; c += kBlock) {
-        u32x4 a[4];
-        if (wait_record<4>(part_rsrc(P), chunk_off(P, b, c), a, P.epoch)) {
-            const ChunkSums v = unpack_chunk(a);
-            timed_out |= (v.flags & kFlagTimeout) != 0;
-            if (c < kFinalCache) s_cs[c] = v;
-        } else {
-            chunks_ok = 0;
-        }
-    }
-    chunks_ok = __syncthreads_and(chunks_ok);
-    timed_out = __syncthreads_or(timed_out);
-    auto chunk_at = [&](int c) -> ChunkSums { return c < kFinalCache ? s_cs[c] : get_chunk(P, b, c); };
-    if (!chunks_ok || timed_out || s.status) {
+    if (s.status) {
         emit<TREE>(P, b, -1, -1, 0.0, path);
         return;
     }
-    const int g = (nchunks + kBlock - 1) / kBlock;
-    const int c0 = tid * g;
-    const int c1 = min(nchunks, c0 + g);
+    const int k = s.k;
+    emit_accepted<TREE>(P, b, k, path);
+    if (tid == 0) s_token = -1;
+    auto chunk_at = [&](int c) -> ChunkSums { return c < kFinalCache ? s_cs[c] : get_chunk(P, b, c); };
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
     const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
 
-    // --- totals ---
-    double rho = 0.0, M = 0.0, sq = 0.0, resid_mass = 0.0;
+    // --- wave 0: records, totals, location ---
+    const int g = (nchunks + 63) / 64;
+    const int c0 = lane * g, c1 = min(nchunks, c0 + g);
     int mode = s.mode;
+    double rho = 0.0, M = 0.0, sq = 0.0;
     bool near_any = false;
-    if (mode == kModeResidual) {
-        // sums of a and b over the row, and how many chunks hold
-        // near-threshold tokens, in one reduction
-        double sqp[3] = {0.0, 0.0, 0.0};
-        for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = chunk_at(c);
-            sqp[0] += p.sa;
-            sqp[1] += p.sb;
-            sqp[2] += (p.na != 0.0 || p.nb != 0.0 || p.dmin <= p.dmax) ? 1.0 : 0.0;
-        }
-        __shared__ double red3[kWaves * 3];
-        block_sum_n<3>(sqp, red3);
-        sq = sqp[0];
-        rho = sqp[0] / sqp[1];
-        near_any = sqp[2] > 0.0;  // uniform across the block
-        if (near_any) {
-            // near-threshold tokens: exact when they share one zq - zp (one
-            // ratio q/p), else the chunk is rescanned with the exact rho
-            for (int c = tid; c < nchunks; c += kBlock) {
-                const ChunkSums p = chunk_at(c);
-                s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
-            }
-            __syncthreads();
-            for (int c = 0; c < nchunks; ++c) {
-                if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
-                stage_chunk<DT>(qrow, P.V, c, s_q);
-                stage_chunk<DT>(prow, P.V, c, s_p);
-                double w[1] = {0.0};
-#pragma unroll
-                for (int j = 0; j < kPerThread; ++j) {
-                    const float zq = s_q.get(tid * kPerThread + j), zp = s_p.get(tid * kPerThread + j);
-                    const float d = zq - zp;
-                    if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(zq, zp, s, eq, ep, rho);
-                }
-                block_sum_n<1>(w, red);
-                if (tid == 0) s_near[c] = w[0];
-                __syncthreads();
-            }
-        }
-    } else {
-        float lm = -INFINITY;
-        int bad = 0;
-        for (int c = c0; c < c1; ++c) {
-            const ChunkSums p = chunk_at(c);
-            lm = fmaxf(lm, (float)p.sa);
-            bad |= (p.flags & kFlagBad) != 0;
-        }
-        M = (double)block_max(lm, redf);
-        bad = __syncthreads_or(bad);
-        if (bad || M == -INFINITY) {
-            emit<TREE>(P, b, -1, -1, 0.0, path);
-            return;
-        }
-    }
     auto chunk_weight = [&](int c) -> double {
         const ChunkSums p = chunk_at(c);
         if (mode == kModeResidual) return (p.pa - rho * p.pb) + (near_any ? s_near[c] : 0.0);
         if (mode == kModeFallback) return p.sa;
         return (p.sa == -INFINITY) ? 0.0 : p.sb * exp((p.sa - M) * invT);
     };
-
-    // --- locate the chunk: first chunk whose running weight exceeds u*W ---
-    // The owner is the last thread whose group starts at or below the
-    // threshold; it scans its group and, if rounding leaves the threshold past
-    // its end, takes its last chunk of positive weight.
-    double gsum = 0.0;
-    for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
-    double Wtot;
-    double gbase = block_exclusive_scan(gsum, red, &Wtot);
-    if (mode == kModeResidual) {
-        // the residual's mass; none (q <= p everywhere) falls back to q
-        if (Wtot > 0.0) {
-            resid_mass = Wtot / sq;
-        } else {
-            mode = kModeFallback;
-            gsum = 0.0;
-            for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
-            gbase = block_exclusive_scan(gsum, red, &Wtot);
-        }
-    }
-    const double target = s.u * Wtot;
-    if (tid == 0) {
-        s_owner = -1;
-        s_chunk = 0;  // never left unset, even if no thread could claim
-        s_base = 0.0;
-    }
-    __syncthreads();
-    if (gsum > 0.0 && gbase <= target) atomicMax(&s_owner, tid);
-    __syncthreads();
-    if (tid == s_owner) {
-        double cum = gbase;
-        int pick = -1, last = -1;
-        double pick_base = 0.0, last_base = 0.0;
-        for (int c = c0; c < c1; ++c) {
-            const double w = chunk_weight(c);
-            if (w > 0.0) {
-                last = c;
-                last_base = cum;
-                if (pick < 0 && cum + w > target) {
-                    pick = c;
-                    pick_base = cum;
-                }
+    // the first chunk whose running weight exceeds u*W: its owner is the
+    // last lane whose group starts at or below the threshold; it scans its
+    // group and, if rounding leaves the threshold past its end, takes its
+    // last chunk of positive weight
+    auto locate = [&]() {
+        double gsum = 0.0;
+        for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
+        double Wtot, gbase = wave_exclusive_scan(gsum, &Wtot);
+        double resid = 0.0;
+        if (mode == kModeResidual) {
+            // the residual's mass; none (q <= p everywhere) falls back to q
+            if (Wtot > 0.0) {
+                resid = Wtot / sq;
+            } else {
+                mode = kModeFallback;
+                gsum = 0.0;
+                for (int c = c0; c < c1; ++c) gsum += chunk_weight(c);
+                gbase = wave_exclusive_scan(gsum, &Wtot);
             }
-            cum += w;
         }
-        if (pick < 0) {
-            pick = last;
-            pick_base = last_base;
+        const double target = s.u * Wtot;
+        const uint64_t cand = __ballot(gsum > 0.0 && gbase <= target);
+        const int owner = cand ? 63 - __clzll((long long)cand) : -1;
+        if (lane == 0) {
+            s_plan.mode = mode;
+            s_plan.resid = resid;
+            s_plan.target = target;
+            s_plan.cs = 0;  // never left unset, even if no lane could claim
+            s_plan.cbase = 0.0;
         }
-        s_chunk = pick < 0 ? 0 : pick;
-        s_base = pick_base;
+        if (lane == owner) {
+            double cum = gbase;
+            int pick = -1, last = -1;
+            double pick_base = 0.0, last_base = 0.0;
+            for (int c = c0; c < c1; ++c) {
+                const double w = chunk_weight(c);
+                if (w > 0.0) {
+                    last = c;
+                    last_base = cum;
+                    if (pick < 0 && cum + w > target) {
+                        pick = c;
+                        pick_base = cum;
+                    }
+                }
+                cum += w;
+            }
+            if (pick < 0) {
+                pick = last;
+                pick_base = last_base;
+            }
+            s_plan.cs = pick < 0 ? 0 : pick;
+            s_plan.cbase = pick_base;
+        }
+    };
+    if (wave == 0) {
+        int ok = 1, tmo = 0, bad = 0;
+        double sums[3] = {0.0, 0.0, 0.0};  // sa, sb, chunks with near tokens
+        float lm = -INFINITY;
+        auto take = [&](int c, const ChunkSums& v) {
+            tmo |= (v.flags & kFlagTimeout) != 0;
+            if (c < kFinalCache) s_cs[c] = v;
+            if (mode == kModeResidual) {
+                sums[0] += v.sa;
+                sums[1] += v.sb;
+                sums[2] += (v.na != 0.0 || v.nb != 0.0 || v.dmin <= v.dmax) ? 1.0 : 0.0;
+            } else {
+                lm = fmaxf(lm, (float)v.sa);
+                bad |= (v.flags & kFlagBad) != 0;
+            }
+        };
+        const __amdgpu_buffer_rsrc_t r = part_rsrc(P);
+        // the first kFinalLaneBatch records of the lane requested together
+        u32x4 a[kFinalLaneBatch][4];
+#pragma unroll
+        for (int j = 0; j < kFinalLaneBatch; ++j)
+            if (c0 + j < c1)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[j][i] = get_atom(r, chunk_off(P, b, c0 + j) + 16u * i);
+#pragma unroll
+        for (int j = 0; j < kFinalLaneBatch; ++j)
+            if (c0 + j < c1) {
+                if (a[j][3].w == record_tag<4>(a[j], P.epoch) ||
+                    wait_record<4>(r, chunk_off(P, b, c0 + j), a[j], P.epoch))
+                    take(c0 + j, unpack_chunk(a[j]));
+                else
+                    ok = 0;
+            }
+        for (int c = c0 + kFinalLaneBatch; c < c1; ++c) {
+            u32x4 x[4];
+            if (wait_record<4>(r, chunk_off(P, b, c), x, P.epoch)) take(c, unpack_chunk(x));
+            else ok = 0;
+        }
+        int fail = !__all(ok) || __any(tmo);
+        if (!fail) {
+            if (mode == kModeResidual) {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) sums[i] = wave_sum(sums[i]);
+                sq = sums[0];
+                rho = sums[0] / sums[1];
+                near_any = sums[2] > 0.0;
+            } else {
+                M = (double)wave_max(lm);
+                fail = __any(bad) || M == -INFINITY;
+            }
+        }
+        if (!fail && !near_any) locate();
+        if (lane == 0) {
+            s_plan.fail = fail;
+            s_plan.near_any = near_any;
+            s_plan.rho = rho;
+            s_plan.M = M;
+            s_plan.sq = sq;
+        }
     }
     __syncthreads();
-    const int cs = s_chunk;
-    const double cbase = s_base;
+    if (s_plan.fail) {
+        emit<TREE>(P, b, -1, -1, 0.0, path);
+        return;
+    }
+    rho = s_plan.rho;
+    M = s_plan.M;
+    sq = s_plan.sq;
+    near_any = s_plan.near_any != 0;
+    if (near_any) {
+        // near-threshold tokens (rare): exact when they share one zq - zp
+        // (one ratio q/p), else the chunk is rescanned with the exact rho
+        for (int c = tid; c < nchunks; c += kBlock) {
+            const ChunkSums p = chunk_at(c);
+            s_near[c] = (p.dmin < p.dmax) ? NAN : fmax(0.0, p.na - rho * p.nb);
+        }
+        __syncthreads();
+        for (int c = 0; c < nchunks; ++c) {
+            if (!(s_near[c] != s_near[c])) continue;  // uniform across the block
+            float xq[kPerThread], xp[kPerThread];
+            load_chunk16<DT>(qrow, P.V, c, tid, xq);
+            load_chunk16<DT>(prow, P.V, c, tid, xp);
+            double w[1] = {0.0};
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) {
+                const float d = xq[j] - xp[j];
+                if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(xq[j], xp[j], s, eq, ep, rho);
+            }
+            block_sum_n<1>(w, red);
+            if (tid == 0) s_near[c] = w[0];
+            __syncthreads();
+        }
+        if (wave == 0) locate();
+        __syncthreads();
+    }
+    mode = s_plan.mode;
+    const int cs = s_plan.cs;
+    const double cbase = s_plan.cbase, target = s_plan.target, resid = s_plan.resid;
 
-    // --- rescan the chunk ---
-    // Each thread stages its 16 tokens in LDS and walks them one at a time
-    // (it reads back only what it wrote itself).
-    stage_chunk<DT>(qrow, P.V, cs, s_q);
-    if (mode == kModeResidual) stage_chunk<DT>(prow, P.V, cs, s_p);
+    // --- rescan the chunk: each thread its 8 tokens, from registers ---
+    float xq[kPerThread], xp[kPerThread];
+    load_chunk16<DT>(qrow, P.V, cs, tid, xq);
+    if (mode == kModeResidual) load_chunk16<DT>(prow, P.V, cs, tid, xp);
     double scale = 1.0, mc = 0.0;
     if (mode == kModeBonus) {
         mc = chunk_at(cs).sa;
         scale = exp((mc - M) * invT);
     }
     const ExpRow ec = exp_row(P, mc, t32);
-    auto weight = [&](int j) -> double {
-        const int i = tid * kPerThread + j;
-        const float a = s_q.get(i);
-        if (mode == kModeResidual) return residual_weight(a, s_p.get(i), s, eq, ep, rho);
-        if (mode == kModeFallback) return eq(a);
-        return ec(a);
-    };
-    // the thread's weights, their lookups issued together, kept for the
-    // sum, the fallback and the walk
     double wv[kPerThread];
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) wv[j] = weight(j);
+    for (int j = 0; j < kPerThread; ++j) {
+        if (mode == kModeResidual) wv[j] = residual_weight(xq[j], xp[j], s, eq, ep, rho);
+        else if (mode == kModeFallback) wv[j] = eq(xq[j]);
+        else wv[j] = ec(xq[j]);
+    }
     double tsum = 0.0;
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) tsum += wv[j];
     double ctotal;
     const double tbase = block_exclusive_scan(tsum, red, &ctotal);
     const double local = (target - cbase) / scale;
-    if (tid == 0) {
-        s_owner = -1;
-        s_token = -1;
-    }
+    // the owner is the last thread whose tokens start at or below the
+    // threshold: per-wave candidates by ballot, then the highest wave's
+    const uint64_t cand = __ballot(tsum > 0.0 && tbase <= local);
+    if (lane == 0) s_cand[wave] = cand ? wave * 64 + 63 - __clzll((long long)cand) : -1;
     __syncthreads();
-    if (tsum > 0.0 && tbase <= local) atomicMax(&s_owner, tid);
-    __syncthreads();
-    if (s_owner < 0) {
-        // no positive weight at or below the threshold in this chunk (only
-        // possible through rounding): take its last element of positive weight
-        int last = -1;
+    int owner = -1;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j)
-            if (wv[j] > 0.0) last = cs * kChunk + tid * kPerThread + j;
-        atomicMax(&s_token, last);
-    } else if (tid == s_owner) {
-        double cum = tbase;
-        int pick = -1, last = -1;
+    for (int w = 0; w < kWaves; ++w) owner = max(owner, s_cand[w]);
+    const double rmass = (s.mode == kModeResidual) ? resid : 0.0;
+    if (owner >= 0) {
+        if (tid == owner) {
+            double cum = tbase;
+            int pick = -1, last = -1;
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) {
-            const double wj = wv[j];
-            if (wj > 0.0) {
-                last = j;
-                if (pick < 0 && cum + wj > local) pick = j;
+            for (int j = 0; j < kPerThread; ++j) {
+                const double wj = wv[j];
+                if (wj > 0.0) {
+                    last = j;
+                    if (pick < 0 && cum + wj > local) pick = j;
+                }
+                cum += wj;
             }
-            cum += wj;
+            if (pick < 0) pick = last;
+            emit_sample(P, b, k, cs * kChunk + tid * kPerThread + pick, rmass);
         }
-        if (pick < 0) pick = last;
-        s_token = pick < 0 ? -1 : cs * kChunk + tid * kPerThread + pick;
+        return;
     }
+    // no positive weight at or below the threshold in this chunk (only
+    // possible through rounding): take its last element of positive weight
+    int last = -1;
+#pragma unroll
+    for (int j = 0; j < kPerThread; ++j)
+        if (wv[j] > 0.0) last = cs * kChunk + tid * kPerThread + j;
+    atomicMax(&s_token, last);
     __syncthreads();
-    emit<TREE>(P, b, s.k, s_token, (s.mode == kModeResidual) ? resid_mass : 0.0, path);
+    if (s_token >= 0) {
+        if (tid == 0) emit_sample(P, b, k, s_token, rmass);
+    } else {
+        emit<TREE>(P, b, -1, -1, 0.0, path);
+    }
 }
 
 // ===========================================================================

@@ -429,6 +429,22 @@ __device__ __forceinline__ float block_max(float v, float* red)
 
 // Exclusive prefix sum over the block in thread order; returns the prefix of
 // this thread and writes the block total.  `scan` holds kWaves doubles.
+// Exclusive prefix sum over the lanes of a wave (Hillis-Steele); *total gets
+// the wave's sum in every lane.
+__device__ __forceinline__ double wave_exclusive_scan(double v, double* total)
+{
+    const int lane = threadIdx.x & 63;
+    double incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+    }
+    *total = __shfl(incl, 63, 64);
+    const double excl = __shfl_up(incl, 1, 64);
+    return lane == 0 ? 0.0 : excl;
+}
+
 __device__ __forceinline__ double block_exclusive_scan(double v, double* scan, double* total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
