@@ -294,6 +294,7 @@ __device__ __forceinline__ bool wait_record(__amdgpu_buffer_rsrc_t r, uint32_t o
     while (!try_record<K>(r, off, a, epoch)) {
         if (++spins > kSpinLimit) return false;
         __builtin_amdgcn_s_sleep(2);
+        asm volatile("" ::: "memory");  // the next try loads again
     }
     return true;
 }
@@ -370,25 +371,46 @@ __device__ __forceinline__ ChunkSums get_chunk(const VerifyParams& P, int b, int
 constexpr int kStatBatch = 8;
 
 // Requests the records of segments [i0, i0 + kStatBatch) of row `row` of b.
+// Slots past the last segment re-read it (fold_row_stat skips them), so the
+// loads carry no branches and issue back to back.
 __device__ __forceinline__ void issue_row_stat(const VerifyParams& P, int b, int row, int i0, u32x4* a)
 {
     const __amdgpu_buffer_rsrc_t r = stats_rsrc(P);
     const int64_t grow = (int64_t)b * P.rows + row;
 #pragma unroll
-    for (int j = 0; j < kStatBatch; ++j)
-        if (i0 + j < P.segs) a[j] = get_atom(r, stat_off(P, grow, i0 + j));
+    for (int j = 0; j < kStatBatch; ++j) a[j] = get_atom(r, stat_off(P, grow, min(i0 + j, P.segs - 1)));
 }
 
-// Folds the records requested by issue_row_stat into acc, in segment order.
+// Folds the records requested by issue_row_stat into acc: the batch's
+// maximum first, then each segment's sum scaled to it (independent exps, in
+// segment order), then the batch into acc.  Branch-free (slots past the last
+// segment are masked by selects), so no load is sunk next to its use.
 __device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int i0, const u32x4* a, RowStat& acc, bool& ok)
 {
+    float xm[kStatBatch];
+    double xs[kStatBatch];
+    float bm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kStatBatch; ++j)
-        if (i0 + j < P.segs) {
-            ok &= a[j].w == record_tag<1>(&a[j], P.epoch);
-            const RowStat x = unpack_rowstat(&a[j]);
-            combine_stat(acc.m, acc.s, x.m, x.s, P.cd);
-        }
+    for (int j = 0; j < kStatBatch; ++j) {
+        const bool in = i0 + j < P.segs;
+        const RowStat x = unpack_rowstat(&a[j]);
+        ok &= !in || a[j].w == record_tag<1>(&a[j], P.epoch);
+        xm[j] = in ? x.m : -INFINITY;
+        xs[j] = in ? x.s : 0.0;
+        bm = fmaxf(bm, xm[j]);
+    }
+    double bs = 0.0;
+#pragma unroll
+    for (int j = 0; j < kStatBatch; ++j) {
+        const double e = exp2((double)(xm[j] - bm) * P.cd);
+        bs += xs[j] * ((xm[j] == bm) ? 1.0 : e);
+    }
+    if (i0 == 0) {
+        acc.m = bm;
+        acc.s = bs;
+    } else {
+        combine_stat(acc.m, acc.s, bm, bs, P.cd);
+    }
 }
 
 // Statistics of R rows of sequence b, every record of a batch of each row
@@ -485,8 +507,10 @@ __device__ __forceinline__ void fill_residual_state(SeqState& s, const RowStat& 
     s.thr_hi = (float)(theta + margin);
 }
 
-// Chain accept of sequence b, run by wave 0 (lane i = position i+1): b's
-// state into `out` (LDS); with `outputs`, also the accept flags and
+constexpr int kMaxChainN = 64;  // longest draft chain
+
+// Chain accept of sequence b, run by a one-wave block (lane i = position
+// i+1): b's state into `out`; with `outputs`, also the accept flags and
 // probabilities.
 template <int DT>
 __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool outputs)
@@ -496,19 +520,26 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     const bool active = lane < N;
     int err = 0, acc = 1;
     // every independent load first: the token, then (with the token's
-    // logits in flight) the records of rows q_i, p_i and of the bonus row
-    // (used if all accept; inactive lanes read it three times)
+    // logits in flight) the records of the 2N+1 pass-1 rows, lane j folding
+    // row j (and j + 64 ...), so each lane combines one row's segments
     const int tok = active ? P.tokens[(int64_t)b * N + lane] : 0;
-    const int rows[3] = {active ? lane : N, active ? N + 1 + lane : N, N};
     const bool tok_ok = tok >= 0 && tok < P.V;
     float zqd = 0.0f, zpd = 0.0f;
     if (active && tok_ok) {
         zqd = load_logit<DT>(qrow_ptr<DT>(P, b, lane), tok);
         zpd = load_logit<DT>(prow_ptr<DT>(P, b, lane), tok);
     }
-    RowStat st[3];
-    load_row_stats<3>(P, b, rows, st);
-    const RowStat rq = st[0], rp = st[1], qn = st[2];
+    __shared__ RowStat s_rows[2 * kMaxChainN + 1];
+    for (int r0 = 0; r0 < P.rows; r0 += 64) {
+        const int row = min(r0 + lane, P.rows - 1);
+        RowStat st;
+        load_row_stats<1>(P, b, &row, &st);
+        if (r0 + lane < P.rows) s_rows[row] = st;
+    }
+    __syncthreads();
+    // the bonus row's statistics (used if all accept) and those of q_i, p_i
+    const RowStat qn = s_rows[N];
+    const RowStat rq = s_rows[active ? lane : N], rp = s_rows[active ? N + 1 + lane : N];
     if (active) {
         if (!tok_ok || stat_bad(rq) || stat_bad(rp)) {
             err = 1;

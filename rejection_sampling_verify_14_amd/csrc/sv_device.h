@@ -193,8 +193,7 @@ __device__ __forceinline__ uint4 encode16(const float* x)
 // invalidation is involved.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCpolSc1 = 16;                            // agent-coherent access
-constexpr int kCpolSc1Volatile = 16 | (int)(1u << 31);  // ... never merged or hoisted
+constexpr int kCpolSc1 = 16;  // agent-coherent access: misses the CU cache, served by L2
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
@@ -206,9 +205,12 @@ __device__ __forceinline__ void put_atom(__amdgpu_buffer_rsrc_t r, uint32_t off,
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kCpolSc1);
 }
 
+// Not volatile: a volatile access is widened to system scope, which sends it
+// past L2; loops that poll a record re-read it after a compiler barrier
+// instead (wait_record).
 __device__ __forceinline__ u32x4 get_atom(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1Volatile);
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1);
 }
 
 // Word hash of the record tags (multiply-rotate rounds and a final avalanche).
