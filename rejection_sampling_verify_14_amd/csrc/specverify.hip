@@ -1594,8 +1594,13 @@ __global__ __launch_bounds__(64) void k_accept(const VerifyParams P)
     chain_accept<DT>(P, (int)blockIdx.x, P.seqs[blockIdx.x], true);
 }
 
-// Block (b, g): chunk sums of group g of sequence b's chunks, one contiguous
-// share per wave, stored as records.
+// Blocks [0, B*groups): block (b, g) forms the chunk sums of group g of
+// sequence b's chunks, one contiguous share per wave, stored as records.
+// Blocks [B*groups, B*groups + B): the final step of sequence blockIdx.x -
+// B*groups.  A grid's blocks are dispatched in index order, so when a final
+// block starts every chunk block is running or done; it waits (bounded) for
+// its sequence's records, and the finals of early sequences run while the
+// last chunk blocks drain.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void
 #if SV_CHUNK_WAVES
@@ -1603,9 +1608,18 @@ __attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
 #endif
 k_chunks(const VerifyParams P)
 {
+    __shared__ double s_t32[32];
+    const int nblocks = P.B * P.groups;
+    if ((int)blockIdx.x >= nblocks) {
+        const int b = (int)blockIdx.x - nblocks;
+        const SeqState s = P.seqs[b];
+        // first read after sample_final's first barrier
+        fill_t32(s_t32);
+        sample_final<DT, false>(P, b, s, nullptr, s_t32);
+        return;
+    }
     const int b = (int)blockIdx.x / P.groups;
     const int g = (int)blockIdx.x - b * P.groups;
-    __shared__ double s_t32[32];
     const SeqState s = P.seqs[b];  // in flight with the table fill
     fill_t32(s_t32);
     __syncthreads();
@@ -1630,18 +1644,6 @@ k_chunks(const VerifyParams P)
         if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_t32);
         if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
     }
-}
-
-// Final step of sequence blockIdx.x.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_final(const VerifyParams P)
-{
-    __shared__ double s_t32[32];
-    const SeqState s = P.seqs[blockIdx.x];
-    // the table is first read after sample_final's first barrier, so its
-    // fill needs none of its own and the record loads overlap the state's
-    fill_t32(s_t32);
-    sample_final<DT, false>(P, (int)blockIdx.x, s, nullptr, s_t32);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -1759,7 +1761,7 @@ void set_groups(sv::VerifyParams& P)
 #ifndef SV_CHUNKS_PER_BLOCK
 #define SV_CHUNKS_PER_BLOCK 4
 #endif
-// Chains: the row kernel, then the sample step (accept, chunk sums, final).
+// Chains: the row kernel, then the sample step (accept; chunk sums and final).
 template <int DT>
 int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
@@ -1773,8 +1775,9 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
                        stream, P);
     if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
     hipLaunchKernelGGL((sv::k_accept<DT>), dim3(B), dim3(64), 0, stream, P);
-    hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * P.groups)), dim3(sv::kBlock), 0, stream, P);
-    hipLaunchKernelGGL((sv::k_final<DT>), dim3(B), dim3(sv::kBlock), 0, stream, P);
+    // chunk-sum blocks, then one final-step block per sequence
+    hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
+                       stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
@@ -1839,7 +1842,7 @@ bool item_count_ok(int B, int rows, int V)
 {
     int segs, seg_len;
     segments_of(V, &segs, &seg_len);
-    return 2 * (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * nchunks_of(V) < (int64_t)INT32_MAX;
+    return 2 * (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * (nchunks_of(V) + 1) < (int64_t)INT32_MAX;
 }
 
 }  // namespace
