@@ -39,9 +39,9 @@
  *     different workspaces and outputs.  The only process-wide state is a
  *     call counter (an atomic) that tags each call's results, and cached
  *     occupancy figures.
- *   - A chain verify call is four kernel launches (row statistics, accept,
- *     chunk sums, final step); a tree verify call is two (row statistics,
- *     accept and sampling).  Row statistics are summed per fixed segment of
+ *   - A chain verify call is three kernel launches (row statistics, accept,
+ *     chunk sums with the final step in the same grid); a tree verify call
+ *     is two (row statistics, accept and sampling).  Row statistics are summed per fixed segment of
  *     about 32K tokens and combined in segment order, so results do not
  *     depend on the device's compute-unit count.
  */
