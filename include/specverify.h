@@ -69,11 +69,12 @@ enum sv_status {
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
-/* Optional timing hook: when non-NULL, each non-NULL event is recorded on
- * `stream`: `begin` right before the row-statistics kernel, `rows_done`
- * between it and the kernels of the sample step, `end` right after them, so
- * a caller can time the row kernel and the sample step.  The records sit
- * between kernels on the stream; timing costs a few microseconds a call. */
+/* Optional timing hook: when non-NULL, `begin` and `rows_done` are the
+ * start and stop events of the row-statistics kernel (stamped by that
+ * kernel's own start and end on `stream`), and `end`, when non-NULL, is
+ * recorded right after the kernels of the sample step, so a caller can time
+ * the row kernel and the sample step.  The `end` record sits between
+ * kernels on the stream; timing costs a few microseconds a call. */
 typedef struct sv_timing {
     hipEvent_t begin;
     hipEvent_t rows_done;

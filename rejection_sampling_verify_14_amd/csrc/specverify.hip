@@ -41,6 +41,7 @@
 // W = sum_{q>p} (a_t - rho b_t) + band, rho = Sq/Sp, once the exact Sq, Sp
 // are known.  The band is exact: its tokens share one zq - zp (one ratio
 // q/p) or their chunk is rescanned with the exact rho.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -168,12 +169,36 @@ __device__ __forceinline__ uint4 neg_inf16()
     return make_uint4(w, w, w, w);
 }
 
+// Batch bt of a row's 16-byte vectors into x, U per thread, every address
+// clamped into the row (a lane past the end re-reads the last vector), so
+// the loads carry no branches.  nvec > 0.
+template <int U>
+__device__ __forceinline__ void load_batch(const uint4* __restrict__ vrow, int nvec, int bt, uint4* x)
+{
+    const int v0 = bt * U * kBlock + (int)threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = stream_load16(vrow + min(v0 + u * kBlock, nvec - 1));
+}
+
+// The vectors of batch bt past the row's end replaced by -inf (for the one
+// partial batch, once its loads are in).
+template <int DT, int U>
+__device__ __forceinline__ void mask_batch(int nvec, int bt, uint4* x)
+{
+    const int v0 = bt * U * kBlock + (int)threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (v0 + u * kBlock >= nvec) x[u] = neg_inf16<DT>();
+}
+
 // (m, s) of n consecutive elements starting at `row`, valid in thread 0.
 // Rows need only be element-aligned: the elements before the first 16-byte
 // boundary are read one by one, the rest as 16-byte vectors in batches of U
-// per thread, the next batch's loads issued before the current batch is used
-// (the last batch is padded with -inf, so every batch is a full set of
-// loads in flight).
+// per thread, the next batch's loads issued before the current batch is used.
+// The loop runs over pairs of whole batches with two register sets and an
+// unconditional (clamped) prefetch: no register a load is still writing is
+// copied or overwritten, and no branch merges load states, so each batch
+// waits only for its own loads.  The partial batch, if any, is masked after.
 template <int DT, int U>
 __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row, int n, float c, double cd)
 {
@@ -195,23 +220,30 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     n -= head;
     const int nvec = n / EPV;
     const uint4* __restrict__ vrow = reinterpret_cast<const uint4*>(row);
-    const int nbatch = (nvec + U * kBlock - 1) / (U * kBlock);
-    int v = threadIdx.x;
-    uint4 cur[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = (v + u * kBlock < nvec) ? stream_load16(vrow + v + u * kBlock) : neg_inf16<DT>();
-    for (int bt = 0; bt < nbatch; ++bt) {
-        const int nv = v + U * kBlock;
-        uint4 nxt[U];
-        if (bt + 1 < nbatch) {
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-                nxt[u] = (nv + u * kBlock < nvec) ? stream_load16(vrow + nv + u * kBlock) : neg_inf16<DT>();
+    const int nfull = nvec / (U * kBlock);
+    const bool part = nvec > nfull * U * kBlock;
+    if (nvec > 0) {
+        uint4 x0[U], x1[U];
+        load_batch<U>(vrow, nvec, 0, x0);
+        int bt = 0;
+        for (; bt + 2 <= nfull; bt += 2) {
+            load_batch<U>(vrow, nvec, bt + 1, x1);
+            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+            load_batch<U>(vrow, nvec, bt + 2, x0);
+            accumulate_batch<DT, U>(x1, c, cd, ref, acc);
         }
-        accumulate_batch<DT, U>(cur, c, cd, ref, acc);
-        v = nv;
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        // x0 holds batch bt: the last whole one, the partial one, or none
+        if (bt < nfull) {
+            load_batch<U>(vrow, nvec, bt + 1, x1);
+            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+            if (part) {
+                mask_batch<DT, U>(nvec, bt + 1, x1);
+                accumulate_batch<DT, U>(x1, c, cd, ref, acc);
+            }
+        } else if (part) {
+            mask_batch<DT, U>(nvec, bt, x0);
+            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+        }
     }
     const int tail = n - nvec * EPV;
     if ((int)threadIdx.x < tail) {
@@ -1761,6 +1793,16 @@ void set_groups(sv::VerifyParams& P)
 #ifndef SV_CHUNKS_PER_BLOCK
 #define SV_CHUNKS_PER_BLOCK 4
 #endif
+// The row kernel; with a timing hook, its begin and rows_done events are
+// stamped by the kernel's own start and end (not by records beside it, whose
+// interval would also hold the dispatch gap before the kernel).
+template <int DT, bool TREE>
+void launch_rows(const sv::VerifyParams& P, int64_t grid, const sv_timing* timing, hipStream_t stream)
+{
+    const hipEvent_t t0 = timing ? timing->begin : nullptr, t1 = timing ? timing->rows_done : nullptr;
+    hipExtLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)grid), dim3(sv::kBlock), 0, stream, t0, t1, 0, P);
+}
+
 // Chains: the row kernel, then the sample step (accept; chunk sums and final).
 template <int DT>
 int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
@@ -1770,10 +1812,7 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
     P.cpb = (P.nch + groups - 1) / groups;
     P.groups = (P.nch + P.cpb - 1) / P.cpb;
     const unsigned B = (unsigned)P.B;
-    if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
-    hipLaunchKernelGGL((sv::k_rows<DT, false>), dim3((unsigned)((int64_t)P.B * P.r_items)), dim3(sv::kBlock), 0,
-                       stream, P);
-    if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
+    launch_rows<DT, false>(P, (int64_t)P.B * P.r_items, timing, stream);
     hipLaunchKernelGGL((sv::k_accept<DT>), dim3(B), dim3(64), 0, stream, P);
     // chunk-sum blocks, then one final-step block per sequence
     hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
@@ -1791,10 +1830,12 @@ int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream
     // at least one row block: the row kernel also fills the exp table
     const int64_t row_grid = (int64_t)P.B * P.r_items;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
-    if (timing && timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
-    if (row_grid > 0)
-        hipLaunchKernelGGL((sv::k_rows<DT, true>), dim3((unsigned)row_grid), dim3(sv::kBlock), 0, stream, P);
-    if (timing && timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
+    if (row_grid > 0) {
+        launch_rows<DT, true>(P, row_grid, timing, stream);
+    } else if (timing) {
+        if (timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
+        if (timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
+    }
     hipLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;

@@ -127,11 +127,13 @@ __device__ __forceinline__ float load_logit(const char* row, int64_t t)
     }
 }
 
-// 16-byte streaming load of pass-1 rows.  SV_STREAM_NT selects the
-// nontemporal hint (rows are read once by pass 1; the rows a sequence samples
-// from are re-read soon after, so the default keeps ordinary caching).
+// 16-byte streaming load of pass-1 rows, with the nontemporal hint by
+// default (SV_STREAM_NT): pass 1 reads every row once, and the rows a
+// sequence samples from (a few percent) are re-read from HBM either way.
+// With the row kernel's loads kept in flight across batches the hint lifts
+// its stream from ~6.0 to ~6.8 TB/s on C3.
 #ifndef SV_STREAM_NT
-#define SV_STREAM_NT 0
+#define SV_STREAM_NT 1
 #endif
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 stream_load16(const uint4* p)
