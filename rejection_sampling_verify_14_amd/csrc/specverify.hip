@@ -484,19 +484,13 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
 // exp_rel); the argument is one fma, z/T - m/T.
 struct ExpRow {
     double invT, mb;  // 1/T and -m/T
-    lds_dptr t32;     // the block's copy of kExp2Table (see exp_rel)
-    __device__ __forceinline__ double operator()(float z) const { return exp_rel(fma((double)z, invT, mb), t32); }
+    lds_dptr tab;     // the block's copy of the 2^(j/N) table (see exp_rel)
+    __device__ __forceinline__ double operator()(float z) const { return exp_rel(fma((double)z, invT, mb), tab); }
 };
 
-__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* t32)
+__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* etab)
 {
-    return ExpRow{P.invT, -m * P.invT, (lds_dptr)t32};
-}
-
-// The block's copy of kExp2Table (call before a barrier).
-__device__ __forceinline__ void fill_t32(double* t32)
-{
-    if (threadIdx.x < 32) t32[threadIdx.x] = kExp2Table[threadIdx.x];
+    return ExpRow{P.invT, -m * P.invT, (lds_dptr)etab};
 }
 
 // ===========================================================================
@@ -1133,7 +1127,7 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
 // wave; valid in every lane.
 template <int DT>
 __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, const char* qrow, const char* prow,
-                                     int c, const ExpRow& eq, const ExpRow& ep, const double* t32)
+                                     int c, const ExpRow& eq, const ExpRow& ep, const double* etab)
 {
     ChunkSums out{};
     if (s.mode == kModeResidual) {
@@ -1161,7 +1155,7 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         bonus_max<DT>(P, qrow, c, lm, bad);
         const float mc = wave_max(lm);
         double sa = 0.0;
-        if (mc != -INFINITY) sa = bonus_sum<DT>(P, qrow, c, exp_row(P, mc, t32));
+        if (mc != -INFINITY) sa = bonus_sum<DT>(P, qrow, c, exp_row(P, mc, etab));
         out.sa = (double)mc;
         out.sb = wave_sum(sa);
         out.flags = __any(bad) ? kFlagBad : 0u;
@@ -1263,7 +1257,7 @@ struct FinalPlan {
 // through one barrier; the block then rescans the chunk.
 template <int DT, bool TREE>
 __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path,
-                             const double* t32)
+                             const double* etab)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nchunks = P.nch;
@@ -1286,7 +1280,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     auto chunk_at = [&](int c) -> ChunkSums { return c < kFinalCache ? s_cs[c] : get_chunk(P, b, c); };
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, t32), ep = exp_row(P, s.mp, t32);
+    const ExpRow eq = exp_row(P, s.mq, etab), ep = exp_row(P, s.mp, etab);
 
     // --- wave 0: records, totals, location ---
     const int g = (nchunks + 63) / 64;
@@ -1462,7 +1456,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         mc = chunk_at(cs).sa;
         scale = exp((mc - M) * invT);
     }
-    const ExpRow ec = exp_row(P, mc, t32);
+    const ExpRow ec = exp_row(P, mc, etab);
     double wv[kPerThread];
 #pragma unroll
     for (int j = 0; j < kPerThread; ++j) {
@@ -1575,15 +1569,15 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     const int g = (int)blockIdx.x - b * P.groups;
     __shared__ SeqState s_state;
     __shared__ int32_t s_path[kMaxNodes];
-    __shared__ double s_t32[32];
-    fill_t32(s_t32);
+    __shared__ double s_etab[kExpTabN];
+    fill_exp_table(s_etab);
     tree_accept<DT>(P, b, s_state, s_path, g == 0);
     __syncthreads();
     const SeqState s = s_state;
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, s_t32), ep = exp_row(P, s.mp, s_t32);
+    const ExpRow eq = exp_row(P, s.mq, s_etab), ep = exp_row(P, s.mp, s_etab);
     // each wave takes a contiguous share of the block's chunks; whole chunks
     // of aligned rows stream with loads in flight across chunk boundaries
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
@@ -1601,14 +1595,14 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     }
     for (; c < cb; ++c) {
         ChunkSums out{};
-        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_t32);
+        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_etab);
         if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
     }
     __syncthreads();
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
     __syncthreads();
-    if (s_last) sample_final<DT, true>(P, b, s, s_path, s_t32);
+    if (s_last) sample_final<DT, true>(P, b, s, s_path, s_etab);
 }
 
 // ---------------------------------------------------------------------------
@@ -1640,25 +1634,25 @@ __attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
 #endif
 k_chunks(const VerifyParams P)
 {
-    __shared__ double s_t32[32];
+    __shared__ double s_etab[kExpTabN];
     const int nblocks = P.B * P.groups;
     if ((int)blockIdx.x >= nblocks) {
         const int b = (int)blockIdx.x - nblocks;
         const SeqState s = P.seqs[b];
         // first read after sample_final's first barrier
-        fill_t32(s_t32);
-        sample_final<DT, false>(P, b, s, nullptr, s_t32);
+        fill_exp_table(s_etab);
+        sample_final<DT, false>(P, b, s, nullptr, s_etab);
         return;
     }
     const int b = (int)blockIdx.x / P.groups;
     const int g = (int)blockIdx.x - b * P.groups;
     const SeqState s = P.seqs[b];  // in flight with the table fill
-    fill_t32(s_t32);
+    fill_exp_table(s_etab);
     __syncthreads();
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, s_t32), ep = exp_row(P, s.mp, s_t32);
+    const ExpRow eq = exp_row(P, s.mq, s_etab), ep = exp_row(P, s.mp, s_etab);
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
     const int wave = (int)threadIdx.x >> 6;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
@@ -1673,7 +1667,7 @@ k_chunks(const VerifyParams P)
     }
     for (; c < cb; ++c) {
         ChunkSums out{};
-        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_t32);
+        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_etab);
         if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
     }
 }

@@ -77,37 +77,62 @@ __device__ __forceinline__ double sample_uniform(uint64_t seed, uint64_t round, 
 
 // ---------------------------------------------------------------------------
 // exp(x) in double by Tang's table-driven method (P.T.P. Tang, ACM TOMS
-// 15(2), 1989): n = round(32x/ln2), r = x - n ln2/32, so |r| <= ln2/64 up to
-// rounding, and exp(x) = 2^(n>>5) 2^((n&31)/32) exp(r) with exp(r) - 1 from
-// its Taylor polynomial of degree 4 (truncation below 1.3e-12 relative).
-// 2^((n&31)/32) comes from the block's LDS copy of kExp2Table: its 32
-// doubles sit in distinct banks, so a wave's lookups never conflict.
+// 15(2), 1989), with a table of kExpTabN = 64 (or 32, SV_EXP_TAB) entries
+// 2^(j/N): n = round(N x/ln2), r = x - n ln2/N, so |r| <= ln2/(2N) up to
+// rounding, and exp(x) = 2^(n>>log2 N) 2^((n&(N-1))/N) exp(r).  The 2^(j/N)
+// come from the block's LDS copy of the table (fill_exp_table).  exp(r) - 1
+// is r g(r) with g from its Chebyshev interpolant of degree 2 on
+// |r| <= ln2/128 (N = 64; below 1e-11 relative), or r times the Taylor
+// polynomial of degree 3 of g (N = 32; truncation below 1.3e-12 relative).
 //
-// r is formed by one fma against ln2/32 rounded to a double: the product is
+// r is formed by one fma against ln2/N rounded to a double: the product is
 // exact inside the fma, and the rounding of the constant shifts r by at most
-// |n| * 2.4e-18, below 1e-14 relative for |x| <= 40 and below 8e-14 over the
-// whole clamped range.  n is the low word of 32x/ln2 + 1.5 * 2^52.  x is
-// clamped below at -1000, where 2^(n>>5) underflows ldexp to exactly 0, so a
-// masked logit (-inf) contributes nothing; terms between exp(-745) and
-// exp(-708) come out as denormals.  x must not exceed 700 (callers' x are
+// |n| * 1.2e-18 * 32/N, below 1e-14 relative for |x| <= 40 and below 8e-14
+// over the whole clamped range.  n is the low word of N x/ln2 + 1.5 * 2^52.
+// x is clamped below at -1000, where the final ldexp underflows to exactly
+// 0, so a masked logit (-inf) contributes nothing; terms between exp(-745)
+// and exp(-708) come out as denormals.  x must not exceed 700 (callers' x are
 // relative to their row's reference, so at most 6T or so).  NaN is not
-// propagated (callers screen it).  About 15 full-rate operations.
+// propagated (callers screen it).  14 (N = 64) or 15 full-rate operations.
 // ---------------------------------------------------------------------------
+#ifndef SV_EXP_TAB
+#define SV_EXP_TAB 64
+#endif
+constexpr int kExpTabN = SV_EXP_TAB;
+static_assert(kExpTabN == 32 || kExpTabN == 64, "exp table of 32 or 64 entries");
 typedef const double __attribute__((address_space(3)))* lds_dptr;  // LDS-typed: ds_read, 32-bit address
 
-__device__ __forceinline__ double exp_rel(double x, lds_dptr t32)
+__device__ __forceinline__ double exp_rel(double x, lds_dptr tab)
 {
     constexpr double kRound = 0x1.8p52;
     x = fmax(x, -1000.0);
-    const double kd = fma(x, k32ByLn2, kRound);
-    const int n = (int)(uint32_t)__double_as_longlong(kd);
-    const double r = fma(kd - kRound, -kLn2By32, x);
-    double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
-    p = fma(r, p, 0.5);
-    p = fma(r, p, 1.0);
-    p *= r;
-    const double t = t32[n & 31];
-    return ldexp(fma(t, p, t), n >> 5);
+    if constexpr (kExpTabN == 64) {
+        const double kd = fma(x, k64ByLn2, kRound);
+        const int n = (int)(uint32_t)__double_as_longlong(kd);
+        const double r = fma(kd - kRound, -kLn2By64, x);
+        double p = fma(r, kExpG2, kExpG1);
+        p = fma(r, p, 1.0);
+        p *= r;
+        const double t = tab[n & 63];
+        return ldexp(fma(t, p, t), n >> 6);
+    } else {
+        const double kd = fma(x, k32ByLn2, kRound);
+        const int n = (int)(uint32_t)__double_as_longlong(kd);
+        const double r = fma(kd - kRound, -kLn2By32, x);
+        double p = fma(r, 1.0 / 24.0, 1.0 / 6.0);
+        p = fma(r, p, 0.5);
+        p = fma(r, p, 1.0);
+        p *= r;
+        const double t = tab[n & 31];
+        return ldexp(fma(t, p, t), n >> 5);
+    }
+}
+
+// The block's LDS copy of the 2^(j/N) table (its N doubles; publish it with
+// a barrier before the first exp_rel).
+__device__ __forceinline__ void fill_exp_table(double* tab)
+{
+    if (threadIdx.x < kExpTabN) tab[threadIdx.x] = kExpTabN == 64 ? kExp2Table64[threadIdx.x] : kExp2Table32[threadIdx.x & 31];
 }
 
 // ---------------------------------------------------------------------------
