@@ -177,6 +177,54 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
+def tree_mask_bench(steps: int, warmup: int):
+    """tree_attention_mask on config 5's trees (B=128, 61 nodes, per-sequence
+    parents from the dynamic-tree recipe; the logits only shape the trees, so
+    they are drawn at a small V).  One JSON line of its own."""
+    import torch
+
+    import rejection_sampling_verify_14_amd as sv
+    import synth
+
+    w = synth.WORKLOADS["c5"]
+    parents = synth.dynamic_tree_inputs(w.with_sizes(V=1024), seed=7, B=w.B)["parents"].to("cuda")
+    B, nn = parents.shape
+    L0 = torch.full((B,), w.L0, dtype=torch.int32, device="cuda")
+    out = sv.tree_attention_mask(parents, kv_len_in=L0)
+    for _ in range(warmup):
+        sv.tree_attention_mask(parents, kv_len_in=L0, out=out)
+    torch.cuda.synchronize()
+    # a call takes less GPU time than its Python launch, so the calls are
+    # captured in a graph of `per_graph` launches and the graph is replayed
+    per_graph = 50
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            sv.tree_attention_mask(parents, kv_len_in=L0, out=out)
+    reps = max(1, steps // per_graph)
+    graph.replay()
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    a, b = hip.event(), hip.event()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(a), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(reps):
+        graph.replay()
+    hip.lib.hipEventRecord(ctypes.c_void_p(b), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    steps = reps * per_graph
+    us = hip.elapsed_ms(a, b) * 1000.0 / steps
+    W = (nn + 63) // 64
+    nbytes = B * nn * 4 + B * 4 + B * nn * (8 * W + 4)   # parents + kv_len read, mask + positions written
+    print(json.dumps({
+        "metric": "tree attention mask builds/s (config 5 trees)", "value": round(1e6 / us, 1), "unit": "calls/s",
+        "us_per_call": round(us, 3), "steps": steps, "warmup": warmup, "higher_is_better": True,
+        "data": "synthetic", "config": {"workload": f"tree mask B={B} nodes={nn} (config 5 dynamic trees)"},
+        "roofline": {"bound": "latency", "bytes_per_call": nbytes, "achieved": round(nbytes / us / 1e3, 2),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / us / 1e3 / 8000.0, 6)}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +235,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -201,6 +250,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.tree_mask:
+        tree_mask_bench(args.steps, args.warmup)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]

@@ -206,6 +206,30 @@ int kv_compact_indices(const int32_t* path_nodes, const int32_t* num_accepted, c
                        hipStream_t stream);
 
 /*
+ * tree_attention_mask -- the verifier-side inputs of a tree verify pass
+ * ([ZH] section 3, "草稿树与树形注意力掩码": the draft tree is flattened into
+ * one sequence of numbered nodes and every node attends only to itself and
+ * its ancestors, never to its siblings, so one verifier forward pass scores
+ * every node; [PT] "Reversao de KV cache": the verifier runs attention with a
+ * non-causal mask that follows the tree's topology).
+ *
+ * parents as for spec_verify_tree: [T+1] shared by every sequence
+ * (parents_shared != 0) or [B, T+1]; parent[0] = -1 and 0 <= parent[n] < n.
+ * For node n of sequence b:
+ *   out_mask [B, T+1, W] uint64, W = ceil((T+1)/64): bit (j & 63) of word
+ *     (j >> 6) of row n is set iff node j is n or an ancestor of n (the tree
+ *     part of the attention mask; every node also sees the KV prefix, which
+ *     the mask does not cover).
+ *   out_positions [B, T+1] int32: L0 + depth(n), with depth(0) = 0 and
+ *     L0 = kv_len_in[b] (the KV row of node 0, as for kv_compact_indices;
+ *     0 when kv_len_in is NULL): node n's position id.
+ * A sequence whose parents break the rule gets an all-zero mask and -1
+ * positions.  0 <= T <= 1023; out_mask and out_positions are required.
+ */
+int tree_attention_mask(const int32_t* parents, int parents_shared, const int32_t* kv_len_in, int B, int T,
+                        uint64_t* out_mask, int32_t* out_positions, hipStream_t stream);
+
+/*
  * sv_philox_uniforms -- the uniforms the verify step draws, for tests of
  * the device generator: for sequences [0, nseq) and positions 1..npos,
  * out_acc[s*npos + p-1] and out_samp[s*npos + p-1] (device double arrays,

@@ -76,6 +76,8 @@ def lib():
         L.orc_verify_tree.restype = ctypes.c_int
         L.orc_kv_compact.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i64, i64, i32, i32, i64]
         L.orc_kv_compact.restype = ctypes.c_int
+        L.orc_tree_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp]
+        L.orc_tree_mask.restype = ctypes.c_int
         L.orc_accept_prob.argtypes = [vp, vp, i32, i32, ctypes.c_double, i32]
         L.orc_accept_prob.restype = ctypes.c_double
         L.orc_residual_probs.argtypes = [vp, vp, i32, i32, ctypes.c_double, vp]
@@ -290,6 +292,29 @@ def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o
+
+
+def tree_mask(parents, kv_len_in=None, B: int = None):
+    """Tree attention mask and position ids ("投机解码与 EAGLE", section 3):
+    parents [T+1] (shared; B required) or [B, T+1].  Returns mask uint64
+    [B, T+1, ceil((T+1)/64)] (bit j of row n: j is n or an ancestor of n) and
+    positions int32 [B, T+1] = kv_len_in[b] + depth(n)."""
+    parents = np.ascontiguousarray(parents, dtype=np.int32)
+    shared = parents.ndim == 1
+    if shared:
+        if B is None:
+            raise ValueError("B is required with shared parents")
+    else:
+        B = parents.shape[0]
+    nn = parents.shape[-1]
+    W = (nn + 63) // 64
+    if kv_len_in is not None:
+        kv_len_in = np.ascontiguousarray(kv_len_in, dtype=np.int32)
+    mask = np.zeros((B, nn, W), np.uint64)
+    pos = np.zeros((B, nn), np.int32)
+    if lib().orc_tree_mask(_ptr(parents), int(shared), _ptr(kv_len_in), B, nn - 1, _ptr(mask), _ptr(pos)) != 0:
+        raise ValueError("oracle rejected the arguments")
+    return mask, pos
 
 
 def kv_compact(path_nodes, num_accepted, kv_len_in, max_depth: int, kv=None):

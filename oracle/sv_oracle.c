@@ -661,6 +661,46 @@ int orc_kv_compact(const int32_t* path_nodes, const int32_t* num_accepted, const
 }
 
 /* ------------------------------------------------------------------------- */
+/* Tree attention mask and position ids ("投机解码与 EAGLE", section 3: the     */
+/* flattened tree is verified in one pass in which each node sees only itself */
+/* and its ancestors).  Row n of sequence b has bit j set iff j is n or an    */
+/* ancestor of n, found by following parent links from n to the root;         */
+/* positions[n] = L0 + depth(n).  Parents breaking parent[0] = -1,            */
+/* 0 <= parent[n] < n zero the sequence's mask and set its positions to -1.   */
+/* mask is [B][T+1][W] 64-bit words, W = ceil((T+1)/64), bit j of the row is  */
+/* bit (j % 64) of word j / 64.                                               */
+/* ------------------------------------------------------------------------- */
+int orc_tree_mask(const int32_t* parents, int parents_shared, const int32_t* kv_len_in, int B, int T,
+                  uint64_t* mask, int32_t* positions)
+{
+    if (B < 0 || T < 0) return 1;
+    const int nn = T + 1, W = (nn + 63) / 64;
+    for (int b = 0; b < B; ++b) {
+        const int32_t* par = parents_shared ? parents : parents + (int64_t)b * nn;
+        int ok = par[0] == -1;
+        for (int n = 1; n < nn; ++n)
+            if (par[n] < 0 || par[n] >= n) ok = 0;
+        const int L0 = kv_len_in ? kv_len_in[b] : 0;
+        for (int n = 0; n < nn; ++n) {
+            uint64_t* row = mask + ((int64_t)b * nn + n) * W;
+            for (int w = 0; w < W; ++w) row[w] = 0;
+            if (!ok) {
+                positions[(int64_t)b * nn + n] = -1;
+                continue;
+            }
+            int depth = 0;
+            for (int j = n;; j = par[j]) {
+                row[j / 64] |= (uint64_t)1 << (j % 64);
+                if (j == 0) break;
+                ++depth;
+            }
+            positions[(int64_t)b * nn + n] = L0 + depth;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Primitives exposed for the pins.                                           */
 /* ------------------------------------------------------------------------- */
 

@@ -14,6 +14,9 @@ Functions (same names as the C ABI):
                         sections 3 and 4)
   kv_compact_indices -- KV rollback / compaction ([PT] Passo 4; [ZH]
                         section 3)
+  tree_attention_mask -- ancestor mask and position ids of flattened draft
+                        trees, the verifier-side inputs of a tree verify
+                        pass ([ZH] section 3)
   sv_philox_uniforms -- the step's uniforms (for tests)
 """
 from __future__ import annotations
@@ -69,6 +72,8 @@ def _lib():
                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
         L.kv_compact_indices.restype = i32
         L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
+        L.tree_attention_mask.restype = i32
+        L.tree_attention_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
         L.sv_philox_uniforms.restype = i32
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
         if L.sv_abi_version() != 2:
@@ -257,6 +262,31 @@ def kv_compact_indices(path_nodes: Optional[torch.Tensor], num_accepted: torch.T
     return o
 
 
+def tree_attention_mask(parents: torch.Tensor, kv_len_in: Optional[torch.Tensor] = None, B: Optional[int] = None,
+                        out: Optional[dict] = None, stream=None) -> dict:
+    """Tree attention mask and position ids of flattened draft trees.
+    parents int32 [T+1] (shared; B required) or [B, T+1]; kv_len_in int32 [B]
+    (the KV row of node 0) or None (0).  Returns mask int64 [B, T+1, W]
+    (W = ceil((T+1)/64) 64-bit words; bit j of row n: node j is n or an
+    ancestor of n) and positions int32 [B, T+1] (kv_len_in + depth)."""
+    shared = parents.dim() == 1
+    if shared and B is None:
+        raise ValueError("B is required with shared parents")
+    B = B if shared else parents.shape[0]
+    nn = parents.shape[-1]
+    W = (nn + 63) // 64
+    dev = parents.device
+    o = out if out is not None else {
+        "mask": torch.empty((B, nn, W), dtype=torch.int64, device=dev),
+        "positions": torch.empty((B, nn), dtype=torch.int32, device=dev),
+    }
+    rc = _lib().tree_attention_mask(_p(parents), int(shared), _p(kv_len_in), B, nn - 1, _p(o["mask"]),
+                                    _p(o["positions"]), _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "tree_attention_mask")
+    return o
+
+
 def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda", stream=None):
     """(u_acc, u_samp) [nseq, npos] float64 for positions 1..npos."""
     a = torch.empty((nseq, npos), dtype=torch.float64, device=device)
@@ -268,6 +298,6 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
     return a, s
 
 
-__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "sv_philox_uniforms",
+__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "sv_philox_uniforms",
            "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",
            "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16"]

@@ -103,6 +103,12 @@ def test_tree_and_kv_argument_errors(sv):
     assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 128, 1, 0, None) == 1  # row > stride
     assert kv(None, FAKE, FAKE, 0, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 0
     assert L.sv_philox_uniforms(0, 0, -1, 3, FAKE, None, None) == 1
+    tm = L.tree_attention_mask
+    assert tm(FAKE, 1, None, 2, 1024, FAKE, FAKE, None) == 3      # T + 1 > 1024
+    assert tm(FAKE, 1, None, -1, 5, FAKE, FAKE, None) == 1 and tm(FAKE, 1, None, 2, -1, FAKE, FAKE, None) == 1
+    assert tm(None, 1, None, 2, 5, FAKE, FAKE, None) == 1 and tm(FAKE, 1, None, 2, 5, None, FAKE, None) == 1
+    assert tm(FAKE, 1, None, 2, 5, FAKE, None, None) == 1
+    assert tm(FAKE, 1, None, 0, 5, FAKE, FAKE, None) == 0         # empty batch
 
 
 def test_product_never_reaches_the_oracle():

@@ -362,3 +362,40 @@ def test_kv_chain_indices_and_invalid_paths():
     torch.cuda.synchronize()
     assert out["kv_len"].tolist() == [-1, -1]
     assert torch.equal(kv, before)
+
+
+def test_tree_attention_mask_parity():
+    """Ancestor masks and position ids of flattened trees, bit-exact against the
+    oracle: config 4's static tree (shared parents), config 5's dynamic trees,
+    random trees of 1..1024 nodes (one to sixteen 64-bit words per row), a
+    1024-node chain (the deepest walk) and sequences with broken parents."""
+    import rejection_sampling_verify_14_amd as sv
+    rng = np.random.default_rng(5)
+
+    def random_trees(nn, B):
+        return np.stack([np.concatenate([[-1], rng.integers(0, np.arange(1, nn))]).astype(np.int32)
+                         if nn > 1 else np.array([-1], np.int32) for _ in range(B)])
+
+    w5 = synth.WORKLOADS["c5"].with_sizes(V=512)
+    cases = [("c4_static", np.array(synth.STATIC_TREE_PARENTS, np.int32), 32),
+             ("c5_dynamic", synth.dynamic_tree_inputs(w5, seed=4, B=16)["parents"].numpy(), None)]
+    for nn in (1, 2, 63, 64, 65, 200, 1024):
+        cases.append((f"random_{nn}", random_trees(nn, 5), None))
+    cases.append(("chain_1024", np.array([[-1] + list(range(1023))], np.int32), None))
+    broken = random_trees(40, 6)
+    broken[1, 0] = 0
+    broken[3, 17] = 17
+    broken[4, 30] = -3
+    cases.append(("broken", broken, None))
+    for name, P, B in cases:
+        Bn = B if P.ndim == 1 else P.shape[0]
+        L0 = rng.integers(0, 5000, Bn).astype(np.int32)
+        for with_len in (True, False):
+            log(f"[case] tree_mask {name} kv_len={with_len}")
+            kv_len = torch.tensor(L0, device="cuda") if with_len else None
+            out = sv.tree_attention_mask(torch.tensor(P, device="cuda"), kv_len_in=kv_len, B=B)
+            torch.cuda.synchronize()
+            m_o, p_o = oracle.tree_mask(P, L0 if with_len else None, B=B)
+            assert np.array_equal(out["mask"].cpu().numpy().view(np.uint64), m_o), name
+            assert np.array_equal(out["positions"].cpu().numpy(), p_o), name
+    log("[done] tree_mask parity")

@@ -15,6 +15,7 @@ import oracle
 import test_oracle_pins as P
 import test_oracle_stats as S
 import test_oracle_tree_kv as TK
+import test_oracle_tree_mask as TM
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sv_oracle.c")
 
@@ -42,6 +43,10 @@ MUTANTS = {
                                 "            if (next < 0) {\n                residual = 0;"),
     "kv_len_off_by_one": ("out_kv_len[b] = L0 + k + 1;", "out_kv_len[b] = L0 + k;"),
     "kv_gather_wrong_dst": ("memcpy(seqbase + (int64_t)(L0 + i) * row_stride,", "memcpy(seqbase + (int64_t)(L0 + k - i) * row_stride,"),
+    "mask_misses_self": ("            for (int j = n;; j = par[j]) {", "            for (int j = n ? par[n] : 0;; j = par[j]) {"),
+    "mask_one_word": ("row[j / 64] |= (uint64_t)1 << (j % 64);", "row[0] |= (uint64_t)1 << (j % 64);"),
+    "mask_depth_counts_self": ("positions[(int64_t)b * nn + n] = L0 + depth;", "positions[(int64_t)b * nn + n] = L0 + depth + 1;"),
+    "mask_root_unchecked": ("int ok = par[0] == -1;", "int ok = 1;"),
 }
 
 
@@ -65,6 +70,9 @@ def _battery():
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 4)
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 7)
     yield lambda: TK.test_kv_gather_matches_fancy_indexing(oracle, False)
+    yield lambda: TM.test_chain_is_the_causal_mask(130)
+    yield lambda: TM.test_every_small_tree_by_matrix_powers(5)
+    yield lambda: TM.test_bad_parents_mark_only_their_sequence()
 
 
 @pytest.fixture(scope="module")
