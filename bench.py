@@ -225,6 +225,43 @@ def tree_mask_bench(steps: int, warmup: int):
                      "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / us / 1e3 / 8000.0, 6)}}), flush=True)
 
 
+def tree_build_bench(steps: int, warmup: int):
+    """The EAGLE-2 dynamic tree grown on the device (tree_expand per level,
+    tree_select between levels, tree_finalize) over config 5's draft rows:
+    B=128, depth 6, top-10, budget 60, V=152064 bf16, T=0.7.  One JSON line
+    of its own; the HBM roofline counts every expanded row read once."""
+    import torch
+
+    import rejection_sampling_verify_14_amd as sv
+    import synth
+
+    w = synth.WORKLOADS["c5"]
+    rows = synth.dynamic_tree_inputs(w, seed=7, device="cuda")["expanded_p"]
+    B, n_exp, V = rows.shape
+    for _ in range(warmup):
+        sv.tree_build(rows, depth=w.depth, topk=w.topk, budget=w.budget, temperature=w.T)
+    hip = Hip()
+    stream = torch.cuda.current_stream()
+    a, b = hip.event(), hip.event()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(a), ctypes.c_void_p(stream.cuda_stream))
+    for _ in range(steps):
+        sv.tree_build(rows, depth=w.depth, topk=w.topk, budget=w.budget, temperature=w.T)
+    hip.lib.hipEventRecord(ctypes.c_void_p(b), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    us = hip.elapsed_ms(a, b) * 1000.0 / steps
+    nbytes = B * n_exp * V * rows.element_size()
+    gbps = nbytes / us / 1e3
+    print(json.dumps({
+        "metric": "dynamic draft trees built/s (config 5)", "value": round(1e6 / us * B, 1), "unit": "trees/s",
+        "us_per_batch": round(us, 2), "steps": steps, "warmup": warmup, "higher_is_better": True, "data": "synthetic",
+        "config": {"workload": f"EAGLE-2 tree build B={B} depth={w.depth} topk={w.topk} budget={w.budget} "
+                               f"V={V} bf16 T={w.T}"},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbps / 8000.0, 4), "bytes_per_batch": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,6 +273,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
+    ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on config 5 rows instead")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -253,6 +291,9 @@ def main():
         return
     if args.tree_mask:
         tree_mask_bench(args.steps, args.warmup)
+        return
+    if args.tree_build:
+        tree_build_bench(args.steps, args.warmup)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]

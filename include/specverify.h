@@ -230,6 +230,62 @@ int tree_attention_mask(const int32_t* parents, int parents_shared, const int32_
                         uint64_t* out_mask, int32_t* out_positions, hipStream_t stream);
 
 /*
+ * EAGLE-2 dynamic draft tree, built level by level on the device ([ZH]
+ * section 4, "eagle_round" step 2: every frontier node adds its top-k draft
+ * tokens as children whose score is the parent's score times p(token), and
+ * the best nodes are picked to grow next; section 5, EAGLE-2: nodes are
+ * allotted globally by that score, and the tree keeps the `budget` best).
+ * The draft model runs between the levels (not here): the caller feeds
+ * each level's frontier rows to tree_expand, picks the next frontier with
+ * tree_select, and flattens the tree with tree_finalize.
+ *
+ * Candidate table (caller-owned device arrays, n_max <= 2048 entries per
+ * sequence, entry (b, i) at b*n_max + i): cand_token, cand_parent (the
+ * parent's candidate id; -1 = the root), cand_level (1 = child of the
+ * root), cand_score (double: the sum of ln p along the path, i.e. the
+ * logarithm of the pages' product of probabilities; NaN marks a failed row).
+ * Creation order is the candidate id; ties in score go to the lower id.
+ */
+
+/*
+ * tree_expand -- one level: frontier row f of sequence b (logits at
+ * frontier_logits + (b*seq_stride + f*row_stride) elements, V of them,
+ * dtype SV_F32 / SV_BF16) gives its top-k tokens by (logit desc, token asc)
+ * with p = softmax(logits / temperature), as candidates offset + f*topk + r
+ * (r = rank): token, parent frontier_ids[b*F + f] (NULL: -1, the root),
+ * level, score frontier_score[b*F + f] (NULL: 0) + ln p(token).  The row's
+ * log-sum-exp sums fp32 exp2 terms in double (about 1e-8 relative).  A row
+ * with NaN or +inf, or of -inf only, gives NaN scores.  1 <= topk <= 16,
+ * topk <= V, offset + F*topk <= n_max <= 2048.
+ */
+int tree_expand(const void* frontier_logits, int64_t seq_stride, int64_t row_stride, int dtype, int B, int F, int V,
+                int topk, float temperature, const int32_t* frontier_ids, const double* frontier_score, int level,
+                int n_max, int offset, int32_t* cand_token, int32_t* cand_parent, int32_t* cand_level,
+                double* cand_score, hipStream_t stream);
+
+/*
+ * tree_select -- the next frontier: of candidates [offset, offset + count)
+ * of each sequence, the k best by (score desc, id asc), in that order:
+ * out_ids [B, k] (candidate ids) and out_score [B, k].  NaN ranks lowest.
+ */
+int tree_select(const double* cand_score, int B, int n_max, int offset, int count, int k, int32_t* out_ids,
+                double* out_score, hipStream_t stream);
+
+/*
+ * tree_finalize -- the kept set, the `budget` best of candidates [0, n) by
+ * (score desc, id asc) (ancestor-closed: a child never outscores its parent
+ * and is created after it), numbered 1..budget by (level asc, score desc,
+ * id asc): out_parents, out_tokens, out_depth [B, budget+1] int32 and
+ * out_score [B, budget+1] double; node 0 is the root (parent -1, token 0,
+ * depth 0, score 0).  out_parents feeds spec_verify_tree and
+ * tree_attention_mask.  A sequence with a NaN score gets -1 (score 0) in
+ * every slot.  1 <= budget <= n <= n_max <= 2048.
+ */
+int tree_finalize(const int32_t* cand_token, const int32_t* cand_parent, const int32_t* cand_level,
+                  const double* cand_score, int B, int n_max, int n, int budget, int32_t* out_parents,
+                  int32_t* out_tokens, int32_t* out_depth, double* out_score, hipStream_t stream);
+
+/*
  * sv_philox_uniforms -- the uniforms the verify step draws, for tests of
  * the device generator: for sequences [0, nseq) and positions 1..npos,
  * out_acc[s*npos + p-1] and out_samp[s*npos + p-1] (device double arrays,

@@ -76,6 +76,8 @@ def lib():
         L.orc_verify_tree.restype = ctypes.c_int
         L.orc_kv_compact.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i64, i64, i32, i32, i64]
         L.orc_kv_compact.restype = ctypes.c_int
+        L.orc_tree_build.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, vp]
+        L.orc_tree_build.restype = ctypes.c_int
         L.orc_tree_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp]
         L.orc_tree_mask.restype = ctypes.c_int
         L.orc_accept_prob.argtypes = [vp, vp, i32, i32, ctypes.c_double, i32]
@@ -292,6 +294,31 @@ def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o
+
+
+def tree_build(rows, depth: int, topk: int, budget: int, T: float = 1.0):
+    """EAGLE-2 dynamic draft tree ("投机解码与 EAGLE", section 4, eagle_round
+    step 2; section 5, the dynamic tree).  rows [B, 1 + topk*(depth-1), V]
+    (float32, float64 or bf16 bits as uint16): the draft logits of the root
+    (row 0) and of each level's frontier in rank order.  Returns parents,
+    tokens, depth (int32 [B, budget+1]), log-scores (float64 [B, budget+1])
+    and the frontiers' candidate ids (int32 [B, depth-1, topk])."""
+    rows = np.ascontiguousarray(rows)
+    B, n_exp, V = rows.shape
+    if n_exp != 1 + topk * (depth - 1):
+        raise ValueError("rows must hold 1 + topk*(depth-1) expanded rows")
+    ss, rs = _strides3(rows)
+    nn = budget + 1
+    par = np.empty((B, nn), np.int32)
+    tok = np.empty((B, nn), np.int32)
+    dep = np.empty((B, nn), np.int32)
+    score = np.empty((B, nn), np.float64)
+    front = np.full((B, max(depth - 1, 0), topk), -1, np.int32)
+    rc = lib().orc_tree_build(_ptr(rows), ss, rs, _dtype_code(rows), B, V, depth, topk, budget, _temperature(T),
+                              _ptr(par), _ptr(tok), _ptr(dep), _ptr(score), _ptr(front))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return {"parents": par, "tokens": tok, "depth": dep, "score": score, "frontier": front}
 
 
 def tree_mask(parents, kv_len_in=None, B: int = None):

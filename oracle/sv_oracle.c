@@ -701,6 +701,162 @@ int orc_tree_mask(const int32_t* parents, int parents_shared, const int32_t* kv_
 }
 
 /* ------------------------------------------------------------------------- */
+/* EAGLE-2 dynamic draft tree ("投机解码与 EAGLE", section 4, eagle_round step */
+/* 2: every frontier node adds its top-k draft tokens as children with score  */
+/* parent score * p(token); the dynamic tree (section 5, EAGLE-2) picks the   */
+/* globally best nodes to expand and keeps the best `budget` overall).        */
+/*                                                                           */
+/* rows [B][n_exp][V] (strides in elements): the draft logits of the expanded */
+/* nodes -- row 0 the root's, then for level l = 1..depth-1 the `topk` rows   */
+/* of level l's frontier in rank order (row 1 + (l-1)*topk + r).              */
+/* Readings: scores are kept as log-scores (sums of ln p, the logarithm of    */
+/* the pages' product: same order, no underflow); p = softmax(logits / T);    */
+/* a row's top-k is taken by (logit desc, token asc); the frontier of level   */
+/* l is the top-k of level l's candidates and the kept set the top-budget of */
+/* all candidates, both by (score desc, creation order asc), creation order  */
+/* being level, then frontier rank, then token rank; the kept nodes are      */
+/* numbered 1..budget by (level asc, score desc, creation order asc).  The    */
+/* kept set is ancestor-closed: a child's score never exceeds its parent's   */
+/* and the parent was created first.                                         */
+/* Outputs [B][budget+1]: parents (node 0: -1), tokens (node 0: 0), depth,   */
+/* log-score (node 0: 0); frontier_out (optional) [B][depth-1][topk]: the    */
+/* candidate ids of each level's frontier.  A sequence with NaN or +inf in   */
+/* an expanded row, or a row of -inf only, gets -1 in every output slot.    */
+/* Returns 1 on bad sizes.                                                  */
+/* ------------------------------------------------------------------------- */
+typedef struct {
+    double score;
+    int id;
+} scored_id;
+
+static int by_score_then_id(const void* a, const void* b)
+{
+    const scored_id* x = (const scored_id*)a;
+    const scored_id* y = (const scored_id*)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->id > y->id) - (x->id < y->id);
+}
+
+int orc_tree_build(const void* rows, int64_t seq_stride, int64_t row_stride, int dtype, int B, int V, int depth,
+                   int topk, int budget, double T, int32_t* out_parents, int32_t* out_tokens, int32_t* out_depth,
+                   double* out_score, int32_t* frontier_out)
+{
+    if (B < 0 || V < 1 || depth < 1 || topk < 1 || topk > V || budget < 1 || !(T > 0.0)) return 1;
+    const int n_cand = topk + (depth - 1) * topk * topk;
+    if (budget > n_cand) return 1;
+    const int nn = budget + 1;
+    int* c_tok = (int*)malloc(sizeof(int) * n_cand);
+    int* c_par = (int*)malloc(sizeof(int) * n_cand);
+    int* c_lev = (int*)malloc(sizeof(int) * n_cand);
+    double* c_score = (double*)malloc(sizeof(double) * n_cand);
+    scored_id* order = (scored_id*)malloc(sizeof(scored_id) * n_cand);
+    int* node_of = (int*)malloc(sizeof(int) * n_cand);
+    int* top_tok = (int*)malloc(sizeof(int) * topk);
+    double* top_val = (double*)malloc(sizeof(double) * topk);
+    int* f_ids = (int*)malloc(sizeof(int) * topk);
+    double* f_score = (double*)malloc(sizeof(double) * topk);
+    for (int b = 0; b < B; ++b) {
+        int n = 0, F = 1, bad = 0;
+        f_ids[0] = -1;
+        f_score[0] = 0.0;
+        for (int level = 1; level <= depth; ++level) {
+            const int first = n;
+            for (int f = 0; f < F; ++f) {
+                const int slot = level == 1 ? 0 : 1 + (level - 2) * topk + f;
+                const void* row = row_ptr(rows, dtype, seq_stride, row_stride, b, slot);
+                double m, lse;
+                if (orc_row_lse(row, dtype, V, T, &m, &lse)) bad = 1;
+                /* top-k by (logit desc, token asc): one pass over the row
+                   keeping a sorted list; a later token displaces only a
+                   strictly smaller logit */
+                int cnt = 0;
+                for (int t = 0; t < V; ++t) {
+                    const double v = logit_at(row, dtype, t);
+                    if (cnt == topk && !(v > top_val[topk - 1])) continue;
+                    int pos = cnt < topk ? cnt++ : topk - 1;
+                    while (pos > 0 && top_val[pos - 1] < v) {
+                        top_val[pos] = top_val[pos - 1];
+                        top_tok[pos] = top_tok[pos - 1];
+                        --pos;
+                    }
+                    top_val[pos] = v;
+                    top_tok[pos] = t;
+                }
+                for (int r = 0; r < topk; ++r) {
+                    c_tok[n] = top_tok[r];
+                    c_par[n] = f_ids[f];
+                    c_lev[n] = level;
+                    c_score[n] = f_score[f] + (top_val[r] / T - lse);
+                    ++n;
+                }
+            }
+            if (level < depth) {
+                const int cnt = n - first;
+                for (int i = 0; i < cnt; ++i) {
+                    order[i].score = c_score[first + i];
+                    order[i].id = first + i;
+                }
+                qsort(order, (size_t)cnt, sizeof(scored_id), by_score_then_id);
+                F = topk;
+                for (int r = 0; r < topk; ++r) {
+                    f_ids[r] = order[r].id;
+                    f_score[r] = order[r].score;
+                    if (frontier_out) frontier_out[((int64_t)b * (depth - 1) + (level - 1)) * topk + r] = order[r].id;
+                }
+            }
+        }
+        /* the kept set: top-budget of all candidates */
+        for (int i = 0; i < n; ++i) {
+            order[i].score = c_score[i];
+            order[i].id = i;
+            node_of[i] = -1;
+        }
+        qsort(order, (size_t)n, sizeof(scored_id), by_score_then_id);
+        /* number the kept nodes by (level asc, score desc, id asc): a stable
+           pass per level over the kept set in score order */
+        int next = 1;
+        for (int level = 1; level <= depth; ++level)
+            for (int i = 0; i < budget; ++i)
+                if (c_lev[order[i].id] == level) node_of[order[i].id] = next++;
+        int32_t* P = out_parents + (int64_t)b * nn;
+        int32_t* K = out_tokens + (int64_t)b * nn;
+        int32_t* D = out_depth + (int64_t)b * nn;
+        double* S = out_score + (int64_t)b * nn;
+        if (bad) { /* NaN or +inf in an expanded row, or a row of -inf only */
+            for (int i = 0; i < nn; ++i) {
+                P[i] = K[i] = D[i] = -1;
+                S[i] = 0.0;
+            }
+            continue;
+        }
+        P[0] = -1;
+        K[0] = 0;
+        D[0] = 0;
+        S[0] = 0.0;
+        for (int i = 0; i < budget; ++i) {
+            const int c = order[i].id;
+            const int node = node_of[c];
+            P[node] = c_par[c] < 0 ? 0 : node_of[c_par[c]];
+            K[node] = c_tok[c];
+            D[node] = c_lev[c];
+            S[node] = c_score[c];
+        }
+    }
+    free(c_tok);
+    free(c_par);
+    free(c_lev);
+    free(c_score);
+    free(order);
+    free(node_of);
+    free(top_tok);
+    free(top_val);
+    free(f_ids);
+    free(f_score);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Primitives exposed for the pins.                                           */
 /* ------------------------------------------------------------------------- */
 

@@ -17,6 +17,9 @@ Functions (same names as the C ABI):
   tree_attention_mask -- ancestor mask and position ids of flattened draft
                         trees, the verifier-side inputs of a tree verify
                         pass ([ZH] section 3)
+  tree_expand, tree_select, tree_finalize -- EAGLE-2 dynamic draft tree,
+                        level by level ([ZH] sections 4 and 5); tree_build
+                        chains them over draft rows given up front
   sv_philox_uniforms -- the step's uniforms (for tests)
 """
 from __future__ import annotations
@@ -72,6 +75,13 @@ def _lib():
                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
         L.kv_compact_indices.restype = i32
         L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
+        L.tree_expand.restype = i32
+        L.tree_expand.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, ctypes.c_float, vp, vp, i32, i32, i32, vp, vp,
+                                  vp, vp, vp]
+        L.tree_select.restype = i32
+        L.tree_select.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp]
+        L.tree_finalize.restype = i32
+        L.tree_finalize.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.tree_attention_mask.restype = i32
         L.tree_attention_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
         L.sv_philox_uniforms.restype = i32
@@ -287,6 +297,92 @@ def tree_attention_mask(parents: torch.Tensor, kv_len_in: Optional[torch.Tensor]
     return o
 
 
+def alloc_tree_table(B: int, n_max: int, device) -> dict:
+    """A candidate table for tree_expand / tree_select / tree_finalize."""
+    return {"token": torch.empty((B, n_max), dtype=torch.int32, device=device),
+            "parent": torch.empty((B, n_max), dtype=torch.int32, device=device),
+            "level": torch.empty((B, n_max), dtype=torch.int32, device=device),
+            "score": torch.empty((B, n_max), dtype=torch.float64, device=device)}
+
+
+def tree_expand(frontier_logits: torch.Tensor, table: dict, *, topk: int, level: int, offset: int,
+                temperature: float = 1.0, frontier_ids: Optional[torch.Tensor] = None,
+                frontier_score: Optional[torch.Tensor] = None, stream=None) -> None:
+    """One level of a dynamic draft tree: frontier_logits [B, F, V] (rows
+    with a unit last stride) add topk candidates per row at offset +
+    f*topk of the table."""
+    if frontier_logits.dim() != 3 or frontier_logits.stride(2) != 1:
+        raise ValueError("frontier_logits must be [B, F, V] with a unit last stride")
+    B, F, V = frontier_logits.shape
+    n_max = table["score"].shape[1]
+    rc = _lib().tree_expand(_p(frontier_logits), frontier_logits.stride(0), frontier_logits.stride(1),
+                            _dtype_code(frontier_logits), B, F, V, topk, float(temperature), _p(frontier_ids),
+                            _p(frontier_score), level, n_max, offset, _p(table["token"]), _p(table["parent"]),
+                            _p(table["level"]), _p(table["score"]), _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "tree_expand")
+
+
+def tree_select(table: dict, *, offset: int, count: int, k: int, stream=None):
+    """The next frontier: ids and scores [B, k] of the k best candidates in
+    [offset, offset + count)."""
+    B, n_max = table["score"].shape
+    dev = table["score"].device
+    ids = torch.empty((B, k), dtype=torch.int32, device=dev)
+    sc = torch.empty((B, k), dtype=torch.float64, device=dev)
+    rc = _lib().tree_select(_p(table["score"]), B, n_max, offset, count, k, _p(ids), _p(sc), _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "tree_select")
+    return ids, sc
+
+
+def tree_finalize(table: dict, *, n: int, budget: int, stream=None) -> dict:
+    """The kept set of candidates [0, n), flattened: parents, tokens, depth
+    [B, budget+1] int32 and score [B, budget+1] float64."""
+    B, n_max = table["score"].shape
+    dev = table["score"].device
+    o = {"parents": torch.empty((B, budget + 1), dtype=torch.int32, device=dev),
+         "tokens": torch.empty((B, budget + 1), dtype=torch.int32, device=dev),
+         "depth": torch.empty((B, budget + 1), dtype=torch.int32, device=dev),
+         "score": torch.empty((B, budget + 1), dtype=torch.float64, device=dev)}
+    rc = _lib().tree_finalize(_p(table["token"]), _p(table["parent"]), _p(table["level"]), _p(table["score"]), B,
+                              n_max, n, budget, _p(o["parents"]), _p(o["tokens"]), _p(o["depth"]), _p(o["score"]),
+                              _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "tree_finalize")
+    return o
+
+
+def tree_build(rows: torch.Tensor, *, depth: int, topk: int, budget: int, temperature: float = 1.0,
+               stream=None) -> dict:
+    """A whole dynamic tree from draft rows that exist up front (synthetic
+    runs): rows [B, 1 + topk*(depth-1), V] hold the root's row, then each
+    level's frontier rows in rank order.  Chains tree_expand (per level),
+    tree_select (between levels) and tree_finalize; adds the frontiers'
+    candidate ids [B, depth-1, topk] to the result."""
+    B, n_exp, V = rows.shape
+    if n_exp != 1 + topk * (depth - 1):
+        raise ValueError("rows must hold 1 + topk*(depth-1) expanded rows")
+    n = topk + (depth - 1) * topk * topk
+    table = alloc_tree_table(B, n, rows.device)
+    ids = sc = None
+    frontiers = []
+    offset, F = 0, 1
+    for level in range(1, depth + 1):
+        slot = 0 if level == 1 else 1 + (level - 2) * topk
+        tree_expand(rows[:, slot:slot + F], table, topk=topk, level=level, offset=offset, temperature=temperature,
+                    frontier_ids=ids, frontier_score=sc, stream=stream)
+        if level < depth:
+            ids, sc = tree_select(table, offset=offset, count=F * topk, k=topk, stream=stream)
+            frontiers.append(ids)
+        offset += F * topk
+        F = topk
+    out = tree_finalize(table, n=n, budget=budget, stream=stream)
+    out["frontier"] = torch.stack(frontiers, 1) if frontiers else torch.empty((B, 0, topk), dtype=torch.int32,
+                                                                               device=rows.device)
+    return out
+
+
 def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda", stream=None):
     """(u_acc, u_samp) [nseq, npos] float64 for positions 1..npos."""
     a = torch.empty((nseq, npos), dtype=torch.float64, device=device)
@@ -298,6 +394,7 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
     return a, s
 
 
-__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "sv_philox_uniforms",
+__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "tree_expand",
+           "tree_select", "tree_finalize", "tree_build", "alloc_tree_table", "sv_philox_uniforms",
            "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",
            "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16"]

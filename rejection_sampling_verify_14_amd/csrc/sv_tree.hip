@@ -3,6 +3,7 @@
 // its ancestors only).  gfx950, wave64.
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 #include "specverify.h"
@@ -62,6 +63,363 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree_mask(const int32_t* __restr
     }
 }
 
+// ---------------------------------------------------------------------------
+// EAGLE-2 dynamic draft tree ("投机解码与 EAGLE", section 4, eagle_round step
+// 2; section 5, the dynamic tree).  Candidates live in a caller-owned table
+// of n_max entries per sequence: token, parent candidate id (-1 = the
+// root), level, log-score (the sum of ln p along the path: the logarithm of
+// the pages' product of probabilities).
+// ---------------------------------------------------------------------------
+constexpr int kTopkMax = 16;
+constexpr int kTreeMaxCand = 2048;
+
+// A 64-bit key ordering (logit desc, token asc): the logit's bits made
+// order-preserving in the high word, the token inverted in the low word.
+__device__ __forceinline__ uint64_t topk_key(float x, int t)
+{
+    const uint32_t u = __float_as_uint(x);
+    const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return ((uint64_t)o << 32) | (uint32_t)~(uint32_t)t;
+}
+
+__device__ __forceinline__ float key_value(uint64_t k)
+{
+    const uint32_t o = (uint32_t)(k >> 32);
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+__device__ __forceinline__ int key_token(uint64_t k) { return (int)~(uint32_t)k; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint64_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+struct ExpandArgs {
+    const char* rows;
+    int64_t seq_stride, row_stride;  // elements
+    const int32_t* frontier_ids;     // [B, F] or null (the root)
+    const double* frontier_score;    // [B, F] or null (0)
+    int F, V, topk, level, n_max, offset;
+    float invT;
+    double invTd, c;                  // 1/T, log2(e)/T
+    int32_t *cand_token, *cand_parent, *cand_level;
+    double* cand_score;
+};
+
+template <int DT>
+__device__ __forceinline__ float logit_of(const char* row, int64_t t)
+{
+    if constexpr (DT == 1) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[t] << 16);
+    else return reinterpret_cast<const float*>(row)[t];
+}
+
+// Block (b, f): one pass over frontier row f of sequence b: its log-sum-exp
+// and its top-k tokens by (logit desc, token asc); then k candidates at
+// offset + f*k of the table.  A row holding NaN or +inf, or only -inf,
+// gives NaN scores (the finalize step fails the sequence).
+//
+// Every decision that could diverge inside a wave is taken wave-uniformly:
+// - log-sum-exp: the terms of a 16-byte vector are fp32 exp2 against a
+//   reference that is the wave's running maximum (it moves, with an fp64
+//   rescale of the double sums, only when a vector raises it), summed in
+//   double;
+// - top-k: the wave holds one sorted list of its 16 best keys spread over
+//   lanes 0..15, and its 16th key tau is a wave-uniform threshold.  A vector
+//   whose largest value is below tau's is skipped; otherwise each key above
+//   tau is inserted, one lane at a time, by a parallel shift.  A key at or
+//   below tau is never among the 16 best of what the wave has seen (16
+//   distinct keys exceed it), so nothing is lost.
+template <int DT>
+__global__ __launch_bounds__(256) void k_tree_expand(ExpandArgs A)
+{
+    const int b = (int)blockIdx.x / A.F, f = (int)blockIdx.x - b * A.F;
+    constexpr int EB = DT == 1 ? 2 : 4;
+    constexpr int EPV = 16 / EB;
+    constexpr int U = 4;  // 16-byte loads per lane in flight
+    const char* row = A.rows + ((int64_t)b * A.seq_stride + (int64_t)f * A.row_stride) * EB;
+    const float cf = (float)A.c;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    float ref = -INFINITY;  // wave-uniform
+    double s = 0.0;         // this lane's terms against ref
+    int bad = 0;
+    uint64_t L = 0;    // lane j < 16: the wave's j-th best key (0 = none yet)
+    uint64_t tau = 0;  // wave-uniform: the wave's 16th best key
+    float tauv = -INFINITY;
+    auto insert = [&](uint64_t kn) {  // kn wave-uniform, not yet held, above tau
+        const uint64_t prev = __shfl_up(L, 1, 64);
+        const bool keep = L > kn;
+        L = lane < kTopkMax ? (keep ? L : ((lane == 0 || prev > kn) ? kn : prev)) : 0;
+        tau = __shfl(L, kTopkMax - 1, 64);
+        tauv = tau == 0 ? -INFINITY : key_value(tau);
+    };
+    // EPV logits of this lane at tokens t0.. (every lane of the wave calls;
+    // `real` false: padding, which adds nothing and is never a candidate)
+    auto take = [&](const float* x, int t0, bool real) {
+        float lm = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            bad |= real && ((x[i] != x[i]) || (x[i] == INFINITY));
+            lm = real ? fmaxf(lm, x[i]) : lm;
+        }
+        float wm = lm;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
+        if (wm > ref) {
+            s = (ref == -INFINITY) ? 0.0 : s * exp2((double)(ref - wm) * A.c);
+            ref = wm;
+        }
+        if (real && ref != -INFINITY) {
+            float g = 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f((x[i] - ref) * cf);
+            s += (double)g;
+        }
+        if (__ballot(real && lm >= tauv)) {
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) {
+                const uint64_t k = real ? topk_key(x[i], t0 + i) : 0;
+                uint64_t cm = __ballot(k > tau);
+                while (cm) {
+                    const int l = __ffsll((unsigned long long)cm) - 1;
+                    insert(__shfl(k, l, 64));
+                    cm = __ballot(k > tau) & (~0ull << l << 1);
+                }
+            }
+        }
+    };
+    const bool vec = ((((uintptr_t)row) & 15u) == 0);
+    const int nvec = vec ? A.V / EPV : 0;
+    // whole batches of U vectors per lane, then the rest (each lane's tokens
+    // increase along the row)
+    const int nfull = nvec / (U * 256) * (U * 256);
+    for (int v0 = 0; v0 < nfull; v0 += U * 256) {
+        uint4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) w[u] = reinterpret_cast<const uint4*>(row)[v0 + u * 256 + threadIdx.x];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float x[EPV];
+            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (DT == 1) {
+                    x[2 * q] = __uint_as_float(ws[q] << 16);
+                    x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
+                } else {
+                    x[q] = __uint_as_float(ws[q]);
+                }
+            }
+            take(x, (v0 + u * 256 + (int)threadIdx.x) * EPV, true);
+        }
+    }
+    for (int v0 = nfull; v0 < nvec; v0 += 256) {
+        const int v = v0 + (int)threadIdx.x;
+        float x[EPV];
+        if (v < nvec) {
+            const uint4 w = reinterpret_cast<const uint4*>(row)[v];
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if constexpr (DT == 1) {
+                    x[2 * q] = __uint_as_float(ws[q] << 16);
+                    x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
+                } else {
+                    x[q] = __uint_as_float(ws[q]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) x[i] = -INFINITY;
+        }
+        take(x, v * EPV, v < nvec);
+    }
+    for (int t0 = nvec * EPV; t0 < A.V; t0 += 256) {
+        // one logit per lane (unaligned rows, or the tail past the vectors);
+        // lanes past V hold -inf, add nothing and offer no key
+        const int t = t0 + (int)threadIdx.x;
+        const float x0 = t < A.V ? logit_of<DT>(row, t) : -INFINITY;
+        bad |= (t < A.V) && ((x0 != x0) || (x0 == INFINITY));
+        float wm = x0;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
+        if (wm > ref) {
+            s = (ref == -INFINITY) ? 0.0 : s * exp2((double)(ref - wm) * A.c);
+            ref = wm;
+        }
+        if (t < A.V && ref != -INFINITY) s += (double)__builtin_amdgcn_exp2f((x0 - ref) * cf);
+        const uint64_t k = t < A.V ? topk_key(x0, t) : 0;
+        uint64_t cm = __ballot(k > tau);
+        while (cm) {
+            const int l = __ffsll((unsigned long long)cm) - 1;
+            insert(__shfl(k, l, 64));
+            cm = __ballot(k > tau) & (~0ull << l << 1);
+        }
+    }
+    // the wave's sum (every lane shares ref)
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    __shared__ uint64_t s_keys[4 * kTopkMax];
+    __shared__ float s_m[4];
+    __shared__ double s_s[4];
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    if (lane < kTopkMax) s_keys[wave * kTopkMax + lane] = L;
+    if (lane == 0) {
+        s_m[wave] = ref;
+        s_s[wave] = s;
+    }
+    __syncthreads();
+    if (bad) s_bad = 1;
+    __syncthreads();
+    if (wave != 0) return;
+    // the row's log-sum-exp and the block's top-k by rank among the waves' lists
+    double S = 0.0;
+    float M = -INFINITY;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w]);
+    for (int w = 0; w < 4; ++w)
+        if (s_m[w] != -INFINITY) S += s_m[w] == M ? s_s[w] : s_s[w] * exp2((double)(s_m[w] - M) * A.c);
+    const uint64_t mine = s_keys[lane];
+    int rank = 0;
+    for (int j = 0; j < 4 * kTopkMax; ++j) rank += s_keys[j] > mine;
+    if (rank < A.topk) {
+        const double lse = (double)M * A.invTd + log(S);
+        const bool fail = s_bad || M == -INFINITY || mine == 0;
+        const int64_t at = (int64_t)b * A.n_max + A.offset + (int64_t)f * A.topk + rank;
+        const double fs = A.frontier_score ? A.frontier_score[(int64_t)b * A.F + f] : 0.0;
+        A.cand_token[at] = fail ? -1 : key_token(mine);
+        A.cand_parent[at] = A.frontier_ids ? A.frontier_ids[(int64_t)b * A.F + f] : -1;
+        A.cand_level[at] = A.level;
+        A.cand_score[at] = fail ? NAN : fs + ((double)key_value(mine) * A.invTd - lse);
+    }
+}
+
+// NaN-safe order of (score desc, id asc): NaN ranks as -inf.
+__device__ __forceinline__ double order_score(double v) { return v != v ? -INFINITY : v; }
+
+// Block b: the k best of candidates [offset, offset + count) of sequence b by
+// (score desc, id asc), in that order: their ids and scores.
+__global__ __launch_bounds__(256) void k_tree_select(const double* __restrict__ cand_score, int n_max, int offset,
+                                                     int count, int k, int32_t* __restrict__ out_ids,
+                                                     double* __restrict__ out_score)
+{
+    __shared__ double s_sc[kTreeMaxCand];
+    const int b = blockIdx.x;
+    const double* sc = cand_score + (int64_t)b * n_max + offset;
+    for (int i = threadIdx.x; i < count; i += 256) s_sc[i] = order_score(sc[i]);
+    __syncthreads();
+    for (int i = threadIdx.x; i < count; i += 256) {
+        const double v = s_sc[i];
+        int rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < count; ++j) {  // branch-free: bitwise, not short-circuit
+            const double sj = s_sc[j];
+            rank += (int)(sj > v) | ((int)(sj == v) & (int)(j < i));
+        }
+        if (rank < k) {
+            out_ids[(int64_t)b * k + rank] = offset + i;
+            out_score[(int64_t)b * k + rank] = sc[i];
+        }
+    }
+}
+
+// Block b: the kept set of sequence b -- the `budget` best candidates by
+// (score desc, id asc) -- numbered 1..budget by (level asc, score desc, id
+// asc), and the flattened tree: parents (node 0: -1), tokens (0), depth (0),
+// log-scores (0).  A NaN score, or a kept candidate whose parent is not kept
+// (never for tables the expand step wrote), fails the sequence: -1 in every
+// slot.
+__global__ __launch_bounds__(256) void k_tree_finalize(const int32_t* __restrict__ cand_token,
+                                                       const int32_t* __restrict__ cand_parent,
+                                                       const int32_t* __restrict__ cand_level,
+                                                       const double* __restrict__ cand_score, int n_max, int n,
+                                                       int budget, int32_t* __restrict__ out_parents,
+                                                       int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_depth,
+                                                       double* __restrict__ out_score)
+{
+    __shared__ double s_sc[kTreeMaxCand];
+    __shared__ int s_lev[kTreeMaxCand];
+    __shared__ int s_node[kTreeMaxCand];
+    __shared__ int s_pos[kTreeMaxCand];
+    const int b = blockIdx.x;
+    const int64_t base = (int64_t)b * n_max;
+    const int nn = budget + 1;
+    int bad = 0;
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const double v = cand_score[base + i];
+        bad |= v != v;
+        s_sc[i] = order_score(v);
+        s_lev[i] = cand_level[base + i];
+        s_node[i] = -1;
+    }
+    bad = __syncthreads_or(bad);
+    // kept: rank by (score desc, id asc) below budget
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const double v = s_sc[i];
+        int rank = 0;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {  // branch-free: bitwise, not short-circuit
+            const double sj = s_sc[j];
+            rank += (int)(sj > v) | ((int)(sj == v) & (int)(j < i));
+        }
+        if (rank < budget) s_node[i] = 0;
+    }
+    __syncthreads();
+    // node number of a kept candidate: 1 + the kept ones before it by
+    // (level asc, score desc, id asc)
+    for (int i = threadIdx.x; i < n; i += 256) {
+        s_pos[i] = -1;
+        if (s_node[i] < 0) continue;
+        const double v = s_sc[i];
+        const int lv = s_lev[i];
+        int pos = 0;
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {  // branch-free: bitwise, not short-circuit
+            const double sj = s_sc[j];
+            const int lj = s_lev[j];
+            const int before = (int)(sj > v) | ((int)(sj == v) & (int)(j < i));
+            pos += (int)(s_node[j] >= 0) & ((int)(lj < lv) | ((int)(lj == lv) & before));
+        }
+        s_pos[i] = pos + 1;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < n; i += 256) s_node[i] = s_pos[i];
+    __syncthreads();
+    int32_t* P = out_parents + (int64_t)b * nn;
+    int32_t* K = out_tokens + (int64_t)b * nn;
+    int32_t* D = out_depth + (int64_t)b * nn;
+    double* S = out_score + (int64_t)b * nn;
+    for (int i = threadIdx.x; i < n && !bad; i += 256) {
+        if (s_node[i] <= 0) continue;
+        const int node = s_node[i];  // 1..budget
+        const int par = cand_parent[base + i];
+        int pnode = 0;
+        if (par >= 0) pnode = (par < i && s_node[par] > 0) ? s_node[par] : -1;
+        P[node] = pnode;
+        K[node] = cand_token[base + i];
+        D[node] = s_lev[i];
+        S[node] = cand_score[base + i];
+        if (pnode < 0) bad = 1;
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0 && !bad) {
+        P[0] = -1;
+        K[0] = 0;
+        D[0] = 0;
+        S[0] = 0.0;
+    }
+    if (bad)
+        for (int i = threadIdx.x; i < nn; i += 256) {
+            P[i] = K[i] = D[i] = -1;
+            S[i] = 0.0;
+        }
+}
+
 }  // namespace sv
 
 extern "C" int tree_attention_mask(const int32_t* parents, int parents_shared, const int32_t* kv_len_in, int B,
@@ -73,5 +431,73 @@ extern "C" int tree_attention_mask(const int32_t* parents, int parents_shared, c
     if (!parents || !out_mask || !out_positions) return SV_EINVAL;
     hipLaunchKernelGGL(sv::k_tree_mask, dim3((unsigned)B), dim3(sv::kTreeBlock), 0, stream, parents, parents_shared,
                        kv_len_in, T, out_mask, out_positions);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" int tree_expand(const void* frontier_logits, int64_t seq_stride, int64_t row_stride, int dtype, int B,
+                           int F, int V, int topk, float temperature, const int32_t* frontier_ids,
+                           const double* frontier_score, int level, int n_max, int offset, int32_t* cand_token,
+                           int32_t* cand_parent, int32_t* cand_level, double* cand_score, hipStream_t stream)
+{
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
+    if (B < 0 || F < 1 || V < 1 || level < 1 || offset < 0 || seq_stride < 0 || row_stride < 0) return SV_EINVAL;
+    if (!(temperature > 0.0f) || !(temperature < INFINITY)) return SV_EINVAL;
+    if (topk < 1 || topk > sv::kTopkMax || topk > V) return SV_ESHAPE;
+    if (n_max > sv::kTreeMaxCand || (int64_t)offset + (int64_t)F * topk > n_max) return SV_ESHAPE;
+    if (B == 0) return SV_OK;
+    if (!frontier_logits || !cand_token || !cand_parent || !cand_level || !cand_score) return SV_EINVAL;
+    const int es = dtype == SV_BF16 ? 2 : 4;
+    if (((uintptr_t)frontier_logits) % es) return SV_EALIGN;
+    if ((int64_t)B * F > 0x7FFFFFFF) return SV_ESHAPE;
+    sv::ExpandArgs A;
+    A.rows = static_cast<const char*>(frontier_logits);
+    A.seq_stride = seq_stride;
+    A.row_stride = row_stride;
+    A.frontier_ids = frontier_ids;
+    A.frontier_score = frontier_score;
+    A.F = F;
+    A.V = V;
+    A.topk = topk;
+    A.level = level;
+    A.n_max = n_max;
+    A.offset = offset;
+    A.invT = 1.0f / temperature;
+    A.invTd = 1.0 / (double)temperature;
+    A.c = 1.4426950408889634074 / (double)temperature;
+    A.cand_token = cand_token;
+    A.cand_parent = cand_parent;
+    A.cand_level = cand_level;
+    A.cand_score = cand_score;
+    if (dtype == SV_BF16)
+        hipLaunchKernelGGL(sv::k_tree_expand<1>, dim3((unsigned)(B * F)), dim3(256), 0, stream, A);
+    else
+        hipLaunchKernelGGL(sv::k_tree_expand<0>, dim3((unsigned)(B * F)), dim3(256), 0, stream, A);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" int tree_select(const double* cand_score, int B, int n_max, int offset, int count, int k,
+                           int32_t* out_ids, double* out_score, hipStream_t stream)
+{
+    if (B < 0 || offset < 0 || count < 1 || k < 1 || k > count) return SV_EINVAL;
+    if (n_max > sv::kTreeMaxCand || (int64_t)offset + count > n_max) return SV_ESHAPE;
+    if (B == 0) return SV_OK;
+    if (!cand_score || !out_ids || !out_score) return SV_EINVAL;
+    hipLaunchKernelGGL(sv::k_tree_select, dim3((unsigned)B), dim3(256), 0, stream, cand_score, n_max, offset, count, k,
+                       out_ids, out_score);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+extern "C" int tree_finalize(const int32_t* cand_token, const int32_t* cand_parent, const int32_t* cand_level,
+                             const double* cand_score, int B, int n_max, int n, int budget, int32_t* out_parents,
+                             int32_t* out_tokens, int32_t* out_depth, double* out_score, hipStream_t stream)
+{
+    if (B < 0 || n < 1 || budget < 1 || budget > n || n > n_max) return SV_EINVAL;
+    if (n_max > sv::kTreeMaxCand) return SV_ESHAPE;
+    if (B == 0) return SV_OK;
+    if (!cand_token || !cand_parent || !cand_level || !cand_score || !out_parents || !out_tokens || !out_depth ||
+        !out_score)
+        return SV_EINVAL;
+    hipLaunchKernelGGL(sv::k_tree_finalize, dim3((unsigned)B), dim3(256), 0, stream, cand_token, cand_parent,
+                       cand_level, cand_score, n_max, n, budget, out_parents, out_tokens, out_depth, out_score);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }

@@ -203,7 +203,9 @@ def dynamic_tree_inputs(w: Workload, seed: int, device="cpu", B: Optional[int] =
 
     Returns zq, zp [B, budget+1, V], tokens [B, budget+1], parents
     [B, budget+1] (node 0 = root, nodes ordered by (depth, score desc,
-    creation order)), and depth_of [B, budget+1]."""
+    creation order)), depth_of [B, budget+1], and expanded_p
+    [B, 1 + topk*(depth-1), V]: the draft rows the tree was grown from (the
+    root's, then each level's frontier in rank order)."""
     B = w.B if B is None else B
     depth = w.depth if depth is None else depth
     topk = w.topk if topk is None else topk
@@ -295,7 +297,8 @@ def dynamic_tree_inputs(w: Workload, seed: int, device="cpu", B: Optional[int] =
     zp[:, 1:] = torch.where(has[:, :, None], gp, fp)
     depth_of = torch.zeros((B, nn), dtype=torch.int32, device=device)
     depth_of[:, 1:] = keep_level.to(torch.int32)
-    return {"zq": zq, "zp": zp, "tokens": tokens, "parents": parents, "depth_of": depth_of}
+    return {"zq": zq, "zp": zp, "tokens": tokens, "parents": parents, "depth_of": depth_of,
+            "expanded_p": exp_p}
 
 
 def _top_stable(score: torch.Tensor, k: int) -> torch.Tensor:

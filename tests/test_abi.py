@@ -109,6 +109,20 @@ def test_tree_and_kv_argument_errors(sv):
     assert tm(None, 1, None, 2, 5, FAKE, FAKE, None) == 1 and tm(FAKE, 1, None, 2, 5, None, FAKE, None) == 1
     assert tm(FAKE, 1, None, 2, 5, FAKE, None, None) == 1
     assert tm(FAKE, 1, None, 0, 5, FAKE, FAKE, None) == 0         # empty batch
+    def ex(**kw):
+        a = dict(rows=FAKE, dt=1, B=2, F=3, V=100, k=10, T=1.0, lvl=1, nmax=30, off=0)
+        a.update(kw)
+        return L.tree_expand(a["rows"], 300, 100, a["dt"], a["B"], a["F"], a["V"], a["k"], a["T"], None, None, a["lvl"],
+                             a["nmax"], a["off"], FAKE, FAKE, FAKE, FAKE, None)
+    assert ex(dt=5) == 2 and ex(k=17) == 3 and ex(k=0) == 3 and ex(V=5) == 3      # topk in [1, min(16, V)]
+    assert ex(off=1) == 3 and ex(nmax=4096) == 3 and ex(T=0.0) == 1 and ex(lvl=0) == 1
+    assert ex(rows=None) == 1 and ex(rows=FAKE + 1) == 4 and ex(B=0) == 0
+    assert L.tree_select(FAKE, 2, 30, 0, 31, 10, FAKE, FAKE, None) == 3          # past n_max
+    assert L.tree_select(FAKE, 2, 30, 0, 20, 21, FAKE, FAKE, None) == 1          # k > count
+    assert L.tree_select(FAKE, 0, 30, 0, 20, 10, FAKE, FAKE, None) == 0
+    assert L.tree_finalize(FAKE, FAKE, FAKE, FAKE, 2, 30, 30, 31, FAKE, FAKE, FAKE, FAKE, None) == 1  # budget > n
+    assert L.tree_finalize(FAKE, FAKE, FAKE, FAKE, 2, 4096, 510, 60, FAKE, FAKE, FAKE, FAKE, None) == 3
+    assert L.tree_finalize(FAKE, FAKE, FAKE, FAKE, 2, 30, 30, 10, None, FAKE, FAKE, FAKE, None) == 1
 
 
 def test_product_never_reaches_the_oracle():

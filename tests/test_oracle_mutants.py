@@ -15,6 +15,7 @@ import oracle
 import test_oracle_pins as P
 import test_oracle_stats as S
 import test_oracle_tree_kv as TK
+import test_oracle_tree_build as TB
 import test_oracle_tree_mask as TM
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sv_oracle.c")
@@ -47,6 +48,11 @@ MUTANTS = {
     "mask_one_word": ("row[j / 64] |= (uint64_t)1 << (j % 64);", "row[0] |= (uint64_t)1 << (j % 64);"),
     "mask_depth_counts_self": ("positions[(int64_t)b * nn + n] = L0 + depth;", "positions[(int64_t)b * nn + n] = L0 + depth + 1;"),
     "mask_root_unchecked": ("int ok = par[0] == -1;", "int ok = 1;"),
+    "tree_ties_to_later_token": ("while (pos > 0 && top_val[pos - 1] < v) {", "while (pos > 0 && top_val[pos - 1] <= v) {"),
+    "tree_score_without_lse": ("c_score[n] = f_score[f] + (top_val[r] / T - lse);", "c_score[n] = f_score[f] + top_val[r] / T;"),
+    "tree_frontier_worst": ("                    f_ids[r] = order[r].id;\n                    f_score[r] = order[r].score;",
+                            "                    f_ids[r] = order[cnt - 1 - r].id;\n                    f_score[r] = order[cnt - 1 - r].score;"),
+    "tree_parent_score_dropped": ("c_score[n] = f_score[f] + (top_val[r] / T - lse);", "c_score[n] = top_val[r] / T - lse;"),
 }
 
 
@@ -73,6 +79,10 @@ def _battery():
     yield lambda: TM.test_chain_is_the_causal_mask(130)
     yield lambda: TM.test_every_small_tree_by_matrix_powers(5)
     yield lambda: TM.test_bad_parents_mark_only_their_sequence()
+    yield lambda: TB.test_ties_go_to_the_lower_token()
+    yield lambda: TB.test_depth1_is_the_roots_topk(1.0)
+    yield lambda: TB.test_matches_the_generators_construction(512, 3)
+    yield lambda: TB.test_level2_scores_are_path_sums()
 
 
 @pytest.fixture(scope="module")
