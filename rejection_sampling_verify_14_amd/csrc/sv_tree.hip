@@ -72,6 +72,10 @@ __global__ __launch_bounds__(kTreeBlock) void k_tree_mask(const int32_t* __restr
 // ---------------------------------------------------------------------------
 constexpr int kTopkMax = 16;
 constexpr int kTreeMaxCand = 2048;
+constexpr int kExpandFewRows = 512;  // below this many rows an expand block has 16 waves
+#ifndef SV_TREE_BATCH
+#define SV_TREE_BATCH 4  // 16-byte loads per lane per batch of the expand kernel
+#endif
 
 // A 64-bit key ordering (logit desc, token asc): the logit's bits made
 // order-preserving in the high word, the token inverted in the low word.
@@ -119,177 +123,252 @@ __device__ __forceinline__ float logit_of(const char* row, int64_t t)
     else return reinterpret_cast<const float*>(row)[t];
 }
 
-// Block (b, f): one pass over frontier row f of sequence b: its log-sum-exp
-// and its top-k tokens by (logit desc, token asc); then k candidates at
-// offset + f*k of the table.  A row holding NaN or +inf, or only -inf,
-// gives NaN scores (the finalize step fails the sequence).
+// Element i (0 .. 16/es - 1) of a 16-byte vector of logits.
+template <int DT>
+__device__ __forceinline__ float vec_elem(const uint4& w, int i)
+{
+    const uint32_t ws = i / (DT == 1 ? 2 : 1) == 0 ? w.x : i / (DT == 1 ? 2 : 1) == 1 ? w.y
+                      : i / (DT == 1 ? 2 : 1) == 2 ? w.z : w.w;
+    if constexpr (DT == 1) return __uint_as_float((i & 1) ? (ws & 0xFFFF0000u) : (ws << 16));
+    else return __uint_as_float(ws);
+}
+
+__device__ __forceinline__ float wave_max_f(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// The 16th largest of the 64 lanes' values, in every lane: a bitonic sort
+// across the wave into descending lane order.
+__device__ __forceinline__ float wave_16th_largest(float v, int lane)
+{
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const float o = __shfl_xor(v, j, 64);
+            const bool desc = (lane & k) == 0, lower = (lane & j) == 0;
+            v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
+        }
+    }
+    return __shfl(v, kTopkMax - 1, 64);
+}
+
+constexpr int kClassNanPinf = 0x203;  // class-test mask: signalling NaN, quiet NaN, +inf
+
+// One wave's running state over its share of a row.
+struct ExpandWave {
+    float ref = -INFINITY;  // wave-uniform reference (the wave's running maximum)
+    double s = 0.0;         // this lane's exp terms against ref
+    uint64_t bad = 0;       // wave-uniform: lanes that met NaN or +inf
+    uint64_t L = 0;         // lane j < 16: the wave's j-th best key (0 = none yet)
+    uint64_t tau = 0;       // wave-uniform: the wave's 16th best key
+    float tauv = -INFINITY; // its value
+    float theta = -INFINITY;  // wave-uniform: a value at or below the 16th best seen
+};
+
+// Insert every key k of the wave above tau into the sorted list, one lane
+// at a time (a wave-uniform loop): each insert shifts the list by one lane
+// from the new key's place down.
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane j of each 16-lane row receives lane j - 1's value (DPP row_shr:1);
+// lane 0 of a row receives 0.
+__device__ __forceinline__ uint64_t row_shift_up_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x111, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x111, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void insert_keys(ExpandWave& st, uint64_t k, int lane)
+{
+    uint64_t cm = __ballot(k > st.tau);
+    while (cm) {
+        const int l = __ffsll((unsigned long long)cm) - 1;
+        const uint64_t kn = readlane_u64(k, l);  // wave-uniform, not yet held, above tau
+        const uint64_t prev = row_shift_up_u64(st.L);  // the list lives in lanes 0..15
+        const bool keep = st.L > kn;
+        st.L = lane < kTopkMax ? (keep ? st.L : ((lane == 0 || prev > kn) ? kn : prev)) : 0;
+        st.tau = readlane_u64(st.L, kTopkMax - 1);
+        st.tauv = st.tau == 0 ? -INFINITY : key_value(st.tau);
+        cm = __ballot(k > st.tau) & (~0ull << l << 1);
+    }
+}
+
+// A batch of U 16-byte vectors per lane (vector u of this lane starts at
+// token t0[u]; real[u] false: padding that adds nothing and offers no key).
+template <int DT, int U>
+__device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U], const int (&t0)[U],
+                                             const bool (&real)[U], float cf, double c, int lane)
+{
+    constexpr int EPV = DT == 1 ? 8 : 4;
+    float vm[U];
+    float lm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        vm[u] = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            const float x = vec_elem<DT>(w[u], i);
+            st.bad |= __ballot(__builtin_amdgcn_classf(x, kClassNanPinf));  // padding is -inf
+            vm[u] = fmaxf(vm[u], x);
+        }
+        vm[u] = real[u] ? vm[u] : -INFINITY;
+        lm = fmaxf(lm, vm[u]);
+    }
+    const float wm = wave_max_f(lm);
+    if (wm > st.ref) {
+        st.s = (st.ref == -INFINITY) ? 0.0 : st.s * exp2((double)(st.ref - wm) * c);
+        st.ref = wm;
+    }
+    if (st.ref != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float g = 0.0f;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f((vec_elem<DT>(w[u], i) - st.ref) * cf);
+            st.s += real[u] ? (double)g : 0.0;
+        }
+    }
+    // Until the wave holds 16 keys, 16 lanes' batch maxima bound the 16th
+    // best from below: 16 distinct keys reach that bound, so a value under
+    // it can never be among the 16 best.
+    if (st.tau == 0) st.theta = fmaxf(st.theta, wave_16th_largest(lm, lane));
+    const float thr = fmaxf(st.tauv, st.theta);
+    if (!__ballot(lm >= thr)) return;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (!__ballot(vm[u] >= thr)) continue;
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) {
+            // thr only rises while keys go in, so the test against its
+            // value at the batch's start passes every key that may insert
+            const float x = vec_elem<DT>(w[u], i);
+            if (__ballot(real[u] && x >= thr)) insert_keys(st, (real[u] && x >= st.theta) ? topk_key(x, t0[u] + i) : 0, lane);
+        }
+    }
+}
+
+// Block (b, f) of NW waves: one pass over frontier row f of sequence b: its
+// log-sum-exp and its top-k tokens by (logit desc, token asc); then k
+// candidates at offset + f*k of the table.  A row holding NaN or +inf, or
+// only -inf, gives NaN scores (the finalize step fails the sequence).
 //
 // Every decision that could diverge inside a wave is taken wave-uniformly:
 // - log-sum-exp: the terms of a 16-byte vector are fp32 exp2 against a
 //   reference that is the wave's running maximum (it moves, with an fp64
-//   rescale of the double sums, only when a vector raises it), summed in
-//   double;
+//   rescale of the double sums, only when a batch raises it), each vector's
+//   sum added in double;
 // - top-k: the wave holds one sorted list of its 16 best keys spread over
 //   lanes 0..15, and its 16th key tau is a wave-uniform threshold.  A vector
 //   whose largest value is below tau's is skipped; otherwise each key above
 //   tau is inserted, one lane at a time, by a parallel shift.  A key at or
 //   below tau is never among the 16 best of what the wave has seen (16
-//   distinct keys exceed it), so nothing is lost.
-template <int DT>
-__global__ __launch_bounds__(256) void k_tree_expand(ExpandArgs A)
+//   distinct keys exceed it), so nothing is lost.  Before 16 keys are held
+//   the threshold is the 16th largest lane maximum of the batch, so the
+//   first batch inserts a few dozen keys, not every one it holds.
+// NW = 16 serves levels with few rows (the root), NW = 4 the wide ones.
+template <int DT, int NW>
+__global__ __launch_bounds__(NW * 64) void k_tree_expand(ExpandArgs A)
 {
+    constexpr int NT = NW * 64;
     const int b = (int)blockIdx.x / A.F, f = (int)blockIdx.x - b * A.F;
     constexpr int EB = DT == 1 ? 2 : 4;
     constexpr int EPV = 16 / EB;
-    constexpr int U = 4;  // 16-byte loads per lane in flight
+    constexpr int U = SV_TREE_BATCH;  // 16-byte loads per lane in flight
     const char* row = A.rows + ((int64_t)b * A.seq_stride + (int64_t)f * A.row_stride) * EB;
     const float cf = (float)A.c;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    float ref = -INFINITY;  // wave-uniform
-    double s = 0.0;         // this lane's terms against ref
-    int bad = 0;
-    uint64_t L = 0;    // lane j < 16: the wave's j-th best key (0 = none yet)
-    uint64_t tau = 0;  // wave-uniform: the wave's 16th best key
-    float tauv = -INFINITY;
-    auto insert = [&](uint64_t kn) {  // kn wave-uniform, not yet held, above tau
-        const uint64_t prev = __shfl_up(L, 1, 64);
-        const bool keep = L > kn;
-        L = lane < kTopkMax ? (keep ? L : ((lane == 0 || prev > kn) ? kn : prev)) : 0;
-        tau = __shfl(L, kTopkMax - 1, 64);
-        tauv = tau == 0 ? -INFINITY : key_value(tau);
-    };
-    // EPV logits of this lane at tokens t0.. (every lane of the wave calls;
-    // `real` false: padding, which adds nothing and is never a candidate)
-    auto take = [&](const float* x, int t0, bool real) {
-        float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-            bad |= real && ((x[i] != x[i]) || (x[i] == INFINITY));
-            lm = real ? fmaxf(lm, x[i]) : lm;
-        }
-        float wm = lm;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
-        if (wm > ref) {
-            s = (ref == -INFINITY) ? 0.0 : s * exp2((double)(ref - wm) * A.c);
-            ref = wm;
-        }
-        if (real && ref != -INFINITY) {
-            float g = 0.0f;
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f((x[i] - ref) * cf);
-            s += (double)g;
-        }
-        if (__ballot(real && lm >= tauv)) {
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) {
-                const uint64_t k = real ? topk_key(x[i], t0 + i) : 0;
-                uint64_t cm = __ballot(k > tau);
-                while (cm) {
-                    const int l = __ffsll((unsigned long long)cm) - 1;
-                    insert(__shfl(k, l, 64));
-                    cm = __ballot(k > tau) & (~0ull << l << 1);
-                }
-            }
-        }
-    };
+    ExpandWave st;
     const bool vec = ((((uintptr_t)row) & 15u) == 0);
     const int nvec = vec ? A.V / EPV : 0;
-    // whole batches of U vectors per lane, then the rest (each lane's tokens
-    // increase along the row)
-    const int nfull = nvec / (U * 256) * (U * 256);
-    for (int v0 = 0; v0 < nfull; v0 += U * 256) {
-        uint4 w[U];
+    // whole batches of U vectors per lane, then one vector per lane, then
+    // single logits (each lane's tokens increase along the row)
+    const int nb = nvec / (U * NT);
+    const int nfull = nb * (U * NT);
+    // two register sets: batch i + 1 is in flight while batch i is taken
+    // (a set is never copied, which would wait for its loads); a load past
+    // the last batch reads the last batch again and is not taken
+    const uint4* rv = reinterpret_cast<const uint4*>(row) + threadIdx.x;
+    bool real[U];
+    int ta[U], tb[U];
+    uint4 wa[U], wb[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) w[u] = reinterpret_cast<const uint4*>(row)[v0 + u * 256 + threadIdx.x];
+    for (int u = 0; u < U; ++u) real[u] = true;
+    auto load = [&](uint4 (&w)[U], int (&t)[U], int bi) {
+        const int v0 = min(bi, nb - 1) * (U * NT);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float x[EPV];
-            const uint32_t ws[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (DT == 1) {
-                    x[2 * q] = __uint_as_float(ws[q] << 16);
-                    x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
-                } else {
-                    x[q] = __uint_as_float(ws[q]);
-                }
-            }
-            take(x, (v0 + u * 256 + (int)threadIdx.x) * EPV, true);
+            w[u] = rv[v0 + u * NT];
+            t[u] = (v0 + u * NT + (int)threadIdx.x) * EPV;
         }
+    };
+    if (nb > 0) load(wa, ta, 0);
+    for (int bi = 0; bi < nb; bi += 2) {
+        load(wb, tb, bi + 1);
+        expand_batch<DT, U>(st, wa, ta, real, cf, A.c, lane);
+        if (bi + 1 >= nb) break;
+        load(wa, ta, bi + 2);
+        expand_batch<DT, U>(st, wb, tb, real, cf, A.c, lane);
     }
-    for (int v0 = nfull; v0 < nvec; v0 += 256) {
+    for (int v0 = nfull; v0 < nvec; v0 += NT) {
         const int v = v0 + (int)threadIdx.x;
-        float x[EPV];
-        if (v < nvec) {
-            const uint4 w = reinterpret_cast<const uint4*>(row)[v];
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if constexpr (DT == 1) {
-                    x[2 * q] = __uint_as_float(ws[q] << 16);
-                    x[2 * q + 1] = __uint_as_float(ws[q] & 0xFFFF0000u);
-                } else {
-                    x[q] = __uint_as_float(ws[q]);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) x[i] = -INFINITY;
-        }
-        take(x, v * EPV, v < nvec);
+        constexpr uint32_t kNegInf = DT == 1 ? 0xFF80FF80u : 0xFF800000u;  // -inf logits
+        uint4 w[1] = {make_uint4(kNegInf, kNegInf, kNegInf, kNegInf)};
+        if (v < nvec) w[0] = reinterpret_cast<const uint4*>(row)[v];
+        const int t0[1] = {v * EPV};
+        const bool real[1] = {v < nvec};
+        expand_batch<DT, 1>(st, w, t0, real, cf, A.c, lane);
     }
-    for (int t0 = nvec * EPV; t0 < A.V; t0 += 256) {
+    for (int t0 = nvec * EPV; t0 < A.V; t0 += NT) {
         // one logit per lane (unaligned rows, or the tail past the vectors);
         // lanes past V hold -inf, add nothing and offer no key
         const int t = t0 + (int)threadIdx.x;
         const float x0 = t < A.V ? logit_of<DT>(row, t) : -INFINITY;
-        bad |= (t < A.V) && ((x0 != x0) || (x0 == INFINITY));
-        float wm = x0;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) wm = fmaxf(wm, __shfl_xor(wm, off, 64));
-        if (wm > ref) {
-            s = (ref == -INFINITY) ? 0.0 : s * exp2((double)(ref - wm) * A.c);
-            ref = wm;
+        st.bad |= __ballot(__builtin_amdgcn_classf(x0, kClassNanPinf));
+        const float wm = wave_max_f(x0);
+        if (wm > st.ref) {
+            st.s = (st.ref == -INFINITY) ? 0.0 : st.s * exp2((double)(st.ref - wm) * A.c);
+            st.ref = wm;
         }
-        if (t < A.V && ref != -INFINITY) s += (double)__builtin_amdgcn_exp2f((x0 - ref) * cf);
-        const uint64_t k = t < A.V ? topk_key(x0, t) : 0;
-        uint64_t cm = __ballot(k > tau);
-        while (cm) {
-            const int l = __ffsll((unsigned long long)cm) - 1;
-            insert(__shfl(k, l, 64));
-            cm = __ballot(k > tau) & (~0ull << l << 1);
-        }
+        if (t < A.V && st.ref != -INFINITY) st.s += (double)__builtin_amdgcn_exp2f((x0 - st.ref) * cf);
+        insert_keys(st, t < A.V ? topk_key(x0, t) : 0, lane);
     }
     // the wave's sum (every lane shares ref)
+    double s = st.s;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    __shared__ uint64_t s_keys[4 * kTopkMax];
-    __shared__ float s_m[4];
-    __shared__ double s_s[4];
-    __shared__ int s_bad;
-    if (threadIdx.x == 0) s_bad = 0;
-    if (lane < kTopkMax) s_keys[wave * kTopkMax + lane] = L;
+    __shared__ uint64_t s_keys[NW * kTopkMax];
+    __shared__ float s_m[NW];
+    __shared__ double s_s[NW];
+    if (lane < kTopkMax) s_keys[wave * kTopkMax + lane] = st.L;
     if (lane == 0) {
-        s_m[wave] = ref;
+        s_m[wave] = st.ref;
         s_s[wave] = s;
     }
-    __syncthreads();
-    if (bad) s_bad = 1;
-    __syncthreads();
-    if (wave != 0) return;
+    const int bad = __syncthreads_or(st.bad != 0);
     // the row's log-sum-exp and the block's top-k by rank among the waves' lists
+    if (threadIdx.x >= NW * kTopkMax) return;
     double S = 0.0;
     float M = -INFINITY;
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w]);
-    for (int w = 0; w < 4; ++w)
-        if (s_m[w] != -INFINITY) S += s_m[w] == M ? s_s[w] : s_s[w] * exp2((double)(s_m[w] - M) * A.c);
-    const uint64_t mine = s_keys[lane];
+    for (int q = 0; q < NW; ++q) M = fmaxf(M, s_m[q]);
+    for (int q = 0; q < NW; ++q)
+        if (s_m[q] != -INFINITY) S += s_m[q] == M ? s_s[q] : s_s[q] * exp2((double)(s_m[q] - M) * A.c);
+    const uint64_t mine = s_keys[threadIdx.x];
     int rank = 0;
-    for (int j = 0; j < 4 * kTopkMax; ++j) rank += s_keys[j] > mine;
+#pragma unroll 8
+    for (int j = 0; j < NW * kTopkMax; ++j) rank += s_keys[j] > mine;
     if (rank < A.topk) {
         const double lse = (double)M * A.invTd + log(S);
-        const bool fail = s_bad || M == -INFINITY || mine == 0;
+        const bool fail = bad || M == -INFINITY || mine == 0;
         const int64_t at = (int64_t)b * A.n_max + A.offset + (int64_t)f * A.topk + rank;
         const double fs = A.frontier_score ? A.frontier_score[(int64_t)b * A.F + f] : 0.0;
         A.cand_token[at] = fail ? -1 : key_token(mine);
@@ -468,10 +547,16 @@ extern "C" int tree_expand(const void* frontier_logits, int64_t seq_stride, int6
     A.cand_parent = cand_parent;
     A.cand_level = cand_level;
     A.cand_score = cand_score;
-    if (dtype == SV_BF16)
-        hipLaunchKernelGGL(sv::k_tree_expand<1>, dim3((unsigned)(B * F)), dim3(256), 0, stream, A);
-    else
-        hipLaunchKernelGGL(sv::k_tree_expand<0>, dim3((unsigned)(B * F)), dim3(256), 0, stream, A);
+    // few rows (the root level): 16 waves per row, else 4
+    const bool wide = (int64_t)B * F < sv::kExpandFewRows;
+    const dim3 grid((unsigned)(B * F));
+    if (dtype == SV_BF16) {
+        if (wide) hipLaunchKernelGGL((sv::k_tree_expand<1, 16>), grid, dim3(1024), 0, stream, A);
+        else hipLaunchKernelGGL((sv::k_tree_expand<1, 4>), grid, dim3(256), 0, stream, A);
+    } else {
+        if (wide) hipLaunchKernelGGL((sv::k_tree_expand<0, 16>), grid, dim3(1024), 0, stream, A);
+        else hipLaunchKernelGGL((sv::k_tree_expand<0, 4>), grid, dim3(256), 0, stream, A);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
 
