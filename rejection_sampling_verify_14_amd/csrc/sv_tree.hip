@@ -407,94 +407,120 @@ __global__ __launch_bounds__(256) void k_tree_select(const double* __restrict__ 
     }
 }
 
+// An order-preserving 64-bit image of a double (NaN excluded): larger
+// values give larger keys, -0 and +0 the same key.
+__device__ __forceinline__ uint64_t double_key(double v)
+{
+    const uint64_t u = (uint64_t)__double_as_longlong(v + 0.0);  // -0 + 0 = +0
+    return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+constexpr int kFinalizeBlock = 1024;
+
 // Block b: the kept set of sequence b -- the `budget` best candidates by
 // (score desc, id asc) -- numbered 1..budget by (level asc, score desc, id
 // asc), and the flattened tree: parents (node 0: -1), tokens (0), depth (0),
 // log-scores (0).  A NaN score, or a kept candidate whose parent is not kept
 // (never for tables the expand step wrote), fails the sequence: -1 in every
 // slot.
-__global__ __launch_bounds__(256) void k_tree_finalize(const int32_t* __restrict__ cand_token,
-                                                       const int32_t* __restrict__ cand_parent,
-                                                       const int32_t* __restrict__ cand_level,
-                                                       const double* __restrict__ cand_score, int n_max, int n,
-                                                       int budget, int32_t* __restrict__ out_parents,
-                                                       int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_depth,
-                                                       double* __restrict__ out_score)
+//
+// Two bitonic sorts in LDS, one compare-exchange per thread and stage: the
+// n candidates (padded to a power of two) by (score desc, id asc), whose
+// first `budget` are the kept set; then the kept ranks by (level asc, rank
+// asc), whose order is the node numbering.
+__global__ __launch_bounds__(kFinalizeBlock) void k_tree_finalize(
+    const int32_t* __restrict__ cand_token, const int32_t* __restrict__ cand_parent,
+    const int32_t* __restrict__ cand_level, const double* __restrict__ cand_score, int n_max, int n, int budget,
+    int32_t* __restrict__ out_parents, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_depth,
+    double* __restrict__ out_score)
 {
-    __shared__ double s_sc[kTreeMaxCand];
-    __shared__ int s_lev[kTreeMaxCand];
-    __shared__ int s_node[kTreeMaxCand];
-    __shared__ int s_pos[kTreeMaxCand];
-    const int b = blockIdx.x;
+    __shared__ uint64_t s_key[kTreeMaxCand];
+    __shared__ int s_id[kTreeMaxCand];
+    __shared__ int s_node[kTreeMaxCand];  // candidate id -> node number (0: not kept)
+    const int b = blockIdx.x, tid = threadIdx.x;
     const int64_t base = (int64_t)b * n_max;
     const int nn = budget + 1;
+    int P = 1;
+    while (P < n) P <<= 1;
     int bad = 0;
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const double v = cand_score[base + i];
-        bad |= v != v;
-        s_sc[i] = order_score(v);
-        s_lev[i] = cand_level[base + i];
-        s_node[i] = -1;
+    for (int i = tid; i < P; i += kFinalizeBlock) {
+        uint64_t key = 0;  // padding: below every score's key (-inf's is 0x000F...)
+        if (i < n) {
+            const double v = cand_score[base + i];
+            bad |= v != v;
+            key = double_key(order_score(v));
+            s_node[i] = 0;
+        }
+        s_key[i] = key;
+        s_id[i] = i;  // padding ids follow every real one
     }
     bad = __syncthreads_or(bad);
-    // kept: rank by (score desc, id asc) below budget
-    for (int i = threadIdx.x; i < n; i += 256) {
-        const double v = s_sc[i];
-        int rank = 0;
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {  // branch-free: bitwise, not short-circuit
-            const double sj = s_sc[j];
-            rank += (int)(sj > v) | ((int)(sj == v) & (int)(j < i));
+    // sort 1: descending by (key, -id)
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = tid; t < (P >> 1); t += kFinalizeBlock) {
+                const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
+                const uint64_t ki = s_key[i], kl = s_key[l];
+                const int ii = s_id[i], il = s_id[l];
+                const bool l_first = (kl > ki) | ((kl == ki) & (il < ii));
+                if (l_first == ((i & k) == 0)) {
+                    s_key[i] = kl;
+                    s_key[l] = ki;
+                    s_id[i] = il;
+                    s_id[l] = ii;
+                }
+            }
+            __syncthreads();
         }
-        if (rank < budget) s_node[i] = 0;
     }
+    // sort 2: the kept ranks r < budget, ascending by (level, r)
+    int P2 = 1;
+    while (P2 < budget) P2 <<= 1;
+    for (int r = tid; r < P2; r += kFinalizeBlock)
+        s_key[r] = r < budget ? ((uint64_t)((uint32_t)cand_level[base + s_id[r]] ^ 0x80000000u) << 32) | (uint32_t)r
+                              : ~0ull;
     __syncthreads();
-    // node number of a kept candidate: 1 + the kept ones before it by
-    // (level asc, score desc, id asc)
-    for (int i = threadIdx.x; i < n; i += 256) {
-        s_pos[i] = -1;
-        if (s_node[i] < 0) continue;
-        const double v = s_sc[i];
-        const int lv = s_lev[i];
-        int pos = 0;
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {  // branch-free: bitwise, not short-circuit
-            const double sj = s_sc[j];
-            const int lj = s_lev[j];
-            const int before = (int)(sj > v) | ((int)(sj == v) & (int)(j < i));
-            pos += (int)(s_node[j] >= 0) & ((int)(lj < lv) | ((int)(lj == lv) & before));
+    for (int k = 2; k <= P2; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int t = tid; t < (P2 >> 1); t += kFinalizeBlock) {
+                const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
+                const uint64_t ki = s_key[i], kl = s_key[l];
+                if ((kl < ki) == ((i & k) == 0)) {
+                    s_key[i] = kl;
+                    s_key[l] = ki;
+                }
+            }
+            __syncthreads();
         }
-        s_pos[i] = pos + 1;
     }
+    for (int q = tid; q < budget; q += kFinalizeBlock) s_node[s_id[(uint32_t)s_key[q]]] = q + 1;
     __syncthreads();
-    for (int i = threadIdx.x; i < n; i += 256) s_node[i] = s_pos[i];
-    __syncthreads();
-    int32_t* P = out_parents + (int64_t)b * nn;
+    int32_t* Po = out_parents + (int64_t)b * nn;
     int32_t* K = out_tokens + (int64_t)b * nn;
     int32_t* D = out_depth + (int64_t)b * nn;
     double* S = out_score + (int64_t)b * nn;
-    for (int i = threadIdx.x; i < n && !bad; i += 256) {
-        if (s_node[i] <= 0) continue;
-        const int node = s_node[i];  // 1..budget
+    for (int q = tid; q < budget && !bad; q += kFinalizeBlock) {
+        const int i = s_id[(uint32_t)s_key[q]];
+        const int node = q + 1;
         const int par = cand_parent[base + i];
         int pnode = 0;
         if (par >= 0) pnode = (par < i && s_node[par] > 0) ? s_node[par] : -1;
-        P[node] = pnode;
+        Po[node] = pnode;
         K[node] = cand_token[base + i];
-        D[node] = s_lev[i];
+        D[node] = cand_level[base + i];
         S[node] = cand_score[base + i];
         if (pnode < 0) bad = 1;
     }
     bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0 && !bad) {
-        P[0] = -1;
+    if (tid == 0 && !bad) {
+        Po[0] = -1;
         K[0] = 0;
         D[0] = 0;
         S[0] = 0.0;
     }
     if (bad)
-        for (int i = threadIdx.x; i < nn; i += 256) {
-            P[i] = K[i] = D[i] = -1;
+        for (int i = tid; i < nn; i += kFinalizeBlock) {
+            Po[i] = K[i] = D[i] = -1;
             S[i] = 0.0;
         }
 }
@@ -582,7 +608,7 @@ extern "C" int tree_finalize(const int32_t* cand_token, const int32_t* cand_pare
     if (!cand_token || !cand_parent || !cand_level || !cand_score || !out_parents || !out_tokens || !out_depth ||
         !out_score)
         return SV_EINVAL;
-    hipLaunchKernelGGL(sv::k_tree_finalize, dim3((unsigned)B), dim3(256), 0, stream, cand_token, cand_parent,
+    hipLaunchKernelGGL(sv::k_tree_finalize, dim3((unsigned)B), dim3(sv::kFinalizeBlock), 0, stream, cand_token, cand_parent,
                        cand_level, cand_score, n_max, n, budget, out_parents, out_tokens, out_depth, out_score);
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }
