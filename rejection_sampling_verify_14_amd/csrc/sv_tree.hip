@@ -123,6 +123,14 @@ __device__ __forceinline__ float logit_of(const char* row, int64_t t)
     else return reinterpret_cast<const float*>(row)[t];
 }
 
+// 16-byte load with the nontemporal hint: a draft row is read once.
+__device__ __forceinline__ uint4 load_nt16(const uint4* p)
+{
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // Element i (0 .. 16/es - 1) of a 16-byte vector of logits.
 template <int DT>
 __device__ __forceinline__ float vec_elem(const uint4& w, int i)
@@ -156,13 +164,15 @@ __device__ __forceinline__ float wave_16th_largest(float v, int lane)
     return __shfl(v, kTopkMax - 1, 64);
 }
 
-constexpr int kClassNanPinf = 0x203;  // class-test mask: signalling NaN, quiet NaN, +inf
-
-// One wave's running state over its share of a row.
+// One wave's running state over its share of a row.  A term is
+// 2^(fma(x, cf, -p)) with p = RN(ref * cf): 2^((x - ref) cf) times 2^e,
+// e = ref * cf - p (exact in fp32), a factor common to every term that the
+// sum sheds when ref moves and at the end.
 struct ExpandWave {
     float ref = -INFINITY;  // wave-uniform reference (the wave's running maximum)
-    double s = 0.0;         // this lane's exp terms against ref
-    uint64_t bad = 0;       // wave-uniform: lanes that met NaN or +inf
+    float p = 0.0f, e = 0.0f;
+    double s = 0.0;         // this lane's exp terms against ref, times 2^e
+    uint64_t bad = 0;       // wave-uniform: lanes whose sum met NaN or +inf
     uint64_t L = 0;         // lane j < 16: the wave's j-th best key (0 = none yet)
     uint64_t tau = 0;       // wave-uniform: the wave's 16th best key
     float tauv = -INFINITY; // its value
@@ -180,34 +190,47 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
 }
 
 // Lane j of each 16-lane row receives lane j - 1's value (DPP row_shr:1);
-// lane 0 of a row receives 0.
+// lane 0 of a row receives ~0, above every key.
 __device__ __forceinline__ uint64_t row_shift_up_u64(uint64_t v)
 {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x111, 0xF, 0xF, false);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x111, 0xF, 0xF, false);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)v, 0x111, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)(uint32_t)(v >> 32), 0x111, 0xF, 0xF, false);
     return ((uint64_t)hi << 32) | lo;
 }
 
-__device__ __forceinline__ void insert_keys(ExpandWave& st, uint64_t k, int lane)
+__device__ __forceinline__ void insert_keys(ExpandWave& st, uint64_t k)
 {
     uint64_t cm = __ballot(k > st.tau);
     while (cm) {
         const int l = __ffsll((unsigned long long)cm) - 1;
         const uint64_t kn = readlane_u64(k, l);  // wave-uniform, not yet held, above tau
-        const uint64_t prev = row_shift_up_u64(st.L);  // the list lives in lanes 0..15
-        const bool keep = st.L > kn;
-        st.L = lane < kTopkMax ? (keep ? st.L : ((lane == 0 || prev > kn) ? kn : prev)) : 0;
+        // the list lives in lanes 0..15 (the other lanes hold junk)
+        const uint64_t prev = row_shift_up_u64(st.L);
+        st.L = st.L > kn ? st.L : (prev > kn ? kn : prev);
         st.tau = readlane_u64(st.L, kTopkMax - 1);
         st.tauv = st.tau == 0 ? -INFINITY : key_value(st.tau);
         cm = __ballot(k > st.tau) & (~0ull << l << 1);
     }
 }
 
+// Raise the wave's reference to wm (> ref): rescale the sum to the new
+// reference and offset.
+__device__ __forceinline__ void raise_ref(ExpandWave& st, float wm, float cf)
+{
+    const float p = wm * cf;
+    const float e = __builtin_fmaf(wm, cf, -p);
+    st.s = (st.ref == -INFINITY) ? st.s * 0.0  // 0, or NaN kept
+                                 : st.s * exp2(((double)st.ref - (double)wm) * (double)cf + (double)(e - st.e));
+    st.ref = wm;
+    st.p = p;
+    st.e = e;
+}
+
 // A batch of U 16-byte vectors per lane (vector u of this lane starts at
 // token t0[u]; real[u] false: padding that adds nothing and offers no key).
 template <int DT, int U>
 __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U], const int (&t0)[U],
-                                             const bool (&real)[U], float cf, double c, int lane)
+                                             const bool (&real)[U], float cf, int lane)
 {
     constexpr int EPV = DT == 1 ? 8 : 4;
     float vm[U];
@@ -217,26 +240,21 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
         vm[u] = -INFINITY;
 #pragma unroll
         for (int i = 0; i < EPV; ++i) {
-            const float x = vec_elem<DT>(w[u], i);
-            st.bad |= __ballot(__builtin_amdgcn_classf(x, kClassNanPinf));  // padding is -inf
-            vm[u] = fmaxf(vm[u], x);
+            vm[u] = fmaxf(vm[u], vec_elem<DT>(w[u], i));
         }
         vm[u] = real[u] ? vm[u] : -INFINITY;
         lm = fmaxf(lm, vm[u]);
     }
     const float wm = wave_max_f(lm);
-    if (wm > st.ref) {
-        st.s = (st.ref == -INFINITY) ? 0.0 : st.s * exp2((double)(st.ref - wm) * c);
-        st.ref = wm;
-    }
-    if (st.ref != -INFINITY) {
+    if (wm > st.ref) raise_ref(st, wm, cf);
+    // NaN and +inf show as a NaN sum: a NaN term, or inf - inf.  While
+    // ref is -inf (p = 0) every term is 0 or NaN.
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float g = 0.0f;
+    for (int u = 0; u < U; ++u) {
+        float g = 0.0f;
 #pragma unroll
-            for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f((vec_elem<DT>(w[u], i) - st.ref) * cf);
-            st.s += real[u] ? (double)g : 0.0;
-        }
+        for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(w[u], i), cf, -st.p));
+        st.s += real[u] ? (double)g : 0.0;
     }
     // Until the wave holds 16 keys, 16 lanes' batch maxima bound the 16th
     // best from below: 16 distinct keys reach that bound, so a value under
@@ -252,7 +270,7 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
             // thr only rises while keys go in, so the test against its
             // value at the batch's start passes every key that may insert
             const float x = vec_elem<DT>(w[u], i);
-            if (__ballot(real[u] && x >= thr)) insert_keys(st, (real[u] && x >= st.theta) ? topk_key(x, t0[u] + i) : 0, lane);
+            if (__ballot(real[u] && x >= thr)) insert_keys(st, (real[u] && x >= st.theta) ? topk_key(x, t0[u] + i) : 0);
         }
     }
 }
@@ -277,7 +295,7 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
 //   first batch inserts a few dozen keys, not every one it holds.
 // NW = 16 serves levels with few rows (the root), NW = 4 the wide ones.
 template <int DT, int NW>
-__global__ __launch_bounds__(NW * 64) void k_tree_expand(ExpandArgs A)
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 1) void k_tree_expand(ExpandArgs A)
 {
     constexpr int NT = NW * 64;
     const int b = (int)blockIdx.x / A.F, f = (int)blockIdx.x - b * A.F;
@@ -307,17 +325,17 @@ __global__ __launch_bounds__(NW * 64) void k_tree_expand(ExpandArgs A)
         const int v0 = min(bi, nb - 1) * (U * NT);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            w[u] = rv[v0 + u * NT];
+            w[u] = load_nt16(rv + v0 + u * NT);
             t[u] = (v0 + u * NT + (int)threadIdx.x) * EPV;
         }
     };
     if (nb > 0) load(wa, ta, 0);
     for (int bi = 0; bi < nb; bi += 2) {
         load(wb, tb, bi + 1);
-        expand_batch<DT, U>(st, wa, ta, real, cf, A.c, lane);
+        expand_batch<DT, U>(st, wa, ta, real, cf, lane);
         if (bi + 1 >= nb) break;
         load(wa, ta, bi + 2);
-        expand_batch<DT, U>(st, wb, tb, real, cf, A.c, lane);
+        expand_batch<DT, U>(st, wb, tb, real, cf, lane);
     }
     for (int v0 = nfull; v0 < nvec; v0 += NT) {
         const int v = v0 + (int)threadIdx.x;
@@ -326,24 +344,21 @@ __global__ __launch_bounds__(NW * 64) void k_tree_expand(ExpandArgs A)
         if (v < nvec) w[0] = reinterpret_cast<const uint4*>(row)[v];
         const int t0[1] = {v * EPV};
         const bool real[1] = {v < nvec};
-        expand_batch<DT, 1>(st, w, t0, real, cf, A.c, lane);
+        expand_batch<DT, 1>(st, w, t0, real, cf, lane);
     }
     for (int t0 = nvec * EPV; t0 < A.V; t0 += NT) {
         // one logit per lane (unaligned rows, or the tail past the vectors);
         // lanes past V hold -inf, add nothing and offer no key
         const int t = t0 + (int)threadIdx.x;
         const float x0 = t < A.V ? logit_of<DT>(row, t) : -INFINITY;
-        st.bad |= __ballot(__builtin_amdgcn_classf(x0, kClassNanPinf));
         const float wm = wave_max_f(x0);
-        if (wm > st.ref) {
-            st.s = (st.ref == -INFINITY) ? 0.0 : st.s * exp2((double)(st.ref - wm) * A.c);
-            st.ref = wm;
-        }
-        if (t < A.V && st.ref != -INFINITY) st.s += (double)__builtin_amdgcn_exp2f((x0 - st.ref) * cf);
-        insert_keys(st, t < A.V ? topk_key(x0, t) : 0, lane);
+        if (wm > st.ref) raise_ref(st, wm, cf);
+        st.s += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x0, cf, -st.p));  // 0 past V
+        insert_keys(st, t < A.V ? topk_key(x0, t) : 0);
     }
-    // the wave's sum (every lane shares ref)
-    double s = st.s;
+    // the wave's sum against ref (every lane shares ref, p and e)
+    st.bad |= __ballot(st.s != st.s);
+    double s = st.ref == -INFINITY ? 0.0 : st.s * exp2(-(double)st.e);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     __shared__ uint64_t s_keys[NW * kTopkMax];
@@ -361,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void k_tree_expand(ExpandArgs A)
     float M = -INFINITY;
     for (int q = 0; q < NW; ++q) M = fmaxf(M, s_m[q]);
     for (int q = 0; q < NW; ++q)
-        if (s_m[q] != -INFINITY) S += s_m[q] == M ? s_s[q] : s_s[q] * exp2((double)(s_m[q] - M) * A.c);
+        if (s_m[q] != -INFINITY) S += s_m[q] == M ? s_s[q] : s_s[q] * exp2(((double)s_m[q] - (double)M) * (double)cf);
     const uint64_t mine = s_keys[threadIdx.x];
     int rank = 0;
 #pragma unroll 8

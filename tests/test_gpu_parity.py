@@ -434,8 +434,19 @@ def test_tree_build_parity():
         _tree_build_case(f"d{depth}_k{topk}", rows, depth, topk, budget, 1.0)
     rows = (torch.randn((4, 1 + 3 * 2, 500), generator=g, device="cuda") * 3).to(torch.bfloat16)
     rows[2, 4, 100] = float("nan")
+    rows[0, 0, 7] = float("inf")
     out = _tree_build_case("nan_row", rows, 3, 3, 10, 1.0)
-    assert (out["parents"][2] == -1).all().item()
+    assert (out["parents"][2] == -1).all().item() and (out["parents"][0] == -1).all().item()
+    # a NaN inside a stretch of -inf that one wave reads alone (its running
+    # maximum never leaves -inf), the rest of the row finite elsewhere; row
+    # lengths that end in the one-vector loop and in whole batches
+    for V in (4096, 16384):
+        rows = (torch.randn((3, 1 + 2 * 1, V), generator=g, device="cuda") * 3).to(torch.bfloat16)
+        rows[1, 1, :] = float("-inf")
+        rows[1, 1, :8] = 1.0
+        rows[1, 1, 200 * 8 + 3] = float("nan")  # vector 200: lane 200 of the block, its fourth wave
+        out = _tree_build_case(f"nan_in_neg_inf_V{V}", rows, 2, 2, 4, 1.0)
+        assert (out["parents"][1] == -1).all().item() and (out["parents"][0, 1:] >= 0).all().item()
     log("[done] tree_build parity")
 
 
