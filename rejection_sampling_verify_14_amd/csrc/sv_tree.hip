@@ -148,9 +148,9 @@ __device__ __forceinline__ float wave_max_f(float v)
     return v;
 }
 
-// The 16th largest of the 64 lanes' values, in every lane: a bitonic sort
-// across the wave into descending lane order.
-__device__ __forceinline__ float wave_16th_largest(float v, int lane)
+// The k-th largest (k <= 64, wave-uniform) of the 64 lanes' values, in
+// every lane: a bitonic sort across the wave into descending lane order.
+__device__ __forceinline__ float wave_kth_largest(float v, int lane, int k)
 {
 #pragma unroll
     for (int k = 2; k <= 64; k <<= 1) {
@@ -161,7 +161,7 @@ __device__ __forceinline__ float wave_16th_largest(float v, int lane)
             v = (lower == desc) ? fmaxf(v, o) : fminf(v, o);
         }
     }
-    return __shfl(v, kTopkMax - 1, 64);
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), k - 1));
 }
 
 // One wave's running state over its share of a row.  A term is
@@ -173,10 +173,11 @@ struct ExpandWave {
     float p = 0.0f, e = 0.0f;
     double s = 0.0;         // this lane's exp terms against ref, times 2^e
     uint64_t bad = 0;       // wave-uniform: lanes whose sum met NaN or +inf
-    uint64_t L = 0;         // lane j < 16: the wave's j-th best key (0 = none yet)
-    uint64_t tau = 0;       // wave-uniform: the wave's 16th best key
+    uint64_t L = 0;         // lane j < K: the wave's j-th best key (0 = none yet)
+    uint64_t tau = 0;       // wave-uniform: the wave's K-th best key
     float tauv = -INFINITY; // its value
-    float theta = -INFINITY;  // wave-uniform: a value at or below the 16th best seen
+    float theta = -INFINITY;  // wave-uniform: a value at or below the K-th best seen
+    int K;                  // the list's length: the k of the top-k
 };
 
 // Insert every key k of the wave above tau into the sorted list, one lane
@@ -207,7 +208,7 @@ __device__ __forceinline__ void insert_keys(ExpandWave& st, uint64_t k)
         // the list lives in lanes 0..15 (the other lanes hold junk)
         const uint64_t prev = row_shift_up_u64(st.L);
         st.L = st.L > kn ? st.L : (prev > kn ? kn : prev);
-        st.tau = readlane_u64(st.L, kTopkMax - 1);
+        st.tau = readlane_u64(st.L, st.K - 1);
         st.tauv = st.tau == 0 ? -INFINITY : key_value(st.tau);
         cm = __ballot(k > st.tau) & (~0ull << l << 1);
     }
@@ -228,9 +229,9 @@ __device__ __forceinline__ void raise_ref(ExpandWave& st, float wm, float cf)
 
 // A batch of U 16-byte vectors per lane (vector u of this lane starts at
 // token t0[u]; real[u] false: padding that adds nothing and offers no key).
-template <int DT, int U>
+template <int DT, int U, int NW>
 __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U], const int (&t0)[U],
-                                             const bool (&real)[U], float cf, int lane)
+                                             const bool (&real)[U], float cf, int lane, float* s_thr, int wave)
 {
     constexpr int EPV = DT == 1 ? 8 : 4;
     float vm[U];
@@ -256,11 +257,14 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
         for (int i = 0; i < EPV; ++i) g += __builtin_amdgcn_exp2f(__builtin_fmaf(vec_elem<DT>(w[u], i), cf, -st.p));
         st.s += real[u] ? (double)g : 0.0;
     }
-    // Until the wave holds 16 keys, 16 lanes' batch maxima bound the 16th
-    // best from below: 16 distinct keys reach that bound, so a value under
-    // it can never be among the 16 best.
-    if (st.tau == 0) st.theta = fmaxf(st.theta, wave_16th_largest(lm, lane));
-    const float thr = fmaxf(st.tauv, st.theta);
+    // At the start (no K keys held, no bound yet), K lanes' batch maxima
+    // bound the K-th best from below: K distinct keys reach that bound, so a
+    // value under it can never be among the K best.  (A wave whose keys the
+    // shared threshold keeps out may never hold K keys; it seeds once.)
+    if (st.tau == 0 && st.theta == -INFINITY) st.theta = wave_kth_largest(lm, lane, st.K);
+    float thr = fmaxf(st.tauv, st.theta);
+#pragma unroll
+    for (int q = 0; q < NW; ++q) thr = fmaxf(thr, __hip_atomic_load(s_thr + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
     if (!__ballot(lm >= thr)) return;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -270,9 +274,12 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
             // thr only rises while keys go in, so the test against its
             // value at the batch's start passes every key that may insert
             const float x = vec_elem<DT>(w[u], i);
-            if (__ballot(real[u] && x >= thr)) insert_keys(st, (real[u] && x >= st.theta) ? topk_key(x, t0[u] + i) : 0);
+            if (__ballot(real[u] && x >= thr)) insert_keys(st, (real[u] && x >= thr) ? topk_key(x, t0[u] + i) : 0);
         }
     }
+    // publish this wave's threshold (other waves read it without a barrier:
+    // any value it has held is a valid bound)
+    if (lane == 0) __hip_atomic_store(s_thr + wave, fmaxf(st.tauv, st.theta), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Block (b, f) of NW waves: one pass over frontier row f of sequence b: its
@@ -285,14 +292,19 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
 //   reference that is the wave's running maximum (it moves, with an fp64
 //   rescale of the double sums, only when a batch raises it), each vector's
 //   sum added in double;
-// - top-k: the wave holds one sorted list of its 16 best keys spread over
-//   lanes 0..15, and its 16th key tau is a wave-uniform threshold.  A vector
-//   whose largest value is below tau's is skipped; otherwise each key above
-//   tau is inserted, one lane at a time, by a parallel shift.  A key at or
-//   below tau is never among the 16 best of what the wave has seen (16
-//   distinct keys exceed it), so nothing is lost.  Before 16 keys are held
-//   the threshold is the 16th largest lane maximum of the batch, so the
-//   first batch inserts a few dozen keys, not every one it holds.
+// - top-k: the wave holds one sorted list of its K = k best keys spread
+//   over lanes 0..K-1, and its K-th key tau is a wave-uniform threshold.  A
+//   vector whose largest value is below tau's is skipped; otherwise each key
+//   above tau is inserted, one lane at a time, by a parallel shift.  A key at
+//   or below tau is never among the K best of what the wave has seen (K
+//   distinct keys exceed it), so nothing is lost.  Before K keys are held
+//   the threshold is the K-th largest lane maximum of the batch, so the
+//   first batch inserts a few dozen keys, not every one it holds.  (Lanes
+//   K..15 keep keys shifted out of the list: real logits of the row, so the
+//   block's merge may count them.)  After each batch a wave publishes its
+//   threshold in LDS, and every wave filters by the largest published one:
+//   a logit below another wave's threshold has K distinct keys of that
+//   wave above it, so it is not among the block's K best either.
 // NW = 16 serves levels with few rows (the root), NW = 4 the wide ones.
 template <int DT, int NW>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 1) void k_tree_expand(ExpandArgs A)
@@ -306,6 +318,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 1) void k_tree_expand(Expand
     const float cf = (float)A.c;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     ExpandWave st;
+    st.K = A.topk;
+    __shared__ float s_thr[NW];  // each wave's published filter threshold
+    if (threadIdx.x < NW) s_thr[threadIdx.x] = -INFINITY;
+    __syncthreads();
     const bool vec = ((((uintptr_t)row) & 15u) == 0);
     const int nvec = vec ? A.V / EPV : 0;
     // whole batches of U vectors per lane, then one vector per lane, then
@@ -332,10 +348,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 1) void k_tree_expand(Expand
     if (nb > 0) load(wa, ta, 0);
     for (int bi = 0; bi < nb; bi += 2) {
         load(wb, tb, bi + 1);
-        expand_batch<DT, U>(st, wa, ta, real, cf, lane);
+        expand_batch<DT, U, NW>(st, wa, ta, real, cf, lane, s_thr, wave);
         if (bi + 1 >= nb) break;
         load(wa, ta, bi + 2);
-        expand_batch<DT, U>(st, wb, tb, real, cf, lane);
+        expand_batch<DT, U, NW>(st, wb, tb, real, cf, lane, s_thr, wave);
     }
     for (int v0 = nfull; v0 < nvec; v0 += NT) {
         const int v = v0 + (int)threadIdx.x;
@@ -344,7 +360,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 4 : 1) void k_tree_expand(Expand
         if (v < nvec) w[0] = reinterpret_cast<const uint4*>(row)[v];
         const int t0[1] = {v * EPV};
         const bool real[1] = {v < nvec};
-        expand_batch<DT, 1>(st, w, t0, real, cf, lane);
+        expand_batch<DT, 1, NW>(st, w, t0, real, cf, lane, s_thr, wave);
     }
     for (int t0 = nvec * EPV; t0 < A.V; t0 += NT) {
         // one logit per lane (unaligned rows, or the tail past the vectors);
