@@ -74,7 +74,7 @@ constexpr int kTopkMax = 16;
 constexpr int kTreeMaxCand = 2048;
 constexpr int kExpandFewRows = 512;  // below this many rows an expand block has 16 waves
 #ifndef SV_TREE_BATCH
-#define SV_TREE_BATCH 4  // 16-byte loads per lane per batch of the expand kernel
+#define SV_TREE_BATCH 2  // 16-byte loads per lane per batch (2: 80 VGPRs, 5 waves per SIMD)
 #endif
 
 // A 64-bit key ordering (logit desc, token asc): the logit's bits made
