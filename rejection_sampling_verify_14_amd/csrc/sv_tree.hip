@@ -169,7 +169,8 @@ __device__ __forceinline__ float wave_kth_largest(float v, int lane, int k)
 // e = ref * cf - p (exact in fp32), a factor common to every term that the
 // sum sheds when ref moves and at the end.
 struct ExpandWave {
-    float ref = -INFINITY;  // wave-uniform reference (the wave's running maximum)
+    float ref = -INFINITY;  // wave-uniform reference: the wave's maximum when last moved
+    float lim = -INFINITY;  // ref moves once a logit passes lim (= ref + 2 / cf)
     float p = 0.0f, e = 0.0f;
     double s = 0.0;         // this lane's exp terms against ref, times 2^e
     uint64_t bad = 0;       // wave-uniform: lanes whose sum met NaN or +inf
@@ -223,6 +224,7 @@ __device__ __forceinline__ void raise_ref(ExpandWave& st, float wm, float cf)
     st.s = (st.ref == -INFINITY) ? st.s * 0.0  // 0, or NaN kept
                                  : st.s * exp2(((double)st.ref - (double)wm) * (double)cf + (double)(e - st.e));
     st.ref = wm;
+    st.lim = wm + 2.0f / cf;
     st.p = p;
     st.e = e;
 }
@@ -246,8 +248,9 @@ __device__ __forceinline__ void expand_batch(ExpandWave& st, const uint4 (&w)[U]
         vm[u] = real[u] ? vm[u] : -INFINITY;
         lm = fmaxf(lm, vm[u]);
     }
-    const float wm = wave_max_f(lm);
-    if (wm > st.ref) raise_ref(st, wm, cf);
+    // ref lags the maximum by less than 2 in the exponent (terms below 4,
+    // so the fma's rounding stays near that of a term at 1)
+    if (__ballot(lm > st.lim)) raise_ref(st, wave_max_f(lm), cf);
     // NaN and +inf show as a NaN sum: a NaN term, or inf - inf.  While
     // ref is -inf (p = 0) every term is 0 or NaN.
 #pragma unroll
