@@ -70,7 +70,7 @@ def lib():
         L.orc_verify_chain.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, ctypes.c_uint64,
                                        ctypes.c_uint64, ctypes.c_double, vp, i32, i32, i32, ctypes.POINTER(_Out)]
         L.orc_verify_chain.restype = ctypes.c_int
-        L.orc_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32,
+        L.orc_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, i32,
                                       ctypes.c_uint64, ctypes.c_uint64, ctypes.c_double, vp, i32, i32, i32,
                                       ctypes.POINTER(_Out)]
         L.orc_verify_tree.restype = ctypes.c_int
@@ -274,9 +274,12 @@ def verify_chain(zq, zp, d, seed: int, rnd: int, T: float = 1.0, *, u=None, b_ra
 
 
 def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.0, *, max_depth: int, u=None,
-                b_range=None, nthreads=None, query=None):
+                b_range=None, nthreads=None, query=None, walk: int = 0):
     """Tree verify.  zq, zp [B, T+1, V]; node_tokens [B, T+1]; parents [T+1]
-    (shared) or [B, T+1].  u (optional) [B, T + max_depth + 1]."""
+    (shared) or [B, T+1].  u (optional) [B, T + max_depth + 1].  walk 0:
+    descend into the first accepted child; walk 1: the pages' literal walk,
+    only the best (lowest-index) child is followed and its rejection ends
+    the walk."""
     B, nn, V = zq.shape
     Tn = nn - 1
     qs, qr = _strides3(zq)
@@ -289,7 +292,7 @@ def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.
     lo, hi = b_range if b_range is not None else (0, B)
     o, s = _alloc_out(B, max_depth + 1, nn, nn, True, query)
     rc = lib().orc_verify_tree(_ptr(zq), qs, qr, _ptr(zp), ps, pr, _dtype_code(zq), _ptr(node_tokens), _ptr(parents),
-                               shared, B, Tn, V, max_depth, seed, rnd, _temperature(T), _ptr(u), lo, hi,
+                               shared, B, Tn, V, max_depth, int(walk), seed, rnd, _temperature(T), _ptr(u), lo, hi,
                                nthreads or threads_available(), ctypes.byref(s))
     if rc != 0:
         raise ValueError("oracle rejected the arguments")

@@ -40,6 +40,12 @@
  *       into the lowest-index accepted child, stops at a leaf (bonus from the
  *       leaf's q) or at a node with no accepted child (residual of that
  *       node's q and p), and never appends a bonus after a rejection.
+ *   R5b the pages' literal walk ([ZH] section 4, "eagle_round" step 4: take
+ *       the node's best child, accept and descend, or reject, resample and
+ *       end): the best child is the lowest-index child (siblings come in
+ *       descending draft probability); the walk stops with the residual of
+ *       the node's q and p as soon as that child is rejected, whatever its
+ *       siblings' decisions.  Selected by walk = 1.
  *   R6  data errors (NaN or +inf in a row the outcome reads, a row that is
  *       all -inf, a token outside [0,V), a parent not in [0,n), a walk longer
  *       than max_depth) mark the sequence with num_accepted = -1.
@@ -469,16 +475,16 @@ int orc_verify_chain(const void* zq, int64_t q_seq_stride, int64_t q_row_stride,
 /* else [B, T+1]; parents[n] must lie in [0, n) for n >= 1.                  */
 /* u_in (optional) gives per sequence T + max_depth + 1 uniforms: the accept  */
 /* uniforms of nodes 1..T, then the sampling uniforms of slots              */
-/* 1..max_depth+1.                                                           */
+/* 1..max_depth+1.  walk: 0 = reading R5, 1 = reading R5b.                   */
 /* ------------------------------------------------------------------------- */
 int orc_verify_tree(const void* zq, int64_t q_seq_stride, int64_t q_row_stride, const void* zp,
                     int64_t p_seq_stride, int64_t p_row_stride, int dtype, const int32_t* node_tokens,
-                    const int32_t* parents, int parents_shared, int B, int T, int V, int max_depth, uint64_t seed,
-                    uint64_t round, double temp, const double* u_in, int b_begin, int b_end, int nthreads,
-                    orc_out* o)
+                    const int32_t* parents, int parents_shared, int B, int T, int V, int max_depth, int walk,
+                    uint64_t seed, uint64_t round, double temp, const double* u_in, int b_begin, int b_end,
+                    int nthreads, orc_out* o)
 {
     if (B < 0 || T < 0 || V <= 0 || max_depth < 0 || !(temp > 0.0) || b_begin < 0 || b_end > B || !o ||
-        !o->tokens || !o->num_accepted)
+        !o->tokens || !o->num_accepted || (walk != 0 && walk != 1))
         return 1;
     const int nn = T + 1;
     const int width = max_depth + 1;
@@ -549,7 +555,7 @@ int orc_verify_tree(const void* zq, int64_t q_seq_stride, int64_t q_row_stride, 
             OUT_F64(o, ratio, at, r);
             OUT_F64(o, u_acc, at, u);
         }
-        /* the walk (R5) */
+        /* the walk (R5, or R5b when walk = 1) */
         int* path = (int*)malloc(sizeof(int) * (size_t)(width > 0 ? width : 1));
         int depth = 0, cur = 0;
         path[0] = 0;
@@ -557,11 +563,17 @@ int orc_verify_tree(const void* zq, int64_t q_seq_stride, int64_t q_row_stride, 
         for (;;) {
             if (!has_child[cur]) break; /* leaf: bonus from q at cur */
             int next = -1;
-            for (int n = cur + 1; n < nn; ++n)
-                if (par[n] == cur && acc[n]) {
+            for (int n = cur + 1; n < nn; ++n) {
+                if (par[n] != cur) continue;
+                if (walk == 1) {        /* R5b: the best child decides alone */
+                    if (acc[n]) next = n;
+                    break;
+                }
+                if (acc[n]) {           /* R5: the first accepted child */
                     next = n;
                     break;
                 }
+            }
             if (next < 0) {
                 residual = 1;
                 break;

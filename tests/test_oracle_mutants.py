@@ -38,8 +38,11 @@ MUTANTS = {
     "philox_key_bump": ("k0 += 0x9E3779B9u;", "k0 += 0x9E3779B1u;"),
     "u53_shift": ("double lo = (double)(b >> 6);", "double lo = (double)(b >> 5);"),
     "tree_child_own_rows": ("            int pa = par[n];", "            int pa = n;"),
-    "tree_highest_child": ("            for (int n = cur + 1; n < nn; ++n)\n                if (par[n] == cur && acc[n]) {",
-                           "            for (int n = nn - 1; n > cur; --n)\n                if (par[n] == cur && acc[n]) {"),
+    "tree_highest_child": ("            for (int n = cur + 1; n < nn; ++n) {\n                if (par[n] != cur) continue;",
+                           "            for (int n = nn - 1; n > cur; --n) {\n                if (par[n] != cur) continue;"),
+    "tree_best_child_tries_siblings": ("                    if (acc[n]) next = n;\n                    break;",
+                                       "                    if (acc[n]) {\n                        next = n;\n                        break;\n                    }"),
+    "tree_best_child_ignored": ("                if (walk == 1) {        /* R5b", "                if (walk == 2) {        /* R5b"),
     "tree_bonus_after_reject": ("            if (next < 0) {\n                residual = 1;",
                                 "            if (next < 0) {\n                residual = 0;"),
     "kv_len_off_by_one": ("out_kv_len[b] = L0 + k + 1;", "out_kv_len[b] = L0 + k;"),
@@ -75,6 +78,8 @@ def _battery():
     yield lambda: S.test_c1_every_slot_is_distributed_as_q(oracle)
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 4)
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 7)
+    yield lambda: TK.test_best_child_walk_ignores_an_accepted_sibling(oracle)
+    yield lambda: TK.test_best_child_walk_under_forced_flags(oracle, 5)
     yield lambda: TK.test_kv_gather_matches_fancy_indexing(oracle, False)
     yield lambda: TM.test_chain_is_the_causal_mask(130)
     yield lambda: TM.test_every_small_tree_by_matrix_powers(5)

@@ -128,6 +128,117 @@ def test_tree_walk_under_forced_flags(orc, nn):
             assert abs(mass - law[t]) < 1e-12
 
 
+def _walk_best(parents, flags):
+    """Brute-force literal walk: only the lowest-index child is tried."""
+    nn = len(parents)
+    kids = {n: [c for c in range(1, nn) if parents[c] == n] for n in range(nn)}
+    path, cur = [0], 0
+    while True:
+        if not kids[cur]:
+            return path, cur, "bonus"
+        if not flags[kids[cur][0]]:
+            return path, cur, "residual"
+        cur = kids[cur][0]
+        path.append(cur)
+
+
+@pytest.mark.parametrize("nn", [3, 5, 8])
+def test_best_child_walk_under_forced_flags(orc, nn):
+    """walk = 1 (the pages' literal walk): for random tiny trees and every
+    accept-flag pattern the rows allow, path, stop node and sample kind equal
+    a brute-force walk that only tries each node's first child."""
+    rng = np.random.default_rng(100 + nn)
+    V = 6
+    for trial in range(6):
+        parents = _random_tree(rng, nn)
+        md = _depth(parents)
+        zq = rng.normal(0, 1.5, size=(nn, V))
+        zp = zq + rng.normal(0, 1.0, size=(nn, V))
+        tok = [0] + [int(rng.integers(0, V)) for _ in range(1, nn)]
+        q, p = softmax(zq, axis=1), softmax(zp, axis=1)
+        a = np.array([1.0] + [min(1.0, q[parents[n], tok[n]] / p[parents[n], tok[n]]) for n in range(1, nn)])
+        pats = [f for f in itertools.product([0, 1], repeat=nn - 1)
+                if all((fl == 1 and a[n + 1] > 0) or (fl == 0 and a[n + 1] < 1) for n, fl in enumerate(f))]
+        B = len(pats)
+        u = np.zeros((B, nn - 1 + md + 1))
+        for i, f in enumerate(pats):
+            u[i, :nn - 1] = [0.0 if fl else TOP for fl in f]
+        u[:, nn - 1:] = 0.37
+        out = orc.verify_tree(np.broadcast_to(zq[None], (B, nn, V)), np.broadcast_to(zp[None], (B, nn, V)),
+                              np.tile(np.array(tok, np.int32), (B, 1)), np.array(parents, np.int32), 0, 0,
+                              max_depth=md, u=u, walk=1)
+        for i, f in enumerate(pats):
+            path, stop, kind = _walk_best(parents, (1,) + f)
+            k = len(path) - 1
+            assert out["num_accepted"][i] == k
+            assert out["path_nodes"][i, :k + 1].tolist() == path
+            assert out["stop_node"][i] == stop
+            assert out["accept"][i, 1:].tolist() == list(f)  # every node is still decided
+            want = orc.KIND_BONUS if kind == "bonus" else orc.KIND_RESIDUAL
+            assert out["sample_kind"][i] == want
+
+
+def test_best_child_walk_ignores_an_accepted_sibling(orc):
+    """Root with two children: the first rejected, the second accepted.
+    The default walk takes the second; the literal walk stops at the root
+    and resamples from the root's residual."""
+    V = 5
+    zq = np.log(np.array([[0.05, 0.60, 0.15, 0.10, 0.10]] * 3))
+    zp = np.log(np.array([[0.60, 0.05, 0.15, 0.10, 0.10]] * 3))
+    tok = np.array([[0, 0, 1]], np.int32)                      # child 1: a = 1/12, child 2: a = 1
+    parents = np.array([-1, 0, 0], np.int32)
+    u = np.array([[0.5, 0.5, 0.3, 0.3]])                       # child 1 rejected (0.5 > 1/12), child 2 accepted
+    d0 = orc.verify_tree(zq[None], zp[None], tok, parents, 0, 0, max_depth=1, u=u, walk=0)
+    d1 = orc.verify_tree(zq[None], zp[None], tok, parents, 0, 0, max_depth=1, u=u, walk=1)
+    assert d0["num_accepted"][0] == 1 and d0["path_nodes"][0].tolist() == [0, 2]
+    assert d0["sample_kind"][0] == orc.KIND_BONUS
+    assert d1["num_accepted"][0] == 0 and d1["path_nodes"][0, 0] == 0 and d1["stop_node"][0] == 0
+    assert d1["sample_kind"][0] == orc.KIND_RESIDUAL
+    # residual of the root: (q - p)_+ = 0.55 on token 1 only
+    assert d1["tokens"][0, 0] == 1 and abs(d1["resid_mass"][0] - 0.55) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_best_child_walk_is_the_chain_on_the_best_child_path(orc, seed):
+    """walk = 1 on any tree equals the chain verify (a separate code path)
+    run on the tree's best-child path: the chain's rows are those of the path
+    nodes, its drafts their tokens, its uniforms the path nodes' accept
+    uniforms and the tree's sampling uniforms."""
+    rng = np.random.default_rng(seed)
+    nn, V, B = 14, 700, 96
+    parents = _random_tree(rng, nn)
+    md = _depth(parents)
+    zq = rng.normal(0, 2.0, size=(B, nn, V))
+    zp = zq + rng.normal(0, 0.7, size=(B, nn, V))
+    tok = np.concatenate([np.zeros((B, 1), np.int32),
+                          rng.integers(0, V, size=(B, nn - 1)).astype(np.int32)], axis=1)
+    # the best-child path, and drafts that are likely enough to be accepted
+    path = [0]
+    while True:
+        kids = [c for c in range(1, nn) if parents[c] == path[-1]]
+        if not kids:
+            break
+        path.append(kids[0])
+    for i, n in enumerate(path[1:]):
+        tok[:, n] = np.argsort(-zp[:, path[i]], axis=1)[:, rng.integers(0, 3)]
+    u = rng.random((B, nn - 1 + md + 1))
+    tr = orc.verify_tree(zq, zp, tok, np.array(parents, np.int32), 0, 0, max_depth=md, u=u, walk=1)
+    N = len(path) - 1
+    cq = np.ascontiguousarray(zq[:, path])
+    cp = np.ascontiguousarray(zp[:, path[:-1]])
+    d = np.ascontiguousarray(tok[:, path[1:]])
+    cu = np.concatenate([u[:, [n - 1 for n in path[1:]]], u[:, nn - 1:nn - 1 + N + 1]], axis=1)
+    ch = orc.verify_chain(cq, cp, d, 0, 0, u=cu)
+    k = ch["num_accepted"]
+    assert np.array_equal(k, tr["num_accepted"])
+    assert np.array_equal(ch["tokens"], tr["tokens"][:, :N + 1])
+    assert np.array_equal(ch["weight_total"], tr["weight_total"])
+    assert np.array_equal(ch["sample_kind"], tr["sample_kind"])
+    for b in range(B):
+        assert tr["path_nodes"][b, :k[b] + 1].tolist() == path[:k[b] + 1]
+    assert (k == N).any() and (k < N).any()  # both ends of the walk exercised
+
+
 def test_tree_law_chi_square(orc):
     """Philox-driven tree rounds fit the exact law of (stop node, token)
     obtained by enumerating all 2^T accept patterns with weights
