@@ -69,6 +69,13 @@ enum sv_status {
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
 
+/* Tree walks (spec_verify_tree's `walk`). */
+enum sv_walk {
+    SV_WALK_FIRST_ACCEPTED = 0, /* descend into the lowest-index accepted child */
+    SV_WALK_BEST_CHILD = 1      /* the pages' literal walk: only the lowest-index
+                                   child is tried; its rejection ends the walk */
+};
+
 /* Optional timing hook: when non-NULL, `begin` and `rows_done` are the
  * start and stop events of the row-statistics kernel (stamped by that
  * kernel's own start and end on `stream`), and `end`, when non-NULL, is
@@ -151,6 +158,14 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  * uniform is that of slot depth(stop) + 1, so a path-shaped tree reproduces
  * spec_verify_chain bit for bit.
  *
+ * walk = SV_WALK_BEST_CHILD follows the pages' pseudocode literally ([ZH]
+ * section 4, "eagle_round" step 4: take the node's best child; accept and
+ * go on, or reject, resample and end): from each node only its
+ * lowest-index child is tried, and its rejection stops the walk with the
+ * residual at that node even when a sibling was accepted.  This is the
+ * chain verify of the tree's best-child path.  Every node is still tested
+ * (out_accept, out_probs).
+ *
  *   target_logits  [B, T+1, V]  q-logits per node (node 0 = root).
  *   draft_logits   [B, T+1, V]  p-logits per node (rows of leaves unread).
  *   node_tokens    [B, T+1] int32 (entry 0 unread).
@@ -158,6 +173,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  *                  parents[n] in [0, n) for n >= 1 (entry 0 unread).
  *   0 <= T <= 1023, 0 <= max_depth <= T; a walk longer than max_depth is a
  *   data error, so max_depth should be at least the tree's depth.
+ *   walk: SV_WALK_FIRST_ACCEPTED or SV_WALK_BEST_CHILD (else SV_EINVAL).
  * Outputs (tokens, path_nodes, num_accepted required):
  *   out_tokens        [B, max_depth+1] int32: tokens of the accepted path,
  *                     then the correction/bonus token, then -1.
@@ -173,10 +189,10 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
                      const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
                      const int32_t* node_tokens, const int32_t* parents, int parents_shared, int B, int T, int V,
-                     int max_depth, uint64_t seed, uint64_t round, float temperature, int32_t* out_tokens,
-                     int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept, float* out_probs,
-                     double* out_residual_mass, void* workspace, size_t workspace_bytes, const sv_timing* timing,
-                     hipStream_t stream);
+                     int max_depth, int walk, uint64_t seed, uint64_t round, float temperature,
+                     int32_t* out_tokens, int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept,
+                     float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
+                     const sv_timing* timing, hipStream_t stream);
 
 /*
  * kv_compact_indices -- KV rollback and compaction after a verify round

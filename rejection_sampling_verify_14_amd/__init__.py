@@ -34,6 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SV_F32, SV_BF16 = 0, 1
+SV_WALK_FIRST_ACCEPTED, SV_WALK_BEST_CHILD = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EDTYPE", 3: "SV_ESHAPE", 4: "SV_EALIGN", 5: "SV_EWORKSPACE",
           6: "SV_EHIP"}
 
@@ -71,7 +72,7 @@ def _lib():
         L.spec_verify_chain.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, u64, u64,
                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
         L.spec_verify_tree.restype = i32
-        L.spec_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, u64, u64,
+        L.spec_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, i32, u64, u64,
                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
         L.kv_compact_indices.restype = i32
         L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
@@ -86,7 +87,7 @@ def _lib():
         L.tree_attention_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
         L.sv_philox_uniforms.restype = i32
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
-        if L.sv_abi_version() != 2:
+        if L.sv_abi_version() != 3:
             raise ImportError("libspecverify.so ABI version mismatch")
         _L = L
     return _L
@@ -211,10 +212,12 @@ def alloc_tree_outputs(B: int, T: int, max_depth: int, device):
 
 def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, node_tokens: torch.Tensor,
                      parents: torch.Tensor, seed: int, round: int, temperature: float = 1.0, *, max_depth: int,
-                     out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, timing=None,
-                     stream=None) -> dict:
+                     walk: int = 0, out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                     timing=None, stream=None) -> dict:
     """Verify B flattened trees: logits [B, T+1, V] per node, node_tokens
-    [B, T+1] int32, parents [T+1] (shared) or [B, T+1] int32."""
+    [B, T+1] int32, parents [T+1] (shared) or [B, T+1] int32.  walk 0
+    (SV_WALK_FIRST_ACCEPTED) descends into the first accepted child; walk 1
+    (SV_WALK_BEST_CHILD) is the pages' literal best-child walk."""
     _check_logits(target_logits, "target_logits")
     _check_logits(draft_logits, "draft_logits")
     B, nn, V = target_logits.shape
@@ -232,7 +235,7 @@ def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, no
     rc = _lib().spec_verify_tree(
         _p(target_logits), target_logits.stride(0), target_logits.stride(1), _p(draft_logits),
         draft_logits.stride(0), draft_logits.stride(1), _dtype_code(target_logits), _p(node_tokens), _p(parents),
-        1 if parents.dim() == 1 else 0, B, T, V, max_depth, seed & (2 ** 64 - 1), round & (2 ** 64 - 1),
+        1 if parents.dim() == 1 else 0, B, T, V, max_depth, int(walk), seed & (2 ** 64 - 1), round & (2 ** 64 - 1),
         float(temperature), _p(o["tokens"]), _p(o["path_nodes"]), _p(o["num_accepted"]), _p(o.get("accept")),
         _p(o.get("probs")), _p(o.get("residual_mass")), _p(ws), ws.numel() * ws.element_size(), _timing(timing),
         _stream(stream))
@@ -397,4 +400,5 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
 __all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "tree_expand",
            "tree_select", "tree_finalize", "tree_build", "alloc_tree_table", "sv_philox_uniforms",
            "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",
-           "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16"]
+           "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16", "SV_WALK_FIRST_ACCEPTED",
+           "SV_WALK_BEST_CHILD"]

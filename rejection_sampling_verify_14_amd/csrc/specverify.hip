@@ -291,6 +291,7 @@ struct VerifyParams {
     int parents_shared;
     int B, V, N, nn;          // chain: N drafts, nn = N+1; tree: nn = T+1 nodes, N unused
     int max_depth, width;     // output row width (chain N+1, tree max_depth+1)
+    int walk;                 // tree: 0 first accepted child, 1 best child only
     int rows;                 // pass-1 rows per sequence (chain 2N+1, tree 2 nn)
     int segs, seg_len;        // segments per row, elements per segment
     int r_items, nch;         // row blocks per sequence (rows x segs), sample chunks per sequence
@@ -618,7 +619,8 @@ constexpr int kMaxNodes = 1024;
 
 // Tree accept of sequence b, run by the whole block: every node n >= 1 is
 // tested against its parent's q/p rows, then wave 0 walks from the root into
-// the lowest-index accepted child.  The state goes to `out` and the path to
+// the lowest-index accepted child (walk 0), or into the lowest-index child
+// while it is accepted (walk 1, the pages' literal best-child walk).  The state goes to `out` and the path to
 // `path` (both LDS); with `outputs`, also the accept flags and probabilities.
 template <int DT>
 __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t* path, bool outputs)
@@ -693,13 +695,15 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
         int next = -1;
         for (int base = cur + 1; base < nn; base += 64) {
             const int n = base + lane;
-            const bool pred = n < nn && s_par[n] == cur && s_acc[n];
+            const bool pred = n < nn && s_par[n] == cur && (P.walk == 1 || s_acc[n]);
             const uint64_t m = __ballot(pred);
             if (m) {
                 next = base + __ffsll((unsigned long long)m) - 1;
                 break;
             }
         }
+        // walk 1: the best child decides alone (its rejection ends the walk)
+        if (next >= 0 && P.walk == 1 && !s_acc[next]) next = -1;
         if (next < 0) {
             residual = 1;
             break;
@@ -1884,7 +1888,7 @@ bool item_count_ok(int B, int rows, int V)
 
 extern "C" {
 
-int sv_abi_version(void) { return 2; }
+int sv_abi_version(void) { return 3; }
 
 const char* sv_status_string(int status)
 {
@@ -1961,13 +1965,14 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
                      const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
                      const int32_t* node_tokens, const int32_t* parents, int parents_shared, int B, int T, int V,
-                     int max_depth, uint64_t seed, uint64_t round, float temperature, int32_t* out_tokens,
-                     int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept, float* out_probs,
-                     double* out_residual_mass, void* workspace, size_t workspace_bytes, const sv_timing* timing,
-                     hipStream_t stream)
+                     int max_depth, int walk, uint64_t seed, uint64_t round, float temperature,
+                     int32_t* out_tokens, int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept,
+                     float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
+                     const sv_timing* timing, hipStream_t stream)
 {
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
-    if (B < 0 || T < 0 || V < 1 || max_depth < 0 || !(temperature > 0.0f) || !(temperature < INFINITY))
+    if (B < 0 || T < 0 || V < 1 || max_depth < 0 || !(temperature > 0.0f) || !(temperature < INFINITY) ||
+        (walk != SV_WALK_FIRST_ACCEPTED && walk != SV_WALK_BEST_CHILD))
         return SV_EINVAL;
     if (T + 1 > sv::kMaxNodes || max_depth > T || V > sv::kMaxChunks * sv::kChunk) return SV_ESHAPE;
     if (B == 0) return SV_OK;
@@ -1998,6 +2003,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     P.nn = nn;
     P.max_depth = max_depth;
     P.width = max_depth + 1;
+    P.walk = walk;
     fill_common(P, B, V, 2 * nn, seed, round, temperature);
     P.out_tokens = out_tokens;
     P.out_path = out_path_nodes;

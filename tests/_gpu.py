@@ -39,15 +39,16 @@ def run_chain(w, seed: int, rnd: int, *, B=None, N=None, T=None, b_range=None, m
     return rep, g, inp
 
 
-def run_tree(zq, zp, tokens, parents, seed: int, rnd: int, T: float, max_depth: int, *, b_range=None):
+def run_tree(zq, zp, tokens, parents, seed: int, rnd: int, T: float, max_depth: int, *, b_range=None, walk=0):
     import rejection_sampling_verify_14_amd as sv
-    out = sv.spec_verify_tree(zq, zp, tokens, parents, seed=seed, round=rnd, temperature=T, max_depth=max_depth)
+    out = sv.spec_verify_tree(zq, zp, tokens, parents, seed=seed, round=rnd, temperature=T, max_depth=max_depth,
+                              walk=walk)
     torch.cuda.synchronize()
     g = _np(out)
     par = parents.cpu().numpy()
     o = oracle.verify_tree(synth.to_oracle(zq), synth.to_oracle(zp), tokens.cpu().numpy(), par, seed, rnd, T,
                            max_depth=max_depth, b_range=b_range, nthreads=ORACLE_THREADS,
-                           query=compare.sampled_tokens(g))
+                           query=compare.sampled_tokens(g), walk=walk)
     rep = compare.compare_tree(g, o, par, b_range)
     return rep, g
 

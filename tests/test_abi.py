@@ -44,7 +44,7 @@ def test_header_symbols_exported(sv):
 
 def test_status_strings_and_sizes(sv):
     L = sv.library()
-    assert L.sv_abi_version() == 2
+    assert L.sv_abi_version() == 3
     for code in range(7):
         assert L.sv_status_string(code)
     assert sv.chain_workspace_bytes(256, 7, 128256) > 0
@@ -87,14 +87,15 @@ def test_tree_and_kv_argument_errors(sv):
 
     def tree(**kw):
         a = dict(tq=FAKE, tp=FAKE, dt=0, tok=FAKE, par=FAKE, shared=1, B=2, T=5, V=32, md=3, T_=1.0, out=FAKE,
-                 path=FAKE, num=FAKE, ws=FAKE, wsb=1 << 30)
+                 path=FAKE, num=FAKE, ws=FAKE, wsb=1 << 30, walk=0)
         a.update(kw)
         return L.spec_verify_tree(a["tq"], 6 * 32, 32, a["tp"], 6 * 32, 32, a["dt"], a["tok"], a["par"], a["shared"],
-                                  a["B"], a["T"], a["V"], a["md"], 0, 0, a["T_"], a["out"], a["path"], a["num"],
+                                  a["B"], a["T"], a["V"], a["md"], a["walk"], 0, 0, a["T_"], a["out"], a["path"], a["num"],
                                   None, None, None, a["ws"], a["wsb"], None, None)
     assert tree(T=1024) == 3 and tree(md=6) == 3 and tree(md=-1) == 1
     assert tree(par=None) == 1 and tree(path=None) == 1 and tree(T_=0.0) == 1 and tree(dt=9) == 2
     assert tree(wsb=100) == 5 and tree(B=0) == 0
+    assert tree(walk=2) == 1 and tree(walk=-1) == 1 and tree(walk=1, B=0) == 0
     kv = L.kv_compact_indices
     assert kv(None, FAKE, FAKE, 2, -1, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1
     assert kv(None, None, FAKE, 2, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1

@@ -254,6 +254,32 @@ def test_dynamic_tree_reduced():
     _done("dynamic_tree_reduced", rep)
 
 
+@pytest.mark.parametrize("wl", ["c4", "c5"])
+def test_best_child_walk_reduced(wl):
+    """The pages' literal walk (walk = 1) on config 4's static tree and
+    config 5's dynamic trees, reduced V: device vs oracle with walk = 1."""
+    log(f"[case] best_child_walk_{wl}")
+    w = W[wl].with_sizes(V=9001 if wl == "c4" else 7001)
+    rep = compare.Report()
+    kd, ks = [], []
+    for rnd in range(2):
+        if wl == "c4":
+            inp = synth.static_tree_inputs(w, 70 + rnd, "cuda", B=16)
+        else:
+            inp = synth.dynamic_tree_inputs(w, 70 + rnd, "cuda", B=12)
+        r, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 70 + rnd, rnd, w.T, w.depth, walk=1)
+        rep.merge(r)
+        r0, g0 = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 70 + rnd, rnd, w.T, w.depth, walk=0)
+        rep.merge(r0)
+        # same decisions, and the literal walk never goes deeper than the default one
+        assert np.array_equal(g["accept"], g0["accept"])
+        assert (g["num_accepted"] <= g0["num_accepted"]).all()
+        kd.append(g0["num_accepted"].mean())
+        ks.append(g["num_accepted"].mean())
+    log(f"   mean accepted depth: first accepted child {np.mean(kd):.3f}, best child only {np.mean(ks):.3f}")
+    _done(f"best_child_walk_{wl}", rep)
+
+
 def test_tree_edge_cases():
     """Root-only tree (bonus from q_root), a bad parent, a walk deeper than
     max_depth, NaN in an internal row -- per-sequence -1 flags."""
@@ -304,6 +330,10 @@ def test_tree_full_size(wl):
     rep, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 900, 3, w.T, w.depth, b_range=rng)
     log(f"   mean accepted depth {g['num_accepted'].mean():.3f}")
     _done(f"{wl}_full", rep)
+    rep, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 900, 3, w.T, w.depth, b_range=rng,
+                      walk=1)
+    log(f"   best-child walk: mean accepted depth {g['num_accepted'].mean():.3f}")
+    _done(f"{wl}_full_best_child", rep)
 
 
 # --------------------------------------------------------------------------- #
