@@ -18,6 +18,8 @@ host's cores on a bounded sample (cpu_baseline).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
   python bench.py --copy-calibration     # plain copy of known size, for PMC scaling
+  python bench.py --tree-mask | --tree-build   # the tree kernels on config 5
+  python bench.py --walk-compare          # exercise 3: [2,2,2] tree vs 14-draft chain
 """
 from __future__ import annotations
 
@@ -262,6 +264,145 @@ def tree_build_bench(steps: int, warmup: int):
                      "frac": round(gbps / 8000.0, 4), "bytes_per_batch": nbytes}}), flush=True)
 
 
+TREE_222 = [-1, 0, 0, 1, 1, 2, 2, 3, 3, 4, 4, 5, 5, 6, 6]  # [2, 2, 2]: 14 drafts, 8 leaves
+
+
+def _accept_probs(zq, zp, par, tok, T):
+    """a_n = min(1, q_par(t_n) / p_par(t_n)) in fp64, [B, nodes-1]."""
+    import torch
+    lq = torch.log_softmax(zq.double() / T, dim=-1)
+    lp = torch.log_softmax(zp.double() / T, dim=-1)
+    pa = torch.tensor(par[1:], device=zq.device, dtype=torch.long)
+    t = tok[:, 1:].long()
+    ar = torch.arange(zq.shape[0], device=zq.device)[:, None]
+    return torch.clamp(torch.exp(lq[ar, pa[None, :], t] - lp[ar, pa[None, :], t]), max=1.0)
+
+
+def _tree_expectations(a, par):
+    """Exact expected accepted depth of both walks and the probability that
+    the first-accepted-child walk reaches each node, from the per-node
+    accept probabilities a [B, nodes-1] (decisions are independent)."""
+    import torch
+    nn = len(par)
+    kids = [[c for c in range(1, nn) if par[c] == n] for n in range(nn)]
+    B = a.shape[0]
+    e0 = [None] * nn
+    e1 = [None] * nn
+    for n in reversed(range(nn)):
+        if not kids[n]:
+            e0[n] = e1[n] = torch.zeros(B, dtype=torch.float64, device=a.device)
+            continue
+        none_yet = torch.ones(B, dtype=torch.float64, device=a.device)
+        acc = torch.zeros(B, dtype=torch.float64, device=a.device)
+        for c in kids[n]:
+            acc = acc + none_yet * a[:, c - 1] * (1.0 + e0[c])
+            none_yet = none_yet * (1.0 - a[:, c - 1])
+        e0[n] = acc
+        c = kids[n][0]
+        e1[n] = a[:, c - 1] * (1.0 + e1[c])
+    reach = [None] * nn
+    reach[0] = torch.ones(B, dtype=torch.float64, device=a.device)
+    for n in range(nn):
+        none_yet = torch.ones(B, dtype=torch.float64, device=a.device)
+        for c in kids[n]:
+            reach[c] = reach[n] * none_yet * a[:, c - 1]
+            none_yet = none_yet * (1.0 - a[:, c - 1])
+    return e0[0], e1[0], torch.stack(reach, 1)
+
+
+def walk_compare(rounds: int = 8, B: int = 256, V: int = 128256, seed: int = 11, sigma_noise=None) -> dict:
+    """[PT] / [FA] exercise 3: a [2, 2, 2] draft tree (children = the draft's
+    top-2 at each node, 8 candidate paths) against a chain of equal verifier
+    compute (14 drafts, d_i ~ p_i), on config 3's logit recipe (sigma_noise,
+    the draft's distance from the verifier, may be overridden).  For both
+    tree walks and the chain: tokens per verifier call (accepted + 1) from the
+    device verify, and its exact expectation from the same logits (fp64); and
+    per leaf, the rate at which the first-accepted-child walk reaches it."""
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_14_amd as sv
+    import synth
+
+    w = synth.WORKLOADS["c3"].with_sizes(V=V, B=B)
+    if sigma_noise is not None:
+        w = w.with_sizes(sigma_noise=float(sigma_noise))
+    T = w.T
+    par = TREE_222
+    nn = len(par)
+    N = nn - 1
+    parents = torch.tensor(par, dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    mc = {"tree_first_accepted": [], "tree_best_child": [], "chain": []}
+    ex = {"tree_first_accepted": [], "tree_best_child": [], "chain": []}
+    leaf_mc, leaf_ex = [], []
+    for r in range(rounds):
+        zq = synth.verifier_logits(w, B * nn, g, "cuda").view(B, nn, V)
+        zp = synth.draft_from_verifier(w, zq, g)
+        zq, zp = zq.to(w.torch_dtype), zp.to(w.torch_dtype)
+        tok = torch.zeros((B, nn), dtype=torch.int32, device="cuda")
+        for n in range(nn):
+            kids = [c for c in range(1, nn) if par[c] == n]
+            if kids:
+                top = torch.topk(zp[:, n].float(), len(kids), dim=-1).indices.to(torch.int32)
+                for j, c in enumerate(kids):
+                    tok[:, c] = top[:, j]
+        t0 = sv.spec_verify_tree(zq, zp, tok, parents, seed=seed, round=r, temperature=T, max_depth=3, walk=0)
+        t1 = sv.spec_verify_tree(zq, zp, tok, parents, seed=seed, round=r, temperature=T, max_depth=3, walk=1)
+        a = _accept_probs(zq, zp, par, tok, T)
+        e0, e1, reach = _tree_expectations(a, par)
+        mc["tree_first_accepted"].append(t0["num_accepted"].double() + 1)
+        mc["tree_best_child"].append(t1["num_accepted"].double() + 1)
+        ex["tree_first_accepted"].append(e0 + 1)
+        ex["tree_best_child"].append(e1 + 1)
+        path = t0["path_nodes"].long()
+        hit = torch.zeros((B, nn), dtype=torch.float64, device="cuda")
+        hit.scatter_(1, path.clamp_min(0), (path >= 0).double())
+        leaf_mc.append(hit[:, 7:])
+        leaf_ex.append(reach[:, 7:])
+        del zq, zp
+        # the chain: fresh rows, drafts sampled from the draft
+        cq = synth.verifier_logits(w, B * (N + 1), g, "cuda").view(B, N + 1, V)
+        cp = synth.draft_from_verifier(w, cq[:, :N], g)
+        cq, cp = cq.to(w.torch_dtype), cp.to(w.torch_dtype)
+        d = synth.gumbel_max(cp.float(), T, g)
+        ch = sv.spec_verify_chain(cq, cp, d, seed=seed, round=r, temperature=T)
+        q = torch.softmax(cq[:, :N].double() / T, dim=-1)
+        p = torch.softmax(cp.double() / T, dim=-1)
+        alpha = torch.minimum(q, p).sum(-1)          # [B, N]: P(accept) of a draft drawn from p
+        mc["chain"].append(ch["num_accepted"].double() + 1)
+        ex["chain"].append(1.0 + torch.cumprod(alpha, dim=1).sum(1))
+        del cq, cp, q, p
+    out = {}
+    for k in mc:
+        m = torch.cat(mc[k]).cpu().numpy()
+        e = torch.cat(ex[k]).cpu().numpy()
+        out[k] = {"tokens_per_call": round(float(m.mean()), 4), "expected": round(float(e.mean()), 4),
+                  "std_err": round(float(m.std(ddof=1) / np.sqrt(m.size)), 4)}
+    lm = torch.cat(leaf_mc).mean(0).cpu().numpy()
+    le = torch.cat(leaf_ex).mean(0).cpu().numpy()
+    out["alpha_per_leaf"] = [round(float(x), 4) for x in lm]
+    out["alpha_per_leaf_expected"] = [round(float(x), 4) for x in le]
+    out["samples"] = rounds * B
+    return out
+
+
+def walk_compare_bench(rounds: int):
+    """One JSON line per draft quality: config 3's own recipe (the draft close
+    to the verifier, sigma_noise 0.4) and a far draft (sigma_noise 3.0)."""
+    for noise in (None, 3.0):
+        res = walk_compare(rounds=rounds, sigma_noise=noise)
+        print(json.dumps({
+            "metric": "tokens per verifier call: [2,2,2] tree vs 14-draft chain (exercise 3)",
+            "value": res["tree_first_accepted"]["tokens_per_call"], "unit": "tokens/call", "higher_is_better": True,
+            "data": "synthetic",
+            "config": {"workload": "config 3 logit recipe, B=256, V=128256 bf16, T=1.0; tree [2,2,2] (draft top-2 "
+                                   "per node); chain N=14 (d ~ p)",
+                       "sigma_noise": 0.4 if noise is None else noise},
+            **res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -274,6 +415,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
     ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on config 5 rows instead")
+    ap.add_argument("--walk-compare", action="store_true",
+                    help="exercise 3: [2,2,2] tree (both walks) vs a 14-draft chain, tokens per verifier call")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -294,6 +437,9 @@ def main():
         return
     if args.tree_build:
         tree_build_bench(args.steps, args.warmup)
+        return
+    if args.walk_compare:
+        walk_compare_bench(rounds=8)
         return
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     w = synth.WORKLOADS[args.workload]

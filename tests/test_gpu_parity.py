@@ -280,6 +280,30 @@ def test_best_child_walk_reduced(wl):
     _done(f"best_child_walk_{wl}", rep)
 
 
+def test_walk_compare_matches_its_expectations():
+    """Exercise 3's experiment (bench.py --walk-compare) at a reduced V: the
+    device's tokens per verifier call for both walks and the chain lie within
+    5 standard errors of their exact expectations from the same logits, and
+    each leaf's reach rate within 5 binomial standard errors."""
+    import importlib.util
+    import os
+    log("[case] walk_compare")
+    spec = importlib.util.spec_from_file_location(
+        "bench", os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    res = bench.walk_compare(rounds=4, B=256, V=16384, seed=5)
+    log(f"   {res}")
+    for k in ("tree_first_accepted", "tree_best_child", "chain"):
+        r = res[k]
+        assert abs(r["tokens_per_call"] - r["expected"]) < 5 * r["std_err"] + 1e-3, (k, r)
+    n = res["samples"]
+    for m, e in zip(res["alpha_per_leaf"], res["alpha_per_leaf_expected"]):
+        assert abs(m - e) < 5 * np.sqrt(max(e * (1 - e), 1e-4) / n) + 1e-3, (m, e)
+    assert res["tree_first_accepted"]["expected"] >= res["tree_best_child"]["expected"]
+    log("[done] walk_compare")
+
+
 def test_tree_edge_cases():
     """Root-only tree (bonus from q_root), a bad parent, a walk deeper than
     max_depth, NaN in an internal row -- per-sequence -1 flags."""
