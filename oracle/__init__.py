@@ -76,6 +76,9 @@ def lib():
         L.orc_verify_tree.restype = ctypes.c_int
         L.orc_kv_compact.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i64, i64, i32, i32, i64]
         L.orc_kv_compact.restype = ctypes.c_int
+        L.orc_sample_draft.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.c_double, ctypes.c_uint64,
+                                       ctypes.c_uint64, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32]
+        L.orc_sample_draft.restype = ctypes.c_int
         L.orc_tree_build.argtypes = [vp, i64, i64, i32, i32, i32, i32, i32, i32, ctypes.c_double, vp, vp, vp, vp, vp]
         L.orc_tree_build.restype = ctypes.c_int
         L.orc_tree_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp]
@@ -294,6 +297,34 @@ def verify_tree(zq, zp, node_tokens, parents, seed: int, rnd: int, T: float = 1.
     rc = lib().orc_verify_tree(_ptr(zq), qs, qr, _ptr(zp), ps, pr, _dtype_code(zq), _ptr(node_tokens), _ptr(parents),
                                shared, B, Tn, V, max_depth, int(walk), seed, rnd, _temperature(T), _ptr(u), lo, hi,
                                nthreads or threads_available(), ctypes.byref(s))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return o
+
+
+def sample_draft(zp, seed: int, rnd: int, T: float = 1.0, *, pos0: int = 0, u=None, query=None, nthreads=None):
+    """Draft tokens d ~ softmax(z / T), one per row of zp [B, R, V] (float32,
+    float64 or bf16 bits as uint16), by the inverse CDF in token order with
+    the uniform of Philox stream 1 at (sequence b, position pos0 + r).  u
+    [B, R] replaces the uniforms; query [B, R] int32 asks for the CDF edges
+    of given tokens.  Returns tokens, logprob, u, target, W, edge_lo, edge_hi
+    (and qedge_lo, qedge_hi with query), each [B, R]."""
+    zp = np.asarray(zp)
+    B, R, V = zp.shape
+    ss, rs = _strides3(zp)
+    o = {"tokens": np.empty((B, R), np.int32)}
+    for k in ("logprob", "u", "target", "W", "edge_lo", "edge_hi"):
+        o[k] = np.full((B, R), np.nan)
+    if u is not None:
+        u = np.ascontiguousarray(u, dtype=np.float64).reshape(B, R)
+    if query is not None:
+        query = np.ascontiguousarray(query, dtype=np.int32).reshape(B, R)
+        o["qedge_lo"] = np.full((B, R), np.nan)
+        o["qedge_hi"] = np.full((B, R), np.nan)
+    rc = lib().orc_sample_draft(_ptr(zp), ss, rs, _dtype_code(zp), B, R, V, _temperature(T), seed, rnd, pos0, _ptr(u),
+                                _ptr(o["tokens"]), _ptr(o["logprob"]), _ptr(o["u"]), _ptr(o["target"]), _ptr(o["W"]),
+                                _ptr(o["edge_lo"]), _ptr(o["edge_hi"]), _ptr(query), _ptr(o.get("qedge_lo")),
+                                _ptr(o.get("qedge_hi")), nthreads or threads_available())
     if rc != 0:
         raise ValueError("oracle rejected the arguments")
     return o

@@ -356,6 +356,67 @@ static int sample_at(const orc_out* o, int64_t b, const void* qrow, double lse_q
 }
 
 /* ------------------------------------------------------------------------- */
+/* Draft-token sampling ([PT] O Conceito and Implementando, Passo 1: the     */
+/* draft proposes d ~ p, the draft's distribution; [ZH] section 2 draws each */
+/* draft token from the draft model's softmax in turn).  Row r of sequence b */
+/* (at zp + (b*seq_stride + r*row_stride) elements) gives one token drawn   */
+/* from softmax(z / T) by the inverse CDF of R3 with the uniform of R4's     */
+/* block (seed, round, sequence b, position pos0 + r, stream 1), words 0 and */
+/* 1.  u_in [B, R] (optional) replaces the uniforms.  Outputs [B, R]: token  */
+/* (-1 on a bad row, R6), ln p(token) (NaN on a bad row), the uniform, the   */
+/* target u*W, W, the CDF edges of the token drawn, and (with query) of the  */
+/* query token.                                                             */
+/* ------------------------------------------------------------------------- */
+int orc_sample_draft(const void* zp, int64_t seq_stride, int64_t row_stride, int dtype, int B, int R, int V,
+                     double T, uint64_t seed, uint64_t round, int pos0, const double* u_in, int32_t* tokens,
+                     double* logprob, double* u_out, double* target_out, double* W_out, double* lo_out,
+                     double* hi_out, const int32_t* query, double* qlo_out, double* qhi_out, int nthreads)
+{
+    if (B < 0 || R < 0 || V <= 0 || !(T > 0.0) || pos0 < 0 || !tokens) return 1;
+#ifdef _OPENMP
+    if (nthreads < 1) nthreads = 1;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < (int64_t)B * R; ++i) {
+        const int b = (int)(i / R), r = (int)(i % R);
+        const void* row = row_ptr(zp, dtype, seq_stride, row_stride, b, r);
+        double u;
+        if (u_in) {
+            u = u_in[i];
+        } else {
+            uint32_t w4[4];
+            orc_philox_block(seed, round, (uint32_t)b, (uint32_t)(pos0 + r), 1u, w4);
+            u = orc_u53(w4[0], w4[1]);
+        }
+        if (u_out) u_out[i] = u;
+        double lse;
+        if (orc_row_lse(row, dtype, V, T, NULL, &lse) != 0) {
+            tokens[i] = -1;
+            if (logprob) logprob[i] = NAN;
+            continue;
+        }
+        double* w = (double*)malloc(sizeof(double) * (size_t)V);
+        row_probs(row, dtype, V, T, lse, w);
+        double W, target, lo, hi;
+        const int tok = inverse_cdf(w, V, u, &W, &target, &lo, &hi);
+        tokens[i] = tok;
+        if (logprob) logprob[i] = tok >= 0 ? logit_at(row, dtype, tok) / T - lse : NAN;
+        if (target_out) target_out[i] = target;
+        if (W_out) W_out[i] = W;
+        if (lo_out) lo_out[i] = lo;
+        if (hi_out) hi_out[i] = hi;
+        if (query && qlo_out && qhi_out) {
+            double qlo = NAN, qhi = NAN;
+            if (query[i] >= 0 && query[i] < V) cdf_edges(w, V, query[i], &qlo, &qhi);
+            qlo_out[i] = qlo;
+            qhi_out[i] = qhi;
+        }
+        free(w);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Chain verify ([PT] O Conceito: N stacked accept calls, left to right; at */
 /* the first rejection at position j sample residual(q_j, p_j) and stop; if  */
 /* everything is accepted, a bonus token from q_{N+1}.  [ZH] section 2 and   */

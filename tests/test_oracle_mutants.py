@@ -17,6 +17,7 @@ import test_oracle_stats as S
 import test_oracle_tree_kv as TK
 import test_oracle_tree_build as TB
 import test_oracle_tree_mask as TM
+import test_oracle_draft as TD
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "sv_oracle.c")
 
@@ -55,6 +56,11 @@ MUTANTS = {
     "tree_score_without_lse": ("c_score[n] = f_score[f] + (top_val[r] / T - lse);", "c_score[n] = f_score[f] + top_val[r] / T;"),
     "tree_frontier_worst": ("                    f_ids[r] = order[r].id;\n                    f_score[r] = order[r].score;",
                             "                    f_ids[r] = order[cnt - 1 - r].id;\n                    f_score[r] = order[cnt - 1 - r].score;"),
+    "draft_verify_stream": ("orc_philox_block(seed, round, (uint32_t)b, (uint32_t)(pos0 + r), 1u, w4);",
+                            "orc_philox_block(seed, round, (uint32_t)b, (uint32_t)(pos0 + r), 0u, w4);"),
+    "draft_logprob_without_T": ("logit_at(row, dtype, tok) / T - lse : NAN;", "logit_at(row, dtype, tok) - lse : NAN;"),
+    "draft_wrong_row": ("const void* row = row_ptr(zp, dtype, seq_stride, row_stride, b, r);",
+                        "const void* row = row_ptr(zp, dtype, seq_stride, row_stride, b, 0);"),
     "tree_parent_score_dropped": ("c_score[n] = f_score[f] + (top_val[r] / T - lse);", "c_score[n] = top_val[r] / T - lse;"),
 }
 
@@ -88,6 +94,8 @@ def _battery():
     yield lambda: TB.test_depth1_is_the_roots_topk(1.0)
     yield lambda: TB.test_matches_the_generators_construction(512, 3)
     yield lambda: TB.test_level2_scores_are_path_sums()
+    yield lambda: TD.test_uniform_source_and_token_by_searchsorted()
+    yield lambda: TD.test_logprob_is_log_softmax()
 
 
 @pytest.fixture(scope="module")
