@@ -302,6 +302,26 @@ int tree_finalize(const int32_t* cand_token, const int32_t* cand_parent, const i
                   int32_t* out_tokens, int32_t* out_depth, double* out_score, hipStream_t stream);
 
 /*
+ * sv_sample_draft -- draft tokens d ~ softmax(z / T) ([PT] O Conceito and
+ * Implementando, Passo 1: the draft proposes d ~ p; [ZH] section 2: each
+ * draft token is drawn from the draft model's softmax).  Row r of sequence
+ * b, at logits + (b*seq_stride + r*row_stride) elements (V of them, dtype
+ * SV_F32 / SV_BF16), gives out_tokens[b*R + r] by the verify step's inverse
+ * CDF in token order (the first token whose running weight exceeds u*W, W
+ * the total; the last token of positive weight if rounding leaves none;
+ * weights exp((z - max)/T) accumulated in double) with the uniform of
+ * Philox stream 1: key seed, counter (pos0 + r, b, round low word,
+ * (round high word << 4) | 1), words 0 and 1 as a 53-bit double, so draft
+ * draws never reuse a verify uniform.  out_logprob[b*R + r] (may be NULL):
+ * ln p(token) in double.  A row with NaN or +inf, or only -inf, gives -1
+ * and NaN.  1 <= V <= 524288, pos0 >= 0, pos0 + R < 2^32.  One launch (a
+ * block per row), no workspace.
+ */
+int sv_sample_draft(const void* logits, int64_t seq_stride, int64_t row_stride, int dtype, int B, int R, int V,
+                    float temperature, uint64_t seed, uint64_t round, int pos0, int32_t* out_tokens,
+                    double* out_logprob, hipStream_t stream);
+
+/*
  * sv_philox_uniforms -- the uniforms the verify step draws, for tests of
  * the device generator: for sequences [0, nseq) and positions 1..npos,
  * out_acc[s*npos + p-1] and out_samp[s*npos + p-1] (device double arrays,

@@ -20,6 +20,8 @@ Functions (same names as the C ABI):
   tree_expand, tree_select, tree_finalize -- EAGLE-2 dynamic draft tree,
                         level by level ([ZH] sections 4 and 5); tree_build
                         chains them over draft rows given up front
+  sample_draft       -- draft tokens d ~ p from draft logits ([PT] O Conceito;
+                        [ZH] section 2)
   sv_philox_uniforms -- the step's uniforms (for tests)
 """
 from __future__ import annotations
@@ -86,6 +88,8 @@ def _lib():
         L.tree_attention_mask.restype = i32
         L.tree_attention_mask.argtypes = [vp, i32, vp, i32, i32, vp, vp, vp]
         L.sv_philox_uniforms.restype = i32
+        L.sv_sample_draft.restype = i32
+        L.sv_sample_draft.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, u64, u64, i32, vp, vp, vp]
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
         if L.sv_abi_version() != 3:
             raise ImportError("libspecverify.so ABI version mismatch")
@@ -386,6 +390,24 @@ def tree_build(rows: torch.Tensor, *, depth: int, topk: int, budget: int, temper
     return out
 
 
+def sample_draft(logits: torch.Tensor, seed: int, round: int, temperature: float = 1.0, *, pos0: int = 0,
+                 logprob: bool = True, stream=None):
+    """Draft tokens d ~ softmax(logits / T), one per row of logits [B, R, V]
+    (unit last stride): int32 tokens [B, R] and, with logprob, float64
+    ln p(token) [B, R]; uniforms from Philox stream 1 at positions pos0 + r."""
+    if logits.dim() != 3 or logits.stride(2) != 1:
+        raise ValueError("logits must be [B, R, V] with a unit last stride")
+    B, R, V = logits.shape
+    tok = torch.empty((B, R), dtype=torch.int32, device=logits.device)
+    lp = torch.empty((B, R), dtype=torch.float64, device=logits.device) if logprob else None
+    rc = _lib().sv_sample_draft(_p(logits), logits.stride(0), logits.stride(1), _dtype_code(logits), B, R, V,
+                                float(temperature), seed & (2 ** 64 - 1), round & (2 ** 64 - 1), pos0, _p(tok),
+                                _p(lp), _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "sv_sample_draft")
+    return tok, lp
+
+
 def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda", stream=None):
     """(u_acc, u_samp) [nseq, npos] float64 for positions 1..npos."""
     a = torch.empty((nseq, npos), dtype=torch.float64, device=device)
@@ -397,7 +419,8 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
     return a, s
 
 
-__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "tree_expand",
+__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "sample_draft",
+           "tree_expand",
            "tree_select", "tree_finalize", "tree_build", "alloc_tree_table", "sv_philox_uniforms",
            "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",
            "SpecVerifyError", "library", "LIB_PATH", "SV_F32", "SV_BF16", "SV_WALK_FIRST_ACCEPTED",

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
-SOURCES = ["specverify.hip", "sv_kv.hip", "sv_tree.hip"]
+SOURCES = ["specverify.hip", "sv_kv.hip", "sv_tree.hip", "sv_draft.hip"]
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 

@@ -1,0 +1,297 @@
+// sv_draft.hip -- draft-token sampling on the device: d ~ softmax(z / T)
+// for every row of a batch of draft logits ([PT] "Decodificacao
+// Especulativa e EAGLE-3", O Conceito and Implementando, Passo 1: the draft
+// proposes d ~ p; [ZH] "投机解码与 EAGLE" section 2: each draft token is drawn
+// from the draft model's softmax in turn).  The draw is the inverse CDF in
+// token order of the verify step's sampling (first token whose running
+// weight exceeds u*W, W the total weight, accumulated in double; the last
+// token of positive weight when rounding leaves none), with the uniform of
+// Philox stream 1.  gfx950, wave64.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "specverify.h"
+#include "sv_device.h"
+
+namespace sv {
+
+constexpr int kDraftWaves = 8;
+constexpr int kDraftBlock = kDraftWaves * 64;
+constexpr int kDraftPerLane = 32;                    // logits per lane per chunk
+constexpr int kDraftChunk = 64 * kDraftPerLane;      // 2048 logits per chunk (one wave)
+constexpr int kDraftMaxChunks = 256;                 // V <= 524288
+
+struct DraftArgs {
+    const char* rows;
+    int64_t seq_stride, row_stride;  // elements
+    int R, V, pos0;
+    double invT;
+    uint64_t seed, round;
+    int32_t* out_tokens;
+    double* out_logprob;
+};
+
+// The uniform of a draft draw: Philox block (position, sequence, round lo,
+// (round hi) << 4 | stream 1), words 0 and 1.
+__device__ __forceinline__ double draft_uniform(uint64_t seed, uint64_t round, uint32_t seq, uint32_t pos)
+{
+    const Words4 w = philox4x32_10(pos, seq, (uint32_t)round, ((uint32_t)(round >> 32) << 4) | 1u, (uint32_t)seed,
+                                   (uint32_t)(seed >> 32));
+    return u53(w.w0, w.w1);
+}
+
+// A lane's kDraftPerLane logits of chunk c (contiguous, token order), as raw
+// 16-byte vectors; padding past V is masked when decoded.
+template <int DT>
+struct ChunkRegs {
+    static constexpr int NV = kDraftPerLane * (DT == DT_BF16 ? 2 : 4) / 16;
+    uint4 v[NV];
+};
+
+template <int DT>
+__device__ __forceinline__ void load_lane_chunk(const char* row, int V, int c, int lane, ChunkRegs<DT>& r)
+{
+    constexpr int EB = DT == DT_BF16 ? 2 : 4;
+    constexpr int EPV = 16 / EB;
+    const int64_t e0 = (int64_t)c * kDraftChunk + (int64_t)lane * kDraftPerLane;
+    const bool vec = ((((uintptr_t)row) & 15u) == 0) && e0 + kDraftPerLane <= V;
+    if (vec) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + e0 * EB);
+#pragma unroll
+        for (int i = 0; i < ChunkRegs<DT>::NV; ++i) r.v[i] = stream_load16(p + i);
+    } else {
+        // ragged tail or unaligned row: element by element, -inf past V
+        float x[kDraftPerLane];
+#pragma unroll
+        for (int j = 0; j < kDraftPerLane; ++j) x[j] = (e0 + j < V) ? load_logit<DT>(row, e0 + j) : -INFINITY;
+#pragma unroll
+        for (int i = 0; i < ChunkRegs<DT>::NV; ++i) r.v[i] = encode16<DT>(x + i * EPV);
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ void decode_lane_chunk(const ChunkRegs<DT>& r, float* x)
+{
+    constexpr int EPV = DT == DT_BF16 ? 8 : 4;
+#pragma unroll
+    for (int i = 0; i < ChunkRegs<DT>::NV; ++i) decode16<DT>(r.v[i], x + i * EPV);
+}
+
+__device__ __forceinline__ double wave_sum_d(double v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max_fl(float v)
+{
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// Exclusive prefix sum over the wave's lanes (lane order), and the total.
+__device__ __forceinline__ double wave_exclusive(double v, int lane, double* total)
+{
+    double x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    *total = __shfl(x, 63, 64);
+    return x - v;
+}
+
+// Block (b, r): one draw from row r of sequence b.
+//  1. Each wave takes chunks w, w + 8, ... (2048 logits, 32 contiguous per
+//     lane, the next chunk's loads in flight): the chunk's maximum m_c and
+//     s_c = sum exp((x - m_c)/T) in double (table-driven exp), into LDS.
+//  2. Wave 0: M = max m_c, chunk weights s_c exp((m_c - M)/T), W, u*W, and
+//     the chunk where the running weight passes u*W (4 chunks per lane, an
+//     exclusive scan over lanes).
+//  3. Wave 0 rescans that chunk in token order with the same weights.
+// A row holding NaN or +inf, or only -inf, gives token -1 and NaN.
+template <int DT>
+__global__ __launch_bounds__(kDraftBlock) void k_draft_sample(DraftArgs A)
+{
+    __shared__ double s_tab[kExpTabN];
+    __shared__ float s_m[kDraftMaxChunks];
+    __shared__ double s_s[kDraftMaxChunks];
+    __shared__ int s_bad;
+    const int row_id = blockIdx.x;
+    const int b = row_id / A.R, r = row_id - b * A.R;
+    const char* row = A.rows + ((int64_t)b * A.seq_stride + (int64_t)r * A.row_stride) * (DT == DT_BF16 ? 2 : 4);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nch = (A.V + kDraftChunk - 1) / kDraftChunk;
+    fill_exp_table(s_tab);
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
+    const lds_dptr tab = (lds_dptr)s_tab;
+    const double invT = A.invT;
+
+    // 1. chunk sums
+    int bad = 0;
+    ChunkRegs<DT> cur, nxt;
+    if (wave < nch) load_lane_chunk<DT>(row, A.V, wave, lane, cur);
+    for (int c = wave; c < nch; c += kDraftWaves) {
+        if (c + kDraftWaves < nch) load_lane_chunk<DT>(row, A.V, c + kDraftWaves, lane, nxt);
+        float x[kDraftPerLane];
+        decode_lane_chunk<DT>(cur, x);
+        float lm = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kDraftPerLane; ++j) {
+            bad |= (int)(x[j] != x[j]) | (int)(x[j] == INFINITY);
+            lm = fmaxf(lm, x[j]);
+        }
+        const float m = wave_max_fl(lm);
+        double s = 0.0;
+        if (m != -INFINITY) {
+#pragma unroll
+            for (int j = 0; j < kDraftPerLane; ++j) s += exp_rel(((double)x[j] - (double)m) * invT, tab);
+        }
+        s = wave_sum_d(s);
+        if (lane == 0) {
+            s_m[c] = m;
+            s_s[c] = s;
+        }
+        cur = nxt;
+    }
+    if (bad) s_bad = 1;
+    __syncthreads();
+    if (wave != 0) return;
+
+    // 2. total weight and the chunk of the draw
+    const int64_t oi = (int64_t)b * A.R + r;
+    float M = -INFINITY;
+    for (int c = lane; c < nch; c += 64) M = fmaxf(M, s_m[c]);
+    M = wave_max_fl(M);
+    if (s_bad || M == -INFINITY) {
+        if (lane == 0) {
+            A.out_tokens[oi] = -1;
+            if (A.out_logprob) A.out_logprob[oi] = NAN;
+        }
+        return;
+    }
+    constexpr int CPL = kDraftMaxChunks / 64;  // chunks per lane, consecutive
+    double cw[CPL];
+    double lsum = 0.0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+        const int c = lane * CPL + i;
+        cw[i] = (c < nch && s_m[c] != -INFINITY) ? s_s[c] * exp_rel(((double)s_m[c] - (double)M) * invT, tab) : 0.0;
+        lsum += cw[i];
+    }
+    double W;
+    const double lbase = wave_exclusive(lsum, lane, &W);
+    const double u = draft_uniform(A.seed, A.round, (uint32_t)b, (uint32_t)(A.pos0 + r));
+    const double target = u * W;
+    // the first lane whose running weight passes the target; else (rounding)
+    // the last lane with positive weight, whose last positive chunk is taken
+    const uint64_t pass = __ballot(lsum > 0.0 && lbase + lsum > target);
+    const uint64_t pos = __ballot(lsum > 0.0);
+    const bool fallback = pass == 0;
+    const int owner = fallback ? 63 - __clzll((long long)pos) : __ffsll((unsigned long long)pass) - 1;
+    int cs = -1;
+    double cbase = 0.0;
+    if (lane == owner) {
+        double cum = lbase;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+            const int c = lane * CPL + i;
+            if (cw[i] > 0.0) {
+                if (!fallback && cs < 0 && cum + cw[i] > target) {
+                    cs = c;
+                    cbase = cum;
+                }
+                if (fallback) {
+                    cs = c;
+                    cbase = cum;
+                }
+            }
+            cum += cw[i];
+        }
+    }
+    cs = __shfl(cs, owner, 64);
+    cbase = __shfl(cbase, owner, 64);
+    const float mc = s_m[cs];
+    const double scale = exp_rel(((double)mc - (double)M) * invT, tab);
+    const double local = fallback ? INFINITY : (target - cbase) / scale;
+
+    // 3. rescan the chunk in token order
+    ChunkRegs<DT> rr;
+    load_lane_chunk<DT>(row, A.V, cs, lane, rr);
+    float x[kDraftPerLane];
+    decode_lane_chunk<DT>(rr, x);
+    double wv[kDraftPerLane];
+    double tsum = 0.0;
+#pragma unroll
+    for (int j = 0; j < kDraftPerLane; ++j) {
+        wv[j] = exp_rel(((double)x[j] - (double)mc) * invT, tab);
+        tsum += wv[j];
+    }
+    double ctot;
+    const double tbase = wave_exclusive(tsum, lane, &ctot);
+    const uint64_t cand = __ballot(tsum > 0.0 && tbase + tsum > local);
+    const uint64_t posl = __ballot(tsum > 0.0);
+    const int own = cand ? __ffsll((unsigned long long)cand) - 1 : 63 - __clzll((long long)posl);
+    if (lane == own) {
+        double cum = tbase;
+        int pick = -1, last = -1;
+        float xpick = 0.0f, xlast = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kDraftPerLane; ++j) {
+            if (wv[j] > 0.0) {
+                last = j;
+                xlast = x[j];
+                if (pick < 0 && cum + wv[j] > local) {
+                    pick = j;
+                    xpick = x[j];
+                }
+            }
+            cum += wv[j];
+        }
+        if (pick < 0) {
+            pick = last;
+            xpick = xlast;
+        }
+        A.out_tokens[oi] = cs * kDraftChunk + lane * kDraftPerLane + pick;
+        if (A.out_logprob) A.out_logprob[oi] = ((double)xpick - (double)M) * invT - log(W);
+    }
+}
+
+}  // namespace sv
+
+extern "C" int sv_sample_draft(const void* logits, int64_t seq_stride, int64_t row_stride, int dtype, int B, int R,
+                               int V, float temperature, uint64_t seed, uint64_t round, int pos0,
+                               int32_t* out_tokens, double* out_logprob, hipStream_t stream)
+{
+    if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
+    if (B < 0 || R < 0 || V < 1 || pos0 < 0 || seq_stride < 0 || row_stride < 0) return SV_EINVAL;
+    if (!(temperature > 0.0f) || !(temperature < INFINITY)) return SV_EINVAL;
+    if (V > sv::kDraftMaxChunks * sv::kDraftChunk || (int64_t)pos0 + R > 0xFFFFFFFFll) return SV_ESHAPE;
+    if ((int64_t)B * R > 0x7FFFFFFF) return SV_ESHAPE;
+    if (B == 0 || R == 0) return SV_OK;
+    if (!logits || !out_tokens) return SV_EINVAL;
+    const int es = dtype == SV_BF16 ? 2 : 4;
+    if (((uintptr_t)logits) % es) return SV_EALIGN;
+    sv::DraftArgs A;
+    A.rows = static_cast<const char*>(logits);
+    A.seq_stride = seq_stride;
+    A.row_stride = row_stride;
+    A.R = R;
+    A.V = V;
+    A.pos0 = pos0;
+    A.invT = 1.0 / (double)temperature;
+    A.seed = seed;
+    A.round = round;
+    A.out_tokens = out_tokens;
+    A.out_logprob = out_logprob;
+    const dim3 grid((unsigned)(B * R));
+    if (dtype == SV_BF16) hipLaunchKernelGGL(sv::k_draft_sample<1>, grid, dim3(sv::kDraftBlock), 0, stream, A);
+    else hipLaunchKernelGGL(sv::k_draft_sample<0>, grid, dim3(sv::kDraftBlock), 0, stream, A);
+    return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
+}

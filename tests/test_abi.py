@@ -118,6 +118,14 @@ def test_tree_and_kv_argument_errors(sv):
     assert ex(dt=5) == 2 and ex(k=17) == 3 and ex(k=0) == 3 and ex(V=5) == 3      # topk in [1, min(16, V)]
     assert ex(off=1) == 3 and ex(nmax=4096) == 3 and ex(T=0.0) == 1 and ex(lvl=0) == 1
     assert ex(rows=None) == 1 and ex(rows=FAKE + 1) == 4 and ex(B=0) == 0
+    def sd(**kw):
+        a = dict(rows=FAKE, dt=1, B=2, R=3, V=100, T=1.0, pos0=0, out=FAKE)
+        a.update(kw)
+        return L.sv_sample_draft(a["rows"], 300, 100, a["dt"], a["B"], a["R"], a["V"], a["T"], 0, 0, a["pos0"],
+                                 a["out"], None, None)
+    assert sd(dt=3) == 2 and sd(V=0) == 1 and sd(V=524289) == 3 and sd(T=0.0) == 1 and sd(T=float("inf")) == 1
+    assert sd(pos0=-1) == 1 and sd(rows=None) == 1 and sd(out=None) == 1 and sd(rows=FAKE + 1) == 4
+    assert sd(B=0) == 0 and sd(R=0) == 0
     assert L.tree_select(FAKE, 2, 30, 0, 31, 10, FAKE, FAKE, None) == 3          # past n_max
     assert L.tree_select(FAKE, 2, 30, 0, 20, 21, FAKE, FAKE, None) == 1          # k > count
     assert L.tree_select(FAKE, 0, 30, 0, 20, 10, FAKE, FAKE, None) == 0

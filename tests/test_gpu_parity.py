@@ -304,6 +304,90 @@ def test_walk_compare_matches_its_expectations():
     log("[done] walk_compare")
 
 
+def _draft_case(name, rows, T, seed, rnd, pos0=0, b_sel=None):
+    """Device draft draws vs the oracle: every device token's CDF interval
+    holds the oracle's u*W (within a 1e-9 relative band, excused and
+    counted), the same uniform, and ln p within 1e-9."""
+    import rejection_sampling_verify_14_amd as sv
+    log(f"[case] draft {name} rows={tuple(rows.shape)} T={T}")
+    tok, lp = sv.sample_draft(rows, seed, rnd, T, pos0=pos0)
+    torch.cuda.synchronize()
+    tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
+    zr = rows if b_sel is None else rows[b_sel]
+    if b_sel is not None:
+        tok, lp = tok[b_sel], lp[b_sel]
+    o = oracle.sample_draft(synth.to_oracle(zr.contiguous()), seed, rnd, T, pos0=pos0 if b_sel is None else pos0,
+                            query=tok)
+    if b_sel is not None:  # the oracle numbered the selected sequences 0..; redo with their own uniforms
+        u = oracle.sample_draft(synth.to_oracle(rows.contiguous()), seed, rnd, T, pos0=pos0)["u"][b_sel]
+        o = oracle.sample_draft(synth.to_oracle(zr.contiguous()), seed, rnd, T, u=u, query=tok)
+    bad = o["tokens"] < 0
+    assert np.array_equal(tok[bad], o["tokens"][bad]) and np.isnan(lp[bad]).all(), f"{name}: bad rows"
+    ok = ~bad
+    band = 1e-9 * o["W"][ok]
+    inside = (o["qedge_lo"][ok] - band <= o["target"][ok]) & (o["target"][ok] < o["qedge_hi"][ok] + band)
+    assert inside.all(), f"{name}: {int((~inside).sum())} draws outside their CDF interval"
+    exact = (tok[ok] == o["tokens"][ok])
+    d = np.abs(lp[ok] - o["logprob"][ok])
+    assert d.max(initial=0.0) < 1e-9, f"{name}: logprob error {d.max()}"
+    log(f"[parity] draft {name}: draws={int(ok.sum())} exact={int(exact.sum())} excused={int((~exact).sum())} "
+        f"bad_rows={int(bad.sum())} max_logprob_err={d.max(initial=0.0):.2e}")
+    return tok, lp
+
+
+def test_draft_sampler_parity():
+    """Reduced sizes: ragged V (not a multiple of the 2048-logit chunk, nor
+    of the 16-byte vector), unaligned rows, both dtypes, two temperatures,
+    and bad rows."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    w = W["c3"]
+    for dt, V, T in (("bf16", 30001, 1.0), ("f32", 4097, 0.7), ("bf16", 2048, 0.8), ("bf16", 5, 1.0)):
+        zq = synth.verifier_logits(w.with_sizes(V=V), 24 * 3, g, "cuda").view(24, 3, V)
+        rows = zq.to(torch.bfloat16 if dt == "bf16" else torch.float32)
+        _draft_case(f"{dt}_V{V}_T{T}", rows, T, seed=31, rnd=4, pos0=2)
+    # unaligned rows: a bf16 row stride of V + 1 elements
+    V = 3001
+    big = synth.verifier_logits(w.with_sizes(V=V + 1), 16 * 2, g, "cuda").view(16, 2, V + 1).to(torch.bfloat16)
+    _draft_case("bf16_unaligned", big[:, :, 1:], 1.0, seed=2, rnd=9)
+    # bad rows
+    rows = synth.verifier_logits(w.with_sizes(V=4096), 6, g, "cuda").view(3, 2, 4096).to(torch.bfloat16)
+    rows[0, 1, 17] = float("nan")
+    rows[1, 0, 4000] = float("inf")
+    rows[2, 1, :] = float("-inf")
+    tok, _ = _draft_case("bad_rows", rows, 1.0, seed=3, rnd=3)
+    assert tok[0, 1] == -1 and tok[1, 0] == -1 and tok[2, 1] == -1 and (tok[[0, 1, 2], [0, 1, 0]] >= 0).all()
+    log("[done] draft parity")
+
+
+def test_draft_sampler_full_size_sampled():
+    """Config 3's draft rows at full size (B=256, 7 positions, V=128256
+    bf16): every draw in range, and the oracle checks 48 sequences."""
+    w = W["c3"]
+    inp = synth.chain_inputs(w, seed=12, device="cuda")
+    rows = inp["zp"]
+    sel = np.arange(0, w.B, w.B // 48)[:48]
+    tok, lp = _draft_case("c3_full", rows, w.T, seed=77, rnd=1, b_sel=sel)
+    log("[done] draft full size")
+
+
+def test_draft_sampler_law():
+    """One row repeated over 8192 sequences (sequence stride 0), 4 rounds:
+    the device's draws fit softmax(z/T) (chi-square, p > 1e-4)."""
+    import rejection_sampling_verify_14_amd as sv
+    from scipy.stats import chisquare
+    V, n = 6, 8192
+    z = torch.tensor([[0.3, -1.0, 2.0, 0.0, 1.2, -0.4]], device="cuda").to(torch.bfloat16)
+    rows = z.view(1, 1, V).expand(n, 1, V)
+    counts = np.zeros(V)
+    for rnd in range(4):
+        tok, _ = sv.sample_draft(rows, 123, rnd, 0.9, logprob=False)
+        counts += np.bincount(tok.cpu().numpy().ravel(), minlength=V)
+    p = torch.softmax(z.double().cpu().view(-1) / float(np.float32(0.9)), dim=0).numpy()
+    stat, pv = chisquare(counts, counts.sum() * p)
+    log(f"[law] draft sampler chi2={stat:.2f} p={pv:.3g}")
+    assert pv > 1e-4
+
+
 def test_tree_edge_cases():
     """Root-only tree (bonus from q_root), a bad parent, a walk deeper than
     max_depth, NaN in an internal row -- per-sequence -1 flags."""
