@@ -20,6 +20,7 @@ host's cores on a bounded sample (cpu_baseline).
   python bench.py --copy-calibration     # plain copy of known size, for PMC scaling
   python bench.py --tree-mask | --tree-build   # the tree kernels on config 5
   python bench.py --walk-compare          # exercise 3: [2,2,2] tree vs 14-draft chain
+  python bench.py --draft-sample          # sv_sample_draft on config 3's draft rows
 """
 from __future__ import annotations
 
@@ -403,6 +404,43 @@ def walk_compare_bench(rounds: int):
             **res}), flush=True)
 
 
+def draft_sample_bench(steps: int, warmup: int):
+    """sv_sample_draft on config 3's draft rows (B=256, V=128256 bf16, T=1):
+    all 7 positions in one call, and one position (the autoregressive
+    step).  One JSON line each; the HBM roofline counts every row read once."""
+    import torch
+
+    import rejection_sampling_verify_14_amd as sv
+    import synth
+
+    w = synth.WORKLOADS["c3"]
+    rows = synth.chain_inputs(w, seed=5, device="cuda")["zp"]
+    hip = Hip()
+    hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    for R in (w.N, 1):
+        x = rows[:, :R]
+        for _ in range(warmup):
+            sv.sample_draft(x, 1, 0, w.T)
+        a, b = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.lib.hipEventRecord(ctypes.c_void_p(a), ctypes.c_void_p(stream.cuda_stream))
+        for i in range(steps):
+            sv.sample_draft(x, 1, i, w.T)
+        hip.lib.hipEventRecord(ctypes.c_void_p(b), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(a, b) * 1000.0 / steps
+        nbytes = w.B * R * w.V * x.element_size()
+        gbps = nbytes / us / 1e3
+        print(json.dumps({
+            "metric": "draft tokens sampled/s", "value": round(w.B * R / us * 1e6, 1), "unit": "tokens/s",
+            "us_per_call": round(us, 2), "steps": steps, "warmup": warmup, "higher_is_better": True,
+            "data": "synthetic",
+            "config": {"workload": f"draft sampling B={w.B} positions={R} V={w.V} bf16 T={w.T}"},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbps / 8000.0, 4), "bytes_per_call": nbytes}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +453,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
     ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on config 5 rows instead")
+    ap.add_argument("--draft-sample", action="store_true", help="time sv_sample_draft on config 3's draft rows")
     ap.add_argument("--walk-compare", action="store_true",
                     help="exercise 3: [2,2,2] tree (both walks) vs a 14-draft chain, tokens per verifier call")
     args = ap.parse_args()
@@ -437,6 +476,9 @@ def main():
         return
     if args.tree_build:
         tree_build_bench(args.steps, args.warmup)
+        return
+    if args.draft_sample:
+        draft_sample_bench(args.steps, args.warmup)
         return
     if args.walk_compare:
         walk_compare_bench(rounds=8)

@@ -17,17 +17,16 @@
 
 namespace sv {
 
-constexpr int kDraftWaves = 8;
-constexpr int kDraftBlock = kDraftWaves * 64;
-constexpr int kDraftPerLane = 32;                    // logits per lane per chunk
-constexpr int kDraftChunk = 64 * kDraftPerLane;      // 2048 logits per chunk (one wave)
-constexpr int kDraftMaxChunks = 256;                 // V <= 524288
+constexpr int kDraftPerLane = 16;                    // logits per lane per chunk
+constexpr int kDraftChunk = 64 * kDraftPerLane;      // 1024 logits per chunk (one wave)
+constexpr int kDraftMaxChunks = 512;                 // V <= 524288
 
 struct DraftArgs {
     const char* rows;
     int64_t seq_stride, row_stride;  // elements
     int R, V, pos0;
     double invT;
+    float c;  // log2(e) / T
     uint64_t seed, round;
     int32_t* out_tokens;
     double* out_logprob;
@@ -107,82 +106,100 @@ __device__ __forceinline__ double wave_exclusive(double v, int lane, double* tot
 }
 
 // Block (b, r): one draw from row r of sequence b.
-//  1. Each wave takes chunks w, w + 8, ... (2048 logits, 32 contiguous per
-//     lane, the next chunk's loads in flight): the chunk's maximum m_c and
-//     s_c = sum exp((x - m_c)/T) in double (table-driven exp), into LDS.
+//  1. Each wave takes chunks w, w + NW, ... (1024 logits, 16 contiguous per
+//     lane, the next chunk's loads in flight): a reference m_c and s_c = sum
+//     of the weights 2^((x - m_c) c), c = log2(e)/T, each an fp32 exp2
+//     (about 1e-7 relative) summed in double, into LDS.
 //  2. Wave 0: M = max m_c, chunk weights s_c exp((m_c - M)/T), W, u*W, and
-//     the chunk where the running weight passes u*W (4 chunks per lane, an
+//     the chunk where the running weight passes u*W (8 chunks per lane, an
 //     exclusive scan over lanes).
-//  3. Wave 0 rescans that chunk in token order with the same weights.
+//  3. Wave 0 rescans that chunk in token order with the same weights (the
+//     same fp32 values), so the draw is the exact inverse CDF of the fp32
+//     weights: within about 1e-7 relative of the exact softmax CDF.
 // A row holding NaN or +inf, or only -inf, gives token -1 and NaN.
-template <int DT>
-__global__ __launch_bounds__(kDraftBlock) void k_draft_sample(DraftArgs A)
+// NW = 8 waves per block for large batches, 16 for small ones (a row's
+// chunks spread over more waves); at 84 VGPRs five waves fit per SIMD.
+template <int DT, int NW>
+__global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
 {
     __shared__ double s_tab[kExpTabN];
     __shared__ float s_m[kDraftMaxChunks];
     __shared__ double s_s[kDraftMaxChunks];
-    __shared__ int s_bad;
+    __shared__ float s_e[kDraftMaxChunks];
     const int row_id = blockIdx.x;
     const int b = row_id / A.R, r = row_id - b * A.R;
     const char* row = A.rows + ((int64_t)b * A.seq_stride + (int64_t)r * A.row_stride) * (DT == DT_BF16 ? 2 : 4);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int nch = (A.V + kDraftChunk - 1) / kDraftChunk;
     fill_exp_table(s_tab);
-    if (threadIdx.x == 0) s_bad = 0;
     __syncthreads();
     const lds_dptr tab = (lds_dptr)s_tab;
     const double invT = A.invT;
 
-    // 1. chunk sums
-    int bad = 0;
+    // 1. chunk sums.  The wave's reference ref (uniform) lags its running
+    // maximum by under 2 in the exponent, so most chunks skip the wave-wide
+    // maximum; a term is 2^(fma(x, c, -p)), p = RN(ref c), which is
+    // 2^((x - ref) c) times 2^e, e = ref c - p (exact in fp32), shed in
+    // step 2.  NaN and +inf reach the sum as NaN (while ref is -inf, p = 0
+    // keeps every term 0 or NaN).
+    float ref = -INFINITY, lim = -INFINITY, pf = 0.0f, ef = 0.0f;
     ChunkRegs<DT> cur, nxt;
     if (wave < nch) load_lane_chunk<DT>(row, A.V, wave, lane, cur);
-    for (int c = wave; c < nch; c += kDraftWaves) {
-        if (c + kDraftWaves < nch) load_lane_chunk<DT>(row, A.V, c + kDraftWaves, lane, nxt);
+    for (int c = wave; c < nch; c += NW) {
+        if (c + NW < nch) load_lane_chunk<DT>(row, A.V, c + NW, lane, nxt);
         float x[kDraftPerLane];
         decode_lane_chunk<DT>(cur, x);
         float lm = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < kDraftPerLane; ++j) {
-            bad |= (int)(x[j] != x[j]) | (int)(x[j] == INFINITY);
-            lm = fmaxf(lm, x[j]);
+        for (int j = 0; j < kDraftPerLane; ++j) lm = fmaxf(lm, x[j]);
+        if (__ballot(lm > lim)) {
+            const float wm = wave_max_fl(lm);
+            ref = wm;
+            lim = wm + 2.0f / A.c;
+            pf = wm * A.c;
+            ef = __builtin_fmaf(wm, A.c, -pf);
         }
-        const float m = wave_max_fl(lm);
         double s = 0.0;
-        if (m != -INFINITY) {
 #pragma unroll
-            for (int j = 0; j < kDraftPerLane; ++j) s += exp_rel(((double)x[j] - (double)m) * invT, tab);
-        }
+        for (int j = 0; j < kDraftPerLane; ++j) s += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pf));
         s = wave_sum_d(s);
         if (lane == 0) {
-            s_m[c] = m;
+            s_m[c] = ref;
+            s_e[c] = ef;
             s_s[c] = s;
         }
         cur = nxt;
     }
-    if (bad) s_bad = 1;
     __syncthreads();
     if (wave != 0) return;
 
     // 2. total weight and the chunk of the draw
     const int64_t oi = (int64_t)b * A.R + r;
     float M = -INFINITY;
-    for (int c = lane; c < nch; c += 64) M = fmaxf(M, s_m[c]);
+    int bad = 0;
+    for (int c = lane; c < nch; c += 64) {
+        M = fmaxf(M, s_m[c]);
+        bad |= s_s[c] != s_s[c];
+    }
     M = wave_max_fl(M);
-    if (s_bad || M == -INFINITY) {
+    if (__ballot(bad) || M == -INFINITY) {
         if (lane == 0) {
             A.out_tokens[oi] = -1;
             if (A.out_logprob) A.out_logprob[oi] = NAN;
         }
         return;
     }
+    // chunk c's weight: s_c 2^(-e_c) exp((ref_c - M)/T)
+    auto chunk_scale = [&](int c) {
+        return exp_rel(((double)s_m[c] - (double)M) * invT - (double)s_e[c] * 0.69314718055994530942, tab);
+    };
     constexpr int CPL = kDraftMaxChunks / 64;  // chunks per lane, consecutive
     double cw[CPL];
     double lsum = 0.0;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane * CPL + i;
-        cw[i] = (c < nch && s_m[c] != -INFINITY) ? s_s[c] * exp_rel(((double)s_m[c] - (double)M) * invT, tab) : 0.0;
+        cw[i] = (c < nch && s_m[c] != -INFINITY) ? s_s[c] * chunk_scale(c) : 0.0;
         lsum += cw[i];
     }
     double W;
@@ -218,7 +235,8 @@ __global__ __launch_bounds__(kDraftBlock) void k_draft_sample(DraftArgs A)
     cs = __shfl(cs, owner, 64);
     cbase = __shfl(cbase, owner, 64);
     const float mc = s_m[cs];
-    const double scale = exp_rel(((double)mc - (double)M) * invT, tab);
+    const float pc = mc * A.c;  // the chunk's p, as pass 1 formed it
+    const double scale = chunk_scale(cs);
     const double local = fallback ? INFINITY : (target - cbase) / scale;
 
     // 3. rescan the chunk in token order
@@ -226,13 +244,10 @@ __global__ __launch_bounds__(kDraftBlock) void k_draft_sample(DraftArgs A)
     load_lane_chunk<DT>(row, A.V, cs, lane, rr);
     float x[kDraftPerLane];
     decode_lane_chunk<DT>(rr, x);
-    double wv[kDraftPerLane];
+    // the weights are recomputed below (the same fp32 values) rather than held
     double tsum = 0.0;
 #pragma unroll
-    for (int j = 0; j < kDraftPerLane; ++j) {
-        wv[j] = exp_rel(((double)x[j] - (double)mc) * invT, tab);
-        tsum += wv[j];
-    }
+    for (int j = 0; j < kDraftPerLane; ++j) tsum += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pc));
     double ctot;
     const double tbase = wave_exclusive(tsum, lane, &ctot);
     const uint64_t cand = __ballot(tsum > 0.0 && tbase + tsum > local);
@@ -244,15 +259,16 @@ __global__ __launch_bounds__(kDraftBlock) void k_draft_sample(DraftArgs A)
         float xpick = 0.0f, xlast = 0.0f;
 #pragma unroll
         for (int j = 0; j < kDraftPerLane; ++j) {
-            if (wv[j] > 0.0) {
+            const double wj = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pc));
+            if (wj > 0.0) {
                 last = j;
                 xlast = x[j];
-                if (pick < 0 && cum + wv[j] > local) {
+                if (pick < 0 && cum + wj > local) {
                     pick = j;
                     xpick = x[j];
                 }
             }
-            cum += wv[j];
+            cum += wj;
         }
         if (pick < 0) {
             pick = last;
@@ -286,12 +302,19 @@ extern "C" int sv_sample_draft(const void* logits, int64_t seq_stride, int64_t r
     A.V = V;
     A.pos0 = pos0;
     A.invT = 1.0 / (double)temperature;
+    A.c = (float)(1.4426950408889634074 / (double)temperature);
     A.seed = seed;
     A.round = round;
     A.out_tokens = out_tokens;
     A.out_logprob = out_logprob;
     const dim3 grid((unsigned)(B * R));
-    if (dtype == SV_BF16) hipLaunchKernelGGL(sv::k_draft_sample<1>, grid, dim3(sv::kDraftBlock), 0, stream, A);
-    else hipLaunchKernelGGL(sv::k_draft_sample<0>, grid, dim3(sv::kDraftBlock), 0, stream, A);
+    const bool few = (int64_t)B * R < 512;  // under two blocks per CU: spread each row over 16 waves
+    if (dtype == SV_BF16) {
+        if (few) hipLaunchKernelGGL((sv::k_draft_sample<1, 16>), grid, dim3(1024), 0, stream, A);
+        else hipLaunchKernelGGL((sv::k_draft_sample<1, 8>), grid, dim3(512), 0, stream, A);
+    } else {
+        if (few) hipLaunchKernelGGL((sv::k_draft_sample<0, 16>), grid, dim3(1024), 0, stream, A);
+        else hipLaunchKernelGGL((sv::k_draft_sample<0, 8>), grid, dim3(512), 0, stream, A);
+    }
     return hipGetLastError() == hipSuccess ? SV_OK : SV_EHIP;
 }

@@ -306,8 +306,9 @@ def test_walk_compare_matches_its_expectations():
 
 def _draft_case(name, rows, T, seed, rnd, pos0=0, b_sel=None):
     """Device draft draws vs the oracle: every device token's CDF interval
-    holds the oracle's u*W (within a 1e-9 relative band, excused and
-    counted), the same uniform, and ln p within 1e-9."""
+    holds the oracle's u*W, up to a band of 1e-6 W (the device's weights are
+    fp32 exp2 terms, ~1e-7 relative; draws decided inside the band are
+    excused and counted), and ln p within 1e-6."""
     import rejection_sampling_verify_14_amd as sv
     log(f"[case] draft {name} rows={tuple(rows.shape)} T={T}")
     tok, lp = sv.sample_draft(rows, seed, rnd, T, pos0=pos0)
@@ -324,12 +325,12 @@ def _draft_case(name, rows, T, seed, rnd, pos0=0, b_sel=None):
     bad = o["tokens"] < 0
     assert np.array_equal(tok[bad], o["tokens"][bad]) and np.isnan(lp[bad]).all(), f"{name}: bad rows"
     ok = ~bad
-    band = 1e-9 * o["W"][ok]
+    band = 1e-6 * o["W"][ok]
     inside = (o["qedge_lo"][ok] - band <= o["target"][ok]) & (o["target"][ok] < o["qedge_hi"][ok] + band)
     assert inside.all(), f"{name}: {int((~inside).sum())} draws outside their CDF interval"
     exact = (tok[ok] == o["tokens"][ok])
     d = np.abs(lp[ok] - o["logprob"][ok])
-    assert d.max(initial=0.0) < 1e-9, f"{name}: logprob error {d.max()}"
+    assert d.max(initial=0.0) < 1e-6, f"{name}: logprob error {d.max()}"
     log(f"[parity] draft {name}: draws={int(ok.sum())} exact={int(exact.sum())} excused={int((~exact).sum())} "
         f"bad_rows={int(bad.sum())} max_logprob_err={d.max(initial=0.0):.2e}")
     return tok, lp
@@ -356,6 +357,13 @@ def test_draft_sampler_parity():
     rows[2, 1, :] = float("-inf")
     tok, _ = _draft_case("bad_rows", rows, 1.0, seed=3, rnd=3)
     assert tok[0, 1] == -1 and tok[1, 0] == -1 and tok[2, 1] == -1 and (tok[[0, 1, 2], [0, 1, 0]] >= 0).all()
+    # a NaN inside a stretch of -inf that one wave reads alone (its chunk
+    # has nothing above -inf), the row finite elsewhere
+    rows = synth.verifier_logits(w.with_sizes(V=4096), 4, g, "cuda").view(2, 2, 4096).to(torch.bfloat16)
+    rows[1, 0, 1024:] = float("-inf")
+    rows[1, 0, 2500] = float("nan")
+    tok, _ = _draft_case("nan_in_neg_inf", rows, 1.0, seed=4, rnd=1)
+    assert tok[1, 0] == -1 and (tok[0] >= 0).all() and tok[1, 1] >= 0
     log("[done] draft parity")
 
 
