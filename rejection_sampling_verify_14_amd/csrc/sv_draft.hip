@@ -107,7 +107,7 @@ __device__ __forceinline__ double wave_exclusive(double v, int lane, double* tot
 
 // Block (b, r): one draw from row r of sequence b.
 //  1. Each wave takes chunks w, w + NW, ... (1024 logits, 16 contiguous per
-//     lane, the next chunk's loads in flight): a reference m_c and s_c = sum
+//     lane, the next two chunks' loads in flight): a reference m_c and s_c = sum
 //     of the weights 2^((x - m_c) c), c = log2(e)/T, each an fp32 exp2
 //     (about 1e-7 relative) summed in double, into LDS.
 //  2. Wave 0: M = max m_c, chunk weights s_c exp((m_c - M)/T), W, u*W, and
@@ -143,12 +143,9 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
     // step 2.  NaN and +inf reach the sum as NaN (while ref is -inf, p = 0
     // keeps every term 0 or NaN).
     float ref = -INFINITY, lim = -INFINITY, pf = 0.0f, ef = 0.0f;
-    ChunkRegs<DT> cur, nxt;
-    if (wave < nch) load_lane_chunk<DT>(row, A.V, wave, lane, cur);
-    for (int c = wave; c < nch; c += NW) {
-        if (c + NW < nch) load_lane_chunk<DT>(row, A.V, c + NW, lane, nxt);
+    auto take = [&](const ChunkRegs<DT>& regs, int c) {
         float x[kDraftPerLane];
-        decode_lane_chunk<DT>(cur, x);
+        decode_lane_chunk<DT>(regs, x);
         float lm = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kDraftPerLane; ++j) lm = fmaxf(lm, x[j]);
@@ -168,7 +165,25 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
             s_e[c] = ef;
             s_s[c] = s;
         }
-        cur = nxt;
+    };
+    // three register sets, loads two chunks ahead; a set is never copied
+    // (a copy would wait for its loads), and a load past the row's chunks
+    // is skipped (wave-uniform)
+    ChunkRegs<DT> ra, rb, rc;
+    auto load = [&](ChunkRegs<DT>& regs, int c) {
+        if (c < nch) load_lane_chunk<DT>(row, A.V, c, lane, regs);
+    };
+    load(ra, wave);
+    load(rb, wave + NW);
+    for (int c = wave; c < nch; c += 3 * NW) {
+        load(rc, c + 2 * NW);
+        take(ra, c);
+        if (c + NW >= nch) break;
+        load(ra, c + 3 * NW);
+        take(rb, c + NW);
+        if (c + 2 * NW >= nch) break;
+        load(rb, c + 4 * NW);
+        take(rc, c + 2 * NW);
     }
     __syncthreads();
     if (wave != 0) return;
