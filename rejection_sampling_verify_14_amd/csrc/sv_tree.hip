@@ -451,6 +451,48 @@ __device__ __forceinline__ uint64_t double_key(double v)
 
 constexpr int kFinalizeBlock = 1024;
 
+// Bitonic sort of P (a power of two, <= the block) pairs held one per thread
+// (thread e holds element e; threads >= P hold padding that is never read)
+// into the order `first` (a precedes b).  Strides below 64 exchange inside
+// the wave by shuffles; wider ones go through LDS (s_k, s_i), with a barrier
+// on each side.  Every thread of the block calls it.
+template <typename First>
+__device__ __forceinline__ void block_bitonic(uint64_t& key, int& id, int P, uint64_t* s_k, int* s_i, First first)
+{
+    const int e = threadIdx.x;
+    for (int k = 2; k <= P; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t ko;
+            int io;
+            if (j >= 64) {
+                if (e < P) {
+                    s_k[e] = key;
+                    s_i[e] = id;
+                }
+                __syncthreads();
+                if (e < P) {
+                    ko = s_k[e ^ j];
+                    io = s_i[e ^ j];
+                }
+                __syncthreads();
+            } else {
+                ko = ((uint64_t)(uint32_t)__shfl_xor((int)(key >> 32), j, 64) << 32) |
+                     (uint32_t)__shfl_xor((int)(uint32_t)key, j, 64);
+                io = __shfl_xor(id, j, 64);
+            }
+            if (e < P) {
+                const bool lower = (e & j) == 0;
+                const uint64_t ki = lower ? key : ko, kl = lower ? ko : key;
+                const int ii = lower ? id : io, il = lower ? io : id;
+                if (first(kl, il, ki, ii) == ((e & k) == 0)) {
+                    key = ko;
+                    id = io;
+                }
+            }
+        }
+    }
+}
+
 // Block b: the kept set of sequence b -- the `budget` best candidates by
 // (score desc, id asc) -- numbered 1..budget by (level asc, score desc, id
 // asc), and the flattened tree: parents (node 0: -1), tokens (0), depth (0),
@@ -490,41 +532,66 @@ __global__ __launch_bounds__(kFinalizeBlock) void k_tree_finalize(
     }
     bad = __syncthreads_or(bad);
     // sort 1: descending by (key, -id)
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int t = tid; t < (P >> 1); t += kFinalizeBlock) {
-                const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
-                const uint64_t ki = s_key[i], kl = s_key[l];
-                const int ii = s_id[i], il = s_id[l];
-                const bool l_first = (kl > ki) | ((kl == ki) & (il < ii));
-                if (l_first == ((i & k) == 0)) {
-                    s_key[i] = kl;
-                    s_key[l] = ki;
-                    s_id[i] = il;
-                    s_id[l] = ii;
+    auto by_score = [](uint64_t ka, int ia, uint64_t kb, int ib) { return (ka > kb) | ((ka == kb) & (ia < ib)); };
+    if (P <= kFinalizeBlock) {
+        uint64_t key = tid < P ? s_key[tid] : 0;
+        int id = tid < P ? s_id[tid] : 0;
+        __syncthreads();
+        block_bitonic(key, id, P, s_key, s_id, by_score);
+        if (tid < P) {
+            s_key[tid] = key;
+            s_id[tid] = id;
+        }
+        __syncthreads();
+    } else {
+        for (int k = 2; k <= P; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int t = tid; t < (P >> 1); t += kFinalizeBlock) {
+                    const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
+                    const uint64_t ki = s_key[i], kl = s_key[l];
+                    const int ii = s_id[i], il = s_id[l];
+                    if (by_score(kl, il, ki, ii) == ((i & k) == 0)) {
+                        s_key[i] = kl;
+                        s_key[l] = ki;
+                        s_id[i] = il;
+                        s_id[l] = ii;
+                    }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
     // sort 2: the kept ranks r < budget, ascending by (level, r)
     int P2 = 1;
     while (P2 < budget) P2 <<= 1;
-    for (int r = tid; r < P2; r += kFinalizeBlock)
-        s_key[r] = r < budget ? ((uint64_t)((uint32_t)cand_level[base + s_id[r]] ^ 0x80000000u) << 32) | (uint32_t)r
-                              : ~0ull;
-    __syncthreads();
-    for (int k = 2; k <= P2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int t = tid; t < (P2 >> 1); t += kFinalizeBlock) {
-                const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
-                const uint64_t ki = s_key[i], kl = s_key[l];
-                if ((kl < ki) == ((i & k) == 0)) {
-                    s_key[i] = kl;
-                    s_key[l] = ki;
+    auto by_level = [](uint64_t ka, int, uint64_t kb, int) { return ka < kb; };
+    if (P2 <= kFinalizeBlock) {
+        uint64_t key = tid < budget ? ((uint64_t)((uint32_t)cand_level[base + s_id[tid]] ^ 0x80000000u) << 32) |
+                                          (uint32_t)tid
+                                    : ~0ull;
+        int id = 0;
+        block_bitonic(key, id, P2, s_key, s_node, by_level);  // s_node as scratch for the ids
+        __syncthreads();
+        if (tid < P2) s_key[tid] = key;
+        for (int i = tid; i < n; i += kFinalizeBlock) s_node[i] = 0;
+        __syncthreads();
+    } else {
+        for (int r = tid; r < P2; r += kFinalizeBlock)
+            s_key[r] = r < budget ? ((uint64_t)((uint32_t)cand_level[base + s_id[r]] ^ 0x80000000u) << 32) | (uint32_t)r
+                                  : ~0ull;
+        __syncthreads();
+        for (int k = 2; k <= P2; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int t = tid; t < (P2 >> 1); t += kFinalizeBlock) {
+                    const int i = ((t & ~(j - 1)) << 1) | (t & (j - 1)), l = i + j;
+                    const uint64_t ki = s_key[i], kl = s_key[l];
+                    if (by_level(kl, 0, ki, 0) == ((i & k) == 0)) {
+                        s_key[i] = kl;
+                        s_key[l] = ki;
+                    }
                 }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
     for (int q = tid; q < budget; q += kFinalizeBlock) s_node[s_id[(uint32_t)s_key[q]]] = q + 1;
