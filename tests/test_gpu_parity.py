@@ -314,14 +314,21 @@ def _draft_case(name, rows, T, seed, rnd, pos0=0, b_sel=None):
     tok, lp = sv.sample_draft(rows, seed, rnd, T, pos0=pos0)
     torch.cuda.synchronize()
     tok, lp = tok.cpu().numpy(), lp.cpu().numpy()
-    zr = rows if b_sel is None else rows[b_sel]
-    if b_sel is not None:
+    if b_sel is None:
+        o = oracle.sample_draft(synth.to_oracle(rows.contiguous()), seed, rnd, T, pos0=pos0, query=tok)
+    else:
+        # a sample of sequences: the oracle numbers them 0.., so it gets
+        # their own uniforms (Philox stream 1 at (b, pos0 + r), words 0, 1)
+        import ctypes
         tok, lp = tok[b_sel], lp[b_sel]
-    o = oracle.sample_draft(synth.to_oracle(zr.contiguous()), seed, rnd, T, pos0=pos0 if b_sel is None else pos0,
-                            query=tok)
-    if b_sel is not None:  # the oracle numbered the selected sequences 0..; redo with their own uniforms
-        u = oracle.sample_draft(synth.to_oracle(rows.contiguous()), seed, rnd, T, pos0=pos0)["u"][b_sel]
-        o = oracle.sample_draft(synth.to_oracle(zr.contiguous()), seed, rnd, T, u=u, query=tok)
+        L = oracle.lib()
+        u = np.empty(tok.shape)
+        for i, b in enumerate(b_sel):
+            for r in range(tok.shape[1]):
+                w4 = (ctypes.c_uint32 * 4)()
+                L.orc_philox_block(seed, rnd, int(b), pos0 + r, 1, w4)
+                u[i, r] = L.orc_u53(w4[0], w4[1])
+        o = oracle.sample_draft(synth.to_oracle(rows[b_sel].contiguous()), seed, rnd, T, u=u, query=tok)
     bad = o["tokens"] < 0
     assert np.array_equal(tok[bad], o["tokens"][bad]) and np.isnan(lp[bad]).all(), f"{name}: bad rows"
     ok = ~bad
