@@ -460,7 +460,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sequences are independent; "
-              "see DESIGN.md for how the step shards). Run with --gpus 1.", file=sys.stderr)
+              "a multi-GPU run would split the batch of sequences across GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
