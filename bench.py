@@ -459,7 +459,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (sequences are independent; "
+        print("bench.py measures one GPU: there is no multi-GPU path (sequences are independent; "
               "a multi-GPU run would split the batch of sequences across GPUs). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
