@@ -94,6 +94,8 @@ extern "C" int kv_compact_indices(const int32_t* path_nodes, const int32_t* num_
             (plane_stride & 15))
             return SV_EALIGN;
         if ((int64_t)row_bytes > row_stride) return SV_EINVAL;
+        // the gather's grid: planes and sequences are grid dimensions
+        if (n_planes > 0 && row_bytes > 0 && (B > 65535 || n_planes > 65535)) return SV_ESHAPE;
     }
     const int threads = 64;
     sv::k_kv_indices<<<dim3((B + threads - 1) / threads), dim3(threads), 0, stream>>>(
@@ -102,7 +104,6 @@ extern "C" int kv_compact_indices(const int32_t* path_nodes, const int32_t* num_
     if (kv && n_planes > 0 && row_bytes > 0) {
         const int ncols = row_bytes / 16;
         const dim3 grid((ncols + threads - 1) / threads, n_planes, B);
-        if (B > 65535 || n_planes > 65535) return SV_ESHAPE;
         sv::k_kv_gather<<<grid, dim3(threads), 0, stream>>>(static_cast<char*>(kv), seq_stride, row_stride, ncols,
                                                               plane_stride, max_depth, out_src_rows, out_kv_len);
         if (hipGetLastError() != hipSuccess) return SV_EHIP;

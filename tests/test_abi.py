@@ -103,6 +103,9 @@ def test_tree_and_kv_argument_errors(sv):
     assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 72, 1, 0, None) == 4
     assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 128, 1, 0, None) == 1  # row > stride
     assert kv(None, FAKE, FAKE, 0, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 0
+    # the gather's grid limits are checked before anything is launched
+    assert kv(None, FAKE, FAKE, 70000, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 64, 1, 0, None) == 3   # B > 65535
+    assert kv(None, FAKE, FAKE, 2, 3, FAKE, FAKE, FAKE, 64, 4096, 64, 64, 70000, 0, None) == 3   # n_planes > 65535
     assert L.sv_philox_uniforms(0, 0, -1, 3, FAKE, None, None) == 1
     tm = L.tree_attention_mask
     assert tm(FAKE, 1, None, 2, 1024, FAKE, FAKE, None) == 3      # T + 1 > 1024

@@ -338,8 +338,12 @@ def _draft_case(name, rows, T, seed, rnd, pos0=0, b_sel=None):
     exact = (tok[ok] == o["tokens"][ok])
     d = np.abs(lp[ok] - o["logprob"][ok])
     assert d.max(initial=0.0) < 1e-6, f"{name}: logprob error {d.max()}"
-    log(f"[parity] draft {name}: draws={int(ok.sum())} exact={int(exact.sum())} excused={int((~exact).sum())} "
+    excused = int((~exact).sum())
+    log(f"[parity] draft {name}: draws={int(ok.sum())} exact={int(exact.sum())} excused={excused} "
         f"bad_rows={int(bad.sum())} max_logprob_err={d.max(initial=0.0):.2e}")
+    # the budget of the comparison rules: excused mismatches below 1e-4 of the draws
+    assert excused == 0 or excused < compare.MISMATCH_BUDGET * int(ok.sum()), \
+        f"{name}: {excused} excused draws in {int(ok.sum())}"
     return tok, lp
 
 

@@ -61,6 +61,9 @@ MUTANTS = {
     "draft_logprob_without_T": ("logit_at(row, dtype, tok) / T - lse : NAN;", "logit_at(row, dtype, tok) - lse : NAN;"),
     "draft_wrong_row": ("const void* row = row_ptr(zp, dtype, seq_stride, row_stride, b, r);",
                         "const void* row = row_ptr(zp, dtype, seq_stride, row_stride, b, 0);"),
+    "cdf_edges_off_by_one": ("for (int t = 0; t < V && t < g; ++t) cum += w[t];",
+                             "for (int t = 0; t < V && t <= g; ++t) cum += w[t];"),
+    "cdf_edges_hi_without_token": ("*hi = (g >= 0 && g < V) ? cum + w[g] : cum;", "*hi = cum;"),
     "tree_parent_score_dropped": ("c_score[n] = f_score[f] + (top_val[r] / T - lse);", "c_score[n] = top_val[r] / T - lse;"),
 }
 
@@ -79,6 +82,7 @@ def _battery():
     yield lambda: P.test_chain_uses_documented_uniforms(oracle)
     yield lambda: P.test_residual_of_equal_rows_falls_back_to_q(oracle)
     yield lambda: P.test_inverse_cdf_edges_are_strict(oracle)
+    yield lambda: P.test_cdf_edges_of_queried_tokens(oracle)
     yield lambda: P.test_exercise4_batched_kv_length(oracle)
     yield lambda: S.test_stratified_sampling_sweep(oracle, 4)
     yield lambda: S.test_c1_every_slot_is_distributed_as_q(oracle)

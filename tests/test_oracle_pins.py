@@ -347,3 +347,53 @@ def test_inverse_cdf_edges_are_strict(orc):
     assert orc.inverse_cdf([0.0, 1.0, 0.0, 1.0], 0.0) == 1
     assert orc.inverse_cdf([0.0, 1.0, 0.0, 1.0], 0.5) == 3
     assert orc.inverse_cdf([3.0, 0.0, 0.0], TOP) == 0
+
+
+def test_cdf_edges_of_queried_tokens(orc):
+    """The CDF edges the oracle reports for a queried token (used to excuse a
+    device token that differs from the oracle's) are the running sums of the
+    distribution sampled from, just before and just after that token: for
+    the bonus (N = 0) against np.cumsum of scipy's softmax, for a rejection
+    against np.cumsum of max(0, q - p) from scipy's softmaxes, and for the
+    draft sampler against np.cumsum of softmax(z / T).  Querying the oracle's
+    own token returns its (edge_lo, edge_hi) exactly."""
+    rng = np.random.default_rng(41)
+    B, V, T = 64, 700, 0.8125
+    # bonus: q_1 sampled directly
+    zq = rng.normal(0, 3, size=(B, 1, V))
+    d0 = np.zeros((B, 0), np.int32)
+    own = orc.verify_chain(zq, np.zeros((B, 0, V)), d0, seed=3, rnd=1, T=T)
+    assert (own["sample_kind"] == orc.KIND_BONUS).all()
+    same = orc.verify_chain(zq, np.zeros((B, 0, V)), d0, seed=3, rnd=1, T=T, query=own["tokens"][:, 0])
+    assert np.array_equal(same["qedge_lo"], own["edge_lo"]) and np.array_equal(same["qedge_hi"], own["edge_hi"])
+    query = rng.integers(0, V, size=B).astype(np.int32)
+    out = orc.verify_chain(zq, np.zeros((B, 0, V)), d0, seed=3, rnd=1, T=T, query=query)
+    for b in range(B):
+        c = np.concatenate([[0.0], np.cumsum(softmax(zq[b, 0] / T))])
+        g = query[b]
+        assert abs(out["qedge_lo"][b] - c[g]) <= 1e-13 and abs(out["qedge_hi"][b] - c[g + 1]) <= 1e-13
+    # residual: one draft, rejected (the largest uniform rejects every ratio below 1)
+    zq = rng.normal(0, 2, size=(B, 2, V))
+    zp = zq[:, :1] + rng.normal(0, 1.5, size=(B, 1, V))
+    d = np.array([[int(np.argmax(zp[b, 0] - zq[b, 0]))] for b in range(B)], np.int32)  # q(d) < p(d)
+    u = np.zeros((B, 3))
+    u[:, 0] = TOP
+    u[:, 1] = rng.random(B)
+    query = rng.integers(0, V, size=B).astype(np.int32)
+    out = orc.verify_chain(zq, zp, d, seed=0, rnd=0, T=T, u=u, query=query)
+    assert (out["num_accepted"] == 0).all() and (out["sample_kind"] == orc.KIND_RESIDUAL).all()
+    for b in range(B):
+        w = np.maximum(0.0, softmax(zq[b, 0] / T) - softmax(zp[b, 0] / T))
+        c = np.concatenate([[0.0], np.cumsum(w)])
+        g = query[b]
+        assert abs(out["qedge_lo"][b] - c[g]) <= 1e-13 and abs(out["qedge_hi"][b] - c[g + 1]) <= 1e-13
+        assert abs(out["weight_total"][b] - c[-1]) <= 1e-13
+    # draft sampler
+    zd = rng.normal(0, 3, size=(8, 3, V))
+    query = rng.integers(0, V, size=(8, 3)).astype(np.int32)
+    o = orc.sample_draft(zd, seed=11, rnd=2, T=T, query=query)
+    for b in range(8):
+        for r in range(3):
+            c = np.concatenate([[0.0], np.cumsum(softmax(zd[b, r] / T))])
+            g = query[b, r]
+            assert abs(o["qedge_lo"][b, r] - c[g]) <= 1e-13 and abs(o["qedge_hi"][b, r] - c[g + 1]) <= 1e-13
