@@ -2,16 +2,18 @@
 
 A step is one verify round over one batch of synthetic inputs: for the chain
 workload (default, B=256 sequences, N=7 drafts, V=128256, bf16 logits, T=1)
-spec_verify_chain plus kv_compact_indices.  Inputs are resident in HBM before
-the timed region; the step cycles through a pool of distinct logit sets
-(8 x 0.99 GB for the chain workload, far beyond the 256 MB Infinity Cache)
-and uses a fresh Philox round per step.
+one spec_verify_chain call, which also writes the KV rows kept; tree
+workloads call spec_verify_tree (config 5 adds the in-place KV gather of
+kv_compact_indices).  Inputs are resident in HBM before the timed region;
+the step cycles through a pool of distinct logit sets (8 x 0.99 GB for the
+chain workload, far beyond the 256 MB Infinity Cache) and uses a fresh
+Philox round per step.
 
-Timing: W untimed warm-up steps, then K steps bracketed by a device
-synchronize and HIP events on the stream the library launches on.  The
-library records events around each of its two kernels in every timed step:
-the dominant one (row statistics, HBM-bound) gives the roofline line, the
-accept/sampling kernel is reported beside it.
+Timing: W untimed warm-up steps, then 5 blocks of exactly K steps, each
+bracketed by a device synchronize and HIP events on the stream the library
+launches on; the median block gives ms_per_step and every block's time is
+in the line.  One more block of K steps takes the verify kernel's own
+start/stop events (stamped by its launch) for the roofline line.
 
 Output: one JSON line (see the keys below); also the oracle timed on this
 host's cores on a bounded sample (cpu_baseline).
@@ -29,6 +31,7 @@ import ctypes
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -36,7 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k_rows_c3_pmc.json")
+REPEATS = 5             # timed blocks of K steps; the median is reported
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_verify_{workload}_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
                   for f in ("specverify.hip", "sv_device.h", "sv_exp_table.h")]
 
@@ -80,11 +84,12 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per launch of the row-statistics kernel from the committed
-    rocprofv3 PMC summary, if it was taken on the current kernel source."""
+def load_traffic(workload: str):
+    """HBM bytes per launch of the verify kernel on this workload from the
+    committed rocprofv3 PMC summary, if it was taken on the current kernel
+    source (else None: the counters no longer describe the kernel)."""
     try:
-        with open(PROFILE_PMC) as f:
+        with open(PROFILE_PMC.format(workload=workload)) as f:
             p = json.load(f)
     except (OSError, ValueError):
         return None, None
@@ -135,35 +140,69 @@ def row_kernel_bytes(w, s) -> int:
     return internal * 2 * w.V * w.elem_bytes
 
 
-def cpu_baseline(w, sets, budget_s: float):
-    """The oracle, as it stands, on this host's cores over a bounded sample of
-    the same workload; rounds/s scaled from sequences/s."""
-    import numpy as np
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def host_threads() -> int:
+    """Host threads the oracle may use: the job's allotment when the
+    environment states one (OMP_NUM_THREADS; a one-GPU job on the GPU machine is
+    allotted 16 host threads), else every core this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    try:
+        n = int(env) if env else 0
+    except ValueError:
+        n = 0
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, cores) if n > 0 else cores)
+
+
+def _oracle_rate(w, s, threads: int, budget_s: float, chunk: int):
+    """Sequences per second of the oracle over the first sequences of logit
+    set s, in calls of `chunk` sequences, for about budget_s seconds."""
     import oracle
     import synth
-    threads = min(os.cpu_count() or 1, 16)
-    s = sets[0]
     zq, zp = synth.to_oracle(s["zq"]), synth.to_oracle(s["zp"])
     done_seq, t_total, reps = 0, 0.0, 0
     B = w.B
-    chunk = min(B, max(2 * threads, 8))
+    d = s["d"].cpu().numpy() if w.kind == "chain" else None
+    if w.kind != "chain":
+        tok, par = s["tokens"].cpu().numpy(), s["parents"].cpu().numpy()
     while t_total < budget_s:
         lo = (reps * chunk) % B
         hi = min(B, lo + chunk)
         t0 = time.perf_counter()
         if w.kind == "chain":
-            oracle.verify_chain(zq, zp, s["d"].cpu().numpy(), 1, reps, w.T, b_range=(lo, hi), nthreads=threads)
+            oracle.verify_chain(zq, zp, d, 1, reps, w.T, b_range=(lo, hi), nthreads=threads)
         else:
-            oracle.verify_tree(zq, zp, s["tokens"].cpu().numpy(), s["parents"].cpu().numpy(), 1, reps, w.T,
-                               max_depth=w.depth, b_range=(lo, hi), nthreads=threads)
+            oracle.verify_tree(zq, zp, tok, par, 1, reps, w.T, max_depth=w.depth, b_range=(lo, hi), nthreads=threads)
         t_total += time.perf_counter() - t0
         done_seq += hi - lo
         reps += 1
-    rounds_per_s = (done_seq / B) / t_total
-    return {"value": rounds_per_s, "unit": "rounds/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done_seq} sequences ({done_seq / B:.3g} rounds of B={B}) of logit set 0, "
-                      f"{t_total:.1f} s, {threads} OpenMP threads; rounds/s = sequences/s / B"}
+    return done_seq, t_total
+
+
+def cpu_baseline(w, sets, budget_s: float):
+    """The oracle, as it stands, on this host's cores over a bounded sample of
+    the same workload (logit set 0); rounds/s scaled from sequences/s.  Also
+    a one-thread figure on a shorter sample."""
+    threads = host_threads()
+    B = w.B
+    n_all, t_all = _oracle_rate(w, sets[0], threads, budget_s, min(B, max(2 * threads, 8)))
+    n_one, t_one = _oracle_rate(w, sets[0], 1, min(5.0, budget_s / 3), 1)
+    return {"value": (n_all / B) / t_all, "unit": "rounds/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "one_thread_rounds_per_s": (n_one / B) / t_one,
+            "sample": f"{n_all} sequences ({n_all / B:.3g} rounds of B={B}) of logit set 0 in {t_all:.1f} s on "
+                      f"{threads} OpenMP threads (the host threads allotted to this job); one thread: {n_one} "
+                      f"sequences in {t_one:.1f} s; rounds/s = sequences/s / B"}
 
 
 def copy_calibration():
@@ -491,12 +530,12 @@ def main():
     dev = "cuda"
     B = w.B
     if w.kind == "chain":
-        outs = sv.alloc_chain_outputs(B, w.N, dev)
+        outs = sv.alloc_chain_outputs(B, w.N, dev, kv=True)
         ws = sv.alloc_workspace(sv.chain_workspace_bytes(B, w.N, w.V), dev)
         width = w.N + 1
     else:
         T = sets[0]["zq"].shape[1] - 1
-        outs = sv.alloc_tree_outputs(B, T, w.depth, dev)
+        outs = sv.alloc_tree_outputs(B, T, w.depth, dev, kv=True)
         ws = sv.alloc_workspace(sv.tree_workspace_bytes(B, T, w.V), dev)
         width = w.depth + 1
     kv_out = {"src_rows": torch.empty((B, width), dtype=torch.int32, device=dev),
@@ -509,54 +548,66 @@ def main():
     def step(i, timing=None):
         s = sets[i % pool]
         if w.kind == "chain":
-            sv.spec_verify_chain(s["zq"], s["zp"], s["d"], seed=2026, round=i, temperature=w.T, out=outs,
-                                 workspace=ws, timing=timing)
-            sv.kv_compact_indices(None, outs["num_accepted"], kv_len_in, w.N, out=kv_out)
+            sv.spec_verify_chain(s["zq"], s["zp"], s["d"], seed=2026, round=i, temperature=w.T,
+                                 kv_len_in=kv_len_in, out=outs, workspace=ws, timing=timing)
         else:
             sv.spec_verify_tree(s["zq"], s["zp"], s["tokens"], s["parents"], seed=2026, round=i, temperature=w.T,
-                                max_depth=w.depth, out=outs, workspace=ws, timing=timing)
-            sv.kv_compact_indices(outs["path_nodes"], outs["num_accepted"], kv_len_in, w.depth, kv=kv, out=kv_out)
+                                max_depth=w.depth, kv_len_in=kv_len_in, out=outs, workspace=ws, timing=timing)
+            if kv is not None:
+                sv.kv_compact_indices(outs["path_nodes"], outs["num_accepted"], kv_len_in, w.depth, kv=kv,
+                                      out=kv_out)
 
     log(f"[bench] warmup {args.warmup} steps")
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    t_begin, t_end = hip.event(), hip.event()
     stream = torch.cuda.current_stream()
     hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    # the timed steps carry no per-step events (their records would sit
-    # between the kernels); the kernel split is timed in a second pass
-    log(f"[bench] timing {K} steps")
-    torch.cuda.synchronize()
-    hip.lib.hipEventRecord(ctypes.c_void_p(t_begin), ctypes.c_void_p(stream.cuda_stream))
-    wall0 = time.perf_counter()
+    t_begin, t_end = hip.event(), hip.event()
+    # REPEATS blocks of exactly K steps, each bracketed by a synchronize and
+    # events on the library's stream; the timed steps carry no per-step
+    # events.  The reported time is the median block.
+    blocks_ms, walls = [], []
+    acc_sum = acc_n = tok_sum = tok_n = 0.0
+    nxt = args.warmup
+    for rep in range(REPEATS):
+        log(f"[bench] timing block {rep + 1}/{REPEATS} of {K} steps")
+        torch.cuda.synchronize()
+        hip.lib.hipEventRecord(ctypes.c_void_p(t_begin), ctypes.c_void_p(stream.cuda_stream))
+        wall0 = time.perf_counter()
+        for i in range(K):
+            step(nxt + i)
+        hip.lib.hipEventRecord(ctypes.c_void_p(t_end), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - wall0)
+        blocks_ms.append(hip.elapsed_ms(t_begin, t_end))
+        nxt += K
+        # acceptance of the block's last step (outputs are overwritten every step)
+        a8 = outs["accept"].float()
+        if w.kind != "chain":
+            a8 = a8[:, 1:]
+        acc_sum += float(a8.sum())
+        acc_n += a8.numel()
+        k = outs["num_accepted"]
+        tok_sum += float((k[k >= 0] + 1).sum())
+        tok_n += int((k >= 0).sum())
+    ms_step = statistics.median(blocks_ms) / K
+    # the kernel's own duration: one more block with start/stop events
+    # stamped by the kernel's launch
+    log(f"[bench] timing the kernel of {K} more steps")
+    ev = [(hip.event(), hip.event()) for _ in range(K)]
     for i in range(K):
-        step(args.warmup + i)
-    hip.lib.hipEventRecord(ctypes.c_void_p(t_end), ctypes.c_void_p(stream.cuda_stream))
+        step(nxt + i, timing=ev[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = hip.elapsed_ms(t_begin, t_end)
-    ms_step = total_ms / K
-    log(f"[bench] timing the kernels of {K} more steps")
-    ev = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
-    for i in range(K):
-        step(args.warmup + K + i, timing=ev[i])
-    torch.cuda.synchronize()
-    rows_ms = [hip.elapsed_ms(a, b) for a, b, _ in ev]
-    samp_ms = [hip.elapsed_ms(b, c) for _, b, c in ev]
-    # [begin, rows_done): the row-statistics kernel; [rows_done, end): the
-    # sample step (chains: accept, chunk sums, final; trees: one kernel)
-    k_mean = sum(rows_ms) / K
-    s_mean = sum(samp_ms) / K
+    kern_ms = [hip.elapsed_ms(a, b) for a, b in ev]
+    k_mean = sum(kern_ms) / K
     per_set = [algorithmic_bytes(w, s) for s in sets]
     full_bytes = sum(per_set) / len(per_set)
-    row_bytes = sum(row_kernel_bytes(w, s) for s in sets) / len(sets)
     rounds_per_s = 1000.0 / ms_step
     eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
-    k_gbps = row_bytes / (k_mean * 1e-3) / 1e9
-    acc = outs["num_accepted"].float()
-    traffic, pmc = load_traffic() if w.name == "c3" else (None, None)
+    k_gbps = full_bytes / (k_mean * 1e-3) / 1e9
+    traffic, pmc = load_traffic(w.name)
     result = {
         "metric": "verified rounds/s + achieved HBM GB/s (% peak), B=256 N=7 V=128256",
         "value": round(rounds_per_s, 2),
@@ -576,14 +627,18 @@ def main():
                          "c4": "static 26-node tree verify B=32 V=128256 bf16 logits T=1.0",
                          "c5": "dynamic 61-node tree verify B=128 V=152064 bf16 T=0.7 + KV gather"}[w.name],
             "logits": w.dtype, "B": B, "V": w.V, "pool_sets": pool,
-            "arithmetic": "row statistics f32 (f64 accumulation), accept ratio and sampled rows f64",
+            "arithmetic": "row statistics f32 exp2 summed in f64; accept ratio and sampled rows f64",
+            "step": "one spec_verify_* launch (KV rows included)" + (" + the in-place KV gather" if kv is not None
+                                                                      else ""),
         },
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(full_bytes),
-        "mean_accepted": round(float(acc[acc >= 0].mean()), 4),
+        "block_ms_per_step": [round(t / K, 5) for t in blocks_ms],
+        "alpha_measured": round(acc_sum / max(acc_n, 1), 4),
+        "tokens_per_round": round(tok_sum / max(tok_n, 1), 4),
         "roofline": {
-            "kernel": "k_rows (row statistics)",
+            "kernel": "k_verify (row statistics, accept and sampling in one launch)",
             "bound": "hbm",
             "achieved": round(k_gbps, 1),
             "peak": PEAK_HBM_GBPS,
@@ -591,10 +646,9 @@ def main():
             "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "kernel_ms": round(k_mean, 5),
-            "algorithmic_bytes_per_launch": int(row_bytes),
+            "algorithmic_bytes_per_launch": int(full_bytes),
         },
-        "sample_step_ms": round(s_mean, 5),
-        "wall_s_timed": round(wall, 3),
+        "wall_s_timed": round(sum(walls), 3),
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_budget:.0f} s of oracle work)")

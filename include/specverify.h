@@ -35,16 +35,23 @@
  *     the block at position n; the sampling uniform of slot s is the one of
  *     words 2,3 of the block at position s.  A call is a pure function of its
  *     inputs and (seed, round).
+ *   - Workspace (verify calls): caller-owned device memory, ZERO-FILLED once
+ *     before its first use.  Each call tags its records and counters with
+ *     its own number (the low word of a 64-bit call counter that starts at a
+ *     value drawn when the library is loaded), so after that single zero
+ *     fill a workspace is reused as is by any later call (chain or tree, any
+ *     sizes that fit).  A record or counter left by an earlier call is
+ *     recognised as stale unless its call's number matches this one's in the
+ *     low 32 bits.
  *   - Reentrant; calls on different streams may overlap as long as they use
- *     different workspaces and outputs.  The only process-wide state is a
- *     call counter (an atomic) that tags each call's results, and cached
- *     occupancy figures.
+ *     different workspaces and outputs.  The only process-wide state is that
+ *     call counter (an atomic) and cached occupancy figures.
  *   - A chain verify call is three kernel launches (row statistics, accept,
  *     chunk sums with the final step in the same grid); a tree verify call
- *     is two (row statistics, accept and sampling).  Row statistics are summed per fixed segment of
- *     about 32K tokens and combined in segment order, so results do not
- *     depend on the device's compute-unit count.
- */
+ *     is two (row statistics, accept and sampling).  Row statistics are
+ *     summed per fixed segment of about 32K tokens and combined in segment
+ *     order, so results do not depend on the device's compute-unit count.
+  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
 
@@ -76,15 +83,12 @@ enum sv_walk {
                                    child is tried; its rejection ends the walk */
 };
 
-/* Optional timing hook: when non-NULL, `begin` and `rows_done` are the
- * start and stop events of the row-statistics kernel (stamped by that
- * kernel's own start and end on `stream`), and `end`, when non-NULL, is
- * recorded right after the kernels of the sample step, so a caller can time
- * the row kernel and the sample step.  The `end` record sits between
- * kernels on the stream; timing costs a few microseconds a call. */
+/* Optional timing hook: when non-NULL, `begin` (if not NULL) is stamped by
+ * the start of the call's first kernel and `end` (if not NULL) by the end of
+ * its last kernel on `stream`, so a caller can time the call without events
+ * between its kernels. */
 typedef struct sv_timing {
     hipEvent_t begin;
-    hipEvent_t rows_done;
     hipEvent_t end;
 } sv_timing;
 
@@ -126,20 +130,27 @@ size_t sv_tree_workspace_bytes(int B, int T, int V);
  *   out_probs         [B, N, 2] float: (q_i(d_i), p_i(d_i)).
  *   out_residual_mass [B] double: sum_t (q_{k+1}(t) - p_{k+1}(t))_+ after a
  *                     rejection, 0 after the bonus.
+ * KV rows ([PT] Implementando, Passo 4: after the round the KV cache keeps
+ * the pending token and the k accepted drafts), optional: kv_len_in [B]
+ * int32 is L0, the KV row of the pending token (position 0); the verify
+ * pass wrote position i at row L0 + i.  out_src_rows [B, N+1] int32 gets
+ * L0 + i for i <= k and -1 after; out_kv_len [B] int32 gets L0 + k + 1.  A
+ * failed sequence gets -1 rows and keeps L0.  kv_len_in is required when
+ * either output is given (SV_EINVAL otherwise); these are the values
+ * kv_compact_indices(NULL, ...) computes, without its launch.
  * Sampling is an inverse CDF in token-id order: the first token whose
  * running weight exceeds u*W, W the total weight, accumulated in double.
  * workspace: device memory of at least sv_chain_workspace_bytes(B, N, V)
- * bytes, 16-byte aligned, ZERO-FILLED before its first use.  It holds
- * per-call records and counters tagged with the call, so after that single
- * zero fill it is reused as is (with any B, N, V that fit).  Calls that
- * overlap in time must use different workspaces.
+ * bytes, 16-byte aligned, zero-filled before its first use (see the
+ * conventions above).
  */
 int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
                       const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
                       const int32_t* draft_tokens, int B, int N, int V, uint64_t seed, uint64_t round,
                       float temperature, int32_t* out_tokens, int32_t* out_num_accepted, int8_t* out_accept,
-                      float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
-                      const sv_timing* timing, hipStream_t stream);
+                      float* out_probs, double* out_residual_mass, const int32_t* kv_len_in, int32_t* out_src_rows,
+                      int32_t* out_kv_len, void* workspace, size_t workspace_bytes, const sv_timing* timing,
+                      hipStream_t stream);
 
 /*
  * spec_verify_tree -- one verify round over B flattened draft trees ([ZH]
@@ -183,6 +194,11 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  *   out_probs         [B, T+1, 2] float: (q_par(tok_n), p_par(tok_n)), node 0
  *                     (0, 0).
  *   out_residual_mass [B] double, as for chains.
+ * KV rows, optional, as for chains with the path: node n was written at row
+ * L0 + n, so out_src_rows [B, max_depth+1] gets L0 + path_nodes[i] for
+ * i <= k ([ZH] section 3: the accepted path's rows are kept and moved
+ * together) and out_kv_len L0 + k + 1; the in-place gather of the KV rows
+ * themselves is kv_compact_indices.
  * workspace: at least sv_tree_workspace_bytes(B, T, V) bytes, zero-filled
  * before first use, as for chains.
  */
@@ -191,8 +207,9 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
                      const int32_t* node_tokens, const int32_t* parents, int parents_shared, int B, int T, int V,
                      int max_depth, int walk, uint64_t seed, uint64_t round, float temperature,
                      int32_t* out_tokens, int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept,
-                     float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
-                     const sv_timing* timing, hipStream_t stream);
+                     float* out_probs, double* out_residual_mass, const int32_t* kv_len_in, int32_t* out_src_rows,
+                     int32_t* out_kv_len, void* workspace, size_t workspace_bytes, const sv_timing* timing,
+                     hipStream_t stream);
 
 /*
  * kv_compact_indices -- KV rollback and compaction after a verify round

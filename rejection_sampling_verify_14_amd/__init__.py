@@ -48,7 +48,7 @@ class SpecVerifyError(RuntimeError):
 
 
 class SvTiming(ctypes.Structure):
-    _fields_ = [("begin", ctypes.c_void_p), ("rows_done", ctypes.c_void_p), ("end", ctypes.c_void_p)]
+    _fields_ = [("begin", ctypes.c_void_p), ("end", ctypes.c_void_p)]
 
 
 _L = None
@@ -72,10 +72,12 @@ def _lib():
         L.sv_tree_workspace_bytes.argtypes = [i32, i32, i32]
         L.spec_verify_chain.restype = i32
         L.spec_verify_chain.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, u64, u64,
-                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
+                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        ctypes.POINTER(SvTiming), vp]
         L.spec_verify_tree.restype = i32
         L.spec_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, i32, u64, u64,
-                                       ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, sz, ctypes.POINTER(SvTiming), vp]
+                                       ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                       ctypes.POINTER(SvTiming), vp]
         L.kv_compact_indices.restype = i32
         L.kv_compact_indices.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, i32, i64, i64, i32, i32, i64, vp]
         L.tree_expand.restype = i32
@@ -91,7 +93,7 @@ def _lib():
         L.sv_sample_draft.restype = i32
         L.sv_sample_draft.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, u64, u64, i32, vp, vp, vp]
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
-        if L.sv_abi_version() != 3:
+        if L.sv_abi_version() != 4:
             raise ImportError("libspecverify.so ABI version mismatch")
         _L = L
     return _L
@@ -127,14 +129,10 @@ def _check_logits(t: torch.Tensor, name: str):
 
 
 def _timing(timing):
-    """(begin, end) or (begin, rows_done, end) hipEvent_t handles, or None."""
+    """(begin, end) hipEvent_t handles stamped by the call's kernel, or None."""
     if timing is None:
         return None
-    if len(timing) == 2:
-        t = SvTiming(timing[0], None, timing[1])
-    else:
-        t = SvTiming(timing[0], timing[1], timing[2])
-    return ctypes.byref(t)
+    return ctypes.byref(SvTiming(timing[0], timing[1]))
 
 
 def chain_workspace_bytes(B: int, N: int, V: int) -> int:
@@ -146,9 +144,10 @@ def tree_workspace_bytes(B: int, T: int, V: int) -> int:
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled workspace (the library's counters start at zero and
-    every call leaves them zero, so one workspace serves any number of
-    calls)."""
+    """A zero-filled workspace.  Zero-filled once: each call tags its records
+    and counters with the workspace's count of finished calls (its first
+    word) and stores the new count at its end, so one workspace serves any
+    number of later calls without being cleared again."""
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
@@ -160,23 +159,30 @@ def _workspace(nbytes: int, device, workspace):
     return alloc_workspace(nbytes, device)
 
 
-def alloc_chain_outputs(B: int, N: int, device):
-    return {
+def alloc_chain_outputs(B: int, N: int, device, kv: bool = False):
+    o = {
         "tokens": torch.empty((B, N + 1), dtype=torch.int32, device=device),
         "num_accepted": torch.empty(B, dtype=torch.int32, device=device),
         "accept": torch.empty((B, N), dtype=torch.int8, device=device),
         "probs": torch.empty((B, N, 2), dtype=torch.float32, device=device),
         "residual_mass": torch.empty(B, dtype=torch.float64, device=device),
     }
+    if kv:
+        o["src_rows"] = torch.empty((B, N + 1), dtype=torch.int32, device=device)
+        o["kv_len"] = torch.empty(B, dtype=torch.int32, device=device)
+    return o
 
 
 def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor], draft_tokens: torch.Tensor,
-                      seed: int, round: int, temperature: float = 1.0, *, out: Optional[dict] = None,
-                      workspace: Optional[torch.Tensor] = None, timing=None, stream=None) -> dict:
+                      seed: int, round: int, temperature: float = 1.0, *, kv_len_in: Optional[torch.Tensor] = None,
+                      out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, timing=None,
+                      stream=None) -> dict:
     """Verify B chains: target_logits [B, N+1, V], draft_logits [B, N, V]
     (float32 or bfloat16), draft_tokens [B, N] int32.  Returns (or fills)
     a dict with tokens [B, N+1], num_accepted [B], accept [B, N] (int8),
-    probs [B, N, 2] (q(d), p(d)) and residual_mass [B]."""
+    probs [B, N, 2] (q(d), p(d)) and residual_mass [B]; with kv_len_in
+    (int32 [B], the KV row of the pending token) also src_rows [B, N+1] and
+    kv_len [B], the KV rows kept."""
     _check_logits(target_logits, "target_logits")
     B, N1, V = target_logits.shape
     N = N1 - 1
@@ -187,7 +193,8 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.
         if draft_tokens.shape != (B, N) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
             raise ValueError("draft_tokens must be a contiguous int32 [B, N] tensor")
     dev = target_logits.device
-    o = out if out is not None else alloc_chain_outputs(B, N, dev)
+    o = out if out is not None else alloc_chain_outputs(B, N, dev, kv=kv_len_in is not None)
+    _check_kv(kv_len_in, o, B)
     nbytes = chain_workspace_bytes(B, N, V)
     ws = _workspace(nbytes, dev, workspace)
     dl = draft_logits if N > 0 else None
@@ -196,15 +203,15 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.
         _p(dl), dl.stride(0) if dl is not None else 0, dl.stride(1) if dl is not None else 0,
         _dtype_code(target_logits), _p(draft_tokens) if N > 0 else None, B, N, V, seed & (2 ** 64 - 1),
         round & (2 ** 64 - 1), float(temperature), _p(o["tokens"]), _p(o["num_accepted"]), _p(o.get("accept")),
-        _p(o.get("probs")), _p(o.get("residual_mass")), _p(ws), ws.numel() * ws.element_size(), _timing(timing),
-        _stream(stream))
+        _p(o.get("probs")), _p(o.get("residual_mass")), *_kv_args(kv_len_in, o), _p(ws),
+        ws.numel() * ws.element_size(), _timing(timing), _stream(stream))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_chain")
     return o
 
 
-def alloc_tree_outputs(B: int, T: int, max_depth: int, device):
-    return {
+def alloc_tree_outputs(B: int, T: int, max_depth: int, device, kv: bool = False):
+    o = {
         "tokens": torch.empty((B, max_depth + 1), dtype=torch.int32, device=device),
         "path_nodes": torch.empty((B, max_depth + 1), dtype=torch.int32, device=device),
         "num_accepted": torch.empty(B, dtype=torch.int32, device=device),
@@ -212,12 +219,31 @@ def alloc_tree_outputs(B: int, T: int, max_depth: int, device):
         "probs": torch.empty((B, T + 1, 2), dtype=torch.float32, device=device),
         "residual_mass": torch.empty(B, dtype=torch.float64, device=device),
     }
+    if kv:
+        o["src_rows"] = torch.empty((B, max_depth + 1), dtype=torch.int32, device=device)
+        o["kv_len"] = torch.empty(B, dtype=torch.int32, device=device)
+    return o
+
+
+def _check_kv(kv_len_in, o, B):
+    if kv_len_in is None:
+        return
+    if kv_len_in.shape != (B,) or kv_len_in.dtype != torch.int32 or not kv_len_in.is_contiguous():
+        raise ValueError("kv_len_in must be a contiguous int32 [B] tensor")
+    if "src_rows" not in o or "kv_len" not in o:
+        raise ValueError("out must hold src_rows and kv_len when kv_len_in is given")
+
+
+def _kv_args(kv_len_in, o):
+    if kv_len_in is None:
+        return None, None, None
+    return _p(kv_len_in), _p(o["src_rows"]), _p(o["kv_len"])
 
 
 def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, node_tokens: torch.Tensor,
                      parents: torch.Tensor, seed: int, round: int, temperature: float = 1.0, *, max_depth: int,
-                     walk: int = 0, out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
-                     timing=None, stream=None) -> dict:
+                     walk: int = 0, kv_len_in: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                     workspace: Optional[torch.Tensor] = None, timing=None, stream=None) -> dict:
     """Verify B flattened trees: logits [B, T+1, V] per node, node_tokens
     [B, T+1] int32, parents [T+1] (shared) or [B, T+1] int32.  walk 0
     (SV_WALK_FIRST_ACCEPTED) descends into the first accepted child; walk 1
@@ -233,7 +259,8 @@ def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, no
     if parents.dtype != torch.int32 or not parents.is_contiguous() or parents.shape not in ((nn,), (B, nn)):
         raise ValueError("parents must be a contiguous int32 [T+1] or [B, T+1] tensor")
     dev = target_logits.device
-    o = out if out is not None else alloc_tree_outputs(B, T, max_depth, dev)
+    o = out if out is not None else alloc_tree_outputs(B, T, max_depth, dev, kv=kv_len_in is not None)
+    _check_kv(kv_len_in, o, B)
     nbytes = tree_workspace_bytes(B, T, V)
     ws = _workspace(nbytes, dev, workspace)
     rc = _lib().spec_verify_tree(
@@ -241,8 +268,8 @@ def spec_verify_tree(target_logits: torch.Tensor, draft_logits: torch.Tensor, no
         draft_logits.stride(0), draft_logits.stride(1), _dtype_code(target_logits), _p(node_tokens), _p(parents),
         1 if parents.dim() == 1 else 0, B, T, V, max_depth, int(walk), seed & (2 ** 64 - 1), round & (2 ** 64 - 1),
         float(temperature), _p(o["tokens"]), _p(o["path_nodes"]), _p(o["num_accepted"]), _p(o.get("accept")),
-        _p(o.get("probs")), _p(o.get("residual_mass")), _p(ws), ws.numel() * ws.element_size(), _timing(timing),
-        _stream(stream))
+        _p(o.get("probs")), _p(o.get("residual_mass")), *_kv_args(kv_len_in, o), _p(ws),
+        ws.numel() * ws.element_size(), _timing(timing), _stream(stream))
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_tree")
     return o

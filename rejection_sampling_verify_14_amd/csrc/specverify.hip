@@ -48,6 +48,8 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <chrono>
+#include <random>
 
 #include "sv_device.h"
 #include "specverify.h"
@@ -313,6 +315,9 @@ struct VerifyParams {
     int8_t* out_acc;
     float* out_probs;
     double* out_resid;
+    const int32_t* kv_len_in;
+    int32_t* out_src_rows;
+    int32_t* out_kv_len;
 };
 
 // ~0.5 s of polling; never reached (every record waited for is stored by a
@@ -1201,7 +1206,12 @@ __device__ void emit_accepted(const VerifyParams& P, int b, int k, const int32_t
         }
         if (i != k) P.out_tokens[(int64_t)b * width + i] = t;
         if (TREE) P.out_path[(int64_t)b * width + i] = pn;
+        if (P.out_src_rows) {
+            const int node = TREE ? pn : (i <= k ? i : -1);
+            P.out_src_rows[(int64_t)b * width + i] = node >= 0 ? P.kv_len_in[b] + node : -1;
+        }
     }
+    if (threadIdx.x == 0 && P.out_kv_len) P.out_kv_len[b] = P.kv_len_in[b] + k + 1;
 }
 
 // Block-wide: the outputs of sequence b.  k < 0 or token < 0 marks the
@@ -1227,10 +1237,17 @@ __device__ void emit(const VerifyParams& P, int b, int k, int token, double resi
         }
         P.out_tokens[(int64_t)b * width + i] = t;
         if (TREE) P.out_path[(int64_t)b * width + i] = pn;
+        if (P.out_src_rows) {
+            const int node = !ok ? -1 : TREE ? pn : (i <= k ? i : -1);
+            P.out_src_rows[(int64_t)b * width + i] = node >= 0 ? P.kv_len_in[b] + node : -1;
+        }
     }
     if (threadIdx.x == 0) {
         P.out_num[b] = ok ? k : -1;
         if (P.out_resid) P.out_resid[b] = ok ? resid : 0.0;
+        // the KV cache keeps the pending token and the k accepted drafts; a
+        // failed sequence keeps its length
+        if (P.out_kv_len) P.out_kv_len[b] = P.kv_len_in[b] + (ok ? k + 1 : 0);
     }
 }
 
@@ -1763,12 +1780,25 @@ int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
     return SV_OK;
 }
 
-std::atomic<uint32_t> g_epoch{0};
+// Calls are numbered by a 64-bit counter that starts at a value drawn when
+// the library is loaded (so a reloaded library does not repeat the numbers
+// of the instance before it); records and counters carry the low word.
+uint64_t epoch_start()
+{
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    const uint64_t a = (uint64_t)(uintptr_t)&t;
+    uint64_t x = t ^ (a << 17) ^ (uint64_t)std::random_device{}();
+    x ^= x >> 33;
+    x *= 0xff51afd7ed558ccdull;
+    x ^= x >> 33;
+    return x;
+}
+std::atomic<uint64_t> g_epoch{epoch_start()};
 uint32_t next_epoch()
 {
     uint32_t e;
     do {
-        e = g_epoch.fetch_add(1) + 1;
+        e = (uint32_t)(g_epoch.fetch_add(1) + 1);
     } while (e == 0);
     return e;
 }
@@ -1797,8 +1827,9 @@ void set_groups(sv::VerifyParams& P)
 template <int DT, bool TREE>
 void launch_rows(const sv::VerifyParams& P, int64_t grid, const sv_timing* timing, hipStream_t stream)
 {
-    const hipEvent_t t0 = timing ? timing->begin : nullptr, t1 = timing ? timing->rows_done : nullptr;
-    hipExtLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)grid), dim3(sv::kBlock), 0, stream, t0, t1, 0, P);
+    const hipEvent_t t0 = timing ? timing->begin : nullptr;
+    hipExtLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)grid), dim3(sv::kBlock), 0, stream, t0, nullptr, 0,
+                          P);
 }
 
 // Chains: the row kernel, then the sample step (accept; chunk sums and final).
@@ -1813,10 +1844,9 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
     launch_rows<DT, false>(P, (int64_t)P.B * P.r_items, timing, stream);
     hipLaunchKernelGGL((sv::k_accept<DT>), dim3(B), dim3(64), 0, stream, P);
     // chunk-sum blocks, then one final-step block per sequence
-    hipLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
-                       stream, P);
+    hipExtLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
+                          stream, nullptr, timing ? timing->end : nullptr, 0, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -1828,15 +1858,10 @@ int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream
     // at least one row block: the row kernel also fills the exp table
     const int64_t row_grid = (int64_t)P.B * P.r_items;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
-    if (row_grid > 0) {
-        launch_rows<DT, true>(P, row_grid, timing, stream);
-    } else if (timing) {
-        if (timing->begin && hipEventRecord(timing->begin, stream) != hipSuccess) return SV_EHIP;
-        if (timing->rows_done && hipEventRecord(timing->rows_done, stream) != hipSuccess) return SV_EHIP;
-    }
-    hipLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, P);
+    launch_rows<DT, true>(P, row_grid, timing, stream);
+    hipExtLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, nullptr,
+                          timing ? timing->end : nullptr, 0, P);
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
-    if (timing && timing->end && hipEventRecord(timing->end, stream) != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
 
@@ -1888,7 +1913,7 @@ bool item_count_ok(int B, int rows, int V)
 
 extern "C" {
 
-int sv_abi_version(void) { return 3; }
+int sv_abi_version(void) { return 4; }
 
 const char* sv_status_string(int status)
 {
@@ -1920,8 +1945,9 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
                       const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
                       const int32_t* draft_tokens, int B, int N, int V, uint64_t seed, uint64_t round,
                       float temperature, int32_t* out_tokens, int32_t* out_num_accepted, int8_t* out_accept,
-                      float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
-                      const sv_timing* timing, hipStream_t stream)
+                      float* out_probs, double* out_residual_mass, const int32_t* kv_len_in, int32_t* out_src_rows,
+                      int32_t* out_kv_len, void* workspace, size_t workspace_bytes, const sv_timing* timing,
+                      hipStream_t stream)
 {
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
     if (B < 0 || N < 0 || V < 1 || !(temperature > 0.0f) || !(temperature < INFINITY)) return SV_EINVAL;
@@ -1929,6 +1955,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     if (B == 0) return SV_OK;
     if (!target_logits || !out_tokens || !out_num_accepted) return SV_EINVAL;
     if (N > 0 && (!draft_logits || !draft_tokens)) return SV_EINVAL;
+    if ((out_src_rows || out_kv_len) && !kv_len_in) return SV_EINVAL;
     const int es = dtype == SV_BF16 ? 2 : 4;
     int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
     if (rc) return rc;
@@ -1959,6 +1986,9 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     P.out_acc = out_accept;
     P.out_probs = out_probs;
     P.out_resid = out_residual_mass;
+    P.kv_len_in = kv_len_in;
+    P.out_src_rows = out_src_rows;
+    P.out_kv_len = out_kv_len;
     return launch_verify<false>(P, dtype, workspace, L, timing, stream);
 }
 
@@ -1967,8 +1997,9 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
                      const int32_t* node_tokens, const int32_t* parents, int parents_shared, int B, int T, int V,
                      int max_depth, int walk, uint64_t seed, uint64_t round, float temperature,
                      int32_t* out_tokens, int32_t* out_path_nodes, int32_t* out_num_accepted, int8_t* out_accept,
-                     float* out_probs, double* out_residual_mass, void* workspace, size_t workspace_bytes,
-                     const sv_timing* timing, hipStream_t stream)
+                     float* out_probs, double* out_residual_mass, const int32_t* kv_len_in, int32_t* out_src_rows,
+                     int32_t* out_kv_len, void* workspace, size_t workspace_bytes, const sv_timing* timing,
+                     hipStream_t stream)
 {
     if (dtype != SV_F32 && dtype != SV_BF16) return SV_EDTYPE;
     if (B < 0 || T < 0 || V < 1 || max_depth < 0 || !(temperature > 0.0f) || !(temperature < INFINITY) ||
@@ -1979,6 +2010,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if (!target_logits || !draft_logits || !node_tokens || !parents || !out_tokens || !out_path_nodes ||
         !out_num_accepted)
         return SV_EINVAL;
+    if ((out_src_rows || out_kv_len) && !kv_len_in) return SV_EINVAL;
     const int es = dtype == SV_BF16 ? 2 : 4;
     int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
     if (rc) return rc;
@@ -2011,6 +2043,9 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     P.out_acc = out_accept;
     P.out_probs = out_probs;
     P.out_resid = out_residual_mass;
+    P.kv_len_in = kv_len_in;
+    P.out_src_rows = out_src_rows;
+    P.out_kv_len = out_kv_len;
     return launch_verify<true>(P, dtype, workspace, L, timing, stream);
 }
 

@@ -171,6 +171,14 @@ __device__ __forceinline__ uint4 stream_load16(const uint4* p)
 #endif
 }
 
+// 16-byte streaming load through a buffer resource: `voff` per lane,
+// `soff` uniform; an access past the resource's size reads zeros.
+__device__ __forceinline__ uint4 stream_buf16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, SV_STREAM_NT ? 2 : 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DT>
 constexpr int elem_bytes()
 {
@@ -209,18 +217,20 @@ __device__ __forceinline__ uint4 encode16(const float* x)
 // Records passed between blocks of one launch
 // ---------------------------------------------------------------------------
 // A record is a whole number of 16-byte atoms whose last word is a tag:
-// tag = epoch ^ hash(every other word), with epoch a per-call number that is
-// never 0.  Writers store the atoms with agent-coherent (sc1) 16-byte buffer
-// stores and never wait; readers load all atoms with coherent loads and take
-// the record once the tag matches what they loaded.  A record left by an
-// earlier call fails the check (its tag carries another epoch), and so does a
-// record read while its stores are still landing (the hash no longer matches
-// the mixture), so no ordering between the stores is needed.  Coherent
-// accesses go to the level shared by all XCDs: no cache-wide write-back or
+// tag = gen ^ hash(every other word), with gen the low word of the call's
+// generation (a per-workspace count of finished calls, plus one).  Writers
+// store the atoms with agent-coherent (sc1) 16-byte buffer stores; readers
+// load all atoms with coherent loads and take the record once the tag
+// matches what they loaded.  A record left by an earlier call fails the
+// check (its tag carries another generation), and so does a record read
+// while its stores are still landing (the hash no longer matches the
+// mixture), so no ordering between the stores is needed.  Coherent accesses
+// go to the level shared by all XCDs: no cache-wide write-back or
 // invalidation is involved.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kCpolSc1 = 16;  // agent-coherent access: misses the CU cache, served by L2
+constexpr int kCpolNT = 2;    // nontemporal: the line is not kept for reuse
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
 {
@@ -349,7 +359,7 @@ struct ChunkSums {
     uint32_t flags;
 };
 
-constexpr uint32_t kRowStatBytes = 16, kChunkSumsBytes = 64;
+constexpr uint32_t kRowStatBytes = 16, kChunkSumsBytes = 64, kSeqStateBytes = 64;
 
 __device__ __forceinline__ void pack(const RowStat& v, u32x4* a)
 {
@@ -358,6 +368,31 @@ __device__ __forceinline__ void pack(const RowStat& v, u32x4* a)
 __device__ __forceinline__ RowStat unpack_rowstat(const u32x4* a)
 {
     return RowStat{d64(a[0].x, a[0].y), __uint_as_float(a[0].z)};
+}
+
+__device__ __forceinline__ void pack(const SeqState& v, u32x4* a)
+{
+    a[0] = u32x4{lo32(v.sq), hi32(v.sq), lo32(v.sp), hi32(v.sp)};
+    a[1] = u32x4{lo32(v.u), hi32(v.u), __float_as_uint(v.mq), __float_as_uint(v.mp)};
+    a[2] = u32x4{__float_as_uint(v.thr_lo), __float_as_uint(v.thr_hi), (uint32_t)v.k, (uint32_t)v.node};
+    a[3] = u32x4{(uint32_t)v.status, (uint32_t)v.mode, (uint32_t)v.bonus_ref, 0u};
+}
+__device__ __forceinline__ SeqState unpack_state(const u32x4* a)
+{
+    SeqState v;
+    v.sq = d64(a[0].x, a[0].y);
+    v.sp = d64(a[0].z, a[0].w);
+    v.u = d64(a[1].x, a[1].y);
+    v.mq = __uint_as_float(a[1].z);
+    v.mp = __uint_as_float(a[1].w);
+    v.thr_lo = __uint_as_float(a[2].x);
+    v.thr_hi = __uint_as_float(a[2].y);
+    v.k = (int)a[2].z;
+    v.node = (int)a[2].w;
+    v.status = (int)a[3].x;
+    v.mode = (int)a[3].y;
+    v.bonus_ref = (int)a[3].z;
+    return v;
 }
 
 __device__ __forceinline__ void pack(const ChunkSums& v, u32x4* a)

@@ -44,7 +44,7 @@ def test_header_symbols_exported(sv):
 
 def test_status_strings_and_sizes(sv):
     L = sv.library()
-    assert L.sv_abi_version() == 3
+    assert L.sv_abi_version() == 4
     for code in range(7):
         assert L.sv_status_string(code)
     assert sv.chain_workspace_bytes(256, 7, 128256) > 0
@@ -60,11 +60,12 @@ FAKE = 0x10000  # 16-byte aligned host address never dereferenced: validation re
 
 def _chain(L, **kw):
     a = dict(tq=FAKE, qs=8 * 32, qr=32, tp=FAKE, ps=8 * 32, pr=32, dt=0, d=FAKE, B=2, N=3, V=32, seed=0, rnd=0,
-             T=1.0, tok=FAKE, num=FAKE, acc=None, probs=None, mass=None, ws=FAKE, wsb=1 << 30)
+             T=1.0, tok=FAKE, num=FAKE, acc=None, probs=None, mass=None, kvin=None, src=None, kvl=None, ws=FAKE,
+             wsb=1 << 30)
     a.update(kw)
     return L.spec_verify_chain(a["tq"], a["qs"], a["qr"], a["tp"], a["ps"], a["pr"], a["dt"], a["d"], a["B"], a["N"],
                                a["V"], a["seed"], a["rnd"], a["T"], a["tok"], a["num"], a["acc"], a["probs"],
-                               a["mass"], a["ws"], a["wsb"], None, None)
+                               a["mass"], a["kvin"], a["src"], a["kvl"], a["ws"], a["wsb"], None, None)
 
 
 def test_chain_argument_errors(sv):
@@ -80,6 +81,7 @@ def test_chain_argument_errors(sv):
     assert _chain(L, qr=-32) == 1                    # negative stride
     assert _chain(L, wsb=16) == 5 and _chain(L, ws=None) == 5   # SV_EWORKSPACE
     assert _chain(L, B=0) == 0                       # empty batch: nothing to do
+    assert _chain(L, src=FAKE) == 1 and _chain(L, kvl=FAKE) == 1   # KV outputs need kv_len_in
 
 
 def test_tree_and_kv_argument_errors(sv):
@@ -87,15 +89,16 @@ def test_tree_and_kv_argument_errors(sv):
 
     def tree(**kw):
         a = dict(tq=FAKE, tp=FAKE, dt=0, tok=FAKE, par=FAKE, shared=1, B=2, T=5, V=32, md=3, T_=1.0, out=FAKE,
-                 path=FAKE, num=FAKE, ws=FAKE, wsb=1 << 30, walk=0)
+                 path=FAKE, num=FAKE, kvin=None, src=None, kvl=None, ws=FAKE, wsb=1 << 30, walk=0)
         a.update(kw)
         return L.spec_verify_tree(a["tq"], 6 * 32, 32, a["tp"], 6 * 32, 32, a["dt"], a["tok"], a["par"], a["shared"],
                                   a["B"], a["T"], a["V"], a["md"], a["walk"], 0, 0, a["T_"], a["out"], a["path"], a["num"],
-                                  None, None, None, a["ws"], a["wsb"], None, None)
+                                  None, None, None, a["kvin"], a["src"], a["kvl"], a["ws"], a["wsb"], None, None)
     assert tree(T=1024) == 3 and tree(md=6) == 3 and tree(md=-1) == 1
     assert tree(par=None) == 1 and tree(path=None) == 1 and tree(T_=0.0) == 1 and tree(dt=9) == 2
     assert tree(wsb=100) == 5 and tree(B=0) == 0
     assert tree(walk=2) == 1 and tree(walk=-1) == 1 and tree(walk=1, B=0) == 0
+    assert tree(src=FAKE) == 1 and tree(kvl=FAKE) == 1
     kv = L.kv_compact_indices
     assert kv(None, FAKE, FAKE, 2, -1, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1
     assert kv(None, None, FAKE, 2, 3, FAKE, FAKE, None, 0, 0, 0, 0, 0, 0, None) == 1

@@ -613,3 +613,27 @@ def test_tree_build_full_size_sampled():
     rows = synth.dynamic_tree_inputs(w, seed=22, B=16, device="cuda")["expanded_p"]
     _tree_build_case("c5_full", rows, w.depth, w.topk, w.budget, w.T)
     log("[done] tree_build full size")
+
+
+def test_workspace_reused_across_calls_and_shapes():
+    """One workspace serves a run of chain and tree calls of different sizes
+    (records and counters carry each call's number): every call matches the
+    oracle, including calls whose records sit where a larger earlier call
+    left its own."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] workspace_reuse")
+    wc, wt = W["c3"].with_sizes(V=9001), W["c4"].with_sizes(V=6007)
+    nbytes = max(sv.chain_workspace_bytes(24, 7, 9001), sv.tree_workspace_bytes(12, 25, 9001))
+    ws = sv.alloc_workspace(nbytes, "cuda")
+    rep = compare.Report()
+    for i, (kind, B) in enumerate([("chain", 24), ("tree", 12), ("chain", 5), ("chain", 24), ("tree", 3),
+                                   ("chain", 17)]):
+        log(f"   call {i}: {kind} B={B}")
+        if kind == "chain":
+            r, g, _ = run_chain(wc, seed=70 + i, rnd=i, B=B, workspace=ws)
+        else:
+            inp = synth.static_tree_inputs(wt, 80 + i, "cuda", B=B)
+            r, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 80 + i, i, wt.T, wt.depth,
+                            workspace=ws)
+        rep.merge(r)
+    _done("workspace_reuse", rep)
