@@ -71,7 +71,8 @@ enum sv_status {
     SV_ESHAPE = 3,      /* N > 64, T+1 > 1024, max_depth < 0, ... */
     SV_EALIGN = 4,      /* logits not element-aligned / KV rows not 16-byte aligned */
     SV_EWORKSPACE = 5,  /* workspace NULL or smaller than required */
-    SV_EHIP = 6         /* a HIP launch failed */
+    SV_EHIP = 6,        /* a HIP launch failed */
+    SV_ESCRATCH = 7     /* sizes beyond spec_verify_chain_noalloc's static scratch */
 };
 
 enum sv_dtype { SV_F32 = 0, SV_BF16 = 1 };
@@ -151,6 +152,31 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
                       float* out_probs, double* out_residual_mass, const int32_t* kv_len_in, int32_t* out_src_rows,
                       int32_t* out_kv_len, void* workspace, size_t workspace_bytes, const sv_timing* timing,
                       hipStream_t stream);
+
+/*
+ * spec_verify_chain_noalloc -- spec_verify_chain without a workspace
+ * argument, for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * outputs are those of spec_verify_chain.  The call allocates nothing: its
+ * workspace is a static device array of the library,
+ * SV_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, zero when the library is loaded
+ * and kept until the process ends (config 3's chains, B=256 N=7 V=128256,
+ * need about 1.3 MB).  Sizes whose sv_chain_workspace_bytes exceed it
+ * return SV_ESCRATCH before any HIP call.  Every call on one GPU shares that
+ * GPU's array (each call tags its records, so what an earlier call left
+ * needs no clearing); calls that overlap in time on one GPU race and must
+ * not be made.  The first call on a device looks the array's address up
+ * with hipGetSymbolAddress (with that device current); SV_EHIP if that
+ * fails.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (4u << 20)
+int spec_verify_chain_noalloc(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                              const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
+                              const int32_t* draft_tokens, int B, int N, int V, uint64_t seed, uint64_t round,
+                              float temperature, int32_t* out_tokens, int32_t* out_num_accepted,
+                              int8_t* out_accept, float* out_probs, double* out_residual_mass,
+                              const int32_t* kv_len_in, int32_t* out_src_rows, int32_t* out_kv_len,
+                              const sv_timing* timing, hipStream_t stream);
 
 /*
  * spec_verify_tree -- one verify round over B flattened draft trees ([ZH]

@@ -38,7 +38,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 SV_F32, SV_BF16 = 0, 1
 SV_WALK_FIRST_ACCEPTED, SV_WALK_BEST_CHILD = 0, 1
 STATUS = {0: "SV_OK", 1: "SV_EINVAL", 2: "SV_EDTYPE", 3: "SV_ESHAPE", 4: "SV_EALIGN", 5: "SV_EWORKSPACE",
-          6: "SV_EHIP"}
+          6: "SV_EHIP", 7: "SV_ESCRATCH"}
 
 
 class SpecVerifyError(RuntimeError):
@@ -74,6 +74,10 @@ def _lib():
         L.spec_verify_chain.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, u64, u64,
                                         ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                         ctypes.POINTER(SvTiming), vp]
+        L.spec_verify_chain_noalloc.restype = i32
+        L.spec_verify_chain_noalloc.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, i32, i32, i32, u64, u64,
+                                                ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.POINTER(SvTiming), vp]
         L.spec_verify_tree.restype = i32
         L.spec_verify_tree.argtypes = [vp, i64, i64, vp, i64, i64, i32, vp, vp, i32, i32, i32, i32, i32, i32, u64, u64,
                                        ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -208,6 +212,36 @@ def spec_verify_chain(target_logits: torch.Tensor, draft_logits: Optional[torch.
     if rc != 0:
         raise SpecVerifyError(rc, "spec_verify_chain")
     return o
+
+
+def spec_verify_chain_noalloc(target_logits: torch.Tensor, draft_logits: Optional[torch.Tensor],
+                              draft_tokens: torch.Tensor, seed: int, round: int, temperature: float = 1.0, *,
+                              kv_len_in: Optional[torch.Tensor] = None, out: dict, timing=None, stream=None) -> dict:
+    """spec_verify_chain through the entry point that allocates nothing: the
+    library's static per-GPU scratch replaces the workspace, and `out`
+    (preallocated outputs, alloc_chain_outputs) is required, so the call
+    itself allocates no device memory."""
+    _check_logits(target_logits, "target_logits")
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    if N > 0:
+        _check_logits(draft_logits, "draft_logits")
+        if draft_logits.shape != (B, N, V) or draft_logits.dtype != target_logits.dtype:
+            raise ValueError("draft_logits must be [B, N, V] with the dtype of target_logits")
+        if draft_tokens.shape != (B, N) or draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+            raise ValueError("draft_tokens must be a contiguous int32 [B, N] tensor")
+    _check_kv(kv_len_in, out, B)
+    dl = draft_logits if N > 0 else None
+    rc = _lib().spec_verify_chain_noalloc(
+        _p(target_logits), target_logits.stride(0), target_logits.stride(1),
+        _p(dl), dl.stride(0) if dl is not None else 0, dl.stride(1) if dl is not None else 0,
+        _dtype_code(target_logits), _p(draft_tokens) if N > 0 else None, B, N, V, seed & (2 ** 64 - 1),
+        round & (2 ** 64 - 1), float(temperature), _p(out["tokens"]), _p(out["num_accepted"]), _p(out.get("accept")),
+        _p(out.get("probs")), _p(out.get("residual_mass")), *_kv_args(kv_len_in, out), _timing(timing),
+        _stream(stream))
+    if rc != 0:
+        raise SpecVerifyError(rc, "spec_verify_chain_noalloc")
+    return out
 
 
 def alloc_tree_outputs(B: int, T: int, max_depth: int, device, kv: bool = False):
@@ -446,7 +480,7 @@ def sv_philox_uniforms(seed: int, round: int, nseq: int, npos: int, device="cuda
     return a, s
 
 
-__all__ = ["spec_verify_chain", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "sample_draft",
+__all__ = ["spec_verify_chain", "spec_verify_chain_noalloc", "spec_verify_tree", "kv_compact_indices", "tree_attention_mask", "sample_draft",
            "tree_expand",
            "tree_select", "tree_finalize", "tree_build", "alloc_tree_table", "sv_philox_uniforms",
            "chain_workspace_bytes", "tree_workspace_bytes", "alloc_workspace", "alloc_chain_outputs", "alloc_tree_outputs",

@@ -49,6 +49,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 #include <random>
 
 #include "sv_device.h"
@@ -1911,6 +1912,36 @@ bool item_count_ok(int B, int rows, int V)
 
 }  // namespace
 
+// Workspace of spec_verify_chain_noalloc: device memory of the library
+// itself, zero when the library is loaded, one copy per GPU.  In host code
+// the name only stands for the symbol; the device address comes from
+// hipGetSymbolAddress (scratch_on_current_device).
+static __device__ __align__(256) char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SV_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int sv_abi_version(void) { return 4; }
@@ -1925,6 +1956,7 @@ const char* sv_status_string(int status)
         case SV_EALIGN: return "logits not element-aligned or KV rows not 16-byte aligned";
         case SV_EWORKSPACE: return "workspace missing or too small";
         case SV_EHIP: return "HIP launch failed";
+        case SV_ESCRATCH: return "sizes exceed the no-allocation entry point's static scratch";
         default: return "unknown status";
     }
 }
@@ -1990,6 +2022,31 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     P.out_src_rows = out_src_rows;
     P.out_kv_len = out_kv_len;
     return launch_verify<false>(P, dtype, workspace, L, timing, stream);
+}
+
+int spec_verify_chain_noalloc(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
+                              const void* draft_logits, int64_t drf_seq_stride, int64_t drf_row_stride, int dtype,
+                              const int32_t* draft_tokens, int B, int N, int V, uint64_t seed, uint64_t round,
+                              float temperature, int32_t* out_tokens, int32_t* out_num_accepted,
+                              int8_t* out_accept, float* out_probs, double* out_residual_mass,
+                              const int32_t* kv_len_in, int32_t* out_src_rows, int32_t* out_kv_len,
+                              const sv_timing* timing, hipStream_t stream)
+{
+    // sizes the static scratch cannot hold are refused before any HIP call
+    const size_t need = sv_chain_workspace_bytes(B, N, V);
+    if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_ESCRATCH;
+    if (B == 0 || need == 0)  // empty batch or invalid sizes: the regular entry point's status
+        return spec_verify_chain(target_logits, tgt_seq_stride, tgt_row_stride, draft_logits, drf_seq_stride,
+                                 drf_row_stride, dtype, draft_tokens, B, N, V, seed, round, temperature, out_tokens,
+                                 out_num_accepted, out_accept, out_probs, out_residual_mass, kv_len_in, out_src_rows,
+                                 out_kv_len, nullptr, 0, timing, stream);
+    void* ws = nullptr;
+    const int rc = scratch_on_current_device(&ws);
+    if (rc) return rc;
+    return spec_verify_chain(target_logits, tgt_seq_stride, tgt_row_stride, draft_logits, drf_seq_stride,
+                             drf_row_stride, dtype, draft_tokens, B, N, V, seed, round, temperature, out_tokens,
+                             out_num_accepted, out_accept, out_probs, out_residual_mass, kv_len_in, out_src_rows,
+                             out_kv_len, ws, (size_t)SV_NOALLOC_SCRATCH_BYTES, timing, stream);
 }
 
 int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,

@@ -45,7 +45,7 @@ def test_header_symbols_exported(sv):
 def test_status_strings_and_sizes(sv):
     L = sv.library()
     assert L.sv_abi_version() == 4
-    for code in range(7):
+    for code in range(8):
         assert L.sv_status_string(code)
     assert sv.chain_workspace_bytes(256, 7, 128256) > 0
     assert sv.chain_workspace_bytes(1, 65, 10) == 0
@@ -82,6 +82,14 @@ def test_chain_argument_errors(sv):
     assert _chain(L, wsb=16) == 5 and _chain(L, ws=None) == 5   # SV_EWORKSPACE
     assert _chain(L, B=0) == 0                       # empty batch: nothing to do
     assert _chain(L, src=FAKE) == 1 and _chain(L, kvl=FAKE) == 1   # KV outputs need kv_len_in
+    # the no-allocation entry point refuses sizes beyond its static scratch before any HIP call
+    na = L.spec_verify_chain_noalloc
+    assert na(FAKE, 8 * 128256, 128256, FAKE, 8 * 128256, 128256, 1, FAKE, 1024, 7, 128256, 0, 0, 1.0, FAKE, FAKE,
+              None, None, None, None, None, None, None, None) == 7                 # SV_ESCRATCH
+    assert na(FAKE, 8 * 32, 32, FAKE, 8 * 32, 32, 0, FAKE, 0, 3, 32, 0, 0, 1.0, FAKE, FAKE,
+              None, None, None, None, None, None, None, None) == 0                 # empty batch
+    assert na(FAKE, 8 * 32, 32, FAKE, 8 * 32, 32, 0, FAKE, 2, 65, 32, 0, 0, 1.0, FAKE, FAKE,
+              None, None, None, None, None, None, None, None) == 3                 # N > 64 (SV_ESHAPE)
 
 
 def test_tree_and_kv_argument_errors(sv):

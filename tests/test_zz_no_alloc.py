@@ -1,0 +1,52 @@
+"""The entry point that allocates nothing (spec_verify_chain_noalloc, the
+library's static per-GPU scratch as its workspace) against spec_verify_chain
+with a workspace of its own: identical outputs, element by element, on two
+calls in a row, the second with smaller inputs (so it runs over what the
+first left in the scratch), plus a third call that repeats the first."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from _gpu import kv_rows_in, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import rejection_sampling_verify_14_amd as sv
+    sv.library()
+
+
+def _both(w, seed, rnd, B, N):
+    import rejection_sampling_verify_14_amd as sv
+    inp = synth.chain_inputs(w, seed, "cuda", B=B, N=N)
+    L0 = kv_rows_in(B, seed)
+    ref = sv.spec_verify_chain(inp["zq"], inp["zp"], inp["d"], seed=seed, round=rnd, temperature=w.T, kv_len_in=L0)
+    out = sv.alloc_chain_outputs(B, N, "cuda", kv=True)
+    for v in out.values():
+        v.fill_(-99) if v.dtype != torch.float64 else v.fill_(-99.0)
+    torch.cuda.synchronize()
+    sv.spec_verify_chain_noalloc(inp["zq"], inp["zp"], inp["d"], seed=seed, round=rnd, temperature=w.T,
+                                 kv_len_in=L0, out=out)
+    torch.cuda.synchronize()
+    for k in ref:
+        a, b = ref[k].cpu().numpy(), out[k].cpu().numpy()
+        assert np.array_equal(a, b, equal_nan=True), f"{k} differs: {a.ravel()[:8]} vs {b.ravel()[:8]}"
+    return ref
+
+
+def test_noalloc_matches_the_workspace_entry_point():
+    w = synth.WORKLOADS["c3"].with_sizes(V=20011)
+    log("[case] noalloc call 1: B=24 N=7 V=20011")
+    r1 = _both(w, 301, 0, 24, 7)
+    log("[case] noalloc call 2: B=5 N=3 V=9001 (smaller, over the first call's scratch)")
+    _both(synth.WORKLOADS["c3"].with_sizes(V=9001), 302, 1, 5, 3)
+    log("[case] noalloc call 3: the first call again")
+    r3 = _both(w, 301, 0, 24, 7)
+    for k in r1:
+        assert torch.equal(r1[k].cpu(), r3[k].cpu()), k
+    log("[done] noalloc")
