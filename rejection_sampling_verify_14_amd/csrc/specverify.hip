@@ -60,30 +60,16 @@ namespace sv {
 // ===========================================================================
 // Pass 1: row statistics
 // ===========================================================================
-template <int K>
-__device__ __forceinline__ void accumulate_values(const float* x, float c, double cd, float& ref, double& acc)
+// Head and tail elements of a row that is not 16-byte aligned or not a whole
+// number of vectors: one element at a time, against a per-lane reference.
+__device__ __forceinline__ void accumulate_value(float x, float c, double cd, float& ref, double& acc)
 {
-    float lm = x[0];
-#pragma unroll
-    for (int i = 1; i < K; ++i) lm = fmaxf(lm, x[i]);
-    // move the reference when the first finite value arrives or the maximum
-    // grows by more than one binary order of magnitude: the terms that
-    // dominate the sum then have exponent arguments in (-few, 1], where the
-    // fp32 rounding of (x - ref) * c is smallest
-    if ((lm - ref) * c > 1.0f) {
-        acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
-        ref = lm;
+    if ((x - ref) * c > 1.0f) {
+        acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - x) * cd);
+        ref = x;
     }
     const float r = (ref == -INFINITY) ? 0.0f : ref;
-    float e[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) e[i] = __builtin_amdgcn_exp2f((x[i] - r) * c);
-#pragma unroll
-    for (int w = 1; w < K; w <<= 1) {
-#pragma unroll
-        for (int i = 0; i + w < K; i += 2 * w) e[i] += e[i + w];
-    }
-    acc += (double)e[0];
+    acc += (double)__builtin_amdgcn_exp2f((x - r) * c);
 }
 
 __device__ __forceinline__ void combine_stat(float& m, double& s, float m2, double s2, double cd)
@@ -95,19 +81,50 @@ __device__ __forceinline__ void combine_stat(float& m, double& s, float m2, doub
     m = M;
 }
 
+// A wave's running sum over the 16-byte vectors of a segment, against a
+// reference `ref` that is the same in every lane: acc = sum 2^(x c - p) with
+// p = RN(ref * c), so that each term's exponent argument is one fma; the sum
+// relative to ref is acc * 2^-(ref c - p), where ref c - p (the rounding of
+// the product, exact as fma(ref, c, -p)) is applied once at the end.  When
+// ref * c is not a finite float (logits beyond ~2^127 T) the terms fall back
+// to 2^((x - ref) c) and p = ref * c is not used.
+struct WaveSum {
+    float ref, p;
+    double acc;
+};
+
+__device__ __forceinline__ bool wide_ref(const WaveSum& w) { return !(fabsf(w.p) < INFINITY); }
+
+// Moves the reference up to lm (> ref), rescaling the sum.
+__device__ __forceinline__ void move_ref(WaveSum& w, float lm, float c, double cd)
+{
+    const float np = lm * c;
+    if (w.ref == -INFINITY) {
+        w.acc = 0.0;
+    } else if (!(fabsf(np) < INFINITY) || wide_ref(w)) {
+        // leave the p form: rescale by 2^((ref - lm) c) relative to the old form's reference
+        const double old = wide_ref(w) ? 1.0 : exp2(-(double)fmaf(w.ref, c, -w.p));
+        w.acc *= old * exp2(((double)w.ref - (double)lm) * cd);
+        if (fabsf(np) < INFINITY) w.acc *= exp2((double)fmaf(lm, c, -np));
+    } else {
+        w.acc *= exp2((double)w.p - (double)np);
+    }
+    w.ref = lm;
+    w.p = np;
+}
+
 // One batch of U 16-byte vectors per lane (vectors past the end carry -inf),
-// in fp32 groups of (at most) 32 terms exp2((x - ref) * c) added to the double
-// accumulator.  The reference is the same in every lane of the wave.  When a
-// group sum of any lane exceeds kGroupLimit (so a term exceeds it: an element
-// more than three binary orders of magnitude, in units of the scaled logits,
-// above the reference), is not finite, or comes before any reference exists,
-// the reference moves to the wave's maximum of the group and the group is
-// summed again; so the dominant terms keep exponent arguments below 3, where
-// the fp32 rounding of (x - ref) * c stays small.
+// in fp32 groups of (at most) 32 terms added to the double accumulator.  When
+// a group sum of any lane exceeds kGroupLimit (so a term exceeds it: an
+// element more than three binary orders of magnitude, in units of the scaled
+// logits, above the reference), is not finite, or comes before any reference
+// exists, the reference moves to the wave's maximum of the group and the
+// group is summed again; so the dominant terms keep exponent arguments below
+// 3, where the fp32 rounding of the argument stays small.
 constexpr float kGroupLimit = 8.0f;
 
 template <int DT, int U>
-__device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, double cd, float& ref, double& acc)
+__device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, double cd, WaveSum& w)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int GE = (U * EPV < 32) ? U * EPV : 32;  // elements per fp32 group
@@ -115,52 +132,56 @@ __device__ __forceinline__ void accumulate_batch(const uint4* raw, float c, doub
     static_assert(U % G == 0, "batch must hold whole groups");
 #pragma unroll
     for (int g = 0; g < U / G; ++g) {
-        auto group_sum = [&](float r) {
+        auto group_sum = [&]() {
             float e[GE];
+            if (!wide_ref(w)) {
+                const float np = -w.p;
 #pragma unroll
-            for (int u = 0; u < G; ++u) {
-                float x[EPV];
-                decode16<DT>(raw[g * G + u], x);
+                for (int u = 0; u < G; ++u) {
+                    float x[EPV];
+                    decode16<DT>(raw[g * G + u], x);
 #pragma unroll
-                for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f((x[i] - r) * c);
+                    for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f(fmaf(x[i], c, np));
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < G; ++u) {
+                    float x[EPV];
+                    decode16<DT>(raw[g * G + u], x);
+#pragma unroll
+                    for (int i = 0; i < EPV; ++i) e[u * EPV + i] = __builtin_amdgcn_exp2f((x[i] - w.ref) * c);
+                }
             }
 #pragma unroll
-            for (int w = 1; w < GE; w <<= 1) {
+            for (int s = 1; s < GE; s <<= 1) {
 #pragma unroll
-                for (int i = 0; i + w < GE; i += 2 * w) e[i] += e[i + w];
+                for (int i = 0; i + s < GE; i += 2 * s) e[i] += e[i + s];
             }
             return e[0];
         };
-        if (ref == -INFINITY) {
+        auto group_max = [&]() {
+            float lm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                float x[EPV];
+                decode16<DT>(raw[g * G + u], x);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
+            }
+            return wave_max(lm);
+        };
+        if (w.ref == -INFINITY) {
             // no reference yet (uniform across the wave): take the group maximum
-            float lm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                float x[EPV];
-                decode16<DT>(raw[g * G + u], x);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
-            }
-            ref = wave_max(lm);
+            const float lm = group_max();
+            if (lm != -INFINITY) move_ref(w, lm, c, cd);
         }
-        float s = (ref == -INFINITY) ? 0.0f : group_sum(ref);
+        float s = (w.ref == -INFINITY) ? 0.0f : group_sum();
         if (__any(!(s <= kGroupLimit))) {
-            float lm = -INFINITY;
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                float x[EPV];
-                decode16<DT>(raw[g * G + u], x);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) lm = fmaxf(lm, x[i]);
-            }
-            lm = wave_max(lm);
-            if (lm > ref) {
-                acc = (ref == -INFINITY) ? 0.0 : acc * exp2((double)(ref - lm) * cd);
-                ref = lm;
-            }
-            s = (ref == -INFINITY) ? 0.0f : group_sum(ref);
+            const float lm = group_max();
+            if (lm > w.ref) move_ref(w, lm, c, cd);
+            s = (w.ref == -INFINITY) ? 0.0f : group_sum();
         }
-        acc += (double)s;
+        w.acc += (double)s;
     }
 }
 
@@ -202,23 +223,20 @@ __device__ __forceinline__ void mask_batch(int nvec, int bt, uint4* x)
 // unconditional (clamped) prefetch: no register a load is still writing is
 // copied or overwritten, and no branch merges load states, so each batch
 // waits only for its own loads.  The partial batch, if any, is masked after.
+// Every lane of a wave shares the reference, so the wave's sum is a plain sum
+// of doubles; the four waves' (m, s) are combined by thread 0.
 template <int DT, int U>
 __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row, int n, float c, double cd)
 {
     constexpr int EB = elem_bytes<DT>();
     constexpr int EPV = 16 / EB;
-    float ref = -INFINITY;
-    double acc = 0.0;
+    WaveSum w{-INFINITY, 0.0f, 0.0};
     int head = (int)(((16u - ((uint32_t)(uintptr_t)row & 15u)) & 15u) / EB);
     head = head < n ? head : n;
-    // head and tail elements go to a per-lane accumulator of their own (the
-    // batch reference is wave-uniform)
+    // head and tail elements go to a per-lane accumulator of their own
     float ref1 = -INFINITY;
     double acc1 = 0.0;
-    if ((int)threadIdx.x < head) {
-        float x[1] = {load_logit<DT>(row, threadIdx.x)};
-        accumulate_values<1>(x, c, cd, ref1, acc1);
-    }
+    if ((int)threadIdx.x < head) accumulate_value(load_logit<DT>(row, threadIdx.x), c, cd, ref1, acc1);
     row += head * EB;
     n -= head;
     const int nvec = n / EPV;
@@ -231,42 +249,47 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
         int bt = 0;
         for (; bt + 2 <= nfull; bt += 2) {
             load_batch<U>(vrow, nvec, bt + 1, x1);
-            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+            accumulate_batch<DT, U>(x0, c, cd, w);
             load_batch<U>(vrow, nvec, bt + 2, x0);
-            accumulate_batch<DT, U>(x1, c, cd, ref, acc);
+            accumulate_batch<DT, U>(x1, c, cd, w);
         }
         // x0 holds batch bt: the last whole one, the partial one, or none
         if (bt < nfull) {
             load_batch<U>(vrow, nvec, bt + 1, x1);
-            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+            accumulate_batch<DT, U>(x0, c, cd, w);
             if (part) {
                 mask_batch<DT, U>(nvec, bt + 1, x1);
-                accumulate_batch<DT, U>(x1, c, cd, ref, acc);
+                accumulate_batch<DT, U>(x1, c, cd, w);
             }
         } else if (part) {
             mask_batch<DT, U>(nvec, bt, x0);
-            accumulate_batch<DT, U>(x0, c, cd, ref, acc);
+            accumulate_batch<DT, U>(x0, c, cd, w);
         }
     }
     const int tail = n - nvec * EPV;
-    if ((int)threadIdx.x < tail) {
-        float x[1] = {load_logit<DT>(row, (int64_t)nvec * EPV + threadIdx.x)};
-        accumulate_values<1>(x, c, cd, ref1, acc1);
-    }
-    combine_stat(ref, acc, ref1, acc1, cd);
+    if ((int)threadIdx.x < tail)
+        accumulate_value(load_logit<DT>(row, (int64_t)nvec * EPV + threadIdx.x), c, cd, ref1, acc1);
+    // the wave's vector sum (one reference): a plain sum, then the fma offset
+    float m = w.ref;
+    double s = wave_sum(w.acc);
+    if (m != -INFINITY && !wide_ref(w)) s *= exp2(-(double)fmaf(w.ref, c, -w.p));
+    // head and tail lanes (rare): their own (m, s), folded in
+    if (__any(ref1 != -INFINITY)) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const float m2 = __shfl_xor(ref, off, 64);
-        const double s2 = __shfl_xor(acc, off, 64);
-        combine_stat(ref, acc, m2, s2, cd);
+        for (int off = 32; off > 0; off >>= 1) {
+            const float m2 = __shfl_xor(ref1, off, 64);
+            const double s2 = __shfl_xor(acc1, off, 64);
+            combine_stat(ref1, acc1, m2, s2, cd);
+        }
+        combine_stat(m, s, ref1, acc1, cd);
     }
     __shared__ float red_m[kWaves];
     __shared__ double red_s[kWaves];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __syncthreads();
     if (lane == 0) {
-        red_m[wave] = ref;
-        red_s[wave] = acc;
+        red_m[wave] = m;
+        red_s[wave] = s;
     }
     __syncthreads();
     RowStat st;
@@ -274,7 +297,7 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
     st.s = red_s[0];
     if (threadIdx.x == 0) {
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) combine_stat(st.m, st.s, red_m[w], red_s[w], cd);
+        for (int k = 1; k < kWaves; ++k) combine_stat(st.m, st.s, red_m[k], red_s[k], cd);
     }
     return st;
 }
