@@ -326,11 +326,16 @@ struct VerifyParams {
     float T, c;               // temperature, log2(e)/T
     double cd, invT;
     uint32_t epoch;
+    // exp(z/T) over the bf16 grid (bf16 logits; see kTabKeys)
+    int use_tab;              // the table is filled and used
+    int tab_blocks;           // row-kernel blocks that fill it
+    uint32_t tab_lo;          // first magnitude key of the table
     // workspace
     uint64_t* chunk_arrivals; // [B] epoch-tagged arrival counters of the sample blocks
     SeqState* seqs;           // [B] chains: accept state of each sequence (accept kernel -> sample kernels)
     char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
+    double* etab_g;           // [kTabEntries] the exp(z/T) table (row kernel -> sample kernels)
     uint32_t stats_bytes, part_bytes;
     // outputs
     int32_t* out_tokens;
@@ -445,18 +450,24 @@ __device__ __forceinline__ void issue_row_stat(const VerifyParams& P, int b, int
 
 // Folds the records requested by issue_row_stat into acc: the batch's
 // maximum first, then each segment's sum scaled to it (independent exps, in
-// segment order), then the batch into acc.  Branch-free (slots past the last
-// segment are masked by selects), so no load is sunk next to its use.
-__device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int i0, const u32x4* a, RowStat& acc, bool& ok)
+// segment order), then the batch into acc.  A record that is not yet this
+// call's (its row block may still be running when the reader is a block of
+// the same launch) is polled until it is; one that never arrives poisons the
+// row's result (NaN sum).  Past the poll the fold is branch-free.
+__device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int b, int row, int i0, u32x4* a,
+                                              RowStat& acc, bool& ok)
 {
     float xm[kStatBatch];
     double xs[kStatBatch];
     float bm = -INFINITY;
+    const int64_t grow = (int64_t)b * P.rows + row;
 #pragma unroll
     for (int j = 0; j < kStatBatch; ++j) {
         const bool in = i0 + j < P.segs;
+        if (in && a[j].w != record_tag<1>(&a[j], P.epoch) &&
+            !wait_record<1>(stats_rsrc(P), stat_off(P, grow, i0 + j), &a[j], P.epoch))
+            ok = false;
         const RowStat x = unpack_rowstat(&a[j]);
-        ok &= !in || a[j].w == record_tag<1>(&a[j], P.epoch);
         xm[j] = in ? x.m : -INFINITY;
         xs[j] = in ? x.s : 0.0;
         bm = fmaxf(bm, xm[j]);
@@ -491,7 +502,7 @@ __device__ __forceinline__ void load_row_stats(const VerifyParams& P, int b, con
 #pragma unroll
         for (int q = 0; q < R; ++q) issue_row_stat(P, b, rows[q], i0, a[q]);
 #pragma unroll
-        for (int q = 0; q < R; ++q) fold_row_stat(P, i0, a[q], out[q], ok[q]);
+        for (int q = 0; q < R; ++q) fold_row_stat(P, b, rows[q], i0, a[q], out[q], ok[q]);
     }
 #pragma unroll
     for (int q = 0; q < R; ++q)
@@ -510,17 +521,60 @@ __device__ __forceinline__ const char* prow_ptr(const VerifyParams& P, int b, in
     return P.zp + ((int64_t)b * P.ps + (int64_t)r * P.pr) * elem_bytes<DT>();
 }
 
-// exp((z - m)/T) over the logits of one row, m the row's reference (see
-// exp_rel); the argument is one fma, z/T - m/T.
+// exp((z - m)/T) over the logits of one row, m the row's reference: E(z) R
+// from the bf16-grid table when the row has one (vt), else exp_rel with the
+// argument as one fma, z/T - m/T.
 struct ExpRow {
-    double invT, mb;  // 1/T and -m/T
-    lds_dptr tab;     // the block's copy of the 2^(j/N) table (see exp_rel)
-    __device__ __forceinline__ double operator()(float z) const { return exp_rel(fma((double)z, invT, mb), tab); }
+    double invT, mb;   // 1/T and -m/T
+    lds_dptr tab;      // the block's copy of the 2^(j/N) table (see exp_rel)
+    lds_dptr vt;       // the block's LDS copy of the exp(z/T) table, if tabbed (an
+                       // LDS-typed pointer: reads through a generic one are
+                       // flat loads, whose waits serialize; its value 0 is a
+                       // valid address, so `tabbed` says whether there is one)
+    double R;          // exp(-m/T), if tabbed
+    uint32_t lo;       // the table's first magnitude key
+    bool tabbed;
+    // exp_rel inline: the streaming loops of rows without the table
+    __device__ __forceinline__ double slow(float z) const { return exp_rel(fma((double)z, invT, mb), tab); }
+    // the table where it holds z, else exp_rel (element by element; the
+    // batched form is exp_batch)
+    __device__ __forceinline__ double inl(float z) const
+    {
+        if (tabbed) {
+            const int i = tab_index(z, lo);
+            if (i >= 0) return vt[i] * R;
+        }
+        return slow(z);
+    }
 };
 
-__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* etab)
+// vt: the block's LDS copy of the bf16-grid table (null for none); a row
+// takes it when its reference is within kTabRefLimit of zero in units of T.
+__device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* etab, const double* vt)
 {
-    return ExpRow{P.invT, -m * P.invT, (lds_dptr)etab};
+    ExpRow e{P.invT, -m * P.invT, (lds_dptr)etab, (lds_dptr)etab, 0.0, P.tab_lo, false};
+    if (vt && fabs(e.mb) <= kTabRefLimit) {
+        e.vt = (lds_dptr)vt;
+        e.R = exp(e.mb);
+        e.tabbed = true;
+    }
+    return e;
+}
+
+// ExpRow of K logits outside the streaming loops: the table reads of all K
+// are issued together (one round trip, also from a global table); logits
+// outside the table (the -inf past the end of a row among them) take
+// exp_rel inline: a call would spill to scratch and wait on it.
+template <int K>
+__device__ __forceinline__ void exp_batch(const ExpRow& e, const float* z, double* out)
+{
+    int idx[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) idx[i] = e.tabbed ? tab_index(z[i], e.lo) : -1;
+#pragma unroll
+    for (int i = 0; i < K; ++i) out[i] = idx[i] >= 0 ? e.vt[idx[i]] : 0.0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) out[i] = idx[i] >= 0 ? out[i] * e.R : e.slow(z[i]);
 }
 
 // ===========================================================================
@@ -565,9 +619,9 @@ __device__ __forceinline__ void fill_residual_state(SeqState& s, const RowStat& 
 
 constexpr int kMaxChainN = 64;  // longest draft chain
 
-// Chain accept of sequence b, run by a one-wave block (lane i = position
-// i+1): b's state into `out`; with `outputs`, also the accept flags and
-// probabilities.
+// Chain accept of sequence b, run by one wave (lane i = position i+1), the
+// only wave of its block that calls it: b's state into `out`; with
+// `outputs`, also the accept flags and probabilities.
 template <int DT>
 __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool outputs)
 {
@@ -592,7 +646,10 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
         load_row_stats<1>(P, b, &row, &st);
         if (r0 + lane < P.rows) s_rows[row] = st;
     }
-    __syncthreads();
+    // one wave runs this: its LDS stores are published to its own lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // the bonus row's statistics (used if all accept) and those of q_i, p_i
     const RowStat qn = s_rows[N];
     const RowStat rq = s_rows[active ? lane : N], rp = s_rows[active ? N + 1 + lane : N];
@@ -782,8 +839,13 @@ __device__ __forceinline__ void load_chunk16(const char* __restrict__ row, int V
 #pragma unroll
         for (int i = 0; i < NV; ++i) decode16<DT>(raw[i], x + i * (16 / elem_bytes<DT>()));
     } else {
+        // unconditional loads (past V, of the chunk's first token), then -inf
 #pragma unroll
-        for (int j = 0; j < kPerThread; ++j) x[j] = (e0 + j < V) ? load_logit<DT>(row, e0 + j) : -INFINITY;
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t e = e0 + j;
+            const float v = load_logit<DT>(row, e < V ? e : (int64_t)c * kChunk);
+            x[j] = e < V ? v : -INFINITY;
+        }
     }
 }
 
@@ -849,25 +911,30 @@ __device__ __forceinline__ uint4 chunk_vec(const char* __restrict__ row, int c, 
     return reinterpret_cast<const uint4*>(row)[(int64_t)c * (kChunk / EPV) + 64 * k + lane];
 }
 
-// Token t of the lane's share in the element-by-element path.
+// Token t of the lane's share in the element-by-element path (chunk c <
+// nch); past V an unconditional load of the chunk's first token, then -inf.
 template <int DT>
 __device__ __forceinline__ float chunk_token(const char* row, int V, int c, int lane, int k, int i)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     const int64_t e = (int64_t)c * kChunk + (int64_t)(lane + 64 * k) * EPV + i;
-    return e < V ? load_logit<DT>(row, e) : -INFINITY;
+    const float x = load_logit<DT>(row, e < V ? e : (int64_t)c * kChunk);
+    return e < V ? x : -INFINITY;
 }
 
-// The lane's k-th vector of chunk c of a row that row_vectors admits, -inf
-// past V.
+// The lane's k-th vector of chunk c (c < nch) of a row that row_vectors
+// admits, -inf past V.  The load is unconditional (past V it re-reads the
+// chunk's first vector, which lies inside the row) and the select comes
+// after: a load under a branch would be waited for at the branch's end.
 template <int DT>
 __device__ __forceinline__ uint4 chunk_vec_tail(const char* __restrict__ row, int V, int c, int k, int lane)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     const int64_t e0 = (int64_t)c * kChunk + (int64_t)(64 * k + lane) * EPV;
-    if (e0 < V) return chunk_vec<DT>(row, c, k, lane);
+    const bool in = e0 < V;
+    const uint4 v = chunk_vec<DT>(row, c, in ? k : 0, in ? lane : 0);
     const uint32_t ninf = DT == DT_BF16 ? 0xFF80FF80u : 0xFF800000u;
-    return make_uint4(ninf, ninf, ninf, ninf);
+    return in ? v : make_uint4(ninf, ninf, ninf, ninf);
 }
 
 // The lane's k-th vector of chunk c, decoded, for any row (vec: the row
@@ -884,12 +951,17 @@ __device__ __forceinline__ void chunk_elems(const char* row, bool vec, int V, in
     }
 }
 
-// ExpRow of K logits.
-template <int K>
+// ExpRow of K logits: TAB, the table's batched reads (exp_batch); else
+// exp_rel inline (kernels that never take the table).
+template <int K, bool TAB>
 __device__ __forceinline__ void exp_vec(const ExpRow& e, const float* x, double* out)
 {
+    if constexpr (TAB) {
+        exp_batch<K>(e, x, out);
+    } else {
 #pragma unroll
-    for (int i = 0; i < K; ++i) out[i] = e(x[i]);
+        for (int i = 0; i < K; ++i) out[i] = e.slow(x[i]);
+    }
 }
 
 // Centre and widened half-width of the near-threshold band [thr_lo, thr_hi]
@@ -910,14 +982,14 @@ __device__ __forceinline__ NearBand near_band(const SeqState& s)
 // The residual's all-token and certain-region sums (sa sb pa pb of
 // ChunkSums) over K token pairs; nd tracks the smallest |d - mid| (see
 // NearBand), so a lane saw a near-threshold token iff nd <= hw.
-template <int K>
+template <int K, bool TAB>
 __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, const SeqState& s,
                                              const NearBand& nb, const ExpRow& eq, const ExpRow& ep,
                                              double* acc, float& nd)
 {
     double a[K], bb[K];
-    exp_vec<K>(eq, zq, a);
-    exp_vec<K>(ep, zp, bb);
+    exp_vec<K, TAB>(eq, zq, a);
+    exp_vec<K, TAB>(ep, zp, bb);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
         acc[0] += a[i];
@@ -935,7 +1007,7 @@ __device__ __forceinline__ void residual_vec(const float* zq, const float* zp, c
 // element in the lane order of the vector loops, so each lane's sums equal
 // those the fused loop would form.  Taken only when a wave saw a near token
 // in the chunk (none in most chunks).
-template <int DT>
+template <int DT, bool TAB>
 __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
                                            const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
                                            ChunkSums& out)
@@ -955,8 +1027,8 @@ __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState
         for (int i = 0; i < EPV; ++i) {
             const float d = xq[i] - xp[i];
             if (d >= s.thr_lo && !(d > s.thr_hi)) {
-                na += eq(xq[i]);
-                nb += ep(xp[i]);
+                na += TAB ? eq.inl(xq[i]) : eq.slow(xq[i]);
+                nb += TAB ? ep.inl(xp[i]) : ep.slow(xp[i]);
                 dmin = fminf(dmin, d);
                 dmax = fmaxf(dmax, d);
             }
@@ -971,7 +1043,7 @@ __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState
 // The residual's sums over chunk c by one wave (see residual_vec); returns
 // whether the wave saw a near-threshold token.  Vector rows: every load of
 // the chunk issued first, then one vector at a time.
-template <int DT>
+template <int DT, bool TAB>
 __device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqState& s, const char* qrow,
                                                const char* prow, int c, const ExpRow& eq, const ExpRow& ep,
                                                double* acc)
@@ -993,7 +1065,7 @@ __device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqS
             float xq[EPV], xp[EPV];
             decode16<DT>(vq[k], xq);
             decode16<DT>(vp[k], xp);
-            residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
+            residual_vec<EPV, TAB>(xq, xp, s, nb, eq, ep, acc, nd);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
@@ -1002,7 +1074,7 @@ __device__ __forceinline__ bool residual_chunk(const VerifyParams& P, const SeqS
             float xq[EPV], xp[EPV];
             chunk_elems<DT>(qrow, false, P.V, c, k, lane, xq);
             chunk_elems<DT>(prow, false, P.V, c, k, lane, xp);
-            residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
+            residual_vec<EPV, TAB>(xq, xp, s, nb, eq, ep, acc, nd);
         }
     }
     return nd <= nb.hw;
@@ -1042,7 +1114,7 @@ __device__ __forceinline__ void bonus_max(const VerifyParams& P, const char* qro
     }
 }
 
-template <int DT>
+template <int DT, bool TAB>
 __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* qrow, int c, const ExpRow& ec)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
@@ -1051,7 +1123,7 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
     double sa = 0.0;
     auto add = [&](const float* x) {
         double a[EPV];
-        exp_vec<EPV>(ec, x, a);
+        exp_vec<EPV, TAB>(ec, x, a);
 #pragma unroll
         for (int i = 0; i < EPV; ++i) sa += a[i];
     };
@@ -1078,10 +1150,12 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
 }
 
 // Chunk sums of the whole chunks [ca, cb) of 16-byte aligned rows, by one
-// wave, stored as records: the loads of the next batch are issued before the
-// current batch is used, across chunk boundaries.  BONUS: the q row alone,
-// summed against its pass-1 reference s.mq; otherwise the residual's sums
-// over the q and p rows.
+// wave, stored as records, through exp_rel.  BONUS: the q row alone, summed
+// against its pass-1 reference s.mq; otherwise the residual's sums over the
+// q and p rows.  The loop runs over whole chunks with the chunk's vectors
+// unrolled: D slots per row, slot k % D refilled with the vector D ahead
+// (clamped to the range's last), and no exit inside a chunk, so the slots
+// keep their registers and each vector waits only for its own loads.
 template <int DT, bool BONUS>
 __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
                             int ca, int cb, const ExpRow& eq, const ExpRow& ep)
@@ -1089,83 +1163,284 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;  // vectors per lane per chunk: bf16 4, fp32 8
     constexpr int D = BONUS ? kBonusAhead : kLaneAhead;
+    static_assert(PER % D == 0, "slots rotate within a chunk");
     const int lane = threadIdx.x & 63;
-    // the lane's t-th vector of the range: vector k = t % PER of chunk ca + t / PER
-    auto vec_q = [&](int t) { return chunk_vec<DT>(qrow, ca + t / PER, t % PER, lane); };
-    auto vec_p = [&](int t) { return chunk_vec<DT>(prow, ca + t / PER, t % PER, lane); };
-    const int tend = (cb - ca) * PER;
-    if (tend <= 0) return;
-    // D slots per row hold the next D vectors; step t uses slot t % D and
-    // refills it with vector t + D.  The loop is unrolled by D so the slots
-    // rotate without register moves (moving a register a load is still
-    // writing would wait for that load).
-    uint4 rq[D], rp[D];
+    const int nvec = (cb - ca) * PER;
+    if (nvec <= 0) return;
+    const uint4* vq = reinterpret_cast<const uint4*>(qrow) + (int64_t)ca * (kChunk / EPV) + lane;
+    const uint4* vp = reinterpret_cast<const uint4*>(prow) + (int64_t)ca * (kChunk / EPV) + lane;
+    uint4 sq[D], sp[D];
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-        rq[j] = j < tend ? vec_q(j) : rq[0];
-        if constexpr (!BONUS) rp[j] = j < tend ? vec_p(j) : rp[0];
+        const int t = min(j, nvec - 1);
+        sq[j] = vq[64 * t];
+        sp[j] = BONUS ? sq[j] : vp[64 * t];
     }
     double acc[4] = {0.0, 0.0, 0.0, 0.0};
     const NearBand nb = near_band(s);
     float nd = INFINITY;
 #pragma unroll 1
-    for (int t0 = 0; t0 < tend; t0 += D) {
+    for (int c = ca; c < cb; ++c) {
+        const int t0 = (c - ca) * PER;
 #pragma unroll
-        for (int j = 0; j < D; ++j) {
-            const int t = t0 + j;
-            if (t >= tend) break;
+        for (int k = 0; k < PER; ++k) {
+            const int j = k % D;
             float xq[EPV], xp[EPV];
-            decode16<DT>(rq[j], xq);
-            if constexpr (!BONUS) decode16<DT>(rp[j], xp);
-            if (t + D < tend) {
-                rq[j] = vec_q(t + D);
-                if constexpr (!BONUS) rp[j] = vec_p(t + D);
-            }
+            decode16<DT>(sq[j], xq);
+            if constexpr (!BONUS) decode16<DT>(sp[j], xp);
+            const int tn = min(t0 + k + D, nvec - 1);
+            sq[j] = vq[64 * tn];
+            if constexpr (!BONUS) sp[j] = vp[64 * tn];
             if constexpr (BONUS) {
                 double a[EPV];
-                exp_vec<EPV>(eq, xq, a);
+                exp_vec<EPV, false>(eq, xq, a);
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) acc[0] += a[i];
             } else {
-                residual_vec<EPV>(xq, xp, s, nb, eq, ep, acc, nd);
+                residual_vec<EPV, false>(xq, xp, s, nb, eq, ep, acc, nd);
             }
-            if ((t + 1) % PER == 0) {
-                const int c = ca + t / PER;
-                ChunkSums out{};
-                if constexpr (BONUS) {
-                    out.sa = (double)s.mq;
-                    out.sb = wave_sum(acc[0]);
-                } else {
-                    out.sa = wave_sum(acc[0]);
-                    out.sb = wave_sum(acc[1]);
-                    out.pa = wave_sum(acc[2]);
-                    out.pb = wave_sum(acc[3]);
-                    out.dmin = INFINITY;
-                    out.dmax = -INFINITY;
-                    if (__ballot(nd <= nb.hw)) near_chunk<DT>(P, s, qrow, prow, c, eq, ep, out);
-                    nd = INFINITY;
-                }
-                if (lane == 0) put_chunk(P, b, c, out);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[i] = 0.0;
-            }
+            // the sums are formed here, vector by vector
+            asm volatile("" : "+v"(acc[0]), "+v"(acc[1]), "+v"(acc[2]), "+v"(acc[3]), "+v"(nd));
 #if SV_STEP_BARRIER
             __builtin_amdgcn_sched_barrier(0);  // one vector's work at a time
 #endif
         }
+        ChunkSums out{};
+        if constexpr (BONUS) {
+            out.sa = (double)s.mq;
+            out.sb = wave_sum(acc[0]);
+        } else {
+            out.sa = wave_sum(acc[0]);
+            out.sb = wave_sum(acc[1]);
+            out.pa = wave_sum(acc[2]);
+            out.pb = wave_sum(acc[3]);
+            out.dmin = INFINITY;
+            out.dmax = -INFINITY;
+            if (__ballot(nd <= nb.hw)) near_chunk<DT, false>(P, s, qrow, prow, c, eq, ep, out);
+            nd = INFINITY;
+        }
+        if (lane == 0) put_chunk(P, b, c, out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = 0.0;
     }
+}
+
+// Sums of one wave over a chunk of the table path.
+struct TabSums {
+    double acc[4];  // sa sb pa pb: table values, units of exp(z/T)
+    double fix[4];  // the same from logits outside the table, units of exp((z - m)/T)
+    float nd;       // smallest |d - mid| seen (see NearBand)
+};
+
+// One 16-byte vector per row (8 token pairs, or 8 tokens of the q row alone
+// for BONUS) into the sums: 16 table reads issued together, then the terms;
+// a ballot sends a vector with a logit outside the table to the rare path,
+// one element per trip.
+template <bool BONUS>
+__device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const SeqState& s, const NearBand& nb,
+                                           const ExpRow& eq, const ExpRow& ep, uint32_t lo, lds_cptr tab,
+                                           TabSums& A)
+{
+    const uint32_t wq[4] = {vq.x, vq.y, vq.z, vq.w};
+    const uint32_t wp[4] = {vp.x, vp.y, vp.z, vp.w};
+    const u16x2 lo2 = {(unsigned short)lo, (unsigned short)lo};
+    u16x2 worst = {0, 0};
+    double e[8], f[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t a0, a1;
+        tab_offsets(wq[k], lo2, a0, a1, worst);
+        e[2 * k] = lds_f64(tab, a0);
+        e[2 * k + 1] = lds_f64(tab, a1);
+        if constexpr (!BONUS) {
+            tab_offsets(wp[k], lo2, a0, a1, worst);
+            f[2 * k] = lds_f64(tab, a0);
+            f[2 * k + 1] = lds_f64(tab, a1);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if constexpr (BONUS) {
+            A.acc[0] += e[i];
+        } else {
+            const float zq = (i & 1) ? bf16_hi(wq[i >> 1]) : bf16_lo(wq[i >> 1]);
+            const float zp = (i & 1) ? bf16_hi(wp[i >> 1]) : bf16_lo(wp[i >> 1]);
+            const float d = zq - zp;
+            const double fa = d > s.thr_hi ? 1.0 : 0.0;
+            A.acc[0] += e[i];
+            A.acc[1] += f[i];
+            A.acc[2] = fma(fa, e[i], A.acc[2]);
+            A.acc[3] = fma(fa, f[i], A.acc[3]);
+            A.nd = fminf(A.nd, fabsf(d - nb.mid));
+        }
+    }
+    if (__any(max((uint32_t)worst.x, (uint32_t)worst.y) >= (uint32_t)kTabKeys)) {
+        // logits outside the table: their terms went in as zeros.  One
+        // element per trip, its word chosen by selects (a rolled loop keeps
+        // the rare path's registers few).
+#pragma unroll 1
+        for (int i = 0; i < 8; ++i) {
+            const int k = i >> 1;
+            const uint32_t w = k == 0 ? wq[0] : k == 1 ? wq[1] : k == 2 ? wq[2] : wq[3];
+            const float zq = (i & 1) ? bf16_hi(w) : bf16_lo(w);
+            const bool oq = tab_index(zq, lo) < 0;
+            if constexpr (BONUS) {
+                if (oq) A.fix[0] += eq.slow(zq);
+            } else {
+                const uint32_t v = k == 0 ? wp[0] : k == 1 ? wp[1] : k == 2 ? wp[2] : wp[3];
+                const float zp = (i & 1) ? bf16_hi(v) : bf16_lo(v);
+                const bool op = tab_index(zp, lo) < 0;
+                const double fa = (zq - zp > s.thr_hi) ? 1.0 : 0.0;
+                if (oq) {
+                    const double a = eq.slow(zq);
+                    A.fix[0] += a;
+                    A.fix[2] = fma(fa, a, A.fix[2]);
+                }
+                if (op) {
+                    const double bb = ep.slow(zp);
+                    A.fix[1] += bb;
+                    A.fix[3] = fma(fa, bb, A.fix[3]);
+                }
+            }
+        }
+    }
+}
+
+// chunk_range for 16-byte aligned bf16 rows with the bf16-grid table in LDS
+// (tab; see kTabKeys): each exponential is one table read.  The lane sums of
+// table values are in units of exp(z/T) and are scaled by the row's R once
+// per chunk; logits outside the table (none in most vectors) are added
+// through exp_rel, in units of exp((z - m)/T), to sums of their own.  Both
+// rows must have the table (eq.tabbed, and ep.tabbed unless BONUS).  The loop runs
+// over whole chunks with the chunk's vectors unrolled: D slots per row, slot
+// k % D refilled with the vector D ahead (clamped to the range's last), and
+// no exit inside a chunk, so the slots keep their registers.
+template <bool BONUS>
+__device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+                                int ca, int cb, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
+{
+    constexpr int PER = kChunk / 8 / 64;  // vectors per lane per chunk
+    constexpr int D = BONUS ? kBonusAhead : kLaneAhead;
+    static_assert(PER % D == 0, "slots rotate within a chunk");
+    const int lane = threadIdx.x & 63;
+    const int nvec = (cb - ca) * PER;
+    if (nvec <= 0) return;
+    const uint4* vq = reinterpret_cast<const uint4*>(qrow) + (int64_t)ca * (kChunk / 8) + lane;
+    const uint4* vp = reinterpret_cast<const uint4*>(prow) + (int64_t)ca * (kChunk / 8) + lane;
+    uint4 sq[D], sp[D];
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+        const int t = min(j, nvec - 1);
+        sq[j] = vq[64 * t];
+        sp[j] = BONUS ? sq[j] : vp[64 * t];
+    }
+    const NearBand nb = near_band(s);
+    TabSums A;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        A.acc[i] = 0.0;
+        A.fix[i] = 0.0;
+    }
+    A.nd = INFINITY;
+#pragma unroll 1
+    for (int c = ca; c < cb; ++c) {
+        const int t0 = (c - ca) * PER;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int j = k % D;
+            const uint4 xq = sq[j], xp = sp[j];
+            const int tn = min(t0 + k + D, nvec - 1);
+            sq[j] = vq[64 * tn];
+            if constexpr (!BONUS) sp[j] = vp[64 * tn];
+            tab_vector<BONUS>(xq, xp, s, nb, eq, ep, P.tab_lo, tab, A);
+            // the sums are formed here, vector by vector: without this the
+            // compiler may defer the additions to the chunk's end and keep
+            // every table value of the chunk in registers
+            asm volatile("" : "+v"(A.acc[0]), "+v"(A.acc[1]), "+v"(A.acc[2]), "+v"(A.acc[3]), "+v"(A.nd));
+#if SV_STEP_BARRIER
+            __builtin_amdgcn_sched_barrier(0);
+#endif
+        }
+        ChunkSums out{};
+        if constexpr (BONUS) {
+            out.sa = (double)s.mq;
+            out.sb = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+        } else {
+            out.sa = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+            out.sb = wave_sum(fma(ep.R, A.acc[1], A.fix[1]));
+            out.pa = wave_sum(fma(eq.R, A.acc[2], A.fix[2]));
+            out.pb = wave_sum(fma(ep.R, A.acc[3], A.fix[3]));
+            out.dmin = INFINITY;
+            out.dmax = -INFINITY;
+            if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+            A.nd = INFINITY;
+        }
+        if (lane == 0) put_chunk(P, b, c, out);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            A.acc[i] = 0.0;
+            A.fix[i] = 0.0;
+        }
+    }
+}
+
+// The partial last chunk c (V not a multiple of kChunk) of 16-byte aligned
+// bf16 rows from the LDS table, by one wave: as one chunk of
+// chunk_range_tab, with the vectors past V read as -inf (chunk_vec_tail);
+// their keys lie outside the table and add exp_rel(-inf) = 0.
+template <bool BONUS>
+__device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
+                                  const char* prow, int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
+{
+    constexpr int PER = kChunk / 8 / 64;
+    const int lane = threadIdx.x & 63;
+    uint4 vq[PER], vp[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        vq[k] = chunk_vec_tail<DT_BF16>(qrow, P.V, c, k, lane);
+        vp[k] = BONUS ? vq[k] : chunk_vec_tail<DT_BF16>(prow, P.V, c, k, lane);
+    }
+    const NearBand nb = near_band(s);
+    TabSums A;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        A.acc[i] = 0.0;
+        A.fix[i] = 0.0;
+    }
+    A.nd = INFINITY;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        tab_vector<BONUS>(vq[k], vp[k], s, nb, eq, ep, P.tab_lo, tab, A);
+        asm volatile("" : "+v"(A.acc[0]), "+v"(A.acc[1]), "+v"(A.acc[2]), "+v"(A.acc[3]), "+v"(A.nd));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    ChunkSums out{};
+    if constexpr (BONUS) {
+        out.sa = (double)s.mq;
+        out.sb = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+    } else {
+        out.sa = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+        out.sb = wave_sum(fma(ep.R, A.acc[1], A.fix[1]));
+        out.pa = wave_sum(fma(eq.R, A.acc[2], A.fix[2]));
+        out.pb = wave_sum(fma(ep.R, A.acc[3], A.fix[3]));
+        out.dmin = INFINITY;
+        out.dmax = -INFINITY;
+        if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+    }
+    if (lane == 0) put_chunk(P, b, c, out);
 }
 
 // Chunk sums of the row(s) a sequence samples from (see ChunkSums), by one
 // wave; valid in every lane.
-template <int DT>
-__device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, const char* qrow, const char* prow,
-                                     int c, const ExpRow& eq, const ExpRow& ep, const double* etab)
+template <int DT, bool TAB>
+__device__ __forceinline__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, const char* qrow, const char* prow,
+                                     int c, const ExpRow& eq, const ExpRow& ep, const double* etab,
+                                     const double* vt)
 {
     ChunkSums out{};
     if (s.mode == kModeResidual) {
         double acc[4] = {0.0, 0.0, 0.0, 0.0};  // sa sb pa pb
-        const bool near = residual_chunk<DT>(P, s, qrow, prow, c, eq, ep, acc);
+        const bool near = residual_chunk<DT, TAB>(P, s, qrow, prow, c, eq, ep, acc);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = wave_sum(acc[i]);
         out.sa = acc[0];
@@ -1174,11 +1449,11 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         out.pb = acc[3];
         out.dmin = INFINITY;
         out.dmax = -INFINITY;
-        if (__ballot(near)) near_chunk<DT>(P, s, qrow, prow, c, eq, ep, out);
+        if (__ballot(near)) near_chunk<DT, TAB>(P, s, qrow, prow, c, eq, ep, out);
     } else if (s.bonus_ref) {
         // against the row's pass-1 reference (its NaN/+inf check is the
         // pass-1 statistics')
-        const double sa = bonus_sum<DT>(P, qrow, c, eq);
+        const double sa = bonus_sum<DT, TAB>(P, qrow, c, eq);
         out.sa = (double)s.mq;
         out.sb = wave_sum(sa);
     } else {
@@ -1188,7 +1463,7 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
         bonus_max<DT>(P, qrow, c, lm, bad);
         const float mc = wave_max(lm);
         double sa = 0.0;
-        if (mc != -INFINITY) sa = bonus_sum<DT>(P, qrow, c, exp_row(P, mc, etab));
+        if (mc != -INFINITY) sa = bonus_sum<DT, TAB>(P, qrow, c, exp_row(P, mc, etab, vt));
         out.sa = (double)mc;
         out.sb = wave_sum(sa);
         out.flags = __any(bad) ? kFlagBad : 0u;
@@ -1198,15 +1473,22 @@ __device__ ChunkSums wave_chunk_sums(const VerifyParams& P, const SeqState& s, c
 
 // Exact weight of one element of the residual: a - rho*b where q > p for
 // certain, max(0, a - rho*b) in the near-threshold band, 0 below it.
+__device__ __forceinline__ double residual_weight_of(float xq, float xp, const SeqState& s, double a, double bb,
+                                                     double rho)
+{
+    const float d = xq - xp;
+    if (!(d >= s.thr_lo)) return 0.0;
+    const double w = a - rho * bb;
+    return (d > s.thr_hi) ? w : fmax(0.0, w);
+}
+
+template <bool TAB>
 __device__ __forceinline__ double residual_weight(float xq, float xp, const SeqState& s, const ExpRow& eq,
                                                   const ExpRow& ep, double rho)
 {
     const float d = xq - xp;
     if (!(d >= s.thr_lo)) return 0.0;
-    const double a = eq(xq);
-    const double bb = ep(xp);
-    const double w = a - rho * bb;
-    return (d > s.thr_hi) ? w : fmax(0.0, w);
+    return residual_weight_of(xq, xp, s, TAB ? eq.inl(xq) : eq.slow(xq), TAB ? ep.inl(xp) : ep.slow(xp), rho);
 }
 
 // Block-wide: every output slot of sequence b that does not depend on the
@@ -1300,21 +1582,21 @@ struct FinalPlan {
 // owns chunks [L*g, L*g + g), g = ceil(nch / 64)), forms the totals and
 // locates the chunk with wave scans and ballots, and hands the block a plan
 // through one barrier; the block then rescans the chunk.
-template <int DT, bool TREE>
-__device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path,
-                             const double* etab)
+// s_cs and s_near are LDS arrays of the caller (kFinalCache records and
+// kMaxChunks doubles); vt is the bf16-grid table or null.
+template <int DT, bool TREE, bool TAB>
+__device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const SeqState& s, const int32_t* path,
+                             const double* etab, ChunkSums* s_cs, double* s_near, const double* vt)
 {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nchunks = P.nch;
     const double invT = P.invT;
     __shared__ double red[kWaves];
-    __shared__ double s_near[kMaxChunks];
     __shared__ FinalPlan s_plan;
     __shared__ int s_cand[kWaves];
     __shared__ int s_token;
-    // the chunk records, kept in LDS (the first kFinalCache of them; later
-    // ones are read again when needed)
-    __shared__ ChunkSums s_cs[kFinalCache];
+    // the chunk records are kept in s_cs (the first kFinalCache of them;
+    // later ones are read again when needed)
     if (s.status) {
         emit<TREE>(P, b, -1, -1, 0.0, path);
         return;
@@ -1325,7 +1607,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
     auto chunk_at = [&](int c) -> ChunkSums { return c < kFinalCache ? s_cs[c] : get_chunk(P, b, c); };
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, etab), ep = exp_row(P, s.mp, etab);
+    const ExpRow eq = exp_row(P, s.mq, etab, vt), ep = exp_row(P, s.mp, etab, vt);
 
     // --- wave 0: records, totals, location ---
     const int g = (nchunks + 63) / 64;
@@ -1479,7 +1761,7 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
 #pragma unroll
             for (int j = 0; j < kPerThread; ++j) {
                 const float d = xq[j] - xp[j];
-                if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight(xq[j], xp[j], s, eq, ep, rho);
+                if (d >= s.thr_lo && !(d > s.thr_hi)) w[0] += residual_weight<TAB>(xq[j], xp[j], s, eq, ep, rho);
             }
             block_sum_n<1>(w, red);
             if (tid == 0) s_near[c] = w[0];
@@ -1501,13 +1783,16 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
         mc = chunk_at(cs).sa;
         scale = exp((mc - M) * invT);
     }
-    const ExpRow ec = exp_row(P, mc, etab);
+    const ExpRow ec = exp_row(P, mc, etab, vt);
     double wv[kPerThread];
+    if (mode == kModeResidual) {
+        double av[kPerThread], bv[kPerThread];
+        exp_vec<kPerThread, TAB>(eq, xq, av);
+        exp_vec<kPerThread, TAB>(ep, xp, bv);
 #pragma unroll
-    for (int j = 0; j < kPerThread; ++j) {
-        if (mode == kModeResidual) wv[j] = residual_weight(xq[j], xp[j], s, eq, ep, rho);
-        else if (mode == kModeFallback) wv[j] = eq(xq[j]);
-        else wv[j] = ec(xq[j]);
+        for (int j = 0; j < kPerThread; ++j) wv[j] = residual_weight_of(xq[j], xp[j], s, av[j], bv[j], rho);
+    } else {
+        exp_vec<kPerThread, TAB>(mode == kModeFallback ? eq : ec, xq, wv);
     }
     double tsum = 0.0;
 #pragma unroll
@@ -1560,13 +1845,80 @@ __device__ void sample_final(const VerifyParams& P, int b, const SeqState& s, co
 // ===========================================================================
 // Kernels
 // ===========================================================================
+// Entries x * kBlock + threadIdx.x of the bf16-grid table (see kTabKeys).
+__device__ __forceinline__ void fill_value_table(const VerifyParams& P, int x)
+{
+    const int i = x * kBlock + (int)threadIdx.x;
+    if (i >= kTabEntries) return;
+    const int sgn = i >= kTabHalf ? 1 : 0;
+    const int t = i - sgn * kTabHalf;
+    double v = 0.0;
+    if (t < kTabKeys) {
+        const uint32_t key = (P.tab_lo + (uint32_t)t) | ((uint32_t)sgn << 15);
+        v = exp((double)__uint_as_float(key << 16) / (double)P.T);
+    }
+    P.etab_g[i] = v;
+}
+
+// The block's LDS copy of the table (publish it with a barrier): every load
+// is issued before the first LDS store, so the copy costs one round trip.
+__device__ __forceinline__ void copy_value_table(const VerifyParams& P, double* pool)
+{
+    constexpr int N2 = kTabEntries / 2;
+    constexpr int PER = (N2 + kBlock - 1) / kBlock;
+    const double2* src = reinterpret_cast<const double2*>(P.etab_g);
+    double2* dst = reinterpret_cast<double2*>(pool);
+    double2 v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * kBlock;
+        v[k] = src[i < N2 ? i : N2 - 1];
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * kBlock;
+        if (i < N2) dst[i] = v[k];
+    }
+}
+
+// The final step's LDS arrays, carved from one pool: kFinalCache chunk
+// records, then kMaxChunks doubles.
+constexpr int kFinalPoolDoubles = (int)(kFinalCache * sizeof(ChunkSums) / sizeof(double));
+constexpr int kFinalPool = kFinalPoolDoubles + kMaxChunks;
+static_assert(kTabEntries % 2 == 0, "table copied as double2");
+
+// Chunk sums of chunks [c, cb) of sequence b by the calling wave through
+// exp_rel: whole chunks of aligned rows in one streaming range, the rest
+// chunk by chunk.
+template <int DT>
+__device__ __forceinline__ void wave_chunks(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
+                                            const char* prow, int c, int cb, const ExpRow& eq, const ExpRow& ep,
+                                            const double* etab)
+{
+    if (s.status == 0 && (s.mode == kModeResidual || s.bonus_ref) &&
+        ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
+        const int whole = min(cb, P.V / kChunk);
+        if (whole > c) {
+            if (s.mode == kModeResidual) chunk_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
+            else chunk_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
+            c = whole;
+        }
+    }
+    for (; c < cb; ++c) {
+        ChunkSums out{};
+        if (s.status == 0) out = wave_chunk_sums<DT, false>(P, s, qrow, prow, c, eq, ep, etab, nullptr);
+        if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
+    }
+}
+
 // 16-byte loads per thread per batch of a row block
 #ifndef SV_ROW_BATCH
 #define SV_ROW_BATCH 4
 #endif
 constexpr int kRowBatch = SV_ROW_BATCH;
 // Row kernel: block (b, row, segment) streams one segment of a pass-1 row
-// and stores its (m, s) record.  Chains: rows 0..N are q rows 0..N (row N
+// and stores its (m, s) record.  Then come the blocks that fill the bf16-grid
+// table (bf16 logits) and, for chains, B blocks of one accept test each.  Chains: rows 0..N are q rows 0..N (row N
 // the bonus row) and rows N+1..2N the p rows 0..N-1.  Trees: row 2n is node
 // n's q row and 2n+1 its p row, streamed only for nodes that have a child
 // (an accept test reads them; the others get a placeholder record).  Many small blocks, dispatched as
@@ -1575,6 +1927,21 @@ constexpr int kRowBatch = SV_ROW_BATCH;
 template <int DT, bool TREE>
 __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
 {
+    const int nrow_blocks = P.B * P.r_items;
+    if ((int)blockIdx.x >= nrow_blocks) {
+        const int x = (int)blockIdx.x - nrow_blocks;
+        if (x < P.tab_blocks) {
+            fill_value_table(P, x);
+            return;
+        }
+        // chains: the accept test of sequence x - tab_blocks, by wave 0.
+        // Blocks are dispatched in index order, so every row block has
+        // started when this one does; it polls b's records as they land.
+        if (TREE || threadIdx.x >= 64) return;
+        const int b = x - P.tab_blocks;
+        chain_accept<DT>(P, b, P.seqs[b], true);
+        return;
+    }
     const int b = (int)blockIdx.x / P.r_items;
     const int idx = (int)blockIdx.x - b * P.r_items;
     const int row = idx / P.segs, seg = idx - row * P.segs;
@@ -1615,6 +1982,7 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     __shared__ SeqState s_state;
     __shared__ int32_t s_path[kMaxNodes];
     __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_pool[kFinalPool];
     fill_exp_table(s_etab);
     tree_accept<DT>(P, b, s_state, s_path, g == 0);
     __syncthreads();
@@ -1622,48 +1990,28 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, s_etab), ep = exp_row(P, s.mp, s_etab);
+    const ExpRow eq = exp_row(P, s.mq, s_etab, nullptr), ep = exp_row(P, s.mp, s_etab, nullptr);
     // each wave takes a contiguous share of the block's chunks; whole chunks
     // of aligned rows stream with loads in flight across chunk boundaries
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
     const int wave = (int)threadIdx.x >> 6;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
-    int c = ca;
-    if (s.status == 0 && (s.mode == kModeResidual || s.bonus_ref) &&
-        ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
-        const int whole = min(cb, P.V / kChunk);
-        if (whole > c) {
-            if (s.mode == kModeResidual) chunk_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-            else chunk_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-            c = whole;
-        }
-    }
-    for (; c < cb; ++c) {
-        ChunkSums out{};
-        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_etab);
-        if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
-    }
+    wave_chunks<DT>(P, b, s, qrow, prow, ca, cb, eq, ep, s_etab);
     __syncthreads();
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
     __syncthreads();
-    if (s_last) sample_final<DT, true>(P, b, s, s_path, s_etab);
+    if (s_last)
+        sample_final<DT, true, false>(P, b, s, s_path, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
+                               s_pool + kFinalPoolDoubles, nullptr);
 }
 
 // ---------------------------------------------------------------------------
-// Chain sample step in three launches
+// Chain sample step
 // ---------------------------------------------------------------------------
-// Each latency-bound step runs once per sequence, in its own launch: the
-// accept test (one wave per sequence), the chunk sums (many blocks per
-// sequence, where the arithmetic is), the final step (one block per
-// sequence).  Launch boundaries order them; nothing waits on another block.
-
-// Accept test of sequence blockIdx.x into P.seqs (and the accept outputs).
-template <int DT>
-__global__ __launch_bounds__(64) void k_accept(const VerifyParams P)
-{
-    chain_accept<DT>(P, (int)blockIdx.x, P.seqs[blockIdx.x], true);
-}
+// The accept tests ran at the end of the row launch; this launch forms the
+// chunk sums (many blocks per sequence, where the arithmetic is) and ends
+// with the final step (one block per sequence).
 
 // Blocks [0, B*groups): block (b, g) forms the chunk sums of group g of
 // sequence b's chunks, one contiguous share per wave, stored as records.
@@ -1680,13 +2028,15 @@ __attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
 k_chunks(const VerifyParams P)
 {
     __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_pool[kFinalPool];
     const int nblocks = P.B * P.groups;
     if ((int)blockIdx.x >= nblocks) {
         const int b = (int)blockIdx.x - nblocks;
         const SeqState s = P.seqs[b];
         // first read after sample_final's first barrier
         fill_exp_table(s_etab);
-        sample_final<DT, false>(P, b, s, nullptr, s_etab);
+        sample_final<DT, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
+                                s_pool + kFinalPoolDoubles, nullptr);
         return;
     }
     const int b = (int)blockIdx.x / P.groups;
@@ -1697,24 +2047,97 @@ k_chunks(const VerifyParams P)
     const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
     const char* qrow = sample_qrow<DT>(P, b, s);
     const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, s_etab), ep = exp_row(P, s.mp, s_etab);
+    const ExpRow eq = exp_row(P, s.mq, s_etab, nullptr), ep = exp_row(P, s.mp, s_etab, nullptr);
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
     const int wave = (int)threadIdx.x >> 6;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
-    int c = ca;
-    if (s.status == 0 && ((((uintptr_t)qrow) | ((uintptr_t)prow)) & 15u) == 0) {
-        const int whole = min(cb, P.V / kChunk);
-        if (whole > c) {
-            if (s.mode == kModeResidual) chunk_range<DT, false>(P, b, s, qrow, prow, c, whole, eq, ep);
-            else chunk_range<DT, true>(P, b, s, qrow, prow, c, whole, eq, ep);
-            c = whole;
+    wave_chunks<DT>(P, b, s, qrow, prow, ca, cb, eq, ep, s_etab);
+}
+
+// ---------------------------------------------------------------------------
+// Chain sample step of bf16 logits in 16-byte aligned rows: the table path
+// ---------------------------------------------------------------------------
+// Whether sequence b's whole chunks are formed by k_chunk_tab: both rows it
+// samples from take the bf16-grid table.
+__device__ __forceinline__ bool tab_rows(const SeqState& s, const ExpRow& eq, const ExpRow& ep)
+{
+    return s.status == 0 && eq.tabbed && (s.mode != kModeResidual || ep.tabbed);
+}
+
+// Block g * B + b forms the sums of group g of sequence b's whole chunks
+// from the block's LDS copy of the table, one contiguous share per wave;
+// wave 0 of group 0 also forms the partial last chunk.  Nothing here calls a
+// function, so the streaming loop keeps its registers.
+__global__ __launch_bounds__(kBlock) void
+#if SV_CHUNK_WAVES
+__attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
+#endif
+k_chunk_tab(const VerifyParams P)
+{
+    __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_tab[kTabEntries];
+    // group-major: every sequence's group 0 is in the first blocks dispatched
+    const int g = (int)blockIdx.x / P.B;
+    const int b = (int)blockIdx.x - g * P.B;
+    const SeqState s = P.seqs[b];  // in flight with the table copies
+    fill_exp_table(s_etab);
+    copy_value_table(P, s_tab);
+    __syncthreads();
+    const ExpRow eq = exp_row(P, s.mq, s_etab, s_tab), ep = exp_row(P, s.mp, s_etab, s_tab);
+    if (!tab_rows(s, eq, ep)) return;  // the final step forms them
+    const int whole = P.V / kChunk;
+    const int c0 = g * P.cpb, c1 = min(whole, c0 + P.cpb);
+    const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+    const int wave = (int)threadIdx.x >> 6;
+    const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+    const char* qrow = sample_qrow<DT_BF16>(P, b, s);
+    const char* prow = s.mode == kModeResidual ? sample_prow<DT_BF16>(P, b, s) : qrow;
+    // the partial chunk (if any) first, by wave 0 of group 0: its latency
+    // passes while the rest of the grid streams
+    const bool partial = P.nch > whole && g == 0 && wave == 0;
+    if (s.mode == kModeResidual) {
+        if (partial) partial_chunk_tab<false>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_tab);
+        chunk_range_tab<false>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_tab);
+    } else {
+        if (partial) partial_chunk_tab<true>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_tab);
+        chunk_range_tab<true>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_tab);
+    }
+}
+
+// The final step of sequence blockIdx.x after k_chunk_tab: first, for a
+// sequence whose rows do not take the table, its chunk sums (k_chunk_tab
+// skipped it), then sample_final; element-wise exponentials read the block's
+// LDS copy of the table.
+__global__ __launch_bounds__(kBlock) void k_final_tab(const VerifyParams P)
+{
+    __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_pool[kFinalPool];
+    __shared__ __align__(16) double s_tab[kTabEntries];
+    const int b = (int)blockIdx.x;
+    const SeqState s = P.seqs[b];
+    fill_exp_table(s_etab);
+    copy_value_table(P, s_tab);
+    __syncthreads();
+    const ExpRow eqt = exp_row(P, s.mq, s_etab, s_tab), ept = exp_row(P, s.mp, s_etab, s_tab);
+    if (s.status == 0 && !tab_rows(s, eqt, ept)) {
+        // rows without the table: every chunk here, through exp_rel
+        const int c_begin = 0;
+        const char* qrow = sample_qrow<DT_BF16>(P, b, s);
+        const char* prow = s.mode == kModeResidual ? sample_prow<DT_BF16>(P, b, s) : qrow;
+        const int n = P.nch - c_begin;
+        const int cpw = (n + kWaves - 1) / kWaves;
+        const int wave = (int)threadIdx.x >> 6;
+        const int ca = min(P.nch, c_begin + wave * cpw), cb = min(P.nch, ca + cpw);
+        // chunk by chunk, from the table where the row has it (as the
+        // streamed chunks were), else through exp_rel
+        for (int c = ca; c < cb; ++c) {
+            const ChunkSums out = wave_chunk_sums<DT_BF16, true>(P, s, qrow, prow, c, eqt, ept, s_etab, s_tab);
+            if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
         }
     }
-    for (; c < cb; ++c) {
-        ChunkSums out{};
-        if (s.status == 0) out = wave_chunk_sums<DT>(P, s, qrow, prow, c, eq, ep, s_etab);
-        if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
-    }
+    // sample_final reads every record, polling those this block just wrote
+    sample_final<DT_BF16, false, true>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
+                                 s_pool + kFinalPoolDoubles, s_tab);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -1775,7 +2198,7 @@ int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 }
 
 struct Layout {
-    size_t chunk_arr, seqs, stats, part, total;
+    size_t chunk_arr, seqs, stats, part, tab, total;
 };
 
 Layout make_layout(int B, int rows, int V)
@@ -1787,14 +2210,31 @@ Layout make_layout(int B, int rows, int V)
     L.seqs = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
     L.stats = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
     L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
-    L.total = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
+    L.tab = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
+    L.total = L.tab + align_up((size_t)sv::kTabEntries * sizeof(double));
     return L;
 }
 
 // The record regions are addressed with 32-bit buffer offsets.
 bool regions_fit(const Layout& L)
 {
-    return L.part - L.stats <= (size_t)INT32_MAX && L.total - L.part <= (size_t)INT32_MAX;
+    return L.part - L.stats <= (size_t)INT32_MAX && L.tab - L.part <= (size_t)INT32_MAX;
+}
+
+// The bf16-grid table of a temperature: binades [2^(e-12), 2^(e+7)), e =
+// floor(log2 T), as magnitude keys from `lo`; false where that range leaves
+// the normal bf16 exponents (then calls use exp_rel throughout).
+#ifndef SV_VALUE_TABLE
+#define SV_VALUE_TABLE 1
+#endif
+bool value_table_range(float T, uint32_t* lo)
+{
+    int e2 = 0;
+    frexp((double)T, &e2);  // T = f 2^e2, f in [0.5, 1)
+    const int blo = 127 + (e2 - 1) - 12;
+    if (!SV_VALUE_TABLE || blo < 1 || blo + sv::kTabBinades > 255) return false;
+    *lo = (uint32_t)blo << 7;
+    return true;
 }
 
 int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
@@ -1841,9 +2281,13 @@ void set_groups(sv::VerifyParams& P)
 }
 
 // Chunk-sum blocks per sequence (chains): about SV_CHUNKS_PER_BLOCK chunks
-// each.
+// each, SV_TAB_CHUNKS_PER_BLOCK with the bf16-grid table (each block copies
+// the table into LDS first, so fewer blocks carry more chunks).
 #ifndef SV_CHUNKS_PER_BLOCK
 #define SV_CHUNKS_PER_BLOCK 4
+#endif
+#ifndef SV_TAB_CHUNKS_PER_BLOCK
+#define SV_TAB_CHUNKS_PER_BLOCK 8
 #endif
 // The row kernel; with a timing hook, its begin and rows_done events are
 // stamped by the kernel's own start and end (not by records beside it, whose
@@ -1856,20 +2300,35 @@ void launch_rows(const sv::VerifyParams& P, int64_t grid, const sv_timing* timin
                           P);
 }
 
-// Chains: the row kernel, then the sample step (accept; chunk sums and final).
+// Chains: the row kernel (row statistics, table, accept tests), then the
+// sample step: with the bf16-grid table, the table's chunk kernel and the
+// final kernel; otherwise one kernel of chunk sums and finals.
 template <int DT>
 int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
-    int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
-    groups = groups < 1 ? 1 : groups;
-    P.cpb = (P.nch + groups - 1) / groups;
-    P.groups = (P.nch + P.cpb - 1) / P.cpb;
-    const unsigned B = (unsigned)P.B;
-    launch_rows<DT, false>(P, (int64_t)P.B * P.r_items, timing, stream);
-    hipLaunchKernelGGL((sv::k_accept<DT>), dim3(B), dim3(64), 0, stream, P);
-    // chunk-sum blocks, then one final-step block per sequence
-    hipExtLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
-                          stream, nullptr, timing ? timing->end : nullptr, 0, P);
+    const hipEvent_t t_end = timing ? timing->end : nullptr;
+    if (P.use_tab) {
+        const int whole = P.V / sv::kChunk;
+        int groups = (whole + SV_TAB_CHUNKS_PER_BLOCK - 1) / SV_TAB_CHUNKS_PER_BLOCK;
+        groups = groups < 1 ? 1 : groups;
+        P.cpb = (whole + groups - 1) / groups;
+        P.cpb = P.cpb < 1 ? 1 : P.cpb;
+        P.groups = groups;
+        launch_rows<DT, false>(P, (int64_t)P.B * (P.r_items + 1) + P.tab_blocks, timing, stream);
+        hipLaunchKernelGGL(sv::k_chunk_tab, dim3((unsigned)((int64_t)P.B * P.groups)), dim3(sv::kBlock), 0, stream,
+                           P);
+        hipExtLaunchKernelGGL(sv::k_final_tab, dim3((unsigned)P.B), dim3(sv::kBlock), 0, stream, nullptr, t_end, 0,
+                              P);
+    } else {
+        int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
+        groups = groups < 1 ? 1 : groups;
+        P.cpb = (P.nch + groups - 1) / groups;
+        P.groups = (P.nch + P.cpb - 1) / P.cpb;
+        launch_rows<DT, false>(P, (int64_t)P.B * (P.r_items + 1) + P.tab_blocks, timing, stream);
+        // chunk-sum blocks, then one final-step block per sequence
+        hipExtLaunchKernelGGL((sv::k_chunks<DT>), dim3((unsigned)((int64_t)P.B * (P.groups + 1))),
+                              dim3(sv::kBlock), 0, stream, nullptr, t_end, 0, P);
+    }
     if (hipGetLastError() != hipSuccess) return SV_EHIP;
     return SV_OK;
 }
@@ -1879,8 +2338,7 @@ template <int DT>
 int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
     set_groups<DT>(P);
-    // at least one row block: the row kernel also fills the exp table
-    const int64_t row_grid = (int64_t)P.B * P.r_items;
+    const int64_t row_grid = (int64_t)P.B * P.r_items + P.tab_blocks;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     launch_rows<DT, true>(P, row_grid, timing, stream);
     hipExtLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, nullptr,
@@ -1898,8 +2356,14 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     P.seqs = reinterpret_cast<sv::SeqState*>(ws + L.seqs);
     P.stats = ws + L.stats;
     P.part = ws + L.part;
+    P.etab_g = reinterpret_cast<double*>(ws + L.tab);
     P.stats_bytes = (uint32_t)(L.part - L.stats);
-    P.part_bytes = (uint32_t)(L.total - L.part);
+    P.part_bytes = (uint32_t)(L.tab - L.part);
+    // the table path: chains of bf16 logits whose rows are all 16-byte aligned
+    const bool aligned = (((uintptr_t)P.zq | (uintptr_t)P.zp) & 15u) == 0 && P.qs % 8 == 0 && P.qr % 8 == 0 &&
+                         P.ps % 8 == 0 && P.pr % 8 == 0;
+    P.use_tab = !TREE && dtype == SV_BF16 && aligned && value_table_range(P.T, &P.tab_lo) ? 1 : 0;
+    P.tab_blocks = P.use_tab ? (sv::kTabEntries + sv::kBlock - 1) / sv::kBlock : 0;
     P.epoch = next_epoch();
     if constexpr (!TREE)
         return dtype == SV_BF16 ? launch_chain<sv::DT_BF16>(P, timing, stream)
@@ -1930,7 +2394,7 @@ bool item_count_ok(int B, int rows, int V)
 {
     int segs, seg_len;
     segments_of(V, &segs, &seg_len);
-    return 2 * (int64_t)B * rows * segs < (int64_t)INT32_MAX && (int64_t)B * (nchunks_of(V) + 1) < (int64_t)INT32_MAX;
+    return 2 * (int64_t)B * rows * segs + 64 < (int64_t)INT32_MAX && (int64_t)B * (nchunks_of(V) + 1) < (int64_t)INT32_MAX;
 }
 
 }  // namespace

@@ -136,6 +136,68 @@ __device__ __forceinline__ void fill_exp_table(double* tab)
 }
 
 // ---------------------------------------------------------------------------
+// exp(z/T) over the bf16 grid
+// ---------------------------------------------------------------------------
+// A bf16 logit has 8 significant bits, so the logits of a row take few
+// distinct values.  A call with bf16 logits fills a table E of exp(z/T) in
+// double (the math library's exp, one rounding of z/T before it) for every
+// bf16 z whose magnitude lies in the kTabBinades binades [2^(e-12), 2^(e+7)),
+// e = floor(log2 T): there |z|/T lies in (2^-13, 2^7).  Entry s (kTabKeys +
+// 1) + t holds the value with magnitude bits (lo + t) and sign s, lo = (127 +
+// e - 12) << 7; entries t = kTabKeys are zero.  exp((z - m)/T) is then
+// E(z) * R with R = exp(-m/T), for rows whose reference has |m/T| <=
+// kTabRefLimit (both factors and the product stay far inside the double
+// range).  Logits outside the table (tiny or huge magnitudes, -inf, NaN) take
+// exp_rel.  The table is split by sign, kTabKeys + 1 entries each (so the
+// logits of one sign, the common case, spread over every LDS bank).
+constexpr int kTabBinades = 19;
+constexpr int kTabKeys = kTabBinades * 128;
+constexpr int kTabHalf = kTabKeys + 1;
+constexpr int kTabEntries = 2 * kTabHalf;
+constexpr double kTabRefLimit = 512.0;
+
+// Entry index of a bf16 logit (decoded to a float), or -1 outside the table.
+__host__ __device__ __forceinline__ int tab_index(float z, uint32_t lo)
+{
+    const uint32_t key = __builtin_bit_cast(uint32_t, z) >> 16;
+    const uint32_t t = (key & 0x7FFFu) - lo;
+    return t < (uint32_t)kTabKeys ? (int)(t + (key >> 15) * (uint32_t)kTabHalf) : -1;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef const char __attribute__((address_space(3)))* lds_cptr;
+
+// LDS byte offsets (8 * entry index) of the two bf16 logits packed in w, low
+// half first, both formed by 16-bit packed arithmetic; a magnitude outside
+// the table maps to a zero entry.  `worst` keeps the largest unclamped index
+// t per half: a value of kTabKeys or more marks an element outside the table.
+static_assert(8 * kTabEntries < 65536, "byte offsets fit 16 bits");
+__host__ __device__ __forceinline__ void tab_offsets(uint32_t w, u16x2 lo2, uint32_t& a0, uint32_t& a1,
+                                                     u16x2& worst)
+{
+    const u16x2 t = __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu) - lo2;
+    worst = __builtin_elementwise_max(worst, t);
+    const u16x2 c = __builtin_elementwise_min(t, u16x2{(unsigned short)kTabKeys, (unsigned short)kTabKeys});
+    const u16x2 c8 = c << (unsigned short)3;
+    // the sign bit spread over its half (arithmetic shift), masked to the
+    // second half's byte offset
+    typedef short i16x2 __attribute__((ext_vector_type(2)));
+    const i16x2 sgn = __builtin_bit_cast(i16x2, w) >> (short)15;
+    // (a 32-bit add of the packed halves: each half's sum stays below 2^16,
+    // so no carry crosses into the other)
+    constexpr uint32_t kHalfOff = 8u * kTabHalf;
+    const uint32_t a = (__builtin_bit_cast(uint32_t, sgn) & (kHalfOff | (kHalfOff << 16))) +
+                       __builtin_bit_cast(uint32_t, c8);
+    a0 = a & 0xFFFFu;
+    a1 = a >> 16;
+}
+
+__device__ __forceinline__ double lds_f64(lds_cptr base, uint32_t byte_off)
+{
+    return *reinterpret_cast<lds_dptr>(base + byte_off);
+}
+
+// ---------------------------------------------------------------------------
 // Logits
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

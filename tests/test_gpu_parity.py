@@ -1,7 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
 Every case prints its name before it runs.  Sizes: reduced cases span
-several 4096-element chunks and a ragged tail and run the oracle on every
+several 2048-element chunks and a ragged tail and run the oracle on every
 sequence; the full-size workloads (C1..C5) run the device path in the launch
 configuration the benchmark times and the oracle on a window of sequences.
 """
@@ -75,6 +75,66 @@ def test_chain_parity_reduced(name, wl, ov):
         r, g, _ = run_chain(w, seed=1000 + rnd, rnd=rnd, B=ov.get("B"), N=ov.get("N"))
         rep.merge(r)
     _done(name, rep)
+
+
+# --------------------------------------------------------------------------- #
+# Chains of bf16 logits in 16-byte aligned rows (V a multiple of 8): the
+# sample step that reads exp(z/T) from the bf16-grid table
+# --------------------------------------------------------------------------- #
+TABLE_CASES = [
+    # name, overrides: less than one chunk, whole chunks only, several
+    # temperatures (each moves the table's binades)
+    ("tab_v1504", dict(B=16, N=3, V=1504, T=1.0)),
+    ("tab_v2048", dict(B=16, N=5, V=2048, T=1.0)),
+    ("tab_v6144_t07", dict(B=16, N=4, V=6144, T=0.7)),
+    ("tab_v10008_t33", dict(B=16, N=7, V=10008, T=3.3)),
+    ("tab_v8000_t013", dict(B=12, N=2, V=8000, T=0.13)),
+]
+
+
+@pytest.mark.parametrize("name,ov", TABLE_CASES, ids=[c[0] for c in TABLE_CASES])
+def test_chain_parity_table_path(name, ov):
+    log(f"[case] {name}")
+    w = W["c3"].with_sizes(V=ov["V"], T=ov["T"])
+    rep = compare.Report()
+    for rnd in range(3):
+        r, g, _ = run_chain(w, seed=4000 + rnd, rnd=rnd, B=ov["B"], N=ov["N"])
+        rep.merge(r)
+    _done(name, rep)
+
+
+def test_chain_table_path_logits_outside_table():
+    """bf16 rows with logits the table does not hold: zeros, tiny
+    magnitudes (below 2^-12 T), large ones (at and above 2^7 T), -inf
+    entries, subnormals; and whole sequences whose reference is beyond
+    512 T (their rows take exp_rel throughout)."""
+    log("[case] tab_outside")
+    w = W["c3"].with_sizes(V=8000)
+    B, N = 16, 4
+
+    def plant(inp):
+        zq, zp = inp["zq"], inp["zp"]
+        g = torch.Generator(device="cuda").manual_seed(5)
+        V = w.V
+        for t, v in [(0.0, 11), (-0.0, 12), (1e-6, 13), (-3e-5, 14), (2.0 ** -13, 15), (128.0, 16), (-200.0, 17),
+                     (1e-40, 18), (-1e-39, 19)]:
+            idx = torch.randint(0, V, (B, 64), generator=g, device="cuda")
+            zq[:, :, :].scatter_(2, idx[:, None, :].expand(B, N + 1, 64), torch.full((B, N + 1, 64), t,
+                                                                                  device="cuda", dtype=zq.dtype))
+            idx2 = torch.randint(0, V, (B, 64), generator=g, device="cuda")
+            zp[:, :, :].scatter_(2, idx2[:, None, :].expand(B, N, 64), torch.full((B, N, 64), -t if v % 2 else t,
+                                                                               device="cuda", dtype=zp.dtype))
+        zq[:, :, 100:160] = float("-inf")
+        zp[:, :, 130:190] = float("-inf")
+        zq[3] += 600.0      # reference beyond 512 T: no table for these rows
+        zp[3] += 600.0
+        zq[5] -= 700.0
+        zp[5] -= 700.0
+    rep = compare.Report()
+    for rnd in range(3):
+        r, g, _ = run_chain(w, seed=61 + rnd, rnd=rnd, B=B, N=N, modify=plant)
+        rep.merge(r)
+    _done("tab_outside", rep)
 
 
 def test_chain_n0_plain_sampling():
