@@ -532,6 +532,7 @@ struct ExpRow {
                        // flat loads, whose waits serialize; its value 0 is a
                        // valid address, so `tabbed` says whether there is one)
     double R;          // exp(-m/T), if tabbed
+    double iR;         // exp(m/T) = 1/R, if tabbed
     uint32_t lo;       // the table's first magnitude key
     bool tabbed;
     // exp_rel inline: the streaming loops of rows without the table
@@ -552,10 +553,11 @@ struct ExpRow {
 // takes it when its reference is within kTabRefLimit of zero in units of T.
 __device__ __forceinline__ ExpRow exp_row(const VerifyParams& P, double m, const double* etab, const double* vt)
 {
-    ExpRow e{P.invT, -m * P.invT, (lds_dptr)etab, (lds_dptr)etab, 0.0, P.tab_lo, false};
+    ExpRow e{P.invT, -m * P.invT, (lds_dptr)etab, (lds_dptr)etab, 0.0, 0.0, P.tab_lo, false};
     if (vt && fabs(e.mb) <= kTabRefLimit) {
         e.vt = (lds_dptr)vt;
         e.R = exp(e.mb);
+        e.iR = exp(-e.mb);
         e.tabbed = true;
     }
     return e;
@@ -896,6 +898,11 @@ __device__ __forceinline__ bool chunk_whole(int V, int c)
 // steps, or one row of the shorter bonus steps
 constexpr int kLaneAhead = SV_LANE_AHEAD;
 constexpr int kBonusAhead = SV_BONUS_AHEAD;
+// the table path's vectors in flight per row (two measured best on C3)
+#ifndef SV_TAB_AHEAD
+#define SV_TAB_AHEAD 2
+#endif
+constexpr int kTabAhead = SV_TAB_AHEAD;
 #ifndef SV_STEP_BARRIER
 #define SV_STEP_BARRIER 1
 #endif
@@ -1227,8 +1234,7 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
 
 // Sums of one wave over a chunk of the table path.
 struct TabSums {
-    double acc[4];  // sa sb pa pb: table values, units of exp(z/T)
-    double fix[4];  // the same from logits outside the table, units of exp((z - m)/T)
+    double acc[4];  // sa sb pa pb in units of exp(z/T)
     float nd;       // smallest |d - mid| seen (see NearBand)
 };
 
@@ -1245,34 +1251,42 @@ __device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const
     const uint32_t wp[4] = {vp.x, vp.y, vp.z, vp.w};
     const u16x2 lo2 = {(unsigned short)lo, (unsigned short)lo};
     u16x2 worst = {0, 0};
-    double e[8], f[8];
+    // two halves of four token pairs: eight table reads in flight, then
+    // their terms (the halves keep the live table values to 16 registers)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        uint32_t a0, a1;
-        tab_offsets(wq[k], lo2, a0, a1, worst);
-        e[2 * k] = lds_f64(tab, a0);
-        e[2 * k + 1] = lds_f64(tab, a1);
-        if constexpr (!BONUS) {
-            tab_offsets(wp[k], lo2, a0, a1, worst);
-            f[2 * k] = lds_f64(tab, a0);
-            f[2 * k + 1] = lds_f64(tab, a1);
-        }
-    }
+    for (int h = 0; h < 2; ++h) {
+        double e[4], f[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        if constexpr (BONUS) {
-            A.acc[0] += e[i];
-        } else {
-            const float zq = (i & 1) ? bf16_hi(wq[i >> 1]) : bf16_lo(wq[i >> 1]);
-            const float zp = (i & 1) ? bf16_hi(wp[i >> 1]) : bf16_lo(wp[i >> 1]);
-            const float d = zq - zp;
-            const double fa = d > s.thr_hi ? 1.0 : 0.0;
-            A.acc[0] += e[i];
-            A.acc[1] += f[i];
-            A.acc[2] = fma(fa, e[i], A.acc[2]);
-            A.acc[3] = fma(fa, f[i], A.acc[3]);
-            A.nd = fminf(A.nd, fabsf(d - nb.mid));
+        for (int kk = 0; kk < 2; ++kk) {
+            const int k = 2 * h + kk;
+            uint32_t a0, a1;
+            tab_offsets(wq[k], lo2, a0, a1, worst);
+            e[2 * kk] = lds_f64(tab, a0);
+            e[2 * kk + 1] = lds_f64(tab, a1);
+            if constexpr (!BONUS) {
+                tab_offsets(wp[k], lo2, a0, a1, worst);
+                f[2 * kk] = lds_f64(tab, a0);
+                f[2 * kk + 1] = lds_f64(tab, a1);
+            }
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * h + j;
+            if constexpr (BONUS) {
+                A.acc[0] += e[j];
+            } else {
+                const float zq = (i & 1) ? bf16_hi(wq[i >> 1]) : bf16_lo(wq[i >> 1]);
+                const float zp = (i & 1) ? bf16_hi(wp[i >> 1]) : bf16_lo(wp[i >> 1]);
+                const float d = zq - zp;
+                const double fa = d > s.thr_hi ? 1.0 : 0.0;
+                A.acc[0] += e[j];
+                A.acc[1] += f[j];
+                A.acc[2] = fma(fa, e[j], A.acc[2]);
+                A.acc[3] = fma(fa, f[j], A.acc[3]);
+                A.nd = fminf(A.nd, fabsf(d - nb.mid));
+            }
+        }
+        asm volatile("" : "+v"(A.acc[0]), "+v"(A.acc[1]), "+v"(A.acc[2]), "+v"(A.acc[3]), "+v"(A.nd));
     }
     if (__any(max((uint32_t)worst.x, (uint32_t)worst.y) >= (uint32_t)kTabKeys)) {
         // logits outside the table: their terms went in as zeros.  One
@@ -1284,22 +1298,23 @@ __device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const
             const uint32_t w = k == 0 ? wq[0] : k == 1 ? wq[1] : k == 2 ? wq[2] : wq[3];
             const float zq = (i & 1) ? bf16_hi(w) : bf16_lo(w);
             const bool oq = tab_index(zq, lo) < 0;
+            // exp((z - m)/T) / R = exp(z/T): into the table values' units
             if constexpr (BONUS) {
-                if (oq) A.fix[0] += eq.slow(zq);
+                if (oq) A.acc[0] = fma(eq.slow(zq), eq.iR, A.acc[0]);
             } else {
                 const uint32_t v = k == 0 ? wp[0] : k == 1 ? wp[1] : k == 2 ? wp[2] : wp[3];
                 const float zp = (i & 1) ? bf16_hi(v) : bf16_lo(v);
                 const bool op = tab_index(zp, lo) < 0;
                 const double fa = (zq - zp > s.thr_hi) ? 1.0 : 0.0;
                 if (oq) {
-                    const double a = eq.slow(zq);
-                    A.fix[0] += a;
-                    A.fix[2] = fma(fa, a, A.fix[2]);
+                    const double a = eq.slow(zq) * eq.iR;
+                    A.acc[0] += a;
+                    A.acc[2] = fma(fa, a, A.acc[2]);
                 }
                 if (op) {
-                    const double bb = ep.slow(zp);
-                    A.fix[1] += bb;
-                    A.fix[3] = fma(fa, bb, A.fix[3]);
+                    const double bb = ep.slow(zp) * ep.iR;
+                    A.acc[1] += bb;
+                    A.acc[3] = fma(fa, bb, A.acc[3]);
                 }
             }
         }
@@ -1320,7 +1335,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
                                 int ca, int cb, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
 {
     constexpr int PER = kChunk / 8 / 64;  // vectors per lane per chunk
-    constexpr int D = BONUS ? kBonusAhead : kLaneAhead;
+    constexpr int D = kTabAhead;
     static_assert(PER % D == 0, "slots rotate within a chunk");
     const int lane = threadIdx.x & 63;
     const int nvec = (cb - ca) * PER;
@@ -1337,10 +1352,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
     const NearBand nb = near_band(s);
     TabSums A;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        A.acc[i] = 0.0;
-        A.fix[i] = 0.0;
-    }
+    for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
     A.nd = INFINITY;
 #pragma unroll 1
     for (int c = ca; c < cb; ++c) {
@@ -1364,12 +1376,12 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
         ChunkSums out{};
         if constexpr (BONUS) {
             out.sa = (double)s.mq;
-            out.sb = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+            out.sb = wave_sum(eq.R * A.acc[0]);
         } else {
-            out.sa = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
-            out.sb = wave_sum(fma(ep.R, A.acc[1], A.fix[1]));
-            out.pa = wave_sum(fma(eq.R, A.acc[2], A.fix[2]));
-            out.pb = wave_sum(fma(ep.R, A.acc[3], A.fix[3]));
+            out.sa = wave_sum(eq.R * A.acc[0]);
+            out.sb = wave_sum(ep.R * A.acc[1]);
+            out.pa = wave_sum(eq.R * A.acc[2]);
+            out.pb = wave_sum(ep.R * A.acc[3]);
             out.dmin = INFINITY;
             out.dmax = -INFINITY;
             if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
@@ -1377,10 +1389,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
         }
         if (lane == 0) put_chunk(P, b, c, out);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            A.acc[i] = 0.0;
-            A.fix[i] = 0.0;
-        }
+        for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
     }
 }
 
@@ -1403,10 +1412,7 @@ __device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& 
     const NearBand nb = near_band(s);
     TabSums A;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        A.acc[i] = 0.0;
-        A.fix[i] = 0.0;
-    }
+    for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
     A.nd = INFINITY;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
@@ -1417,12 +1423,12 @@ __device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& 
     ChunkSums out{};
     if constexpr (BONUS) {
         out.sa = (double)s.mq;
-        out.sb = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
+        out.sb = wave_sum(eq.R * A.acc[0]);
     } else {
-        out.sa = wave_sum(fma(eq.R, A.acc[0], A.fix[0]));
-        out.sb = wave_sum(fma(ep.R, A.acc[1], A.fix[1]));
-        out.pa = wave_sum(fma(eq.R, A.acc[2], A.fix[2]));
-        out.pb = wave_sum(fma(ep.R, A.acc[3], A.fix[3]));
+        out.sa = wave_sum(eq.R * A.acc[0]);
+        out.sb = wave_sum(ep.R * A.acc[1]);
+        out.pa = wave_sum(eq.R * A.acc[2]);
+        out.pb = wave_sum(ep.R * A.acc[3]);
         out.dmin = INFINITY;
         out.dmax = -INFINITY;
         if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
