@@ -352,9 +352,12 @@ int tree_finalize(const int32_t* cand_token, const int32_t* cand_parent, const i
  * SV_F32 / SV_BF16), gives out_tokens[b*R + r] by the verify step's inverse
  * CDF in token order (the first token whose running weight exceeds u*W, W
  * the total; the last token of positive weight if rounding leaves none;
- * weights 2^((z - m) log2(e)/T) as fp32 exp2 terms, about 1e-7 relative,
- * accumulated in double, so the draw is the inverse CDF of softmax(z/T)
- * within ~1e-7 relative, and ln p within ~1e-7) with the uniform of
+ * double weights: for bf16 rows exp(z/T) from a per-block table over the
+ * bf16 grid (one rounding each), otherwise, and for rows with a logit above
+ * 700 T or a total below 1e-280, exp((z - ref)/T) by a table-driven fp64
+ * exp (~1e-11 relative) against a running reference; accumulated in
+ * double, so the draw is the inverse CDF of softmax(z/T) to ~1e-11 and ln
+ * p within ~1e-11) with the uniform of
  * Philox stream 1: key seed, counter (pos0 + r, b, round low word,
  * (round high word << 4) | 1), words 0 and 1 as a 53-bit double, so draft
  * draws never reuse a verify uniform.  out_logprob[b*R + r] (may be NULL):

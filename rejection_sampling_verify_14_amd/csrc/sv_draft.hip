@@ -26,7 +26,9 @@ struct DraftArgs {
     int64_t seq_stride, row_stride;  // elements
     int R, V, pos0;
     double invT;
-    float c;  // log2(e) / T
+    float T;
+    int use_tab;      // bf16 rows: the temperature has a bf16-grid table
+    uint32_t tab_lo;  // its first magnitude key
     uint64_t seed, round;
     int32_t* out_tokens;
     double* out_logprob;
@@ -105,85 +107,211 @@ __device__ __forceinline__ double wave_exclusive(double v, int lane, double* tot
     return x - v;
 }
 
+// Weights.  bf16 rows whose temperature gives a bf16-grid table (see
+// kTabKeys) take E(z) = exp(z/T) from the block's LDS copy of it, summed
+// without a reference (logits outside the table add exp_rel(z/T)); a row
+// with a logit above 700 T (its exp(z/T) would overflow) or whose total
+// weight falls below 1e-280 (every logit far below zero) is redone by the
+// reference path.  The reference path (f32 rows, and those rows) sums
+// exp((z - ref)/T) by exp_rel against a running reference per wave, as in
+// the verify step's sampling.  Either way the weights are double, ~1e-11
+// relative (exp_rel) or one rounding (table), so the draw is the inverse CDF
+// of softmax(z/T) to far below the comparison band.
+constexpr int kDraftTabPath = 1, kDraftRefPath = 2;
+constexpr double kDraftOverflowArg = 700.0;  // exp_rel's arguments stay below this
+constexpr double kDraftTinyTotal = 1e-280;
+
 // Block (b, r): one draw from row r of sequence b.
 //  1. Each wave takes chunks w, w + NW, ... (1024 logits, 16 contiguous per
-//     lane, the next two chunks' loads in flight): a reference m_c and s_c = sum
-//     of the weights 2^((x - m_c) c), c = log2(e)/T, each an fp32 exp2
-//     (about 1e-7 relative) summed in double, into LDS.
-//  2. Wave 0: M = max m_c, chunk weights s_c exp((m_c - M)/T), W, u*W, and
-//     the chunk where the running weight passes u*W (8 chunks per lane, an
-//     exclusive scan over lanes).
-//  3. Wave 0 rescans that chunk in token order with the same weights (the
-//     same fp32 values), so the draw is the exact inverse CDF of the fp32
-//     weights: within about 1e-7 relative of the exact softmax CDF.
+//     lane, the next two chunks' loads in flight) and stores the chunk's
+//     weight sum (and, on the reference path, its reference) in LDS.
+//  2. Wave 0: total W, u*W, and the chunk where the running weight passes
+//     u*W (8 chunks per lane, an exclusive scan over lanes).
+//  3. Wave 0 rescans that chunk in token order with the same weights, so
+//     the draw is the exact inverse CDF of the weights.
 // A row holding NaN or +inf, or only -inf, gives token -1 and NaN.
 // NW = 8 waves per block for large batches, 16 for small ones (a row's
-// chunks spread over more waves); at 84 VGPRs five waves fit per SIMD.
+// chunks spread over more waves); bf16 at least six waves per SIMD (the
+// LDS table fits three 8-wave blocks per CU), f32 four (exp_rel's registers
+// without spills).
 template <int DT, int NW>
-__global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
+__global__ __launch_bounds__(NW * 64, DT == DT_BF16 ? 6 : 4) void k_draft_sample(DraftArgs A)
 {
-    __shared__ double s_tab[kExpTabN];
+    constexpr bool TAB = DT == DT_BF16;
+    __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_tab[TAB ? kTabEntries : 2];
     __shared__ float s_m[kDraftMaxChunks];
     __shared__ double s_s[kDraftMaxChunks];
-    __shared__ float s_e[kDraftMaxChunks];
+    __shared__ int s_flags;
     const int row_id = blockIdx.x;
     const int b = row_id / A.R, r = row_id - b * A.R;
     const char* row = A.rows + ((int64_t)b * A.seq_stride + (int64_t)r * A.row_stride) * (DT == DT_BF16 ? 2 : 4);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nch = (A.V + kDraftChunk - 1) / kDraftChunk;
-    fill_exp_table(s_tab);
-    __syncthreads();
-    const lds_dptr tab = (lds_dptr)s_tab;
     const double invT = A.invT;
+    if (tid == 0) s_flags = 0;
+    bool tab_path = false;
+    if constexpr (TAB) tab_path = A.use_tab != 0;
+    const lds_dptr etab = (lds_dptr)s_etab;
+    const lds_cptr tabc = (lds_cptr)s_tab;
 
-    // 1. chunk sums.  The wave's reference ref (uniform) lags its running
-    // maximum by under 2 in the exponent, so most chunks skip the wave-wide
-    // maximum; a term is 2^(fma(x, c, -p)), p = RN(ref c), which is
-    // 2^((x - ref) c) times 2^e, e = ref c - p (exact in fp32), shed in
-    // step 2.  NaN and +inf reach the sum as NaN (while ref is -inf, p = 0
-    // keeps every term 0 or NaN).
-    float ref = -INFINITY, lim = -INFINITY, pf = 0.0f, ef = 0.0f;
-    auto take = [&](const ChunkRegs<DT>& regs, int c) {
-        float x[kDraftPerLane];
-        decode_lane_chunk<DT>(regs, x);
-        float lm = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < kDraftPerLane; ++j) lm = fmaxf(lm, x[j]);
-        if (__ballot(lm > lim)) {
-            const float wm = wave_max_fl(lm);
-            ref = wm;
-            lim = wm + 2.0f / A.c;
-            pf = wm * A.c;
-            ef = __builtin_fmaf(wm, A.c, -pf);
-        }
-        double s = 0.0;
-#pragma unroll
-        for (int j = 0; j < kDraftPerLane; ++j) s += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pf));
-        s = wave_sum_d(s);
-        if (lane == 0) {
-            s_m[c] = ref;
-            s_e[c] = ef;
-            s_s[c] = s;
-        }
-    };
     // three register sets, loads two chunks ahead; a set is never copied
     // (a copy would wait for its loads), and a load past the row's chunks
-    // is skipped (wave-uniform)
-    ChunkRegs<DT> ra, rb, rc;
-    auto load = [&](ChunkRegs<DT>& regs, int c) {
-        if (c < nch) load_lane_chunk<DT>(row, A.V, c, lane, regs);
+    // is skipped (wave-uniform).  `before` runs (in every wave, so it may
+    // hold barriers) once the first loads are in flight.
+    auto stream_row = [&](auto&& take, auto&& before) {
+        ChunkRegs<DT> ra, rb, rc;
+        auto load = [&](ChunkRegs<DT>& regs, int c) {
+            if (c < nch) load_lane_chunk<DT>(row, A.V, c, lane, regs);
+        };
+        load(ra, wave);
+        load(rb, wave + NW);
+        before();
+        for (int c = wave; c < nch; c += 3 * NW) {
+            load(rc, c + 2 * NW);
+            take(ra, c);
+            if (c + NW >= nch) break;
+            load(ra, c + 3 * NW);
+            take(rb, c + NW);
+            if (c + 2 * NW >= nch) break;
+            load(rb, c + 4 * NW);
+            take(rc, c + 2 * NW);
+        }
     };
-    load(ra, wave);
-    load(rb, wave + NW);
-    for (int c = wave; c < nch; c += 3 * NW) {
-        load(rc, c + 2 * NW);
-        take(ra, c);
-        if (c + NW >= nch) break;
-        load(ra, c + 3 * NW);
-        take(rb, c + NW);
-        if (c + 2 * NW >= nch) break;
-        load(rb, c + 4 * NW);
-        take(rc, c + 2 * NW);
+
+    // 1a. table path: chunk sums of E(z) = exp(z/T)
+    if constexpr (TAB) {
+        if (tab_path) {
+            const u16x2 lo2 = {(unsigned short)A.tab_lo, (unsigned short)A.tab_lo};
+            int flags = 0;  // 1: NaN or +inf, 2: a logit above 700 T
+            auto take = [&](const ChunkRegs<DT>& regs, int c) {
+                double sum = 0.0;
+                u16x2 worst = {0, 0};
+                const uint32_t w[8] = {regs.v[0].x, regs.v[0].y, regs.v[0].z, regs.v[0].w,
+                                       regs.v[1].x, regs.v[1].y, regs.v[1].z, regs.v[1].w};
+                // two halves of eight table reads (the halves keep the live
+                // table values to 16 registers)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    double v[8];
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk) {
+                        uint32_t a0, a1;
+                        tab_offsets(w[4 * h + kk], lo2, a0, a1, worst);
+                        v[2 * kk] = lds_f64(tabc, a0);
+                        v[2 * kk + 1] = lds_f64(tabc, a1);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sum += v[j];
+                    asm volatile("" : "+v"(sum));
+                }
+                if (__any(max((uint32_t)worst.x, (uint32_t)worst.y) >= (uint32_t)kTabKeys)) {
+                    // logits outside the table went in as zeros
+#pragma unroll 1
+                    for (int i = 0; i < 16; ++i) {
+                        const int k = i >> 1;
+                        uint32_t x = w[0];
+#pragma unroll
+                        for (int q = 1; q < 8; ++q) x = k == q ? w[q] : x;
+                        const float z = (i & 1) ? bf16_hi(x) : bf16_lo(x);
+                        if (tab_index(z, A.tab_lo) >= 0 || z == -INFINITY) continue;
+                        if (!(z < INFINITY)) {
+                            flags |= 1;  // NaN or +inf
+                            continue;
+                        }
+                        const double arg = (double)z * invT;
+                        if (arg > kDraftOverflowArg) flags |= 2;
+                        else sum += exp_rel(arg, etab);
+                    }
+                }
+                sum = wave_sum_d(sum);
+                if (lane == 0) s_s[c] = sum;
+            };
+            // the block's table, built while the first loads are in flight:
+            // entry s (kTabKeys + 1) + t = exp(z/T) (exp_rel) for the bf16 z
+            // of magnitude bits lo + t and sign s (t = kTabKeys: 0)
+            auto build_table = [&]() {
+                fill_exp_table(s_etab);
+                __syncthreads();
+                for (int i = tid; i < kTabEntries; i += NW * 64) {
+                    const int sgn = i >= kTabHalf ? 1 : 0;
+                    const int t = i - sgn * kTabHalf;
+                    double v = 0.0;
+                    if (t < kTabKeys) {
+                        const uint32_t key = (A.tab_lo + (uint32_t)t) | ((uint32_t)sgn << 15);
+                        v = exp_rel((double)__uint_as_float(key << 16) * invT, etab);
+                    }
+                    s_tab[i] = v;
+                }
+                __syncthreads();
+            };
+            stream_row(take, build_table);
+            flags = (__any(flags & 1) ? 1 : 0) | (__any(flags & 2) ? 2 : 0);
+            if (lane == 0 && flags) atomicOr(&s_flags, flags);
+        }
+    }
+
+    // 1b. reference path (f32 rows; bf16 rows without the table; rows the
+    // table path hands over): sums of exp((z - ref_c)/T) against a
+    // reference that lags the wave's running maximum by less than 2 ln2 T.
+    // NaN and +inf reach the sum as NaN.
+    auto ref_path = [&]() {
+        float ref = -INFINITY, lim = -INFINITY;
+        const float step = (float)(2.0 * 0.69314718055994530942 / invT);
+        auto take = [&](const ChunkRegs<DT>& regs, int c) {
+            float x[kDraftPerLane];
+            decode_lane_chunk<DT>(regs, x);
+            float lm = -INFINITY;
+            int bad = 0;
+#pragma unroll
+            for (int j = 0; j < kDraftPerLane; ++j) {
+                lm = fmaxf(lm, x[j]);
+                bad |= !(x[j] < INFINITY) && x[j] != -INFINITY;
+            }
+            if (__ballot(lm > lim)) {
+                const float wm = wave_max_fl(lm);
+                ref = wm;
+                lim = wm + step;
+            }
+            double sum = 0.0;
+            if (ref != -INFINITY) {
+#pragma unroll
+                for (int j = 0; j < kDraftPerLane; ++j)
+                    sum += exp_rel(((double)x[j] - (double)ref) * invT, etab);
+            }
+            sum = __any(bad) ? NAN : wave_sum_d(sum);
+            if (lane == 0) {
+                s_m[c] = ref;
+                s_s[c] = sum;
+            }
+        };
+        stream_row(take, [] {});
+    };
+    bool use_ref = !tab_path;
+    if (use_ref) {
+        fill_exp_table(s_etab);
+        __syncthreads();
+    }
+    if (!use_ref) {
+        __syncthreads();
+        const int fl = s_flags;
+        if (fl & 1) {
+            // NaN or +inf: the row fails
+            if (tid == 0) {
+                const int64_t oi = (int64_t)b * A.R + r;
+                A.out_tokens[oi] = -1;
+                if (A.out_logprob) A.out_logprob[oi] = NAN;
+            }
+            return;
+        }
+        double tot = 0.0;
+        for (int c = lane; c < nch; c += 64) tot += s_s[c];
+        tot = wave_sum_d(tot);
+        use_ref = (fl & 2) || !(tot >= kDraftTinyTotal);
+        __syncthreads();  // every wave read s_s before the reference path rewrites it
+    }
+    if (use_ref) {
+        ref_path();
     }
     __syncthreads();
     if (wave != 0) return;
@@ -191,30 +319,31 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
     // 2. total weight and the chunk of the draw
     const int64_t oi = (int64_t)b * A.R + r;
     float M = -INFINITY;
-    int bad = 0;
-    for (int c = lane; c < nch; c += 64) {
-        M = fmaxf(M, s_m[c]);
-        bad |= s_s[c] != s_s[c];
-    }
-    M = wave_max_fl(M);
-    if (__ballot(bad) || M == -INFINITY) {
-        if (lane == 0) {
-            A.out_tokens[oi] = -1;
-            if (A.out_logprob) A.out_logprob[oi] = NAN;
+    if (use_ref) {
+        int bad = 0;
+        for (int c = lane; c < nch; c += 64) {
+            M = fmaxf(M, s_m[c]);
+            bad |= s_s[c] != s_s[c];
         }
-        return;
+        M = wave_max_fl(M);
+        if (__ballot(bad) || M == -INFINITY) {
+            if (lane == 0) {
+                A.out_tokens[oi] = -1;
+                if (A.out_logprob) A.out_logprob[oi] = NAN;
+            }
+            return;
+        }
     }
-    // chunk c's weight: s_c 2^(-e_c) exp((ref_c - M)/T)
-    auto chunk_scale = [&](int c) {
-        return exp_rel(((double)s_m[c] - (double)M) * invT - (double)s_e[c] * 0.69314718055994530942, tab);
-    };
+    // chunk c's weight: the table path's sum as is; the reference path's
+    // s_c exp((ref_c - M)/T)
+    auto chunk_scale = [&](int c) { return use_ref ? exp_rel(((double)s_m[c] - (double)M) * invT, etab) : 1.0; };
     constexpr int CPL = kDraftMaxChunks / 64;  // chunks per lane, consecutive
     double cw[CPL];
     double lsum = 0.0;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
         const int c = lane * CPL + i;
-        cw[i] = (c < nch && s_m[c] != -INFINITY) ? s_s[c] * chunk_scale(c) : 0.0;
+        cw[i] = (c < nch && (!use_ref || s_m[c] != -INFINITY)) ? s_s[c] * chunk_scale(c) : 0.0;
         lsum += cw[i];
     }
     double W;
@@ -249,20 +378,28 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
     }
     cs = __shfl(cs, owner, 64);
     cbase = __shfl(cbase, owner, 64);
-    const float mc = s_m[cs];
-    const float pc = mc * A.c;  // the chunk's p, as pass 1 formed it
+    const double mc = use_ref ? (double)s_m[cs] : 0.0;
     const double scale = chunk_scale(cs);
     const double local = fallback ? INFINITY : (target - cbase) / scale;
 
-    // 3. rescan the chunk in token order
+    // 3. rescan the chunk in token order, the same weights as step 1
     ChunkRegs<DT> rr;
     load_lane_chunk<DT>(row, A.V, cs, lane, rr);
     float x[kDraftPerLane];
     decode_lane_chunk<DT>(rr, x);
-    // the weights are recomputed below (the same fp32 values) rather than held
+    // the weight of token j of the lane (computed again where needed rather
+    // than held: the same value both times)
+    auto weight = [&](int j) -> double {
+        if (!use_ref) {
+            const int ti = TAB ? tab_index(x[j], A.tab_lo) : -1;
+            return ti >= 0 ? ((lds_dptr)s_tab)[ti]
+                           : (x[j] == -INFINITY ? 0.0 : exp_rel((double)x[j] * invT, etab));
+        }
+        return exp_rel(((double)x[j] - mc) * invT, etab);
+    };
     double tsum = 0.0;
 #pragma unroll
-    for (int j = 0; j < kDraftPerLane; ++j) tsum += (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pc));
+    for (int j = 0; j < kDraftPerLane; ++j) tsum += weight(j);
     double ctot;
     const double tbase = wave_exclusive(tsum, lane, &ctot);
     const uint64_t cand = __ballot(tsum > 0.0 && tbase + tsum > local);
@@ -274,7 +411,7 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
         float xpick = 0.0f, xlast = 0.0f;
 #pragma unroll
         for (int j = 0; j < kDraftPerLane; ++j) {
-            const double wj = (double)__builtin_amdgcn_exp2f(__builtin_fmaf(x[j], A.c, -pc));
+            const double wj = weight(j);
             if (wj > 0.0) {
                 last = j;
                 xlast = x[j];
@@ -290,7 +427,10 @@ __global__ __launch_bounds__(NW * 64, 4) void k_draft_sample(DraftArgs A)
             xpick = xlast;
         }
         A.out_tokens[oi] = cs * kDraftChunk + lane * kDraftPerLane + pick;
-        if (A.out_logprob) A.out_logprob[oi] = ((double)xpick - (double)M) * invT - log(W);
+        // ln p = z/T - ln W (table path, W in units of exp(z/T)), or
+        // (z - M)/T - ln W (reference path, W relative to M)
+        if (A.out_logprob)
+            A.out_logprob[oi] = (use_ref ? ((double)xpick - (double)M) * invT : (double)xpick * invT) - log(W);
     }
 }
 
@@ -317,7 +457,13 @@ extern "C" int sv_sample_draft(const void* logits, int64_t seq_stride, int64_t r
     A.V = V;
     A.pos0 = pos0;
     A.invT = 1.0 / (double)temperature;
-    A.c = (float)(1.4426950408889634074 / (double)temperature);
+    A.T = temperature;
+    // the bf16-grid table of T: binades [2^(e-12), 2^(e+7)), e = floor(log2 T)
+    int e2 = 0;
+    frexp((double)temperature, &e2);
+    const int blo = 127 + (e2 - 1) - 12;
+    A.use_tab = dtype == SV_BF16 && blo >= 1 && blo + sv::kTabBinades <= 255;
+    A.tab_lo = A.use_tab ? (uint32_t)blo << 7 : 0u;
     A.seed = seed;
     A.round = round;
     A.out_tokens = out_tokens;
