@@ -40,7 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 REPEATS = 5             # timed blocks of K steps; the median is reported
-PROFILE_PMC = os.path.join(ROOT, "profiles", "k_verify_{workload}_pmc.json")
+PROFILE_PMC = os.path.join(ROOT, "profiles", "k_rows_{workload}_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
                   for f in ("specverify.hip", "sv_device.h", "sv_exp_table.h")]
 
@@ -85,7 +85,7 @@ def kernel_hash() -> str:
 
 
 def load_traffic(workload: str):
-    """HBM bytes per launch of the verify kernel on this workload from the
+    """HBM bytes per launch of the row kernel on this workload from the
     committed rocprofv3 PMC summary, if it was taken on the current kernel
     source (else None: the counters no longer describe the kernel)."""
     try:
@@ -96,6 +96,65 @@ def load_traffic(workload: str):
     if p.get("kernel_hash") != kernel_hash():
         return None, "stale"
     return int(p["hbm_bytes_per_launch"]), p
+
+
+def row_kernel_bytes(w, s) -> int:
+    """Bytes the row kernel must read: every row a test of the step reads
+    (chain: B*(2N+1)*V*s; tree: the q and p rows of every node with a child,
+    2*internal*V*s per sequence; a leaf's q row is read only if the walk ends
+    there, by the sample step)."""
+    import numpy as np
+    if w.kind == "chain":
+        return w.B * (2 * w.N + 1) * w.V * w.elem_bytes
+    par = s["parents"].cpu().numpy()
+    p2 = par if par.ndim == 2 else np.repeat(par[None], w.B, 0)
+    internal = sum(len(set(int(x) for x in row[1:] if x >= 0)) for row in p2)
+    return 2 * internal * w.V * w.elem_bytes
+
+
+def _pmc_per_dispatch(csv_path: str, name_part: str, counter: str) -> float:
+    """Mean per dispatch of a rocprofv3 counter over the dispatches of the
+    kernels whose name contains name_part (values of one dispatch summed)."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if name_part in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise ValueError(f"no {counter} for {name_part} in {csv_path}")
+    return sum(per.values()) / len(per)
+
+
+def pmc_summary(workload: str, fetch_csv: str, write_csv: str, cfetch_csv: str, cwrite_csv: str, commands):
+    """The row kernel's HBM bytes per launch from two rocprofv3 --pmc runs of
+    this bench (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled
+    by what the same counter reads for a plain 1 GiB device copy
+    (--copy-calibration); written to profiles/k_rows_<workload>_pmc.json with
+    the hash of the kernel sources it was taken on."""
+    import synth
+    w = synth.WORKLOADS[workload]
+    name = "k_rows<"
+    fk = _pmc_per_dispatch(fetch_csv, name, "FETCH_SIZE")
+    wk = _pmc_per_dispatch(write_csv, name, "WRITE_SIZE")
+    copy_k_f = _pmc_per_dispatch(cfetch_csv, "copy", "FETCH_SIZE")
+    copy_k_w = _pmc_per_dispatch(cwrite_csv, "copy", "WRITE_SIZE")
+    n = 1 << 30
+    fs, ws = n / (copy_k_f * 1024.0), n / (copy_k_w * 1024.0)
+    hbm = fk * 1024.0 * fs + wk * 1024.0 * ws
+    sets = build_pool(w, 1, "cpu") if w.kind != "chain" else [None]
+    alg = row_kernel_bytes(w, sets[0])
+    out = {"kernel": "sv::k_rows (row statistics)", "workload": workload, "kernel_hash": kernel_hash(),
+           "fetch_kib_per_launch": round(fk, 1), "write_kib_per_launch": round(wk, 1),
+           "calibration": {"copy_bytes": n, "copy_fetch_kib": round(copy_k_f, 1), "copy_write_kib": round(copy_k_w, 1),
+                           "fetch_scale": fs, "write_scale": ws,
+                           "note": "scale = bytes of a plain 1 GiB device copy / (counter KiB x 1024) for that copy"},
+           "hbm_bytes_per_launch": int(hbm), "algorithmic_bytes_per_launch": int(alg),
+           "traffic_over_algorithmic": hbm / alg, "commands": list(commands)}
+    path = PROFILE_PMC.format(workload=workload)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
 
 
 def build_pool(w, pool: int, device: str):
@@ -490,6 +549,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the row kernel's PMC summary for --workload from rocprofv3 counter CSVs")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help="the commands that made the CSVs (recorded)")
     ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
     ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on config 5 rows instead")
     ap.add_argument("--draft-sample", action="store_true", help="time sv_sample_draft on config 3's draft rows")
@@ -509,6 +571,9 @@ def main():
 
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary, args.pmc_commands)
         return
     if args.tree_mask:
         tree_mask_bench(args.steps, args.warmup)
@@ -593,20 +658,25 @@ def main():
         tok_sum += float((k[k >= 0] + 1).sum())
         tok_n += int((k >= 0).sum())
     ms_step = statistics.median(blocks_ms) / K
-    # the kernel's own duration: one more block with start/stop events
-    # stamped by the kernel's launch
-    log(f"[bench] timing the kernel of {K} more steps")
-    ev = [(hip.event(), hip.event()) for _ in range(K)]
+    # the row kernel's own duration (the step's dominant kernel) and the
+    # call's: one more block of K steps whose events are stamped by the
+    # kernels' own starts and ends (no event between a call's kernels)
+    log(f"[bench] timing the kernels of {K} more steps")
+    ev = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
     for i in range(K):
         step(nxt + i, timing=ev[i])
     torch.cuda.synchronize()
-    kern_ms = [hip.elapsed_ms(a, b) for a, b in ev]
-    k_mean = sum(kern_ms) / K
+    rows_ms = [hip.elapsed_ms(a, m) for a, m, _ in ev]
+    call_ms = [hip.elapsed_ms(a, b) for a, _, b in ev]
+    k_mean = sum(rows_ms) / K
+    call_mean = sum(call_ms) / K
     per_set = [algorithmic_bytes(w, s) for s in sets]
     full_bytes = sum(per_set) / len(per_set)
+    row_set = [row_kernel_bytes(w, s) for s in sets]
+    row_bytes = sum(row_set) / len(row_set)
     rounds_per_s = 1000.0 / ms_step
     eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
-    k_gbps = full_bytes / (k_mean * 1e-3) / 1e9
+    k_gbps = row_bytes / (k_mean * 1e-3) / 1e9
     traffic, pmc = load_traffic(w.name)
     result = {
         "metric": "verified rounds/s + achieved HBM GB/s (% peak), B=256 N=7 V=128256",
@@ -638,7 +708,7 @@ def main():
         "alpha_measured": round(acc_sum / max(acc_n, 1), 4),
         "tokens_per_round": round(tok_sum / max(tok_n, 1), 4),
         "roofline": {
-            "kernel": "k_verify (row statistics, accept and sampling in one launch)",
+            "kernel": "k_rows (row statistics of every logit row the step reads; the dominant kernel)",
             "bound": "hbm",
             "achieved": round(k_gbps, 1),
             "peak": PEAK_HBM_GBPS,
@@ -646,8 +716,9 @@ def main():
             "frac": round(k_gbps / PEAK_HBM_GBPS, 4),
             "traffic": traffic,
             "kernel_ms": round(k_mean, 5),
-            "algorithmic_bytes_per_launch": int(full_bytes),
+            "algorithmic_bytes_per_launch": int(row_bytes),
         },
+        "call_ms_with_kernel_events": round(call_mean, 5),
         "wall_s_timed": round(sum(walls), 3),
     }
     if not args.no_cpu_baseline:

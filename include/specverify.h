@@ -84,12 +84,14 @@ enum sv_walk {
                                    child is tried; its rejection ends the walk */
 };
 
-/* Optional timing hook: when non-NULL, `begin` (if not NULL) is stamped by
- * the start of the call's first kernel and `end` (if not NULL) by the end of
- * its last kernel on `stream`, so a caller can time the call without events
- * between its kernels. */
+/* Optional timing hook: when non-NULL, each non-NULL event is stamped by a
+ * kernel of the call on `stream`: `begin` by the start of the row kernel
+ * (the call's first kernel), `rows_done` by that kernel's end, and `end` by
+ * the end of the call's last kernel.  A caller can time the call, and its
+ * row-statistics kernel alone, without events between the kernels. */
 typedef struct sv_timing {
     hipEvent_t begin;
+    hipEvent_t rows_done;
     hipEvent_t end;
 } sv_timing;
 

@@ -48,7 +48,7 @@ class SpecVerifyError(RuntimeError):
 
 
 class SvTiming(ctypes.Structure):
-    _fields_ = [("begin", ctypes.c_void_p), ("end", ctypes.c_void_p)]
+    _fields_ = [("begin", ctypes.c_void_p), ("rows_done", ctypes.c_void_p), ("end", ctypes.c_void_p)]
 
 
 _L = None
@@ -97,7 +97,7 @@ def _lib():
         L.sv_sample_draft.restype = i32
         L.sv_sample_draft.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, u64, u64, i32, vp, vp, vp]
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
-        if L.sv_abi_version() != 4:
+        if L.sv_abi_version() != 5:
             raise ImportError("libspecverify.so ABI version mismatch")
         _L = L
     return _L
@@ -133,10 +133,13 @@ def _check_logits(t: torch.Tensor, name: str):
 
 
 def _timing(timing):
-    """(begin, end) hipEvent_t handles stamped by the call's kernel, or None."""
+    """(begin, end) or (begin, rows_done, end) hipEvent_t handles (None for
+    any not wanted) stamped by the call's kernels, or None."""
     if timing is None:
         return None
-    return ctypes.byref(SvTiming(timing[0], timing[1]))
+    if len(timing) == 2:
+        return ctypes.byref(SvTiming(timing[0], None, timing[1]))
+    return ctypes.byref(SvTiming(timing[0], timing[1], timing[2]))
 
 
 def chain_workspace_bytes(B: int, N: int, V: int) -> int:

@@ -2303,8 +2303,8 @@ template <int DT, bool TREE>
 void launch_rows(const sv::VerifyParams& P, int64_t grid, const sv_timing* timing, hipStream_t stream)
 {
     const hipEvent_t t0 = timing ? timing->begin : nullptr;
-    hipExtLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)grid), dim3(sv::kBlock), 0, stream, t0, nullptr, 0,
-                          P);
+    const hipEvent_t t1 = timing ? timing->rows_done : nullptr;
+    hipExtLaunchKernelGGL((sv::k_rows<DT, TREE>), dim3((unsigned)grid), dim3(sv::kBlock), 0, stream, t0, t1, 0, P);
 }
 
 // Chains: the row kernel (row statistics, table, accept tests), then the
@@ -2438,7 +2438,7 @@ int scratch_on_current_device(void** out)
 
 extern "C" {
 
-int sv_abi_version(void) { return 4; }
+int sv_abi_version(void) { return 5; }
 
 const char* sv_status_string(int status)
 {
