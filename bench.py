@@ -29,6 +29,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -76,11 +77,21 @@ class Hip:
         self.lib.hipEventDestroy(ctypes.c_void_p(e))
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with comments removed and white space collapsed: what the
+    compiler sees, so that a change of comments alone keeps the hash."""
+    out = _CODE_TOKENS.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(out.split())
+
+
 def kernel_hash() -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -162,7 +162,7 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
  * outputs are those of spec_verify_chain.  The call allocates nothing: its
  * workspace is a static device array of the library,
  * SV_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, zero when the library is loaded
- * and kept until the process ends (config 3's chains, B=256 N=7 V=128256,
+ * and kept until the process ends (chains of B=256 N=7 V=128256
  * need about 1.3 MB).  Sizes whose sv_chain_workspace_bytes exceed it
  * return SV_ESCRATCH before any HIP call.  Every call on one GPU shares that
  * GPU's array (each call tags its records, so what an earlier call left

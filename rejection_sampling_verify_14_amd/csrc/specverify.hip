@@ -10,37 +10,37 @@
 //        section 3 (flattened tree, one verifier pass) and section 4
 //        ("eagle_round" step 4, the walk from the root).
 //
-// One call is two kernel launches on the caller's stream.
-//   * Row kernel, one block per (sequence b, row, segment) of every q/p logit
-//     row that an accept test reads: it streams the segment (16-byte loads,
-//     eight per thread per batch, the next batch issued before the current
-//     one is used) and stores (m, s), s = sum exp((z - m)/T) from the
-//     hardware exp2 in fp32, summed in groups of 32 and accumulated in
-//     double.  This is the HBM-bound part.  The last of b's blocks to finish
-//     (an arrival counter per sequence) runs b's accept step: one wave64 for
-//     a chain (lane i = position i+1, ratio q(d)/p(d) in double, ballot + ffs
-//     for the first rejection) or the whole block for a tree (every node
-//     tested in parallel, then a wave walks the parent array with ballots).
-//     For bf16 logits a few extra blocks fill a table of exp(z/T) for every
-//     bf16 bit pattern.
-//   * Sample kernel, one block per (b, 4096-token chunk) of the row(s) b
-//     samples from: chunk sums in double (exp from the table, or a
-//     table-driven fp64 routine for fp32 logits).  The last of b's blocks to
-//     finish runs the final step: it combines the chunk sums, finds the chunk
-//     holding u*W, rescans it with a block-wide prefix scan and writes the
-//     token (inverse CDF in token order).
-// Blocks of one kernel exchange data through self-validating records
+// Launches of one call, all on the caller's stream:
+//   * Row kernel k_rows: one block per (sequence b, row, segment) of every
+//     q/p logit row an accept test reads.  It streams the segment (16-byte
+//     nontemporal loads, U per thread per batch, the next batch in flight)
+//     and stores (m, s), s = sum exp((z - m)/T) from the hardware exp2 in
+//     fp32 (one fma per exponent argument against a wave-uniform reference)
+//     summed in double.  This is the HBM-bound part.  After the row blocks
+//     come, for bf16 chains, the blocks that fill a per-call table of
+//     exp(z/T) over the bf16 grid (kTabKeys), and for chains one accept block
+//     per sequence: one wave (lane i = position i+1) polls the sequence's
+//     row records, forms q(d)/p(d) in the log domain in double, ballots, and
+//     stores the sequence's state.  Blocks are dispatched in index order, so
+//     an accept block only waits on row blocks that have started.
+//   * Chains of bf16 logits in 16-byte aligned rows: k_chunk_tab forms the
+//     chunk sums (2048-token chunks) of the row(s) each sequence samples
+//     from with every exponential one read of the block's LDS copy of the
+//     table; k_final_tab then runs each sequence's final step: it combines
+//     the chunk sums, finds the chunk holding u*W, rescans it with a
+//     block-wide prefix scan and writes the token (inverse CDF in token
+//     order).
+//   * Other chains (fp32 logits, unaligned rows): k_chunks forms the chunk
+//     sums through a table-driven fp64 exp (exp_rel) and ends with one
+//     final-step block per sequence, which waits (bounded) for its records.
+//   * Trees: k_sample, whose blocks each run the sequence's tree accept
+//     (every node tested in parallel, a wave walks the parent array with
+//     ballots), form their group of chunk sums, and whose last block to
+//     finish for a sequence (an arrival counter) runs the final step.
+// Blocks of one launch exchange data through self-validating records
 // (sv_device.h): no cache-wide fences and no waits on blocks that have not
-// started; the row kernel's results reach the sample kernel across the
-// kernel boundary.
+// started; launch boundaries carry the rest.
 //
-// The residual avoids an extra sweep: with pass-1 statistics it decides
-// which tokens certainly have q > p or q < p (a log-domain comparison with a
-// margin), accumulates sum a_t, sum b_t, the same two sums over the certain
-// q > p set and over the near-threshold band in double, and forms
-// W = sum_{q>p} (a_t - rho b_t) + band, rho = Sq/Sp, once the exact Sq, Sp
-// are known.  The band is exact: its tokens share one zq - zp (one ratio
-// q/p) or their chunk is rescanned with the exact rho.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -279,14 +279,15 @@ __device__ __forceinline__ uint4 encode16(const float* x)
 // Records passed between blocks of one launch
 // ---------------------------------------------------------------------------
 // A record is a whole number of 16-byte atoms whose last word is a tag:
-// tag = gen ^ hash(every other word), with gen the low word of the call's
-// generation (a per-workspace count of finished calls, plus one).  Writers
-// store the atoms with agent-coherent (sc1) 16-byte buffer stores; readers
-// load all atoms with coherent loads and take the record once the tag
-// matches what they loaded.  A record left by an earlier call fails the
-// check (its tag carries another generation), and so does a record read
-// while its stores are still landing (the hash no longer matches the
-// mixture), so no ordering between the stores is needed.  Coherent accesses
+// tag = epoch ^ hash(every other word), with epoch the low word of the
+// call's number (a 64-bit count of the library's calls that starts at a
+// value taken from the clock when the library is loaded).  Writers store
+// the atoms with agent-coherent (sc1) 16-byte buffer stores; readers load
+// all atoms with coherent loads and take the record once the tag matches
+// what they loaded.  A record left by an earlier call fails the check (its
+// tag carries another call's number), and so does a record read while its
+// stores are still landing (the hash no longer matches the mixture), so no
+// ordering between the stores is needed.  Coherent accesses
 // go to the level shared by all XCDs: no cache-wide write-back or
 // invalidation is involved.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -1,6 +1,9 @@
-// sv_tree.hip -- the tree attention mask and position ids of a flattened
-// draft tree ("投机解码与 EAGLE", section 3: each node attends to itself and
-// its ancestors only).  gfx950, wave64.
+// sv_tree.hip -- draft-tree kernels: the tree attention mask and position
+// ids of a flattened draft tree ("投机解码与 EAGLE", section 3: each node
+// attends to itself and its ancestors only), and the EAGLE-2 dynamic draft
+// tree build (section 4, eagle_round steps 1-2: expand the frontier's top-k
+// children by cumulative log-probability, keep the best budget nodes),
+// as expand / select / finalize launches.  gfx950, wave64.
 
 #include <hip/hip_runtime.h>
 #include <math.h>

@@ -165,3 +165,16 @@ def test_missing_library_fails_loudly(tmp_path):
             "sys.exit(3)\n")
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True)
     assert r.returncode == 0 and "IMPORT-ERROR" in r.stdout, r.stdout + r.stderr
+
+
+def test_bench_kernel_hash_ignores_comments_only():
+    """The row kernel's PMC summary is keyed by a hash of its sources with
+    comments removed: a comment change keeps it, a code change does not."""
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(ROOT, "bench.py"))
+    b = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(b)
+    code = 'int f(int a) { return a + 1; } // note\nconst char* s = "x // y";\n'
+    assert b.code_text(code) == b.code_text("/* head */\n" + code.replace("// note", "// other"))
+    assert b.code_text(code) != b.code_text(code.replace("a + 1", "a + 2"))
+    assert '"x // y"' in b.code_text(code)
