@@ -54,6 +54,7 @@
 
 #include "sv_device.h"
 #include "specverify.h"
+#include "sv_host.h"
 
 namespace sv {
 
@@ -2244,10 +2245,13 @@ bool value_table_range(float T, uint32_t* lo)
     return true;
 }
 
-int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es)
+// Logit rows of B sequences x nrows rows x V elements of es bytes.
+int check_rows(const void* base, int64_t seq_stride, int64_t row_stride, int es, int B, int nrows, int V)
 {
     if (((uintptr_t)base % (uintptr_t)es) != 0) return SV_EALIGN;
     if (seq_stride < 0 || row_stride < 0) return SV_EINVAL;
+    if (seq_stride > INT64_MAX / es || row_stride > INT64_MAX / es) return SV_EINVAL;
+    if (!sv::span_fits(B, seq_stride * es, nrows, row_stride * es, 1, 0, (int64_t)V * es)) return SV_EINVAL;
     return SV_OK;
 }
 
@@ -2463,7 +2467,7 @@ size_t sv_chain_workspace_bytes(int B, int N, int V)
 
 size_t sv_tree_workspace_bytes(int B, int T, int V)
 {
-    if (B < 0 || T < 0 || T + 1 > sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
+    if (B < 0 || T < 0 || T >= sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
     return make_layout(B, 2 * (T + 1), V).total;
 }
 
@@ -2483,9 +2487,9 @@ int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t
     if (N > 0 && (!draft_logits || !draft_tokens)) return SV_EINVAL;
     if ((out_src_rows || out_kv_len) && !kv_len_in) return SV_EINVAL;
     const int es = dtype == SV_BF16 ? 2 : 4;
-    int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
+    int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es, B, N + 1, V);
     if (rc) return rc;
-    if (N > 0 && (rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
+    if (N > 0 && (rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es, B, N, V))) return rc;
     if (!item_count_ok(B, 2 * N + 1, V)) return SV_ESHAPE;
     const Layout L = make_layout(B, 2 * N + 1, V);
     if (!regions_fit(L)) return SV_ESHAPE;
@@ -2556,17 +2560,17 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if (B < 0 || T < 0 || V < 1 || max_depth < 0 || !(temperature > 0.0f) || !(temperature < INFINITY) ||
         (walk != SV_WALK_FIRST_ACCEPTED && walk != SV_WALK_BEST_CHILD))
         return SV_EINVAL;
-    if (T + 1 > sv::kMaxNodes || max_depth > T || V > sv::kMaxChunks * sv::kChunk) return SV_ESHAPE;
+    if (T >= sv::kMaxNodes || max_depth > T || V > sv::kMaxChunks * sv::kChunk) return SV_ESHAPE;
     if (B == 0) return SV_OK;
     if (!target_logits || !draft_logits || !node_tokens || !parents || !out_tokens || !out_path_nodes ||
         !out_num_accepted)
         return SV_EINVAL;
     if ((out_src_rows || out_kv_len) && !kv_len_in) return SV_EINVAL;
     const int es = dtype == SV_BF16 ? 2 : 4;
-    int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es);
-    if (rc) return rc;
-    if ((rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es))) return rc;
     const int nn = T + 1;
+    int rc = check_rows(target_logits, tgt_seq_stride, tgt_row_stride, es, B, nn, V);
+    if (rc) return rc;
+    if ((rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es, B, nn, V))) return rc;
     if (!item_count_ok(B, 2 * nn, V)) return SV_ESHAPE;
     const Layout L = make_layout(B, 2 * nn, V);
     if (!regions_fit(L)) return SV_ESHAPE;

@@ -11,6 +11,7 @@
 namespace sv {
 
 constexpr int kBlock = 256;          // threads per block in every kernel
+
 constexpr int kWaves = kBlock / 64;  // wave64
 constexpr int kChunk = 2048;         // elements per sampling chunk (8 per thread)
 constexpr int kPerThread = kChunk / kBlock;

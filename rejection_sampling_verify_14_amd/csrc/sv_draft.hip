@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "specverify.h"
+#include "sv_host.h"
 #include "sv_device.h"
 
 namespace sv {
@@ -449,6 +450,9 @@ extern "C" int sv_sample_draft(const void* logits, int64_t seq_stride, int64_t r
     if (!logits || !out_tokens) return SV_EINVAL;
     const int es = dtype == SV_BF16 ? 2 : 4;
     if (((uintptr_t)logits) % es) return SV_EALIGN;
+    if (seq_stride > INT64_MAX / es || row_stride > INT64_MAX / es ||
+        !sv::span_fits(B, seq_stride * es, R, row_stride * es, 1, 0, (int64_t)V * es))
+        return SV_EINVAL;
     sv::DraftArgs A;
     A.rows = static_cast<const char*>(logits);
     A.seq_stride = seq_stride;

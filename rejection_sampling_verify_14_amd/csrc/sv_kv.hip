@@ -17,6 +17,7 @@
 #include <stdint.h>
 
 #include "specverify.h"
+#include "sv_host.h"
 
 namespace sv {
 
@@ -94,6 +95,7 @@ extern "C" int kv_compact_indices(const int32_t* path_nodes, const int32_t* num_
             (plane_stride & 15))
             return SV_EALIGN;
         if ((int64_t)row_bytes > row_stride) return SV_EINVAL;
+        if (!sv::span_fits(n_planes, plane_stride, B, seq_stride, kv_rows, row_stride, row_bytes)) return SV_EINVAL;
         // the gather's grid: planes and sequences are grid dimensions
         if (n_planes > 0 && row_bytes > 0 && (B > 65535 || n_planes > 65535)) return SV_ESHAPE;
     }

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "specverify.h"
+#include "sv_host.h"
 
 namespace sv {
 
@@ -635,7 +636,7 @@ extern "C" int tree_attention_mask(const int32_t* parents, int parents_shared, c
                                    int T, uint64_t* out_mask, int32_t* out_positions, hipStream_t stream)
 {
     if (B < 0 || T < 0) return SV_EINVAL;
-    if (T + 1 > sv::kTreeMaxNodes) return SV_ESHAPE;
+    if (T >= sv::kTreeMaxNodes) return SV_ESHAPE;
     if (B == 0) return SV_OK;
     if (!parents || !out_mask || !out_positions) return SV_EINVAL;
     hipLaunchKernelGGL(sv::k_tree_mask, dim3((unsigned)B), dim3(sv::kTreeBlock), 0, stream, parents, parents_shared,
@@ -658,6 +659,9 @@ extern "C" int tree_expand(const void* frontier_logits, int64_t seq_stride, int6
     const int es = dtype == SV_BF16 ? 2 : 4;
     if (((uintptr_t)frontier_logits) % es) return SV_EALIGN;
     if ((int64_t)B * F > 0x7FFFFFFF) return SV_ESHAPE;
+    if (seq_stride > INT64_MAX / es || row_stride > INT64_MAX / es ||
+        !sv::span_fits(B, seq_stride * es, F, row_stride * es, 1, 0, (int64_t)V * es))
+        return SV_EINVAL;
     sv::ExpandArgs A;
     A.rows = static_cast<const char*>(frontier_logits);
     A.seq_stride = seq_stride;

@@ -82,6 +82,8 @@ def test_chain_argument_errors(sv):
     assert _chain(L, wsb=16) == 5 and _chain(L, ws=None) == 5   # SV_EWORKSPACE
     assert _chain(L, B=0) == 0                       # empty batch: nothing to do
     assert _chain(L, src=FAKE) == 1 and _chain(L, kvl=FAKE) == 1   # KV outputs need kv_len_in
+    # strides whose last element lies past a 64-bit byte offset are refused
+    assert _chain(L, qr=(1 << 62) // 4) == 1 and _chain(L, qs=(1 << 61), qr=32) == 1
     # the no-allocation entry point refuses sizes beyond its static scratch before any HIP call
     na = L.spec_verify_chain_noalloc
     assert na(FAKE, 8 * 128256, 128256, FAKE, 8 * 128256, 128256, 1, FAKE, 1024, 7, 128256, 0, 0, 1.0, FAKE, FAKE,
@@ -103,6 +105,7 @@ def test_tree_and_kv_argument_errors(sv):
                                   a["B"], a["T"], a["V"], a["md"], a["walk"], 0, 0, a["T_"], a["out"], a["path"], a["num"],
                                   None, None, None, a["kvin"], a["src"], a["kvl"], a["ws"], a["wsb"], None, None)
     assert tree(T=1024) == 3 and tree(md=6) == 3 and tree(md=-1) == 1
+    assert tree(T=2**31 - 1) == 3                                 # no overflow in T + 1
     assert tree(par=None) == 1 and tree(path=None) == 1 and tree(T_=0.0) == 1 and tree(dt=9) == 2
     assert tree(wsb=100) == 5 and tree(B=0) == 0
     assert tree(walk=2) == 1 and tree(walk=-1) == 1 and tree(walk=1, B=0) == 0
