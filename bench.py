@@ -3,7 +3,7 @@
 A step is one verify round over one batch of synthetic inputs: for the chain
 workload (default, B=256 sequences, N=7 drafts, V=128256, bf16 logits, T=1)
 one spec_verify_chain call, which also writes the KV rows kept; tree
-workloads call spec_verify_tree (config 5 adds the in-place KV gather of
+workloads call spec_verify_tree (the dynamic-tree workload adds the in-place KV gather of
 kv_compact_indices).  Inputs are resident in HBM before the timed region;
 the step cycles through a pool of distinct logit sets (8 x 0.99 GB for the
 chain workload, far beyond the 256 MB Infinity Cache) and uses a fresh
@@ -18,11 +18,11 @@ start/stop events (stamped by its launch) for the roofline line.
 Output: one JSON line (see the keys below); also the oracle timed on this
 host's cores on a bounded sample (cpu_baseline).
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload chain_b256_v128256]
   python bench.py --copy-calibration     # plain copy of known size, for PMC scaling
-  python bench.py --tree-mask | --tree-build   # the tree kernels on config 5
+  python bench.py --tree-mask | --tree-build   # the tree kernels on the dynamic trees (B=128, 61 nodes)
   python bench.py --walk-compare          # exercise 3: [2,2,2] tree vs 14-draft chain
-  python bench.py --draft-sample          # sv_sample_draft on config 3's draft rows
+  python bench.py --draft-sample          # sv_sample_draft on the draft rows of B=256 chains (V=128256 bf16)
 """
 from __future__ import annotations
 
@@ -290,7 +290,7 @@ def copy_calibration():
 
 
 def tree_mask_bench(steps: int, warmup: int):
-    """tree_attention_mask on config 5's trees (B=128, 61 nodes, per-sequence
+    """tree_attention_mask on the dynamic trees (B=128, 61 nodes, per-sequence
     parents from the dynamic-tree recipe; the logits only shape the trees, so
     they are drawn at a small V).  One JSON line of its own."""
     import torch
@@ -298,7 +298,7 @@ def tree_mask_bench(steps: int, warmup: int):
     import rejection_sampling_verify_14_amd as sv
     import synth
 
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"]
     parents = synth.dynamic_tree_inputs(w.with_sizes(V=1024), seed=7, B=w.B)["parents"].to("cuda")
     B, nn = parents.shape
     L0 = torch.full((B,), w.L0, dtype=torch.int32, device="cuda")
@@ -330,16 +330,16 @@ def tree_mask_bench(steps: int, warmup: int):
     W = (nn + 63) // 64
     nbytes = B * nn * 4 + B * 4 + B * nn * (8 * W + 4)   # parents + kv_len read, mask + positions written
     print(json.dumps({
-        "metric": "tree attention mask builds/s (config 5 trees)", "value": round(1e6 / us, 1), "unit": "calls/s",
+        "metric": "tree attention mask builds/s (B=128 dynamic 61-node trees)", "value": round(1e6 / us, 1), "unit": "calls/s",
         "us_per_call": round(us, 3), "steps": steps, "warmup": warmup, "higher_is_better": True,
-        "data": "synthetic", "config": {"workload": f"tree mask B={B} nodes={nn} (config 5 dynamic trees)"},
+        "data": "synthetic", "config": {"workload": f"tree mask B={B} nodes={nn} (dynamic trees)"},
         "roofline": {"bound": "latency", "bytes_per_call": nbytes, "achieved": round(nbytes / us / 1e3, 2),
                      "peak": 8000.0, "unit": "GB/s", "frac": round(nbytes / us / 1e3 / 8000.0, 6)}}), flush=True)
 
 
 def tree_build_bench(steps: int, warmup: int):
     """The EAGLE-2 dynamic tree grown on the device (tree_expand per level,
-    tree_select between levels, tree_finalize) over config 5's draft rows:
+    tree_select between levels, tree_finalize) over the dynamic-tree draft rows (B=128, V=152064 bf16):
     B=128, depth 6, top-10, budget 60, V=152064 bf16, T=0.7.  One JSON line
     of its own; the HBM roofline counts every expanded row read once."""
     import torch
@@ -347,7 +347,7 @@ def tree_build_bench(steps: int, warmup: int):
     import rejection_sampling_verify_14_amd as sv
     import synth
 
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"]
     rows = synth.dynamic_tree_inputs(w, seed=7, device="cuda")["expanded_p"]
     B, n_exp, V = rows.shape
     for _ in range(warmup):
@@ -366,7 +366,7 @@ def tree_build_bench(steps: int, warmup: int):
     nbytes = B * n_exp * V * rows.element_size()
     gbps = nbytes / us / 1e3
     print(json.dumps({
-        "metric": "dynamic draft trees built/s (config 5)", "value": round(1e6 / us * B, 1), "unit": "trees/s",
+        "metric": "dynamic draft trees built/s (B=128, depth 6, top-10, budget 60)", "value": round(1e6 / us * B, 1), "unit": "trees/s",
         "us_per_batch": round(us, 2), "steps": steps, "warmup": warmup, "higher_is_better": True, "data": "synthetic",
         "config": {"workload": f"EAGLE-2 tree build B={B} depth={w.depth} topk={w.topk} budget={w.budget} "
                                f"V={V} bf16 T={w.T}"},
@@ -423,7 +423,7 @@ def _tree_expectations(a, par):
 def walk_compare(rounds: int = 8, B: int = 256, V: int = 128256, seed: int = 11, sigma_noise=None) -> dict:
     """[PT] / [FA] exercise 3: a [2, 2, 2] draft tree (children = the draft's
     top-2 at each node, 8 candidate paths) against a chain of equal verifier
-    compute (14 drafts, d_i ~ p_i), on config 3's logit recipe (sigma_noise,
+    compute (14 drafts, d_i ~ p_i), on the B=256 chain logit recipe (sigma_noise,
     the draft's distance from the verifier, may be overridden).  For both
     tree walks and the chain: tokens per verifier call (accepted + 1) from the
     device verify, and its exact expectation from the same logits (fp64); and
@@ -434,7 +434,7 @@ def walk_compare(rounds: int = 8, B: int = 256, V: int = 128256, seed: int = 11,
     import rejection_sampling_verify_14_amd as sv
     import synth
 
-    w = synth.WORKLOADS["c3"].with_sizes(V=V, B=B)
+    w = synth.WORKLOADS["chain_b256_v128256"].with_sizes(V=V, B=B)
     if sigma_noise is not None:
         w = w.with_sizes(sigma_noise=float(sigma_noise))
     T = w.T
@@ -499,7 +499,7 @@ def walk_compare(rounds: int = 8, B: int = 256, V: int = 128256, seed: int = 11,
 
 
 def walk_compare_bench(rounds: int):
-    """One JSON line per draft quality: config 3's own recipe (the draft close
+    """One JSON line per draft quality: the B=256 chain recipe (the draft close
     to the verifier, sigma_noise 0.4) and a far draft (sigma_noise 3.0)."""
     for noise in (None, 3.0):
         res = walk_compare(rounds=rounds, sigma_noise=noise)
@@ -507,14 +507,14 @@ def walk_compare_bench(rounds: int):
             "metric": "tokens per verifier call: [2,2,2] tree vs 14-draft chain (exercise 3)",
             "value": res["tree_first_accepted"]["tokens_per_call"], "unit": "tokens/call", "higher_is_better": True,
             "data": "synthetic",
-            "config": {"workload": "config 3 logit recipe, B=256, V=128256 bf16, T=1.0; tree [2,2,2] (draft top-2 "
+            "config": {"workload": "chain logit recipe, B=256, V=128256 bf16, T=1.0; tree [2,2,2] (draft top-2 "
                                    "per node); chain N=14 (d ~ p)",
                        "sigma_noise": 0.4 if noise is None else noise},
             **res}), flush=True)
 
 
 def draft_sample_bench(steps: int, warmup: int):
-    """sv_sample_draft on config 3's draft rows (B=256, V=128256 bf16, T=1):
+    """sv_sample_draft on the draft rows of B=256 chains (V=128256 bf16) (B=256, V=128256 bf16, T=1):
     all 7 positions in one call, and one position (the autoregressive
     step).  One JSON line each; the HBM roofline counts every row read once."""
     import torch
@@ -522,7 +522,7 @@ def draft_sample_bench(steps: int, warmup: int):
     import rejection_sampling_verify_14_amd as sv
     import synth
 
-    w = synth.WORKLOADS["c3"]
+    w = synth.WORKLOADS["chain_b256_v128256"]
     rows = synth.chain_inputs(w, seed=5, device="cuda")["zp"]
     hip = Hip()
     hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -555,7 +555,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="chain_b256_v128256", choices=["chain_b64_v32000", "chain_b256_v128256", "tree_static_b32_v128256", "tree_dynamic_b128_v152064"])
     ap.add_argument("--pool", type=int, default=None)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -563,9 +563,9 @@ def main():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the row kernel's PMC summary for --workload from rocprofv3 counter CSVs")
     ap.add_argument("--pmc-commands", nargs="*", default=[], help="the commands that made the CSVs (recorded)")
-    ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on config 5 trees instead")
-    ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on config 5 rows instead")
-    ap.add_argument("--draft-sample", action="store_true", help="time sv_sample_draft on config 3's draft rows")
+    ap.add_argument("--tree-mask", action="store_true", help="time tree_attention_mask on the dynamic trees (B=128, 61 nodes) instead")
+    ap.add_argument("--tree-build", action="store_true", help="time the dynamic tree build on the dynamic-tree rows (B=128, V=152064) instead")
+    ap.add_argument("--draft-sample", action="store_true", help="time sv_sample_draft on the draft rows of B=256 chains (V=128256 bf16)")
     ap.add_argument("--walk-compare", action="store_true",
                     help="exercise 3: [2,2,2] tree (both walks) vs a 14-draft chain, tokens per verifier call")
     args = ap.parse_args()
@@ -703,10 +703,10 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": {"c3": "chain verify B=256 N=7 V=128256 bf16 logits T=1.0",
-                         "c2": "chain verify B=64 N=5 V=32000 fp32 logits T=1.0",
-                         "c4": "static 26-node tree verify B=32 V=128256 bf16 logits T=1.0",
-                         "c5": "dynamic 61-node tree verify B=128 V=152064 bf16 T=0.7 + KV gather"}[w.name],
+            "workload": {"chain_b256_v128256": "chain verify B=256 N=7 V=128256 bf16 logits T=1.0",
+                         "chain_b64_v32000": "chain verify B=64 N=5 V=32000 fp32 logits T=1.0",
+                         "tree_static_b32_v128256": "static 26-node tree verify B=32 V=128256 bf16 logits T=1.0",
+                         "tree_dynamic_b128_v152064": "dynamic 61-node tree verify B=128 V=152064 bf16 T=0.7 + KV gather"}[w.name],
             "logits": w.dtype, "B": B, "V": w.V, "pool_sets": pool,
             "arithmetic": "row statistics f32 exp2 summed in f64; accept ratio and sampled rows f64",
             "step": "one spec_verify_* launch (KV rows included)" + (" + the in-place KV gather" if kv is not None

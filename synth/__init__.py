@@ -78,18 +78,18 @@ class Workload:
 
 WORKLOADS = {
     # chain, B=1, N=4, V=32, fp32, q-logits N(0,2^2) fixed from seed 0, noise 0.5
-    "c1": Workload("c1", "chain", B=1, N=4, V=32, dtype="f32", sigma_q=2.0, sigma_noise=0.5, rounds=10000),
+    "chain_b1_v32": Workload("chain_b1_v32", "chain", B=1, N=4, V=32, dtype="f32", sigma_q=2.0, sigma_noise=0.5, rounds=10000),
     # chain, B=64, N=5, V=32000, fp32, N(0,3^2) + 8 peaks (+6), noise 0.7
-    "c2": Workload("c2", "chain", B=64, N=5, V=32000, dtype="f32", sigma_q=3.0, sigma_noise=0.7, prior="peaks",
+    "chain_b64_v32000": Workload("chain_b64_v32000", "chain", B=64, N=5, V=32000, dtype="f32", sigma_q=3.0, sigma_noise=0.7, prior="peaks",
                    peaks=8, peak_boost=6.0, rounds=1000, pool=4),
     # chain, B=256, N=7, V=128256, bf16, N(0,3^2) - 1.1 ln rank, noise 0.4
-    "c3": Workload("c3", "chain", B=256, N=7, V=128256, dtype="bf16", sigma_q=3.0, sigma_noise=0.4, prior="zipf",
+    "chain_b256_v128256": Workload("chain_b256_v128256", "chain", B=256, N=7, V=128256, dtype="bf16", sigma_q=3.0, sigma_noise=0.4, prior="zipf",
                    rounds=500, pool=8),
     # static 26-node tree, B=32, V=128256, bf16, noise 0.5
-    "c4": Workload("c4", "tree_static", B=32, V=128256, dtype="bf16", sigma_q=3.0, sigma_noise=0.5, prior="zipf",
+    "tree_static_b32_v128256": Workload("tree_static_b32_v128256", "tree_static", B=32, V=128256, dtype="bf16", sigma_q=3.0, sigma_noise=0.5, prior="zipf",
                    depth=5, rounds=200, pool=8, L0=4095),
     # dynamic 60-node tree, depth 6, topk 10, B=128, V=152064, bf16, T=0.7, noise 0.3, KV [B, 4156, 8, 128]
-    "c5": Workload("c5", "tree_dynamic", B=128, V=152064, dtype="bf16", T=0.7, sigma_q=3.0, sigma_noise=0.3,
+    "tree_dynamic_b128_v152064": Workload("tree_dynamic_b128_v152064", "tree_dynamic", B=128, V=152064, dtype="bf16", T=0.7, sigma_q=3.0, sigma_noise=0.3,
                    prior="zipf", depth=6, topk=10, budget=60, rounds=200, pool=4, L0=4095, kv_heads=8, kv_dim=128),
 }
 

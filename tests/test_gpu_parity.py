@@ -2,7 +2,7 @@
 
 Every case prints its name before it runs.  Sizes: reduced cases span
 several 2048-element chunks and a ragged tail and run the oracle on every
-sequence; the full-size workloads (C1..C5) run the device path in the launch
+sequence; the full-size workloads (chains of B=1, 64, 256 sequences, static and dynamic trees) run the device path in the launch
 configuration the benchmark times and the oracle on a window of sequences.
 """
 import numpy as np
@@ -54,15 +54,15 @@ def test_device_philox_matches_oracle():
 # --------------------------------------------------------------------------- #
 CHAIN_CASES = [
     # name, workload, overrides (B, N, V, T, dtype)
-    ("c2_small_ragged", "c2", dict(B=16, N=5, V=9001)),
-    ("c3_small_bf16", "c3", dict(B=24, N=7, V=20011)),
-    ("c3_temp07", "c3", dict(B=16, N=4, V=12289, T=0.7)),
-    ("c3_n1", "c3", dict(B=40, N=1, V=5000)),
-    ("c3_n64", "c3", dict(B=4, N=64, V=3001)),
-    ("c1_tiny_v", "c1", dict(B=50, N=4, V=32)),
-    ("v_tail_only", "c2", dict(B=8, N=3, V=7)),
-    ("v_one_token", "c2", dict(B=4, N=2, V=1)),
-    ("f32_temp19", "c2", dict(B=12, N=6, V=4097, T=1.9)),
+    ("chain_b64_small_ragged", "chain_b64_v32000", dict(B=16, N=5, V=9001)),
+    ("chain_b256_small_bf16", "chain_b256_v128256", dict(B=24, N=7, V=20011)),
+    ("chain_b256_temp07", "chain_b256_v128256", dict(B=16, N=4, V=12289, T=0.7)),
+    ("chain_b256_n1", "chain_b256_v128256", dict(B=40, N=1, V=5000)),
+    ("chain_b256_n64", "chain_b256_v128256", dict(B=4, N=64, V=3001)),
+    ("chain_b1_tiny_v", "chain_b1_v32", dict(B=50, N=4, V=32)),
+    ("v_tail_only", "chain_b64_v32000", dict(B=8, N=3, V=7)),
+    ("v_one_token", "chain_b64_v32000", dict(B=4, N=2, V=1)),
+    ("f32_temp19", "chain_b64_v32000", dict(B=12, N=6, V=4097, T=1.9)),
 ]
 
 
@@ -95,7 +95,7 @@ TABLE_CASES = [
 @pytest.mark.parametrize("name,ov", TABLE_CASES, ids=[c[0] for c in TABLE_CASES])
 def test_chain_parity_table_path(name, ov):
     log(f"[case] {name}")
-    w = W["c3"].with_sizes(V=ov["V"], T=ov["T"])
+    w = W["chain_b256_v128256"].with_sizes(V=ov["V"], T=ov["T"])
     rep = compare.Report()
     for rnd in range(3):
         r, g, _ = run_chain(w, seed=4000 + rnd, rnd=rnd, B=ov["B"], N=ov["N"])
@@ -109,7 +109,7 @@ def test_chain_table_path_logits_outside_table():
     entries, subnormals; and whole sequences whose reference is beyond
     512 T (their rows take exp_rel throughout)."""
     log("[case] tab_outside")
-    w = W["c3"].with_sizes(V=8000)
+    w = W["chain_b256_v128256"].with_sizes(V=8000)
     B, N = 16, 4
 
     def plant(inp):
@@ -140,7 +140,7 @@ def test_chain_table_path_logits_outside_table():
 def test_chain_n0_plain_sampling():
     """N = 0: the step samples q_1 directly (no drafts)."""
     log("[case] chain_n0")
-    w = W["c3"].with_sizes(V=30001)
+    w = W["chain_b256_v128256"].with_sizes(V=30001)
     rep, g, _ = run_chain(w, seed=3, rnd=3, B=32, N=0)
     assert (g["num_accepted"] == 0).all()
     _done("chain_n0", rep)
@@ -151,7 +151,7 @@ def test_chain_edge_cases():
     (accepted), q(d) = -inf (rejected), p == q (all accepted), and masked
     vocab entries, all in one batch."""
     log("[case] chain_edges")
-    w = W["c2"].with_sizes(V=6007)
+    w = W["chain_b64_v32000"].with_sizes(V=6007)
     B, N = 12, 4
 
     def plant(inp):
@@ -182,7 +182,7 @@ def test_residual_near_threshold_exact(dtype, noise):
     logits 1e-7 apart): many tokens sit at the q > p threshold.  The
     residual mass and the sampled token must still match the oracle."""
     log(f"[case] near_threshold {dtype} noise={noise}")
-    w = W["c3"].with_sizes(V=20000, dtype=dtype)
+    w = W["chain_b256_v128256"].with_sizes(V=20000, dtype=dtype)
     B, N = 24, 3
 
     def plant(inp):
@@ -203,7 +203,7 @@ def test_residual_near_threshold_exact(dtype, noise):
 def test_chain_strided_inputs():
     """Sequence and row strides larger than the packed layout."""
     log("[case] chain_strided")
-    w = W["c3"].with_sizes(V=8000)
+    w = W["chain_b256_v128256"].with_sizes(V=8000)
     B, N = 10, 3
     inp = synth.chain_inputs(w, 5, "cuda", B=B, N=N)
     bigq = torch.zeros((B, N + 3, w.V + 24), dtype=inp["zq"].dtype, device="cuda")
@@ -218,12 +218,12 @@ def test_chain_strided_inputs():
 # --------------------------------------------------------------------------- #
 # Chains, full sizes
 # --------------------------------------------------------------------------- #
-def test_c1_full_10000_rounds():
-    """C1 (B=1, N=4, V=32, fp32), 10,000 rounds with Philox keyed by
+def test_chain_b1_full_10000_rounds():
+    """Chains of B=1, N=4, V=32 fp32, 10,000 rounds with Philox keyed by
     (seed, round, position); fixed logits, fresh d ~ p each round."""
     import rejection_sampling_verify_14_amd as sv
-    log("[case] c1_full")
-    w = W["c1"]
+    log("[case] chain_b1_full")
+    w = W["chain_b1_v32"]
     zq, zp = synth.chain_logits(w, 0, "cuda")
     R = w.rounds
     d_all = synth.chain_draft_tokens(w, zp.expand(R, -1, -1).contiguous(), seed=77)
@@ -247,12 +247,12 @@ def test_c1_full_10000_rounds():
         o = oracle.verify_chain(zqn, zpn, dn[r:r + 1], 0, r, w.T, nthreads=1,
                                 query=compare.sampled_tokens({k: v[r:r + 1] for k, v in g.items()}))
         rep.merge(compare.compare_chain({k: v[r:r + 1] for k, v in g.items()}, o))
-    _done("c1_full", rep)
+    _done("chain_b1_full", rep)
 
 
-@pytest.mark.parametrize("wl,rounds,window", [("c2", 3, 64), ("c3", 2, 24)])
+@pytest.mark.parametrize("wl,rounds,window", [("chain_b64_v32000", 3, 64), ("chain_b256_v128256", 2, 24)])
 def test_chain_full_size(wl, rounds, window):
-    """C2 (all 64 sequences) and C3 (a window of sequences per round) at full
+    """Chains of B=64 (all 64 sequences) and B=256 (a window of sequences per round) at full
     size, in the benchmark's launch configuration."""
     w = W[wl]
     rep = compare.Report()
@@ -265,25 +265,25 @@ def test_chain_full_size(wl, rounds, window):
     _done(f"{wl}_full", rep)
 
 
-def test_c3_full_all_sequences_20_rounds():
-    """C3 at full size (B=256, N=7, V=128256 bf16) in the benchmark's launch
+def test_chain_b256_full_all_sequences_20_rounds():
+    """Chains at full size (B=256, N=7, V=128256 bf16) in the benchmark's launch
     configuration: every sequence of 20 rounds (4 logit sets x 5 rounds)
     against the oracle.  Logs the decision band, flip, exclusion and excused
     mismatch counts; the comparison rules bound the excused mismatches."""
-    w = W["c3"]
+    w = W["chain_b256_v128256"]
     rep = compare.Report()
     for s in range(4):
         inp = synth.chain_inputs(w, 7000 + s, "cuda")
         for r in range(5):
             rnd = 5 * s + r
-            log(f"[case] c3_all set={s} round={rnd}")
+            log(f"[case] chain_b256_all set={s} round={rnd}")
             rr, g, _ = run_chain(w, seed=7000 + s, rnd=rnd, inputs=inp)
             rep.merge(rr)
         del inp
         torch.cuda.empty_cache()
-    log(f"[rates] c3_all: {rep.summary()} band_rate={rep.band_decisions / max(rep.decisions, 1):.3e} "
+    log(f"[rates] chain_b256_all: {rep.summary()} band_rate={rep.band_decisions / max(rep.decisions, 1):.3e} "
         f"excused_rate={rep.token_mismatch_excused / max(rep.samples, 1):.3e}")
-    _done("c3_all", rep)
+    _done("chain_b256_all", rep)
 
 
 # --------------------------------------------------------------------------- #
@@ -297,7 +297,7 @@ def test_path_tree_equals_chain_on_device():
     1e-9 relative."""
     import rejection_sampling_verify_14_amd as sv
     log("[case] path_tree_eq_chain")
-    w = W["c3"].with_sizes(V=10008)
+    w = W["chain_b256_v128256"].with_sizes(V=10008)
     B, N = 20, 6
     inp = synth.chain_inputs(w, 8, "cuda", B=B, N=N)
     ch = sv.spec_verify_chain(inp["zq"], inp["zp"], inp["d"], seed=4, round=9, temperature=0.9)
@@ -315,7 +315,7 @@ def test_path_tree_equals_chain_on_device():
 
 def test_static_tree_reduced():
     log("[case] static_tree_reduced")
-    w = W["c4"].with_sizes(V=9001)
+    w = W["tree_static_b32_v128256"].with_sizes(V=9001)
     rep = compare.Report()
     for rnd in range(3):
         inp = synth.static_tree_inputs(w, 40 + rnd, "cuda", B=12)
@@ -326,7 +326,7 @@ def test_static_tree_reduced():
 
 def test_dynamic_tree_reduced():
     log("[case] dynamic_tree_reduced")
-    w = W["c5"].with_sizes(V=7001)
+    w = W["tree_dynamic_b128_v152064"].with_sizes(V=7001)
     rep = compare.Report()
     for rnd in range(2):
         inp = synth.dynamic_tree_inputs(w, 60 + rnd, "cuda", B=10)
@@ -335,16 +335,16 @@ def test_dynamic_tree_reduced():
     _done("dynamic_tree_reduced", rep)
 
 
-@pytest.mark.parametrize("wl", ["c4", "c5"])
+@pytest.mark.parametrize("wl", ["tree_static_b32_v128256", "tree_dynamic_b128_v152064"])
 def test_best_child_walk_reduced(wl):
-    """The pages' literal walk (walk = 1) on config 4's static tree and
-    config 5's dynamic trees, reduced V: device vs oracle with walk = 1."""
+    """The pages' literal walk (walk = 1) on the static 26-node tree and
+    the dynamic 61-node trees, reduced V: device vs oracle with walk = 1."""
     log(f"[case] best_child_walk_{wl}")
-    w = W[wl].with_sizes(V=9001 if wl == "c4" else 7001)
+    w = W[wl].with_sizes(V=9001 if wl == "tree_static_b32_v128256" else 7001)
     rep = compare.Report()
     kd, ks = [], []
     for rnd in range(2):
-        if wl == "c4":
+        if wl == "tree_static_b32_v128256":
             inp = synth.static_tree_inputs(w, 70 + rnd, "cuda", B=16)
         else:
             inp = synth.dynamic_tree_inputs(w, 70 + rnd, "cuda", B=12)
@@ -433,7 +433,7 @@ def test_draft_sampler_parity():
     of the 16-byte vector), unaligned rows, both dtypes, two temperatures,
     and bad rows."""
     g = torch.Generator(device="cuda").manual_seed(5)
-    w = W["c3"]
+    w = W["chain_b256_v128256"]
     for dt, V, T in (("bf16", 30001, 1.0), ("f32", 4097, 0.7), ("bf16", 2048, 0.8), ("bf16", 5, 1.0)):
         zq = synth.verifier_logits(w.with_sizes(V=V), 24 * 3, g, "cuda").view(24, 3, V)
         rows = zq.to(torch.bfloat16 if dt == "bf16" else torch.float32)
@@ -459,12 +459,12 @@ def test_draft_sampler_parity():
     log("[done] draft parity")
 
 
-def test_draft_sampler_mismatch_rate_c3():
-    """Config 3's draft rows (B=256, 7 positions, V=128256 bf16) over 60
+def test_draft_sampler_mismatch_rate_chain_b256():
+    """The draft rows of B=256 chains (B=256, 7 positions, V=128256 bf16) over 60
     rounds: 107,520 draws, every one against the oracle.  No draw may fall
     outside its token's CDF interval widened by the 1e-6 W band, and the
     excused draws (inside the band, other token) stay below 1e-4 of all."""
-    w = W["c3"]
+    w = W["chain_b256_v128256"]
     inp = synth.chain_inputs(w, seed=31, device="cuda")
     rows = inp["zp"]
     host = synth.to_oracle(rows.contiguous())
@@ -487,20 +487,20 @@ def test_draft_sampler_mismatch_rate_c3():
         same = tok[ok] == o["tokens"][ok]
         excused += int((~same).sum())
         worst = max(worst, float(np.abs(lp[ok][same] - o["logprob"][ok][same]).max(initial=0.0)))
-    log(f"[rates] draft_c3: draws={draws} excused={excused} rate={excused / draws:.3e} "
+    log(f"[rates] draft_chain_b256: draws={draws} excused={excused} rate={excused / draws:.3e} "
         f"max_logprob_err={worst:.2e}")
     assert worst < 1e-6
     assert excused < compare.MISMATCH_BUDGET * draws, f"{excused} excused draws in {draws}"
 
 
 def test_draft_sampler_full_size_sampled():
-    """Config 3's draft rows at full size (B=256, 7 positions, V=128256
+    """The draft rows of B=256 chains at full size (B=256, 7 positions, V=128256
     bf16): every draw in range, and the oracle checks 48 sequences."""
-    w = W["c3"]
+    w = W["chain_b256_v128256"]
     inp = synth.chain_inputs(w, seed=12, device="cuda")
     rows = inp["zp"]
     sel = np.arange(0, w.B, w.B // 48)[:48]
-    tok, lp = _draft_case("c3_full", rows, w.T, seed=77, rnd=1, b_sel=sel)
+    tok, lp = _draft_case("chain_b256_full", rows, w.T, seed=77, rnd=1, b_sel=sel)
     log("[done] draft full size")
 
 
@@ -527,7 +527,7 @@ def test_tree_edge_cases():
     max_depth, NaN in an internal row -- per-sequence -1 flags."""
     import rejection_sampling_verify_14_amd as sv
     log("[case] tree_edges")
-    w = W["c4"].with_sizes(V=3000)
+    w = W["tree_static_b32_v128256"].with_sizes(V=3000)
     inp = synth.static_tree_inputs(w, 3, "cuda", B=6)
     zq, zp, tok = inp["zq"], inp["zp"], inp["tokens"]
     par = inp["parents"].expand(6, -1).contiguous().clone()
@@ -557,13 +557,13 @@ def test_tree_edge_cases():
     assert (deep["num_accepted"] == -1).all()
 
 
-@pytest.mark.parametrize("wl", ["c4", "c5"])
+@pytest.mark.parametrize("wl", ["tree_static_b32_v128256", "tree_dynamic_b128_v152064"])
 def test_tree_full_size(wl):
-    """C4 (static 26-node tree, B=32) and C5 (dynamic 61-node trees, B=128,
+    """The static 26-node tree (B=32) and the dynamic 61-node trees (B=128,
     T=0.7) at full size; the oracle checks a window of sequences."""
     w = W[wl]
     log(f"[case] {wl}_full")
-    if wl == "c4":
+    if wl == "tree_static_b32_v128256":
         inp = synth.static_tree_inputs(w, 900, "cuda")
         rng = (0, w.B)
     else:
@@ -578,33 +578,33 @@ def test_tree_full_size(wl):
     _done(f"{wl}_full_best_child", rep)
 
 
-def test_c5_full_all_sequences():
-    """C5 at full size (B=128 dynamic 61-node trees, V=152064 bf16, T=0.7):
+def test_tree_dynamic_full_all_sequences():
+    """Dynamic trees at full size (B=128 dynamic 61-node trees, V=152064 bf16, T=0.7):
     every sequence against the oracle, both walks, two rounds."""
-    w = W["c5"]
+    w = W["tree_dynamic_b128_v152064"]
     rep = compare.Report()
     inp = synth.dynamic_tree_inputs(w, 905, "cuda")
     for rnd in range(2):
         for walk in (0, 1):
-            log(f"[case] c5_all round={rnd} walk={walk}")
+            log(f"[case] tree_dynamic_all round={rnd} walk={walk}")
             r, g = run_tree(inp["zq"], inp["zp"], inp["tokens"], inp["parents"], 905, rnd, w.T, w.depth, walk=walk)
             rep.merge(r)
-    log(f"[rates] c5_all: {rep.summary()} band_rate={rep.band_decisions / max(rep.decisions, 1):.3e} "
+    log(f"[rates] tree_dynamic_all: {rep.summary()} band_rate={rep.band_decisions / max(rep.decisions, 1):.3e} "
         f"excused_rate={rep.token_mismatch_excused / max(rep.samples, 1):.3e}")
-    _done("c5_all", rep)
+    _done("tree_dynamic_all", rep)
 
 
 # --------------------------------------------------------------------------- #
 # KV compaction
 # --------------------------------------------------------------------------- #
-def test_kv_compaction_full_c5():
-    """C5's KV buffer [B=128, 4096+60, 8, 128] bf16 (two planes): the
+def test_kv_compaction_full_tree_dynamic():
+    """The dynamic-tree workload's KV buffer [B=128, 4096+60, 8, 128] bf16 (two planes): the
     in-place gather equals torch.index_select on a copy, the indices and
     lengths equal the oracle's, and rows outside the kept path are
     untouched."""
     import rejection_sampling_verify_14_amd as sv
     log("[case] kv_c5_full")
-    w = W["c5"]
+    w = W["tree_dynamic_b128_v152064"]
     B, L = w.B, 4096 + w.budget
     rng = np.random.default_rng(0)
     # a valid random path per sequence (strictly increasing from node 0)
@@ -654,7 +654,7 @@ def test_kv_chain_indices_and_invalid_paths():
 
 def test_tree_attention_mask_parity():
     """Ancestor masks and position ids of flattened trees, bit-exact against the
-    oracle: config 4's static tree (shared parents), config 5's dynamic trees,
+    oracle: the static 26-node tree (shared parents), the dynamic 61-node trees,
     random trees of 1..1024 nodes (one to sixteen 64-bit words per row), a
     1024-node chain (the deepest walk) and sequences with broken parents."""
     import rejection_sampling_verify_14_amd as sv
@@ -664,9 +664,9 @@ def test_tree_attention_mask_parity():
         return np.stack([np.concatenate([[-1], rng.integers(0, np.arange(1, nn))]).astype(np.int32)
                          if nn > 1 else np.array([-1], np.int32) for _ in range(B)])
 
-    w5 = synth.WORKLOADS["c5"].with_sizes(V=512)
-    cases = [("c4_static", np.array(synth.STATIC_TREE_PARENTS, np.int32), 32),
-             ("c5_dynamic", synth.dynamic_tree_inputs(w5, seed=4, B=16)["parents"].numpy(), None)]
+    w5 = synth.WORKLOADS["tree_dynamic_b128_v152064"].with_sizes(V=512)
+    cases = [("tree_static_static", np.array(synth.STATIC_TREE_PARENTS, np.int32), 32),
+             ("tree_dynamic_dynamic", synth.dynamic_tree_inputs(w5, seed=4, B=16)["parents"].numpy(), None)]
     for nn in (1, 2, 63, 64, 65, 200, 1024):
         cases.append((f"random_{nn}", random_trees(nn, 5), None))
     cases.append(("chain_1024", np.array([[-1] + list(range(1023))], np.int32), None))
@@ -709,13 +709,13 @@ def test_tree_build_parity():
     """EAGLE-2 dynamic trees grown on the device level by level (tree_expand,
     tree_select, tree_finalize) against the oracle's construction: exact
     trees and frontiers, scores within 1e-6 (the device's row log-sum-exp is
-    accurate to ~1e-8).  Config 5's recipe at a reduced V in bf16 and fp32,
+    accurate to ~1e-8).  The dynamic-tree recipe at a reduced V in bf16 and fp32,
     other top-k / depth settings, and a sequence with a NaN row."""
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"]
     for dt, T in (("bf16", 0.7), ("f32", 1.0)):
         wr = w.with_sizes(V=4096, dtype=dt, T=T)
         rows = synth.dynamic_tree_inputs(wr, seed=21, B=24, device="cuda")["expanded_p"]
-        _tree_build_case(f"c5_reduced_{dt}", rows, w.depth, w.topk, w.budget, T)
+        _tree_build_case(f"tree_dynamic_reduced_{dt}", rows, w.depth, w.topk, w.budget, T)
     g = torch.Generator(device="cuda").manual_seed(3)
     for depth, topk, budget, V in ((3, 16, 100, 1000), (4, 1, 4, 777), (2, 5, 30, 64)):
         rows = (torch.randn((8, 1 + topk * (depth - 1), V), generator=g, device="cuda") * 3).to(torch.bfloat16)
@@ -739,10 +739,10 @@ def test_tree_build_parity():
 
 
 def test_tree_build_full_size_sampled():
-    """Config 5's full vocabulary (V = 152064, bf16, T = 0.7) for 16 sequences."""
-    w = synth.WORKLOADS["c5"]
+    """The dynamic-tree workload's full vocabulary (V = 152064, bf16, T = 0.7) for 16 sequences."""
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"]
     rows = synth.dynamic_tree_inputs(w, seed=22, B=16, device="cuda")["expanded_p"]
-    _tree_build_case("c5_full", rows, w.depth, w.topk, w.budget, w.T)
+    _tree_build_case("tree_dynamic_full", rows, w.depth, w.topk, w.budget, w.T)
     log("[done] tree_build full size")
 
 
@@ -753,7 +753,7 @@ def test_workspace_reused_across_calls_and_shapes():
     left its own."""
     import rejection_sampling_verify_14_amd as sv
     log("[case] workspace_reuse")
-    wc, wt = W["c3"].with_sizes(V=9001), W["c4"].with_sizes(V=6007)
+    wc, wt = W["chain_b256_v128256"].with_sizes(V=9001), W["tree_static_b32_v128256"].with_sizes(V=6007)
     nbytes = max(sv.chain_workspace_bytes(24, 7, 9001), sv.tree_workspace_bytes(12, 25, 9001))
     ws = sv.alloc_workspace(nbytes, "cuda")
     rep = compare.Report()

@@ -85,7 +85,7 @@ def _battery():
     yield lambda: P.test_cdf_edges_of_queried_tokens(oracle)
     yield lambda: P.test_exercise4_batched_kv_length(oracle)
     yield lambda: S.test_stratified_sampling_sweep(oracle, 4)
-    yield lambda: S.test_c1_every_slot_is_distributed_as_q(oracle)
+    yield lambda: S.test_chain_b1_every_slot_is_distributed_as_q(oracle)
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 4)
     yield lambda: TK.test_tree_walk_under_forced_flags(oracle, 7)
     yield lambda: TK.test_best_child_walk_ignores_an_accepted_sibling(oracle)

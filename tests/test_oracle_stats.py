@@ -28,7 +28,7 @@ def _broadcast(z, R):
 
 
 def _c1_runs(orc, R, seed):
-    w = synth.WORKLOADS["c1"]
+    w = synth.WORKLOADS["chain_b1_v32"]
     zq, zp = synth.chain_logits(w, 0, "cpu")           # fixed logits (seed 0)
     d = synth.chain_draft_tokens(w, zp.expand(R, -1, -1).contiguous(), seed).numpy()
     q = softmax(zq[0].double().numpy(), axis=1)
@@ -41,7 +41,7 @@ def _c1_runs(orc, R, seed):
 def test_pages_chi_square_50000_steps(orc):
     """[PT] Implementando, Passo 5 and Exercicios 1: 50,000 speculative steps
     against 50,000 direct draws from q; the two-sample chi-square statistic of
-    the first emitted token is below the 95% critical value.  Workload C1
+    the first emitted token is below the 95% critical value.  The B=1, N=4, V=32 chain workload
     (B=1, N=4, V=32, fp32, q-logits N(0, 2^2) from seed 0, draft noise 0.5)."""
     R = 50000
     out, q, w = _c1_runs(orc, R, seed=20240101)
@@ -56,8 +56,8 @@ def test_pages_chi_square_50000_steps(orc):
     assert stat < chi2.ppf(0.95, df), (stat, df)
 
 
-def test_c1_every_slot_is_distributed_as_q(orc):
-    """C1, 10,000 rounds: conditional on reaching slot s (s = 1..N+1), the
+def test_chain_b1_every_slot_is_distributed_as_q(orc):
+    """The B=1, N=4, V=32 chain, 10,000 rounds: conditional on reaching slot s (s = 1..N+1), the
     token emitted there is distributed as q_s ([PT] O Conceito: the output is
     distributed as q whatever p is); acceptance of slot s matches
     alpha_s = sum min(p_s, q_s)."""

@@ -23,10 +23,10 @@ def _rows(B, depth, topk, V, seed, scale=3.0):
 
 @pytest.mark.parametrize("V,seed", [(512, 3), (3000, 11)])
 def test_matches_the_generators_construction(V, seed):
-    """Config 5's recipe (depth 6, top-10, budget 60) on fp32 rows at T = 1:
+    """The dynamic-tree recipe (depth 6, top-10, budget 60) on fp32 rows at T = 1:
     the oracle's tree equals the one the input generator grows with torch
     (log_softmax in double, stable sorts)."""
-    w = synth.WORKLOADS["c5"].with_sizes(V=V, dtype="f32", T=1.0)
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"].with_sizes(V=V, dtype="f32", T=1.0)
     inp = synth.dynamic_tree_inputs(w, seed=seed, B=6)
     o = oracle.tree_build(inp["expanded_p"].numpy(), w.depth, w.topk, w.budget, w.T)
     assert np.array_equal(o["parents"], inp["parents"].numpy())
@@ -89,7 +89,7 @@ def test_full_budget_keeps_every_candidate():
 def test_structure_of_the_kept_tree():
     """Parents precede children, depth grows by one per edge, a child never
     outscores its parent, and within a level scores do not increase."""
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"]
     rows = _rows(4, w.depth, w.topk, 2000, 6)
     o = oracle.tree_build(rows, w.depth, w.topk, w.budget, 0.7)
     for b in range(4):

@@ -64,7 +64,7 @@ def _chain_as_tree(zq, zp, d):
 def test_path_tree_equals_chain_bit_for_bit(orc, dtype):
     """A path-shaped tree (parent[n] = n-1) is the chain: same decisions,
     tokens, ratios and uniforms, bit for bit (independent code paths)."""
-    w = synth.WORKLOADS["c3"].with_sizes(V=3001, dtype=dtype, B=40, N=6)
+    w = synth.WORKLOADS["chain_b256_v128256"].with_sizes(V=3001, dtype=dtype, B=40, N=6)
     inp = synth.chain_inputs(w, seed=3, device="cpu")
     zq, zp, d = synth.to_oracle(inp["zq"]), synth.to_oracle(inp["zp"]), inp["d"].numpy()
     ch = orc.verify_chain(zq, zp, d, seed=17, rnd=5, T=0.9)
@@ -306,7 +306,7 @@ def test_static_tree_shape():
     assert len(par) == 26 and max(depth) == 5
     assert [depth.count(L) for L in range(1, 6)] == [4, 8, 8, 3, 2]
     assert len(set(par[1:])) == 18
-    w = synth.WORKLOADS["c4"].with_sizes(V=500, B=3)
+    w = synth.WORKLOADS["tree_static_b32_v128256"].with_sizes(V=500, B=3)
     inp = synth.static_tree_inputs(w, seed=1)
     for n in range(len(par)):
         kids = [c for c in range(1, len(par)) if par[c] == n]
@@ -318,7 +318,7 @@ def test_static_tree_shape():
 def test_dynamic_tree_shape():
     """Dynamic trees: budget+1 nodes, parents before children, depth <= 6,
     siblings by descending path score, and every kept node's ancestors kept."""
-    w = synth.WORKLOADS["c5"].with_sizes(V=400, B=4)
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"].with_sizes(V=400, B=4)
     inp = synth.dynamic_tree_inputs(w, seed=2)
     par = inp["parents"].numpy()
     assert par.shape == (4, 61)

@@ -103,9 +103,9 @@ def test_eagle1_default_tree_recursive_definition():
 
 
 def test_positions_match_the_generators_levels():
-    """Per-sequence dynamic trees (config 5's recipe, small V): position - L0 is
+    """Per-sequence dynamic trees (the dynamic-tree recipe, small V): position - L0 is
     the level the generator created each node at."""
-    w = synth.WORKLOADS["c5"].with_sizes(V=512)
+    w = synth.WORKLOADS["tree_dynamic_b128_v152064"].with_sizes(V=512)
     inp = synth.dynamic_tree_inputs(w, seed=3, B=6)
     L0 = np.array([0, 1, 17, 400, 4095, 9], np.int32)
     mask, pos = oracle.tree_mask(inp["parents"].numpy(), L0)

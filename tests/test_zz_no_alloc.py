@@ -40,11 +40,11 @@ def _both(w, seed, rnd, B, N):
 
 
 def test_noalloc_matches_the_workspace_entry_point():
-    w = synth.WORKLOADS["c3"].with_sizes(V=20011)
+    w = synth.WORKLOADS["chain_b256_v128256"].with_sizes(V=20011)
     log("[case] noalloc call 1: B=24 N=7 V=20011")
     r1 = _both(w, 301, 0, 24, 7)
     log("[case] noalloc call 2: B=5 N=3 V=9001 (smaller, over the first call's scratch)")
-    _both(synth.WORKLOADS["c3"].with_sizes(V=9001), 302, 1, 5, 3)
+    _both(synth.WORKLOADS["chain_b256_v128256"].with_sizes(V=9001), 302, 1, 5, 3)
     log("[case] noalloc call 3: the first call again")
     r3 = _both(w, 301, 0, 24, 7)
     for k in r1:
