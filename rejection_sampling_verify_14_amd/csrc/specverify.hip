@@ -23,12 +23,12 @@
 //     row records, forms q(d)/p(d) in the log domain in double, ballots, and
 //     stores the sequence's state.  Blocks are dispatched in index order, so
 //     an accept block only waits on row blocks that have started.
-//   * Chains of bf16 logits in 16-byte aligned rows: k_chunk_tab forms the
-//     chunk sums (2048-token chunks) of the row(s) each sequence samples
-//     from with every exponential one read of the block's LDS copy of the
-//     table; k_final_tab then runs each sequence's final step: it combines
-//     the chunk sums, finds the chunk holding u*W, rescans it with a
-//     block-wide prefix scan and writes the token (inverse CDF in token
+//   * Chains of bf16 logits in 16-byte aligned rows: k_sample_tab's first
+//     blocks form the chunk sums (2048-token chunks) of the row(s) each
+//     sequence samples from, every exponential one read of the block's LDS
+//     copy of the table; its last B blocks run each sequence's final step:
+//     combine the chunk sums, find the chunk holding u*W, rescan it with a
+//     block-wide prefix scan and write the token (inverse CDF in token
 //     order).
 //   * Other chains (fp32 logits, unaligned rows): k_chunks forms the chunk
 //     sums through a table-driven fp64 exp (exp_rel) and ends with one
@@ -420,6 +420,21 @@ __device__ __forceinline__ void put_chunk(const VerifyParams& P, int b, int c, c
     u32x4 a[4];
     pack(v, a);
     put_record<4>(part_rsrc(P), chunk_off(P, b, c), a, P.epoch);
+}
+
+// Lane 0 stores a chunk record whose fields hold the same value in every
+// lane; its tag is formed before the branch, so it stays scalar arithmetic.
+__device__ __forceinline__ void put_chunk_uniform(const VerifyParams& P, int b, int c, const ChunkSums& v)
+{
+    u32x4 a[4];
+    pack(v, a);
+    a[3].w = record_tag<4>(a, P.epoch);
+    if ((threadIdx.x & 63) == 0) {
+        const __amdgpu_buffer_rsrc_t r = part_rsrc(P);
+        const uint32_t off = chunk_off(P, b, c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) put_atom(r, off + 16u * i, a[i]);
+    }
 }
 
 // A chunk record already known to be this call's.
@@ -1332,9 +1347,32 @@ __device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const
 // over whole chunks with the chunk's vectors unrolled: D slots per row, slot
 // k % D refilled with the vector D ahead (clamped to the range's last), and
 // no exit inside a chunk, so the slots keep their registers.
+// The first kTabAhead vectors per row of chunks [ca, cb) of the calling
+// lane (a range's loads in flight before the table is in LDS).
+struct TabSlots {
+    uint4 q[kTabAhead], p[kTabAhead];
+};
+
+template <bool BONUS>
+__device__ __forceinline__ void tab_first_loads(const char* qrow, const char* prow, int ca, int cb, TabSlots& sl)
+{
+    constexpr int PER = kChunk / 8 / 64;
+    const int lane = threadIdx.x & 63;
+    const int nvec = (cb - ca) * PER;
+    if (nvec <= 0) return;  // no range: chunk_range_tab loads nothing either
+    const uint4* vq = reinterpret_cast<const uint4*>(qrow) + (int64_t)ca * (kChunk / 8) + lane;
+    const uint4* vp = reinterpret_cast<const uint4*>(prow) + (int64_t)ca * (kChunk / 8) + lane;
+#pragma unroll
+    for (int j = 0; j < kTabAhead; ++j) {
+        const int t = min(j, nvec - 1);
+        sl.q[j] = vq[64 * t];
+        sl.p[j] = BONUS ? sl.q[j] : vp[64 * t];
+    }
+}
+
 template <bool BONUS>
 __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
-                                int ca, int cb, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
+                                int ca, int cb, const ExpRow& eq, const ExpRow& ep, lds_cptr tab, TabSlots& sl)
 {
     constexpr int PER = kChunk / 8 / 64;  // vectors per lane per chunk
     constexpr int D = kTabAhead;
@@ -1344,13 +1382,8 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
     if (nvec <= 0) return;
     const uint4* vq = reinterpret_cast<const uint4*>(qrow) + (int64_t)ca * (kChunk / 8) + lane;
     const uint4* vp = reinterpret_cast<const uint4*>(prow) + (int64_t)ca * (kChunk / 8) + lane;
-    uint4 sq[D], sp[D];
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-        const int t = min(j, nvec - 1);
-        sq[j] = vq[64 * t];
-        sp[j] = BONUS ? sq[j] : vp[64 * t];
-    }
+    uint4 (&sq)[D] = sl.q;
+    uint4 (&sp)[D] = sl.p;
     const NearBand nb = near_band(s);
     TabSums A;
 #pragma unroll
@@ -1375,21 +1408,32 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
             __builtin_amdgcn_sched_barrier(0);
 #endif
         }
+        // the chunk's record: sums made wave-uniform, so its tag is
+        // computed by scalar instructions
         ChunkSums out{};
         if constexpr (BONUS) {
             out.sa = (double)s.mq;
-            out.sb = wave_sum(eq.R * A.acc[0]);
+            out.sb = lane_value(wave_sum(eq.R * A.acc[0]), 0);
         } else {
-            out.sa = wave_sum(eq.R * A.acc[0]);
-            out.sb = wave_sum(ep.R * A.acc[1]);
-            out.pa = wave_sum(eq.R * A.acc[2]);
-            out.pb = wave_sum(ep.R * A.acc[3]);
+            double t[4];
+            wave_sum4(eq.R * A.acc[0], ep.R * A.acc[1], eq.R * A.acc[2], ep.R * A.acc[3], t);
+            out.sa = t[0];
+            out.sb = t[1];
+            out.pa = t[2];
+            out.pb = t[3];
             out.dmin = INFINITY;
             out.dmax = -INFINITY;
-            if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+            if (__ballot(A.nd <= nb.hw)) {
+                near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+                // equal in every lane already: taken from lane 0 as scalars
+                out.na = lane_value(out.na, 0);
+                out.nb = lane_value(out.nb, 0);
+                out.dmin = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(out.dmin)));
+                out.dmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(out.dmax)));
+            }
             A.nd = INFINITY;
         }
-        if (lane == 0) put_chunk(P, b, c, out);
+        put_chunk_uniform(P, b, c, out);
 #pragma unroll
         for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
     }
@@ -2065,87 +2109,78 @@ k_chunks(const VerifyParams P)
 // ---------------------------------------------------------------------------
 // Chain sample step of bf16 logits in 16-byte aligned rows: the table path
 // ---------------------------------------------------------------------------
-// Whether sequence b's whole chunks are formed by k_chunk_tab: both rows it
-// samples from take the bf16-grid table.
+// Whether sequence b's chunks take the table: both rows it samples from do.
 __device__ __forceinline__ bool tab_rows(const SeqState& s, const ExpRow& eq, const ExpRow& ep)
 {
     return s.status == 0 && eq.tabbed && (s.mode != kModeResidual || ep.tabbed);
 }
 
-// Block g * B + b forms the sums of group g of sequence b's whole chunks
-// from the block's LDS copy of the table, one contiguous share per wave;
-// wave 0 of group 0 also forms the partial last chunk.  Nothing here calls a
-// function, so the streaming loop keeps its registers.
-__global__ __launch_bounds__(kBlock) void
-#if SV_CHUNK_WAVES
-__attribute__((amdgpu_waves_per_eu(SV_CHUNK_WAVES)))
-#endif
-k_chunk_tab(const VerifyParams P)
+// The sample step of chains of bf16 logits in 16-byte aligned rows, after
+// the row launch (which filled the table and ran the accept tests).
+// Blocks [0, B*groups): block g*B + b forms the sums of group g of
+// sequence b's whole chunks from the block's LDS copy of the
+// table, one contiguous share per wave, each wave's first loads in flight
+// while the table is copied; group 0's wave 0 first forms the partial last
+// chunk.  A sequence whose rows do not take the table (a row maximum beyond
+// kTabRefLimit in units of T) has its chunks, partial one included, formed
+// through exp_rel instead.  Blocks [B*groups, B*groups + B): the final step
+// of one sequence each (exp_rel for the rescan).  Blocks are dispatched in
+// index order: a final block waits (bounded) only on chunk blocks that have
+// started, and the finals of early sequences run while the last chunk
+// blocks stream.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_tab(const VerifyParams P)
 {
     __shared__ double s_etab[kExpTabN];
-    __shared__ __align__(16) double s_tab[kTabEntries];
-    // group-major: every sequence's group 0 is in the first blocks dispatched
+    // the table (chunk blocks) or the final step's records and band sums
+    __shared__ __align__(16) double s_buf[kTabEntries > kFinalPool ? kTabEntries : kFinalPool];
+    const int nblocks = P.B * P.groups;
+    if ((int)blockIdx.x >= nblocks) {
+        const int b = (int)blockIdx.x - nblocks;
+        const SeqState s = P.seqs[b];
+        fill_exp_table(s_etab);  // first read after sample_final's first barrier
+        sample_final<DT_BF16, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_buf),
+                                            s_buf + kFinalPoolDoubles, nullptr);
+        return;
+    }
+    // group-major: block g*B + b (groups of one sequence far apart in the
+    // grid stream faster than neighbouring ones)
     const int g = (int)blockIdx.x / P.B;
     const int b = (int)blockIdx.x - g * P.B;
-    const SeqState s = P.seqs[b];  // in flight with the table copies
+    const SeqState s = P.seqs[b];
     fill_exp_table(s_etab);
-    copy_value_table(P, s_tab);
-    __syncthreads();
-    const ExpRow eq = exp_row(P, s.mq, s_etab, s_tab), ep = exp_row(P, s.mp, s_etab, s_tab);
-    if (!tab_rows(s, eq, ep)) return;  // the final step forms them
+    const ExpRow eq = exp_row(P, s.mq, s_etab, s_buf), ep = exp_row(P, s.mp, s_etab, s_buf);
+    const int wave = (int)threadIdx.x >> 6;
+    const char* qrow = sample_qrow<DT_BF16>(P, b, s);
+    const char* prow = s.mode == kModeResidual ? sample_prow<DT_BF16>(P, b, s) : qrow;
+    if (!tab_rows(s, eq, ep)) {
+        if (s.status) return;  // the final step emits the failure
+        // through exp_rel: this group's chunks, the last group's up to nch
+        __syncthreads();
+        const int c0 = g * P.cpb, c1 = (g == P.groups - 1) ? P.nch : min(P.nch, c0 + P.cpb);
+        const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+        const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+        const ExpRow rq = exp_row(P, s.mq, s_etab, nullptr), rp = exp_row(P, s.mp, s_etab, nullptr);
+        wave_chunks<DT_BF16>(P, b, s, qrow, prow, ca, cb, rq, rp, s_etab);
+        return;
+    }
     const int whole = P.V / kChunk;
     const int c0 = g * P.cpb, c1 = min(whole, c0 + P.cpb);
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
-    const int wave = (int)threadIdx.x >> 6;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
-    const char* qrow = sample_qrow<DT_BF16>(P, b, s);
-    const char* prow = s.mode == kModeResidual ? sample_prow<DT_BF16>(P, b, s) : qrow;
-    // the partial chunk (if any) first, by wave 0 of group 0: its latency
-    // passes while the rest of the grid streams
-    const bool partial = P.nch > whole && g == 0 && wave == 0;
-    if (s.mode == kModeResidual) {
-        if (partial) partial_chunk_tab<false>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_tab);
-        chunk_range_tab<false>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_tab);
-    } else {
-        if (partial) partial_chunk_tab<true>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_tab);
-        chunk_range_tab<true>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_tab);
-    }
-}
-
-// The final step of sequence blockIdx.x after k_chunk_tab: first, for a
-// sequence whose rows do not take the table, its chunk sums (k_chunk_tab
-// skipped it), then sample_final; element-wise exponentials read the block's
-// LDS copy of the table.
-__global__ __launch_bounds__(kBlock) void k_final_tab(const VerifyParams P)
-{
-    __shared__ double s_etab[kExpTabN];
-    __shared__ __align__(16) double s_pool[kFinalPool];
-    __shared__ __align__(16) double s_tab[kTabEntries];
-    const int b = (int)blockIdx.x;
-    const SeqState s = P.seqs[b];
-    fill_exp_table(s_etab);
-    copy_value_table(P, s_tab);
+    const bool residual = s.mode == kModeResidual;
+    TabSlots sl;
+    if (residual) tab_first_loads<false>(qrow, prow, ca, cb, sl);
+    else tab_first_loads<true>(qrow, prow, ca, cb, sl);
+    copy_value_table(P, s_buf);
     __syncthreads();
-    const ExpRow eqt = exp_row(P, s.mq, s_etab, s_tab), ept = exp_row(P, s.mp, s_etab, s_tab);
-    if (s.status == 0 && !tab_rows(s, eqt, ept)) {
-        // rows without the table: every chunk here, through exp_rel
-        const int c_begin = 0;
-        const char* qrow = sample_qrow<DT_BF16>(P, b, s);
-        const char* prow = s.mode == kModeResidual ? sample_prow<DT_BF16>(P, b, s) : qrow;
-        const int n = P.nch - c_begin;
-        const int cpw = (n + kWaves - 1) / kWaves;
-        const int wave = (int)threadIdx.x >> 6;
-        const int ca = min(P.nch, c_begin + wave * cpw), cb = min(P.nch, ca + cpw);
-        // chunk by chunk, from the table where the row has it (as the
-        // streamed chunks were), else through exp_rel
-        for (int c = ca; c < cb; ++c) {
-            const ChunkSums out = wave_chunk_sums<DT_BF16, true>(P, s, qrow, prow, c, eqt, ept, s_etab, s_tab);
-            if ((threadIdx.x & 63) == 0) put_chunk(P, b, c, out);
-        }
+    const bool partial = P.nch > whole && g == 0 && wave == 0;
+    if (residual) {
+        if (partial) partial_chunk_tab<false>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_buf);
+        chunk_range_tab<false>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_buf, sl);
+    } else {
+        if (partial) partial_chunk_tab<true>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_buf);
+        chunk_range_tab<true>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_buf, sl);
     }
-    // sample_final reads every record, polling those this block just wrote
-    sample_final<DT_BF16, false, true>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
-                                 s_pool + kFinalPoolDoubles, s_tab);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -2298,7 +2333,7 @@ void set_groups(sv::VerifyParams& P)
 #define SV_CHUNKS_PER_BLOCK 4
 #endif
 #ifndef SV_TAB_CHUNKS_PER_BLOCK
-#define SV_TAB_CHUNKS_PER_BLOCK 8
+#define SV_TAB_CHUNKS_PER_BLOCK 21
 #endif
 // The row kernel; with a timing hook, its begin and rows_done events are
 // stamped by the kernel's own start and end (not by records beside it, whose
@@ -2326,10 +2361,9 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         P.cpb = P.cpb < 1 ? 1 : P.cpb;
         P.groups = groups;
         launch_rows<DT, false>(P, (int64_t)P.B * (P.r_items + 1) + P.tab_blocks, timing, stream);
-        hipLaunchKernelGGL(sv::k_chunk_tab, dim3((unsigned)((int64_t)P.B * P.groups)), dim3(sv::kBlock), 0, stream,
-                           P);
-        hipExtLaunchKernelGGL(sv::k_final_tab, dim3((unsigned)P.B), dim3(sv::kBlock), 0, stream, nullptr, t_end, 0,
-                              P);
+        // chunk-sum blocks, then one final-step block per sequence
+        hipExtLaunchKernelGGL(sv::k_sample_tab, dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
+                              stream, nullptr, t_end, 0, P);
     } else {
         int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
         groups = groups < 1 ? 1 : groups;

@@ -314,12 +314,13 @@ __device__ __forceinline__ u32x4 get_atom(__amdgpu_buffer_rsrc_t r, uint32_t off
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCpolSc1);
 }
 
-// Word hash of the record tags (multiply-rotate rounds and a final avalanche).
+// Word hash of the record tags: per word an xor, an odd multiply and an
+// xor-shift (each a bijection of h, and each with a scalar instruction, so a
+// wave-uniform record is tagged by the scalar unit), then a final avalanche.
 __device__ __forceinline__ uint32_t hash_step(uint32_t h, uint32_t w)
 {
-    h ^= w * 0x9e3779b1u;
-    h = (h << 13) | (h >> 19);
-    return h * 0x85ebca77u + 0x27d4eb2fu;
+    h = (h ^ w) * 0x9e3779b1u;
+    return h ^ (h >> 15);
 }
 
 __device__ __forceinline__ uint32_t hash_final(uint32_t h)
@@ -495,6 +496,36 @@ __device__ __forceinline__ double wave_sum(double v)
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
     return v;
+}
+
+// A double that every lane holds the same value of, taken from lane `src`
+// as a wave-uniform (scalar) value.
+__device__ __forceinline__ double lane_value(double v, int src)
+{
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)__double_as_longlong(v), src);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(__double_as_longlong(v) >> 32), src);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// Sums over the wave of four doubles at once, returned wave-uniform.  The
+// first two exchanges halve the data each (lanes 32..63 keep the last two
+// sums, then lanes 16..31 and 48..63 the odd ones), so 7 additions do the
+// work of 24; the totals end in lanes 0, 16, 32 and 48.
+__device__ __forceinline__ void wave_sum4(double a0, double a1, double a2, double a3, double* out)
+{
+    const int lane = threadIdx.x & 63;
+    const bool h32 = (lane & 32) != 0, h16 = (lane & 16) != 0;
+    double k0 = h32 ? a2 : a0, k1 = h32 ? a3 : a1;
+    k0 += __shfl_xor(h32 ? a0 : a2, 32, 64);
+    k1 += __shfl_xor(h32 ? a1 : a3, 32, 64);
+    double k = h16 ? k1 : k0;
+    k += __shfl_xor(h16 ? k0 : k1, 16, 64);
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) k += __shfl_xor(k, off, 64);
+    out[0] = lane_value(k, 0);
+    out[1] = lane_value(k, 16);
+    out[2] = lane_value(k, 32);
+    out[3] = lane_value(k, 48);
 }
 
 __device__ __forceinline__ float wave_max(float v)
