@@ -309,6 +309,8 @@ __device__ __forceinline__ bool stat_bad(const RowStat& r) { return !(r.s > 0.0 
 // ===========================================================================
 // Parameters of one call
 // ===========================================================================
+constexpr int kMaxSections = 128;  // sections of the one-launch chain step's grid
+
 struct VerifyParams {
     const char* zq;
     const char* zp;
@@ -337,7 +339,19 @@ struct VerifyParams {
     char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
     double* etab_g;           // [kTabEntries] the exp(z/T) table (row kernel -> sample kernels)
+    char* tab_done;           // [tab_blocks] records: table block x has stored its entries
     uint32_t stats_bytes, part_bytes;
+    // one-launch chain step (k_chain_tab): sequences in groups of fuse_gs;
+    // section k holds the row blocks of group k, then the accept blocks of
+    // group k - fuse_la, the chunk blocks of group k - fuse_lc and the final
+    // blocks of group k - fuse_lf (those that exist); sched[k] is the first
+    // block of section k (after the table blocks), sched[nsec] the grid's end
+    int fuse_gs, fuse_ng, fuse_la, fuse_lc, fuse_lf, fuse_nsec;
+    int sched[kMaxSections + 1];
+    // chunks per chunk block and chunk blocks per sequence of each group
+    // (groups whose chunk blocks come after every row block take smaller
+    // ones: nothing else is left to overlap their latency with)
+    int16_t fuse_cpb[kMaxSections / 2], fuse_groups[kMaxSections / 2];
     // outputs
     int32_t* out_tokens;
     int32_t* out_path;
@@ -640,8 +654,45 @@ constexpr int kMaxChainN = 64;  // longest draft chain
 // Chain accept of sequence b, run by one wave (lane i = position i+1), the
 // only wave of its block that calls it: b's state into `out`; with
 // `outputs`, also the accept flags and probabilities.
+// The accept step's state of sequence b, stored by lane 0 of the calling
+// wave as a tagged four-atom record (a launch that runs both the accept test
+// and the sampling polls for it; later launches read it directly).
+__device__ __forceinline__ void put_seq_state(const VerifyParams& P, int b, const SeqState& s)
+{
+    if ((threadIdx.x & 63) != 0) return;
+    u32x4 a[4];
+    __builtin_memcpy(a, &s, sizeof(a));
+    put_record<4>(make_rsrc(P.seqs, (size_t)P.B * kSeqStateBytes), (uint32_t)b * kSeqStateBytes, a, P.epoch);
+}
+
+// Sequence b's state once its record has landed (bounded wait), as
+// wave-uniform values (lane 0's copy: every lane polled the same whole
+// record), so what depends on it stays scalar; a state that never arrives
+// reads as a data error of the sequence.
+__device__ __forceinline__ SeqState wait_seq_state(const VerifyParams& P, int b)
+{
+    u32x4 a[4];
+    const bool ok = wait_record<4>(make_rsrc(P.seqs, (size_t)P.B * kSeqStateBytes), (uint32_t)b * kSeqStateBytes, a,
+                                   P.epoch);
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[4 * i + 0] = __builtin_amdgcn_readfirstlane(a[i].x);
+        w[4 * i + 1] = __builtin_amdgcn_readfirstlane(a[i].y);
+        w[4 * i + 2] = __builtin_amdgcn_readfirstlane(a[i].z);
+        w[4 * i + 3] = __builtin_amdgcn_readfirstlane(a[i].w);
+    }
+    SeqState s;
+    __builtin_memcpy(&s, w, sizeof(w));
+    if (!__all(ok)) {
+        s = SeqState{};
+        s.status = 1;
+    }
+    return s;
+}
+
 template <int DT>
-__device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool outputs)
+__device__ void chain_accept(const VerifyParams& P, int b, RowStat* s_rows, bool outputs)
 {
     const int lane = threadIdx.x;
     const int N = P.N;
@@ -657,7 +708,6 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
         zqd = load_logit<DT>(qrow_ptr<DT>(P, b, lane), tok);
         zpd = load_logit<DT>(prow_ptr<DT>(P, b, lane), tok);
     }
-    __shared__ RowStat s_rows[2 * kMaxChainN + 1];
     for (int r0 = 0; r0 < P.rows; r0 += 64) {
         const int row = min(r0 + lane, P.rows - 1);
         RowStat st;
@@ -689,7 +739,7 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
     SeqState s{};
     if (errmask) {
         s.status = 1;
-        if (lane == 0) out = s;
+        put_seq_state(P, b, s);
         return;
     }
     const int k = rejmask ? (__ffsll((unsigned long long)rejmask) - 1) : N;
@@ -716,7 +766,7 @@ __device__ void chain_accept(const VerifyParams& P, int b, SeqState& out, bool o
             s.bonus_ref = 1;
         }
     }
-    if (lane == 0) out = s;
+    put_seq_state(P, b, s);
 }
 
 constexpr int kMaxNodes = 1024;
@@ -1898,18 +1948,79 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
 // Kernels
 // ===========================================================================
 // Entries x * kBlock + threadIdx.x of the bf16-grid table (see kTabKeys).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t etab_rsrc(const VerifyParams& P)
+{
+    return make_rsrc(P.etab_g, (uint32_t)(kTabEntries * sizeof(double)));
+}
+
+// Table block x stores entries [x*kBlock, (x+1)*kBlock) with agent-coherent
+// stores, waits until they have landed, and then stores its done record, so
+// a block of the same launch that has seen every done record reads the
+// whole table with coherent loads.
 __device__ __forceinline__ void fill_value_table(const VerifyParams& P, int x)
 {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     const int i = x * kBlock + (int)threadIdx.x;
-    if (i >= kTabEntries) return;
-    const int sgn = i >= kTabHalf ? 1 : 0;
-    const int t = i - sgn * kTabHalf;
-    double v = 0.0;
-    if (t < kTabKeys) {
-        const uint32_t key = (P.tab_lo + (uint32_t)t) | ((uint32_t)sgn << 15);
-        v = exp((double)__uint_as_float(key << 16) / (double)P.T);
+    if (i < kTabEntries) {
+        const int sgn = i >= kTabHalf ? 1 : 0;
+        const int t = i - sgn * kTabHalf;
+        double v = 0.0;
+        if (t < kTabKeys) {
+            const uint32_t key = (P.tab_lo + (uint32_t)t) | ((uint32_t)sgn << 15);
+            v = exp((double)__uint_as_float(key << 16) / (double)P.T);
+        }
+        const uint64_t w = (uint64_t)__double_as_longlong(v);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{(uint32_t)w, (uint32_t)(w >> 32)}, etab_rsrc(P),
+                                              i * (int)sizeof(double), 0, kCpolSc1);
     }
-    P.etab_g[i] = v;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        u32x4 a[1] = {u32x4{(uint32_t)x, 0x7ab1e000u, 0u, 0u}};
+        put_record<1>(make_rsrc(P.tab_done, (uint32_t)(P.tab_blocks * 16)), (uint32_t)x * 16u, a, P.epoch);
+    }
+}
+
+// Every table block's done record (wave 0 polls, the block waits at the
+// barrier); false if one never arrived.
+__device__ __forceinline__ bool wait_value_table(const VerifyParams& P)
+{
+    __shared__ int s_ok;
+    if (threadIdx.x < 64) {
+        int ok = 1;
+        for (int x = (int)threadIdx.x; x < P.tab_blocks; x += 64) {
+            u32x4 a[1];
+            ok &= wait_record<1>(make_rsrc(P.tab_done, (uint32_t)(P.tab_blocks * 16)), (uint32_t)x * 16u, a,
+                                 P.epoch)
+                      ? 1
+                      : 0;
+        }
+        ok = __all(ok);
+        if (threadIdx.x == 0) s_ok = ok;
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+// The block's LDS copy of the table through coherent loads (the table was
+// stored in this launch): every load issued before the first LDS store.
+__device__ __forceinline__ void copy_value_table_coherent(const VerifyParams& P, double* pool)
+{
+    constexpr int N2 = kTabEntries / 2;
+    constexpr int PER = (N2 + kBlock - 1) / kBlock;
+    const __amdgpu_buffer_rsrc_t r = etab_rsrc(P);
+    u32x4 v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * kBlock;
+        v[k] = get_atom(r, (uint32_t)(i < N2 ? i : N2 - 1) * 16u);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(pool);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+        const int i = (int)threadIdx.x + k * kBlock;
+        if (i < N2) dst[i] = v[k];
+    }
 }
 
 // The block's LDS copy of the table (publish it with a barrier): every load
@@ -1976,26 +2087,11 @@ constexpr int kRowBatch = SV_ROW_BATCH;
 // (an accept test reads them; the others get a placeholder record).  Many small blocks, dispatched as
 // compute units free up, balance the stream better than a resident grid
 // with fixed shares.
+// Row block (b, idx): idx = row * segs + segment; streams the segment and
+// stores its (m, s) record.
 template <int DT, bool TREE>
-__global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
+__device__ __forceinline__ void row_block(const VerifyParams& P, int b, int idx)
 {
-    const int nrow_blocks = P.B * P.r_items;
-    if ((int)blockIdx.x >= nrow_blocks) {
-        const int x = (int)blockIdx.x - nrow_blocks;
-        if (x < P.tab_blocks) {
-            fill_value_table(P, x);
-            return;
-        }
-        // chains: the accept test of sequence x - tab_blocks, by wave 0.
-        // Blocks are dispatched in index order, so every row block has
-        // started when this one does; it polls b's records as they land.
-        if (TREE || threadIdx.x >= 64) return;
-        const int b = x - P.tab_blocks;
-        chain_accept<DT>(P, b, P.seqs[b], true);
-        return;
-    }
-    const int b = (int)blockIdx.x / P.r_items;
-    const int idx = (int)blockIdx.x - b * P.r_items;
     const int row = idx / P.segs, seg = idx - row * P.segs;
     const char* base;
     bool work = true;
@@ -2020,6 +2116,29 @@ __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
         pack(st, a);
         put_record<1>(stats_rsrc(P), stat_off(P, (int64_t)b * P.rows + row, seg), a, P.epoch);
     }
+}
+
+template <int DT, bool TREE>
+__global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
+{
+    const int nrow_blocks = P.B * P.r_items;
+    if ((int)blockIdx.x >= nrow_blocks) {
+        const int x = (int)blockIdx.x - nrow_blocks;
+        if (x < P.tab_blocks) {
+            fill_value_table(P, x);
+            return;
+        }
+        // chains: the accept test of sequence x - tab_blocks, by wave 0.
+        // Blocks are dispatched in index order, so every row block has
+        // started when this one does; it polls b's records as they land.
+        if (TREE || threadIdx.x >= 64) return;
+        const int b = x - P.tab_blocks;
+        __shared__ RowStat s_rows[2 * kMaxChainN + 1];
+        chain_accept<DT>(P, b, s_rows, true);
+        return;
+    }
+    const int b = (int)blockIdx.x / P.r_items;
+    row_block<DT, TREE>(P, b, (int)blockIdx.x - b * P.r_items);
 }
 
 // Sample kernel: block (b, group) runs b's accept step itself (a few records
@@ -2115,38 +2234,19 @@ __device__ __forceinline__ bool tab_rows(const SeqState& s, const ExpRow& eq, co
     return s.status == 0 && eq.tabbed && (s.mode != kModeResidual || ep.tabbed);
 }
 
-// The sample step of chains of bf16 logits in 16-byte aligned rows, after
-// the row launch (which filled the table and ran the accept tests).
-// Blocks [0, B*groups): block g*B + b forms the sums of group g of
-// sequence b's whole chunks from the block's LDS copy of the
-// table, one contiguous share per wave, each wave's first loads in flight
-// while the table is copied; group 0's wave 0 first forms the partial last
-// chunk.  A sequence whose rows do not take the table (a row maximum beyond
-// kTabRefLimit in units of T) has its chunks, partial one included, formed
-// through exp_rel instead.  Blocks [B*groups, B*groups + B): the final step
-// of one sequence each (exp_rel for the rescan).  Blocks are dispatched in
-// index order: a final block waits (bounded) only on chunk blocks that have
-// started, and the finals of early sequences run while the last chunk
-// blocks stream.
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_tab(const VerifyParams P)
+// Chunk block (b, g) of chains of bf16 logits in 16-byte aligned rows: the
+// sums of group g of sequence b's whole chunks from the block's LDS copy of
+// the table, one contiguous share per wave, each wave's first loads in
+// flight while the table is copied; group 0's wave 0 first forms the partial
+// last chunk.  A sequence whose rows do not take the table (a row maximum
+// beyond kTabRefLimit in units of T) has its chunks, partial one included,
+// formed through exp_rel instead.  ONE: the accept state and the table come
+// from the same launch (polled; the table read through coherent loads).
+template <bool ONE>
+__device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, int g, int cpb, int groups,
+                                                double* s_etab, double* s_buf)
 {
-    __shared__ double s_etab[kExpTabN];
-    // the table (chunk blocks) or the final step's records and band sums
-    __shared__ __align__(16) double s_buf[kTabEntries > kFinalPool ? kTabEntries : kFinalPool];
-    const int nblocks = P.B * P.groups;
-    if ((int)blockIdx.x >= nblocks) {
-        const int b = (int)blockIdx.x - nblocks;
-        const SeqState s = P.seqs[b];
-        fill_exp_table(s_etab);  // first read after sample_final's first barrier
-        sample_final<DT_BF16, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_buf),
-                                            s_buf + kFinalPoolDoubles, nullptr);
-        return;
-    }
-    // group-major: block g*B + b (groups of one sequence far apart in the
-    // grid stream faster than neighbouring ones)
-    const int g = (int)blockIdx.x / P.B;
-    const int b = (int)blockIdx.x - g * P.B;
-    const SeqState s = P.seqs[b];
+    const SeqState s = ONE ? wait_seq_state(P, b) : P.seqs[b];
     fill_exp_table(s_etab);
     const ExpRow eq = exp_row(P, s.mq, s_etab, s_buf), ep = exp_row(P, s.mp, s_etab, s_buf);
     const int wave = (int)threadIdx.x >> 6;
@@ -2156,7 +2256,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         if (s.status) return;  // the final step emits the failure
         // through exp_rel: this group's chunks, the last group's up to nch
         __syncthreads();
-        const int c0 = g * P.cpb, c1 = (g == P.groups - 1) ? P.nch : min(P.nch, c0 + P.cpb);
+        const int c0 = g * cpb, c1 = (g == groups - 1) ? P.nch : min(P.nch, c0 + cpb);
         const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
         const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
         const ExpRow rq = exp_row(P, s.mq, s_etab, nullptr), rp = exp_row(P, s.mp, s_etab, nullptr);
@@ -2164,14 +2264,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         return;
     }
     const int whole = P.V / kChunk;
-    const int c0 = g * P.cpb, c1 = min(whole, c0 + P.cpb);
+    const int c0 = g * cpb, c1 = min(whole, c0 + cpb);
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
     const bool residual = s.mode == kModeResidual;
     TabSlots sl;
     if (residual) tab_first_loads<false>(qrow, prow, ca, cb, sl);
     else tab_first_loads<true>(qrow, prow, ca, cb, sl);
-    copy_value_table(P, s_buf);
+    if constexpr (ONE) {
+        if (!wait_value_table(P)) return;  // never expected: the final step times out and fails b
+        copy_value_table_coherent(P, s_buf);
+    } else {
+        copy_value_table(P, s_buf);
+    }
     __syncthreads();
     const bool partial = P.nch > whole && g == 0 && wave == 0;
     if (residual) {
@@ -2181,6 +2286,102 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         if (partial) partial_chunk_tab<true>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_buf);
         chunk_range_tab<true>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_buf, sl);
     }
+}
+
+// Final-step block of sequence b (exp_rel for the rescan; the chunk records
+// are polled).
+template <bool ONE>
+__device__ __forceinline__ void final_block_tab(const VerifyParams& P, int b, double* s_etab, double* s_buf)
+{
+    const SeqState s = ONE ? wait_seq_state(P, b) : P.seqs[b];
+    fill_exp_table(s_etab);  // first read after sample_final's first barrier
+    sample_final<DT_BF16, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_buf),
+                                        s_buf + kFinalPoolDoubles, nullptr);
+}
+
+// LDS of the table path's blocks: the table (chunk blocks), the final step's
+// records and band sums, or the accept test's row statistics.
+constexpr int kTabBuf = kTabEntries > kFinalPool ? kTabEntries : kFinalPool;
+static_assert((2 * kMaxChainN + 1) * sizeof(RowStat) <= kTabBuf * sizeof(double), "accept rows fit the buffer");
+
+// The sample step of chains of bf16 logits in 16-byte aligned rows, after
+// the row launch (which filled the table and ran the accept tests).  Blocks
+// [0, B*groups): chunk block (b, g) is block g*B + b (groups of one
+// sequence far apart in the grid stream faster than neighbouring ones).
+// Blocks [B*groups, B*groups + B): the final step of one sequence each.
+// Blocks are dispatched in index order: a final block waits (bounded) only
+// on chunk blocks that have started.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_sample_tab(const VerifyParams P)
+{
+    __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_buf[kTabBuf];
+    const int nblocks = P.B * P.groups;
+    if ((int)blockIdx.x >= nblocks) {
+        final_block_tab<false>(P, (int)blockIdx.x - nblocks, s_etab, s_buf);
+        return;
+    }
+    const int g = (int)blockIdx.x / P.B;
+    chunk_block_tab<false>(P, (int)blockIdx.x - g * P.B, g, P.cpb, P.groups, s_etab, s_buf);
+}
+
+// The whole chain step of bf16 logits in 16-byte aligned rows in one launch.
+// Blocks [0, tab_blocks) fill the table; the rest form sections (see
+// VerifyParams::sched): section k holds the row blocks of sequence group k,
+// then the accept blocks of group k - fuse_la, the chunk blocks of group
+// k - fuse_lc (group-major within the group) and the final blocks of group
+// k - fuse_lf.  Every block waits only on blocks before it (rows <- accept
+// <- chunks <- finals, table <- chunks), which the in-order dispatch has
+// started, and every wait is bounded.  Sample work of early groups thus runs
+// while later groups' rows still stream.
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_chain_tab(const VerifyParams P)
+{
+    __shared__ double s_etab[kExpTabN];
+    __shared__ __align__(16) double s_buf[kTabBuf];
+    int x = (int)blockIdx.x;
+    if (x < P.tab_blocks) {
+        fill_value_table(P, x);
+        return;
+    }
+    x -= P.tab_blocks;
+    int lo = 0, hi = P.fuse_nsec;  // the section: the last k with sched[k] <= x
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (P.sched[mid] <= x) lo = mid;
+        else hi = mid;
+    }
+    const int k = lo, gs = P.fuse_gs, ng = P.fuse_ng;
+    int off = x - P.sched[k];
+    if (k < ng) {
+        const int n = min(gs, P.B - k * gs) * P.r_items;
+        if (off < n) {
+            const int r = off / P.r_items;
+            row_block<DT_BF16, false>(P, k * gs + r, off - r * P.r_items);
+            return;
+        }
+        off -= n;
+    }
+    int j = k - P.fuse_la;
+    if (j >= 0 && j < ng) {
+        const int n = min(gs, P.B - j * gs);
+        if (off < n) {
+            if (threadIdx.x < 64) chain_accept<DT_BF16>(P, j * gs + off, reinterpret_cast<RowStat*>(s_buf), true);
+            return;
+        }
+        off -= n;
+    }
+    j = k - P.fuse_lc;
+    if (j >= 0 && j < ng) {
+        const int nj = min(gs, P.B - j * gs), n = nj * P.fuse_groups[j];
+        if (off < n) {
+            const int g = off / nj;
+            chunk_block_tab<true>(P, j * gs + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab, s_buf);
+            return;
+        }
+        off -= n;
+    }
+    j = k - P.fuse_lf;  // the rest of the section: final blocks
+    if (j < 0 || j >= ng || off >= min(gs, P.B - j * gs)) return;  // not reached: sched is exact
+    final_block_tab<true>(P, j * gs + off, s_etab, s_buf);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -2208,7 +2409,7 @@ int nchunks_of(int V) { return (V + sv::kChunk - 1) / sv::kChunk; }
 // Row segments of about SV_SEG_TARGET elements (a multiple of 64 elements,
 // so every segment keeps the row's 16-byte alignment): one row block each.
 #ifndef SV_SEG_TARGET
-#define SV_SEG_TARGET 32768
+#define SV_SEG_TARGET 65536
 #endif
 constexpr int kSegTarget = SV_SEG_TARGET;
 void segments_of(int V, int* segs, int* seg_len)
@@ -2241,7 +2442,7 @@ int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 }
 
 struct Layout {
-    size_t chunk_arr, seqs, stats, part, tab, total;
+    size_t chunk_arr, seqs, stats, part, tab, tab_done, total;
 };
 
 Layout make_layout(int B, int rows, int V)
@@ -2254,7 +2455,8 @@ Layout make_layout(int B, int rows, int V)
     L.stats = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
     L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
     L.tab = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
-    L.total = L.tab + align_up((size_t)sv::kTabEntries * sizeof(double));
+    L.tab_done = L.tab + align_up((size_t)sv::kTabEntries * sizeof(double));
+    L.total = L.tab_done + align_up((size_t)((sv::kTabEntries + sv::kBlock - 1) / sv::kBlock) * 16);
     return L;
 }
 
@@ -2333,7 +2535,28 @@ void set_groups(sv::VerifyParams& P)
 #define SV_CHUNKS_PER_BLOCK 4
 #endif
 #ifndef SV_TAB_CHUNKS_PER_BLOCK
-#define SV_TAB_CHUNKS_PER_BLOCK 21
+#define SV_TAB_CHUNKS_PER_BLOCK 8
+#endif
+// The table path in one launch (k_chain_tab) rather than a row launch and a
+// sample launch; sequences per section, and the lags (in sections) of a
+// group's accept, chunk and final blocks behind its row blocks.
+#ifndef SV_ONE_LAUNCH
+#define SV_ONE_LAUNCH 1
+#endif
+#ifndef SV_FUSE_GROUP
+#define SV_FUSE_GROUP 16
+#endif
+#ifndef SV_TAIL_CHUNKS_PER_BLOCK
+#define SV_TAIL_CHUNKS_PER_BLOCK 4
+#endif
+#ifndef SV_FUSE_LA
+#define SV_FUSE_LA 2
+#endif
+#ifndef SV_FUSE_LC
+#define SV_FUSE_LC 4
+#endif
+#ifndef SV_FUSE_LF
+#define SV_FUSE_LF 6
 #endif
 // The row kernel; with a timing hook, its begin and rows_done events are
 // stamped by the kernel's own start and end (not by records beside it, whose
@@ -2360,10 +2583,48 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         P.cpb = (whole + groups - 1) / groups;
         P.cpb = P.cpb < 1 ? 1 : P.cpb;
         P.groups = groups;
+#if SV_ONE_LAUNCH
+        // sections of sequence groups (at most 64 groups)
+        int gs = SV_FUSE_GROUP;
+        gs = gs < (P.B + 63) / 64 ? (P.B + 63) / 64 : gs;
+        gs = gs < 1 ? 1 : gs;
+        const int ng = (P.B + gs - 1) / gs;
+        P.fuse_gs = gs;
+        P.fuse_ng = ng;
+        P.fuse_la = SV_FUSE_LA < ng ? SV_FUSE_LA : ng;
+        P.fuse_lc = SV_FUSE_LC < ng ? SV_FUSE_LC : ng;
+        P.fuse_lf = SV_FUSE_LF < ng ? SV_FUSE_LF : ng;
+        P.fuse_lc = P.fuse_lc < P.fuse_la ? P.fuse_la : P.fuse_lc;
+        P.fuse_lf = P.fuse_lf < P.fuse_lc ? P.fuse_lc : P.fuse_lf;
+        P.fuse_nsec = ng + P.fuse_lf;
+        for (int j = 0; j < ng; ++j) {
+            const int want = j + P.fuse_lc >= ng ? SV_TAIL_CHUNKS_PER_BLOCK : SV_TAB_CHUNKS_PER_BLOCK;
+            int gj = (whole + want - 1) / want;
+            gj = gj < 1 ? 1 : gj;
+            int cj = (whole + gj - 1) / gj;
+            cj = cj < 1 ? 1 : cj;
+            P.fuse_cpb[j] = (int16_t)cj;
+            P.fuse_groups[j] = (int16_t)gj;
+        }
+        auto nseq = [&](int j) -> int64_t { return (j >= 0 && j < ng) ? (P.B - j * gs < gs ? P.B - j * gs : gs) : 0; };
+        auto nchunkb = [&](int j) -> int64_t { return (j >= 0 && j < ng) ? nseq(j) * P.fuse_groups[j] : 0; };
+        int64_t at = 0;
+        for (int k = 0; k < P.fuse_nsec; ++k) {
+            P.sched[k] = (int)at;
+            at += nseq(k) * P.r_items + nseq(k - P.fuse_la) + nchunkb(k - P.fuse_lc) + nseq(k - P.fuse_lf);
+        }
+        P.sched[P.fuse_nsec] = (int)at;
+        const hipEvent_t t0 = timing ? timing->begin : nullptr;
+        const hipEvent_t t1 = timing ? timing->rows_done : nullptr;
+        hipExtLaunchKernelGGL(sv::k_chain_tab, dim3((unsigned)(P.tab_blocks + at)), dim3(sv::kBlock), 0, stream, t0,
+                              t1, 0, P);
+        if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return SV_EHIP;
+#else
         launch_rows<DT, false>(P, (int64_t)P.B * (P.r_items + 1) + P.tab_blocks, timing, stream);
         // chunk-sum blocks, then one final-step block per sequence
         hipExtLaunchKernelGGL(sv::k_sample_tab, dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
                               stream, nullptr, t_end, 0, P);
+#endif
     } else {
         int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
         groups = groups < 1 ? 1 : groups;
@@ -2402,6 +2663,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     P.stats = ws + L.stats;
     P.part = ws + L.part;
     P.etab_g = reinterpret_cast<double*>(ws + L.tab);
+    P.tab_done = ws + L.tab_done;
     P.stats_bytes = (uint32_t)(L.part - L.stats);
     P.part_bytes = (uint32_t)(L.tab - L.part);
     // the table path: chains of bf16 logits whose rows are all 16-byte aligned

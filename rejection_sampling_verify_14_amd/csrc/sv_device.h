@@ -409,7 +409,9 @@ struct SeqState {
     int status;       // 0 ok, 1 data error
     int mode;         // 0 residual, 1 bonus
     int bonus_ref;    // bonus: mq is the pass-1 reference of the bonus row
+    uint32_t tag;     // record tag (the state is stored as a four-atom record)
 };
+static_assert(sizeof(SeqState) == 64, "SeqState is four 16-byte atoms");
 
 // Per-chunk sums of the sampled row(s).  Residual: sa = sum a, sb = sum b
 // (a = exp((zq - mq)/T), b = exp((zp - mp)/T)); pa, pb = the same over the
