@@ -696,11 +696,12 @@ def main():
     row_set = [row_kernel_bytes(w, s) for s in sets]
     row_bytes = sum(row_set) / len(row_set)
     if one_launch(w):
-        # the one launch also reads the row(s) each sequence samples from:
-        # both rows of the rejected position, or the bonus row
+        # the one launch reads the 2N draft-position rows of every sequence
+        # once, then the row(s) each sequence samples from: both rows of the
+        # rejected position, or the bonus row (read only when sampled)
         k = nacc.long()
         nrows = torch.where(k < 0, 0, torch.where(k < w.N, 2, 1)).sum(dim=1).double()
-        row_bytes += float(nrows.mean()) * w.V * w.elem_bytes
+        row_bytes = w.B * 2 * w.N * w.V * w.elem_bytes + float(nrows.mean()) * w.V * w.elem_bytes
     rounds_per_s = 1000.0 / ms_step
     eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
     k_gbps = row_bytes / (k_mean * 1e-3) / 1e9

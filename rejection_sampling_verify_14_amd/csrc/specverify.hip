@@ -331,6 +331,7 @@ struct VerifyParams {
     uint32_t epoch;
     // exp(z/T) over the bf16 grid (bf16 logits; see kTabKeys)
     int use_tab;              // the table is filled and used
+    int lazy_bonus;           // the bonus row q_N is not in the row pass: read only by a bonus sample
     int tab_blocks;           // row-kernel blocks that fill it
     uint32_t tab_lo;          // first magnitude key of the table
     // workspace
@@ -710,8 +711,8 @@ __device__ void chain_accept(const VerifyParams& P, int b, RowStat* s_rows, bool
     }
     for (int r0 = 0; r0 < P.rows; r0 += 64) {
         const int row = min(r0 + lane, P.rows - 1);
-        RowStat st;
-        load_row_stats<1>(P, b, &row, &st);
+        RowStat st{0.0, -INFINITY};
+        if (!(P.lazy_bonus && row == N)) load_row_stats<1>(P, b, &row, &st);
         if (r0 + lane < P.rows) s_rows[row] = st;
     }
     // one wave runs this: its LDS stores are published to its own lanes
@@ -759,7 +760,12 @@ __device__ void chain_accept(const VerifyParams& P, int b, RowStat* s_rows, bool
         fill_residual_state(s, kq, kp, P.T);
     } else {
         s.mode = kModeBonus;
-        if (stat_bad(qn)) {
+        if (P.lazy_bonus) {
+            // the bonus row has no row statistics: its chunks are summed in
+            // units of exp(z/T) (reference 0) and the sampler checks it
+            s.mq = 0.0f;
+            s.bonus_ref = 0;
+        } else if (stat_bad(qn)) {
             s.status = 1;  // NaN, +inf or no mass in the bonus row
         } else {
             s.mq = qn.m;
@@ -1303,7 +1309,57 @@ __device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, con
 struct TabSums {
     double acc[4];  // sa sb pa pb in units of exp(z/T)
     float nd;       // smallest |d - mid| seen (see NearBand)
+    // bonus rows (summed with no row statistics): the logits outside the
+    // table, per lane against the largest of them, oref: oacc = sum of
+    // exp((z - oref)/T); obad: a NaN or +inf logit
+    float oref;
+    double oacc;
+    int obad;
 };
+
+__device__ __forceinline__ void tab_sums_clear(TabSums& A)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
+    A.nd = INFINITY;
+    A.oref = -INFINITY;
+    A.oacc = 0.0;
+    A.obad = 0;
+}
+
+// A bonus-row logit outside the table into the lane's running sum against
+// its own largest such logit (rescaled when a larger one comes).
+__device__ __forceinline__ void bonus_outside(float z, const ExpRow& e, TabSums& A)
+{
+    if (!(z == z) || z == INFINITY) {
+        A.obad = 1;
+    } else if (z > -INFINITY) {
+        if (z > A.oref) {
+            if (A.oref > -INFINITY) A.oacc *= exp_rel(((double)A.oref - (double)z) * e.invT, e.tab);
+            A.oref = z;
+        }
+        A.oacc += exp_rel(((double)z - (double)A.oref) * e.invT, e.tab);
+    }
+}
+
+// The chunk record of a bonus row from a wave's table sums: the reference is
+// the larger of 0 (the units of the table sums) and the largest logit
+// outside the table, sb the chunk's sum of exp((z - reference)/T); a chunk
+// without mass gets reference -inf.  Fields wave-uniform.
+__device__ __forceinline__ void bonus_record(const TabSums& A, const ExpRow& e, ChunkSums& out)
+{
+    const double sin = lane_value(wave_sum(A.acc[0]), 0);
+    double ref = 0.0, sb = sin;
+    if (__ballot(A.oref > -INFINITY)) {
+        const float mo = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(wave_max(A.oref))));
+        ref = fmax(0.0, (double)mo);
+        const double own = A.oref > -INFINITY ? A.oacc * exp_rel(((double)A.oref - ref) * e.invT, e.tab) : 0.0;
+        sb = sin * exp_rel(-ref * e.invT, e.tab) + lane_value(wave_sum(own), 0);
+    }
+    out.sa = sb > 0.0 ? ref : -INFINITY;
+    out.sb = sb;
+    out.flags = __ballot(A.obad) ? kFlagBad : 0u;
+}
 
 // One 16-byte vector per row (8 token pairs, or 8 tokens of the q row alone
 // for BONUS) into the sums: 16 table reads issued together, then the terms;
@@ -1367,7 +1423,7 @@ __device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const
             const bool oq = tab_index(zq, lo) < 0;
             // exp((z - m)/T) / R = exp(z/T): into the table values' units
             if constexpr (BONUS) {
-                if (oq) A.acc[0] = fma(eq.slow(zq), eq.iR, A.acc[0]);
+                if (oq) bonus_outside(zq, eq, A);
             } else {
                 const uint32_t v = k == 0 ? wp[0] : k == 1 ? wp[1] : k == 2 ? wp[2] : wp[3];
                 const float zp = (i & 1) ? bf16_hi(v) : bf16_lo(v);
@@ -1436,9 +1492,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
     uint4 (&sp)[D] = sl.p;
     const NearBand nb = near_band(s);
     TabSums A;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
-    A.nd = INFINITY;
+    tab_sums_clear(A);
 #pragma unroll 1
     for (int c = ca; c < cb; ++c) {
         const int t0 = (c - ca) * PER;
@@ -1462,8 +1516,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
         // computed by scalar instructions
         ChunkSums out{};
         if constexpr (BONUS) {
-            out.sa = (double)s.mq;
-            out.sb = lane_value(wave_sum(eq.R * A.acc[0]), 0);
+            bonus_record(A, eq, out);
         } else {
             double t[4];
             wave_sum4(eq.R * A.acc[0], ep.R * A.acc[1], eq.R * A.acc[2], ep.R * A.acc[3], t);
@@ -1484,8 +1537,7 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
             A.nd = INFINITY;
         }
         put_chunk_uniform(P, b, c, out);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
+        tab_sums_clear(A);
     }
 }
 
@@ -1507,9 +1559,7 @@ __device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& 
     }
     const NearBand nb = near_band(s);
     TabSums A;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) A.acc[i] = 0.0;
-    A.nd = INFINITY;
+    tab_sums_clear(A);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
         tab_vector<BONUS>(vq[k], vp[k], s, nb, eq, ep, P.tab_lo, tab, A);
@@ -1518,8 +1568,7 @@ __device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& 
     }
     ChunkSums out{};
     if constexpr (BONUS) {
-        out.sa = (double)s.mq;
-        out.sb = wave_sum(eq.R * A.acc[0]);
+        bonus_record(A, eq, out);
     } else {
         out.sa = wave_sum(eq.R * A.acc[0]);
         out.sb = wave_sum(ep.R * A.acc[1]);
@@ -2092,7 +2141,9 @@ constexpr int kRowBatch = SV_ROW_BATCH;
 template <int DT, bool TREE>
 __device__ __forceinline__ void row_block(const VerifyParams& P, int b, int idx)
 {
-    const int row = idx / P.segs, seg = idx - row * P.segs;
+    int row = idx / P.segs;
+    const int seg = idx - row * P.segs;
+    if (!TREE && P.lazy_bonus && row >= P.N) ++row;  // rows 0..N-1 (q), then N+1..2N (p)
     const char* base;
     bool work = true;
     if constexpr (TREE) {
@@ -2546,6 +2597,9 @@ void set_groups(sv::VerifyParams& P)
 #ifndef SV_FUSE_GROUP
 #define SV_FUSE_GROUP 16
 #endif
+#ifndef SV_LAZY_BONUS
+#define SV_LAZY_BONUS 1
+#endif
 #ifndef SV_TAIL_CHUNKS_PER_BLOCK
 #define SV_TAIL_CHUNKS_PER_BLOCK 4
 #endif
@@ -2584,6 +2638,9 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         P.cpb = P.cpb < 1 ? 1 : P.cpb;
         P.groups = groups;
 #if SV_ONE_LAUNCH
+        // the bonus row is read only by the sequences that sample from it
+        P.lazy_bonus = SV_LAZY_BONUS;
+        if (P.lazy_bonus) P.r_items = (P.rows - 1) * P.segs;
         // sections of sequence groups (at most 64 groups)
         int gs = SV_FUSE_GROUP;
         gs = gs < (P.B + 63) / 64 ? (P.B + 63) / 64 : gs;
