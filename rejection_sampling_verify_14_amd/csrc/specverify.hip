@@ -1541,28 +1541,39 @@ __device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s,
     }
 }
 
-// The partial last chunk c (V not a multiple of kChunk) of 16-byte aligned
-// bf16 rows from the LDS table, by one wave: as one chunk of
-// chunk_range_tab, with the vectors past V read as -inf (chunk_vec_tail);
-// their keys lie outside the table and add exp_rel(-inf) = 0.
+// One chunk c of 16-byte aligned bf16 rows from the LDS table, by one wave,
+// with every vector of the chunk loaded at once (one memory round trip): the
+// partial last chunk, whose vectors past V read as -inf (their keys lie
+// outside the table and add exp_rel(-inf) = 0).  tab_chunk_load issues the
+// loads, tab_chunk_sums forms and stores the record.
+struct TabChunk {
+    uint4 q[kChunk / 8 / 64], p[kChunk / 8 / 64];
+};
+
 template <bool BONUS>
-__device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
-                                  const char* prow, int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
+__device__ __forceinline__ void tab_chunk_load(const VerifyParams& P, const char* qrow, const char* prow, int c,
+                                               TabChunk& ch)
 {
     constexpr int PER = kChunk / 8 / 64;
     const int lane = threadIdx.x & 63;
-    uint4 vq[PER], vp[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        vq[k] = chunk_vec_tail<DT_BF16>(qrow, P.V, c, k, lane);
-        vp[k] = BONUS ? vq[k] : chunk_vec_tail<DT_BF16>(prow, P.V, c, k, lane);
+        ch.q[k] = chunk_vec_tail<DT_BF16>(qrow, P.V, c, k, lane);
+        ch.p[k] = BONUS ? ch.q[k] : chunk_vec_tail<DT_BF16>(prow, P.V, c, k, lane);
     }
+}
+
+template <bool BONUS>
+__device__ void tab_chunk_sums(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+                               int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab, const TabChunk& ch)
+{
+    constexpr int PER = kChunk / 8 / 64;
     const NearBand nb = near_band(s);
     TabSums A;
     tab_sums_clear(A);
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-        tab_vector<BONUS>(vq[k], vp[k], s, nb, eq, ep, P.tab_lo, tab, A);
+        tab_vector<BONUS>(ch.q[k], ch.p[k], s, nb, eq, ep, P.tab_lo, tab, A);
         asm volatile("" : "+v"(A.acc[0]), "+v"(A.acc[1]), "+v"(A.acc[2]), "+v"(A.acc[3]), "+v"(A.nd));
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -1570,15 +1581,32 @@ __device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& 
     if constexpr (BONUS) {
         bonus_record(A, eq, out);
     } else {
-        out.sa = wave_sum(eq.R * A.acc[0]);
-        out.sb = wave_sum(ep.R * A.acc[1]);
-        out.pa = wave_sum(eq.R * A.acc[2]);
-        out.pb = wave_sum(ep.R * A.acc[3]);
+        double t[4];
+        wave_sum4(eq.R * A.acc[0], ep.R * A.acc[1], eq.R * A.acc[2], ep.R * A.acc[3], t);
+        out.sa = t[0];
+        out.sb = t[1];
+        out.pa = t[2];
+        out.pb = t[3];
         out.dmin = INFINITY;
         out.dmax = -INFINITY;
-        if (__ballot(A.nd <= nb.hw)) near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+        if (__ballot(A.nd <= nb.hw)) {
+            near_chunk<DT_BF16, true>(P, s, qrow, prow, c, eq, ep, out);
+            out.na = lane_value(out.na, 0);
+            out.nb = lane_value(out.nb, 0);
+            out.dmin = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(out.dmin)));
+            out.dmax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(out.dmax)));
+        }
     }
-    if (lane == 0) put_chunk(P, b, c, out);
+    put_chunk_uniform(P, b, c, out);
+}
+
+template <bool BONUS>
+__device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
+                                  const char* prow, int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
+{
+    TabChunk ch;
+    tab_chunk_load<BONUS>(P, qrow, prow, c, ch);
+    tab_chunk_sums<BONUS>(P, b, s, qrow, prow, c, eq, ep, tab, ch);
 }
 
 // Chunk sums of the row(s) a sequence samples from (see ChunkSums), by one

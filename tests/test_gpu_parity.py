@@ -137,6 +137,43 @@ def test_chain_table_path_logits_outside_table():
     _done("tab_outside", rep)
 
 
+def test_chain_bonus_row_read_only_when_sampled():
+    """bf16 chains whose bonus row q_{N+1} is read only by the bonus sample
+    (it has no row statistics): all-accepted sequences with a NaN, a +inf,
+    an all -inf bonus row (each -1), logits far outside the table (1000 and
+    900 at T = 1, beyond exp's range in units of exp(z/T)), large ones
+    (300), only tiny ones (below 2^-12 T), a single finite logit; and a
+    rejected sequence whose bonus row holds a NaN (it is never read: valid)."""
+    log("[case] bonus_lazy")
+    w = W["chain_b256_v128256"].with_sizes(V=8000)
+    B, N = 12, 3
+
+    def plant(inp):
+        zq, zp, d = inp["zq"], inp["zp"], inp["d"]
+        for b in range(B):
+            if b != 6:
+                zp[b] = zq[b, :N]          # p == q: every draft accepted
+        zq[0, N, 17] = float("nan")
+        zq[1, N, 4000] = float("inf")
+        zq[2, N, :] = float("-inf")
+        zq[3, N, 100] = 1000.0
+        zq[3, N, 7999] = 900.0
+        zq[4, N, 50:70] = 300.0
+        zq[5, N, :] = 1e-5 * torch.randn(w.V, device="cuda").to(zq.dtype)
+        zq[7, N, :] = float("-inf")
+        zq[7, N, 5555] = 2.5
+        zq[6, 0, int(d[6, 0])] = float("-inf")   # rejected at once ...
+        zq[6, N, 3] = float("nan")                # ... so its bonus row is never read
+        zq[8, N, ::2] = float("-inf")
+        zq[9, N, 2048:4096] = 40.0
+    rep, g, _ = run_chain(w, seed=23, rnd=4, B=B, N=N, modify=plant)
+    k = g["num_accepted"]
+    assert k[0] == -1 and k[1] == -1 and k[2] == -1
+    assert k[6] == 0 and all(int(k[b]) == N for b in (3, 4, 5, 7, 8, 9, 10, 11))
+    assert int(g["tokens"][7, N]) == 5555
+    _done("bonus_lazy", rep)
+
+
 def test_chain_n0_plain_sampling():
     """N = 0: the step samples q_1 directly (no drafts)."""
     log("[case] chain_n0")
