@@ -2325,8 +2325,24 @@ template <bool ONE>
 __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                 double* s_etab, double* s_buf)
 {
-    const SeqState s = ONE ? wait_seq_state(P, b) : P.seqs[b];
     fill_exp_table(s_etab);
+    SeqState s;
+    bool copied = false;
+    if constexpr (ONE) {
+        // if b's accept state is not there yet, the table is copied while
+        // waiting for it; if it is, the first row loads go out first
+        u32x4 a[4];
+        const bool mine =
+            try_record<4>(make_rsrc(P.seqs, (size_t)P.B * kSeqStateBytes), (uint32_t)b * kSeqStateBytes, a, P.epoch);
+        if (!__syncthreads_and(mine)) {
+            if (!wait_value_table(P)) return;  // never expected: the final step times out and fails b
+            copy_value_table_coherent(P, s_buf);
+            copied = true;
+        }
+        s = wait_seq_state(P, b);
+    } else {
+        s = P.seqs[b];
+    }
     const ExpRow eq = exp_row(P, s.mq, s_etab, s_buf), ep = exp_row(P, s.mp, s_etab, s_buf);
     const int wave = (int)threadIdx.x >> 6;
     const char* qrow = sample_qrow<DT_BF16>(P, b, s);
@@ -2351,8 +2367,10 @@ __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, in
     if (residual) tab_first_loads<false>(qrow, prow, ca, cb, sl);
     else tab_first_loads<true>(qrow, prow, ca, cb, sl);
     if constexpr (ONE) {
-        if (!wait_value_table(P)) return;  // never expected: the final step times out and fails b
-        copy_value_table_coherent(P, s_buf);
+        if (!copied) {
+            if (!wait_value_table(P)) return;  // never expected: the final step times out and fails b
+            copy_value_table_coherent(P, s_buf);
+        }
     } else {
         copy_value_table(P, s_buf);
     }
