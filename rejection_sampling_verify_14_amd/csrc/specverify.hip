@@ -342,13 +342,14 @@ struct VerifyParams {
     double* etab_g;           // [kTabEntries] the exp(z/T) table (row kernel -> sample kernels)
     char* tab_done;           // [tab_blocks] records: table block x has stored its entries
     uint32_t stats_bytes, part_bytes;
-    // one-launch chain step (k_chain_tab): sequences in groups of fuse_gs;
+    // one-launch chain step (k_chain_tab): sequences in groups (fuse_gstart);
     // section k holds the row blocks of group k, then the accept blocks of
     // group k - fuse_la, the chunk blocks of group k - fuse_lc and the final
     // blocks of group k - fuse_lf (those that exist); sched[k] is the first
     // block of section k (after the table blocks), sched[nsec] the grid's end
-    int fuse_gs, fuse_ng, fuse_la, fuse_lc, fuse_lf, fuse_nsec;
+    int fuse_ng, fuse_la, fuse_lc, fuse_lf, fuse_nsec;
     int sched[kMaxSections + 1];
+    int fuse_gstart[kMaxSections / 2 + 1];  // group j = sequences [gstart[j], gstart[j+1])
     // chunks per chunk block and chunk blocks per sequence of each group
     // (groups whose chunk blocks come after every row block take smaller
     // ones: nothing else is left to overlap their latency with)
@@ -2446,39 +2447,41 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         if (P.sched[mid] <= x) lo = mid;
         else hi = mid;
     }
-    const int k = lo, gs = P.fuse_gs, ng = P.fuse_ng;
+    const int k = lo, ng = P.fuse_ng;
     int off = x - P.sched[k];
     if (k < ng) {
-        const int n = min(gs, P.B - k * gs) * P.r_items;
+        const int n = (P.fuse_gstart[k + 1] - P.fuse_gstart[k]) * P.r_items;
         if (off < n) {
             const int r = off / P.r_items;
-            row_block<DT_BF16, false>(P, k * gs + r, off - r * P.r_items);
+            row_block<DT_BF16, false>(P, P.fuse_gstart[k] + r, off - r * P.r_items);
             return;
         }
         off -= n;
     }
     int j = k - P.fuse_la;
     if (j >= 0 && j < ng) {
-        const int n = min(gs, P.B - j * gs);
+        const int n = P.fuse_gstart[j + 1] - P.fuse_gstart[j];
         if (off < n) {
-            if (threadIdx.x < 64) chain_accept<DT_BF16>(P, j * gs + off, reinterpret_cast<RowStat*>(s_buf), true);
+            if (threadIdx.x < 64)
+                chain_accept<DT_BF16>(P, P.fuse_gstart[j] + off, reinterpret_cast<RowStat*>(s_buf), true);
             return;
         }
         off -= n;
     }
     j = k - P.fuse_lc;
     if (j >= 0 && j < ng) {
-        const int nj = min(gs, P.B - j * gs), n = nj * P.fuse_groups[j];
+        const int nj = P.fuse_gstart[j + 1] - P.fuse_gstart[j], n = nj * P.fuse_groups[j];
         if (off < n) {
             const int g = off / nj;
-            chunk_block_tab<true>(P, j * gs + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab, s_buf);
+            chunk_block_tab<true>(P, P.fuse_gstart[j] + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab,
+                                  s_buf);
             return;
         }
         off -= n;
     }
     j = k - P.fuse_lf;  // the rest of the section: final blocks
-    if (j < 0 || j >= ng || off >= min(gs, P.B - j * gs)) return;  // not reached: sched is exact
-    final_block_tab<true>(P, j * gs + off, s_etab, s_buf);
+    if (j < 0 || j >= ng || off >= P.fuse_gstart[j + 1] - P.fuse_gstart[j]) return;  // not reached: sched is exact
+    final_block_tab<true>(P, P.fuse_gstart[j] + off, s_etab, s_buf);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -2643,6 +2646,12 @@ void set_groups(sv::VerifyParams& P)
 #ifndef SV_FUSE_GROUP
 #define SV_FUSE_GROUP 16
 #endif
+#ifndef SV_FUSE_TAIL_GROUPS
+#define SV_FUSE_TAIL_GROUPS 0
+#endif
+#ifndef SV_FUSE_TAIL_GROUP
+#define SV_FUSE_TAIL_GROUP 4
+#endif
 #ifndef SV_LAZY_BONUS
 #define SV_LAZY_BONUS 1
 #endif
@@ -2687,12 +2696,20 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         // the bonus row is read only by the sequences that sample from it
         P.lazy_bonus = SV_LAZY_BONUS;
         if (P.lazy_bonus) P.r_items = (P.rows - 1) * P.segs;
-        // sections of sequence groups (at most 64 groups)
+        // sections of sequence groups (at most 64): groups of SV_FUSE_GROUP,
+        // then SV_FUSE_TAIL_GROUPS of SV_FUSE_TAIL_GROUP (smaller last groups
+        // leave less sample work for the end; measured slower at B=256, so
+        // none by default)
+        int tg = SV_FUSE_TAIL_GROUPS, tgs = SV_FUSE_TAIL_GROUP;
+        if ((int64_t)tg * tgs * 2 > P.B) tg = 0;
+        const int main_b = P.B - tg * tgs;
         int gs = SV_FUSE_GROUP;
-        gs = gs < (P.B + 63) / 64 ? (P.B + 63) / 64 : gs;
+        gs = gs < (main_b + 63 - tg) / (64 - tg) ? (main_b + 63 - tg) / (64 - tg) : gs;
         gs = gs < 1 ? 1 : gs;
-        const int ng = (P.B + gs - 1) / gs;
-        P.fuse_gs = gs;
+        int ng = 0;
+        for (int b0 = 0; b0 < main_b; b0 += gs) P.fuse_gstart[ng++] = b0;
+        for (int t = 0; t < tg; ++t) P.fuse_gstart[ng++] = main_b + t * tgs;
+        P.fuse_gstart[ng] = P.B;
         P.fuse_ng = ng;
         P.fuse_la = SV_FUSE_LA < ng ? SV_FUSE_LA : ng;
         P.fuse_lc = SV_FUSE_LC < ng ? SV_FUSE_LC : ng;
@@ -2709,7 +2726,7 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
             P.fuse_cpb[j] = (int16_t)cj;
             P.fuse_groups[j] = (int16_t)gj;
         }
-        auto nseq = [&](int j) -> int64_t { return (j >= 0 && j < ng) ? (P.B - j * gs < gs ? P.B - j * gs : gs) : 0; };
+        auto nseq = [&](int j) -> int64_t { return (j >= 0 && j < ng) ? P.fuse_gstart[j + 1] - P.fuse_gstart[j] : 0; };
         auto nchunkb = [&](int j) -> int64_t { return (j >= 0 && j < ng) ? nseq(j) * P.fuse_groups[j] : 0; };
         int64_t at = 0;
         for (int k = 0; k < P.fuse_nsec; ++k) {
