@@ -41,6 +41,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E peak, 8 TB/s
 REPEATS = 5             # timed blocks of K steps; the median is reported
+RAMP_S = 0.5            # untimed seconds of steps after the warm-up steps
+PRE_STEPS = 10          # untimed steps queued before each timed block's begin event
 PROFILE_PMC = os.path.join(ROOT, "profiles", "{kernel}_{workload}_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verify_14_amd", "csrc", f)
                   for f in ("specverify.hip", "sv_device.h", "sv_exp_table.h")]
@@ -645,6 +647,16 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # then untimed steps until the GPU has run this work for RAMP_S seconds
+    # (a short warm-up leaves the clocks below their sustained level, and the
+    # first timed blocks would measure the ramp)
+    ramp_steps, t_ramp = 0, time.perf_counter()
+    while time.perf_counter() - t_ramp < RAMP_S:
+        for i in range(50):
+            step(args.warmup + ramp_steps + i)
+        torch.cuda.synchronize()
+        ramp_steps += 50
+    log(f"[bench] {ramp_steps} more untimed steps ({RAMP_S} s of clock ramp)")
     K = args.steps
     stream = torch.cuda.current_stream()
     hip.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
@@ -654,10 +666,15 @@ def main():
     # events.  The reported time is the median block.
     blocks_ms, walls = [], []
     acc_sum = acc_n = tok_sum = tok_n = 0.0
-    nxt = args.warmup
+    nxt = args.warmup + ramp_steps
     for rep in range(REPEATS):
         log(f"[bench] timing block {rep + 1}/{REPEATS} of {K} steps")
         torch.cuda.synchronize()
+        # a few untimed steps queued ahead of the block's begin event, so the
+        # block starts on a busy GPU rather than one just idled by the sync
+        for i in range(PRE_STEPS):
+            step(nxt + i)
+        nxt += PRE_STEPS
         hip.lib.hipEventRecord(ctypes.c_void_p(t_begin), ctypes.c_void_p(stream.cuda_stream))
         wall0 = time.perf_counter()
         for i in range(K):
@@ -667,13 +684,15 @@ def main():
         walls.append(time.perf_counter() - wall0)
         blocks_ms.append(hip.elapsed_ms(t_begin, t_end))
         nxt += K
-        # acceptance of the block's last step (outputs are overwritten every step)
-        a8 = outs["accept"].float()
+        # acceptance of the block's last step (outputs are overwritten every
+        # step), copied out as plain host arrays: no device work between
+        # the timed blocks
+        a8 = outs["accept"].cpu().numpy().astype("float64")
         if w.kind != "chain":
             a8 = a8[:, 1:]
         acc_sum += float(a8.sum())
-        acc_n += a8.numel()
-        k = outs["num_accepted"]
+        acc_n += a8.size
+        k = outs["num_accepted"].cpu().numpy()
         tok_sum += float((k[k >= 0] + 1).sum())
         tok_n += int((k >= 0).sum())
     ms_step = statistics.median(blocks_ms) / K
@@ -713,6 +732,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "ramp_steps_untimed": ramp_steps,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
