@@ -694,7 +694,7 @@ __device__ __forceinline__ SeqState wait_seq_state(const VerifyParams& P, int b)
 }
 
 template <int DT>
-__device__ void chain_accept(const VerifyParams& P, int b, RowStat* s_rows, bool outputs)
+__device__ __forceinline__ void chain_accept(const VerifyParams& P, int b, RowStat* s_rows, bool outputs)
 {
     const int lane = threadIdx.x;
     const int N = P.N;
@@ -1095,15 +1095,15 @@ __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
     constexpr int PER = kChunk / EPV / 64;
+    // vectors per row loaded together: the chunk's loads of a group are all
+    // in flight before the first is used (one memory round trip per group)
+    constexpr int G = PER < 4 ? PER : 4;
+    static_assert(PER % G == 0, "whole groups of vectors");
     const int lane = threadIdx.x & 63;
     const bool vec = row_vectors<DT>(qrow, P.V) && row_vectors<DT>(prow, P.V);
     double na = 0.0, nb = 0.0;
     float dmin = INFINITY, dmax = -INFINITY;
-#pragma unroll 1
-    for (int k = 0; k < PER; ++k) {
-        float xq[EPV], xp[EPV];
-        chunk_elems<DT>(qrow, vec, P.V, c, k, lane, xq);
-        chunk_elems<DT>(prow, vec, P.V, c, k, lane, xp);
+    auto add = [&](const float* xq, const float* xp) {
 #pragma unroll
         for (int i = 0; i < EPV; ++i) {
             const float d = xq[i] - xp[i];
@@ -1113,6 +1113,32 @@ __device__ __forceinline__ void near_chunk(const VerifyParams& P, const SeqState
                 dmin = fminf(dmin, d);
                 dmax = fmaxf(dmax, d);
             }
+        }
+    };
+    if (vec) {
+#pragma unroll 1
+        for (int k0 = 0; k0 < PER; k0 += G) {
+            uint4 vq[G], vp[G];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                vq[j] = chunk_vec_tail<DT>(qrow, P.V, c, k0 + j, lane);
+                vp[j] = chunk_vec_tail<DT>(prow, P.V, c, k0 + j, lane);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                float xq[EPV], xp[EPV];
+                decode16<DT>(vq[j], xq);
+                decode16<DT>(vp[j], xp);
+                add(xq, xp);
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int k = 0; k < PER; ++k) {
+            float xq[EPV], xp[EPV];
+            chunk_elems<DT>(qrow, false, P.V, c, k, lane, xq);
+            chunk_elems<DT>(prow, false, P.V, c, k, lane, xp);
+            add(xq, xp);
         }
     }
     out.na = wave_sum(na);
@@ -1238,7 +1264,7 @@ __device__ __forceinline__ double bonus_sum(const VerifyParams& P, const char* q
 // (clamped to the range's last), and no exit inside a chunk, so the slots
 // keep their registers and each vector waits only for its own loads.
 template <int DT, bool BONUS>
-__device__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+__device__ __forceinline__ void chunk_range(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
                             int ca, int cb, const ExpRow& eq, const ExpRow& ep)
 {
     constexpr int EPV = 16 / elem_bytes<DT>();
@@ -1430,12 +1456,15 @@ __device__ __forceinline__ void tab_vector(const uint4 vq, const uint4 vp, const
                 const float zp = (i & 1) ? bf16_hi(v) : bf16_lo(v);
                 const bool op = tab_index(zp, lo) < 0;
                 const double fa = (zq - zp > s.thr_hi) ? 1.0 : 0.0;
-                if (oq) {
+                // -inf adds exactly zero (the padding past V of a partial
+                // chunk is -inf): skipped; NaN still goes through exp_rel,
+                // whose NaN reaches the sums
+                if (oq && zq != -INFINITY) {
                     const double a = eq.slow(zq) * eq.iR;
                     A.acc[0] += a;
                     A.acc[2] = fma(fa, a, A.acc[2]);
                 }
-                if (op) {
+                if (op && zp != -INFINITY) {
                     const double bb = ep.slow(zp) * ep.iR;
                     A.acc[1] += bb;
                     A.acc[3] = fma(fa, bb, A.acc[3]);
@@ -1478,7 +1507,7 @@ __device__ __forceinline__ void tab_first_loads(const char* qrow, const char* pr
 }
 
 template <bool BONUS>
-__device__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+__device__ __forceinline__ void chunk_range_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
                                 int ca, int cb, const ExpRow& eq, const ExpRow& ep, lds_cptr tab, TabSlots& sl)
 {
     constexpr int PER = kChunk / 8 / 64;  // vectors per lane per chunk
@@ -1565,7 +1594,7 @@ __device__ __forceinline__ void tab_chunk_load(const VerifyParams& P, const char
 }
 
 template <bool BONUS>
-__device__ void tab_chunk_sums(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
+__device__ __forceinline__ void tab_chunk_sums(const VerifyParams& P, int b, const SeqState& s, const char* qrow, const char* prow,
                                int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab, const TabChunk& ch)
 {
     constexpr int PER = kChunk / 8 / 64;
@@ -1602,7 +1631,7 @@ __device__ void tab_chunk_sums(const VerifyParams& P, int b, const SeqState& s, 
 }
 
 template <bool BONUS>
-__device__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
+__device__ __forceinline__ void partial_chunk_tab(const VerifyParams& P, int b, const SeqState& s, const char* qrow,
                                   const char* prow, int c, const ExpRow& eq, const ExpRow& ep, lds_cptr tab)
 {
     TabChunk ch;
@@ -2314,10 +2343,25 @@ __device__ __forceinline__ bool tab_rows(const SeqState& s, const ExpRow& eq, co
     return s.status == 0 && eq.tabbed && (s.mode != kModeResidual || ep.tabbed);
 }
 
+// The wave of a sequence's chunk blocks that forms the partial last chunk:
+// the first wave without whole chunks in the sequence's last block (every
+// block layout used leaves one there), else wave 0 of the first block.  So
+// no wave carries both a whole chunk and the partial one.
+__device__ __forceinline__ bool partial_wave(int whole, int cpb, int groups, int g, int wave)
+{
+    const int l0 = (groups - 1) * cpb, l1 = min(whole, l0 + cpb);
+    int used = 0;
+    if (l1 > l0) {
+        const int lcpw = (l1 - l0 + kWaves - 1) / kWaves;
+        used = (l1 - l0 + lcpw - 1) / lcpw;
+    }
+    return used < kWaves ? (g == groups - 1 && wave == used) : (g == 0 && wave == 0);
+}
+
 // Chunk block (b, g) of chains of bf16 logits in 16-byte aligned rows: the
 // sums of group g of sequence b's whole chunks from the block's LDS copy of
 // the table, one contiguous share per wave, each wave's first loads in
-// flight while the table is copied; group 0's wave 0 first forms the partial
+// flight while the table is copied; one wave (partial_wave) forms the partial
 // last chunk.  A sequence whose rows do not take the table (a row maximum
 // beyond kTabRefLimit in units of T) has its chunks, partial one included,
 // formed through exp_rel instead.  ONE: the accept state and the table come
@@ -2364,6 +2408,7 @@ __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, in
     const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
     const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
     const bool residual = s.mode == kModeResidual;
+    const bool partial = P.nch > whole && partial_wave(whole, cpb, groups, g, wave);
     TabSlots sl;
     if (residual) tab_first_loads<false>(qrow, prow, ca, cb, sl);
     else tab_first_loads<true>(qrow, prow, ca, cb, sl);
@@ -2376,7 +2421,6 @@ __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, in
         copy_value_table(P, s_buf);
     }
     __syncthreads();
-    const bool partial = P.nch > whole && g == 0 && wave == 0;
     if (residual) {
         if (partial) partial_chunk_tab<false>(P, b, s, qrow, prow, whole, eq, ep, (lds_cptr)s_buf);
         chunk_range_tab<false>(P, b, s, qrow, prow, ca, cb, eq, ep, (lds_cptr)s_buf, sl);

@@ -89,6 +89,13 @@ TABLE_CASES = [
     ("tab_v6144_t07", dict(B=16, N=4, V=6144, T=0.7)),
     ("tab_v10008_t33", dict(B=16, N=7, V=10008, T=3.3)),
     ("tab_v8000_t013", dict(B=12, N=2, V=8000, T=0.13)),
+    # which wave forms the partial last chunk: a full last block of four
+    # one-chunk waves (wave 0 of the first block takes it), a last block of
+    # three (its idle fourth wave), and 80 sequences, whose first groups use
+    # blocks of eight chunks (two per wave; a full last block)
+    ("tab_v16904_last_full", dict(B=16, N=3, V=16904, T=1.0)),
+    ("tab_v18440_last_three", dict(B=16, N=3, V=18440, T=1.0)),
+    ("tab_v33768_b80", dict(B=80, N=2, V=33768, T=1.0)),
 ]
 
 
