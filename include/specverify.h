@@ -22,6 +22,13 @@
  *     NaN or +inf in a logit row the outcome reads, a row that is all -inf, a
  *     token outside [0, V), a parent outside [0, n), or a walk longer than
  *     max_depth.
+ *   - Blocks of one launch hand data to later blocks of the same launch
+ *     through records (a block waits only for blocks dispatched before it).
+ *     Every such wait is bounded (2^19 polls); one that runs out fails its
+ *     sequence with out_num_accepted[b] = -2 (token row all -1).  That is
+ *     never expected and is not a property of the data.  For tests of this
+ *     path the bound is read from the environment variable
+ *     SV_TEST_SPIN_LIMIT (polls, 0 ... 2^19) at each call when it is set.
  *   - Logit rows: element (b, r, t) of a logits array lives at
  *     base + (b*seq_stride + r*row_stride + t) elements.  The base must be
  *     aligned to the element size (SV_EALIGN otherwise); V and the strides
@@ -45,11 +52,14 @@
  *     low 32 bits.
  *   - Reentrant; calls on different streams may overlap as long as they use
  *     different workspaces and outputs.  The only process-wide state is that
- *     call counter (an atomic) and cached occupancy figures.
- *   - A chain verify call is three kernel launches (row statistics, accept,
- *     chunk sums with the final step in the same grid); a tree verify call
- *     is two (row statistics, accept and sampling).  Row statistics are
- *     summed per fixed segment of about 32K tokens and combined in segment
+ *     call counter (an atomic), cached occupancy figures and the scratch
+ *     array of spec_verify_chain_noalloc.
+ *   - A chain verify call of bf16 logits in 16-byte aligned rows is one
+ *     kernel launch (value table, row statistics, accept tests, chunk sums
+ *     and final step in one grid); other chains take two (row statistics
+ *     and accept tests; chunk sums and final step); a tree verify call takes
+ *     two (row statistics; accept, walk and sampling).  Row statistics are
+ *     summed per fixed segment of about 64K tokens and combined in segment
  *     order, so results do not depend on the device's compute-unit count.
   */
 #ifndef SPECVERIFY_H
@@ -95,7 +105,7 @@ typedef struct sv_timing {
     hipEvent_t end;
 } sv_timing;
 
-/* ABI version (incremented on any signature change). */
+/* ABI version (incremented on any change of a signature or of an output convention). */
 int sv_abi_version(void);
 
 /* Static text for a status code. */
@@ -127,7 +137,8 @@ size_t sv_tree_workspace_bytes(int B, int T, int V);
  * Outputs (out_tokens and out_num_accepted required, the rest optional):
  *   out_tokens        [B, N+1] int32: d_1..d_k, the correction or bonus
  *                     token, then -1.
- *   out_num_accepted  [B] int32: k in [0, N], or -1 on a data error.
+ *   out_num_accepted  [B] int32: k in [0, N], -1 on a data error, -2 if a
+ *                     wait timed out (see the conventions).
  *   out_accept        [B, N] int8: the accept decision of every position
  *                     (positions after the first rejection are decided too).
  *   out_probs         [B, N, 2] float: (q_i(d_i), p_i(d_i)).
@@ -217,7 +228,8 @@ int spec_verify_chain_noalloc(const void* target_logits, int64_t tgt_seq_stride,
  *   out_tokens        [B, max_depth+1] int32: tokens of the accepted path,
  *                     then the correction/bonus token, then -1.
  *   out_path_nodes    [B, max_depth+1] int32: 0, the accepted nodes, -1.
- *   out_num_accepted  [B] int32: accepted depth k, or -1.
+ *   out_num_accepted  [B] int32: accepted depth k, -1 on a data error, -2 if
+ *                     a wait timed out.
  *   out_accept        [B, T+1] int8: the decision of every node (node 0: 1).
  *   out_probs         [B, T+1, 2] float: (q_par(tok_n), p_par(tok_n)), node 0
  *                     (0, 0).

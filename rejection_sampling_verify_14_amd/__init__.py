@@ -97,7 +97,7 @@ def _lib():
         L.sv_sample_draft.restype = i32
         L.sv_sample_draft.argtypes = [vp, i64, i64, i32, i32, i32, i32, ctypes.c_float, u64, u64, i32, vp, vp, vp]
         L.sv_philox_uniforms.argtypes = [u64, u64, i32, i32, vp, vp, vp]
-        if L.sv_abi_version() != 5:
+        if L.sv_abi_version() != 6:
             raise ImportError("libspecverify.so ABI version mismatch")
         _L = L
     return _L
@@ -152,9 +152,10 @@ def tree_workspace_bytes(B: int, T: int, V: int) -> int:
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     """A zero-filled workspace.  Zero-filled once: each call tags its records
-    and counters with the workspace's count of finished calls (its first
-    word) and stores the new count at its end, so one workspace serves any
-    number of later calls without being cleared again."""
+    and counters with its own number (the low word of the library's 64-bit
+    call counter, which starts at a value drawn when the library is loaded),
+    so a record an earlier call left reads as stale and one workspace serves
+    any number of later calls without being cleared again."""
     return torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 

@@ -11,35 +11,39 @@
 //        ("eagle_round" step 4, the walk from the root).
 //
 // Launches of one call, all on the caller's stream:
-//   * Row kernel k_rows: one block per (sequence b, row, segment) of every
-//     q/p logit row an accept test reads.  It streams the segment (16-byte
-//     nontemporal loads, U per thread per batch, the next batch in flight)
-//     and stores (m, s), s = sum exp((z - m)/T) from the hardware exp2 in
-//     fp32 (one fma per exponent argument against a wave-uniform reference)
-//     summed in double.  This is the HBM-bound part.  After the row blocks
-//     come, for bf16 chains, the blocks that fill a per-call table of
-//     exp(z/T) over the bf16 grid (kTabKeys), and for chains one accept block
-//     per sequence: one wave (lane i = position i+1) polls the sequence's
-//     row records, forms q(d)/p(d) in the log domain in double, ballots, and
-//     stores the sequence's state.  Blocks are dispatched in index order, so
-//     an accept block only waits on row blocks that have started.
-//   * Chains of bf16 logits in 16-byte aligned rows: k_sample_tab's first
-//     blocks form the chunk sums (2048-token chunks) of the row(s) each
-//     sequence samples from, every exponential one read of the block's LDS
-//     copy of the table; its last B blocks run each sequence's final step:
-//     combine the chunk sums, find the chunk holding u*W, rescan it with a
-//     block-wide prefix scan and write the token (inverse CDF in token
-//     order).
-//   * Other chains (fp32 logits, unaligned rows): k_chunks forms the chunk
-//     sums through a table-driven fp64 exp (exp_rel) and ends with one
-//     final-step block per sequence, which waits (bounded) for its records.
-//   * Trees: k_sample, whose blocks each run the sequence's tree accept
-//     (every node tested in parallel, a wave walks the parent array with
-//     ballots), form their group of chunk sums, and whose last block to
+//   * Chains of bf16 logits in 16-byte aligned rows: one launch, k_chain_tab.
+//     Its first blocks fill a per-call table of exp(z/T) over the bf16 grid
+//     (kTabKeys); the rest form sections of 16 sequences: section k holds the
+//     row blocks of sequence group k, then the accept blocks of group k - 2,
+//     the chunk blocks of group k - 4 and the final-step blocks of group
+//     k - 6, so the sampling of early groups runs while later groups' rows
+//     stream.  Row block: the statistics (m, s), s = sum exp((z - m)/T), of
+//     one ~64K-token segment of one of the 2N draft-position rows (16-byte
+//     nontemporal loads, the next batch in flight; the hardware exp2 in fp32
+//     with one fma per exponent argument against a wave-uniform reference,
+//     summed in double).  This is the HBM-bound part.  Accept block: one
+//     wave (lane i = position i+1) folds the sequence's row records, forms
+//     q(d)/p(d) in the log domain in double, ballots, and stores the
+//     sequence's state.  Chunk block: the sums of eight 2048-token chunks
+//     (four in the last groups) of the row(s) the sequence samples from, each
+//     exponential one read of the block's LDS copy of the table; the bonus
+//     row is read only by sequences that sample from it.  Final block:
+//     combines the chunk records, finds the chunk holding u*W, rescans it
+//     with a block-wide prefix scan and writes the token (inverse CDF in
+//     token order) and the KV rows.
+//   * Other chains (fp32 logits, unaligned rows): k_rows (row blocks of every
+//     row, then one accept block per sequence), then k_chunks (chunk sums
+//     through a table-driven fp64 exp, exp_rel, then one final-step block
+//     per sequence).
+//   * Trees: k_rows, then k_sample, whose blocks each run the sequence's tree
+//     accept (every node tested in parallel, a wave walks the parent array
+//     with ballots), form their group of chunk sums, and whose last block to
 //     finish for a sequence (an arrival counter) runs the final step.
 // Blocks of one launch exchange data through self-validating records
-// (sv_device.h): no cache-wide fences and no waits on blocks that have not
-// started; launch boundaries carry the rest.
+// (sv_device.h): no cache-wide fences.  A block only waits for blocks of
+// lower index in the same grid, which the in-order dispatch has started, and
+// every wait is bounded (a wait that runs out fails the sequence with -2);
+// launch boundaries carry the rest.
 //
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -305,6 +309,18 @@ __device__ __forceinline__ RowStat block_row_stats(const char* __restrict__ row,
 
 __device__ __forceinline__ bool stat_bad(const RowStat& r) { return !(r.s > 0.0 && r.s < INFINITY); }
 
+// The sum a row's statistics carry when one of its records never arrived (a
+// bounded wait ran out): negative, so no row of data can have it, and bad.
+constexpr double kStatTimedOut = -1.0;
+__device__ __forceinline__ bool stat_timed_out(const RowStat& r) { return r.s == kStatTimedOut; }
+
+// SeqState::status values: 0 ok, 1 data error (emitted as num_accepted =
+// -1), 2 a bounded wait for another block's record ran out (emitted as -2:
+// not a property of the data; never expected, since every block waited on
+// has been dispatched before the waiter).
+constexpr int kStatusData = 1;
+constexpr int kStatusTimeout = 2;
+
 
 // ===========================================================================
 // Parameters of one call
@@ -329,6 +345,7 @@ struct VerifyParams {
     float T, c;               // temperature, log2(e)/T
     double cd, invT;
     uint32_t epoch;
+    int spin_limit;           // polls a wait for another block's record may take
     // exp(z/T) over the bf16 grid (bf16 logits; see kTabKeys)
     int use_tab;              // the table is filled and used
     int lazy_bonus;           // the bonus row q_N is not in the row pass: read only by a bonus sample
@@ -370,30 +387,19 @@ struct VerifyParams {
 // block that has already finished its part)
 constexpr int kSpinLimit = 1 << 19;
 
-// Poll a record until it is this call's and whole; false on timeout.
+// Poll a record until it is this call's and whole; false after `limit`
+// further polls (the call's spin_limit: kSpinLimit unless a test lowers it).
 template <int K>
-__device__ __forceinline__ bool wait_record(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4* a, uint32_t epoch)
+__device__ __forceinline__ bool wait_record(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4* a, uint32_t epoch,
+                                            int limit)
 {
     int spins = 0;
     while (!try_record<K>(r, off, a, epoch)) {
-        if (++spins > kSpinLimit) return false;
+        if (++spins > limit) return false;
         __builtin_amdgcn_s_sleep(2);
         asm volatile("" ::: "memory");  // the next try loads again
     }
     return true;
-}
-
-// Block-wide: wait for n consecutive K-atom records starting at byte `off`;
-// true if all arrived.
-template <int K>
-__device__ __forceinline__ bool wait_records(__amdgpu_buffer_rsrc_t r, uint32_t off, int n, uint32_t epoch)
-{
-    int ok = 1;
-    for (int i = threadIdx.x; i < n; i += kBlock) {
-        u32x4 a[K];
-        ok &= wait_record<K>(r, off + 16u * K * (uint32_t)i, a, epoch) ? 1 : 0;
-    }
-    return __syncthreads_and(ok) != 0;
 }
 
 // Arrival index of the caller among this call's arrivals at a counter (0 for
@@ -466,7 +472,7 @@ __device__ __forceinline__ ChunkSums get_chunk(const VerifyParams& P, int b, int
 // Statistics of pass-1 rows from the records of their segments, kStatBatch
 // segments per batch: every record of a batch is requested before any is
 // used, so a batch costs one memory round trip.  A record that is not this
-// call's (never expected) poisons the row's result (NaN sum).
+// call's (never expected) marks the row's result as timed out (kStatTimedOut).
 constexpr int kStatBatch = 8;
 
 // Requests the records of segments [i0, i0 + kStatBatch) of row `row` of b.
@@ -485,7 +491,7 @@ __device__ __forceinline__ void issue_row_stat(const VerifyParams& P, int b, int
 // segment order), then the batch into acc.  A record that is not yet this
 // call's (its row block may still be running when the reader is a block of
 // the same launch) is polled until it is; one that never arrives poisons the
-// row's result (NaN sum).  Past the poll the fold is branch-free.
+// row's result (sum kStatTimedOut).  Past the poll the fold is branch-free.
 __device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int b, int row, int i0, u32x4* a,
                                               RowStat& acc, bool& ok)
 {
@@ -497,7 +503,7 @@ __device__ __forceinline__ void fold_row_stat(const VerifyParams& P, int b, int 
     for (int j = 0; j < kStatBatch; ++j) {
         const bool in = i0 + j < P.segs;
         if (in && a[j].w != record_tag<1>(&a[j], P.epoch) &&
-            !wait_record<1>(stats_rsrc(P), stat_off(P, grow, i0 + j), &a[j], P.epoch))
+            !wait_record<1>(stats_rsrc(P), stat_off(P, grow, i0 + j), &a[j], P.epoch, P.spin_limit))
             ok = false;
         const RowStat x = unpack_rowstat(&a[j]);
         xm[j] = in ? x.m : -INFINITY;
@@ -538,7 +544,7 @@ __device__ __forceinline__ void load_row_stats(const VerifyParams& P, int b, con
     }
 #pragma unroll
     for (int q = 0; q < R; ++q)
-        if (!ok[q]) out[q].s = NAN;
+        if (!ok[q]) out[q].s = kStatTimedOut;
 }
 
 template <int DT>
@@ -670,12 +676,12 @@ __device__ __forceinline__ void put_seq_state(const VerifyParams& P, int b, cons
 // Sequence b's state once its record has landed (bounded wait), as
 // wave-uniform values (lane 0's copy: every lane polled the same whole
 // record), so what depends on it stays scalar; a state that never arrives
-// reads as a data error of the sequence.
+// reads as a timeout of the sequence.
 __device__ __forceinline__ SeqState wait_seq_state(const VerifyParams& P, int b)
 {
     u32x4 a[4];
     const bool ok = wait_record<4>(make_rsrc(P.seqs, (size_t)P.B * kSeqStateBytes), (uint32_t)b * kSeqStateBytes, a,
-                                   P.epoch);
+                                   P.epoch, P.spin_limit);
     uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -688,7 +694,7 @@ __device__ __forceinline__ SeqState wait_seq_state(const VerifyParams& P, int b)
     __builtin_memcpy(&s, w, sizeof(w));
     if (!__all(ok)) {
         s = SeqState{};
-        s.status = 1;
+        s.status = kStatusTimeout;
     }
     return s;
 }
@@ -723,9 +729,11 @@ __device__ __forceinline__ void chain_accept(const VerifyParams& P, int b, RowSt
     // the bonus row's statistics (used if all accept) and those of q_i, p_i
     const RowStat qn = s_rows[N];
     const RowStat rq = s_rows[active ? lane : N], rp = s_rows[active ? N + 1 + lane : N];
+    int tmo = 0;
     if (active) {
         if (!tok_ok || stat_bad(rq) || stat_bad(rp)) {
             err = 1;
+            tmo = stat_timed_out(rq) || stat_timed_out(rp);
         } else {
             const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(lane + 1));
             const AcceptOut o = accept_logits(zqd, zpd, rq, rp, P.invT, u);
@@ -740,7 +748,7 @@ __device__ __forceinline__ void chain_accept(const VerifyParams& P, int b, RowSt
     const uint64_t rejmask = __ballot(active && !acc);
     SeqState s{};
     if (errmask) {
-        s.status = 1;
+        s.status = __ballot(tmo) ? kStatusTimeout : kStatusData;
         put_seq_state(P, b, s);
         return;
     }
@@ -767,7 +775,8 @@ __device__ __forceinline__ void chain_accept(const VerifyParams& P, int b, RowSt
             s.mq = 0.0f;
             s.bonus_ref = 0;
         } else if (stat_bad(qn)) {
-            s.status = 1;  // NaN, +inf or no mass in the bonus row
+            // NaN, +inf or no mass in the bonus row (or its records timed out)
+            s.status = stat_timed_out(qn) ? kStatusTimeout : kStatusData;
         } else {
             s.mq = qn.m;
             s.bonus_ref = 1;
@@ -821,7 +830,7 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
             load_row_stats<2>(P, b, rows, st);
             const RowStat rq = st[0], rp = st[1];
             if (stat_bad(rq) || stat_bad(rp)) {
-                err = 1;
+                err |= (stat_timed_out(rq) || stat_timed_out(rp)) ? 2 : 1;
                 continue;
             }
             const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)n);
@@ -834,10 +843,11 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
             }
         }
     }
+    const int tmo = __syncthreads_or(err & 2);  // (a predicate: the timeout bit first)
     err = __syncthreads_or(err);
     SeqState s{};
     if (err) {
-        s.status = 1;
+        s.status = tmo ? kStatusTimeout : kStatusData;
         if (tid == 0) out = s;
         return;
     }
@@ -878,7 +888,7 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
         cur = next;
     }
     if (werr) {
-        s.status = 1;
+        s.status = kStatusData;
     } else {
         s.k = depth;
         s.node = cur;
@@ -889,6 +899,9 @@ __device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t
             RowStat st[2];
             load_row_stats<2>(P, b, rows, st);
             fill_residual_state(s, st[0], st[1], P.T);
+            // (read and checked by the node tests above; a record that
+            // vanished since would be a timeout)
+            if (stat_bad(st[0]) || stat_bad(st[1])) s.status = kStatusTimeout;
         } else {
             s.mode = kModeBonus;
         }
@@ -1758,7 +1771,7 @@ __device__ void emit(const VerifyParams& P, int b, int k, int token, double resi
         }
     }
     if (threadIdx.x == 0) {
-        P.out_num[b] = ok ? k : -1;
+        P.out_num[b] = ok ? k : (k == -2 ? -2 : -1);
         if (P.out_resid) P.out_resid[b] = ok ? resid : 0.0;
         // the KV cache keeps the pending token and the k accepted drafts; a
         // failed sequence keeps its length
@@ -1807,7 +1820,7 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
     // the chunk records are kept in s_cs (the first kFinalCache of them;
     // later ones are read again when needed)
     if (s.status) {
-        emit<TREE>(P, b, -1, -1, 0.0, path);
+        emit<TREE>(P, b, s.status == kStatusTimeout ? -2 : -1, -1, 0.0, path);
         return;
     }
     const int k = s.k;
@@ -1885,11 +1898,10 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
         }
     };
     if (wave == 0) {
-        int ok = 1, tmo = 0, bad = 0;
+        int ok = 1, bad = 0;
         double sums[3] = {0.0, 0.0, 0.0};  // sa, sb, chunks with near tokens
         float lm = -INFINITY;
         auto take = [&](int c, const ChunkSums& v) {
-            tmo |= (v.flags & kFlagTimeout) != 0;
             if (c < kFinalCache) s_cs[c] = v;
             if (mode == kModeResidual) {
                 sums[0] += v.sa;
@@ -1912,17 +1924,18 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
         for (int j = 0; j < kFinalLaneBatch; ++j)
             if (c0 + j < c1) {
                 if (a[j][3].w == record_tag<4>(a[j], P.epoch) ||
-                    wait_record<4>(r, chunk_off(P, b, c0 + j), a[j], P.epoch))
+                    wait_record<4>(r, chunk_off(P, b, c0 + j), a[j], P.epoch, P.spin_limit))
                     take(c0 + j, unpack_chunk(a[j]));
                 else
                     ok = 0;
             }
         for (int c = c0 + kFinalLaneBatch; c < c1; ++c) {
             u32x4 x[4];
-            if (wait_record<4>(r, chunk_off(P, b, c), x, P.epoch)) take(c, unpack_chunk(x));
+            if (wait_record<4>(r, chunk_off(P, b, c), x, P.epoch, P.spin_limit)) take(c, unpack_chunk(x));
             else ok = 0;
         }
-        int fail = !__all(ok) || __any(tmo);
+        // 2: a chunk record never arrived (timeout); 1: a data error
+        int fail = !__all(ok) ? 2 : 0;
         if (!fail) {
             if (mode == kModeResidual) {
 #pragma unroll
@@ -1932,7 +1945,7 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
                 near_any = sums[2] > 0.0;
             } else {
                 M = (double)wave_max(lm);
-                fail = __any(bad) || M == -INFINITY;
+                fail = (__any(bad) || M == -INFINITY) ? 1 : 0;
             }
         }
         if (!fail && !near_any) locate();
@@ -1946,7 +1959,7 @@ __device__ __forceinline__ void sample_final(const VerifyParams& P, int b, const
     }
     __syncthreads();
     if (s_plan.fail) {
-        emit<TREE>(P, b, -1, -1, 0.0, path);
+        emit<TREE>(P, b, s_plan.fail == 2 ? -2 : -1, -1, 0.0, path);
         return;
     }
     rho = s_plan.rho;
@@ -2098,7 +2111,7 @@ __device__ __forceinline__ bool wait_value_table(const VerifyParams& P)
         for (int x = (int)threadIdx.x; x < P.tab_blocks; x += 64) {
             u32x4 a[1];
             ok &= wait_record<1>(make_rsrc(P.tab_done, (uint32_t)(P.tab_blocks * 16)), (uint32_t)x * 16u, a,
-                                 P.epoch)
+                                 P.epoch, P.spin_limit)
                       ? 1
                       : 0;
         }
@@ -2659,6 +2672,20 @@ uint32_t next_epoch()
     return e;
 }
 
+// The bound of the kernels' waits for records of other blocks: kSpinLimit
+// polls, or the value of SV_TEST_SPIN_LIMIT in the environment (tests of the
+// timeout path set it to a few polls; every wait stays bounded either way).
+int spin_limit_for_call()
+{
+    const char* e = getenv("SV_TEST_SPIN_LIMIT");
+    if (e && *e) {
+        char* end = nullptr;
+        const long v = strtol(e, &end, 10);
+        if (end && *end == 0 && v >= 0 && v <= sv::kSpinLimit) return (int)v;
+    }
+    return sv::kSpinLimit;
+}
+
 // Sample blocks per sequence: enough for one round of the blocks the device
 // holds at once (a block's four waves share its chunks).
 template <int DT>
@@ -2836,6 +2863,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     P.use_tab = !TREE && dtype == SV_BF16 && aligned && value_table_range(P.T, &P.tab_lo) ? 1 : 0;
     P.tab_blocks = P.use_tab ? (sv::kTabEntries + sv::kBlock - 1) / sv::kBlock : 0;
     P.epoch = next_epoch();
+    P.spin_limit = spin_limit_for_call();
     if constexpr (!TREE)
         return dtype == SV_BF16 ? launch_chain<sv::DT_BF16>(P, timing, stream)
                                 : launch_chain<sv::DT_F32>(P, timing, stream);
@@ -2902,7 +2930,7 @@ int scratch_on_current_device(void** out)
 
 extern "C" {
 
-int sv_abi_version(void) { return 5; }
+int sv_abi_version(void) { return 6; }
 
 const char* sv_status_string(int status)
 {

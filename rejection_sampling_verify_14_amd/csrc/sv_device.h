@@ -485,7 +485,6 @@ __device__ __forceinline__ ChunkSums unpack_chunk(const u32x4* a)
 }
 
 constexpr uint32_t kFlagBad = 1u;
-constexpr uint32_t kFlagTimeout = 2u;
 constexpr int kModeResidual = 0;
 constexpr int kModeBonus = 1;
 constexpr int kMaxChunks = 1024;  // V <= kMaxChunks * kChunk

@@ -44,7 +44,7 @@ def test_header_symbols_exported(sv):
 
 def test_status_strings_and_sizes(sv):
     L = sv.library()
-    assert L.sv_abi_version() == 5
+    assert L.sv_abi_version() == 6
     for code in range(8):
         assert L.sv_status_string(code)
     assert sv.chain_workspace_bytes(256, 7, 128256) > 0

@@ -790,6 +790,62 @@ def test_tree_build_full_size_sampled():
     log("[done] tree_build full size")
 
 
+def test_wait_timeouts_report_minus_two(monkeypatch):
+    """The timeout path, forced from the host: with SV_TEST_SPIN_LIMIT=0 every
+    wait for another block's record polls once.  A chain sequence whose
+    records were not there at that poll reports num_accepted = -2 (a timeout,
+    not a data error: never -1 on clean data) with its token row all -1; every
+    other sequence is unchanged.  Tree verify reads records of an earlier
+    launch only, so its outputs do not change.  The next calls, with the
+    normal bound, are exact again on the same workspace."""
+    import rejection_sampling_verify_14_amd as sv
+    log("[case] wait_timeouts")
+    B, N = 64, 7
+    for name, ov in [("bf16", dict(V=20008)), ("f32", dict(V=9001, dtype="f32"))]:
+        w = W["chain_b256_v128256"].with_sizes(**ov)
+        inp = synth.chain_inputs(w, 31, "cuda", B=B, N=N)
+        ws = sv.alloc_workspace(sv.chain_workspace_bytes(B, N, w.V), "cuda")
+
+        def call():
+            out = sv.spec_verify_chain(inp["zq"], inp["zp"], inp["d"], seed=3, round=5, temperature=1.0,
+                                       workspace=ws)
+            torch.cuda.synchronize()
+            return {k: v.cpu() for k, v in out.items()}
+
+        ref = call()
+        assert bool((ref["num_accepted"] >= 0).all())
+        monkeypatch.setenv("SV_TEST_SPIN_LIMIT", "0")
+        got = call()
+        monkeypatch.delenv("SV_TEST_SPIN_LIMIT")
+        k = got["num_accepted"]
+        assert set(k.tolist()) <= {-2} | set(range(N + 1)), name
+        assert bool((k == -2).any()), f"{name}: the one-poll bound never ran out"
+        ok = k >= 0
+        assert torch.equal(k[ok], ref["num_accepted"][ok])
+        assert torch.equal(got["tokens"][ok], ref["tokens"][ok])
+        assert bool((got["tokens"][~ok] == -1).all())
+        again = call()
+        for key in ("num_accepted", "tokens", "accept", "probs", "residual_mass"):
+            assert torch.equal(again[key], ref[key]), (name, key)
+        log(f"[case] wait_timeouts {name}: {int((k == -2).sum())} of {B} timed out")
+    tw = W["tree_static_b32_v128256"].with_sizes(V=9001)
+    tin = synth.static_tree_inputs(tw, 7, "cuda", B=8)
+
+    def tcall():
+        out = sv.spec_verify_tree(tin["zq"], tin["zp"], tin["tokens"], tin["parents"], seed=7, round=2,
+                                  temperature=1.0, max_depth=tw.depth)
+        torch.cuda.synchronize()
+        return {k: v.cpu() for k, v in out.items()}
+
+    tref = tcall()
+    monkeypatch.setenv("SV_TEST_SPIN_LIMIT", "0")
+    tgot = tcall()
+    monkeypatch.delenv("SV_TEST_SPIN_LIMIT")
+    for key in ("num_accepted", "tokens", "path_nodes"):
+        assert torch.equal(tgot[key], tref[key]), key
+    log("[done] wait_timeouts")
+
+
 def test_workspace_reused_across_calls_and_shapes():
     """One workspace serves a run of chain and tree calls of different sizes
     (records and counters carry each call's number): every call matches the
