@@ -702,9 +702,11 @@ def main():
     log(f"[bench] timing the kernels of {K} more steps")
     ev = [(hip.event(), hip.event(), hip.event()) for _ in range(K)]
     nacc = torch.empty((K, B), dtype=torch.int32, device=dev)
+    nres = torch.empty((K, B), dtype=torch.float64, device=dev)
     for i in range(K):
         step(nxt + i, timing=ev[i])
         nacc[i].copy_(outs["num_accepted"])
+        nres[i].copy_(outs["residual_mass"])
     torch.cuda.synchronize()
     rows_ms = [hip.elapsed_ms(a, m) for a, m, _ in ev]
     call_ms = [hip.elapsed_ms(a, b) for a, _, b in ev]
@@ -721,12 +723,23 @@ def main():
         k = nacc.long()
         nrows = torch.where(k < 0, 0, torch.where(k < w.N, 2, 1)).sum(dim=1).double()
         row_bytes = w.B * 2 * w.N * w.V * w.elem_bytes + float(nrows.mean()) * w.V * w.elem_bytes
+    step_bytes = full_bytes
+    if w.kind != "chain":
+        # a tree step reads q and p of every node with children once, and
+        # the q row of the leaf where a walk ends with a bonus (residual mass
+        # 0); the q rows of the other leaves are never read
+        nbonus = ((nres == 0.0) & (nacc >= 0)).sum(dim=1).double().cpu()
+        step_bytes = sum(row_set[(nxt + i) % pool] + float(nbonus[i]) * w.V * w.elem_bytes for i in range(K)) / K
     rounds_per_s = 1000.0 / ms_step
-    eff_gbps = full_bytes / (ms_step * 1e-3) / 1e9
+    eff_gbps = step_bytes / (ms_step * 1e-3) / 1e9
     k_gbps = row_bytes / (k_mean * 1e-3) / 1e9
     traffic, pmc = load_traffic(w)
     result = {
-        "metric": "verified rounds/s + achieved HBM GB/s (% peak), B=256 N=7 V=128256",
+        "metric": "verified rounds/s + achieved HBM GB/s (% peak), " + {
+            "chain_b256_v128256": "B=256 N=7 V=128256",
+            "chain_b64_v32000": "B=64 N=5 V=32000",
+            "tree_static_b32_v128256": "static 26-node trees B=32 V=128256",
+            "tree_dynamic_b128_v152064": "dynamic 61-node trees B=128 V=152064"}[w.name],
         "value": round(rounds_per_s, 2),
         "unit": "rounds/s",
         "n_gpus": 1,
@@ -752,6 +765,11 @@ def main():
         "effective_GBps": round(eff_gbps, 1),
         "effective_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(full_bytes),
+        "effective_bytes": ("algorithmic bytes: every logit row of the round once, B x (2N+1) x V x e" if w.kind == "chain"
+                            else "bytes a step reads: q and p of every node with children once, plus the q row of "
+                                 "the leaf of each walk that ends with a bonus (the algorithmic figure also counts "
+                                 "the q rows of leaves no walk samples from)"),
+        "bytes_read_per_step": int(step_bytes),
         "block_ms_per_step": [round(t / K, 5) for t in blocks_ms],
         "alpha_measured": round(acc_sum / max(acc_n, 1), 4),
         "tokens_per_round": round(tok_sum / max(tok_n, 1), 4),
