@@ -793,7 +793,7 @@ constexpr int kMaxNodes = 1024;
 // while it is accepted (walk 1, the pages' literal best-child walk).  The state goes to `out` and the path to
 // `path` (both LDS); with `outputs`, also the accept flags and probabilities.
 template <int DT>
-__device__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t* path, bool outputs)
+__device__ __forceinline__ void tree_accept(const VerifyParams& P, int b, SeqState& out, int32_t* path, bool outputs)
 {
     const int nn = P.nn;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1718,7 +1718,7 @@ __device__ __forceinline__ double residual_weight(float xq, float xp, const SeqS
 // (trees) the path up to depth k.  emit_sample then writes slot k, the count
 // and the residual mass; a failure rewrites everything through emit.
 template <bool TREE>
-__device__ void emit_accepted(const VerifyParams& P, int b, int k, const int32_t* path)
+__device__ __forceinline__ void emit_accepted(const VerifyParams& P, int b, int k, const int32_t* path)
 {
     const int width = P.width;
     for (int i = threadIdx.x; i < width; i += kBlock) {
@@ -1745,7 +1745,7 @@ __device__ void emit_accepted(const VerifyParams& P, int b, int k, const int32_t
 // Block-wide: the outputs of sequence b.  k < 0 or token < 0 marks the
 // sequence as failed (every slot -1).
 template <bool TREE>
-__device__ void emit(const VerifyParams& P, int b, int k, int token, double resid, const int32_t* path)
+__device__ __forceinline__ void emit(const VerifyParams& P, int b, int k, int token, double resid, const int32_t* path)
 {
     const int width = P.width;
     const bool ok = k >= 0 && token >= 0;
@@ -2263,41 +2263,6 @@ __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
     row_block<DT, TREE>(P, b, (int)blockIdx.x - b * P.r_items);
 }
 
-// Sample kernel: block (b, group) runs b's accept step itself (a few records
-// and logits; group 0 writes the accept outputs), forms the chunk sums of its
-// group of chunks of the row(s) b samples from, and the last of b's blocks to
-// finish (an arrival counter per sequence) runs b's final step.
-template <int DT>
-__global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
-{
-    const int b = (int)blockIdx.x / P.groups;
-    const int g = (int)blockIdx.x - b * P.groups;
-    __shared__ SeqState s_state;
-    __shared__ int32_t s_path[kMaxNodes];
-    __shared__ double s_etab[kExpTabN];
-    __shared__ __align__(16) double s_pool[kFinalPool];
-    fill_exp_table(s_etab);
-    tree_accept<DT>(P, b, s_state, s_path, g == 0);
-    __syncthreads();
-    const SeqState s = s_state;
-    const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
-    const char* qrow = sample_qrow<DT>(P, b, s);
-    const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
-    const ExpRow eq = exp_row(P, s.mq, s_etab, nullptr), ep = exp_row(P, s.mp, s_etab, nullptr);
-    // each wave takes a contiguous share of the block's chunks; whole chunks
-    // of aligned rows stream with loads in flight across chunk boundaries
-    const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
-    const int wave = (int)threadIdx.x >> 6;
-    const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
-    wave_chunks<DT>(P, b, s, qrow, prow, ca, cb, eq, ep, s_etab);
-    __syncthreads();
-    __shared__ int s_last;
-    if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
-    __syncthreads();
-    if (s_last)
-        sample_final<DT, true, false>(P, b, s, s_path, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
-                               s_pool + kFinalPoolDoubles, nullptr);
-}
 
 // ---------------------------------------------------------------------------
 // Chain sample step
@@ -2380,6 +2345,10 @@ __device__ __forceinline__ bool partial_wave(int whole, int cpb, int groups, int
 // formed through exp_rel instead.  ONE: the accept state and the table come
 // from the same launch (polled; the table read through coherent loads).
 template <bool ONE>
+__device__ __forceinline__ void tab_block_chunks(const VerifyParams& P, int b, int g, int cpb, int groups,
+                                                 const SeqState& s, bool copied, double* s_etab, double* s_buf);
+
+template <bool ONE>
 __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                 double* s_etab, double* s_buf)
 {
@@ -2401,6 +2370,18 @@ __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, in
     } else {
         s = P.seqs[b];
     }
+    tab_block_chunks<ONE>(P, b, g, cpb, groups, s, copied, s_etab, s_buf);
+}
+
+// The chunk work of block (b, g) given b's state (the table path; see
+// chunk_block_tab).  copied: the table is in s_buf already.  With !ONE the
+// table was filled by an earlier launch and is read with plain loads.
+// s_etab holds the exp_rel table (fill_exp_table, published by a barrier
+// here before any use).
+template <bool ONE>
+__device__ __forceinline__ void tab_block_chunks(const VerifyParams& P, int b, int g, int cpb, int groups,
+                                                 const SeqState& s, bool copied, double* s_etab, double* s_buf)
+{
     const ExpRow eq = exp_row(P, s.mq, s_etab, s_buf), ep = exp_row(P, s.mp, s_etab, s_buf);
     const int wave = (int)threadIdx.x >> 6;
     const char* qrow = sample_qrow<DT_BF16>(P, b, s);
@@ -2539,6 +2520,54 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     j = k - P.fuse_lf;  // the rest of the section: final blocks
     if (j < 0 || j >= ng || off >= P.fuse_gstart[j + 1] - P.fuse_gstart[j]) return;  // not reached: sched is exact
     final_block_tab<true>(P, P.fuse_gstart[j] + off, s_etab, s_buf);
+}
+
+// Sample kernel: block (b, group) runs b's accept step itself (a few records
+// and logits; group 0 writes the accept outputs), forms the chunk sums of its
+// group of chunks of the row(s) b samples from, and the last of b's blocks to
+// finish (an arrival counter per sequence) runs b's final step.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
+{
+    const int b = (int)blockIdx.x / P.groups;
+    const int g = (int)blockIdx.x - b * P.groups;
+    __shared__ SeqState s_state;
+    __shared__ int32_t s_path[kMaxNodes];
+    __shared__ double s_etab[kExpTabN];
+    // bf16: the table for the chunk sums, then the final step's records
+    __shared__ __align__(16) double s_pool[DT == DT_BF16 ? kTabBuf : kFinalPool];
+    fill_exp_table(s_etab);
+    tree_accept<DT>(P, b, s_state, s_path, g == 0);
+    __syncthreads();
+    const SeqState s = s_state;
+    bool tab = false;
+    if constexpr (DT == DT_BF16) {
+        if (P.use_tab) {
+            // bf16 rows with the call's table (filled by the row launch)
+            tab_block_chunks<false>(P, b, g, P.cpb, P.groups, s, false, s_etab, s_pool);
+            tab = true;
+        }
+    }
+    if (!tab) {
+        const int c0 = g * P.cpb, c1 = min(P.nch, c0 + P.cpb);
+        const char* qrow = sample_qrow<DT>(P, b, s);
+        const char* prow = s.mode == kModeResidual ? sample_prow<DT>(P, b, s) : qrow;
+        const ExpRow eq = exp_row(P, s.mq, s_etab, nullptr), ep = exp_row(P, s.mp, s_etab, nullptr);
+        // each wave takes a contiguous share of the block's chunks; whole
+        // chunks of aligned rows stream with loads in flight across chunk
+        // boundaries
+        const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+        const int wave = (int)threadIdx.x >> 6;
+        const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+        wave_chunks<DT>(P, b, s, qrow, prow, ca, cb, eq, ep, s_etab);
+    }
+    __syncthreads();
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = arrive(P.chunk_arrivals + b, P.epoch) == (uint32_t)(P.groups - 1);
+    __syncthreads();
+    if (s_last)
+        sample_final<DT, true, false>(P, b, s, s_path, s_etab, reinterpret_cast<ChunkSums*>(s_pool),
+                                      s_pool + kFinalPoolDoubles, nullptr);
 }
 
 __global__ void k_philox_uniforms(uint64_t seed, uint64_t round, int nseq, int npos, double* out_acc,
@@ -2834,7 +2863,23 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
 template <int DT>
 int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
-    set_groups<DT>(P);
+    if (P.use_tab) {
+        // table path: blocks of about SV_TAB_CHUNKS_PER_BLOCK whole chunks
+        // (each block copies the table and runs the tree accept), but no
+        // more than one round of the blocks the device holds at once
+        static std::atomic<int> cache{0};
+        const int resident = resident_blocks(&sv::k_sample<DT>, cache);
+        const int whole = P.V / sv::kChunk;
+        int groups = (whole + SV_TAB_CHUNKS_PER_BLOCK - 1) / SV_TAB_CHUNKS_PER_BLOCK;
+        const int round = resident > 0 && P.B > 0 ? resident / P.B : groups;
+        groups = groups > round ? round : groups;
+        groups = groups < 1 ? 1 : groups;
+        P.cpb = (whole + groups - 1) / groups;
+        P.cpb = P.cpb < 1 ? 1 : P.cpb;
+        P.groups = groups;
+    } else {
+        set_groups<DT>(P);
+    }
     const int64_t row_grid = (int64_t)P.B * P.r_items + P.tab_blocks;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     launch_rows<DT, true>(P, row_grid, timing, stream);
@@ -2860,7 +2905,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     // the table path: chains of bf16 logits whose rows are all 16-byte aligned
     const bool aligned = (((uintptr_t)P.zq | (uintptr_t)P.zp) & 15u) == 0 && P.qs % 8 == 0 && P.qr % 8 == 0 &&
                          P.ps % 8 == 0 && P.pr % 8 == 0;
-    P.use_tab = !TREE && dtype == SV_BF16 && aligned && value_table_range(P.T, &P.tab_lo) ? 1 : 0;
+    P.use_tab = dtype == SV_BF16 && aligned && value_table_range(P.T, &P.tab_lo) ? 1 : 0;
     P.tab_blocks = P.use_tab ? (sv::kTabEntries + sv::kBlock - 1) / sv::kBlock : 0;
     P.epoch = next_epoch();
     P.spin_limit = spin_limit_for_call();
