@@ -99,9 +99,10 @@ def kernel_hash() -> str:
 
 def one_launch(w) -> bool:
     """Whether the library runs this workload's step as the single chain
-    launch (k_chain_tab): chains of bf16 logits in 16-byte aligned rows, at a
-    temperature whose bf16-grid table fits (every benchmark temperature)."""
-    return w.kind == "chain" and w.dtype == "bf16"
+    launch (k_chain_tab): chains of fp32 logits, and of bf16 logits in
+    16-byte aligned rows at a temperature whose bf16-grid table fits (every
+    benchmark chain)."""
+    return w.kind == "chain"
 
 
 def dominant_kernel(w) -> str:

@@ -54,11 +54,12 @@
  *     different workspaces and outputs.  The only process-wide state is that
  *     call counter (an atomic), cached occupancy figures and the scratch
  *     array of spec_verify_chain_noalloc.
- *   - A chain verify call of bf16 logits in 16-byte aligned rows is one
- *     kernel launch (value table, row statistics, accept tests, chunk sums
- *     and final step in one grid); other chains take two (row statistics
- *     and accept tests; chunk sums and final step); a tree verify call takes
- *     two (row statistics; accept, walk and sampling).  Row statistics are
+ *   - A chain verify call is one kernel launch (for bf16 logits the value
+ *     table, then row statistics, accept tests, chunk sums and final step in
+ *     one grid); chains of bf16 logits whose rows are not 16-byte aligned
+ *     take two (row statistics and accept tests; chunk sums and final step);
+ *     a tree verify call takes two (row statistics and the table; accept,
+ *     walk and sampling).  Row statistics are
  *     summed per fixed segment of about 64K tokens and combined in segment
  *     order, so results do not depend on the device's compute-unit count.
   */

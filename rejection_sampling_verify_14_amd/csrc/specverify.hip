@@ -31,10 +31,13 @@
 //     combines the chunk records, finds the chunk holding u*W, rescans it
 //     with a block-wide prefix scan and writes the token (inverse CDF in
 //     token order) and the KV rows.
-//   * Other chains (fp32 logits, unaligned rows): k_rows (row blocks of every
-//     row, then one accept block per sequence), then k_chunks (chunk sums
-//     through a table-driven fp64 exp, exp_rel, then one final-step block
-//     per sequence).
+//   * Chains of fp32 logits: the same one launch, k_chain_tab<DT_F32>,
+//     without the table: its chunk blocks form the sums through a
+//     table-driven fp64 exp (exp_rel).
+//   * Chains of bf16 logits in rows that are not 16-byte aligned: k_rows (row
+//     blocks of every row, then one accept block per sequence), then
+//     k_chunks (chunk sums through exp_rel, then one final-step block per
+//     sequence).
 //   * Trees: k_rows, then k_sample, whose blocks each run the sequence's tree
 //     accept (every node tested in parallel, a wave walks the parent array
 //     with ballots), form their group of chunk sums, and whose last block to
@@ -2348,11 +2351,27 @@ template <bool ONE>
 __device__ __forceinline__ void tab_block_chunks(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                  const SeqState& s, bool copied, double* s_etab, double* s_buf);
 
-template <bool ONE>
+template <int DT, bool ONE>
 __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                 double* s_etab, double* s_buf)
 {
     fill_exp_table(s_etab);
+    if constexpr (DT != DT_BF16) {
+        // rows without the table (fp32 logits): b's state, then this
+        // group's chunks through exp_rel, the last group's up to nch
+        const SeqState st = ONE ? wait_seq_state(P, b) : P.seqs[b];
+        if (st.status) return;  // the final step emits the failure
+        __syncthreads();        // s_etab
+        const int wave = (int)threadIdx.x >> 6;
+        const int c0 = g * cpb, c1 = (g == groups - 1) ? P.nch : min(P.nch, c0 + cpb);
+        const int cpw = (c1 - c0 + kWaves - 1) / kWaves;
+        const int ca = min(c1, c0 + wave * cpw), cb = min(c1, ca + cpw);
+        const char* qrow = sample_qrow<DT>(P, b, st);
+        const char* prow = st.mode == kModeResidual ? sample_prow<DT>(P, b, st) : qrow;
+        const ExpRow rq = exp_row(P, st.mq, s_etab, nullptr), rp = exp_row(P, st.mp, s_etab, nullptr);
+        wave_chunks<DT>(P, b, st, qrow, prow, ca, cb, rq, rp, s_etab);
+        return;
+    }
     SeqState s;
     bool copied = false;
     if constexpr (ONE) {
@@ -2426,19 +2445,19 @@ __device__ __forceinline__ void tab_block_chunks(const VerifyParams& P, int b, i
 
 // Final-step block of sequence b (exp_rel for the rescan; the chunk records
 // are polled).
-template <bool ONE>
+template <int DT, bool ONE>
 __device__ __forceinline__ void final_block_tab(const VerifyParams& P, int b, double* s_etab, double* s_buf)
 {
     const SeqState s = ONE ? wait_seq_state(P, b) : P.seqs[b];
     fill_exp_table(s_etab);  // first read after sample_final's first barrier
-    sample_final<DT_BF16, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_buf),
-                                        s_buf + kFinalPoolDoubles, nullptr);
+    sample_final<DT, false, false>(P, b, s, nullptr, s_etab, reinterpret_cast<ChunkSums*>(s_buf),
+                                   s_buf + kFinalPoolDoubles, nullptr);
 }
 
 // LDS of the table path's blocks: the table (chunk blocks), the final step's
 // records and band sums, or the accept test's row statistics.
 constexpr int kTabBuf = kTabEntries > kFinalPool ? kTabEntries : kFinalPool;
-static_assert((2 * kMaxChainN + 1) * sizeof(RowStat) <= kTabBuf * sizeof(double), "accept rows fit the buffer");
+static_assert((2 * kMaxChainN + 1) * sizeof(RowStat) <= kFinalPool * sizeof(double), "accept rows fit the buffer");
 
 // The sample step of chains of bf16 logits in 16-byte aligned rows, after
 // the row launch (which filled the table and ran the accept tests).  Blocks
@@ -2453,11 +2472,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     __shared__ __align__(16) double s_buf[kTabBuf];
     const int nblocks = P.B * P.groups;
     if ((int)blockIdx.x >= nblocks) {
-        final_block_tab<false>(P, (int)blockIdx.x - nblocks, s_etab, s_buf);
+        final_block_tab<DT_BF16, false>(P, (int)blockIdx.x - nblocks, s_etab, s_buf);
         return;
     }
     const int g = (int)blockIdx.x / P.B;
-    chunk_block_tab<false>(P, (int)blockIdx.x - g * P.B, g, P.cpb, P.groups, s_etab, s_buf);
+    chunk_block_tab<DT_BF16, false>(P, (int)blockIdx.x - g * P.B, g, P.cpb, P.groups, s_etab, s_buf);
 }
 
 // The whole chain step of bf16 logits in 16-byte aligned rows in one launch.
@@ -2469,10 +2488,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
 // <- chunks <- finals, table <- chunks), which the in-order dispatch has
 // started, and every wait is bounded.  Sample work of early groups thus runs
 // while later groups' rows still stream.
+template <int DT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_chain_tab(const VerifyParams P)
 {
     __shared__ double s_etab[kExpTabN];
-    __shared__ __align__(16) double s_buf[kTabBuf];
+    // bf16: the table (chunk blocks) or the final step's records; fp32 rows
+    // have no table
+    __shared__ __align__(16) double s_buf[DT == DT_BF16 ? kTabBuf : kFinalPool];
     int x = (int)blockIdx.x;
     if (x < P.tab_blocks) {
         fill_value_table(P, x);
@@ -2491,7 +2513,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int n = (P.fuse_gstart[k + 1] - P.fuse_gstart[k]) * P.r_items;
         if (off < n) {
             const int r = off / P.r_items;
-            row_block<DT_BF16, false>(P, P.fuse_gstart[k] + r, off - r * P.r_items);
+            row_block<DT, false>(P, P.fuse_gstart[k] + r, off - r * P.r_items);
             return;
         }
         off -= n;
@@ -2501,7 +2523,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int n = P.fuse_gstart[j + 1] - P.fuse_gstart[j];
         if (off < n) {
             if (threadIdx.x < 64)
-                chain_accept<DT_BF16>(P, P.fuse_gstart[j] + off, reinterpret_cast<RowStat*>(s_buf), true);
+                chain_accept<DT>(P, P.fuse_gstart[j] + off, reinterpret_cast<RowStat*>(s_buf), true);
             return;
         }
         off -= n;
@@ -2511,7 +2533,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         const int nj = P.fuse_gstart[j + 1] - P.fuse_gstart[j], n = nj * P.fuse_groups[j];
         if (off < n) {
             const int g = off / nj;
-            chunk_block_tab<true>(P, P.fuse_gstart[j] + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab,
+            chunk_block_tab<DT, true>(P, P.fuse_gstart[j] + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab,
                                   s_buf);
             return;
         }
@@ -2519,7 +2541,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     }
     j = k - P.fuse_lf;  // the rest of the section: final blocks
     if (j < 0 || j >= ng || off >= P.fuse_gstart[j + 1] - P.fuse_gstart[j]) return;  // not reached: sched is exact
-    final_block_tab<true>(P, P.fuse_gstart[j] + off, s_etab, s_buf);
+    final_block_tab<DT, true>(P, P.fuse_gstart[j] + off, s_etab, s_buf);
 }
 
 // Sample kernel: block (b, group) runs b's accept step itself (a few records
@@ -2785,14 +2807,15 @@ template <int DT>
 int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
     const hipEvent_t t_end = timing ? timing->end : nullptr;
-    if (P.use_tab) {
-        const int whole = P.V / sv::kChunk;
-        int groups = (whole + SV_TAB_CHUNKS_PER_BLOCK - 1) / SV_TAB_CHUNKS_PER_BLOCK;
-        groups = groups < 1 ? 1 : groups;
-        P.cpb = (whole + groups - 1) / groups;
-        P.cpb = P.cpb < 1 ? 1 : P.cpb;
-        P.groups = groups;
 #if SV_ONE_LAUNCH
+    // one launch: bf16 rows with the table, and fp32 rows (whose chunk
+    // blocks go through exp_rel); bf16 rows that are not 16-byte aligned
+    // take the two launches below
+    const bool one = P.use_tab || DT == sv::DT_F32;
+#else
+    const bool one = false;
+#endif
+    if (one) {
         // the bonus row is read only by the sequences that sample from it
         P.lazy_bonus = SV_LAZY_BONUS;
         if (P.lazy_bonus) P.r_items = (P.rows - 1) * P.segs;
@@ -2817,11 +2840,15 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         P.fuse_lc = P.fuse_lc < P.fuse_la ? P.fuse_la : P.fuse_lc;
         P.fuse_lf = P.fuse_lf < P.fuse_lc ? P.fuse_lc : P.fuse_lf;
         P.fuse_nsec = ng + P.fuse_lf;
+        // chunk blocks per sequence: the table path splits the whole chunks
+        // (the partial one goes to an idle wave), exp_rel splits every chunk
+        const int span = P.use_tab ? P.V / sv::kChunk : P.nch;
         for (int j = 0; j < ng; ++j) {
-            const int want = j + P.fuse_lc >= ng ? SV_TAIL_CHUNKS_PER_BLOCK : SV_TAB_CHUNKS_PER_BLOCK;
-            int gj = (whole + want - 1) / want;
+            const int want = !P.use_tab ? SV_CHUNKS_PER_BLOCK
+                             : j + P.fuse_lc >= ng ? SV_TAIL_CHUNKS_PER_BLOCK : SV_TAB_CHUNKS_PER_BLOCK;
+            int gj = (span + want - 1) / want;
             gj = gj < 1 ? 1 : gj;
-            int cj = (whole + gj - 1) / gj;
+            int cj = (span + gj - 1) / gj;
             cj = cj < 1 ? 1 : cj;
             P.fuse_cpb[j] = (int16_t)cj;
             P.fuse_groups[j] = (int16_t)gj;
@@ -2836,15 +2863,20 @@ int launch_chain(sv::VerifyParams& P, const sv_timing* timing, hipStream_t strea
         P.sched[P.fuse_nsec] = (int)at;
         const hipEvent_t t0 = timing ? timing->begin : nullptr;
         const hipEvent_t t1 = timing ? timing->rows_done : nullptr;
-        hipExtLaunchKernelGGL(sv::k_chain_tab, dim3((unsigned)(P.tab_blocks + at)), dim3(sv::kBlock), 0, stream, t0,
-                              t1, 0, P);
+        hipExtLaunchKernelGGL((sv::k_chain_tab<DT>), dim3((unsigned)(P.tab_blocks + at)), dim3(sv::kBlock), 0,
+                              stream, t0, t1, 0, P);
         if (t_end && hipEventRecord(t_end, stream) != hipSuccess) return SV_EHIP;
-#else
+    } else if (P.use_tab) {
+        const int whole = P.V / sv::kChunk;
+        int groups = (whole + SV_TAB_CHUNKS_PER_BLOCK - 1) / SV_TAB_CHUNKS_PER_BLOCK;
+        groups = groups < 1 ? 1 : groups;
+        P.cpb = (whole + groups - 1) / groups;
+        P.cpb = P.cpb < 1 ? 1 : P.cpb;
+        P.groups = groups;
         launch_rows<DT, false>(P, (int64_t)P.B * (P.r_items + 1) + P.tab_blocks, timing, stream);
         // chunk-sum blocks, then one final-step block per sequence
         hipExtLaunchKernelGGL(sv::k_sample_tab, dim3((unsigned)((int64_t)P.B * (P.groups + 1))), dim3(sv::kBlock), 0,
                               stream, nullptr, t_end, 0, P);
-#endif
     } else {
         int groups = (P.nch + SV_CHUNKS_PER_BLOCK - 1) / SV_CHUNKS_PER_BLOCK;
         groups = groups < 1 ? 1 : groups;
