@@ -2339,18 +2339,20 @@ __device__ __forceinline__ bool partial_wave(int whole, int cpb, int groups, int
     return used < kWaves ? (g == groups - 1 && wave == used) : (g == 0 && wave == 0);
 }
 
-// Chunk block (b, g) of chains of bf16 logits in 16-byte aligned rows: the
-// sums of group g of sequence b's whole chunks from the block's LDS copy of
-// the table, one contiguous share per wave, each wave's first loads in
-// flight while the table is copied; one wave (partial_wave) forms the partial
-// last chunk.  A sequence whose rows do not take the table (a row maximum
-// beyond kTabRefLimit in units of T) has its chunks, partial one included,
-// formed through exp_rel instead.  ONE: the accept state and the table come
-// from the same launch (polled; the table read through coherent loads).
 template <bool ONE>
 __device__ __forceinline__ void tab_block_chunks(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                  const SeqState& s, bool copied, double* s_etab, double* s_buf);
 
+// Chunk block (b, g) of a chain: the sums of group g of the chunks of the
+// row(s) sequence b samples from.  bf16 logits in 16-byte aligned rows
+// (tab_block_chunks): each exponential one read of the block's LDS copy of
+// the table, one contiguous share of the whole chunks per wave, each wave's
+// first loads in flight while the table is copied; one wave (partial_wave)
+// forms the partial last chunk; a sequence whose rows do not take the table
+// (a row maximum beyond kTabRefLimit in units of T) has its chunks formed
+// through exp_rel instead.  fp32 logits: every chunk through exp_rel.  ONE:
+// the accept state and the table come from the same launch (polled; the
+// table read through coherent loads).
 template <int DT, bool ONE>
 __device__ __forceinline__ void chunk_block_tab(const VerifyParams& P, int b, int g, int cpb, int groups,
                                                 double* s_etab, double* s_buf)
@@ -2479,7 +2481,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     chunk_block_tab<DT_BF16, false>(P, (int)blockIdx.x - g * P.B, g, P.cpb, P.groups, s_etab, s_buf);
 }
 
-// The whole chain step of bf16 logits in 16-byte aligned rows in one launch.
+// The whole chain step in one launch: bf16 logits in 16-byte aligned rows
+// (with the table) and fp32 logits (chunk sums through exp_rel, no table).
 // Blocks [0, tab_blocks) fill the table; the rest form sections (see
 // VerifyParams::sched): section k holds the row blocks of sequence group k,
 // then the accept blocks of group k - fuse_la, the chunk blocks of group
@@ -2534,7 +2537,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
         if (off < n) {
             const int g = off / nj;
             chunk_block_tab<DT, true>(P, P.fuse_gstart[j] + off - g * nj, g, P.fuse_cpb[j], P.fuse_groups[j], s_etab,
-                                  s_buf);
+                                      s_buf);
             return;
         }
         off -= n;
