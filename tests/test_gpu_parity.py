@@ -795,9 +795,9 @@ def test_wait_timeouts_report_minus_two(monkeypatch):
     wait for another block's record polls once.  A chain sequence whose
     records were not there at that poll reports num_accepted = -2 (a timeout,
     not a data error: never -1 on clean data) with its token row all -1; every
-    other sequence is unchanged.  Tree verify reads records of an earlier
-    launch only, so its outputs do not change.  The next calls, with the
-    normal bound, are exact again on the same workspace."""
+    other sequence is unchanged.  Tree verify (one launch as well) obeys the
+    same rule.  The next calls, with the normal bound, are exact again on the
+    same workspace."""
     import rejection_sampling_verify_14_amd as sv
     log("[case] wait_timeouts")
     B, N = 64, 7
@@ -838,11 +838,20 @@ def test_wait_timeouts_report_minus_two(monkeypatch):
         return {k: v.cpu() for k, v in out.items()}
 
     tref = tcall()
+    assert bool((tref["num_accepted"] >= 0).all())
     monkeypatch.setenv("SV_TEST_SPIN_LIMIT", "0")
     tgot = tcall()
     monkeypatch.delenv("SV_TEST_SPIN_LIMIT")
+    tk = tgot["num_accepted"]
+    assert set(tk.tolist()) <= {-2} | set(range(tw.depth + 1))
+    tok_ = tk >= 0
     for key in ("num_accepted", "tokens", "path_nodes"):
-        assert torch.equal(tgot[key], tref[key]), key
+        assert torch.equal(tgot[key][tok_], tref[key][tok_]), key
+    assert bool((tgot["tokens"][~tok_] == -1).all())
+    tagain = tcall()
+    for key in ("num_accepted", "tokens", "path_nodes", "accept", "probs", "residual_mass"):
+        assert torch.equal(tagain[key], tref[key]), key
+    log(f"[case] wait_timeouts trees: {int((tk == -2).sum())} of {tk.numel()} timed out")
     log("[done] wait_timeouts")
 
 
