@@ -780,7 +780,7 @@ def main():
         "roofline": {
             "kernel": ("k_chain_tab (the whole step in one launch: every logit row once, then the row(s) each "
                        "sequence samples from)" if one_launch(w) else
-                       "k_rows (row statistics of every logit row the step reads; the dominant kernel)"),
+                       "k_rows (row statistics of every logit row the step reads, then the accept tests; the dominant kernel)"),
             "bound": "hbm",
             "achieved": round(k_gbps, 1),
             "peak": PEAK_HBM_GBPS,

@@ -58,8 +58,8 @@
  *     table, then row statistics, accept tests, chunk sums and final step in
  *     one grid); chains of bf16 logits whose rows are not 16-byte aligned
  *     take two (row statistics and accept tests; chunk sums and final step);
- *     a tree verify call takes two (row statistics and the table; accept,
- *     walk and sampling).  Row statistics are
+ *     a tree verify call takes two (row statistics, the table, accept tests
+ *     and walk; sampling).  Row statistics are
  *     summed per fixed segment of about 64K tokens and combined in segment
  *     order, so results do not depend on the device's compute-unit count.
   */

@@ -38,10 +38,12 @@
 //     blocks of every row, then one accept block per sequence), then
 //     k_chunks (chunk sums through exp_rel, then one final-step block per
 //     sequence).
-//   * Trees: k_rows, then k_sample, whose blocks each run the sequence's tree
-//     accept (every node tested in parallel, a wave walks the parent array
-//     with ballots), form their group of chunk sums, and whose last block to
-//     finish for a sequence (an arrival counter) runs the final step.
+//   * Trees: k_rows (row blocks, then one tree-accept block per sequence:
+//     every node tested in parallel, a wave walks the parent array with
+//     ballots; the state and the walk's path go to the workspace), then
+//     k_sample, whose blocks form their group of chunk sums and whose last
+//     block to finish for a sequence (an arrival counter) runs the final
+//     step.
 // Blocks of one launch exchange data through self-validating records
 // (sv_device.h): no cache-wide fences.  A block only waits for blocks of
 // lower index in the same grid, which the in-order dispatch has started, and
@@ -356,7 +358,8 @@ struct VerifyParams {
     uint32_t tab_lo;          // first magnitude key of the table
     // workspace
     uint64_t* chunk_arrivals; // [B] epoch-tagged arrival counters of the sample blocks
-    SeqState* seqs;           // [B] chains: accept state of each sequence (accept kernel -> sample kernels)
+    SeqState* seqs;           // [B] accept state of each sequence (accept blocks -> sample blocks)
+    int32_t* paths;           // [B][nn] trees: the walk's node path (accept blocks -> final step)
     char* stats;              // [B * rows][segs] RowStat records (row kernel -> sample kernel)
     char* part;               // [B][nch] ChunkSums records
     double* etab_g;           // [kTabEntries] the exp(z/T) table (row kernel -> sample kernels)
@@ -789,6 +792,9 @@ __device__ __forceinline__ void chain_accept(const VerifyParams& P, int b, RowSt
 }
 
 constexpr int kMaxNodes = 1024;
+// Nodes below this index keep their rows' statistics in LDS from the node
+// tests (the walk's residual step reads them there).
+constexpr int kStatCacheNodes = 64;
 
 // Tree accept of sequence b, run by the whole block: every node n >= 1 is
 // tested against its parent's q/p rows, then wave 0 walks from the root into
@@ -803,6 +809,7 @@ __device__ __forceinline__ void tree_accept(const VerifyParams& P, int b, SeqSta
     __shared__ int s_par[kMaxNodes];
     __shared__ unsigned char s_acc[kMaxNodes];
     __shared__ unsigned char s_kids[kMaxNodes];
+    __shared__ RowStat s_pst[kStatCacheNodes][2];
     const int32_t* par = P.parents_shared ? P.parents : P.parents + (int64_t)b * nn;
     const int32_t* tok = P.tokens + (int64_t)b * nn;
     for (int n = tid; n < nn; n += kBlock) {
@@ -835,6 +842,11 @@ __device__ __forceinline__ void tree_accept(const VerifyParams& P, int b, SeqSta
             if (stat_bad(rq) || stat_bad(rp)) {
                 err |= (stat_timed_out(rq) || stat_timed_out(rp)) ? 2 : 1;
                 continue;
+            }
+            if (p < kStatCacheNodes) {
+                // every child of p stores the same two values
+                s_pst[p][0] = rq;
+                s_pst[p][1] = rp;
             }
             const double u = accept_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)n);
             const AcceptOut o = accept_logits(zqd, zpd, rq, rp, P.invT, u);
@@ -898,9 +910,15 @@ __device__ __forceinline__ void tree_accept(const VerifyParams& P, int b, SeqSta
         s.status = 0;
         s.u = sample_uniform(P.seed, P.round, (uint32_t)b, (uint32_t)(depth + 1));
         if (residual) {
-            const int rows[2] = {2 * cur, 2 * cur + 1};
             RowStat st[2];
-            load_row_stats<2>(P, b, rows, st);
+            if (cur < kStatCacheNodes) {
+                // stored by cur's children's tests (every one passed)
+                st[0] = s_pst[cur][0];
+                st[1] = s_pst[cur][1];
+            } else {
+                const int rows[2] = {2 * cur, 2 * cur + 1};
+                load_row_stats<2>(P, b, rows, st);
+            }
             fill_residual_state(s, st[0], st[1], P.T);
             // (read and checked by the node tests above; a record that
             // vanished since would be a timeout)
@@ -2253,13 +2271,26 @@ __global__ __launch_bounds__(kBlock) void k_rows(const VerifyParams P)
             fill_value_table(P, x);
             return;
         }
-        // chains: the accept test of sequence x - tab_blocks, by wave 0.
-        // Blocks are dispatched in index order, so every row block has
-        // started when this one does; it polls b's records as they land.
-        if (TREE || threadIdx.x >= 64) return;
+        // the accept test of sequence x - tab_blocks (chains: by wave 0;
+        // trees: the whole block, then the state and the walk's path go to
+        // the workspace).  Blocks are dispatched in index order, so every
+        // row block has started when this one does; it polls b's records as
+        // they land.
         const int b = x - P.tab_blocks;
-        __shared__ RowStat s_rows[2 * kMaxChainN + 1];
-        chain_accept<DT>(P, b, s_rows, true);
+        if constexpr (TREE) {
+            __shared__ SeqState s_state;
+            __shared__ int32_t s_path[kMaxNodes];
+            tree_accept<DT>(P, b, s_state, s_path, true);
+            __syncthreads();
+            const SeqState st = s_state;
+            if (threadIdx.x < 64) put_seq_state(P, b, st);
+            if (st.status == 0)
+                for (int i = (int)threadIdx.x; i <= st.k; i += kBlock) P.paths[(int64_t)b * P.nn + i] = s_path[i];
+        } else {
+            if (threadIdx.x >= 64) return;
+            __shared__ RowStat s_rows[2 * kMaxChainN + 1];
+            chain_accept<DT>(P, b, s_rows, true);
+        }
         return;
     }
     const int b = (int)blockIdx.x / P.r_items;
@@ -2547,10 +2578,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4))) voi
     final_block_tab<DT, true>(P, P.fuse_gstart[j] + off, s_etab, s_buf);
 }
 
-// Sample kernel: block (b, group) runs b's accept step itself (a few records
-// and logits; group 0 writes the accept outputs), forms the chunk sums of its
-// group of chunks of the row(s) b samples from, and the last of b's blocks to
-// finish (an arrival counter per sequence) runs b's final step.
+// Sample kernel: block (b, group) reads b's accept state and walk path (from
+// the accept blocks of the row launch), forms the chunk sums of its group of
+// chunks of the row(s) b samples from, and the last of b's blocks to finish
+// (an arrival counter per sequence) runs b's final step.
 template <int DT>
 __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
 {
@@ -2562,7 +2593,9 @@ __global__ __launch_bounds__(kBlock) void k_sample(const VerifyParams P)
     // bf16: the table for the chunk sums, then the final step's records
     __shared__ __align__(16) double s_pool[DT == DT_BF16 ? kTabBuf : kFinalPool];
     fill_exp_table(s_etab);
-    tree_accept<DT>(P, b, s_state, s_path, g == 0);
+    if (threadIdx.x == 0) s_state = P.seqs[b];
+    const int plen = min(P.nn, P.max_depth + 1);
+    for (int i = (int)threadIdx.x; i < plen; i += kBlock) s_path[i] = P.paths[(int64_t)b * P.nn + i];
     __syncthreads();
     const SeqState s = s_state;
     bool tab = false;
@@ -2653,17 +2686,19 @@ int resident_blocks(K kernel, std::atomic<int>& cache, int block = sv::kBlock)
 }
 
 struct Layout {
-    size_t chunk_arr, seqs, stats, part, tab, tab_done, total;
+    size_t chunk_arr, seqs, paths, stats, part, tab, tab_done, total;
 };
 
-Layout make_layout(int B, int rows, int V)
+// path_len: int32 entries per sequence of the walk's path (trees: nodes)
+Layout make_layout(int B, int rows, int V, int path_len = 0)
 {
     int segs, seg_len;
     segments_of(V, &segs, &seg_len);
     Layout L;
     L.chunk_arr = 0;
     L.seqs = L.chunk_arr + align_up((size_t)B * sizeof(uint64_t));
-    L.stats = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
+    L.paths = L.seqs + align_up((size_t)B * sizeof(sv::SeqState));
+    L.stats = L.paths + align_up((size_t)B * path_len * sizeof(int32_t));
     L.part = L.stats + align_up((size_t)B * rows * segs * sv::kRowStatBytes);
     L.tab = L.part + align_up((size_t)B * nchunks_of(V) * sv::kChunkSumsBytes);
     L.tab_done = L.tab + align_up((size_t)sv::kTabEntries * sizeof(double));
@@ -2761,6 +2796,11 @@ void set_groups(sv::VerifyParams& P)
 #endif
 #ifndef SV_TAB_CHUNKS_PER_BLOCK
 #define SV_TAB_CHUNKS_PER_BLOCK 8
+#endif
+// Whole chunks per tree sample block on the table path (each such block
+// also copies the table into LDS).
+#ifndef SV_TREE_CHUNKS_PER_BLOCK
+#define SV_TREE_CHUNKS_PER_BLOCK SV_TAB_CHUNKS_PER_BLOCK
 #endif
 // The table path in one launch (k_chain_tab) rather than a row launch and a
 // sample launch; sequences per section, and the lags (in sections) of a
@@ -2899,13 +2939,13 @@ template <int DT>
 int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream)
 {
     if (P.use_tab) {
-        // table path: blocks of about SV_TAB_CHUNKS_PER_BLOCK whole chunks
-        // (each block copies the table and runs the tree accept), but no
+        // table path: blocks of about SV_TREE_CHUNKS_PER_BLOCK whole chunks
+        // (each block copies the table), but no
         // more than one round of the blocks the device holds at once
         static std::atomic<int> cache{0};
         const int resident = resident_blocks(&sv::k_sample<DT>, cache);
         const int whole = P.V / sv::kChunk;
-        int groups = (whole + SV_TAB_CHUNKS_PER_BLOCK - 1) / SV_TAB_CHUNKS_PER_BLOCK;
+        int groups = (whole + SV_TREE_CHUNKS_PER_BLOCK - 1) / SV_TREE_CHUNKS_PER_BLOCK;
         const int round = resident > 0 && P.B > 0 ? resident / P.B : groups;
         groups = groups > round ? round : groups;
         groups = groups < 1 ? 1 : groups;
@@ -2915,7 +2955,7 @@ int launch_tree(sv::VerifyParams& P, const sv_timing* timing, hipStream_t stream
     } else {
         set_groups<DT>(P);
     }
-    const int64_t row_grid = (int64_t)P.B * P.r_items + P.tab_blocks;
+    const int64_t row_grid = (int64_t)P.B * P.r_items + P.tab_blocks + P.B;
     const int64_t sample_grid = (int64_t)P.B * P.groups;
     launch_rows<DT, true>(P, row_grid, timing, stream);
     hipExtLaunchKernelGGL((sv::k_sample<DT>), dim3((unsigned)sample_grid), dim3(sv::kBlock), 0, stream, nullptr,
@@ -2931,6 +2971,7 @@ int launch_verify(sv::VerifyParams& P, int dtype, void* workspace, const Layout&
     char* ws = static_cast<char*>(workspace);
     P.chunk_arrivals = reinterpret_cast<uint64_t*>(ws + L.chunk_arr);
     P.seqs = reinterpret_cast<sv::SeqState*>(ws + L.seqs);
+    P.paths = reinterpret_cast<int32_t*>(ws + L.paths);
     P.stats = ws + L.stats;
     P.part = ws + L.part;
     P.etab_g = reinterpret_cast<double*>(ws + L.tab);
@@ -3036,7 +3077,7 @@ size_t sv_chain_workspace_bytes(int B, int N, int V)
 size_t sv_tree_workspace_bytes(int B, int T, int V)
 {
     if (B < 0 || T < 0 || T >= sv::kMaxNodes || V < 1 || V > sv::kMaxChunks * sv::kChunk) return 0;
-    return make_layout(B, 2 * (T + 1), V).total;
+    return make_layout(B, 2 * (T + 1), V, T + 1).total;
 }
 
 int spec_verify_chain(const void* target_logits, int64_t tgt_seq_stride, int64_t tgt_row_stride,
@@ -3140,7 +3181,7 @@ int spec_verify_tree(const void* target_logits, int64_t tgt_seq_stride, int64_t 
     if (rc) return rc;
     if ((rc = check_rows(draft_logits, drf_seq_stride, drf_row_stride, es, B, nn, V))) return rc;
     if (!item_count_ok(B, 2 * nn, V)) return SV_ESHAPE;
-    const Layout L = make_layout(B, 2 * nn, V);
+    const Layout L = make_layout(B, 2 * nn, V, nn);
     if (!regions_fit(L)) return SV_ESHAPE;
     if (!workspace || workspace_bytes < L.total || ((uintptr_t)workspace & 15u)) return SV_EWORKSPACE;
 

@@ -601,6 +601,29 @@ def test_tree_edge_cases():
     assert (deep["num_accepted"] == -1).all()
 
 
+def test_tree_deep_residual():
+    """Path-shaped trees of 100 nodes with near-identical draft and verifier
+    logits, tokens the draft row's argmax: walks go deep, and some end with a
+    residual at a node of index >= 64 (whose row statistics the walk loads
+    again rather than reading them from the node tests' LDS copy)."""
+    log("[case] tree_deep_residual")
+    w = W["tree_static_b32_v128256"].with_sizes(V=3000, sigma_noise=0.05)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    nn, B = 100, 96
+    zq = synth.verifier_logits(w, B * nn, g, "cuda").view(B, nn, w.V)
+    zp = synth.draft_from_verifier(w, zq, g)
+    zq, zp = zq.to(w.torch_dtype), zp.to(w.torch_dtype)
+    par = torch.arange(-1, nn - 1, dtype=torch.int32, device="cuda")
+    tok = torch.zeros((B, nn), dtype=torch.int32, device="cuda")
+    tok[:, 1:] = torch.argmax(zp[:, :-1].float(), dim=-1).to(torch.int32)
+    rep, out = run_tree(zq, zp, tok, par, 5, 2, w.T, nn - 1)
+    k = out["num_accepted"]
+    log(f"   residuals past node 63: {int(((k >= 64) & (k < nn - 1)).sum())}, bonus at the leaf: {int((k == nn - 1).sum())}")
+    assert ((k >= 64) & (k < nn - 1)).any()
+    _done("tree_deep_residual", rep)
+
+
 @pytest.mark.parametrize("wl", ["tree_static_b32_v128256", "tree_dynamic_b128_v152064"])
 def test_tree_full_size(wl):
     """The static 26-node tree (B=32) and the dynamic 61-node trees (B=128,
